@@ -1,0 +1,101 @@
+"""Exact simulation of the expert slot pool (oracle side, test infrastructure only).
+
+The pages' expert cache keeps whole expert bundles resident in VRAM, checks
+residency for the experts the router returned, evicts the least recently used
+bundles on a miss, and, when a batch needs more experts than fit, blocks,
+performs the transfers, then executes ("Running 35B MoE Models on 8GB GPUs:
+How vvllm-ms Caches Experts in System RAM", section "Technical Insight"); only
+experts that actually run are loaded ("NovaLLM: Running Massive MoE Models
+Fully In-Memory", section 3, Optimization #1).
+
+Readings taken where the pages are silent:
+
+* the pool holds n_slots bundles and starts empty;
+* per step the touched set is the distinct experts in topk_idx; they are
+  accessed in the order: experts resident at the start of the step (ascending
+  id), then the non-resident ones (ascending id);
+* that sequence is cut into transfer waves of at most n_slots consecutive
+  experts; a wave's transfers complete before its experts run;
+* each access is a textbook LRU access: a hit refreshes the expert's recency;
+  a miss fills the lowest free slot, else evicts the least recently accessed
+  expert and reuses its slot;
+* weights are read-only, so an eviction is a table update with no copy back.
+
+Under this order an eviction never removes an expert of the wave being formed:
+every expert accessed in the wave is more recent than any candidate victim,
+and a wave holds at most n_slots experts.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+
+@dataclass
+class WaveEntry:
+    expert: int
+    slot: int
+    hit: bool
+    evicted: int  # expert evicted to make room, or -1
+
+
+@dataclass
+class StepPlan:
+    waves: list = field(default_factory=list)   # list[list[WaveEntry]]
+
+
+@dataclass
+class CacheStats:
+    hits: int = 0
+    misses: int = 0
+    evictions: int = 0
+    waves: int = 0
+    steps: int = 0
+
+
+class LRUSlotCache:
+    def __init__(self, n_experts: int, n_slots: int):
+        if n_slots < 1 or n_experts < 1:
+            raise ValueError("need at least one expert and one slot")
+        self.E, self.S = n_experts, n_slots
+        self.reset()
+
+    def reset(self):
+        self.slot_of = [-1] * self.E
+        self.owner = [-1] * self.S
+        self.last = [0] * self.E
+        self.clock = 0
+        self.stats = CacheStats()
+
+    def resident(self):
+        return [e for e in range(self.E) if self.slot_of[e] >= 0]
+
+    def _access(self, e: int) -> WaveEntry:
+        self.clock += 1
+        if self.slot_of[e] >= 0:
+            self.last[e] = self.clock
+            self.stats.hits += 1
+            return WaveEntry(e, self.slot_of[e], True, -1)
+        self.stats.misses += 1
+        evicted = -1
+        free = [s for s in range(self.S) if self.owner[s] < 0]
+        if free:
+            slot = free[0]
+        else:
+            evicted = min(self.resident(), key=lambda v: self.last[v])
+            slot = self.slot_of[evicted]
+            self.slot_of[evicted] = -1
+            self.stats.evictions += 1
+        self.owner[slot] = e
+        self.slot_of[e] = slot
+        self.last[e] = self.clock
+        return WaveEntry(e, slot, False, evicted)
+
+    def step(self, touched_experts) -> StepPlan:
+        touched = sorted(set(int(e) for e in touched_experts))
+        order = [e for e in touched if self.slot_of[e] >= 0] + [e for e in touched if self.slot_of[e] < 0]
+        plan = StepPlan()
+        for w0 in range(0, len(order), self.S):
+            plan.waves.append([self._access(e) for e in order[w0:w0 + self.S]])
+        self.stats.waves += len(plan.waves)
+        self.stats.steps += 1
+        return plan

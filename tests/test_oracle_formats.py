@@ -1,0 +1,133 @@
+"""Pins for oracle.formats: the e4m3 codec and bf16 decoding, against the OCP
+spec's named points, torch's own conversions (an independent library) and
+exhaustive nearest-value search."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_points():
+    pts = []
+    for line in open(os.path.join(GOLDEN, "e4m3_points.txt")):
+        line = line.split("#")[0].strip()
+        if line:
+            c, v = line.split()
+            pts.append((int(c, 16), float(v)))
+    return pts
+
+
+def test_e4m3_named_points():
+    for code, val in _read_points():
+        got = formats.decode_e4m3(np.array([code], np.uint8))[0]
+        if np.isnan(val):
+            assert np.isnan(got)
+        else:
+            assert got == val and np.signbit(got) == np.signbit(val), hex(code)
+            if not np.isnan(val):
+                assert formats.encode_e4m3(np.array([val]))[0] == code
+
+
+def test_e4m3_all_codes_match_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = formats.decode_e4m3(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+
+
+def test_e4m3_round_trip_all_finite_codes():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = formats.decode_e4m3(codes)
+    assert np.array_equal(formats.encode_e4m3(vals), codes)
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 0.05, 1, 30, 200)])
+    x = np.clip(x, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = formats.encode_e4m3(x)
+    # torch maps values rounding to zero to +-0 by sign as well
+    assert np.array_equal(got, ref)
+
+
+def test_e4m3_encode_exhaustive_nearest():
+    rng = np.random.default_rng(8)
+    table = formats.e4m3_table()
+    finite = [c for c in range(128) if not np.isnan(table[c])]
+    # include exact midpoints between neighbours to exercise ties-to-even
+    mids = [(table[a] + table[a + 1]) / 2 for a in range(0, 126)]
+    xs = np.concatenate([rng.uniform(0, 448, 3000), np.array(mids)])
+    got = formats.encode_e4m3(xs)
+    for x, g in zip(xs, got):
+        d = [abs(table[c] - x) for c in finite]
+        best = min(d)
+        cands = [c for c, dd in zip(finite, d) if dd == best]
+        want = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        assert g == want, (x, g, want)
+
+
+def test_e4m3_saturates():
+    got = formats.encode_e4m3(np.array([1000.0, -1000.0, 464.0, 449.0]))
+    assert list(got) == [0x7E, 0xFE, 0x7E, 0x7E]
+
+
+def test_bf16_decode_matches_torch():
+    rng = np.random.default_rng(9)
+    bits = rng.integers(0, 2 ** 16, 50000, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = formats.decode_bf16(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_quantize_rows_error_bound_and_amax():
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal((64, 512)) * rng.uniform(0.01, 50, (64, 1))).astype(np.float32)
+    x[3, 128:256] = 0.0                       # an all-zero block takes scale 1
+    q, s = formats.quantize_rows_e4m3(x)
+    assert s.shape == (64, 4) and s.dtype == np.float32
+    assert s[3, 1] == 1.0 and np.all(q[3, 128:256] & 0x7F == 0)
+    deq = formats.dequantize_rows(q, s)
+    y = x.reshape(64, 4, 128) / s[:, :, None]
+    # 3 mantissa bits: relative error <= 2^-4 on normals, absolute <= 2^-10 on subnormals
+    err = np.abs(deq.reshape(64, 4, 128) - x.reshape(64, 4, 128)) / s[:, :, None]
+    bound = np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    # the block maximum lands on the top code 448
+    blk = np.abs(x.reshape(64, 4, 128)).argmax(axis=2)
+    qm = np.take_along_axis(q.reshape(64, 4, 128), blk[:, :, None], axis=2)[..., 0] & 0x7F
+    nz = s != 1.0
+    assert np.all(qm[nz] == 0x7E)
+
+
+def test_quantize_rows_matches_torch_pipeline():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((16, 256)).astype(np.float32)
+    q, s = formats.quantize_rows_e4m3(x)
+    xb = torch.from_numpy(x).view(16, 2, 128)
+    amax = xb.abs().amax(dim=2)
+    scale = amax / 448.0
+    ref = (xb / scale[:, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(q, ref.reshape(16, 256).numpy())
+    assert np.array_equal(s, scale.numpy())
+
+
+def test_dequantize_weight_blocks():
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 256, (256, 384)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    scales = rng.uniform(0.5, 2.0, (2, 3)).astype(np.float32)
+    w = formats.dequantize_weight_blocks(codes, scales)
+    t = formats.e4m3_table()
+    assert w[0, 0] == t[codes[0, 0]] * np.float64(scales[0, 0])
+    assert w[200, 300] == t[codes[200, 300]] * np.float64(scales[1, 2])
+    assert w[127, 129] == t[codes[127, 129]] * np.float64(scales[0, 1])
