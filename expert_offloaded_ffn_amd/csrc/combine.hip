@@ -1,0 +1,108 @@
+// moe_combine: gate-weighted sum of each token's expert rows back in token
+// order, plus the always-resident shared expert ("Running 35B MoE Models on 8GB
+// GPUs", section "Gotcha": shared experts sit outside the routed, cached set).
+//
+// One wavefront per token; each lane owns 8 consecutive columns per step, reads
+// the k expert rows through perm_dst with 16-byte (bf16) or 32-byte (fp32) loads,
+// accumulates in fp32 in slot order j = 0..k-1, adds the shared term last and
+// rounds once.
+#include "moe_internal.h"
+
+namespace moeffn {
+namespace {
+
+template <typename TY>
+__device__ __forceinline__ void load8(const TY* p, float v[8]);
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+template <typename TY, typename TO>
+__global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, const int32_t* __restrict__ perm_dst,
+                                                      const float* __restrict__ gate, const TY* __restrict__ shared_y,
+                                                      const float* __restrict__ shared_gate, TO* __restrict__ out,
+                                                      int T, int k, int d) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  int rows[32];
+  float g[32];
+  for (int j = 0; j < k; ++j) {
+    rows[j] = perm_dst[(size_t)t * k + j];
+    g[j] = gate[(size_t)t * k + j];
+  }
+  const float sg = shared_y ? (shared_gate ? shared_gate[t] : 1.0f) : 0.0f;
+  for (int c = lane * 8; c < d; c += 512) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      float v[8];
+      load8<TY>(y + (size_t)rows[j] * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[i], acc[i]);
+    }
+    if (shared_y) {
+      float v[8];
+      load8<TY>(shared_y + (size_t)t * d + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(sg, v[i], acc[i]);
+    }
+    if constexpr (sizeof(TO) == 2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+      *reinterpret_cast<uint4*>(out + (size_t)t * d + c) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      *reinterpret_cast<float4*>(out + (size_t)t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      *reinterpret_cast<float4*>(out + (size_t)t * d + c + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moeffn
+
+using namespace moeffn;
+
+extern "C" moe_status moe_combine(int32_t T, int32_t k, int32_t d, const void* y, int32_t y_dtype,
+                                  const int32_t* perm_dst, const float* topk_gate, const void* shared_y,
+                                  const float* shared_gate, void* out, int32_t out_dtype, void* stream) {
+  clear_error();
+  MOE_REQUIRE(T >= 0 && k >= 1 && k <= 32 && d >= 8 && d % 8 == 0, MOE_EINVAL,
+              "moe_combine: need T >= 0, 1 <= k <= 32, d a positive multiple of 8 (T=%d k=%d d=%d)", T, k, d);
+  MOE_REQUIRE(y_dtype == MOE_F32 || y_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_combine: y_dtype %d", y_dtype);
+  MOE_REQUIRE(out_dtype == MOE_F32 || out_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_combine: out_dtype %d", out_dtype);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(y && perm_dst && topk_gate && out, MOE_EINVAL, "moe_combine: NULL argument");
+  MOE_REQUIRE(aligned(y, 16) && aligned(out, 16) && (!shared_y || aligned(shared_y, 16)), MOE_EINVAL,
+              "moe_combine: y, shared_y and out must be 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  dim3 grid((T + 3) / 4), block(256);
+  if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), grid, block, 0, s, (const bf16_t*)y, perm_dst, topk_gate,
+                       (const bf16_t*)shared_y, shared_gate, (bf16_t*)out, T, k, d);
+  else if (y_dtype == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<bf16_t, float>), grid, block, 0, s, (const bf16_t*)y, perm_dst, topk_gate,
+                       (const bf16_t*)shared_y, shared_gate, (float*)out, T, k, d);
+  else if (out_dtype == MOE_BF16)
+    hipLaunchKernelGGL((combine_kernel<float, bf16_t>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
+                       (const float*)shared_y, shared_gate, (bf16_t*)out, T, k, d);
+  else
+    hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
+                       (const float*)shared_y, shared_gate, (float*)out, T, k, d);
+  return check_launch("moe_combine");
+}

@@ -1,0 +1,408 @@
+// moe_grouped_ffn: every selected expert's SwiGLU FFN over the rows grouped to it.
+//
+// "The Billion-Token Bottleneck" (section "The Geometry of the Problem") makes
+// each expert a feed-forward network; "NovaLLM: Running Massive MoE Models
+// Fully In-Memory" (section 3) runs only the experts that were hit. The expert
+// weights are read through the slot table (pool + slot * stride), which is how
+// the same kernels serve a fully resident layer and the expert slot pool.
+//
+// Kernels:
+//  ffn_tile_map       per-expert m-tile counts -> prefix (device side; no host sync)
+//  ffn_gemm_bf16      prefill tile engine on MFMA 16x16x32 bf16: 256x256x64 block
+//                     tiles, 4 waves of 128x128, A and B staged through LDS in the
+//                     1 KiB fragment-tile layout (conflict-free 16 B per lane),
+//                     double-buffered, one barrier per k-step; XCD-aware mapping of
+//                     tiles so the m-tiles that share a weight tile run on the same
+//                     XCD's L2. Mode GATEUP writes H = silu(G) * U (bf16), mode
+//                     DOWN writes Y.
+//  ffn_f32_*          fp32 VALU path (one thread per output element) for fp32
+//                     weights.
+#include "moe_internal.h"
+
+namespace moeffn {
+namespace {
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kMaxE = 1024;
+
+// Bundle geometry (must match moe_pack_expert).
+struct BundleGeom {
+  int64_t gu_off, dn_off, sg_off, su_off, sd_off, bytes;
+};
+
+__host__ __device__ inline BundleGeom bundle_geom(int d, int F, int dt) {
+  BundleGeom g{};
+  auto al = [](int64_t v) { return (v + 255) / 256 * 256; };
+  if (dt == MOE_BF16) {
+    g.gu_off = 0;
+    g.dn_off = al((int64_t)2 * F * d * 2);
+    g.bytes = g.dn_off + al((int64_t)d * F * 2);
+  } else if (dt == MOE_FP8_E4M3) {
+    g.gu_off = 0;
+    g.dn_off = al((int64_t)2 * F * d);
+    g.sg_off = g.dn_off + al((int64_t)d * F);
+    g.su_off = g.sg_off + al((int64_t)(F / 128) * (d / 128) * 4);
+    g.sd_off = g.su_off + al((int64_t)(F / 128) * (d / 128) * 4);
+    g.bytes = g.sd_off + al((int64_t)(d / 128) * (F / 128) * 4);
+  } else {
+    g.gu_off = 0;                               // W_gate^T [F, d] then W_up^T [F, d]
+    g.dn_off = al((int64_t)2 * F * d * 4);      // W_down^T [d, F]
+    g.bytes = g.dn_off + al((int64_t)d * F * 4);
+  }
+  return g;
+}
+
+// ----------------------------------------------------------- tile map ---
+// tile_prefix[e] = m-tiles of active experts before e; tile_prefix[E] = total.
+__global__ __launch_bounds__(1024) void ffn_tile_map(const int32_t* __restrict__ offsets,
+                                                     const int32_t* __restrict__ slot_of_expert,
+                                                     int32_t* __restrict__ tile_prefix, int E, int bm) {
+  __shared__ int32_t v[kMaxE];
+  const int e = threadIdx.x;
+  if (e < E) {
+    const int n = offsets[e + 1] - offsets[e];
+    v[e] = (n > 0 && slot_of_expert[e] >= 0) ? (n + bm - 1) / bm : 0;
+  }
+  __syncthreads();
+  if (e == 0) {
+    int acc = 0;
+    for (int i = 0; i < E; ++i) {
+      tile_prefix[i] = acc;
+      acc += v[i];
+    }
+    tile_prefix[E] = acc;
+  }
+}
+
+struct GemmArgs {
+  const bf16_t* a;             // [*, K] row-major
+  const int32_t* a_row_src;    // NULL: GEMM row r reads a row r
+  int a_row_div;
+  const int32_t* offsets;      // [E+1]
+  const int32_t* slot_of_expert;
+  const int32_t* tile_prefix;  // [E+1]
+  const char* pool;
+  int64_t slot_stride;
+  int64_t b_off;               // byte offset of B inside a bundle
+  int N, K;                    // B is [N, K] in 1 KiB fragment tiles
+  void* out;                   // GATEUP: H [rows, N/2] bf16; DOWN: Y [rows, N]
+  int out_dtype;
+  int E;
+};
+
+enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
+
+// Map a block to (expert, m-tile, n-tile). Returns false when the block has no tile.
+__device__ __forceinline__ bool decode_tile(const GemmArgs& p, int NT, int& e, int& mt, int& nt) {
+  const int E = p.E;
+  const int total = p.tile_prefix[E] * NT;
+  const int total_pad = (total + 7) & ~7;
+  const int b = blockIdx.x;
+  if (b >= total_pad) return false;
+  const int L = (b & 7) * (total_pad >> 3) + (b >> 3);  // consecutive tiles on one XCD
+  if (L >= total) return false;
+  const int q = L / NT;
+  int lo = 0, hi = E - 1;  // last e with tile_prefix[e] <= q
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tile_prefix[mid] <= q) lo = mid;
+    else hi = mid - 1;
+  }
+  e = lo;
+  const int base = p.tile_prefix[e];
+  const int mte = p.tile_prefix[e + 1] - base;
+  const int local = L - base * NT;
+  nt = local / mte;
+  mt = local % mte;
+  return true;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[2][2 * kBM * kBK * 2];  // 2 x (A 32 KiB + B 32 KiB)
+  const int NT = p.N / kBN;
+  int e, mt, nt;
+  if (!decode_tile(p, NT, e, mt, nt)) return;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int row0 = p.offsets[e] + mt * kBM;
+  const int row_end = p.offsets[e + 1];
+  const int n0 = nt * kBN;
+  const int KB32 = p.K / 32;
+  const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
+
+  // A rows this thread loads: m-blocks w*4 + i (i = 0..3), row (lane & 15) in the block
+  const bf16_t* arow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int r = row0 + (w * 4 + i) * 16 + (lane & 15);
+    r = r < row_end ? r : row_end - 1;
+    const int src = p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
+    arow[i] = p.a + (size_t)src * p.K + 8 * (lane >> 4);
+  }
+  // B tiles this thread loads: n-blocks w*4 + i, k-blocks 0..1 of the step
+  const char* bptr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bptr[i] = B + ((int64_t)(n0 / 16 + w * 4 + i) * KB32) * 1024 + 16 * lane;
+
+  uint4 ra[8], rb[8];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = j >> 1, kb = j & 1;
+      ra[j] = *reinterpret_cast<const uint4*>(arow[i] + kt * kBK + kb * 32);
+      rb[j] = *reinterpret_cast<const uint4*>(bptr[i] + ((int64_t)kt * 2 + kb) * 1024);
+    }
+  };
+  auto lstore = [&](int buf) {
+    char* sa = smem[buf];
+    char* sb = smem[buf] + kBM * kBK * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int blk = w * 8 + j;  // = mb*2 + kb
+      *reinterpret_cast<uint4*>(sa + blk * 1024 + 16 * lane) = ra[j];
+      *reinterpret_cast<uint4*>(sb + blk * 1024 + 16 * lane) = rb[j];
+    }
+  };
+
+  f32x4_t acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int wm = w >> 1, wn = w & 1;
+  const int KT = p.K / kBK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    const char* sa = smem[buf];
+    const char* sb = smem[buf] + kBM * kBK * 2;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t af[8], bfr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + ((wm * 8 + i) * 2 + kk) * 1024 + 16 * lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + ((wn * 8 + j) * 2 + kk) * 1024 + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile
+  const int rbase = row0 + wm * 128 + 4 * (lane >> 4);
+  if constexpr (MODE == MODE_GATEUP) {
+    const int F = p.N / 2;
+    bf16_t* H = static_cast<bf16_t*>(p.out);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int hcol = n0 / 2 + wn * 64 + pp * 16 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + q;
+          if (r < row_end) {
+            const float g = acc[i][2 * pp][q], u = acc[i][2 * pp + 1][q];
+            H[(size_t)r * F + hcol] = f32_to_bf16(silu_f32(g) * u);
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + q;
+          if (r < row_end) {
+            if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[(size_t)r * p.N + col] = f32_to_bf16(acc[i][j][q]);
+            else static_cast<float*>(p.out)[(size_t)r * p.N + col] = acc[i][j][q];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------- fp32 path ---
+__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int r) {
+  int lo = 0, hi = E - 1;  // last e with offsets[e] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (offsets[mid] <= r) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void ffn_f32_gateup(const float* __restrict__ a, const int32_t* __restrict__ a_row_src,
+                                                      int a_row_div, const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ slot_of_expert,
+                                                      const char* __restrict__ pool, int64_t stride,
+                                                      float* __restrict__ H, int rows, int d, int F, int E) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)rows * F) return;
+  const int r = (int)(gid / F), f = (int)(gid % F);
+  const int e = expert_of_row(offsets, E, r);
+  const int slot = slot_of_expert[e];
+  if (slot < 0) return;
+  const float* wg = reinterpret_cast<const float*>(pool + (int64_t)slot * stride) + (size_t)f * d;
+  const float* wu = wg + (size_t)F * d;
+  const int src = a_row_src ? a_row_src[r] / a_row_div : r;
+  const float* x = a + (size_t)src * d;
+  float g = 0.f, u = 0.f;
+  for (int i = 0; i < d; ++i) {
+    g = fmaf(x[i], wg[i], g);
+    u = fmaf(x[i], wu[i], u);
+  }
+  H[(size_t)r * F + f] = silu_f32(g) * u;
+}
+
+__global__ __launch_bounds__(256) void ffn_f32_down(const float* __restrict__ H, const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ slot_of_expert,
+                                                    const char* __restrict__ pool, int64_t stride, int64_t dn_off,
+                                                    void* __restrict__ y, int y_dtype, int rows, int d, int F, int E) {
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)rows * d) return;
+  const int r = (int)(gid / d), c = (int)(gid % d);
+  const int e = expert_of_row(offsets, E, r);
+  const int slot = slot_of_expert[e];
+  if (slot < 0) return;
+  const float* wd = reinterpret_cast<const float*>(pool + (int64_t)slot * stride + dn_off) + (size_t)c * F;
+  const float* h = H + (size_t)r * F;
+  float s = 0.f;
+  for (int i = 0; i < F; ++i) s = fmaf(h[i], wd[i], s);
+  if (y_dtype == MOE_BF16) static_cast<bf16_t*>(y)[(size_t)r * d + c] = f32_to_bf16(s);
+  else static_cast<float*>(y)[(size_t)r * d + c] = s;
+}
+
+size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off) {
+  const size_t hsz = act_dtype == MOE_F32 ? 4 : 2;
+  *h_off = 0;
+  *map_off = align_up((size_t)rows * t->d_ff * hsz, 256);
+  return *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256);
+}
+
+}  // namespace
+}  // namespace moeffn
+
+using namespace moeffn;
+
+extern "C" size_t moe_bundle_bytes(int32_t d_model, int32_t d_ff, int32_t w_dtype) {
+  if (d_model < 1 || d_ff < 1) return 0;
+  if (w_dtype == MOE_BF16 && (d_model % 32 || d_ff % 32)) return 0;
+  if (w_dtype == MOE_FP8_E4M3 && (d_model % 128 || d_ff % 128)) return 0;
+  if (w_dtype == MOE_F32 && d_model % 4) return 0;
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3) return 0;
+  return (size_t)bundle_geom(d_model, d_ff, w_dtype).bytes;
+}
+
+extern "C" size_t moe_grouped_ffn_workspace_size(const moe_expert_table* table, int32_t rows, int32_t act_dtype) {
+  if (!table || rows < 0) return 0;
+  size_t h, m;
+  return ws_layout(table, rows, act_dtype, &h, &m);
+}
+
+extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t rows, const int32_t* offsets,
+                                      const void* a, const float* a_scale, int32_t act_dtype,
+                                      const int32_t* a_row_src, int32_t a_row_div, void* y, int32_t y_dtype,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  MOE_REQUIRE(table != nullptr, MOE_EINVAL, "moe_grouped_ffn: table is NULL");
+  const moe_expert_table t = *table;
+  MOE_REQUIRE(rows >= 0, MOE_EINVAL, "moe_grouped_ffn: rows=%d < 0", rows);
+  MOE_REQUIRE(t.n_experts >= 1 && t.n_experts <= kMaxE, MOE_EINVAL, "moe_grouped_ffn: n_experts=%d outside [1, %d]",
+              t.n_experts, kMaxE);
+  const size_t bb = moe_bundle_bytes(t.d_model, t.d_ff, t.w_dtype);
+  MOE_REQUIRE(bb > 0, MOE_EINVAL, "moe_grouped_ffn: unsupported sizes d=%d F=%d for w_dtype %d", t.d_model, t.d_ff,
+              t.w_dtype);
+  MOE_REQUIRE(t.slot_stride >= (int64_t)bb && t.slot_stride % 256 == 0, MOE_EINVAL,
+              "moe_grouped_ffn: slot_stride %lld must be >= bundle bytes %zu and a multiple of 256",
+              (long long)t.slot_stride, bb);
+  MOE_REQUIRE(y_dtype == MOE_F32 || y_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_grouped_ffn: y_dtype %d", y_dtype);
+  if (a_row_src) MOE_REQUIRE(a_row_div >= 1, MOE_EINVAL, "moe_grouped_ffn: a_row_div must be >= 1");
+  if (rows == 0) return MOE_OK;
+  MOE_REQUIRE(t.pool && t.slot_of_expert && offsets && a && y && ws, MOE_EINVAL, "moe_grouped_ffn: NULL argument");
+  MOE_REQUIRE(aligned(t.pool, 256) && aligned(a, 16) && aligned(y, 16) && aligned(ws, 256), MOE_EINVAL,
+              "moe_grouped_ffn: pool needs 256-B, a and y 16-B, ws 256-B alignment");
+  size_t h_off, map_off;
+  const size_t need = ws_layout(&t, rows, act_dtype, &h_off, &map_off);
+  MOE_REQUIRE(ws_bytes >= need, MOE_ECAPACITY, "moe_grouped_ffn: workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = as_stream(stream);
+  const BundleGeom g = bundle_geom(t.d_model, t.d_ff, t.w_dtype);
+  char* wsb = static_cast<char*>(ws);
+  const int E = t.n_experts, d = t.d_model, F = t.d_ff;
+
+  if (t.w_dtype == MOE_F32) {
+    MOE_REQUIRE(act_dtype == MOE_F32, MOE_EUNSUPPORTED, "moe_grouped_ffn: fp32 weights need fp32 activations");
+    float* H = reinterpret_cast<float*>(wsb + h_off);
+    const long long n1 = (long long)rows * F, n2 = (long long)rows * d;
+    hipLaunchKernelGGL(ffn_f32_gateup, dim3((unsigned)((n1 + 255) / 256)), dim3(256), 0, s, static_cast<const float*>(a),
+                       a_row_src, a_row_div, offsets, t.slot_of_expert, static_cast<const char*>(t.pool),
+                       t.slot_stride, H, rows, d, F, E);
+    hipLaunchKernelGGL(ffn_f32_down, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, s, H, offsets,
+                       t.slot_of_expert, static_cast<const char*>(t.pool), t.slot_stride, g.dn_off, y, y_dtype, rows,
+                       d, F, E);
+    return check_launch("moe_grouped_ffn f32");
+  }
+  if (t.w_dtype == MOE_BF16) {
+    MOE_REQUIRE(act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_grouped_ffn: bf16 weights need bf16 activations");
+    MOE_REQUIRE((2 * F) % kBN == 0 && d % kBN == 0 && d % kBK == 0 && F % kBK == 0, MOE_EUNSUPPORTED,
+                "moe_grouped_ffn: bf16 prefill tiles need d and 2F multiples of %d and F a multiple of %d", kBN, kBK);
+    int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
+    bf16_t* H = reinterpret_cast<bf16_t*>(wsb + h_off);
+    hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
+                       tile_prefix, E, kBM);
+    const int max_mt = (rows + kBM - 1) / kBM + (E < rows ? E : rows);
+    GemmArgs p{};
+    p.a_row_src = a_row_src;
+    p.a_row_div = a_row_div;
+    p.offsets = offsets;
+    p.slot_of_expert = t.slot_of_expert;
+    p.tile_prefix = tile_prefix;
+    p.pool = static_cast<const char*>(t.pool);
+    p.slot_stride = t.slot_stride;
+    p.E = E;
+    // gate/up + SwiGLU: B = W_gu [2F, d]
+    p.a = static_cast<const bf16_t*>(a);
+    p.b_off = g.gu_off;
+    p.N = 2 * F;
+    p.K = d;
+    p.out = H;
+    p.out_dtype = MOE_BF16;
+    long long nblk = (long long)max_mt * (p.N / kBN);
+    prof_mark(s, MOE_PROF_GATEUP, false);
+    hipLaunchKernelGGL(ffn_gemm_bf16<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    prof_mark(s, MOE_PROF_GATEUP, true);
+    // down: B = W_dn [d, F], A = H (already in row order)
+    p.a = H;
+    p.a_row_src = nullptr;
+    p.a_row_div = 1;
+    p.b_off = g.dn_off;
+    p.N = d;
+    p.K = F;
+    p.out = y;
+    p.out_dtype = y_dtype;
+    nblk = (long long)max_mt * (p.N / kBN);
+    prof_mark(s, MOE_PROF_DOWN, false);
+    hipLaunchKernelGGL(ffn_gemm_bf16<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    prof_mark(s, MOE_PROF_DOWN, true);
+    return check_launch("moe_grouped_ffn bf16");
+  }
+  (void)a_scale;
+  MOE_REQUIRE(false, MOE_EUNSUPPORTED, "moe_grouped_ffn: w_dtype %d not implemented yet", t.w_dtype);
+}

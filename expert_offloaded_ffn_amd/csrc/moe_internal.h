@@ -1,0 +1,73 @@
+// Internal helpers shared by the library's translation units: status/error
+// reporting, argument checks, element conversions and MFMA vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+
+namespace moeffn {
+
+// ---------------------------------------------------------------- errors --
+void set_error(const char* fmt, ...);
+void clear_error();
+
+#define MOE_REQUIRE(cond, code, ...)            \
+  do {                                          \
+    if (!(cond)) {                              \
+      ::moeffn::set_error(__VA_ARGS__);         \
+      return (code);                            \
+    }                                           \
+  } while (0)
+
+#define MOE_HIP(call)                                                              \
+  do {                                                                             \
+    hipError_t e_ = (call);                                                        \
+    if (e_ != hipSuccess) {                                                        \
+      ::moeffn::set_error("%s failed: %s", #call, hipGetErrorString(e_));          \
+      return MOE_EHIP;                                                             \
+    }                                                                              \
+  } while (0)
+
+// Any error left by earlier asynchronous work (or a failed launch) becomes MOE_EHIP.
+moe_status check_launch(const char* what);
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Timing marks around heavy kernels (no-op unless moe_profile_enable(1)).
+void prof_mark(hipStream_t s, int kind, bool end);
+
+// ----------------------------------------------------------- conversions --
+typedef unsigned short bf16_t;  // bf16 bit pattern
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// MFMA operand/accumulator vectors.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace moeffn

@@ -1,0 +1,98 @@
+// moe_pack_expert: writes one expert bundle in the layout the kernels read.
+//
+// The bundle is the unit of residency: an expert's three matrices and, for
+// fp8, their block scales travel together ("Running 35B MoE Models on 8GB
+// GPUs", section "Technical Insight": quantisation scales belong to the atomic
+// cache unit). Pure host code.
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace {
+
+inline size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Row R of the interleaved [2F, K] gate/up matrix -> (is_up, hidden column).
+inline void gu_row(int R, bool* up, int* col) {
+  const int j = R / 32, rr = R % 32;
+  *up = rr >= 16;
+  *col = 16 * j + (rr & 15);
+}
+
+// bf16/f32 element copy helpers
+template <typename T>
+inline T at(const void* p, size_t i) { return static_cast<const T*>(p)[i]; }
+
+// Tiled store of an [N, K] matrix given by get(n, k): 1 KiB tiles of 16 x 32
+// (2-byte elements) or 2 KiB tiles of 16 x 128 (1-byte elements).
+template <typename T, int TK, typename Get>
+void store_tiled(char* dst, int N, int K, Get get) {
+  const int tiles_k = K / TK;
+  const int per_lane = TK / 4;  // elements per lane: 8 (bf16, TK=32) or 32 (fp8, TK=128)
+  for (int nb = 0; nb < N / 16; ++nb)
+    for (int kb = 0; kb < tiles_k; ++kb) {
+      T* tile = reinterpret_cast<T*>(dst + ((size_t)nb * tiles_k + kb) * 1024 * (TK == 32 ? 1 : 2));
+      for (int lane = 0; lane < 64; ++lane)
+        for (int i = 0; i < per_lane; ++i) {
+          const int n = nb * 16 + (lane & 15);
+          const int k = kb * TK + per_lane * (lane >> 4) + i;
+          tile[lane * per_lane + i] = get(n, k);
+        }
+    }
+}
+
+}  // namespace
+
+using namespace moeffn;
+
+extern "C" moe_status moe_pack_expert(int32_t d, int32_t F, int32_t w_dtype, const void* wg, const void* wu,
+                                      const void* wd, const float* sg, const float* su, const float* sd,
+                                      void* bundle_host) {
+  clear_error();
+  const size_t bytes = moe_bundle_bytes(d, F, w_dtype);
+  MOE_REQUIRE(bytes > 0, MOE_EINVAL, "moe_pack_expert: unsupported sizes d=%d F=%d for w_dtype %d", d, F, w_dtype);
+  MOE_REQUIRE(wg && wu && wd && bundle_host, MOE_EINVAL, "moe_pack_expert: NULL argument");
+  char* out = static_cast<char*>(bundle_host);
+  std::memset(out, 0, bytes);
+  if (w_dtype == MOE_F32) {
+    float* g = reinterpret_cast<float*>(out);
+    float* u = g + (size_t)F * d;
+    float* dn = reinterpret_cast<float*>(out + al256((size_t)2 * F * d * 4));
+    for (int i = 0; i < d; ++i)
+      for (int f = 0; f < F; ++f) {
+        g[(size_t)f * d + i] = at<float>(wg, (size_t)i * F + f);
+        u[(size_t)f * d + i] = at<float>(wu, (size_t)i * F + f);
+      }
+    for (int f = 0; f < F; ++f)
+      for (int c = 0; c < d; ++c) dn[(size_t)c * F + f] = at<float>(wd, (size_t)f * d + c);
+    return MOE_OK;
+  }
+  if (w_dtype == MOE_BF16) {
+    store_tiled<uint16_t, 32>(out, 2 * F, d, [&](int n, int k) {
+      bool up; int col; gu_row(n, &up, &col);
+      return at<uint16_t>(up ? wu : wg, (size_t)k * F + col);
+    });
+    char* dn = out + al256((size_t)2 * F * d * 2);
+    store_tiled<uint16_t, 32>(dn, d, F, [&](int n, int k) { return at<uint16_t>(wd, (size_t)k * d + n); });
+    return MOE_OK;
+  }
+  // fp8 e4m3 codes with 128x128 block scales
+  MOE_REQUIRE(sg && su && sd, MOE_EINVAL, "moe_pack_expert: fp8 needs the three scale grids");
+  store_tiled<uint8_t, 128>(out, 2 * F, d, [&](int n, int k) {
+    bool up; int col; gu_row(n, &up, &col);
+    return at<uint8_t>(up ? wu : wg, (size_t)k * F + col);
+  });
+  const size_t dn_off = al256((size_t)2 * F * d);
+  store_tiled<uint8_t, 128>(out + dn_off, d, F, [&](int n, int k) { return at<uint8_t>(wd, (size_t)k * d + n); });
+  const int db = d / 128, fb = F / 128;
+  float* s_g = reinterpret_cast<float*>(out + dn_off + al256((size_t)d * F));
+  float* s_u = reinterpret_cast<float*>(reinterpret_cast<char*>(s_g) + al256((size_t)fb * db * 4));
+  float* s_d = reinterpret_cast<float*>(reinterpret_cast<char*>(s_u) + al256((size_t)fb * db * 4));
+  for (int fi = 0; fi < fb; ++fi)
+    for (int di = 0; di < db; ++di) {
+      s_g[fi * db + di] = sg[di * fb + fi];   // input grids are [in/128][out/128]
+      s_u[fi * db + di] = su[di * fb + fi];
+      s_d[di * fb + fi] = sd[fi * db + di];
+    }
+  return MOE_OK;
+}

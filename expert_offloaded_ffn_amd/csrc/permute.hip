@@ -1,0 +1,242 @@
+// moe_permute: stable expert-major grouping of the (token, slot) pairs, and the
+// optional row gather / per-row e4m3 quantisation of the expert inputs.
+//
+// The grouping lets each selected expert run once over all of its rows ("NovaLLM:
+// Running Massive MoE Models Fully In-Memory", section 3: only the experts that
+// were hit run). The order inside an expert is by ascending token, which makes
+// the permutation unique and the whole path deterministic.
+//
+// Three passes of a counting sort, each a single wavefront per 64-token block:
+//  block_counts  for every expert e, a 64-lane ballot of "this token picked e";
+//                popcount = the block's count for e.
+//  scan          one thread per expert walks the blocks in order (exclusive
+//                scan over blocks), then a block-wide exclusive scan over
+//                experts gives offsets; base[b][e] = offsets[e] + sum_{b'<b}.
+//  scatter       the same ballots; a pair's row is base[b][e] plus the number
+//                of lower lanes (= earlier tokens) in the ballot.
+#include "moe_internal.h"
+
+namespace moeffn {
+namespace {
+
+constexpr int kMaxE = 1024;
+
+__global__ __launch_bounds__(64) void permute_block_counts(const int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+                                                           int T, int k, int E) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int t = b * 64 + lane;
+  int mine[32];
+  const int kk = k;
+  for (int j = 0; j < kk; ++j) mine[j] = t < T ? idx[(size_t)t * k + j] : -1;
+  for (int e = 0; e < E; ++e) {
+    bool has = false;
+    for (int j = 0; j < kk; ++j) has |= (mine[j] == e);
+    const uint64_t m = __ballot(has);
+    if (lane == 0) cnt[(size_t)b * E + e] = __popcll(m);
+  }
+}
+
+// One block of up to 1024 threads; thread e owns expert e.
+__global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__ cnt, int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ offsets, int nb, int E) {
+  __shared__ int32_t tot[kMaxE];
+  const int e = threadIdx.x;
+  int running = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int c = cnt[(size_t)b * E + e];
+      base[(size_t)b * E + e] = running;
+      running += c;
+    }
+    tot[e] = running;
+  }
+  __syncthreads();
+  if (e == 0) {
+    int acc = 0;
+    for (int i = 0; i < E; ++i) {
+      const int c = tot[i];
+      tot[i] = acc;
+      acc += c;
+    }
+    offsets[E] = acc;
+  }
+  __syncthreads();
+  if (e < E) {
+    const int off = tot[e];
+    offsets[e] = off;
+    for (int b = 0; b < nb; ++b) base[(size_t)b * E + e] += off;
+  }
+}
+
+__global__ __launch_bounds__(64) void permute_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+                                                      const int32_t* __restrict__ base, int32_t* __restrict__ perm_src,
+                                                      int32_t* __restrict__ perm_dst, int T, int k, int E) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int t = b * 64 + lane;
+  int mine[32];
+  for (int j = 0; j < k; ++j) mine[j] = t < T ? idx[(size_t)t * k + j] : -1;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int e = 0; e < E; ++e) {
+    if (cnt[(size_t)b * E + e] == 0) continue;  // uniform across the wave
+    int jj = -1;
+    for (int j = 0; j < k; ++j) jj = (mine[j] == e) ? j : jj;
+    const uint64_t m = __ballot(jj >= 0);
+    if (jj >= 0) {
+      const int r = base[(size_t)b * E + e] + __popcll(m & below);
+      const int p = t * k + jj;
+      perm_src[r] = p;
+      perm_dst[p] = r;
+    }
+  }
+}
+
+// ------------------------------------------------------------- gather ---
+// One wavefront per output row, 16 bytes per lane per step.
+__global__ __launch_bounds__(256) void gather_rows_copy(const uint8_t* __restrict__ x, uint8_t* __restrict__ out,
+                                                        const int32_t* __restrict__ perm_src, int rows, int k,
+                                                        int row_bytes) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int src = perm_src ? perm_src[r] / k : r;
+  const uint4* s = reinterpret_cast<const uint4*>(x + (size_t)src * row_bytes);
+  uint4* o = reinterpret_cast<uint4*>(out + (size_t)r * row_bytes);
+  for (int i = lane; i < row_bytes / 16; i += 64) o[i] = s[i];
+}
+
+// fp32 -> OCP e4m3 code, round to nearest even; |v| <= 448 (callers clamp).
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  u &= 0x7FFFFFFFu;
+  const float a = __uint_as_float(u);
+  uint32_t code;
+  if (a < 0.015625f) {                  // below the smallest normal 2^-6: quantum 2^-9
+    code = static_cast<uint32_t>(rintf(a * 512.0f));   // exact scaling, RNE; 8 == 2^-6
+  } else {
+    const uint32_t exp = (u >> 23) - 127u + 7u;        // 1..15
+    const uint32_t mant = u & 0x7FFFFFu;
+    const uint32_t r = mant + 0x7FFFFu + ((mant >> 20) & 1u);
+    code = (exp << 3) + (r >> 20);                     // a mantissa carry bumps the exponent
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return sign | code;
+}
+
+// One wavefront per row; 16 lanes x 8 values cover a 128-column block.
+template <typename TIn>
+__global__ __launch_bounds__(256) void gather_rows_quant_e4m3(const TIn* __restrict__ x, uint8_t* __restrict__ out,
+                                                              float* __restrict__ out_scale,
+                                                              const int32_t* __restrict__ perm_src, int rows, int k,
+                                                              int d) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int src = perm_src ? perm_src[r] / k : r;
+  const TIn* xs = x + (size_t)src * d;
+  for (int c0 = 0; c0 < d; c0 += 512) {   // 4 blocks of 128 per step
+    const int col = c0 + lane * 8;
+    float v[8];
+    if (col < d) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (sizeof(TIn) == 2) v[i] = bf16_to_f32(xs[col + i]);
+        else v[i] = xs[col + i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+    if (col < d) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q = fminf(fmaxf(v[i] / scale, -448.0f), 448.0f);
+        lo |= f32_to_e4m3_rne(q) << (8 * i);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q = fminf(fmaxf(v[4 + i] / scale, -448.0f), 448.0f);
+        hi |= f32_to_e4m3_rne(q) << (8 * i);
+      }
+      *reinterpret_cast<uint2*>(out + (size_t)r * d + col) = make_uint2(lo, hi);
+      if ((lane & 15) == 0) out_scale[(size_t)r * (d / 128) + col / 128] = scale;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace moeffn
+
+using namespace moeffn;
+
+extern "C" size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E) {
+  (void)k;
+  if (T < 0 || E < 1) return 0;
+  const size_t nb = (size_t)(T + 63) / 64;
+  return align_up(nb * E * sizeof(int32_t), 256) * 2;
+}
+
+extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_idx, int32_t* offsets,
+                                  int32_t* perm_src, int32_t* perm_dst, int32_t d, const void* x, int32_t x_dtype,
+                                  void* x_out, int32_t out_dtype, float* x_out_scale, int32_t gather, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  clear_error();
+  MOE_REQUIRE(T >= 0, MOE_EINVAL, "moe_permute: T=%d < 0", T);
+  MOE_REQUIRE(E >= 1 && E <= kMaxE, MOE_EINVAL, "moe_permute: E=%d outside [1, %d]", E, kMaxE);
+  MOE_REQUIRE(k >= 1 && k <= E && k <= 32, MOE_EINVAL, "moe_permute: k=%d outside [1, min(E, 32)]", k);
+  MOE_REQUIRE((long long)T * k < (1ll << 31), MOE_EINVAL, "moe_permute: T*k overflows int32");
+  MOE_REQUIRE(offsets != nullptr, MOE_EINVAL, "moe_permute: offsets is NULL");
+  const size_t need = moe_permute_workspace_size(T, k, E);
+  MOE_REQUIRE(ws_bytes >= need, MOE_ECAPACITY, "moe_permute: workspace %zu < %zu bytes", ws_bytes, need);
+  if (x_out != nullptr) {
+    MOE_REQUIRE(x != nullptr && d > 0, MOE_EINVAL, "moe_permute: x_out needs x and d > 0");
+    MOE_REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_permute: x_dtype %d unsupported", x_dtype);
+    MOE_REQUIRE(out_dtype == x_dtype || out_dtype == MOE_FP8_E4M3, MOE_EUNSUPPORTED,
+                "moe_permute: conversion %d -> %d unsupported", x_dtype, out_dtype);
+    MOE_REQUIRE(aligned(x, 16) && aligned(x_out, 16), MOE_EINVAL, "moe_permute: x and x_out must be 16-byte aligned");
+    const int esz = x_dtype == MOE_F32 ? 4 : 2;
+    MOE_REQUIRE((d * esz) % 16 == 0, MOE_EINVAL, "moe_permute: row bytes must be a multiple of 16");
+    if (out_dtype == MOE_FP8_E4M3) {
+      MOE_REQUIRE(d % 128 == 0 && x_out_scale != nullptr, MOE_EINVAL,
+                  "moe_permute: e4m3 output needs d %% 128 == 0 and x_out_scale");
+    }
+  }
+  hipStream_t s = as_stream(stream);
+  if (T == 0) {
+    // offsets stay well defined for an empty batch
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, (const int32_t*)nullptr,
+                       (int32_t*)nullptr, offsets, 0, E);
+    return check_launch("moe_permute scan");
+  }
+  MOE_REQUIRE(topk_idx && perm_src && perm_dst && ws, MOE_EINVAL, "moe_permute: NULL argument");
+  const int nb = (T + 63) / 64;
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
+  hipLaunchKernelGGL(permute_block_counts, dim3(nb), dim3(64), 0, s, topk_idx, cnt, T, k, E);
+  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, cnt, base, offsets, nb, E);
+  hipLaunchKernelGGL(permute_scatter, dim3(nb), dim3(64), 0, s, topk_idx, cnt, base, perm_src, perm_dst, T, k, E);
+  if (moe_status st = check_launch("moe_permute sort")) return st;
+  if (x_out == nullptr) return MOE_OK;
+  const int rows = gather ? T * k : T;
+  const int32_t* src = gather ? perm_src : nullptr;
+  dim3 grid((rows + 3) / 4);
+  if (out_dtype == x_dtype) {
+    const int esz = x_dtype == MOE_F32 ? 4 : 2;
+    hipLaunchKernelGGL(gather_rows_copy, grid, dim3(256), 0, s, static_cast<const uint8_t*>(x),
+                       static_cast<uint8_t*>(x_out), src, rows, k, d * esz);
+  } else if (x_dtype == MOE_BF16) {
+    hipLaunchKernelGGL(gather_rows_quant_e4m3<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                       static_cast<uint8_t*>(x_out), x_out_scale, src, rows, k, d);
+  } else {
+    hipLaunchKernelGGL(gather_rows_quant_e4m3<float>, grid, dim3(256), 0, s, static_cast<const float*>(x),
+                       static_cast<uint8_t*>(x_out), x_out_scale, src, rows, k, d);
+  }
+  return check_launch("moe_permute gather");
+}

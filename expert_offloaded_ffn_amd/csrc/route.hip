@@ -1,0 +1,355 @@
+// moe_route: router logits, selection keys, group-limited top-k, gates and the
+// expert histogram.
+//
+// The pages leave the router arithmetic open ("The Billion-Token Bottleneck",
+// section "The Geometry of the Problem": a router decides which few experts
+// handle each token). This file implements the reading stated in moe.h.
+//
+// Kernels:
+//  route_logits_mfma  bf16 logits on MFMA 16x16x32: a wave owns 16 tokens x all
+//                     expert columns of its block; operands are read straight
+//                     from global (L2-resident router weights) in the MFMA
+//                     fragment layout.
+//  route_logits_f32   fp32 logits, one thread per (token, expert) dot product.
+//  route_select       one wavefront per token: keys, group limit, k rounds of a
+//                     64-lane arg-max over packed (key, ~index) words, gates, and
+//                     a per-block LDS histogram flushed with one atomic per bin.
+#include "moe_internal.h"
+
+namespace moeffn {
+namespace {
+
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxGroups = 64;
+
+// -------------------------------------------------------------- logits ---
+// Block: 256 threads = 4 waves; block tile = 64 tokens x 64 expert columns.
+// Column c < E reads w_router row c; c == E (when has_shared) reads w_sg.
+// Output: raw logits into scores[t, c] for c < E, and into shared_logit[t].
+__global__ __launch_bounds__(256) void route_logits_mfma(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_router,
+    const bf16_t* __restrict__ w_sg, float* __restrict__ scores, float* __restrict__ shared_logit,
+    int32_t* __restrict__ counts, int T, int d, int E) {
+  if (counts != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
+  }
+  const int ncols = E + (w_sg != nullptr ? 1 : 0);
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 64 + wave * 16;
+  const int c0 = blockIdx.y * 64;
+  if (t0 >= T) return;
+  const int ntile = min(4, (ncols - c0 + 15) / 16);
+
+  const int trow = min(t0 + (lane & 15), T - 1);
+  const int koff = 8 * (lane >> 4);
+  const bf16_t* arow = x + (size_t)trow * d + koff;
+  const bf16_t* brow[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    int c = min(c0 + n * 16 + (lane & 15), ncols - 1);
+    brow[n] = (c < E ? w_router + (size_t)c * d : w_sg) + koff;
+  }
+  f32x4_t acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k = 0; k < d; k += 32) {
+    bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + k);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      if (n < ntile) {
+        bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(brow[n] + k);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
+      }
+    }
+  }
+  // D layout: lane l holds rows 4*(l/16)+i, column l%16.
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    if (n >= ntile) continue;
+    const int c = c0 + n * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * (lane >> 4) + i;
+      if (t < T && c < ncols) {
+        if (c < E) scores[(size_t)t * E + c] = acc[n][i];
+        else shared_logit[t] = acc[n][i];
+      }
+    }
+  }
+}
+
+template <typename T_>
+__device__ __forceinline__ float load_as_f32(const T_* p, size_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, size_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float load_as_f32<bf16_t>(const bf16_t* p, size_t i) { return bf16_to_f32(p[i]); }
+
+template <typename T_>
+__global__ __launch_bounds__(256) void route_logits_valu(
+    const T_* __restrict__ x, const T_* __restrict__ w_router, const T_* __restrict__ w_sg,
+    float* __restrict__ scores, float* __restrict__ shared_logit, int32_t* __restrict__ counts,
+    int T, int d, int E) {
+  if (counts != nullptr && blockIdx.x == 0) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
+  }
+  const int ncols = E + (w_sg != nullptr ? 1 : 0);
+  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (long long)T * ncols) return;
+  const int t = (int)(gid / ncols), c = (int)(gid % ncols);
+  const T_* wrow = c < E ? w_router + (size_t)c * d : w_sg;
+  float s = 0.f;
+  for (int i = 0; i < d; ++i) s = fmaf(load_as_f32(x, (size_t)t * d + i), load_as_f32(wrow, (size_t)i), s);
+  if (c < E) scores[(size_t)t * E + c] = s;
+  else shared_logit[t] = s;
+}
+
+// -------------------------------------------------------------- select ---
+// Orderable encoding: larger (key, then lower index) -> larger word; 0 = none.
+__device__ __forceinline__ uint64_t pack_key(float key, int idx) {
+  if (key == 0.0f) key = 0.0f;  // -0 and +0 tie
+  uint32_t u = __float_as_uint(key);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(idx));
+}
+__device__ __forceinline__ int unpack_idx(uint64_t w) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(w & 0xFFFFFFFFu));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint64_t o = __shfl_xor(v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+constexpr int kSelWaves = 4;     // waves per block
+constexpr int kTokPerWave = 16;  // tokens each wave handles in turn
+
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void route_select(
+    float* __restrict__ scores, const float* __restrict__ logit_bias, const float* __restrict__ select_bias,
+    float* __restrict__ shared_gate, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    int32_t* __restrict__ counts, int T, int E, int k, int score_fn, int renormalize, float route_scale,
+    int n_groups, int topk_groups, int group_topn) {
+  __shared__ int hist[kMaxE];
+  __shared__ float wkeys[kSelWaves][kMaxE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (counts != nullptr)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+
+  const int gsz = n_groups > 0 ? E / n_groups : E;
+  for (int it = 0; it < kTokPerWave; ++it) {
+    const int t = (blockIdx.x * kSelWaves + wave) * kTokPerWave + it;
+    if (t >= T) break;
+    float logit[PER_LANE], key[PER_LANE];
+    bool live[PER_LANE];
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      const int e = lane + 64 * i;
+      live[i] = e < E;
+      float l = 0.f;
+      if (live[i]) {
+        l = scores[(size_t)t * E + e];
+        if (logit_bias) l += logit_bias[e];
+      }
+      logit[i] = l;
+      float kv = l;
+      if (score_fn == MOE_SIGMOID) {
+        const float s = 1.0f / (1.0f + expf(-l));
+        logit[i] = s;  // for sigmoid routing keep s for the gates
+        kv = s;
+        if (select_bias && live[i]) kv = s + select_bias[e];
+      }
+      key[i] = kv;
+      if (live[i]) scores[(size_t)t * E + e] = kv;
+    }
+
+    // group limit: lanes g < n_groups score their group from the keys in LDS
+    if (n_groups > 1 && topk_groups < n_groups) {
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i)
+        if (live[i]) wkeys[wave][lane + 64 * i] = key[i];
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      uint64_t gword = 0;
+      if (lane < n_groups) {
+        // the group's group_topn largest keys, summed largest first in fp32
+        float top[8];
+        const int nt = min(group_topn, 8);
+        for (int i = 0; i < nt; ++i) top[i] = -INFINITY;
+        for (int m = 0; m < gsz; ++m) {
+          float v = wkeys[wave][lane * gsz + m];
+          for (int i = 0; i < nt; ++i) {
+            if (v > top[i]) { float tmp = top[i]; top[i] = v; v = tmp; }
+          }
+        }
+        float sum = top[0];
+        for (int i = 1; i < nt; ++i) sum = sum + top[i];
+        gword = pack_key(sum, lane);
+      }
+      uint64_t keep_mask = 0;
+      for (int r = 0; r < topk_groups; ++r) {
+        const uint64_t best = wave_max_u64(gword);
+        const int g = unpack_idx(best);
+        keep_mask |= 1ull << g;
+        if (lane == g) gword = 0;
+      }
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) {
+        const int e = lane + 64 * i;
+        if (live[i] && !((keep_mask >> (e / gsz)) & 1ull)) live[i] = false;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // top-k: k rounds of a wave-wide arg-max
+    int sel_idx = 0;
+    float sel_val = 0.f;  // logit (softmax) or s (sigmoid) of the lane-th winner
+    for (int r = 0; r < k; ++r) {
+      uint64_t mine = 0;
+      int mine_i = -1;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) {
+        if (live[i]) {
+          const uint64_t w = pack_key(key[i], lane + 64 * i);
+          if (w > mine) { mine = w; mine_i = i; }
+        }
+      }
+      const uint64_t best = wave_max_u64(mine);
+      const int e = unpack_idx(best);
+      float v = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) {
+        if (lane + 64 * i == e) { live[i] = false; v = logit[i]; }
+      }
+      // broadcast the winner's value from its owner lane
+      const int owner = e & 63;
+      v = __shfl(v, owner, 64);
+      if (lane == r) { sel_idx = e; sel_val = v; }
+      (void)mine_i;
+    }
+
+    // gates (lanes r < k hold winner r)
+    float g = 0.f;
+    if (score_fn == MOE_SOFTMAX) {
+      const float m = __shfl(sel_val, 0, 64);  // the best key is the largest selected logit
+      if (renormalize) {
+        const float z = lane < k ? expf(sel_val - m) : 0.f;
+        const float denom = wave_sum_f32(z);
+        g = z / denom;
+      } else {
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i)
+          if (lane + 64 * i < E) part += expf(logit[i] - m);
+        const float denom = wave_sum_f32(part);
+        g = lane < k ? expf(sel_val - m) / denom : 0.f;
+      }
+    } else {
+      const float s = lane < k ? sel_val : 0.f;
+      if (renormalize) g = s / wave_sum_f32(s);
+      else g = s;
+    }
+    g *= route_scale;
+    if (lane < k) {
+      topk_idx[(size_t)t * k + lane] = sel_idx;
+      topk_gate[(size_t)t * k + lane] = g;
+      if (counts) atomicAdd(&hist[sel_idx], 1);
+    }
+    if (shared_gate && lane == 0) {
+      const float l = shared_gate[t];
+      shared_gate[t] = 1.0f / (1.0f + expf(-l));
+    }
+  }
+  if (counts != nullptr) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  }
+}
+
+template <int PL>
+void launch_select(dim3 grid, hipStream_t s, float* scores, const float* lb, const float* sb, float* sg,
+                   int32_t* idx, float* gate, int32_t* counts, const moe_route_cfg& c) {
+  hipLaunchKernelGGL(route_select<PL>, grid, dim3(256), 0, s, scores, lb, sb, sg, idx, gate, counts, c.T,
+                     c.n_experts, c.top_k, c.score_fn, c.renormalize, c.route_scale, c.n_groups,
+                     c.topk_groups, c.group_topn);
+}
+
+}  // namespace
+}  // namespace moeffn
+
+using namespace moeffn;
+
+extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const void* w_router,
+                                const float* logit_bias, const float* select_bias,
+                                const void* w_shared_gate, float* shared_gate, float* scores,
+                                int32_t* topk_idx, float* topk_gate, int32_t* counts, void* stream) {
+  clear_error();
+  MOE_REQUIRE(cfg != nullptr, MOE_EINVAL, "moe_route: cfg is NULL");
+  const moe_route_cfg c = *cfg;
+  MOE_REQUIRE(c.T >= 0, MOE_EINVAL, "moe_route: T=%d < 0", c.T);
+  MOE_REQUIRE(c.d_model >= 1 && c.d_model % 8 == 0, MOE_EINVAL, "moe_route: d_model=%d must be a positive multiple of 8", c.d_model);
+  MOE_REQUIRE(c.n_experts >= 1 && c.n_experts <= kMaxE, MOE_EINVAL, "moe_route: n_experts=%d outside [1, %d]", c.n_experts, kMaxE);
+  MOE_REQUIRE(c.top_k >= 1 && c.top_k <= c.n_experts && c.top_k <= kMaxK, MOE_EINVAL,
+              "moe_route: top_k=%d outside [1, min(E, %d)]", c.top_k, kMaxK);
+  MOE_REQUIRE(c.score_fn == MOE_SOFTMAX || c.score_fn == MOE_SIGMOID, MOE_EINVAL, "moe_route: bad score_fn %d", c.score_fn);
+  MOE_REQUIRE(c.act_dtype == MOE_F32 || c.act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_route: act_dtype %d unsupported", c.act_dtype);
+  MOE_REQUIRE(!(select_bias && c.score_fn == MOE_SOFTMAX), MOE_EINVAL, "moe_route: select_bias needs sigmoid scoring");
+  const int G = c.n_groups < 1 ? 1 : c.n_groups;
+  if (G > 1) {
+    MOE_REQUIRE(G <= kMaxGroups && c.n_experts % G == 0, MOE_EINVAL, "moe_route: n_groups=%d must divide E=%d (max %d)", G, c.n_experts, kMaxGroups);
+    MOE_REQUIRE(c.topk_groups >= 1 && c.topk_groups <= G, MOE_EINVAL, "moe_route: topk_groups=%d outside [1, n_groups]", c.topk_groups);
+    MOE_REQUIRE(c.group_topn >= 1 && c.group_topn <= c.n_experts / G && c.group_topn <= 8, MOE_EINVAL,
+                "moe_route: group_topn=%d outside [1, min(E/n_groups, 8)]", c.group_topn);
+    MOE_REQUIRE(c.top_k <= c.topk_groups * (c.n_experts / G), MOE_EINVAL, "moe_route: top_k exceeds the experts of the kept groups");
+  }
+  MOE_REQUIRE((w_shared_gate == nullptr) == (shared_gate == nullptr), MOE_EINVAL,
+              "moe_route: w_shared_gate and shared_gate go together");
+  if (c.T == 0) return MOE_OK;
+  MOE_REQUIRE(x && w_router && scores && topk_idx && topk_gate, MOE_EINVAL, "moe_route: NULL tensor argument");
+  MOE_REQUIRE(aligned(x, 16) && aligned(w_router, 16) && (!w_shared_gate || aligned(w_shared_gate, 16)), MOE_EINVAL,
+              "moe_route: x, w_router, w_shared_gate must be 16-byte aligned");
+
+  moe_route_cfg cc = c;
+  cc.n_groups = G;
+  hipStream_t s = as_stream(stream);
+  const int ncols = c.n_experts + (w_shared_gate ? 1 : 0);
+  if (c.act_dtype == MOE_BF16 && c.d_model % 32 == 0) {
+    dim3 grid((c.T + 63) / 64, (ncols + 63) / 64);
+    hipLaunchKernelGGL(route_logits_mfma, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                       static_cast<const bf16_t*>(w_router), static_cast<const bf16_t*>(w_shared_gate), scores,
+                       shared_gate, counts, c.T, c.d_model, c.n_experts);
+  } else {
+    const long long n = (long long)c.T * ncols;
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (c.act_dtype == MOE_BF16)
+      hipLaunchKernelGGL(route_logits_valu<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                         static_cast<const bf16_t*>(w_router), static_cast<const bf16_t*>(w_shared_gate), scores,
+                         shared_gate, counts, c.T, c.d_model, c.n_experts);
+    else
+      hipLaunchKernelGGL(route_logits_valu<float>, grid, dim3(256), 0, s, static_cast<const float*>(x),
+                         static_cast<const float*>(w_router), static_cast<const float*>(w_shared_gate), scores,
+                         shared_gate, counts, c.T, c.d_model, c.n_experts);
+  }
+  if (moe_status st = check_launch("moe_route logits")) return st;
+  dim3 sgrid((c.T + kSelWaves * kTokPerWave - 1) / (kSelWaves * kTokPerWave));
+  const int per_lane = (c.n_experts + 63) / 64;
+  if (per_lane <= 1) launch_select<1>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  else if (per_lane <= 2) launch_select<2>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  else if (per_lane <= 4) launch_select<4>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  else launch_select<16>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  return check_launch("moe_route select");
+}

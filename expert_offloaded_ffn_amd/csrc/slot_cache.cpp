@@ -1,0 +1,346 @@
+// expert_slot_cache: expert-granular residency over a fixed HBM slot pool.
+//
+// The pages' design, restated: every expert's weights live in pinned host
+// memory ("NovaLLM: Running Massive MoE Models Fully In-Memory", section 3,
+// Optimization #2); only experts the router selected are brought into VRAM,
+// loaded right before they run, with the loads overlapping compute (same page,
+// Optimization #1); the cache intercepts the router's expert list, checks
+// residency, evicts least-recently-used bundles and, when a batch needs more
+// experts than fit, blocks, transfers, then executes in waves ("Running 35B MoE
+// Models on 8GB GPUs", section "Technical Insight"); transfers are asynchronous
+// host-to-HBM copies issued only for non-resident experts ("The Billion-Token
+// Bottleneck", section "Predictive Prefetching").
+//
+// Two halves:
+//  planner   pure host code: per step, the touched set (from the expert
+//            histogram), the access order (resident ascending, then
+//            non-resident ascending), waves of <= n_slots, LRU with the lowest
+//            free slot first. Runs without a device (dry_run) for tests.
+//  executor  a side stream for host->HBM bundle copies; per-slot "last read"
+//            events recorded on the compute stream (a copy into a slot waits for
+//            the last kernel that read it); per-wave "copies done" events that
+//            the compute stream waits on before the wave's miss experts run.
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace moeffn;
+
+struct expert_slot_cache {
+  moe_cache_cfg cfg{};
+  std::vector<const void*> bundles;
+  // planner
+  std::vector<int32_t> slot_of, owner;
+  std::vector<int64_t> last;
+  int64_t clock = 0;
+  std::vector<std::vector<moe_cache_entry>> waves;
+  bool planned = false;
+  moe_cache_stats st{};
+  // executor
+  int device = -1;
+  hipStream_t side = nullptr;
+  std::vector<hipEvent_t> last_read;     // per slot
+  std::vector<char> last_read_valid;
+  std::vector<hipEvent_t> copy_begin, copy_done;  // per wave
+  std::vector<char> wave_copied;         // copies issued for the wave this step
+  std::vector<char> timing_pending;      // copy span events to be added to copy_ms
+  int32_t* counts_pinned = nullptr;
+  int32_t* tables_pinned = nullptr;      // [max_waves][2][E]
+  int max_waves = 0;
+};
+
+namespace {
+
+void plan_reset(expert_slot_cache* c) {
+  const int E = c->cfg.n_experts, S = c->cfg.n_slots;
+  c->slot_of.assign(E, -1);
+  c->owner.assign(S, -1);
+  c->last.assign(E, 0);
+  c->clock = 0;
+  c->waves.clear();
+  c->planned = false;
+  c->st = moe_cache_stats{};
+}
+
+moe_cache_entry access(expert_slot_cache* c, int e) {
+  moe_cache_entry r{e, -1, 0, -1};
+  c->clock += 1;
+  if (c->slot_of[e] >= 0) {
+    c->last[e] = c->clock;
+    c->st.hits += 1;
+    r.slot = c->slot_of[e];
+    r.hit = 1;
+    return r;
+  }
+  c->st.misses += 1;
+  int slot = -1;
+  for (int s = 0; s < c->cfg.n_slots; ++s)
+    if (c->owner[s] < 0) { slot = s; break; }
+  if (slot < 0) {
+    int victim = -1;
+    for (int s = 0; s < c->cfg.n_slots; ++s) {
+      const int v = c->owner[s];
+      if (victim < 0 || c->last[v] < c->last[victim]) victim = v;
+    }
+    slot = c->slot_of[victim];
+    c->slot_of[victim] = -1;
+    c->st.evictions += 1;
+    r.evicted = victim;
+  }
+  c->owner[slot] = e;
+  c->slot_of[e] = slot;
+  c->last[e] = c->clock;
+  r.slot = slot;
+  return r;
+}
+
+void plan_step(expert_slot_cache* c, const int32_t* counts) {
+  const int E = c->cfg.n_experts, S = c->cfg.n_slots;
+  std::vector<int> order;
+  for (int e = 0; e < E; ++e)
+    if (counts[e] > 0 && c->slot_of[e] >= 0) order.push_back(e);
+  for (int e = 0; e < E; ++e)
+    if (counts[e] > 0 && c->slot_of[e] < 0) order.push_back(e);
+  c->waves.clear();
+  for (size_t w0 = 0; w0 < order.size(); w0 += S) {
+    std::vector<moe_cache_entry> wave;
+    for (size_t i = w0; i < std::min(order.size(), w0 + S); ++i) wave.push_back(access(c, order[i]));
+    c->waves.push_back(std::move(wave));
+  }
+  c->st.waves += (int64_t)c->waves.size();
+  c->st.steps += 1;
+  c->planned = true;
+}
+
+// Adds finished copy spans to the stats (events of earlier steps).
+void collect_timing(expert_slot_cache* c, bool wait) {
+  for (int w = 0; w < c->max_waves; ++w) {
+    if (!c->timing_pending[w]) continue;
+    if (wait) (void)hipEventSynchronize(c->copy_done[w]);
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->copy_begin[w], c->copy_done[w]) == hipSuccess) {
+      c->st.copy_ms += ms;
+      c->timing_pending[w] = 0;
+    }
+  }
+}
+
+void destroy_device(expert_slot_cache* c) {
+  if (c->cfg.dry_run) return;
+  for (auto& e : c->last_read) if (e) (void)hipEventDestroy(e);
+  for (auto& e : c->copy_begin) if (e) (void)hipEventDestroy(e);
+  for (auto& e : c->copy_done) if (e) (void)hipEventDestroy(e);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->counts_pinned) (void)hipHostFree(c->counts_pinned);
+  if (c->tables_pinned) (void)hipHostFree(c->tables_pinned);
+}
+
+}  // namespace
+
+extern "C" moe_status expert_slot_cache_create(const moe_cache_cfg* cfg, expert_slot_cache** out) {
+  clear_error();
+  MOE_REQUIRE(cfg && out, MOE_EINVAL, "expert_slot_cache_create: NULL argument");
+  *out = nullptr;
+  const moe_cache_cfg k = *cfg;
+  MOE_REQUIRE(k.n_experts >= 1 && k.n_experts <= 1024, MOE_EINVAL, "expert_slot_cache_create: n_experts=%d outside [1, 1024]", k.n_experts);
+  MOE_REQUIRE(k.n_slots >= 1, MOE_ECAPACITY, "expert_slot_cache_create: n_slots=%d < 1 (the pool must hold one expert)", k.n_slots);
+  MOE_REQUIRE(k.bundle_bytes > 0, MOE_EINVAL, "expert_slot_cache_create: bundle_bytes must be > 0");
+  MOE_REQUIRE(k.slot_stride >= k.bundle_bytes && k.slot_stride % 256 == 0, MOE_ECAPACITY,
+              "expert_slot_cache_create: slot_stride %lld must be >= bundle_bytes %lld and a multiple of 256",
+              (long long)k.slot_stride, (long long)k.bundle_bytes);
+  if (!k.dry_run) {
+    MOE_REQUIRE(k.bundles_host && k.pool, MOE_EINVAL, "expert_slot_cache_create: bundles_host and pool are required");
+    MOE_REQUIRE(aligned(k.pool, 256), MOE_EINVAL, "expert_slot_cache_create: pool must be 256-byte aligned");
+    for (int e = 0; e < k.n_experts; ++e) {
+      MOE_REQUIRE(k.bundles_host[e] != nullptr, MOE_EINVAL, "expert_slot_cache_create: bundle %d is NULL", e);
+      hipPointerAttribute_t attr;
+      std::memset(&attr, 0, sizeof(attr));
+      const hipError_t err = hipPointerGetAttributes(&attr, k.bundles_host[e]);
+      if (err != hipSuccess) (void)hipGetLastError();
+      MOE_REQUIRE(err == hipSuccess && attr.type == hipMemoryTypeHost, MOE_EINVAL,
+                  "expert_slot_cache_create: bundle %d is not in pinned host memory", e);
+    }
+  }
+  expert_slot_cache* c = new (std::nothrow) expert_slot_cache();
+  MOE_REQUIRE(c != nullptr, MOE_ENOMEM, "expert_slot_cache_create: out of host memory");
+  c->cfg = k;
+  if (!k.dry_run) c->bundles.assign(k.bundles_host, k.bundles_host + k.n_experts);
+  plan_reset(c);
+  c->max_waves = (k.n_experts + k.n_slots - 1) / k.n_slots;
+  if (!k.dry_run) {
+    auto fail = [&](const char* what, hipError_t e) {
+      set_error("expert_slot_cache_create: %s: %s", what, hipGetErrorString(e));
+      destroy_device(c);
+      delete c;
+      return MOE_EHIP;
+    };
+    hipError_t e;
+    if ((e = hipGetDevice(&c->device)) != hipSuccess) return fail("hipGetDevice", e);
+    if ((e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess) return fail("hipStreamCreate", e);
+    c->last_read.assign(k.n_slots, nullptr);
+    c->last_read_valid.assign(k.n_slots, 0);
+    for (auto& ev : c->last_read)
+      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+    c->copy_begin.assign(c->max_waves, nullptr);
+    c->copy_done.assign(c->max_waves, nullptr);
+    c->wave_copied.assign(c->max_waves, 0);
+    c->timing_pending.assign(c->max_waves, 0);
+    for (int w = 0; w < c->max_waves; ++w) {
+      if ((e = hipEventCreate(&c->copy_begin[w])) != hipSuccess) return fail("hipEventCreate", e);
+      if ((e = hipEventCreate(&c->copy_done[w])) != hipSuccess) return fail("hipEventCreate", e);
+    }
+    if ((e = hipHostMalloc((void**)&c->counts_pinned, sizeof(int32_t) * k.n_experts, hipHostMallocDefault)) != hipSuccess)
+      return fail("hipHostMalloc", e);
+    if ((e = hipHostMalloc((void**)&c->tables_pinned, sizeof(int32_t) * k.n_experts * 2 * c->max_waves,
+                           hipHostMallocDefault)) != hipSuccess)
+      return fail("hipHostMalloc", e);
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_destroy(expert_slot_cache* c) {
+  clear_error();
+  if (!c) return MOE_OK;
+  if (!c->cfg.dry_run && c->side) (void)hipStreamSynchronize(c->side);
+  destroy_device(c);
+  delete c;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_reset(expert_slot_cache* c) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_reset: NULL cache");
+  if (!c->cfg.dry_run) {
+    MOE_HIP(hipStreamSynchronize(c->side));
+    std::fill(c->last_read_valid.begin(), c->last_read_valid.end(), 0);
+    std::fill(c->timing_pending.begin(), c->timing_pending.end(), 0);
+  }
+  plan_reset(c);
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_plan_host(expert_slot_cache* c, const int32_t* counts_host, int32_t* n_waves_out) {
+  clear_error();
+  MOE_REQUIRE(c && counts_host, MOE_EINVAL, "expert_slot_cache_plan_host: NULL argument");
+  plan_step(c, counts_host);
+  if (n_waves_out) *n_waves_out = (int32_t)c->waves.size();
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_acquire(expert_slot_cache* c, const int32_t* counts, void* stream,
+                                                int32_t* n_waves_out) {
+  clear_error();
+  MOE_REQUIRE(c && counts, MOE_EINVAL, "expert_slot_cache_acquire: NULL argument");
+  MOE_REQUIRE(!c->cfg.dry_run, MOE_ESTATE, "expert_slot_cache_acquire: cache was created as a dry run");
+  hipStream_t s = as_stream(stream);
+  const int E = c->cfg.n_experts;
+  MOE_HIP(hipMemcpyAsync(c->counts_pinned, counts, sizeof(int32_t) * E, hipMemcpyDeviceToHost, s));
+  MOE_HIP(hipStreamSynchronize(s));  // the router's expert list reaches the host here
+  c->st.d2h_bytes += (int64_t)sizeof(int32_t) * E;
+  collect_timing(c, false);
+  std::fill(c->wave_copied.begin(), c->wave_copied.end(), 0);
+  plan_step(c, c->counts_pinned);
+  if (n_waves_out) *n_waves_out = (int32_t)c->waves.size();
+  return MOE_OK;
+}
+
+namespace {
+
+moe_status issue_copies(expert_slot_cache* c, int w) {
+  if (c->wave_copied[w]) return MOE_OK;
+  c->wave_copied[w] = 1;
+  bool any = false;
+  for (const auto& en : c->waves[w]) {
+    if (en.hit) continue;
+    if (!any) {
+      MOE_HIP(hipEventRecord(c->copy_begin[w], c->side));
+      any = true;
+    }
+    if (c->last_read_valid[en.slot]) MOE_HIP(hipStreamWaitEvent(c->side, c->last_read[en.slot], 0));
+    char* dst = static_cast<char*>(c->cfg.pool) + (int64_t)en.slot * c->cfg.slot_stride;
+    const hipError_t err = hipMemcpyAsync(dst, c->bundles[en.expert], (size_t)c->cfg.bundle_bytes,
+                                          hipMemcpyHostToDevice, c->side);
+    if (err != hipSuccess) {
+      // the slot holds no valid bundle: drop it from the plan's residency
+      c->slot_of[en.expert] = -1;
+      c->owner[en.slot] = -1;
+      set_error("expert_slot_cache: copy of expert %d into slot %d failed: %s", en.expert, en.slot,
+                hipGetErrorString(err));
+      return MOE_EHIP;
+    }
+    c->st.h2d_bytes += c->cfg.bundle_bytes;
+  }
+  MOE_HIP(hipEventRecord(c->copy_done[w], c->side));
+  if (any) c->timing_pending[w] = 1;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status expert_slot_cache_wave(expert_slot_cache* c, int32_t wave, int32_t part, void* stream,
+                                             int32_t* slot_of_expert, int32_t* n_in_part) {
+  clear_error();
+  MOE_REQUIRE(c && slot_of_expert, MOE_EINVAL, "expert_slot_cache_wave: NULL argument");
+  MOE_REQUIRE(!c->cfg.dry_run, MOE_ESTATE, "expert_slot_cache_wave: cache was created as a dry run");
+  MOE_REQUIRE(c->planned, MOE_ESTATE, "expert_slot_cache_wave: call expert_slot_cache_acquire first");
+  MOE_REQUIRE(wave >= 0 && wave < (int)c->waves.size(), MOE_EINVAL, "expert_slot_cache_wave: wave %d out of range", wave);
+  MOE_REQUIRE(part == 0 || part == 1, MOE_EINVAL, "expert_slot_cache_wave: part must be 0 or 1");
+  hipStream_t s = as_stream(stream);
+  const int E = c->cfg.n_experts;
+  if (moe_status st = issue_copies(c, wave)) return st;
+  int32_t* table = c->tables_pinned + ((size_t)wave * 2 + part) * E;
+  std::fill(table, table + E, -1);
+  int n = 0;
+  const bool blocking = c->cfg.blocking != 0;
+  if (blocking ? part == 0 : part == 1) MOE_HIP(hipStreamWaitEvent(s, c->copy_done[wave], 0));
+  for (const auto& en : c->waves[wave]) {
+    const bool take = blocking ? (part == 0) : (part == 0 ? en.hit != 0 : en.hit == 0);
+    if (take) {
+      table[en.expert] = en.slot;
+      ++n;
+    }
+  }
+  MOE_HIP(hipMemcpyAsync(slot_of_expert, table, sizeof(int32_t) * E, hipMemcpyHostToDevice, s));
+  if (n_in_part) *n_in_part = n;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_release(expert_slot_cache* c, int32_t wave, void* stream) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_release: NULL cache");
+  MOE_REQUIRE(!c->cfg.dry_run, MOE_ESTATE, "expert_slot_cache_release: cache was created as a dry run");
+  MOE_REQUIRE(c->planned && wave >= 0 && wave < (int)c->waves.size(), MOE_ESTATE,
+              "expert_slot_cache_release: wave %d was not planned", wave);
+  hipStream_t s = as_stream(stream);
+  for (const auto& en : c->waves[wave]) {
+    MOE_HIP(hipEventRecord(c->last_read[en.slot], s));
+    c->last_read_valid[en.slot] = 1;
+  }
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_wave_plan(const expert_slot_cache* c, int32_t wave, moe_cache_entry* entries,
+                                                  int32_t capacity, int32_t* n_entries) {
+  clear_error();
+  MOE_REQUIRE(c && n_entries, MOE_EINVAL, "expert_slot_cache_wave_plan: NULL argument");
+  MOE_REQUIRE(c->planned && wave >= 0 && wave < (int)c->waves.size(), MOE_ESTATE,
+              "expert_slot_cache_wave_plan: wave %d was not planned", wave);
+  const auto& w = c->waves[wave];
+  *n_entries = (int32_t)w.size();
+  MOE_REQUIRE(entries == nullptr || capacity >= (int32_t)w.size(), MOE_ECAPACITY,
+              "expert_slot_cache_wave_plan: capacity %d < %zu", capacity, w.size());
+  if (entries) std::copy(w.begin(), w.end(), entries);
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_stats(const expert_slot_cache* c, moe_cache_stats* out) {
+  clear_error();
+  MOE_REQUIRE(c && out, MOE_EINVAL, "expert_slot_cache_stats: NULL argument");
+  if (!c->cfg.dry_run) collect_timing(const_cast<expert_slot_cache*>(c), true);
+  *out = c->st;
+  return MOE_OK;
+}

@@ -1,0 +1,139 @@
+"""One MoE FFN layer on the device: buffers plus the sequence of library calls.
+
+Holds the packed expert bundles (a resident pool with an identity slot table, or
+an expert slot pool fed from pinned host bundles), the router weights and the
+workspaces, and runs route -> permute -> grouped FFN (routed, then shared) ->
+combine as calls into libmoeffn. No arithmetic of the layer happens here.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+W_CODE = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_FP8_E4M3}
+
+
+def _bits_to_tensor(a: np.ndarray, act: str, device) -> torch.Tensor:
+    """Storage-format numpy array -> device tensor (bf16 bits reinterpreted, no rounding)."""
+    if act == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    return t.to(device)
+
+
+def pack_bundles(cfg, expert_weights, d, F, pin=False, threads=8):
+    """Packs experts (synth storage tuples) into host bundles; returns a list of uint8 tensors."""
+    w = W_CODE[cfg.dtype]
+    nb = B.bundle_bytes(d, F, w)
+
+    def one(ws):
+        out = torch.empty(nb, dtype=torch.uint8, pin_memory=pin)
+        if cfg.dtype == "fp8":
+            (gq, gs), (uq, us), (dq, ds) = ws
+            return B.pack_expert(d, F, w, gq, uq, dq, gs, us, ds, out=out)
+        return B.pack_expert(d, F, w, ws[0], ws[1], ws[2], out=out)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return list(ex.map(one, expert_weights))
+
+
+class ResidentPool:
+    """All bundles resident in one device tensor [n, stride] with the identity slot table."""
+
+    def __init__(self, bundles, d, F, w_dtype, device):
+        self.n = len(bundles)
+        nb = bundles[0].numel()
+        self.stride = (nb + 255) // 256 * 256
+        self.pool = torch.empty(self.n, self.stride, dtype=torch.uint8, device=device)
+        for i, b in enumerate(bundles):
+            self.pool[i, :nb].copy_(b, non_blocking=False)
+        self.slots = torch.arange(self.n, dtype=torch.int32, device=device)
+        self.table = B.expert_table(self.pool, self.stride, self.slots, self.n, d, F, w_dtype)
+
+
+class MoELayer:
+    def __init__(self, cfg, *, router, experts, shared=None, w_shared_gate=None, select_bias=None, device="cuda",
+                 pool_slots=None, blocking=False, threads=8):
+        """router: W_r [d, E] storage; experts: list of synth expert tuples; shared: synth tuple or None.
+        pool_slots: None = every expert resident; an int = expert slot pool of that many slots."""
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.act = cfg.act_dtype
+        self.act_code = W_CODE[self.act]
+        self.w_code = W_CODE[cfg.dtype]
+        self.E, self.d, self.F, self.k = cfg.E, cfg.d, cfg.F, cfg.k
+        self.w_router_t = _bits_to_tensor(np.ascontiguousarray(np.asarray(router).T), self.act, self.device)
+        self.w_sg = None if w_shared_gate is None else _bits_to_tensor(w_shared_gate, self.act, self.device)
+        self.select_bias = None if select_bias is None else torch.from_numpy(select_bias).to(self.device)
+        bundles = pack_bundles(cfg, experts, self.d, self.F, pin=pool_slots is not None, threads=threads)
+        self.bundle_bytes = bundles[0].numel()
+        self.cache = None
+        if pool_slots is None:
+            self.pool = ResidentPool(bundles, self.d, self.F, self.w_code, self.device)
+            self.table = self.pool.table
+        else:
+            self.host_bundles = bundles
+            stride = (self.bundle_bytes + 255) // 256 * 256
+            self.slot_pool = torch.empty(pool_slots, stride, dtype=torch.uint8, device=self.device)
+            self.slot_table = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
+            self.cache = B.SlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles, self.slot_pool,
+                                     blocking=blocking)
+            self.table = B.expert_table(self.slot_pool, stride, self.slot_table, self.E, self.d, self.F, self.w_code)
+        self.shared = None
+        if shared is not None:
+            Fs = cfg.F_shared
+            sb = pack_bundles(cfg, [shared], self.d, Fs, threads=1)
+            self.shared = ResidentPool(sb, self.d, Fs, self.w_code, self.device)
+        self._ws = {}
+
+    def _buf(self, name, numel, dtype=torch.uint8):
+        t = self._ws.get(name)
+        if t is None or t.numel() < numel or t.dtype != dtype:
+            t = torch.empty(max(numel, 64), dtype=dtype, device=self.device)
+            self._ws[name] = t
+        return t[:max(numel, 1)] if numel else t[:1]
+
+    def route_args(self):
+        c = self.cfg
+        return dict(k=c.k, score_fn=B.MOE_SIGMOID if c.score_fn == "sigmoid" else B.MOE_SOFTMAX,
+                    renormalize=c.renormalize, route_scale=c.route_scale, n_groups=c.n_groups,
+                    topk_groups=c.topk_groups, group_topn=c.group_topn)
+
+    def forward(self, x: torch.Tensor, logit_bias: torch.Tensor | None = None, stream=None) -> dict:
+        """x [T, d] device tensor in the activation dtype. Returns the layer output and routing tensors."""
+        T = x.shape[0]
+        k, E, d = self.k, self.E, self.d
+        r = B.route(x, self.w_router_t, logit_bias=logit_bias, select_bias=self.select_bias,
+                    w_shared_gate=self.w_sg, stream=stream, **self.route_args())
+        ws = self._buf("perm_ws", B.permute_workspace_size(T, k, E))
+        p = B.permute(r["idx"], E, ws=ws, stream=stream)
+        rows = T * k
+        ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
+        y = torch.empty(rows, d, device=self.device, dtype=torch.float32 if ydt == B.MOE_F32 else torch.bfloat16)
+        fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, self.act_code))
+        if self.cache is None:
+            B.grouped_ffn(self.table, rows, p["offsets"], x, a_row_src=p["perm_src"], a_row_div=k, y=y,
+                          y_dtype=ydt, ws=fws, stream=stream)
+            waves = 0
+        else:
+            waves = self.cache.acquire(r["counts"], stream=stream)
+            for w in range(waves):
+                for part in (0, 1):
+                    n = self.cache.wave(w, part, self.slot_table, stream=stream)
+                    if n:
+                        B.grouped_ffn(self.table, rows, p["offsets"], x, a_row_src=p["perm_src"], a_row_div=k, y=y,
+                                      y_dtype=ydt, ws=fws, stream=stream)
+                self.cache.release(w, stream=stream)
+        shared_y = None
+        if self.shared is not None:
+            offs = self._buf("shared_offsets", 2, torch.int32)
+            offs.copy_(torch.tensor([0, T], dtype=torch.int32))
+            shared_y = torch.empty(T, d, device=self.device, dtype=y.dtype)
+            sws = self._buf("shared_ws", B.grouped_ffn_workspace_size(self.shared.table, T, self.act_code))
+            B.grouped_ffn(self.shared.table, T, offs, x, y=shared_y, y_dtype=ydt, ws=sws, stream=stream)
+        out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"], stream=stream)
+        return {"out": out, "route": r, "perm": p, "y": y, "shared_y": shared_y, "waves": waves}

@@ -100,8 +100,8 @@ CONFIGS = {
 }
 
 
-def get_config(name: str, **overrides) -> LayerConfig:
-    return replace(CONFIGS[name], **overrides)
+def get_config(config_name: str, **overrides) -> LayerConfig:
+    return replace(CONFIGS[config_name], **overrides)
 
 
 def _rng(*key: int) -> np.random.Generator:

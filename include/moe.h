@@ -1,0 +1,337 @@
+/*
+ * moe.h -- C ABI of libmoeffn: the forward pass of one Mixture-of-Experts FFN
+ * layer on an AMD Instinct MI355X (gfx950), plus an expert slot pool that keeps
+ * only the experts the router selects in HBM and streams the rest from pinned
+ * host memory.
+ *
+ * Sources (the pages this library follows):
+ *  [NOVA]  "NovaLLM: Running Massive MoE Models Fully In-Memory", sections 2-3:
+ *          a router picks a handful of experts per token and only those run;
+ *          each expert is stored on its own and loaded just before it runs;
+ *          all weights stay resident in pinned host memory; loads overlap compute.
+ *  [BTB]   "The Billion-Token Bottleneck", sections "The Geometry of the Problem"
+ *          (experts are feed-forward networks chosen by a router), "Tiered
+ *          Memory" (HBM hot tier, host DDR warm tier over PCIe) and "Predictive
+ *          Prefetching" (asynchronous host-to-HBM copies guarded by a residency
+ *          check, then compute on resident weights).
+ *  [VVLLM] "Running 35B MoE Models on 8GB GPUs: How vvllm-ms Caches Experts in
+ *          System RAM", section "Technical Insight": a paged expert cache that
+ *          intercepts the router's expert list, keeps whole expert bundles
+ *          (weights and quantisation scales as one unit) in VRAM under LRU
+ *          eviction, and when a batch needs more experts than fit, blocks,
+ *          transfers, then executes in deterministic waves.
+ * The router arithmetic, the SwiGLU expert and the number formats are not fixed
+ * by the pages; each call below states the reading it implements.
+ *
+ * Conventions (all calls):
+ *  - Every call returns a moe_status; 0 is success. On failure the call has
+ *    enqueued nothing, and moe_last_error() returns a thread-local message.
+ *    Nothing aborts, throws or prints.
+ *  - Pointers are device pointers (HBM) unless the name ends in _host.
+ *    Tensors are row-major, contiguous and caller-owned; the library never
+ *    frees or retains a caller pointer beyond the call, except the slot pool
+ *    and host bundles registered with expert_slot_cache_create.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls are
+ *    asynchronous on it, except expert_slot_cache_acquire, which waits for the
+ *    expert histogram (the one host synchronisation per decode step).
+ *  - Device errors of earlier asynchronous work surface as MOE_EHIP at a later
+ *    call.
+ *  - Scratch memory is caller-provided; sizes come from the *_workspace_size
+ *    queries. The library allocates device memory in no compute call.
+ */
+#ifndef MOEFFN_MOE_H
+#define MOEFFN_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* bad argument: null pointer, bad size, misalignment */
+  MOE_EUNSUPPORTED = -2,  /* valid but not implemented (dtype/shape combination) */
+  MOE_EHIP = -3,          /* a HIP runtime call failed */
+  MOE_ECAPACITY = -4,     /* workspace or pool too small */
+  MOE_ENOMEM = -5,        /* host allocation failed */
+  MOE_ESTATE = -6         /* call out of order (e.g. wave before acquire) */
+};
+
+/* Element types. MOE_FP8_E4M3 is the OCP 8-bit E4M3 ("fn": bias 7, max 448,
+ * no infinities), always paired with fp32 scales as described per call. */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
+
+/* Human-readable message for the last failing call on this thread ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+/* ------------------------------------------------------------------ route --
+ * Router scores, top-k gating and the expert histogram ([BTB] "The Geometry
+ * of the Problem": a router decides which experts handle each token; [NOVA]
+ * section 3: only the selected experts are touched).
+ *
+ * Reading implemented (the pages leave the router math open):
+ *  logits  l[t,e] = sum_i x[t,i] * w_router[e,i] (+ logit_bias[e]), fp32
+ *          accumulation of the stored (fp32 or bf16) values;
+ *  keys    softmax: key = l;  sigmoid: s = 1/(1+exp(-l)), key = s (+ select_bias[e]);
+ *  groups  if n_groups > 1: group g = experts [g*E/G, (g+1)*E/G); group score =
+ *          fp32 sum, largest first, of the group's group_topn largest keys; the
+ *          topk_groups best groups are kept (ties -> lower group index);
+ *  top-k   the k best kept experts by (key desc, expert index asc), best first;
+ *  gates   softmax: exp(l_j - l_max_sel) / sum over the selection (renormalize=1)
+ *          or the full softmax probability (renormalize=0); sigmoid: s_j / sum of
+ *          selected s (renormalize=1) or s_j; both then times route_scale;
+ *  shared  if w_shared_gate != NULL: shared_gate[t] = sigmoid(x[t] . w_shared_gate).
+ *
+ * Arguments:
+ *  x            [T, d] act_dtype (MOE_F32 or MOE_BF16)
+ *  w_router     [E, d] act_dtype: row e holds expert e's router weights
+ *  logit_bias   [E] fp32 or NULL: added to every token's logits (a prior)
+ *  select_bias  [E] fp32 or NULL: sigmoid only; steers selection, not gates
+ *  w_shared_gate[d] act_dtype or NULL;  shared_gate [T] fp32 out (with it)
+ *  scores       [T, E] fp32 out: the exact keys top-k selected on
+ *  topk_idx     [T, k] int32 out;  topk_gate [T, k] fp32 out
+ *  counts       [E] int32 out or NULL: counts[e] = #(t, j) with topk_idx = e
+ * Errors: MOE_EINVAL for T < 0, d < 1, E < 1, k outside [1, E], d % 8 != 0,
+ *  n_groups not dividing E, topk_groups > n_groups, group_topn outside
+ *  [1, E/n_groups], k > topk_groups*E/n_groups, E > 1024, null required pointers,
+ *  select_bias with softmax. T = 0 is a no-op.
+ */
+typedef struct {
+  int32_t T, d_model, n_experts, top_k;
+  int32_t score_fn;      /* MOE_SOFTMAX | MOE_SIGMOID */
+  int32_t renormalize;   /* 1: gates renormalised over the selected experts */
+  float route_scale;     /* multiplies every gate (1.0 unless stated) */
+  int32_t n_groups;      /* 1 = no group limit */
+  int32_t topk_groups;
+  int32_t group_topn;
+  int32_t act_dtype;     /* MOE_F32 | MOE_BF16 */
+} moe_route_cfg;
+
+moe_status moe_route(const moe_route_cfg* cfg, const void* x, const void* w_router,
+                     const float* logit_bias, const float* select_bias,
+                     const void* w_shared_gate, float* shared_gate, float* scores,
+                     int32_t* topk_idx, float* topk_gate, int32_t* counts, void* stream);
+
+/* ---------------------------------------------------------------- permute --
+ * Grouping of the (token, slot) pairs by expert, the step that lets each
+ * selected expert run once over all of its tokens ([NOVA] section 3: per-expert
+ * execution of only the experts that were hit; [VVLLM] "Technical Insight": the
+ * router's expert list is intercepted before expert compute).
+ *
+ * Reading implemented: a stable counting sort of p = t*k + j by expert id:
+ *  offsets[e]  = number of pairs routed to experts < e (offsets[E] = T*k);
+ *  perm_src[r] = p for the r-th row, rows expert-major, tokens ascending;
+ *  perm_dst[p] = r (the inverse).
+ * Optional row materialisation when x_out != NULL:
+ *  gather = 1: x_out[r] = cvt(x[perm_src[r] / k]) for r < T*k;
+ *  gather = 0: x_out[t] = cvt(x[t]) for t < T (token order, e.g. quantise once);
+ *  cvt is a copy when out_dtype == x_dtype, or the per-row per-128-column e4m3
+ *  quantisation when out_dtype == MOE_FP8_E4M3: a = max|v| over the 128-block,
+ *  scale = a / 448 (1 if a == 0) in IEEE fp32, code = e4m3_rne(clamp(v/scale,
+ *  +-448)); x_out_scale [rows, d/128] fp32 receives the scales.
+ * Workspace: moe_permute_workspace_size(T, k, E) bytes at `ws` (256-B aligned).
+ * Errors: MOE_EINVAL on bad sizes/null pointers, MOE_ECAPACITY if ws_bytes is
+ *  short, MOE_EUNSUPPORTED for an unsupported conversion. Indices outside
+ *  [0, E) in topk_idx are not checked on the device (they come from moe_route).
+ */
+size_t moe_permute_workspace_size(int32_t T, int32_t k, int32_t E);
+moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_idx,
+                       int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
+                       int32_t d, const void* x, int32_t x_dtype, void* x_out,
+                       int32_t out_dtype, float* x_out_scale, int32_t gather,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------ expert table --
+ * Where each expert's bundle lives. A bundle is one contiguous block holding an
+ * expert's three matrices and, for fp8, their scales: the atomic unit of
+ * residency ([VVLLM] "Technical Insight": weights and quantisation scales move
+ * together). slot_of_expert maps expert e to bundle slot s at
+ * pool + s * slot_stride, or -1 to skip the expert in this call.
+ *
+ * Bundle layout (moe_pack_expert writes it; offsets are multiples of 256 B):
+ *  MOE_BF16: W_gu then W_dn, each in 1 KiB MFMA tiles: for an [N, K] matrix the
+ *   tile (nb, kb) covers rows 16nb..16nb+15 and columns 32kb..32kb+31, stored at
+ *   ((nb * K/32) + kb) * 1024 bytes; inside, lane l (0..63) holds 8 consecutive
+ *   elements: row 16nb + l%16, columns 32kb + 8*(l/16) + 0..7.
+ *   W_gu is [2F, d] (N = 2F, K = d): rows 32j..32j+15 are W_gate columns
+ *   16j..16j+15 and rows 32j+16..32j+31 are W_up columns 16j..16j+15 (the
+ *   gate and up halves of every 16 hidden units are adjacent).
+ *   W_dn is [d, F] (N = d, K = F): row n is W_down column n.
+ *  MOE_FP8_E4M3: same row orders, 2 KiB tiles of 16 rows x 128 columns, lane l
+ *   holding 32 consecutive codes of row 16nb + l%16 at columns 128kb + 32*(l/16);
+ *   then three fp32 scale grids: gate [F/128][d/128], up [F/128][d/128],
+ *   down [d/128][F/128] (one scale per 128x128 block of the original matrix).
+ *  MOE_F32: W_gate^T [F, d], W_up^T [F, d], W_down^T [d, F], plain row-major.
+ * Requirements: d % 32 == 0 and F % 32 == 0 (bf16); d % 128 == 0 and
+ *  F % 128 == 0 (fp8); d % 4 == 0 (f32).
+ */
+typedef struct {
+  const void* pool;               /* device base address of slot 0 */
+  int64_t slot_stride;            /* bytes between slots, >= bundle bytes, % 256 == 0 */
+  const int32_t* slot_of_expert;  /* device [n_experts]: slot or -1 (skip) */
+  int32_t n_experts, d_model, d_ff;
+  int32_t w_dtype;                /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 */
+} moe_expert_table;
+
+/* Bytes of one expert bundle for this layout (0 on invalid sizes). */
+size_t moe_bundle_bytes(int32_t d_model, int32_t d_ff, int32_t w_dtype);
+
+/* Host-side packer: writes one bundle from the expert's matrices in their
+ * natural layouts, W_gate and W_up [d, F], W_down [F, d] (element type w_dtype;
+ * fp8 codes as uint8), plus for fp8 the block scales gate/up [d/128][F/128] and
+ * down [F/128][d/128] (fp32). bundle_host must hold moe_bundle_bytes(...) bytes.
+ * Pure host code; no device is touched. */
+moe_status moe_pack_expert(int32_t d_model, int32_t d_ff, int32_t w_dtype,
+                           const void* w_gate_host, const void* w_up_host,
+                           const void* w_down_host, const float* s_gate_host,
+                           const float* s_up_host, const float* s_down_host,
+                           void* bundle_host);
+
+/* ------------------------------------------------------------- grouped FFN --
+ * The selected experts' SwiGLU feed-forward networks, each run once over the
+ * rows grouped to it ([BTB] "The Geometry of the Problem": experts are
+ * feed-forward networks; [NOVA] section 3: only the experts that were hit run).
+ *
+ * Reading implemented: for every expert e with slot_of_expert[e] >= 0 and rows
+ * r in [offsets[e], offsets[e+1]):
+ *   A_r = a[a_row_src ? a_row_src[r] / a_row_div : r]          (row of `a`)
+ *   H_r = silu(A_r W_gate_e) * (A_r W_up_e)    (fp32 accumulation; rounded to
+ *         bf16 for bf16 weights, re-quantised per row per 128 to e4m3 for fp8)
+ *   y_r = H_r W_down_e                          (fp32 accumulation, y_dtype)
+ * Rows of skipped experts are left untouched in y.
+ *  a        [*, d] act_dtype: MOE_F32 (f32 weights), MOE_BF16 (bf16 weights) or
+ *           MOE_FP8_E4M3 codes (fp8 weights) with a_scale [*, d/128] fp32
+ *  offsets  device [n_experts + 1] int32 (from moe_permute, or [0, rows] for a
+ *           single dense expert such as a shared expert)
+ *  y        [rows, d] y_dtype (MOE_F32 or MOE_BF16)
+ * Workspace: moe_grouped_ffn_workspace_size(table, rows, act_dtype) bytes.
+ * Errors: MOE_EINVAL on bad sizes/pointers/alignment (16 B for a, y, pool),
+ *  MOE_EUNSUPPORTED for dtype combinations not listed, MOE_ECAPACITY for a
+ *  short workspace. Slot values are not range-checked on the device; the slot
+ *  pool owner (e.g. expert_slot_cache) is responsible for them.
+ */
+size_t moe_grouped_ffn_workspace_size(const moe_expert_table* table, int32_t rows,
+                                      int32_t act_dtype);
+moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t rows, const int32_t* offsets,
+                           const void* a, const float* a_scale, int32_t act_dtype,
+                           const int32_t* a_row_src, int32_t a_row_div,
+                           void* y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- combine --
+ * Gate-weighted sum of each token's expert outputs back in token order, plus
+ * the always-resident shared expert ([VVLLM] "Gotcha": shared experts sit
+ * outside the routed set; here they never enter the slot pool).
+ *  out[t] = sum_{j<k} topk_gate[t,j] * y[perm_dst[t*k+j]]
+ *           + (shared_y ? (shared_gate ? shared_gate[t] : 1) * shared_y[t] : 0)
+ * accumulated in fp32 in that order (j ascending, shared last), rounded once to
+ * out_dtype. y and shared_y are [*, d] in y_dtype (MOE_F32 or MOE_BF16).
+ * Errors: MOE_EINVAL on bad sizes/pointers. T = 0 is a no-op.
+ */
+moe_status moe_combine(int32_t T, int32_t k, int32_t d, const void* y, int32_t y_dtype,
+                       const int32_t* perm_dst, const float* topk_gate,
+                       const void* shared_y, const float* shared_gate,
+                       void* out, int32_t out_dtype, void* stream);
+
+/* ------------------------------------------------------- expert slot cache --
+ * Expert-granular residency: a fixed pool of n_slots bundle slots in HBM backed
+ * by every expert's bundle in pinned host memory ([NOVA] section 3,
+ * Optimization #2: weights resident in pinned memory; [BTB] "Tiered Memory" and
+ * "Predictive Prefetching": HBM hot tier, host warm tier, asynchronous copies
+ * guarded by a residency check; [VVLLM] "Technical Insight": LRU eviction of
+ * whole bundles, blocking transfer waves when a batch needs more experts than
+ * fit).
+ *
+ * Reading implemented, per decode step:
+ *  1. acquire: copy counts[E] to the host and wait (the interception of the
+ *     router's expert list); touched = experts with counts > 0; access order =
+ *     resident touched experts (ascending id), then non-resident (ascending);
+ *     cut into waves of <= n_slots; each access is an LRU access (hit refreshes
+ *     recency; a miss takes the lowest free slot, else evicts the least recently
+ *     used expert; eviction copies nothing back since weights are read-only).
+ *  2. per wave w, part 0 (hits): writes the slot table holding the wave's hits
+ *     only and starts the wave's miss copies (host bundle -> slot) on the cache's
+ *     side stream, each after the last compute read of its victim slot;
+ *     part 1 (misses): makes `stream` wait for those copies and writes the
+ *     table holding the wave's misses only. The caller runs moe_grouped_ffn with
+ *     each table, so hit experts compute while misses are in flight.
+ *     In blocking mode (cfg.blocking = 1) part 0 waits for all the wave's
+ *     copies and holds every expert of the wave, and part 1 is empty: block,
+ *     transfer, then execute.
+ *  3. release(w): records that the wave's slots were read by the work enqueued
+ *     so far on `stream` (a later copy into those slots waits for it).
+ * Device-side state is only the pool (caller memory) and the slot tables it
+ * writes (caller memory). The host tables, one side stream, events and a small
+ * pinned staging area are allocated in create and freed in destroy.
+ * dry_run = 1 creates a host-only planner (no HIP calls; acquire/wave/release
+ * fail with MOE_ESTATE) for expert_slot_cache_plan_host.
+ * Errors: MOE_EINVAL (sizes, null pointers, a bundle not in pinned host memory),
+ *  MOE_ECAPACITY (n_slots < 1, slot_stride < bundle_bytes), MOE_ESTATE (calls
+ *  out of order), MOE_EHIP (a copy or event call failed; the affected slot is
+ *  left non-resident).
+ */
+typedef struct expert_slot_cache expert_slot_cache;
+
+typedef struct {
+  int32_t n_experts;
+  int32_t n_slots;
+  int64_t bundle_bytes;
+  int64_t slot_stride;              /* >= bundle_bytes, multiple of 256 */
+  const void* const* bundles_host;  /* [n_experts] pinned host bundles (NULL if dry_run) */
+  void* pool;                       /* device, n_slots * slot_stride bytes (NULL if dry_run) */
+  int32_t blocking;                 /* 1: wait for all copies, then execute */
+  int32_t dry_run;                  /* 1: host-only planner */
+} moe_cache_cfg;
+
+typedef struct {
+  int64_t steps, hits, misses, evictions, waves;
+  int64_t h2d_bytes, d2h_bytes;
+  double copy_ms;   /* sum over steps of side-stream copy spans (events) */
+} moe_cache_stats;
+
+/* One entry of a wave's plan (host query for tests and tools). */
+typedef struct {
+  int32_t expert, slot, hit, evicted;  /* evicted = expert evicted for it, or -1 */
+} moe_cache_entry;
+
+moe_status expert_slot_cache_create(const moe_cache_cfg* cfg, expert_slot_cache** out);
+moe_status expert_slot_cache_destroy(expert_slot_cache* c);
+moe_status expert_slot_cache_reset(expert_slot_cache* c);
+moe_status expert_slot_cache_acquire(expert_slot_cache* c, const int32_t* counts, void* stream,
+                                     int32_t* n_waves_out);
+moe_status expert_slot_cache_plan_host(expert_slot_cache* c, const int32_t* counts_host,
+                                       int32_t* n_waves_out);
+moe_status expert_slot_cache_wave(expert_slot_cache* c, int32_t wave, int32_t part, void* stream,
+                                  int32_t* slot_of_expert, int32_t* n_experts_in_part);
+moe_status expert_slot_cache_release(expert_slot_cache* c, int32_t wave, void* stream);
+moe_status expert_slot_cache_wave_plan(const expert_slot_cache* c, int32_t wave,
+                                       moe_cache_entry* entries_host, int32_t capacity,
+                                       int32_t* n_entries);
+moe_status expert_slot_cache_stats(const expert_slot_cache* c, moe_cache_stats* out);
+
+/* ---------------------------------------------------------------- profile --
+ * Optional per-kernel timing for measurement tools (not part of the layer's
+ * arithmetic). While enabled, moe_grouped_ffn records a hipEvent pair on its
+ * stream around each of its heavy kernels; moe_profile_read waits for the
+ * recorded pairs and returns the summed milliseconds and launch counts per
+ * kernel kind since the last moe_profile_enable call (which also resets).
+ * Kinds: 0 gate/up GEMM with the SwiGLU epilogue, 1 down GEMM.
+ * Errors: MOE_EINVAL for a NULL out, MOE_EHIP if an event cannot be read.
+ */
+enum { MOE_PROF_GATEUP = 0, MOE_PROF_DOWN = 1, MOE_PROF_KINDS = 4 };
+typedef struct {
+  double ms[MOE_PROF_KINDS];
+  int64_t launches[MOE_PROF_KINDS];
+} moe_profile;
+moe_status moe_profile_enable(int32_t on);
+moe_status moe_profile_read(moe_profile* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOEFFN_MOE_H */

@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI (no device work): every symbol the header declares
+is exported, argument validation fails with the documented codes before touching a
+device, the bundle packer writes the documented layout, and the slot-pool planner
+(dry run) matches the oracle's LRU simulation exactly."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from expert_offloaded_ffn_amd import binding as B
+from oracle.slot_cache import LRUSlotCache
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:moe_status|size_t|char\s*\*|const\s+char\s*\*)\s*\**\s*(\w+)\s*\(",
+                       src, flags=re.M)
+    names += re.findall(r"^\s*const char\*\s+(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    names = _declared_functions()
+    assert names == sorted(B.EXPORTS), names   # the binding covers exactly the header
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/moe.h but not exported"
+    assert b"gfx950" in L.moe_version()
+
+
+def test_route_validation_codes():
+    L = B.lib()
+    cfg = B.RouteCfg(16, 128, 8, 2, 0, 1, 1.0, 1, 1, 0, B.MOE_BF16)
+    null = None
+    assert L.moe_route(None, *([null] * 10), null) == -1
+    bad = B.RouteCfg(16, 128, 8, 9, 0, 1, 1.0, 1, 1, 0, B.MOE_BF16)        # k > E
+    assert L.moe_route(ctypes.byref(bad), *([null] * 10), null) == -1
+    assert b"top_k" in L.moe_last_error()
+    bad = B.RouteCfg(16, 128, 256, 8, 1, 1, 2.5, 7, 4, 2, B.MOE_BF16)      # groups do not divide E
+    assert L.moe_route(ctypes.byref(bad), *([null] * 10), null) == -1
+    bad = B.RouteCfg(16, 128, 256, 8, 1, 1, 2.5, 8, 4, 2, B.MOE_FP8_E4M3)  # fp8 router input
+    assert L.moe_route(ctypes.byref(bad), *([null] * 10), null) == -2
+    ok_empty = B.RouteCfg(0, 128, 8, 2, 0, 1, 1.0, 1, 1, 0, B.MOE_BF16)    # T = 0 is a no-op
+    assert L.moe_route(ctypes.byref(ok_empty), *([null] * 10), null) == 0
+    sb = (ctypes.c_float * 8)()
+    args = [null, null, null, ctypes.cast(sb, ctypes.c_void_p)] + [null] * 6
+    assert L.moe_route(ctypes.byref(cfg), *args, null) == -1               # select_bias with softmax
+
+
+def test_permute_and_combine_validation_codes():
+    L = B.lib()
+    assert L.moe_permute(16, 0, 8, *([None] * 4), 0, None, 0, None, 0, None, 1, None, 0, None) == -1
+    need = L.moe_permute_workspace_size(16, 2, 8)
+    assert need > 0
+    fake = ctypes.c_void_p(0x1000)
+    assert L.moe_permute(16, 2, 8, fake, fake, fake, fake, 0, None, 0, None, 0, None, 1, fake, need - 1, None) == -4
+    assert L.moe_combine(4, 40, 128, None, 1, None, None, None, None, None, 1, None) == -1
+    assert L.moe_combine(0, 2, 128, None, 1, None, None, None, None, None, 1, None) == 0
+
+
+def test_grouped_ffn_validation_codes():
+    L = B.lib()
+    t = B.ExpertTable(None, 0, None, 8, 4096, 14336, B.MOE_BF16)
+    assert L.moe_grouped_ffn(ctypes.byref(t), 16, *([None] * 3), 1, None, 1, None, 1, None, 0, None) == -1
+    nb = B.bundle_bytes(4096, 14336, B.MOE_BF16)
+    assert nb == 3 * 4096 * 14336 * 2
+    assert B.bundle_bytes(7168, 2048, B.MOE_FP8_E4M3) == 3 * 7168 * 2048 + 3 * 16 * 56 * 4
+    assert B.bundle_bytes(4096, 1536, B.MOE_BF16) == 37748736
+    assert B.bundle_bytes(100, 256, B.MOE_BF16) == 0          # d % 32 != 0
+    t = B.ExpertTable(ctypes.c_void_p(256), nb - 256, ctypes.c_void_p(256), 8, 4096, 14336, B.MOE_BF16)
+    assert L.moe_grouped_ffn(ctypes.byref(t), 16, *([None] * 3), 1, None, 1, None, 1, None, 0, None) == -1
+    assert b"slot_stride" in L.moe_last_error()
+
+
+def test_pack_bf16_layout():
+    d, F = 64, 32
+    rng = np.random.default_rng(0)
+    wg = rng.integers(0, 2 ** 16, (d, F), dtype=np.uint16)
+    wu = rng.integers(0, 2 ** 16, (d, F), dtype=np.uint16)
+    wd = rng.integers(0, 2 ** 16, (F, d), dtype=np.uint16)
+    b = B.pack_expert(d, F, B.MOE_BF16, wg, wu, wd).numpy().view(np.uint16)
+    gu = b[:2 * F * d]
+
+    def tiled(buf, n, k, K):   # header: tile (n//16, k//32) at (nb*K/32 + kb)*512 elems; lane = n%16 + 16*((k%32)//8)
+        tile = (n // 16) * (K // 32) + k // 32
+        lane = n % 16 + 16 * ((k % 32) // 8)
+        return buf[tile * 512 + lane * 8 + k % 8]
+
+    for _ in range(200):
+        R, kk = rng.integers(0, 2 * F), rng.integers(0, d)
+        j, rr = R // 32, R % 32
+        want = (wu if rr >= 16 else wg)[kk, 16 * j + rr % 16]
+        assert tiled(gu, R, kk, d) == want
+    dn = b[2 * F * d:]
+    for _ in range(200):
+        n, f = rng.integers(0, d), rng.integers(0, F)
+        assert tiled(dn, n, f, F) == wd[f, n]
+
+
+def test_pack_fp8_layout_and_scales():
+    d, F = 256, 128
+    rng = np.random.default_rng(1)
+    wg, wu = rng.integers(0, 255, (d, F), dtype=np.uint8), rng.integers(0, 255, (d, F), dtype=np.uint8)
+    wd = rng.integers(0, 255, (F, d), dtype=np.uint8)
+    sg, su = rng.random((2, 1), dtype=np.float32), rng.random((2, 1), dtype=np.float32)
+    sd = rng.random((1, 2), dtype=np.float32)
+    b = B.pack_expert(d, F, B.MOE_FP8_E4M3, wg, wu, wd, sg, su, sd).numpy()
+    for _ in range(200):
+        R, kk = rng.integers(0, 2 * F), rng.integers(0, d)
+        tile = (R // 16) * (d // 128) + kk // 128
+        lane = R % 16 + 16 * ((kk % 128) // 32)
+        j, rr = R // 32, R % 32
+        assert b[tile * 2048 + lane * 32 + kk % 32] == (wu if rr >= 16 else wg)[kk, 16 * j + rr % 16]
+    off = 2 * F * d + d * F
+    s = b[off:].view(np.float32)
+    assert s[0] == sg[0, 0] and s[1] == sg[1, 0]                # gate stored [F/128][d/128]
+    assert s[64] == su[0, 0] and s[65] == su[1, 0]              # next grid at +256 B
+    assert s[128] == sd[0, 0] and s[129] == sd[0, 1]            # down stored [d/128][F/128]
+
+
+@pytest.mark.parametrize("E,S,k,T", [(8, 3, 2, 4), (60, 16, 4, 8), (128, 32, 8, 32)])
+def test_planner_matches_oracle_simulation(E, S, k, T):
+    rng = np.random.default_rng(E + S)
+    c = B.SlotCache(E, S, 1 << 20, 1 << 20, dry_run=True)
+    sim = LRUSlotCache(E, S)
+    for step in range(60):
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+        counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+        n = c.plan_host(counts)
+        plan = sim.step(idx.ravel())
+        assert n == len(plan.waves)
+        for w, wave in enumerate(plan.waves):
+            assert c.wave_plan(w) == [(en.expert, en.slot, int(en.hit), en.evicted) for en in wave]
+    st = c.stats()
+    assert (st["hits"], st["misses"], st["evictions"], st["waves"], st["steps"]) == \
+        (sim.stats.hits, sim.stats.misses, sim.stats.evictions, sim.stats.waves, sim.stats.steps)
+    c.reset()
+    assert c.stats()["misses"] == 0
+    c.close()
+
+
+def test_cache_create_validation():
+    with pytest.raises(B.MoeError) as ei:
+        B.SlotCache(8, 0, 1024, 1024, dry_run=True)
+    assert ei.value.status == -4
+    with pytest.raises(B.MoeError) as ei:
+        B.SlotCache(8, 2, 1024, 512, dry_run=True)
+    assert ei.value.status == -4
+    c = B.SlotCache(8, 2, 1024, 1024, dry_run=True)
+    with pytest.raises(B.MoeError) as ei:
+        c.acquire(None)
+    assert ei.value.status in (-1, -6)

@@ -1,0 +1,160 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle on seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+from expert_offloaded_ffn_amd import binding as B
+from expert_offloaded_ffn_amd import synth
+from expert_offloaded_ffn_amd.layer import MoELayer
+from oracle import moe
+from parity_util import (assert_close, check_exact_indices, oracle_expert, oracle_route, route_agreement, say,
+                         to_np, decode)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _build(cfg, *, pool_slots=None, blocking=False):
+    router = synth.gen_router(cfg)
+    experts = synth.gen_experts(cfg)
+    shared = synth.gen_shared(cfg) if cfg.F_shared else None
+    w_sg = synth.gen_shared_gate(cfg) if cfg.shared_gate else None
+    sb = synth.gen_select_bias(cfg) if cfg.select_bias else None
+    layer = MoELayer(cfg, router=router, experts=experts, shared=shared, w_shared_gate=w_sg, select_bias=sb,
+                     device=DEV, pool_slots=pool_slots, blocking=blocking)
+    return layer, dict(router=router, experts=experts, shared=shared, w_sg=w_sg, sb=sb)
+
+
+def _x_dev(cfg, x_store):
+    if cfg.act_dtype == "f32":
+        return torch.from_numpy(x_store).to(DEV)
+    return torch.from_numpy(x_store.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _run_and_check(cfg, layer, w, T, xi=0, tokens=None, logit_bias=None):
+    x_store = synth.gen_x(cfg, xi, T=T)
+    x = _x_dev(cfg, x_store)
+    lb = None if logit_bias is None else torch.from_numpy(logit_bias).to(DEV)
+    say(f"  case {cfg.name} T={T} x={xi}: launching")
+    g = layer.forward(x, logit_bias=lb)
+    torch.cuda.synchronize()
+    say("    done")
+    check_exact_indices(cfg, g["route"], g["perm"], T)
+    r_ref = oracle_route(cfg, x_store, w["router"], w["w_sg"], w["sb"], logit_bias)
+    same = route_agreement(cfg, r_ref, g["route"], key_tol=1e-4)
+    if cfg.shared_gate:
+        err = np.abs(to_np(g["route"]["shared_gate"]) - r_ref.shared_gate).max()
+        assert err <= 1e-4, f"shared gate err {err}"
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    toks = toks[same[toks]]
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache.clear()
+            cache[e] = oracle_expert(cfg, w["experts"][e])
+        return cache[e]
+
+    shared = oracle_expert(cfg, w["shared"]) if w["shared"] is not None else None
+    ref = moe.moe_layer(decode(x_store, cfg.act_dtype), r_ref, expert, cfg.E, shared=shared,
+                        quant_act=cfg.dtype == "fp8", tokens=toks)
+    got = to_np(g["out"])[toks]
+    assert_close(got, ref, cfg.dtype)
+    return g
+
+
+def test_tiny_fp32_layer():
+    cfg = synth.get_config("tiny_fp32")
+    layer, w = _build(cfg)
+    for xi in range(3):
+        _run_and_check(cfg, layer, w, cfg.T, xi)
+
+
+@pytest.mark.parametrize("T,d,E,k,F", [(333, 512, 8, 2, 1024), (97, 256, 60, 4, 384), (1, 256, 16, 4, 128),
+                                       (700, 256, 32, 8, 256)])
+def test_bf16_layer_reduced(T, d, E, k, F):
+    cfg = synth.get_config("mixtral_prefill_bf16", T=T, d=d, E=E, k=k, F=F, name=f"bf16_T{T}_d{d}_E{E}_k{k}_F{F}")
+    layer, w = _build(cfg)
+    _run_and_check(cfg, layer, w, T)
+
+
+def test_mixtral_full_size_sampled():
+    cfg = synth.get_config("mixtral_prefill_bf16")
+    layer, w = _build(cfg)
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(cfg.T, 24, replace=False))
+    toks[-1] = cfg.T - 1
+    _run_and_check(cfg, layer, w, cfg.T, 0, tokens=toks)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_qwen_decode_full_size(T):
+    cfg = synth.get_config("qwen_decode_bf16", T=T)
+    layer, w = _build(cfg)
+    for xi in range(2):
+        _run_and_check(cfg, layer, w, T, xi)
+
+
+def test_determinism_bitwise():
+    cfg = synth.get_config("mixtral_prefill_bf16", T=600, d=512, F=1024, name="det")
+    layer, _ = _build(cfg)
+    x = _x_dev(cfg, synth.gen_x(cfg, 0))
+    a = layer.forward(x)["out"].clone()
+    b = layer.forward(x)["out"].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_skewed_routing_and_empty_experts():
+    """A large logit prior sends every token to experts 3 and 5 (others get no rows)."""
+    cfg = synth.get_config("mixtral_prefill_bf16", T=300, d=256, F=256, name="skew")
+    layer, w = _build(cfg)
+    lb = np.zeros(cfg.E, np.float32)
+    lb[3], lb[5] = 40.0, 30.0
+    g = _run_and_check(cfg, layer, w, cfg.T, 0, logit_bias=lb)
+    counts = to_np(g["route"]["counts"])
+    assert counts[3] == cfg.T and counts[5] == cfg.T and counts.sum() == 2 * cfg.T
+
+
+def test_permute_gather_and_e4m3_quantisation_bit_exact():
+    from oracle import formats
+    cfg = synth.get_config("dsv3_prefill_fp8", T=200, d=512, E=32, k=8, n_groups=8, topk_groups=4)
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(cfg.T)]).astype(np.int32)
+    x_store = synth.gen_x(cfg, 0)
+    x = _x_dev(cfg, x_store)
+    say("  case permute gather/quant: launching")
+    p = B.permute(torch.from_numpy(idx).to(DEV), cfg.E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=1)
+    q = B.permute(torch.from_numpy(idx).to(DEV), cfg.E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=0)
+    c = B.permute(torch.from_numpy(idx).to(DEV), cfg.E, x=x, gather=1)
+    torch.cuda.synchronize()
+    off, src, dst = moe.permutation(idx, cfg.E)
+    assert np.array_equal(to_np(p["perm_src"]), src)
+    xf = decode(x_store, "bf16")
+    codes, scales = formats.quantize_rows_e4m3(xf)
+    assert np.array_equal(to_np(q["x_out"]), codes)
+    assert np.array_equal(to_np(q["x_out_scale"]), scales)
+    assert np.array_equal(to_np(p["x_out"]), codes[src // cfg.k])
+    assert np.array_equal(to_np(p["x_out_scale"]), scales[src // cfg.k])
+    assert np.array_equal(to_np(c["x_out"]), xf[src // cfg.k])
+
+
+def test_dsv3_routing_full_size():
+    """Group-limited sigmoid routing with selection bias at the full DeepSeek-V3 shape (bf16 router)."""
+    cfg = synth.get_config("dsv3_prefill_fp8")
+    router = synth.gen_router(cfg)
+    sb = synth.gen_select_bias(cfg)
+    x_store = synth.gen_x(cfg, 0)
+    x = _x_dev(cfg, x_store)
+    wr = torch.from_numpy(np.ascontiguousarray(router.T).view(np.int16)).view(torch.bfloat16).to(DEV)
+    say("  case dsv3 route full: launching")
+    r = B.route(x, wr, k=cfg.k, score_fn=B.MOE_SIGMOID, route_scale=cfg.route_scale, n_groups=8, topk_groups=4,
+                group_topn=2, select_bias=torch.from_numpy(sb).to(DEV))
+    p = B.permute(r["idx"], cfg.E)
+    torch.cuda.synchronize()
+    check_exact_indices(cfg, r, p, cfg.T)
+    r_ref = oracle_route(cfg, x_store, router, select_bias=sb)
+    same = route_agreement(cfg, r_ref, r, key_tol=1e-5)
+    say(f"    near-tie mismatches: {int((~same).sum())} of {cfg.T}")
+    g = to_np(r["gate"])
+    np.testing.assert_allclose(g.sum(axis=1), 2.5, rtol=1e-5)
