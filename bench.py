@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Benchmark of one MoE FFN layer forward pass on one MI355X.
+
+A step is one pass of the whole layer (route -> permute -> grouped SwiGLU FFN ->
+combine, plus the shared expert where the workload has one) over one batch of
+synthetic tokens already resident in HBM. Default workload: the Mixtral-8x7B-shaped
+prefill layer (T=4096, d=4096, E=8, top-2 softmax, F=14336, bf16).
+
+Prints one JSON line: tokens/s for the whole job, the dominant kernel's roofline
+(algorithmic flops or bytes per launch over its average duration, timed with hipEvents
+on its launch stream inside the timed region), and the float64 CPU oracle timed on a
+bounded sample of the same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--tokens T]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; HBM TB/s (decode) & MFMA TFLOP/s (prefill) vs peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = ["mixtral_prefill_bf16", "qwen_decode_bf16", "tiny_fp32"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _x_dev(cfg, x_store, torch):
+    if cfg.act_dtype == "f32":
+        return torch.from_numpy(x_store).to("cuda")
+    return torch.from_numpy(x_store.view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def cpu_baseline(cfg, w, sample_tokens):
+    """The float64 oracle, as it stands, on the first `sample_tokens` tokens of batch 0."""
+    from oracle import formats, moe  # CPU baseline leg only
+
+    def dec(a):
+        return np.asarray(a, np.float64) if cfg.act_dtype == "f32" else formats.decode_bf16(a)
+
+    threads = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            threads = max(p["num_threads"] for p in info)
+    except Exception:
+        pass
+    from expert_offloaded_ffn_amd import synth
+    x_store = synth.gen_x(cfg, 0)[:sample_tokens]
+    t0 = time.perf_counter()
+    x = dec(x_store)
+    r = moe.route(x, dec(w["router"]), k=cfg.k, score_fn=cfg.score_fn, renormalize=bool(cfg.renormalize),
+                  route_scale=cfg.route_scale, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
+                  group_topn=cfg.group_topn,
+                  w_shared_gate=None if w["w_sg"] is None else dec(w["w_sg"]))
+
+    def expert(e):
+        return moe.ExpertWeights(*[dec(m) for m in w["experts"][e]])
+
+    shared = None if w["shared"] is None else moe.ExpertWeights(*[dec(m) for m in w["shared"]])
+    moe.moe_layer(x, r, expert, cfg.E, shared=shared)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of batch 0 of {cfg.name} (T={cfg.T}), float64, "
+                      f"expert weights decoded per expert; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill_bf16", choices=WORKLOADS)
+    ap.add_argument("--tokens", type=int, default=None, help="override T (decode batch size)")
+    ap.add_argument("--batches", type=int, default=4, help="rotating input batches")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not sharded across GPUs.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from expert_offloaded_ffn_amd import binding as B
+    from expert_offloaded_ffn_amd import synth
+    from expert_offloaded_ffn_amd.layer import MoELayer
+
+    cfg = synth.get_config(args.workload)
+    if args.tokens:
+        cfg = cfg.with_T(args.tokens)
+    log(f"[bench] workload {cfg.name} T={cfg.T}: generating inputs")
+    w = dict(router=synth.gen_router(cfg), experts=synth.gen_experts(cfg, threads=16),
+             shared=synth.gen_shared(cfg) if cfg.F_shared else None,
+             w_sg=synth.gen_shared_gate(cfg) if cfg.shared_gate else None)
+    layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
+                     threads=16)
+    xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(args.batches)]
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        layer.forward(xs[i % len(xs)])
+    torch.cuda.synchronize()
+    # rows per expert of each batch (real rows only; used for the algorithmic work)
+    rows_e = []
+    for x in xs:
+        rows_e.append(B.route(x, layer.w_router_t, **layer.route_args())["counts"].cpu().numpy())
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    B.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        layer.forward(xs[i % len(xs)])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = B.profile_read()
+    B.profile_enable(False)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tokens_per_s = cfg.T * args.steps / (ms_total / 1e3)
+
+    d, F, E, T, k = cfg.d, cfg.F, cfg.E, cfg.T, cfg.k
+    rows = np.array([rows_e[i % len(xs)].sum() for i in range(args.steps)], dtype=np.float64)
+    gateup_flops = 4.0 * rows * d * F                        # per launch, real rows only
+    down_flops = 2.0 * rows * F * d
+    router_flops = 2.0 * T * d * E
+    shared_flops = 6.0 * T * d * cfg.F_shared
+    layer_flops = float((gateup_flops + down_flops).mean() + router_flops + shared_flops)
+    gu_ms, gu_n = prof[B.PROF_GATEUP]
+    dn_ms, dn_n = prof[B.PROF_DOWN]
+    dtype = cfg.dtype
+    peak = PEAK_TFLOPS[dtype]
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
+        "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
+                   "d_ff_shared": cfg.F_shared, "score_fn": cfg.score_fn, "all_experts_resident": True},
+    }
+    if gu_n:
+        gu_avg_s = gu_ms / gu_n / 1e3
+        achieved = float(gateup_flops.mean()) / gu_avg_s / 1e12
+        result["roofline"] = {"bound": "mfma", "kernel": "ffn_gemm_bf16<gate/up+SwiGLU>",
+                              "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                              "frac": round(achieved / peak, 4), "traffic": None,
+                              "avg_launch_ms": round(gu_ms / gu_n, 4),
+                              "work_per_launch": f"4*rows*d*F flops, rows = T*k = {int(rows.mean())}"}
+        if dn_n:
+            dn_avg_s = dn_ms / dn_n / 1e3
+            result["down_gemm"] = {"avg_launch_ms": round(dn_ms / dn_n, 4),
+                                   "achieved_tflops": round(float(down_flops.mean()) / dn_avg_s / 1e12, 1)}
+    result["layer_tflops"] = round(layer_flops / (ms_step / 1e3) / 1e12, 1)
+    result["layer_frac_of_peak"] = round(layer_flops / (ms_step / 1e3) / 1e12 / peak, 4)
+    result["host_wall_s"] = round(wall, 3)
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or (512 if cfg.T >= 512 else cfg.T)
+        log(f"[bench] cpu baseline: oracle on {n} tokens")
+        result["cpu_baseline"] = cpu_baseline(cfg, w, n)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -8,13 +8,16 @@
 //
 // Kernels:
 //  ffn_tile_map       per-expert m-tile counts -> prefix (device side; no host sync)
-//  ffn_gemm_bf16      prefill tile engine on MFMA 16x16x32 bf16: 256x256x64 block
-//                     tiles, 4 waves of 128x128, A and B staged through LDS in the
-//                     1 KiB fragment-tile layout (conflict-free 16 B per lane),
-//                     double-buffered, one barrier per k-step; XCD-aware mapping of
-//                     tiles so the m-tiles that share a weight tile run on the same
-//                     XCD's L2. Mode GATEUP writes H = silu(G) * U (bf16), mode
-//                     DOWN writes Y.
+//  ffn_gemm_bf16      prefill tile engine on MFMA 16x16x32 bf16: 256x256 block
+//                     tiles, 4 waves of 128x128. A and B move from global memory
+//                     straight into LDS (global_load_lds_dwordx4, no staging
+//                     registers) in the 1 KiB fragment-tile layout, so every wave
+//                     load and every fragment read is 1 KiB contiguous. A 4-deep ring
+//                     of 32-column stages keeps loads three stages ahead; one
+//                     barrier per stage; the next stage's fragments are read while
+//                     the current stage's 64 MFMAs run. Tiles are mapped XCD-aware so
+//                     the m-tiles that share a weight tile run on one XCD's L2.
+//                     Mode GATEUP writes H = silu(G) * U (bf16), mode DOWN writes Y.
 //  ffn_f32_*          fp32 VALU path (one thread per output element) for fp32
 //                     weights.
 #include "moe_internal.h"
@@ -22,7 +25,7 @@
 namespace moeffn {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kBM = 256, kBN = 256;
 constexpr int kMaxE = 1024;
 
 // Bundle geometry (must match moe_pack_expert).
@@ -117,9 +120,24 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int NT, int& e, i
   return true;
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void gbl_void_t;
+
+// 16 bytes per lane from global straight into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+constexpr int kStages = 4;            // LDS ring depth (BK = 32 per stage)
+constexpr int kStageBytes = 32768;    // A 256x32 + B 256x32 bf16
+
+struct Frags {
+  bf16x8_t a[8], b[8];
+};
+
 template <int MODE>
 __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[2][2 * kBM * kBK * 2];  // 2 x (A 32 KiB + B 32 KiB)
+  __shared__ __attribute__((aligned(1024))) char smem[kStages][kStageBytes];
   const int NT = p.N / kBN;
   int e, mt, nt;
   if (!decode_tile(p, NT, e, mt, nt)) return;
@@ -128,41 +146,35 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
   const int row0 = p.offsets[e] + mt * kBM;
   const int row_end = p.offsets[e + 1];
   const int n0 = nt * kBN;
-  const int KB32 = p.K / 32;
+  const int KS = p.K / 32;  // stages of 32 columns
   const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
 
-  // A rows this thread loads: m-blocks w*4 + i (i = 0..3), row (lane & 15) in the block
+  // this wave loads A blocks (m-blocks) and B blocks (n-blocks) w*4 .. w*4+3 of every stage
   const bf16_t* arow[4];
+  const char* bptr[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int r = row0 + (w * 4 + i) * 16 + (lane & 15);
     r = r < row_end ? r : row_end - 1;
     const int src = p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
     arow[i] = p.a + (size_t)src * p.K + 8 * (lane >> 4);
+    bptr[i] = B + ((int64_t)(n0 / 16 + w * 4 + i) * KS) * 1024 + 16 * lane;
   }
-  // B tiles this thread loads: n-blocks w*4 + i, k-blocks 0..1 of the step
-  const char* bptr[4];
+  auto issue = [&](int s) {
+    char* base = smem[s & (kStages - 1)];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) bptr[i] = B + ((int64_t)(n0 / 16 + w * 4 + i) * KB32) * 1024 + 16 * lane;
-
-  uint4 ra[8], rb[8];
-  auto gload = [&](int kt) {
+    for (int i = 0; i < 4; ++i) dma16(arow[i] + s * 32, base + (w * 4 + i) * 1024);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = j >> 1, kb = j & 1;
-      ra[j] = *reinterpret_cast<const uint4*>(arow[i] + kt * kBK + kb * 32);
-      rb[j] = *reinterpret_cast<const uint4*>(bptr[i] + ((int64_t)kt * 2 + kb) * 1024);
-    }
+    for (int i = 0; i < 4; ++i) dma16(bptr[i] + (int64_t)s * 1024, base + 16384 + (w * 4 + i) * 1024);
   };
-  auto lstore = [&](int buf) {
-    char* sa = smem[buf];
-    char* sb = smem[buf] + kBM * kBK * 2;
+  const int wm = w >> 1, wn = w & 1;
+  auto read = [&](Frags& f, int s) {
+    const char* base = smem[s & (kStages - 1)];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int blk = w * 8 + j;  // = mb*2 + kb
-      *reinterpret_cast<uint4*>(sa + blk * 1024 + 16 * lane) = ra[j];
-      *reinterpret_cast<uint4*>(sb + blk * 1024 + 16 * lane) = rb[j];
-    }
+    for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * 8 + i) * 1024 + 16 * lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8_t*>(base + 16384 + (wn * 8 + j) * 1024 + 16 * lane);
   };
 
   f32x4_t acc[8][8];
@@ -171,33 +183,47 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int wm = w >> 1, wn = w & 1;
-  const int KT = p.K / kBK;
-  gload(0);
-  lstore(0);
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+  // wait until at most n of this wave's DMA instructions are outstanding (n = 16, 8 or 0)
+  auto wait_dma = [&](int n) {
+    if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  // prologue: stages 0..3 in flight, stage 0 visible, its fragments in registers
+  for (int s = 0; s < kStages && s < KS; ++s) issue(s);
+  wait_dma(8 * (min(KS, kStages) - 1));
   __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
-    const char* sa = smem[buf];
-    const char* sb = smem[buf] + kBM * kBK * 2;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8_t af[8], bfr[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(sa + ((wm * 8 + i) * 2 + kk) * 1024 + 16 * lane);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(sb + ((wn * 8 + j) * 2 + kk) * 1024 + 16 * lane);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < KT) lstore(buf ^ 1);
+  Frags f0, f1;
+  read(f0, 0);
+
+  // iteration s: stage s+1 becomes visible, stage s+4 is issued into the buffer stage s
+  // used, the fragments of stage s+1 are read while the MFMAs of stage s run.
+  auto step = [&](int s, Frags& cur, Frags& nxt) {
+    wait_dma(8 * (min(KS - 1, s + 3) - (s + 1)));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __syncthreads();
+    if (s + kStages < KS) issue(s + kStages);
+    if (s + 1 < KS) read(nxt, s + 1);
+    mma(cur);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
+    }
+  };
+  int s = 0;
+  for (; s + 1 < KS; s += 2) {
+    step(s, f0, f1);
+    step(s + 1, f1, f0);
   }
+  if (s < KS) step(s, f0, f1);
 
   // epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile
   const int rbase = row0 + wm * 128 + 4 * (lane >> 4);
@@ -361,8 +387,8 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
   }
   if (t.w_dtype == MOE_BF16) {
     MOE_REQUIRE(act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_grouped_ffn: bf16 weights need bf16 activations");
-    MOE_REQUIRE((2 * F) % kBN == 0 && d % kBN == 0 && d % kBK == 0 && F % kBK == 0, MOE_EUNSUPPORTED,
-                "moe_grouped_ffn: bf16 prefill tiles need d and 2F multiples of %d and F a multiple of %d", kBN, kBK);
+    MOE_REQUIRE((2 * F) % kBN == 0 && d % kBN == 0, MOE_EUNSUPPORTED,
+                "moe_grouped_ffn: bf16 prefill tiles need d and 2F multiples of %d", kBN);
     int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
     bf16_t* H = reinterpret_cast<bf16_t*>(wsb + h_off);
     hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
