@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--batches", type=int, default=4, help="rotating input batches")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only time a plain device-to-device copy of this many MiB (HBM ceiling and the "
+                         "reference for the FETCH_SIZE/WRITE_SIZE counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer is not sharded across GPUs.",
@@ -97,6 +100,24 @@ def main():
     from expert_offloaded_ffn_amd import binding as B
     from expert_offloaded_ffn_amd import synth
     from expert_offloaded_ffn_amd.layer import MoELayer
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"copy_probe_bytes": n, "ms_per_copy": round(ms, 4),
+                          "hbm_read_plus_write_GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}), flush=True)
+        return 0
 
     cfg = synth.get_config(args.workload)
     if args.tokens:

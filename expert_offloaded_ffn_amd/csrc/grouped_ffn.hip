@@ -115,8 +115,13 @@ __device__ __forceinline__ bool decode_tile(const GemmArgs& p, int NT, int& e, i
   const int base = p.tile_prefix[e];
   const int mte = p.tile_prefix[e + 1] - base;
   const int local = L - base * NT;
+#if MOEFFN_TILE_ORDER == 0
   nt = local / mte;
   mt = local % mte;
+#else
+  mt = local / NT;
+  nt = local % NT;
+#endif
   return true;
 }
 
@@ -128,7 +133,22 @@ __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
-constexpr int kStages = 4;            // LDS ring depth (BK = 32 per stage)
+// Workgroup barrier without the release fence __syncthreads() carries: that fence
+// makes the compiler wait for every outstanding global load, including the LDS DMA
+// of later stages. Callers wait for what they need (vmcnt/lgkmcnt) first.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+#ifndef MOEFFN_GEMM_STAGES
+#define MOEFFN_GEMM_STAGES 4
+#endif
+#ifndef MOEFFN_TILE_ORDER
+#define MOEFFN_TILE_ORDER 0   // 0: per expert, n-tile major (m-tiles of one weight tile adjacent)
+#endif
+constexpr int kStages = MOEFFN_GEMM_STAGES;  // LDS ring depth (BK = 32 per stage)
 constexpr int kStageBytes = 32768;    // A 256x32 + B 256x32 bf16
 
 struct Frags {
@@ -149,29 +169,35 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
   const int KS = p.K / 32;  // stages of 32 columns
   const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
 
-  // this wave loads A blocks (m-blocks) and B blocks (n-blocks) w*4 .. w*4+3 of every stage
+  // This wave loads A blocks (m-blocks) and B blocks (n-blocks) w*4 .. w*4+3 of every
+  // stage. An A block is 16 rows x 32 columns; lane l fetches 16 bytes of row l/4, so each
+  // quad of lanes reads one row's 64 contiguous bytes. The 16-byte chunk index is XORed
+  // with l/16, which places chunk c of row r at slot 4r + (c ^ (r/4)) of the block: the
+  // MFMA fragment reads (row l%16, chunk l/16) then hit 16 distinct bank groups.
   const bf16_t* arow[4];
   const char* bptr[4];
+  const int a_chunk = (lane & 3) ^ (lane >> 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int r = row0 + (w * 4 + i) * 16 + (lane & 15);
+    int r = row0 + (w * 4 + i) * 16 + (lane >> 2);
     r = r < row_end ? r : row_end - 1;
     const int src = p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
-    arow[i] = p.a + (size_t)src * p.K + 8 * (lane >> 4);
+    arow[i] = p.a + (size_t)src * p.K + 8 * a_chunk;
     bptr[i] = B + ((int64_t)(n0 / 16 + w * 4 + i) * KS) * 1024 + 16 * lane;
   }
   auto issue = [&](int s) {
-    char* base = smem[s & (kStages - 1)];
+    char* base = smem[s % kStages];
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(arow[i] + s * 32, base + (w * 4 + i) * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(bptr[i] + (int64_t)s * 1024, base + 16384 + (w * 4 + i) * 1024);
   };
   const int wm = w >> 1, wn = w & 1;
+  const int a_slot = 16 * (4 * (lane & 15) + ((lane >> 4) ^ ((lane & 15) >> 2)));  // row l%16, chunk l/16
   auto read = [&](Frags& f, int s) {
-    const char* base = smem[s & (kStages - 1)];
+    const char* base = smem[s % kStages];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * 8 + i) * 1024 + 16 * lane);
+    for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * 8 + i) * 1024 + a_slot);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       f.b[j] = *reinterpret_cast<const bf16x8_t*>(base + 16384 + (wn * 8 + j) * 1024 + 16 * lane);
@@ -183,15 +209,21 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // The MFMAs are written as inline assembly with the accumulators pinned to AGPRs: with
+  // the builtin, the register allocator rotates the 64 loop-carried accumulator tiles
+  // between registers at the loop back-edge, and the copies (plus their hazard NOPs) cost
+  // about a third of the MFMA issue rate.
   auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 8; ++j)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(f.a[i]), "v"(f.b[j]));
   };
   // wait until at most n of this wave's DMA instructions are outstanding (n = 16, 8 or 0)
   auto wait_dma = [&](int n) {
-    if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    if (n >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
@@ -199,16 +231,16 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
   // prologue: stages 0..3 in flight, stage 0 visible, its fragments in registers
   for (int s = 0; s < kStages && s < KS; ++s) issue(s);
   wait_dma(8 * (min(KS, kStages) - 1));
-  __syncthreads();
+  barrier_no_fence();
   Frags f0, f1;
   read(f0, 0);
 
-  // iteration s: stage s+1 becomes visible, stage s+4 is issued into the buffer stage s
-  // used, the fragments of stage s+1 are read while the MFMAs of stage s run.
+  // iteration s: stage s+1 becomes visible, stage s+kStages is issued into the buffer
+  // stage s used, the fragments of stage s+1 are read while the MFMAs of stage s run.
   auto step = [&](int s, Frags& cur, Frags& nxt) {
-    wait_dma(8 * (min(KS - 1, s + 3) - (s + 1)));
+    wait_dma(8 * (min(KS - 1, s + kStages - 1) - (s + 1)));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __syncthreads();
+    barrier_no_fence();
     if (s + kStages < KS) issue(s + kStages);
     if (s + 1 < KS) read(nxt, s + 1);
     mma(cur);
@@ -224,6 +256,9 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
     step(s + 1, f1, f0);
   }
   if (s < KS) step(s, f0, f1);
+  // the last MFMAs must retire before their accumulators are read (the hazard
+  // recognizer does not see inside the inline assembly)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile
   const int rbase = row0 + wm * 128 + 4 * (lane >> 4);

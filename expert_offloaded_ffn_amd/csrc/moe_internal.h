@@ -9,7 +9,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"  // include/ is on the include path
 
 namespace moeffn {
 
