@@ -170,13 +170,15 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
   const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
 
   // This wave loads A blocks (m-blocks) and B blocks (n-blocks) w*4 .. w*4+3 of every
-  // stage. An A block is 16 rows x 32 columns; lane l fetches 16 bytes of row l/4, so each
-  // quad of lanes reads one row's 64 contiguous bytes. The 16-byte chunk index is XORed
-  // with l/16, which places chunk c of row r at slot 4r + (c ^ (r/4)) of the block: the
-  // MFMA fragment reads (row l%16, chunk l/16) then hit 16 distinct bank groups.
+  // stage. An A block is 16 rows x 32 columns; lane l fetches 16 bytes of row r = l/4, so
+  // each quad of lanes reads one row's 64 contiguous bytes. Chunk c of row r is stored at
+  // slot 4r + (c ^ g(r)) with g(r) = (r2 << 1) | (r1 ^ r3) (bits of r): the MFMA fragment
+  // reads (row l%16, chunk l/16) then touch distinct 16-byte bank groups within every
+  // group of 8 lanes and within every group of 16 lanes.
   const bf16_t* arow[4];
   const char* bptr[4];
-  const int a_chunk = (lane & 3) ^ (lane >> 4);
+  auto swz = [](int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); };
+  const int a_chunk = (lane & 3) ^ swz(lane >> 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int r = row0 + (w * 4 + i) * 16 + (lane >> 2);
@@ -193,7 +195,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
     for (int i = 0; i < 4; ++i) dma16(bptr[i] + (int64_t)s * 1024, base + 16384 + (w * 4 + i) * 1024);
   };
   const int wm = w >> 1, wn = w & 1;
-  const int a_slot = 16 * (4 * (lane & 15) + ((lane >> 4) ^ ((lane & 15) >> 2)));  // row l%16, chunk l/16
+  const int a_slot = 16 * (4 * (lane & 15) + ((lane >> 4) ^ swz(lane & 15)));  // row l%16, chunk l/16
   auto read = [&](Frags& f, int s) {
     const char* base = smem[s % kStages];
 #pragma unroll
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
           const int r = rbase + i * 16 + q;
           if (r < row_end) {
             const float g = acc[i][2 * pp][q], u = acc[i][2 * pp + 1][q];
-            H[(size_t)r * F + hcol] = f32_to_bf16(silu_f32(g) * u);
+            H[(size_t)r * F + hcol] = f32_to_bf16(silu_fast(g) * u);
           }
         }
       }

@@ -68,6 +68,9 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
+// silu(g) = g * sigmoid(g). Precise: IEEE division (fp32 paths). Fast: hardware exp and
+// reciprocal (about 1 ulp each), used where the result is rounded to bf16 or e4m3 anyway.
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 }  // namespace moeffn
