@@ -318,7 +318,7 @@ class SlotCache:
 
 # ------------------------------------------------------------- profile ---
 
-PROF_GATEUP, PROF_DOWN = 0, 1
+PROF_GATEUP, PROF_DOWN, PROF_DEC_GATEUP, PROF_DEC_DOWN = 0, 1, 2, 3
 
 
 def profile_enable(on: bool = True):

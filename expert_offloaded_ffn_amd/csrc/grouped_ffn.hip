@@ -301,6 +301,137 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
   }
 }
 
+// -------------------------------------------------------- decode path ---
+// Few rows per expert (decode batches): the layer is bound by streaming each active
+// expert's weights once from HBM. A workgroup owns one active expert and one group of
+// 32 weight rows (GATEUP: 16 gate + 16 up rows -> 16 hidden columns; DOWN: 32 output
+// columns); its 4 waves split K. Weight tiles go straight from global memory into MFMA
+// B fragments (the bundle's 1 KiB tile layout is the fragment layout, so every wave load
+// is 1 KiB contiguous); A rows (at most 64 per pass, in m-blocks of 16) come from L2.
+// The split-K partials are summed through LDS in wave order (deterministic).
+
+// active[0] = number of experts with rows and a slot; active[1..] = their ids, ascending.
+__global__ __launch_bounds__(64) void ffn_active_list(const int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ slot_of_expert,
+                                                      int32_t* __restrict__ active, int E) {
+  if (threadIdx.x != 0) return;
+  int n = 0;
+  for (int e = 0; e < E; ++e)
+    if (offsets[e + 1] > offsets[e] && slot_of_expert[e] >= 0) active[1 + n++] = e;
+  active[0] = n;
+}
+
+struct DecodeArgs {
+  const bf16_t* a;
+  const int32_t* a_row_src;
+  int a_row_div;
+  const int32_t* offsets;
+  const int32_t* slot_of_expert;
+  const int32_t* active;
+  const char* pool;
+  int64_t slot_stride;
+  int64_t b_off;
+  int N, K;
+  void* out;
+  int out_dtype;
+};
+
+constexpr int kDecChunk = 8;   // k-tiles whose loads are issued together
+
+template <int MODE>
+__global__ __launch_bounds__(256) void ffn_decode_bf16(DecodeArgs p) {
+  __shared__ f32x4_t red[3][4][2][64];   // partials of waves 1..3: [wave][m-block][n-tile][lane]
+  const int G = p.N / 32;
+  const int i = blockIdx.x / G, g = blockIdx.x % G;
+  if (i >= p.active[0]) return;
+  const int e = p.active[1 + i];
+  const int row0 = p.offsets[e];
+  const int n_e = p.offsets[e + 1] - row0;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int KT = p.K / 32;
+  const int kt0 = (KT * w) / 4, kt1 = (KT * (w + 1)) / 4;
+  const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
+  const char* b0 = B + ((int64_t)(2 * g) * KT) * 1024 + 16 * lane;      // n-tile 2g
+  const char* b1 = B + ((int64_t)(2 * g + 1) * KT) * 1024 + 16 * lane;  // n-tile 2g+1
+
+  for (int mc = 0; mc < n_e; mc += 64) {
+    const int mbn = min(4, (n_e - mc + 15) / 16);
+    const bf16_t* arow[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      int r = mc + m * 16 + (lane & 15);
+      r = r < n_e ? r : n_e - 1;
+      const int src = p.a_row_src ? p.a_row_src[row0 + r] / p.a_row_div : row0 + r;
+      arow[m] = p.a + (size_t)src * p.K + 8 * (lane >> 4);
+    }
+    f32x4_t acc[4][2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = kt0; k0 < kt1; k0 += kDecChunk) {
+      const int nk = min(kDecChunk, kt1 - k0);
+      bf16x8_t fb[kDecChunk][2];
+#pragma unroll
+      for (int c = 0; c < kDecChunk; ++c) {
+        if (c < nk) {
+          fb[c][0] = *reinterpret_cast<const bf16x8_t*>(b0 + (int64_t)(k0 + c) * 1024);
+          fb[c][1] = *reinterpret_cast<const bf16x8_t*>(b1 + (int64_t)(k0 + c) * 1024);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m < mbn) {
+#pragma unroll
+          for (int c = 0; c < kDecChunk; ++c) {
+            if (c < nk) {
+              const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(arow[m] + (k0 + c) * 32);
+              acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c][0], acc[m][0], 0, 0, 0);
+              acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c][1], acc[m][1], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    if (w > 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        if (m < mbn) {
+          red[w - 1][m][0][lane] = acc[m][0];
+          red[w - 1][m][1][lane] = acc[m][1];
+        }
+    }
+    __syncthreads();
+    if (w == 0) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (m >= mbn) continue;
+#pragma unroll
+        for (int ww = 0; ww < 3; ++ww) {
+          acc[m][0] += red[ww][m][0][lane];
+          acc[m][1] += red[ww][m][1][lane];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = mc + m * 16 + 4 * (lane >> 4) + q;
+          if (r >= n_e) continue;
+          if constexpr (MODE == MODE_GATEUP) {
+            const int F = p.N / 2;
+            static_cast<bf16_t*>(p.out)[(size_t)(row0 + r) * F + g * 16 + (lane & 15)] =
+                f32_to_bf16(silu_fast(acc[m][0][q]) * acc[m][1][q]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const size_t o = (size_t)(row0 + r) * p.N + (2 * g + j) * 16 + (lane & 15);
+              if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[o] = f32_to_bf16(acc[m][j][q]);
+              else static_cast<float*>(p.out)[o] = acc[m][j][q];
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------- fp32 path ---
 __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int r) {
   int lo = 0, hi = E - 1;  // last e with offsets[e] <= r
@@ -357,7 +488,7 @@ size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_o
   const size_t hsz = act_dtype == MOE_F32 ? 4 : 2;
   *h_off = 0;
   *map_off = align_up((size_t)rows * t->d_ff * hsz, 256);
-  return *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256);
+  return *map_off + 2 * align_up((size_t)(t->n_experts + 2) * 4, 256);
 }
 
 }  // namespace
@@ -427,7 +558,44 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     MOE_REQUIRE((2 * F) % kBN == 0 && d % kBN == 0, MOE_EUNSUPPORTED,
                 "moe_grouped_ffn: bf16 prefill tiles need d and 2F multiples of %d", kBN);
     int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
+    int32_t* active = reinterpret_cast<int32_t*>(wsb + map_off + align_up((size_t)(E + 2) * 4, 256));
     bf16_t* H = reinterpret_cast<bf16_t*>(wsb + h_off);
+    // Rows per expert are bounded by the number of distinct source rows: at most
+    // rows / a_row_div tokens (each picks an expert once) or all rows.
+    const int max_rows_e = a_row_src ? (rows + a_row_div - 1) / a_row_div : rows;
+    if (max_rows_e <= 64 && (2 * F) % 32 == 0 && d % 32 == 0) {
+      hipLaunchKernelGGL(ffn_active_list, dim3(1), dim3(64), 0, s, offsets, t.slot_of_expert, active, E);
+      const int max_active = E < rows ? E : rows;
+      DecodeArgs q{};
+      q.a = static_cast<const bf16_t*>(a);
+      q.a_row_src = a_row_src;
+      q.a_row_div = a_row_div;
+      q.offsets = offsets;
+      q.slot_of_expert = t.slot_of_expert;
+      q.active = active;
+      q.pool = static_cast<const char*>(t.pool);
+      q.slot_stride = t.slot_stride;
+      q.b_off = g.gu_off;
+      q.N = 2 * F;
+      q.K = d;
+      q.out = H;
+      q.out_dtype = MOE_BF16;
+      prof_mark(s, MOE_PROF_DEC_GATEUP, false);
+      hipLaunchKernelGGL(ffn_decode_bf16<MODE_GATEUP>, dim3(max_active * (q.N / 32)), dim3(256), 0, s, q);
+      prof_mark(s, MOE_PROF_DEC_GATEUP, true);
+      q.a = H;
+      q.a_row_src = nullptr;
+      q.a_row_div = 1;
+      q.b_off = g.dn_off;
+      q.N = d;
+      q.K = F;
+      q.out = y;
+      q.out_dtype = y_dtype;
+      prof_mark(s, MOE_PROF_DEC_DOWN, false);
+      hipLaunchKernelGGL(ffn_decode_bf16<MODE_DOWN>, dim3(max_active * (q.N / 32)), dim3(256), 0, s, q);
+      prof_mark(s, MOE_PROF_DEC_DOWN, true);
+      return check_launch("moe_grouped_ffn bf16 decode");
+    }
     hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
                        tile_prefix, E, kBM);
     const int max_mt = (rows + kBM - 1) / kBM + (E < rows ? E : rows);

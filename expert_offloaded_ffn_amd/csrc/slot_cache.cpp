@@ -47,6 +47,7 @@ struct expert_slot_cache {
   std::vector<hipEvent_t> copy_begin, copy_done;  // per wave
   std::vector<char> wave_copied;         // copies issued for the wave this step
   std::vector<char> timing_pending;      // copy span events to be added to copy_ms
+  hipEvent_t compute_mark = nullptr;     // blocking mode: all compute enqueued before a wave
   int32_t* counts_pinned = nullptr;
   int32_t* tables_pinned = nullptr;      // [max_waves][2][E]
   int max_waves = 0;
@@ -133,6 +134,7 @@ void destroy_device(expert_slot_cache* c) {
   for (auto& e : c->last_read) if (e) (void)hipEventDestroy(e);
   for (auto& e : c->copy_begin) if (e) (void)hipEventDestroy(e);
   for (auto& e : c->copy_done) if (e) (void)hipEventDestroy(e);
+  if (c->compute_mark) (void)hipEventDestroy(c->compute_mark);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->counts_pinned) (void)hipHostFree(c->counts_pinned);
   if (c->tables_pinned) (void)hipHostFree(c->tables_pinned);
@@ -184,6 +186,8 @@ extern "C" moe_status expert_slot_cache_create(const moe_cache_cfg* cfg, expert_
     c->last_read_valid.assign(k.n_slots, 0);
     for (auto& ev : c->last_read)
       if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+    if ((e = hipEventCreateWithFlags(&c->compute_mark, hipEventDisableTiming)) != hipSuccess)
+      return fail("hipEventCreate", e);
     c->copy_begin.assign(c->max_waves, nullptr);
     c->copy_done.assign(c->max_waves, nullptr);
     c->wave_copied.assign(c->max_waves, 0);
@@ -250,9 +254,14 @@ extern "C" moe_status expert_slot_cache_acquire(expert_slot_cache* c, const int3
 
 namespace {
 
-moe_status issue_copies(expert_slot_cache* c, int w) {
+moe_status issue_copies(expert_slot_cache* c, int w, hipStream_t compute) {
   if (c->wave_copied[w]) return MOE_OK;
   c->wave_copied[w] = 1;
+  if (c->cfg.blocking) {
+    // block, transfer, then execute: no copy starts before all compute enqueued so far
+    MOE_HIP(hipEventRecord(c->compute_mark, compute));
+    MOE_HIP(hipStreamWaitEvent(c->side, c->compute_mark, 0));
+  }
   bool any = false;
   for (const auto& en : c->waves[w]) {
     if (en.hit) continue;
@@ -291,7 +300,7 @@ extern "C" moe_status expert_slot_cache_wave(expert_slot_cache* c, int32_t wave,
   MOE_REQUIRE(part == 0 || part == 1, MOE_EINVAL, "expert_slot_cache_wave: part must be 0 or 1");
   hipStream_t s = as_stream(stream);
   const int E = c->cfg.n_experts;
-  if (moe_status st = issue_copies(c, wave)) return st;
+  if (moe_status st = issue_copies(c, wave, s)) return st;
   int32_t* table = c->tables_pinned + ((size_t)wave * 2 + part) * E;
   std::fill(table, table + E, -1);
   int n = 0;

@@ -260,9 +260,10 @@ moe_status moe_combine(int32_t T, int32_t k, int32_t d, const void* y, int32_t y
  *     part 1 (misses): makes `stream` wait for those copies and writes the
  *     table holding the wave's misses only. The caller runs moe_grouped_ffn with
  *     each table, so hit experts compute while misses are in flight.
- *     In blocking mode (cfg.blocking = 1) part 0 waits for all the wave's
- *     copies and holds every expert of the wave, and part 1 is empty: block,
- *     transfer, then execute.
+ *     In blocking mode (cfg.blocking = 1) the wave's copies start only after
+ *     all work enqueued on `stream` so far, part 0 waits for them and holds
+ *     every expert of the wave, and part 1 is empty: block, transfer, then
+ *     execute, with no copy/compute overlap.
  *  3. release(w): records that the wave's slots were read by the work enqueued
  *     so far on `stream` (a later copy into those slots waits for it).
  * Device-side state is only the pool (caller memory) and the slot tables it
@@ -320,10 +321,11 @@ moe_status expert_slot_cache_stats(const expert_slot_cache* c, moe_cache_stats* 
  * stream around each of its heavy kernels; moe_profile_read waits for the
  * recorded pairs and returns the summed milliseconds and launch counts per
  * kernel kind since the last moe_profile_enable call (which also resets).
- * Kinds: 0 gate/up GEMM with the SwiGLU epilogue, 1 down GEMM.
+ * Kinds: 0 gate/up GEMM with the SwiGLU epilogue, 1 down GEMM (many rows per
+ * expert), 2 and 3 the same for the decode kernels (at most 64 rows per expert).
  * Errors: MOE_EINVAL for a NULL out, MOE_EHIP if an event cannot be read.
  */
-enum { MOE_PROF_GATEUP = 0, MOE_PROF_DOWN = 1, MOE_PROF_KINDS = 4 };
+enum { MOE_PROF_GATEUP = 0, MOE_PROF_DOWN = 1, MOE_PROF_DEC_GATEUP = 2, MOE_PROF_DEC_DOWN = 3, MOE_PROF_KINDS = 4 };
 typedef struct {
   double ms[MOE_PROF_KINDS];
   int64_t launches[MOE_PROF_KINDS];
