@@ -432,6 +432,240 @@ __global__ __launch_bounds__(256) void ffn_decode_bf16(DecodeArgs p) {
   }
 }
 
+// ----------------------------------------------------------- fp8 path ---
+// e4m3 operands with fp32 block scales (per row per 128 columns for activations, per
+// 128x128 block for weights). The scales are arbitrary fp32 values, which the MFMA's
+// power-of-two (E8M0) scale operands cannot carry, so every 16x16x128 MFMA covers exactly
+// one 128-column scale block and its partial product is promoted on the VALU:
+// acc += P * (s_row * s_weight). The accumulators therefore live in VGPRs, which bounds
+// a wave's tile to 64 x 128: block tile 128 x 256, 4 waves (2 x 2), one 128-column scale
+// block per stage, a 3-deep LDS ring fed by direct-to-LDS loads two stages ahead.
+// LDS stage: A 128 rows x 128 B (8 blocks of 16 rows, row r's 16-byte chunk c at slot
+// 8r + (c ^ f(r)), f(r) = ((r >> 1) + 4 (r & 1)) & 7, so a row is one 128-byte DMA
+// segment and fragment reads are bank-conflict-free), B 16 tiles of 2 KiB (the bundle
+// layout), the 128 row scales of the stage's block.
+
+constexpr int kF8BM = 128, kF8BN = 256, kF8Stages = 3;
+constexpr int kF8A = 0, kF8B = 16384, kF8S = 49152, kF8StageBytes = 50176;
+
+struct Fp8Args {
+  const uint8_t* a;
+  const float* a_scale;        // [*, K/128]
+  const int32_t* a_row_src;
+  int a_row_div;
+  const int32_t* offsets;
+  const int32_t* slot_of_expert;
+  const int32_t* tile_prefix;
+  const char* pool;
+  int64_t slot_stride;
+  int64_t b_off;
+  int64_t s_off0, s_off1;      // GATEUP: gate and up scale grids [F/128][K/128]; DOWN: down grid [d/128][F/128]
+  int N, K;
+  void* out;                   // GATEUP: Hq [rows, N/2] e4m3; DOWN: y [rows, N]
+  float* out_scale;            // GATEUP: Hs [rows, N/256]
+  int out_dtype;
+  int E;
+};
+
+__device__ __forceinline__ bool decode_tile_prefix(const int32_t* tile_prefix, int E, int NT, int& e, int& mt,
+                                                   int& nt) {
+  const int total = tile_prefix[E] * NT;
+  const int total_pad = (total + 7) & ~7;
+  const int b = blockIdx.x;
+  if (b >= total_pad) return false;
+  const int L = (b & 7) * (total_pad >> 3) + (b >> 3);
+  if (L >= total) return false;
+  const int q = L / NT;
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tile_prefix[mid] <= q) lo = mid;
+    else hi = mid - 1;
+  }
+  e = lo;
+  const int base = tile_prefix[e];
+  const int mte = tile_prefix[e + 1] - base;
+  const int local = L - base * NT;
+  nt = local / mte;
+  mt = local % mte;
+  return true;
+}
+
+__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kF8Stages][kF8StageBytes];
+  __shared__ float amax_x[2][kF8BM];
+  const int NT = p.N / kF8BN;
+  int e, mt, nt;
+  if (!decode_tile_prefix(p.tile_prefix, p.E, NT, e, mt, nt)) return;
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int row0 = p.offsets[e] + mt * kF8BM;
+  const int row_end = p.offsets[e + 1];
+  const int n0 = nt * kF8BN;
+  const int KB = p.K / 128;
+  const char* bundle = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride;
+  const char* B = bundle + p.b_off;
+  auto f = [](int r) { return ((r >> 1) + 4 * (r & 1)) & 7; };
+  auto src_row = [&](int r) {
+    r = r < row_end ? r : row_end - 1;
+    return p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
+  };
+
+  // A: this wave's 4 DMA instructions per stage cover rows 32w .. 32w+31 of the tile
+  // (8 rows each); lane j loads chunk (j%8) ^ f(r) of row r = (32w + 8t + j/8) % 16 of its block.
+  const uint8_t* aptr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int tr = 32 * w + 8 * t + (lane >> 3);   // row within the 128-row tile
+    const int r16 = tr & 15;
+    aptr[t] = p.a + (size_t)src_row(row0 + tr) * p.K + 16 * ((lane & 7) ^ f(r16));
+  }
+  // row scales: wave w loads rows 64*(w&1) + lane (waves 2, 3 duplicate into the spare half)
+  const float* sptr = p.a_scale + (size_t)src_row(row0 + 64 * (w & 1) + lane) * KB;
+  const char* bptr = B + ((int64_t)(n0 / 16 + w * 4) * KB) * 2048 + 16 * lane;
+
+  auto issue = [&](int s) {
+    char* base = smem[s % kF8Stages];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(aptr[t] + s * 128, base + kF8A + (4 * w + t) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        dma16(bptr + ((int64_t)i * KB + s) * 2048 + h * 1024, base + kF8B + (w * 4 + i) * 2048 + h * 1024);
+    dma4(sptr + s, base + kF8S + w * 256);
+  };
+  auto wait_dma = [&](bool more) {
+    if (more) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  f32x4_t acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // fragment read offsets: A (row l%16, chunks 2(l/16) and 2(l/16)+1), B (two halves)
+  const int ar = lane & 15, ac = 2 * (lane >> 4);
+  const int a_off0 = 16 * (8 * ar + ((ac + 0) ^ f(ar)));
+  const int a_off1 = 16 * (8 * ar + ((ac + 1) ^ f(ar)));
+  const int nt16_0 = n0 / 16 + wn * 8;
+
+  issue(0);
+  if (KB > 1) issue(1);
+  for (int s = 0; s < KB; ++s) {
+    wait_dma(s + 1 < KB);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_no_fence();
+    if (s + 2 < KB) issue(s + 2);
+    const char* base = smem[s % kF8Stages];
+    i32x8_t fa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const char* blk = base + kF8A + (wm * 4 + i) * 2048;
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk + a_off0);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + a_off1);
+      fa[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    f32x4_t sa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sa[i] = *reinterpret_cast<const f32x4_t*>(base + kF8S + 4 * ((wm * 4 + i) * 16 + 4 * (lane >> 4)));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const char* blk = base + kF8B + (wn * 8 + j) * 2048 + 16 * lane;
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
+      const i32x8_t fb = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const int nt16 = nt16_0 + j;
+      float sw;
+      if constexpr (MODE == MODE_GATEUP) {
+        const float* grid = reinterpret_cast<const float*>(bundle + ((nt16 & 1) ? p.s_off1 : p.s_off0));
+        sw = grid[(nt16 >> 4) * KB + s];
+      } else {
+        sw = reinterpret_cast<const float*>(bundle + p.s_off0)[(nt16 >> 3) * KB + s];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb, f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                                              0, 0, 0, 127, 0, 127);
+        acc[i][j] += part * (sa[i] * sw);
+      }
+    }
+  }
+
+  const int rbase = row0 + wm * 64 + 4 * (lane >> 4);
+  if constexpr (MODE == MODE_GATEUP) {
+    // H = silu(G) * U over this tile's 128 hidden columns, then per-row e4m3 quantisation
+    const int F = p.N / 2;
+    float h[4][4][4];  // [m-block][pair][row q]
+    float am[4][4];    // [m-block][row q]
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float m = 0.f;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const float v = silu_f32(acc[i][2 * pp][q]) * acc[i][2 * pp + 1][q];
+          h[i][pp][q] = v;
+          m = fmaxf(m, fabsf(v));
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        am[i][q] = m;
+      }
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) amax_x[wn][wm * 64 + i * 16 + 4 * (lane >> 4) + q] = am[i][q];
+    }
+    __syncthreads();
+    uint8_t* Hq = static_cast<uint8_t*>(p.out);
+    const int hcol0 = n0 / 2 + wn * 64 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lr = wm * 64 + i * 16 + 4 * (lane >> 4) + q;
+        const int r = row0 + lr;
+        const float a = fmaxf(amax_x[0][lr], amax_x[1][lr]);
+        const float scale = a > 0.f ? a / 448.0f : 1.0f;
+        if (r < row_end) {
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp) {
+            const float y = fminf(fmaxf(h[i][pp][q] / scale, -448.0f), 448.0f);
+            Hq[(size_t)r * F + hcol0 + pp * 16] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
+          }
+          if (wn == 0 && (lane & 15) == 0) p.out_scale[(size_t)r * (F / 128) + n0 / kF8BN] = scale;
+        }
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = rbase + i * 16 + q;
+          if (r < row_end) {
+            if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[(size_t)r * p.N + col] = f32_to_bf16(acc[i][j][q]);
+            else static_cast<float*>(p.out)[(size_t)r * p.N + col] = acc[i][j][q];
+          }
+        }
+      }
+  }
+}
+
 // ---------------------------------------------------------- fp32 path ---
 __device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int r) {
   int lo = 0, hi = E - 1;  // last e with offsets[e] <= r
@@ -484,10 +718,16 @@ __global__ __launch_bounds__(256) void ffn_f32_down(const float* __restrict__ H,
   else static_cast<float*>(y)[(size_t)r * d + c] = s;
 }
 
-size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off) {
-  const size_t hsz = act_dtype == MOE_F32 ? 4 : 2;
+// Workspace: H [rows, F] (fp32, bf16 or e4m3) [+ e4m3 H scales [rows, F/128]], then the
+// tile prefix and the active-expert list.
+size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off,
+                 size_t* hs_off = nullptr) {
+  const size_t hsz = act_dtype == MOE_F32 ? 4 : act_dtype == MOE_FP8_E4M3 ? 1 : 2;
   *h_off = 0;
-  *map_off = align_up((size_t)rows * t->d_ff * hsz, 256);
+  size_t end = align_up((size_t)rows * t->d_ff * hsz, 256);
+  if (hs_off) *hs_off = end;
+  if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)rows * (t->d_ff / 128) * 4, 256);
+  *map_off = end;
   return *map_off + 2 * align_up((size_t)(t->n_experts + 2) * 4, 256);
 }
 
@@ -634,6 +874,59 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     prof_mark(s, MOE_PROF_DOWN, true);
     return check_launch("moe_grouped_ffn bf16");
   }
-  (void)a_scale;
-  MOE_REQUIRE(false, MOE_EUNSUPPORTED, "moe_grouped_ffn: w_dtype %d not implemented yet", t.w_dtype);
+  // fp8 weights: e4m3 activations with per-row per-128 scales
+  MOE_REQUIRE(act_dtype == MOE_FP8_E4M3 && a_scale != nullptr, MOE_EUNSUPPORTED,
+              "moe_grouped_ffn: fp8 weights need e4m3 activations and their scales");
+  MOE_REQUIRE((2 * F) % kF8BN == 0 && d % kF8BN == 0 && d % 128 == 0 && F % 128 == 0, MOE_EUNSUPPORTED,
+              "moe_grouped_ffn: fp8 tiles need d and 2F multiples of %d and F a multiple of 128", kF8BN);
+  MOE_REQUIRE(aligned(a_scale, 4), MOE_EINVAL, "moe_grouped_ffn: a_scale must be 4-byte aligned");
+  {
+    size_t hs_off;
+    ws_layout(&t, rows, act_dtype, &h_off, &map_off, &hs_off);
+    int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
+    uint8_t* Hq = reinterpret_cast<uint8_t*>(wsb + h_off);
+    float* Hs = reinterpret_cast<float*>(wsb + hs_off);
+    hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
+                       tile_prefix, E, kF8BM);
+    const int max_mt = (rows + kF8BM - 1) / kF8BM + (E < rows ? E : rows);
+    Fp8Args p{};
+    p.a = static_cast<const uint8_t*>(a);
+    p.a_scale = a_scale;
+    p.a_row_src = a_row_src;
+    p.a_row_div = a_row_div;
+    p.offsets = offsets;
+    p.slot_of_expert = t.slot_of_expert;
+    p.tile_prefix = tile_prefix;
+    p.pool = static_cast<const char*>(t.pool);
+    p.slot_stride = t.slot_stride;
+    p.E = E;
+    p.b_off = g.gu_off;
+    p.s_off0 = g.sg_off;
+    p.s_off1 = g.su_off;
+    p.N = 2 * F;
+    p.K = d;
+    p.out = Hq;
+    p.out_scale = Hs;
+    long long nblk = (long long)max_mt * (p.N / kF8BN);
+    prof_mark(s, MOE_PROF_GATEUP, false);
+    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    prof_mark(s, MOE_PROF_GATEUP, true);
+    p.a = Hq;
+    p.a_scale = Hs;
+    p.a_row_src = nullptr;
+    p.a_row_div = 1;
+    p.b_off = g.dn_off;
+    p.s_off0 = g.sd_off;
+    p.s_off1 = 0;
+    p.N = d;
+    p.K = F;
+    p.out = y;
+    p.out_scale = nullptr;
+    p.out_dtype = y_dtype;
+    nblk = (long long)max_mt * (p.N / kF8BN);
+    prof_mark(s, MOE_PROF_DOWN, false);
+    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    prof_mark(s, MOE_PROF_DOWN, true);
+  }
+  return check_launch("moe_grouped_ffn fp8");
 }

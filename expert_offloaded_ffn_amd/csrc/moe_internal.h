@@ -62,6 +62,26 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// fp32 -> OCP e4m3 code (bias 7, max 448), round to nearest even; |v| <= 448 (callers
+// clamp). Subnormals (below 2^-6) are multiples of 2^-9; normals keep 3 mantissa bits.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v) {
+  uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  u &= 0x7FFFFFFFu;
+  const float a = __uint_as_float(u);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = static_cast<uint32_t>(rintf(a * 512.0f));  // exact scaling, RNE; 8 == 2^-6
+  } else {
+    const uint32_t exp = (u >> 23) - 127u + 7u;        // 1..15
+    const uint32_t mant = u & 0x7FFFFFu;
+    const uint32_t r = mant + 0x7FFFFu + ((mant >> 20) & 1u);
+    code = (exp << 3) + (r >> 20);                     // a mantissa carry bumps the exponent
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return sign | code;
+}
+
 // MFMA operand/accumulator vectors.
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;

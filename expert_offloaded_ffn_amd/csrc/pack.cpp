@@ -23,8 +23,9 @@ inline void gu_row(int R, bool* up, int* col) {
 template <typename T>
 inline T at(const void* p, size_t i) { return static_cast<const T*>(p)[i]; }
 
-// Tiled store of an [N, K] matrix given by get(n, k): 1 KiB tiles of 16 x 32
-// (2-byte elements) or 2 KiB tiles of 16 x 128 (1-byte elements).
+// Tiled store of an [N, K] matrix given by get(n, k). bf16: 1 KiB tiles of 16 x 32, lane
+// l's 8 elements (row l%16, columns 8*(l/16)..+7) at 16*l. fp8: 2 KiB tiles of 16 x 128
+// in two 1 KiB halves; byte h*1024 + 16*l + b holds row l%16, column 32*(l/16) + 16h + b.
 template <typename T, int TK, typename Get>
 void store_tiled(char* dst, int N, int K, Get get) {
   const int tiles_k = K / TK;
@@ -36,7 +37,8 @@ void store_tiled(char* dst, int N, int K, Get get) {
         for (int i = 0; i < per_lane; ++i) {
           const int n = nb * 16 + (lane & 15);
           const int k = kb * TK + per_lane * (lane >> 4) + i;
-          tile[lane * per_lane + i] = get(n, k);
+          const size_t pos = TK == 32 ? (size_t)lane * 8 + i : (size_t)(i >> 4) * 1024 + lane * 16 + (i & 15);
+          tile[pos] = get(n, k);
         }
     }
 }

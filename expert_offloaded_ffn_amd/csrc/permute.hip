@@ -104,25 +104,6 @@ __global__ __launch_bounds__(256) void gather_rows_copy(const uint8_t* __restric
   for (int i = lane; i < row_bytes / 16; i += 64) o[i] = s[i];
 }
 
-// fp32 -> OCP e4m3 code, round to nearest even; |v| <= 448 (callers clamp).
-__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v) {
-  uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  u &= 0x7FFFFFFFu;
-  const float a = __uint_as_float(u);
-  uint32_t code;
-  if (a < 0.015625f) {                  // below the smallest normal 2^-6: quantum 2^-9
-    code = static_cast<uint32_t>(rintf(a * 512.0f));   // exact scaling, RNE; 8 == 2^-6
-  } else {
-    const uint32_t exp = (u >> 23) - 127u + 7u;        // 1..15
-    const uint32_t mant = u & 0x7FFFFFu;
-    const uint32_t r = mant + 0x7FFFFu + ((mant >> 20) & 1u);
-    code = (exp << 3) + (r >> 20);                     // a mantissa carry bumps the exponent
-    code = code > 0x7Eu ? 0x7Eu : code;
-  }
-  return sign | code;
-}
-
 // One wavefront per row; 16 lanes x 8 values cover a 128-column block.
 template <typename TIn>
 __global__ __launch_bounds__(256) void gather_rows_quant_e4m3(const TIn* __restrict__ x, uint8_t* __restrict__ out,

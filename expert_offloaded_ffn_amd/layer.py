@@ -97,6 +97,15 @@ class MoELayer:
             self._ws[name] = t
         return t[:max(numel, 1)] if numel else t[:1]
 
+    def _shared_offsets(self, T):
+        """Device [0, T] offsets of the single shared-expert group (cached per T)."""
+        key = ("shared_offsets", T)
+        t = self._ws.get(key)
+        if t is None:
+            t = torch.tensor([0, T], dtype=torch.int32).to(self.device)
+            self._ws[key] = t
+        return t
+
     def route_args(self):
         c = self.cfg
         return dict(k=c.k, score_fn=B.MOE_SIGMOID if c.score_fn == "sigmoid" else B.MOE_SOFTMAX,
@@ -110,14 +119,21 @@ class MoELayer:
         r = B.route(x, self.w_router_t, logit_bias=logit_bias, select_bias=self.select_bias,
                     w_shared_gate=self.w_sg, stream=stream, **self.route_args())
         ws = self._buf("perm_ws", B.permute_workspace_size(T, k, E))
-        p = B.permute(r["idx"], E, ws=ws, stream=stream)
         rows = T * k
         ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
         y = torch.empty(rows, d, device=self.device, dtype=torch.float32 if ydt == B.MOE_F32 else torch.bfloat16)
-        fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, self.act_code))
+        a, a_scale, a_code = x, None, self.act_code
+        if self.w_code == B.MOE_FP8_E4M3:
+            # grouping plus one e4m3 quantisation of every token (token order); the GEMMs
+            # gather rows through perm_src
+            p = B.permute(r["idx"], E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=0, ws=ws, stream=stream)
+            a, a_scale, a_code = p["x_out"], p["x_out_scale"], B.MOE_FP8_E4M3
+        else:
+            p = B.permute(r["idx"], E, ws=ws, stream=stream)
+        fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
         if self.cache is None:
-            B.grouped_ffn(self.table, rows, p["offsets"], x, a_row_src=p["perm_src"], a_row_div=k, y=y,
-                          y_dtype=ydt, ws=fws, stream=stream)
+            B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
+                          a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=stream)
             waves = 0
         else:
             waves = self.cache.acquire(r["counts"], stream=stream)
@@ -125,15 +141,15 @@ class MoELayer:
                 for part in (0, 1):
                     n = self.cache.wave(w, part, self.slot_table, stream=stream)
                     if n:
-                        B.grouped_ffn(self.table, rows, p["offsets"], x, a_row_src=p["perm_src"], a_row_div=k, y=y,
-                                      y_dtype=ydt, ws=fws, stream=stream)
+                        B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
+                                      a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=stream)
                 self.cache.release(w, stream=stream)
         shared_y = None
         if self.shared is not None:
-            offs = self._buf("shared_offsets", 2, torch.int32)
-            offs.copy_(torch.tensor([0, T], dtype=torch.int32))
+            offs = self._shared_offsets(T)
             shared_y = torch.empty(T, d, device=self.device, dtype=y.dtype)
-            sws = self._buf("shared_ws", B.grouped_ffn_workspace_size(self.shared.table, T, self.act_code))
-            B.grouped_ffn(self.shared.table, T, offs, x, y=shared_y, y_dtype=ydt, ws=sws, stream=stream)
+            sws = self._buf("shared_ws", B.grouped_ffn_workspace_size(self.shared.table, T, a_code))
+            B.grouped_ffn(self.shared.table, T, offs, a, a_scale=a_scale, act_dtype=a_code, y=shared_y, y_dtype=ydt,
+                          ws=sws, stream=stream)
         out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"], stream=stream)
         return {"out": out, "route": r, "perm": p, "y": y, "shared_y": shared_y, "waves": waves}

@@ -163,8 +163,10 @@ moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_idx,
  *   16j..16j+15 and rows 32j+16..32j+31 are W_up columns 16j..16j+15 (the
  *   gate and up halves of every 16 hidden units are adjacent).
  *   W_dn is [d, F] (N = d, K = F): row n is W_down column n.
- *  MOE_FP8_E4M3: same row orders, 2 KiB tiles of 16 rows x 128 columns, lane l
- *   holding 32 consecutive codes of row 16nb + l%16 at columns 128kb + 32*(l/16);
+ *  MOE_FP8_E4M3: same row orders, 2 KiB tiles of 16 rows x 128 columns at
+ *   ((nb * K/128) + kb) * 2048 bytes; byte h*1024 + 16*l + b (h = 0, 1; lane
+ *   l = 0..63; b = 0..15) holds row 16nb + l%16, column 128kb + 32*(l/16) +
+ *   16h + b (each half is one contiguous 1 KiB wave load of 16 bytes per lane);
  *   then three fp32 scale grids: gate [F/128][d/128], up [F/128][d/128],
  *   down [d/128][F/128] (one scale per 128x128 block of the original matrix).
  *  MOE_F32: W_gate^T [F, d], W_up^T [F, d], W_down^T [d, F], plain row-major.

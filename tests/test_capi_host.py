@@ -114,8 +114,9 @@ def test_pack_fp8_layout_and_scales():
         R, kk = rng.integers(0, 2 * F), rng.integers(0, d)
         tile = (R // 16) * (d // 128) + kk // 128
         lane = R % 16 + 16 * ((kk % 128) // 32)
+        half, byte = (kk % 32) // 16, kk % 16
         j, rr = R // 32, R % 32
-        assert b[tile * 2048 + lane * 32 + kk % 32] == (wu if rr >= 16 else wg)[kk, 16 * j + rr % 16]
+        assert b[tile * 2048 + half * 1024 + lane * 16 + byte] == (wu if rr >= 16 else wg)[kk, 16 * j + rr % 16]
     off = 2 * F * d + d * F
     s = b[off:].view(np.float32)
     assert s[0] == sg[0, 0] and s[1] == sg[1, 0]                # gate stored [F/128][d/128]

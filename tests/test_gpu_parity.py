@@ -158,3 +158,18 @@ def test_dsv3_routing_full_size():
     say(f"    near-tie mismatches: {int((~same).sum())} of {cfg.T}")
     g = to_np(r["gate"])
     np.testing.assert_allclose(g.sum(axis=1), 2.5, rtol=1e-5)
+
+
+@pytest.mark.parametrize("T,d,E,k,F,Fs,G,TG", [(300, 512, 16, 4, 256, 256, 4, 2), (70, 256, 32, 8, 128, 128, 8, 4)])
+def test_fp8_layer_reduced(T, d, E, k, F, Fs, G, TG):
+    cfg = synth.get_config("dsv3_prefill_fp8", T=T, d=d, E=E, k=k, F=F, F_shared=Fs, n_groups=G, topk_groups=TG,
+                           name=f"fp8_T{T}_d{d}_E{E}_k{k}_F{F}")
+    layer, w = _build(cfg)
+    _run_and_check(cfg, layer, w, T)
+
+
+def test_dsv3_fp8_full_size_sampled():
+    cfg = synth.get_config("dsv3_prefill_fp8")
+    layer, w = _build(cfg)
+    toks = np.array([0, 1234, 5000, cfg.T - 1])
+    _run_and_check(cfg, layer, w, cfg.T, 0, tokens=toks)
