@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; HBM TB/s (decode) & MFMA TFLOP/s (prefill) vs peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = ["mixtral_prefill_bf16", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16"]
+WORKLOADS = ["mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16"]
 
 
 def log(*a):
@@ -49,6 +49,11 @@ def cpu_baseline(cfg, w, sample_tokens):
     def dec(a):
         return np.asarray(a, np.float64) if cfg.act_dtype == "f32" else formats.decode_bf16(a)
 
+    def dec_w(m):
+        if cfg.dtype == "fp8":
+            return formats.dequantize_weight_blocks(*m)
+        return dec(m)
+
     threads = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
@@ -58,22 +63,23 @@ def cpu_baseline(cfg, w, sample_tokens):
     except Exception:
         pass
     from expert_offloaded_ffn_amd import synth
-    x_store = synth.gen_x(cfg, 0)[:sample_tokens]
+    nb = (sample_tokens + cfg.T - 1) // cfg.T
+    x_store = np.concatenate([synth.gen_x(cfg, i) for i in range(nb)])[:sample_tokens]
     t0 = time.perf_counter()
     x = dec(x_store)
     r = moe.route(x, dec(w["router"]), k=cfg.k, score_fn=cfg.score_fn, renormalize=bool(cfg.renormalize),
                   route_scale=cfg.route_scale, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
-                  group_topn=cfg.group_topn,
+                  group_topn=cfg.group_topn, select_bias=w.get("sb"),
                   w_shared_gate=None if w["w_sg"] is None else dec(w["w_sg"]))
 
     def expert(e):
-        return moe.ExpertWeights(*[dec(m) for m in w["experts"][e]])
+        return moe.ExpertWeights(*[dec_w(m) for m in w["experts"][e]])
 
-    shared = None if w["shared"] is None else moe.ExpertWeights(*[dec(m) for m in w["shared"]])
-    moe.moe_layer(x, r, expert, cfg.E, shared=shared)
+    shared = None if w["shared"] is None else moe.ExpertWeights(*[dec_w(m) for m in w["shared"]])
+    moe.moe_layer(x, r, expert, cfg.E, shared=shared, quant_act=cfg.dtype == "fp8")
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {sample_tokens} tokens of batch 0 of {cfg.name} (T={cfg.T}), float64, "
+            "sample": f"first {sample_tokens} tokens of batches 0.. of {cfg.name} (T={cfg.T}), float64, "
                       f"expert weights decoded per expert; {dt:.1f} s"}
 
 
@@ -251,9 +257,10 @@ def main():
     log(f"[bench] workload {cfg.name} T={cfg.T}: generating inputs")
     w = dict(router=synth.gen_router(cfg), experts=synth.gen_experts(cfg, threads=16),
              shared=synth.gen_shared(cfg) if cfg.F_shared else None,
-             w_sg=synth.gen_shared_gate(cfg) if cfg.shared_gate else None)
+             w_sg=synth.gen_shared_gate(cfg) if cfg.shared_gate else None,
+             sb=synth.gen_select_bias(cfg) if cfg.select_bias else None)
     layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
-                     threads=16)
+                     select_bias=w["sb"], threads=16)
     xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(args.batches)]
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup}")
@@ -285,11 +292,13 @@ def main():
 
     d, F, E, T, k = cfg.d, cfg.F, cfg.E, cfg.T, cfg.k
     rows = np.array([rows_e[i % len(xs)].sum() for i in range(args.steps)], dtype=np.float64)
-    gateup_flops = 4.0 * rows * d * F                        # per launch, real rows only
-    down_flops = 2.0 * rows * F * d
+    # gate/up and down launches per step: the routed experts' (real rows only) and, with a
+    # shared expert, a second launch over all T tokens; achieved = their flops / their time
+    gateup_flops = 4.0 * rows * d * F + 4.0 * T * d * cfg.F_shared
+    down_flops = 2.0 * rows * F * d + 2.0 * T * cfg.F_shared * d
     router_flops = 2.0 * T * d * E
-    shared_flops = 6.0 * T * d * cfg.F_shared
-    layer_flops = float((gateup_flops + down_flops).mean() + router_flops + shared_flops)
+    layer_flops = float((gateup_flops + down_flops).mean() + router_flops)
+    launches = 2 if cfg.F_shared else 1
     gu_ms, gu_n = prof[B.PROF_GATEUP]
     dn_ms, dn_n = prof[B.PROF_DOWN]
     dtype = cfg.dtype
@@ -304,21 +313,25 @@ def main():
     }
     if gu_n:
         gu_avg_s = gu_ms / gu_n / 1e3
-        achieved = float(gateup_flops.mean()) / gu_avg_s / 1e12
-        result["roofline"] = {"bound": "mfma", "kernel": "ffn_gemm_bf16<gate/up+SwiGLU>",
+        achieved = float(gateup_flops.mean()) / (gu_avg_s * launches) / 1e12
+        kname = "ffn_gemm_fp8<gate/up+SwiGLU+requant>" if dtype == "fp8" else "ffn_gemm_bf16<gate/up+SwiGLU>"
+        result["roofline"] = {"bound": "mfma", "kernel": kname,
                               "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                               "frac": round(achieved / peak, 4), "traffic": None,
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
-                              "work_per_launch": f"4*rows*d*F flops, rows = T*k = {int(rows.mean())}"}
+                              "work_per_launch": f"4*rows*d*F flops, rows = T*k = {int(rows.mean())}"
+                              + (f"; plus the shared expert's launch, 4*T*d*F_s" if cfg.F_shared else "")}
         if dn_n:
             dn_avg_s = dn_ms / dn_n / 1e3
             result["down_gemm"] = {"avg_launch_ms": round(dn_ms / dn_n, 4),
-                                   "achieved_tflops": round(float(down_flops.mean()) / dn_avg_s / 1e12, 1)}
+                                   "achieved_tflops": round(float(down_flops.mean()) / (dn_avg_s * launches) / 1e12, 1)}
     result["layer_tflops"] = round(layer_flops / (ms_step / 1e3) / 1e12, 1)
     result["layer_frac_of_peak"] = round(layer_flops / (ms_step / 1e3) / 1e12 / peak, 4)
     result["host_wall_s"] = round(wall, 3)
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or (512 if cfg.T >= 512 else cfg.T)
+        # sized for roughly 10-30 s of oracle work: the fp8 oracle dequantises every touched
+        # expert to float64, so its sample is a handful of tokens
+        n = args.cpu_sample_tokens or (32 if cfg.dtype == "fp8" else 3 * cfg.T)
         log(f"[bench] cpu baseline: oracle on {n} tokens")
         result["cpu_baseline"] = cpu_baseline(cfg, w, n)
     print(json.dumps(result), flush=True)
