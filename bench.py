@@ -166,12 +166,23 @@ def bench_decode(args, torch, B, synth, MoELayer):
     for i in range(args.warmup):
         layer.forward(xs[i % nb])
     torch.cuda.synchronize()
-    B.profile_enable(True)
+    graph = None
+    if args.graph:
+        # the whole layer as one HIP graph; inputs are refilled in place before each replay
+        x_static = torch.empty_like(xs[0])
+        x_static.copy_(xs[0])
+        graph, _ = layer.capture(x_static)
+    B.profile_enable(not args.graph)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
         flush.fill_(i & 255)
-        evs[i][0].record()
-        layer.forward(xs[i % nb])
+        if graph is not None:
+            x_static.copy_(xs[i % nb])
+            evs[i][0].record()
+            graph.replay()
+        else:
+            evs[i][0].record()
+            layer.forward(xs[i % nb])
         evs[i][1].record()
     torch.cuda.synchronize()
     prof = B.profile_read()
@@ -187,7 +198,7 @@ def bench_decode(args, torch, B, synth, MoELayer):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
-                   "d_ff": cfg.F, "d_ff_shared": cfg.F_shared, "mall_flush_MiB": 512},
+                   "d_ff": cfg.F, "d_ff_shared": cfg.F_shared, "mall_flush_MiB": 512, "hip_graph": bool(args.graph)},
         "step_ms_p10_p50_p90": [round(float(np.percentile(ms, q)), 4) for q in (10, 50, 90)],
         "touched_experts_mean": round(float(np.mean([touched[i % nb] for i in range(args.steps)])), 2),
         "layer_hbm": {"achieved": round(hbm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
@@ -214,6 +225,7 @@ def main():
     ap.add_argument("--batches", type=int, default=4, help="rotating input batches")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="decode: replay the layer as one captured HIP graph")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (HBM ceiling and the "
                          "reference for the FETCH_SIZE/WRITE_SIZE counters), then exit")

@@ -311,14 +311,21 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
 // The split-K partials are summed through LDS in wave order (deterministic).
 
 // active[0] = number of experts with rows and a slot; active[1..] = their ids, ascending.
+// One wavefront: 64 experts per step, a ballot and a popcount of lower lanes place each.
 __global__ __launch_bounds__(64) void ffn_active_list(const int32_t* __restrict__ offsets,
                                                       const int32_t* __restrict__ slot_of_expert,
                                                       int32_t* __restrict__ active, int E) {
-  if (threadIdx.x != 0) return;
+  const int lane = threadIdx.x;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int n = 0;
-  for (int e = 0; e < E; ++e)
-    if (offsets[e + 1] > offsets[e] && slot_of_expert[e] >= 0) active[1 + n++] = e;
-  active[0] = n;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const bool on = e < E && offsets[e + 1] > offsets[e] && slot_of_expert[e] >= 0;
+    const uint64_t m = __ballot(on);
+    if (on) active[1 + n + __popcll(m & below)] = e;
+    n += __popcll(m);
+  }
+  if (lane == 0) active[0] = n;
 }
 
 struct DecodeArgs {

@@ -14,6 +14,8 @@
 //                experts gives offsets; base[b][e] = offsets[e] + sum_{b'<b}.
 //  scatter       the same ballots; a pair's row is base[b][e] plus the number
 //                of lower lanes (= earlier tokens) in the ballot.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moeffn {
@@ -21,16 +23,19 @@ namespace {
 
 constexpr int kMaxE = 1024;
 
+// KMAX is a compile-time bound on k, so each lane's expert list stays in registers.
+template <int KMAX>
 __global__ __launch_bounds__(64) void permute_block_counts(const int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
                                                            int T, int k, int E) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const int t = b * 64 + lane;
-  int mine[32];
-  const int kk = k;
-  for (int j = 0; j < kk; ++j) mine[j] = t < T ? idx[(size_t)t * k + j] : -1;
+  int mine[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) mine[j] = (t < T && j < k) ? idx[(size_t)t * k + j] : -1;
   for (int e = 0; e < E; ++e) {
     bool has = false;
-    for (int j = 0; j < kk; ++j) has |= (mine[j] == e);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) has |= (mine[j] == e);
     const uint64_t m = __ballot(has);
     if (lane == 0) cnt[(size_t)b * E + e] = __popcll(m);
   }
@@ -68,18 +73,21 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
   }
 }
 
+template <int KMAX>
 __global__ __launch_bounds__(64) void permute_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
                                                       const int32_t* __restrict__ base, int32_t* __restrict__ perm_src,
                                                       int32_t* __restrict__ perm_dst, int T, int k, int E) {
   const int b = blockIdx.x, lane = threadIdx.x;
   const int t = b * 64 + lane;
-  int mine[32];
-  for (int j = 0; j < k; ++j) mine[j] = t < T ? idx[(size_t)t * k + j] : -1;
+  int mine[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) mine[j] = (t < T && j < k) ? idx[(size_t)t * k + j] : -1;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int e = 0; e < E; ++e) {
     if (cnt[(size_t)b * E + e] == 0) continue;  // uniform across the wave
     int jj = -1;
-    for (int j = 0; j < k; ++j) jj = (mine[j] == e) ? j : jj;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) jj = (mine[j] == e) ? j : jj;
     const uint64_t m = __ballot(jj >= 0);
     if (jj >= 0) {
       const int r = base[(size_t)b * E + e] + __popcll(m & below);
@@ -200,9 +208,17 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
   const int nb = (T + 63) / 64;
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* base = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + need / 2);
-  hipLaunchKernelGGL(permute_block_counts, dim3(nb), dim3(64), 0, s, topk_idx, cnt, T, k, E);
-  hipLaunchKernelGGL(permute_scan, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, cnt, base, offsets, nb, E);
-  hipLaunchKernelGGL(permute_scatter, dim3(nb), dim3(64), 0, s, topk_idx, cnt, base, perm_src, perm_dst, T, k, E);
+  auto sort = [&](auto kmax) {
+    constexpr int KM = decltype(kmax)::value;
+    hipLaunchKernelGGL(permute_block_counts<KM>, dim3(nb), dim3(64), 0, s, topk_idx, cnt, T, k, E);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, cnt, base, offsets, nb, E);
+    hipLaunchKernelGGL(permute_scatter<KM>, dim3(nb), dim3(64), 0, s, topk_idx, cnt, base, perm_src, perm_dst, T, k,
+                       E);
+  };
+  if (k <= 2) sort(std::integral_constant<int, 2>{});
+  else if (k <= 4) sort(std::integral_constant<int, 4>{});
+  else if (k <= 8) sort(std::integral_constant<int, 8>{});
+  else sort(std::integral_constant<int, 32>{});
   if (moe_status st = check_launch("moe_permute sort")) return st;
   if (x_out == nullptr) return MOE_OK;
   const int rows = gather ? T * k : T;

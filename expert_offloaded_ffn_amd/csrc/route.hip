@@ -6,10 +6,9 @@
 // handle each token). This file implements the reading stated in moe.h.
 //
 // Kernels:
-//  route_logits_mfma  bf16 logits on MFMA 16x16x32: a wave owns 16 tokens x all
-//                     expert columns of its block; operands are read straight
-//                     from global (L2-resident router weights) in the MFMA
-//                     fragment layout.
+//  route_logits_mfma  bf16 logits on MFMA 16x16x32, split over K across the waves
+//                     of a block (operands read straight from global in the MFMA
+//                     fragment layout; the router weights stay L2-resident).
 //  route_logits_f32   fp32 logits, one thread per (token, expert) dot product.
 //  route_select       one wavefront per token: keys, group limit, k rounds of a
 //                     64-lane arg-max over packed (key, ~index) words, gates, and
@@ -24,61 +23,84 @@ constexpr int kMaxK = 32;
 constexpr int kMaxGroups = 64;
 
 // -------------------------------------------------------------- logits ---
-// Block: 256 threads = 4 waves; block tile = 64 tokens x 64 expert columns.
-// Column c < E reads w_router row c; c == E (when has_shared) reads w_sg.
+// A block owns MT m-tiles of 16 tokens x 64 expert columns (4 n-tiles of 16); its WK
+// waves split K, each accumulating MT x 4 MFMA tiles over its K range; the partials are
+// summed through LDS in wave order (deterministic) by the first wave. Column c < E reads
+// w_router row c; c == E (when w_sg is given) reads w_sg. Small batches use MT = 1 and
+// WK = 16 (a decode step is a few MFMA steps deep); large batches MT = 4, WK = 4.
 // Output: raw logits into scores[t, c] for c < E, and into shared_logit[t].
-__global__ __launch_bounds__(256) void route_logits_mfma(
+template <int MT, int WK>
+__global__ __launch_bounds__(64 * WK) void route_logits_mfma(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_router,
     const bf16_t* __restrict__ w_sg, float* __restrict__ scores, float* __restrict__ shared_logit,
     int32_t* __restrict__ counts, int T, int d, int E) {
+  __shared__ f32x4_t red[WK - 1][MT][4][64];
   if (counts != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
     for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
   }
   const int ncols = E + (w_sg != nullptr ? 1 : 0);
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 64 + wave * 16;
+  const int t0 = blockIdx.x * 16 * MT;
   const int c0 = blockIdx.y * 64;
-  if (t0 >= T) return;
   const int ntile = min(4, (ncols - c0 + 15) / 16);
+  const int KT = d / 32;
+  const int k0 = (KT * wave) / WK, k1 = (KT * (wave + 1)) / WK;
 
-  const int trow = min(t0 + (lane & 15), T - 1);
   const int koff = 8 * (lane >> 4);
-  const bf16_t* arow = x + (size_t)trow * d + koff;
+  const bf16_t* arow[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) arow[m] = x + (size_t)min(t0 + m * 16 + (lane & 15), T - 1) * d + koff;
   const bf16_t* brow[4];
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
-    int c = min(c0 + n * 16 + (lane & 15), ncols - 1);
+    const int c = min(c0 + n * 16 + (lane & 15), ncols - 1);
     brow[n] = (c < E ? w_router + (size_t)c * d : w_sg) + koff;
   }
-  f32x4_t acc[4];
+  f32x4_t acc[MT][4];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int k = 0; k < d; k += 32) {
-    bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(arow + k);
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if (n < ntile) {
-        bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(brow[n] + k);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
-      }
-    }
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int kt = k0; kt < k1; ++kt) {
+    bf16x8_t b[4], a[MT];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+      if (n < ntile) b[n] = *reinterpret_cast<const bf16x8_t*>(brow[n] + kt * 32);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) a[m] = *reinterpret_cast<const bf16x8_t*>(arow[m] + kt * 32);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        if (n < ntile) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) red[wave - 1][m][n][lane] = acc[m][n];
+  }
+  __syncthreads();
+  if (wave != 0) return;
   // D layout: lane l holds rows 4*(l/16)+i, column l%16.
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    if (n >= ntile) continue;
-    const int c = c0 + n * 16 + (lane & 15);
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * (lane >> 4) + i;
-      if (t < T && c < ncols) {
-        if (c < E) scores[(size_t)t * E + c] = acc[n][i];
-        else shared_logit[t] = acc[n][i];
+    for (int n = 0; n < 4; ++n) {
+      if (n >= ntile) continue;
+      f32x4_t v = acc[m][n];
+      for (int w = 0; w < WK - 1; ++w) v += red[w][m][n][lane];
+      const int c = c0 + n * 16 + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + m * 16 + 4 * (lane >> 4) + i;
+        if (t < T && c < ncols) {
+          if (c < E) scores[(size_t)t * E + c] = v[i];
+          else shared_logit[t] = v[i];
+        }
       }
     }
-  }
 }
 
 template <typename T_>
@@ -134,14 +156,13 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 constexpr int kSelWaves = 4;     // waves per block
-constexpr int kTokPerWave = 16;  // tokens each wave handles in turn
 
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void route_select(
     float* __restrict__ scores, const float* __restrict__ logit_bias, const float* __restrict__ select_bias,
     float* __restrict__ shared_gate, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
     int32_t* __restrict__ counts, int T, int E, int k, int score_fn, int renormalize, float route_scale,
-    int n_groups, int topk_groups, int group_topn) {
+    int n_groups, int topk_groups, int group_topn, int tok_per_wave) {
   __shared__ int hist[kMaxE];
   __shared__ float wkeys[kSelWaves][kMaxE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -150,8 +171,8 @@ __global__ __launch_bounds__(256) void route_select(
   __syncthreads();
 
   const int gsz = n_groups > 0 ? E / n_groups : E;
-  for (int it = 0; it < kTokPerWave; ++it) {
-    const int t = (blockIdx.x * kSelWaves + wave) * kTokPerWave + it;
+  for (int it = 0; it < tok_per_wave; ++it) {
+    const int t = (blockIdx.x * kSelWaves + wave) * tok_per_wave + it;
     if (t >= T) break;
     float logit[PER_LANE], key[PER_LANE];
     bool live[PER_LANE];
@@ -281,11 +302,12 @@ __global__ __launch_bounds__(256) void route_select(
 }
 
 template <int PL>
-void launch_select(dim3 grid, hipStream_t s, float* scores, const float* lb, const float* sb, float* sg,
+void launch_select(int tpw, hipStream_t s, float* scores, const float* lb, const float* sb, float* sg,
                    int32_t* idx, float* gate, int32_t* counts, const moe_route_cfg& c) {
+  dim3 grid((c.T + kSelWaves * tpw - 1) / (kSelWaves * tpw));
   hipLaunchKernelGGL(route_select<PL>, grid, dim3(256), 0, s, scores, lb, sb, sg, idx, gate, counts, c.T,
                      c.n_experts, c.top_k, c.score_fn, c.renormalize, c.route_scale, c.n_groups,
-                     c.topk_groups, c.group_topn);
+                     c.topk_groups, c.group_topn, tpw);
 }
 
 }  // namespace
@@ -328,10 +350,18 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
   hipStream_t s = as_stream(stream);
   const int ncols = c.n_experts + (w_shared_gate ? 1 : 0);
   if (c.act_dtype == MOE_BF16 && c.d_model % 32 == 0) {
-    dim3 grid((c.T + 63) / 64, (ncols + 63) / 64);
-    hipLaunchKernelGGL(route_logits_mfma, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(w_router), static_cast<const bf16_t*>(w_shared_gate), scores,
-                       shared_gate, counts, c.T, c.d_model, c.n_experts);
+    const bf16_t* xb = static_cast<const bf16_t*>(x);
+    const bf16_t* wb = static_cast<const bf16_t*>(w_router);
+    const bf16_t* sgb = static_cast<const bf16_t*>(w_shared_gate);
+    if (c.T <= 256) {
+      dim3 grid((c.T + 15) / 16, (ncols + 63) / 64);
+      hipLaunchKernelGGL((route_logits_mfma<1, 16>), grid, dim3(1024), 0, s, xb, wb, sgb, scores, shared_gate, counts,
+                         c.T, c.d_model, c.n_experts);
+    } else {
+      dim3 grid((c.T + 63) / 64, (ncols + 63) / 64);
+      hipLaunchKernelGGL((route_logits_mfma<4, 4>), grid, dim3(256), 0, s, xb, wb, sgb, scores, shared_gate, counts,
+                         c.T, c.d_model, c.n_experts);
+    }
   } else {
     const long long n = (long long)c.T * ncols;
     dim3 grid((unsigned)((n + 255) / 256));
@@ -345,11 +375,11 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
                          shared_gate, counts, c.T, c.d_model, c.n_experts);
   }
   if (moe_status st = check_launch("moe_route logits")) return st;
-  dim3 sgrid((c.T + kSelWaves * kTokPerWave - 1) / (kSelWaves * kTokPerWave));
+  const int tpw = c.T >= 16384 ? 4 : 1;  // tokens per wavefront
   const int per_lane = (c.n_experts + 63) / 64;
-  if (per_lane <= 1) launch_select<1>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
-  else if (per_lane <= 2) launch_select<2>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
-  else if (per_lane <= 4) launch_select<4>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
-  else launch_select<16>(sgrid, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  if (per_lane <= 1) launch_select<1>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  else if (per_lane <= 2) launch_select<2>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  else if (per_lane <= 4) launch_select<4>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
+  else launch_select<16>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
   return check_launch("moe_route select");
 }

@@ -153,3 +153,21 @@ class MoELayer:
                           ws=sws, stream=stream)
         out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"], stream=stream)
         return {"out": out, "route": r, "perm": p, "y": y, "shared_y": shared_y, "waves": waves}
+
+    def capture(self, x_static: torch.Tensor, logit_bias_static: torch.Tensor | None = None):
+        """Records forward() for fixed input buffers as one HIP graph (resident layers only: the
+        slot pool synchronises with the host every step). Returns (graph, outputs); refill
+        x_static (and logit_bias_static) in place, then graph.replay() recomputes outputs."""
+        if self.cache is not None:
+            raise RuntimeError("capture() needs a resident layer; the slot pool plans on the host each step")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                self.forward(x_static, logit_bias_static)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            outputs = self.forward(x_static, logit_bias_static)
+        return graph, outputs

@@ -173,3 +173,25 @@ def test_dsv3_fp8_full_size_sampled():
     layer, w = _build(cfg)
     toks = np.array([0, 1234, 5000, cfg.T - 1])
     _run_and_check(cfg, layer, w, cfg.T, 0, tokens=toks)
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_decode_graph_replay_matches_eager(T):
+    """The whole decode layer captured as one HIP graph: every replay (with eager work and
+    synchronisations in between) equals the eager result bit for bit, for changing inputs."""
+    cfg = synth.get_config("qwen_decode_bf16", T=T)
+    layer, w = _build(cfg)
+    x_static = _x_dev(cfg, synth.gen_x(cfg, 0))
+    say(f"  case decode graph T={T}: capture")
+    graph, outs = layer.capture(x_static)
+    for i in range(4):
+        xi = _x_dev(cfg, synth.gen_x(cfg, 10 + i))
+        x_static.copy_(xi)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = outs["out"].clone()
+        ref = layer.forward(xi)["out"]            # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i} differs from eager"
+    # and the replayed output still matches the oracle
+    _run_and_check(cfg, layer, w, T, 13)
