@@ -9,13 +9,13 @@
 // Kernels:
 //  ffn_tile_map       per-expert m-tile counts -> prefix (device side; no host sync)
 //  ffn_gemm_bf16      prefill tile engine on MFMA 16x16x32 bf16: 256x256 block
-//                     tiles, 4 waves of 128x128. A and B move from global memory
+//                     tiles, 8 waves of 128x64 (two per SIMD, so one wave's LDS
+//                     reads hide under the other's MFMAs). A and B move from global memory
 //                     straight into LDS (global_load_lds_dwordx4, no staging
 //                     registers) in the 1 KiB fragment-tile layout, so every wave
 //                     load and every fragment read is 1 KiB contiguous. A 4-deep ring
 //                     of 32-column stages keeps loads three stages ahead; one
-//                     barrier per stage; the next stage's fragments are read while
-//                     the current stage's 64 MFMAs run. Tiles are mapped XCD-aware so
+//                     barrier per stage. Tiles are mapped XCD-aware so
 //                     the m-tiles that share a weight tile run on one XCD's L2.
 //                     Mode GATEUP writes H = silu(G) * U (bf16), mode DOWN writes Y.
 //  ffn_f32_*          fp32 VALU path (one thread per output element) for fp32
@@ -151,12 +151,19 @@ __device__ __forceinline__ void barrier_no_fence() {
 constexpr int kStages = MOEFFN_GEMM_STAGES;  // LDS ring depth (BK = 32 per stage)
 constexpr int kStageBytes = 32768;    // A 256x32 + B 256x32 bf16
 
-struct Frags {
-  bf16x8_t a[8], b[8];
-};
+#ifndef MOEFFN_GEMM_WAVES
+#define MOEFFN_GEMM_WAVES 8
+#endif
+#ifndef MOEFFN_GEMM_FRAG_DB
+#define MOEFFN_GEMM_FRAG_DB (MOEFFN_GEMM_WAVES == 4)   // 8 waves: one fragment set (register budget)
+#endif
+constexpr int kGemmWaves = MOEFFN_GEMM_WAVES;   // 4: one wave per SIMD (128x128 each); 8: two (128x64)
+constexpr int kWaveN = 512 / kGemmWaves;        // wave tile columns: 128 or 64
+constexpr int kNB = kWaveN / 16;                // n-blocks per wave
+constexpr int kLoadBlocks = 16 / kGemmWaves;    // A (and B) blocks each wave loads per stage
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
+__global__ __launch_bounds__(64 * kGemmWaves, 1) void ffn_gemm_bf16(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages][kStageBytes];
   const int NT = p.N / kBN;
   int e, mt, nt;
@@ -169,88 +176,91 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
   const int KS = p.K / 32;  // stages of 32 columns
   const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
 
-  // This wave loads A blocks (m-blocks) and B blocks (n-blocks) w*4 .. w*4+3 of every
-  // stage. An A block is 16 rows x 32 columns; lane l fetches 16 bytes of row r = l/4, so
-  // each quad of lanes reads one row's 64 contiguous bytes. Chunk c of row r is stored at
-  // slot 4r + (c ^ g(r)) with g(r) = (r2 << 1) | (r1 ^ r3) (bits of r): the MFMA fragment
-  // reads (row l%16, chunk l/16) then touch distinct 16-byte bank groups within every
-  // group of 8 lanes and within every group of 16 lanes.
-  const bf16_t* arow[4];
-  const char* bptr[4];
+  // This wave loads A blocks (m-blocks) and B blocks (n-blocks) w*L .. w*L+L-1 of every
+  // stage (L = kLoadBlocks). An A block is 16 rows x 32 columns; lane l fetches 16 bytes
+  // of row r = l/4, so each quad of lanes reads one row's 64 contiguous bytes. Chunk c of
+  // row r is stored at slot 4r + (c ^ g(r)) with g(r) = (r2 << 1) | (r1 ^ r3) (bits of r):
+  // the MFMA fragment reads (row l%16, chunk l/16) then touch distinct 16-byte bank groups
+  // within every group of 8 lanes and within every group of 16 lanes.
+  const bf16_t* arow[kLoadBlocks];
+  const char* bptr[kLoadBlocks];
   auto swz = [](int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); };
   const int a_chunk = (lane & 3) ^ swz(lane >> 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = row0 + (w * 4 + i) * 16 + (lane >> 2);
+  for (int i = 0; i < kLoadBlocks; ++i) {
+    int r = row0 + (w * kLoadBlocks + i) * 16 + (lane >> 2);
     r = r < row_end ? r : row_end - 1;
     const int src = p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
     arow[i] = p.a + (size_t)src * p.K + 8 * a_chunk;
-    bptr[i] = B + ((int64_t)(n0 / 16 + w * 4 + i) * KS) * 1024 + 16 * lane;
+    bptr[i] = B + ((int64_t)(n0 / 16 + w * kLoadBlocks + i) * KS) * 1024 + 16 * lane;
   }
   auto issue = [&](int s) {
     char* base = smem[s % kStages];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(arow[i] + s * 32, base + (w * 4 + i) * 1024);
+    for (int i = 0; i < kLoadBlocks; ++i) dma16(arow[i] + s * 32, base + (w * kLoadBlocks + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(bptr[i] + (int64_t)s * 1024, base + 16384 + (w * 4 + i) * 1024);
+    for (int i = 0; i < kLoadBlocks; ++i)
+      dma16(bptr[i] + (int64_t)s * 1024, base + 16384 + (w * kLoadBlocks + i) * 1024);
   };
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w & 1, wn = w >> 1;   // 2 wave rows of 128 x kGemmWaves/2 wave columns
   const int a_slot = 16 * (4 * (lane & 15) + ((lane >> 4) ^ swz(lane & 15)));  // row l%16, chunk l/16
+  struct Frags {
+    bf16x8_t a[8], b[kNB];
+  };
   auto read = [&](Frags& f, int s) {
     const char* base = smem[s % kStages];
 #pragma unroll
     for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * 8 + i) * 1024 + a_slot);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      f.b[j] = *reinterpret_cast<const bf16x8_t*>(base + 16384 + (wn * 8 + j) * 1024 + 16 * lane);
+    for (int j = 0; j < kNB; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8_t*>(base + 16384 + (wn * kNB + j) * 1024 + 16 * lane);
   };
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][kNB];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // The MFMAs are written as inline assembly with the accumulators pinned to AGPRs: with
-  // the builtin, the register allocator rotates the 64 loop-carried accumulator tiles
-  // between registers at the loop back-edge, and the copies (plus their hazard NOPs) cost
-  // about a third of the MFMA issue rate.
+  // the builtin, the register allocator rotates the loop-carried accumulator tiles between
+  // registers at the loop back-edge, and the copies (plus their hazard NOPs) cost about a
+  // third of the MFMA issue rate.
   auto mma = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < kNB; ++j)
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(f.a[i]), "v"(f.b[j]));
   };
-  // wait until at most n of this wave's DMA instructions are outstanding (n = 16, 8 or 0)
+  // wait until at most n of this wave's DMA instructions are outstanding
   auto wait_dma = [&](int n) {
     if (n >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
     else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
     else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
+  constexpr int kDmaPerStage = 2 * kLoadBlocks;
 
-  // prologue: stages 0..3 in flight, stage 0 visible, its fragments in registers
+  // prologue: the first stages in flight, stage 0 visible, its fragments in registers
   for (int s = 0; s < kStages && s < KS; ++s) issue(s);
-  wait_dma(8 * (min(KS, kStages) - 1));
+  wait_dma(kDmaPerStage * (min(KS, kStages) - 1));
   barrier_no_fence();
   Frags f0, f1;
   read(f0, 0);
 
   // iteration s: stage s+1 becomes visible, stage s+kStages is issued into the buffer
   // stage s used, the fragments of stage s+1 are read while the MFMAs of stage s run.
+#if MOEFFN_GEMM_FRAG_DB
   auto step = [&](int s, Frags& cur, Frags& nxt) {
-    wait_dma(8 * (min(KS - 1, s + kStages - 1) - (s + 1)));
+    wait_dma(kDmaPerStage * (min(KS - 1, s + kStages - 1) - (s + 1)));
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier_no_fence();
     if (s + kStages < KS) issue(s + kStages);
     if (s + 1 < KS) read(nxt, s + 1);
     mma(cur);
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // four MFMAs
-    }
   };
   int s = 0;
   for (; s + 1 < KS; s += 2) {
@@ -258,6 +268,20 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
     step(s + 1, f1, f0);
   }
   if (s < KS) step(s, f0, f1);
+#else
+  // single fragment buffer: the other wave on the SIMD covers the LDS read latency
+  (void)f1;
+  for (int s = 0; s < KS; ++s) {
+    if (s > 0) {
+      wait_dma(kDmaPerStage * (min(KS - 1, s + kStages - 2) - s));
+      barrier_no_fence();
+      if (s + kStages - 1 < KS) issue(s + kStages - 1);
+      read(f0, s);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    mma(f0);
+  }
+#endif
   // the last MFMAs must retire before their accumulators are read (the hazard
   // recognizer does not see inside the inline assembly)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -270,8 +294,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int hcol = n0 / 2 + wn * 64 + pp * 16 + (lane & 15);
+      for (int pp = 0; pp < kNB / 2; ++pp) {
+        const int hcol = n0 / 2 + wn * (kWaveN / 2) + pp * 16 + (lane & 15);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rbase + i * 16 + q;
@@ -286,8 +310,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_bf16(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+      for (int j = 0; j < kNB; ++j) {
+        const int col = n0 + wn * kWaveN + j * 16 + (lane & 15);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rbase + i * 16 + q;
@@ -343,11 +367,21 @@ struct DecodeArgs {
   int out_dtype;
 };
 
-constexpr int kDecChunk = 8;   // k-tiles whose loads are issued together
+#ifndef MOEFFN_DEC_CHUNK
+#define MOEFFN_DEC_CHUNK 4
+#endif
+#ifndef MOEFFN_DEC_WAVES
+#define MOEFFN_DEC_WAVES 8
+#endif
+#ifndef MOEFFN_DEC_MINBLOCKS
+#define MOEFFN_DEC_MINBLOCKS 1
+#endif
+constexpr int kDecChunk = MOEFFN_DEC_CHUNK;   // k-tiles whose loads are issued together
+constexpr int kDecWaves = MOEFFN_DEC_WAVES;   // waves per workgroup (split-K)
 
 template <int MODE>
-__global__ __launch_bounds__(256) void ffn_decode_bf16(DecodeArgs p) {
-  __shared__ f32x4_t red[3][4][2][64];   // partials of waves 1..3: [wave][m-block][n-tile][lane]
+__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(DecodeArgs p) {
+  __shared__ f32x4_t red[kDecWaves - 1][4][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
   const int G = p.N / 32;
   const int i = blockIdx.x / G, g = blockIdx.x % G;
   if (i >= p.active[0]) return;
@@ -356,7 +390,7 @@ __global__ __launch_bounds__(256) void ffn_decode_bf16(DecodeArgs p) {
   const int n_e = p.offsets[e + 1] - row0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int KT = p.K / 32;
-  const int kt0 = (KT * w) / 4, kt1 = (KT * (w + 1)) / 4;
+  const int kt0 = (KT * w) / kDecWaves, kt1 = (KT * (w + 1)) / kDecWaves;
   const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
   const char* b0 = B + ((int64_t)(2 * g) * KT) * 1024 + 16 * lane;      // n-tile 2g
   const char* b1 = B + ((int64_t)(2 * g + 1) * KT) * 1024 + 16 * lane;  // n-tile 2g+1
@@ -411,8 +445,7 @@ __global__ __launch_bounds__(256) void ffn_decode_bf16(DecodeArgs p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         if (m >= mbn) continue;
-#pragma unroll
-        for (int ww = 0; ww < 3; ++ww) {
+        for (int ww = 0; ww < kDecWaves - 1; ++ww) {
           acc[m][0] += red[ww][m][0][lane];
           acc[m][1] += red[ww][m][1][lane];
         }
@@ -828,7 +861,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
       q.out = H;
       q.out_dtype = MOE_BF16;
       prof_mark(s, MOE_PROF_DEC_GATEUP, false);
-      hipLaunchKernelGGL(ffn_decode_bf16<MODE_GATEUP>, dim3(max_active * (q.N / 32)), dim3(256), 0, s, q);
+      hipLaunchKernelGGL(ffn_decode_bf16<MODE_GATEUP>, dim3(max_active * (q.N / 32)), dim3(64 * kDecWaves), 0, s, q);
       prof_mark(s, MOE_PROF_DEC_GATEUP, true);
       q.a = H;
       q.a_row_src = nullptr;
@@ -839,7 +872,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
       q.out = y;
       q.out_dtype = y_dtype;
       prof_mark(s, MOE_PROF_DEC_DOWN, false);
-      hipLaunchKernelGGL(ffn_decode_bf16<MODE_DOWN>, dim3(max_active * (q.N / 32)), dim3(256), 0, s, q);
+      hipLaunchKernelGGL(ffn_decode_bf16<MODE_DOWN>, dim3(max_active * (q.N / 32)), dim3(64 * kDecWaves), 0, s, q);
       prof_mark(s, MOE_PROF_DEC_DOWN, true);
       return check_launch("moe_grouped_ffn bf16 decode");
     }
@@ -864,7 +897,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.out_dtype = MOE_BF16;
     long long nblk = (long long)max_mt * (p.N / kBN);
     prof_mark(s, MOE_PROF_GATEUP, false);
-    hipLaunchKernelGGL(ffn_gemm_bf16<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(ffn_gemm_bf16<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(64 * kGemmWaves), 0, s, p);
     prof_mark(s, MOE_PROF_GATEUP, true);
     // down: B = W_dn [d, F], A = H (already in row order)
     p.a = H;
@@ -877,7 +910,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.out_dtype = y_dtype;
     nblk = (long long)max_mt * (p.N / kBN);
     prof_mark(s, MOE_PROF_DOWN, false);
-    hipLaunchKernelGGL(ffn_gemm_bf16<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(ffn_gemm_bf16<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(64 * kGemmWaves), 0, s, p);
     prof_mark(s, MOE_PROF_DOWN, true);
     return check_launch("moe_grouped_ffn bf16");
   }
