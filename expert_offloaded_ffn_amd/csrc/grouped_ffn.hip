@@ -20,6 +20,8 @@
 //                     Mode GATEUP writes H = silu(G) * U (bf16), mode DOWN writes Y.
 //  ffn_f32_*          fp32 VALU path (one thread per output element) for fp32
 //                     weights.
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moeffn {
@@ -59,12 +61,16 @@ __host__ __device__ inline BundleGeom bundle_geom(int d, int F, int dt) {
 // tile_prefix[e] = m-tiles of active experts before e; tile_prefix[E] = total.
 __global__ __launch_bounds__(1024) void ffn_tile_map(const int32_t* __restrict__ offsets,
                                                      const int32_t* __restrict__ slot_of_expert,
-                                                     int32_t* __restrict__ tile_prefix, int E, int bm) {
+                                                     int32_t* __restrict__ tile_prefix, int E, int bm, int tall,
+                                                     int32_t* __restrict__ counters, int n_counters) {
   __shared__ int32_t v[kMaxE];
   const int e = threadIdx.x;
+  if (e < n_counters) counters[e] = 0;
   if (e < E) {
     const int n = offsets[e + 1] - offsets[e];
-    v[e] = (n > 0 && slot_of_expert[e] >= 0) ? (n + bm - 1) / bm : 0;
+    // m-tiles of bm rows; the last one may hold up to bm + tall rows
+    const int m = n <= bm + tall ? 1 : (n - tall + bm - 1) / bm;
+    v[e] = (n > 0 && slot_of_expert[e] >= 0) ? m : 0;
   }
   __syncthreads();
   if (e == 0) {
@@ -84,6 +90,7 @@ struct GemmArgs {
   const int32_t* offsets;      // [E+1]
   const int32_t* slot_of_expert;
   const int32_t* tile_prefix;  // [E+1]
+  int32_t* counters;           // [8] tiles taken from each XCD's range (zeroed by ffn_tile_map)
   const char* pool;
   int64_t slot_stride;
   int64_t b_off;               // byte offset of B inside a bundle
@@ -95,34 +102,63 @@ struct GemmArgs {
 
 enum { MODE_GATEUP = 0, MODE_DOWN = 1 };
 
-// Map a block to (expert, m-tile, n-tile). Returns false when the block has no tile.
-__device__ __forceinline__ bool decode_tile(const GemmArgs& p, int NT, int& e, int& mt, int& nt) {
-  const int E = p.E;
-  const int total = p.tile_prefix[E] * NT;
-  const int total_pad = (total + 7) & ~7;
-  const int b = blockIdx.x;
-  if (b >= total_pad) return false;
-  const int L = (b & 7) * (total_pad >> 3) + (b >> 3);  // consecutive tiles on one XCD
-  if (L >= total) return false;
+// Tile L of a launch -> (expert e, m-tile mt of mte, n-tile nt). Tiles run expert by
+// expert; within an expert the m-tiles of one n-tile are adjacent, so the tiles that
+// share a weight tile are taken close together in time by the same XCD.
+__device__ __forceinline__ void tile_coords(const int32_t* tile_prefix, int E, int NT, int L, int& e, int& mt,
+                                            int& mte, int& nt) {
   const int q = L / NT;
   int lo = 0, hi = E - 1;  // last e with tile_prefix[e] <= q
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.tile_prefix[mid] <= q) lo = mid;
+    if (tile_prefix[mid] <= q) lo = mid;
     else hi = mid - 1;
   }
   e = lo;
-  const int base = p.tile_prefix[e];
-  const int mte = p.tile_prefix[e + 1] - base;
+  const int base = tile_prefix[e];
+  mte = tile_prefix[e + 1] - base;
   const int local = L - base * NT;
-#if MOEFFN_TILE_ORDER == 0
   nt = local / mte;
   mt = local % mte;
-#else
-  mt = local / NT;
-  nt = local % NT;
-#endif
+}
+
+// One tile per block. Workgroups are dealt round-robin over the 8 XCDs, so block b runs
+// on XCD b % 8; tile L = (b % 8) * total/8 + b / 8 gives each XCD a contiguous run of
+// tiles (shared weight tiles stay in that XCD's L2). Returns false when the block has no
+// tile.
+__device__ __forceinline__ bool decode_tile(const int32_t* tile_prefix, int E, int NT, int& e, int& mt, int& mte,
+                                            int& nt) {
+  const int total = tile_prefix[E] * NT;
+  const int total_pad = (total + 7) & ~7;
+  const int b = blockIdx.x;
+  if (b >= total_pad) return false;
+  const int L = (b & 7) * (total_pad >> 3) + (b >> 3);
+  if (L >= total) return false;
+  tile_coords(tile_prefix, E, NT, L, e, mt, mte, nt);
   return true;
+}
+
+// Persistent blocks (one per CU) take tiles from per-XCD queues. The tiles are cut into 8
+// contiguous ranges, one per XCD; block b (on XCD b % 8) takes the next tile of its own
+// XCD's range with an atomic counter and, once that range is used up, of the other ranges
+// in turn. Work moves to whichever CU is free, so tiles of unequal cost (an expert's
+// taller last m-tile) and XCDs with more of them do not leave CUs idle. Returns -1 when
+// every range is used up; each counter is visited at most once more per block after it
+// runs out, so every block reaches that exit.
+__device__ __forceinline__ int take_tile(int32_t* counters, int total, int& range) {
+  const int per = (total + 7) >> 3;
+  const int xcd = blockIdx.x & 7;
+  while (range < 8) {
+    const int x = (xcd + range) & 7;
+    const int lo = x * per;
+    const int n = min(per, total - lo);
+    if (n > 0) {
+      const int i = atomicAdd(counters + x, 1);
+      if (i < n) return lo + i;
+    }
+    ++range;
+  }
+  return -1;
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -131,6 +167,14 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 // 16 bytes per lane from global straight into LDS at lds_base + 16 * lane.
 __device__ __forceinline__ void dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// The same transfer issued as inline assembly. The compiler then does not track the LDS
+// write, so it adds no "vmcnt(0)" before later LDS reads; the caller orders them with
+// explicit vmcnt waits and barriers. lds_base must be wave-uniform.
+__device__ __forceinline__ void dma16_asm(const void* g, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
 // Workgroup barrier without the release fence __syncthreads() carries: that fence
@@ -142,160 +186,144 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
+// Wait until at most n of this wave's vector-memory instructions (here: LDS DMA) are
+// outstanding; n is rounded down to an available immediate, which only waits longer.
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (n >= 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 15) asm volatile("s_waitcnt vmcnt(15)" ::: "memory");
+  else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (n >= 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 #ifndef MOEFFN_GEMM_STAGES
 #define MOEFFN_GEMM_STAGES 4
 #endif
-#ifndef MOEFFN_TILE_ORDER
-#define MOEFFN_TILE_ORDER 0   // 0: per expert, n-tile major (m-tiles of one weight tile adjacent)
+// An expert's last m-tile holds up to kBM + kTallRows rows, so a group of n rows takes
+// ceil((n - kTallRows) / kBM) tiles instead of ceil(n / kBM): a few rows past a multiple
+// of kBM ride along in the last tile rather than costing a whole pass over the weights.
+#ifndef MOEFFN_TALL_ROWS
+#define MOEFFN_TALL_ROWS 64
 #endif
-constexpr int kStages = MOEFFN_GEMM_STAGES;  // LDS ring depth (BK = 32 per stage)
-constexpr int kStageBytes = 32768;    // A 256x32 + B 256x32 bf16
-
-#ifndef MOEFFN_GEMM_WAVES
-#define MOEFFN_GEMM_WAVES 8
+constexpr int kTallRows = MOEFFN_TALL_ROWS;
+#ifndef MOEFFN_ACC
+#define MOEFFN_ACC(x) "+v"(x)
 #endif
-#ifndef MOEFFN_GEMM_FRAG_DB
-#define MOEFFN_GEMM_FRAG_DB (MOEFFN_GEMM_WAVES == 4)   // 8 waves: one fragment set (register budget)
-#endif
-constexpr int kGemmWaves = MOEFFN_GEMM_WAVES;   // 4: one wave per SIMD (128x128 each); 8: two (128x64)
-constexpr int kWaveN = 512 / kGemmWaves;        // wave tile columns: 128 or 64
-constexpr int kNB = kWaveN / 16;                // n-blocks per wave
-constexpr int kLoadBlocks = 16 / kGemmWaves;    // A (and B) blocks each wave loads per stage
+constexpr int kGemmWaves = 8;                 // 2 wave rows x 4 wave columns of 64
+constexpr int kStages = MOEFFN_GEMM_STAGES;   // LDS ring depth (BK = 32 per stage)
+constexpr int kStageA = (kBM + kTallRows) * 64;   // A: up to 320 rows x 32 bf16
+constexpr int kStageBytes = kStageA + kBN * 64;   // + B: 256 rows x 32 bf16 (36 KiB)
 
-template <int MODE>
-__global__ __launch_bounds__(64 * kGemmWaves, 1) void ffn_gemm_bf16(GemmArgs p) {
-  __shared__ __attribute__((aligned(1024))) char smem[kStages][kStageBytes];
-  const int NT = p.N / kBN;
-  int e, mt, nt;
-  if (!decode_tile(p, NT, e, mt, nt)) return;
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row0 = p.offsets[e] + mt * kBM;
-  const int row_end = p.offsets[e + 1];
-  const int n0 = nt * kBN;
+// One 256-column tile of B against a (256 or, on an expert's last m-tile, up to 320)-row
+// tile of A. TALL selects 10 instead of 8 m-blocks of 16 rows per wave.
+template <int MODE, bool TALL>
+__device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[kStageBytes], int e, int row0,
+                                               int row_end, int n0) {
+  constexpr int MB = TALL ? 10 : 8;   // m-blocks per wave
+  // the wave index is uniform across the wave: keep it (and what derives from it) scalar
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int KS = p.K / 32;  // stages of 32 columns
   const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
 
-  // This wave loads A blocks (m-blocks) and B blocks (n-blocks) w*L .. w*L+L-1 of every
-  // stage (L = kLoadBlocks). An A block is 16 rows x 32 columns; lane l fetches 16 bytes
-  // of row r = l/4, so each quad of lanes reads one row's 64 contiguous bytes. Chunk c of
+  // Per stage this wave loads A blocks 2w, 2w+1 (and 16 + w on a tall tile, waves 0-3)
+  // and B blocks 2w, 2w+1. An A block is 16 rows x 32 columns; lane l fetches 16 bytes of
+  // row r = l/4, so each quad of lanes reads one row's 64 contiguous bytes. Chunk c of
   // row r is stored at slot 4r + (c ^ g(r)) with g(r) = (r2 << 1) | (r1 ^ r3) (bits of r):
   // the MFMA fragment reads (row l%16, chunk l/16) then touch distinct 16-byte bank groups
   // within every group of 8 lanes and within every group of 16 lanes.
-  const bf16_t* arow[kLoadBlocks];
-  const char* bptr[kLoadBlocks];
+  const bool extra_a = TALL && w < 4;
+  const int dma_per_stage = 4 + (extra_a ? 1 : 0);
   auto swz = [](int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); };
   const int a_chunk = (lane & 3) ^ swz(lane >> 2);
-#pragma unroll
-  for (int i = 0; i < kLoadBlocks; ++i) {
-    int r = row0 + (w * kLoadBlocks + i) * 16 + (lane >> 2);
+  auto a_src = [&](int blk) {
+    int r = row0 + blk * 16 + (lane >> 2);
     r = r < row_end ? r : row_end - 1;
     const int src = p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
-    arow[i] = p.a + (size_t)src * p.K + 8 * a_chunk;
-    bptr[i] = B + ((int64_t)(n0 / 16 + w * kLoadBlocks + i) * KS) * 1024 + 16 * lane;
-  }
+    return p.a + (size_t)src * p.K + 8 * a_chunk;
+  };
+  // running source pointers, advanced one stage per issue (stages are issued in order);
+  // the DMA instructions take them as their address operands directly
+  const bf16_t* arow0 = a_src(2 * w);
+  const bf16_t* arow1 = a_src(2 * w + 1);
+  const bf16_t* arow2 = extra_a ? a_src(16 + w) : arow0;
+  const char* bptr0 = B + ((int64_t)(n0 / 16 + 2 * w) * KS) * 1024 + 16 * lane;
+  const char* bptr1 = bptr0 + (int64_t)KS * 1024;
   auto issue = [&](int s) {
     char* base = smem[s % kStages];
-#pragma unroll
-    for (int i = 0; i < kLoadBlocks; ++i) dma16(arow[i] + s * 32, base + (w * kLoadBlocks + i) * 1024);
-#pragma unroll
-    for (int i = 0; i < kLoadBlocks; ++i)
-      dma16(bptr[i] + (int64_t)s * 1024, base + 16384 + (w * kLoadBlocks + i) * 1024);
+    dma16_asm(arow0, base + (2 * w) * 1024);
+    dma16_asm(arow1, base + (2 * w + 1) * 1024);
+    if (extra_a) dma16_asm(arow2, base + (16 + w) * 1024);
+    dma16_asm(bptr0, base + kStageA + (2 * w) * 1024);
+    dma16_asm(bptr1, base + kStageA + (2 * w + 1) * 1024);
+    arow0 += 32;
+    arow1 += 32;
+    arow2 += 32;
+    bptr0 += 1024;
+    bptr1 += 1024;
   };
-  const int wm = w & 1, wn = w >> 1;   // 2 wave rows of 128 x kGemmWaves/2 wave columns
+  const int wm = w & 1, wn = w >> 1;   // wave row (MB m-blocks) x wave column (4 n-blocks)
   const int a_slot = 16 * (4 * (lane & 15) + ((lane >> 4) ^ swz(lane & 15)));  // row l%16, chunk l/16
-  struct Frags {
-    bf16x8_t a[8], b[kNB];
-  };
-  auto read = [&](Frags& f, int s) {
+  bf16x8_t fa[MB], fb[4];
+  auto read = [&](int s) {
     const char* base = smem[s % kStages];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) f.a[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * 8 + i) * 1024 + a_slot);
+    for (int i = 0; i < MB; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(base + (wm * MB + i) * 1024 + a_slot);
 #pragma unroll
-    for (int j = 0; j < kNB; ++j)
-      f.b[j] = *reinterpret_cast<const bf16x8_t*>(base + 16384 + (wn * kNB + j) * 1024 + 16 * lane);
+    for (int j = 0; j < 4; ++j)
+      fb[j] = *reinterpret_cast<const bf16x8_t*>(base + kStageA + (wn * 4 + j) * 1024 + 16 * lane);
   };
 
-  f32x4_t acc[8][kNB];
+  f32x4_t acc[MB][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // The MFMAs are written as inline assembly with the accumulators pinned to AGPRs: with
   // the builtin, the register allocator rotates the loop-carried accumulator tiles between
   // registers at the loop back-edge, and the copies (plus their hazard NOPs) cost about a
   // third of the MFMA issue rate.
-  auto mma = [&](const Frags& f) {
+  auto mma = [&]() {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < kNB; ++j)
-        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(f.a[i]), "v"(f.b[j]));
+      for (int j = 0; j < 4; ++j)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : MOEFFN_ACC(acc[i][j]) : "v"(fa[i]), "v"(fb[j]));
   };
-  // wait until at most n of this wave's DMA instructions are outstanding
-  auto wait_dma = [&](int n) {
-    if (n >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-  constexpr int kDmaPerStage = 2 * kLoadBlocks;
 
-  // prologue: the first stages in flight, stage 0 visible, its fragments in registers
-  for (int s = 0; s < kStages && s < KS; ++s) issue(s);
-  wait_dma(kDmaPerStage * (min(KS, kStages) - 1));
-  barrier_no_fence();
-  Frags f0, f1;
-  read(f0, 0);
-
-  // iteration s: stage s+1 becomes visible, stage s+kStages is issued into the buffer
-  // stage s used, the fragments of stage s+1 are read while the MFMAs of stage s run.
-#if MOEFFN_GEMM_FRAG_DB
-  auto step = [&](int s, Frags& cur, Frags& nxt) {
-    wait_dma(kDmaPerStage * (min(KS - 1, s + kStages - 1) - (s + 1)));
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    barrier_no_fence();
-    if (s + kStages < KS) issue(s + kStages);
-    if (s + 1 < KS) read(nxt, s + 1);
-    mma(cur);
-  };
-  int s = 0;
-  for (; s + 1 < KS; s += 2) {
-    step(s, f0, f1);
-    step(s + 1, f1, f0);
-  }
-  if (s < KS) step(s, f0, f1);
-#else
-  // single fragment buffer: the other wave on the SIMD covers the LDS read latency
-  (void)f1;
+  // prologue: the first kStages - 1 stages in flight. Iteration s: stage s is visible
+  // after the barrier, stage s + kStages - 1 goes into the buffer that stage s - 1 used
+  // (every wave is past its reads of it: they completed before the MFMAs of s - 1), the
+  // fragments of stage s are read, then its MFMAs issue. The other wave on the SIMD
+  // covers this wave's LDS read latency.
+  for (int s = 0; s < kStages - 1 && s < KS; ++s) issue(s);
   for (int s = 0; s < KS; ++s) {
-    if (s > 0) {
-      wait_dma(kDmaPerStage * (min(KS - 1, s + kStages - 2) - s));
-      barrier_no_fence();
-      if (s + kStages - 1 < KS) issue(s + kStages - 1);
-      read(f0, s);
-    }
+    wait_vmcnt_le(dma_per_stage * (min(KS - 1, s + kStages - 2) - s));
+    barrier_no_fence();
+    if (s + kStages - 1 < KS) issue(s + kStages - 1);
+    read(s);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    mma(f0);
+    mma();
   }
-#endif
   // the last MFMAs must retire before their accumulators are read (the hazard
   // recognizer does not see inside the inline assembly)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile
-  const int rbase = row0 + wm * 128 + 4 * (lane >> 4);
+  const int rbase = row0 + wm * MB * 16 + 4 * (lane >> 4);
   if constexpr (MODE == MODE_GATEUP) {
     const int F = p.N / 2;
     bf16_t* H = static_cast<bf16_t*>(p.out);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
-      for (int pp = 0; pp < kNB / 2; ++pp) {
-        const int hcol = n0 / 2 + wn * (kWaveN / 2) + pp * 16 + (lane & 15);
+      for (int pp = 0; pp < 2; ++pp) {
+        const int hcol = n0 / 2 + wn * 32 + pp * 16 + (lane & 15);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rbase + i * 16 + q;
@@ -308,10 +336,10 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void ffn_gemm_bf16(GemmArgs p) 
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MB; ++i) {
 #pragma unroll
-      for (int j = 0; j < kNB; ++j) {
-        const int col = n0 + wn * kWaveN + j * 16 + (lane & 15);
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rbase + i * 16 + q;
@@ -322,6 +350,31 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void ffn_gemm_bf16(GemmArgs p) 
         }
       }
     }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64 * kGemmWaves, 1) void ffn_gemm_bf16(GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kStages][kStageBytes];
+  __shared__ int s_tile;
+  const int NT = p.N / kBN;
+  const int total = p.tile_prefix[p.E] * NT;
+  int range = 0;   // thread 0: how many XCD ranges this block has used up
+  for (;;) {
+    if (threadIdx.x == 0) s_tile = take_tile(p.counters, total, range);
+    __syncthreads();
+    const int L = s_tile;
+    if (L < 0) return;
+    int e, mt, mte, nt;
+    tile_coords(p.tile_prefix, p.E, NT, L, e, mt, mte, nt);
+    const int row0 = p.offsets[e] + mt * kBM;
+    const int row_end = mt + 1 < mte ? row0 + kBM : p.offsets[e + 1];
+    if (kTallRows > 0 && row_end - row0 > kBM)
+      gemm_bf16_tile<MODE, (kTallRows > 0)>(p, smem, e, row0, row_end, nt * kBN);
+    else
+      gemm_bf16_tile<MODE, false>(p, smem, e, row0, row_end, nt * kBN);
+    // every wave is done with the LDS ring and has read s_tile before they are reused
+    __syncthreads();
   }
 }
 
@@ -507,30 +560,6 @@ struct Fp8Args {
   int E;
 };
 
-__device__ __forceinline__ bool decode_tile_prefix(const int32_t* tile_prefix, int E, int NT, int& e, int& mt,
-                                                   int& nt) {
-  const int total = tile_prefix[E] * NT;
-  const int total_pad = (total + 7) & ~7;
-  const int b = blockIdx.x;
-  if (b >= total_pad) return false;
-  const int L = (b & 7) * (total_pad >> 3) + (b >> 3);
-  if (L >= total) return false;
-  const int q = L / NT;
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tile_prefix[mid] <= q) lo = mid;
-    else hi = mid - 1;
-  }
-  e = lo;
-  const int base = tile_prefix[e];
-  const int mte = tile_prefix[e + 1] - base;
-  const int local = L - base * NT;
-  nt = local / mte;
-  mt = local % mte;
-  return true;
-}
-
 __device__ __forceinline__ void dma4(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
 }
@@ -540,8 +569,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
   __shared__ __attribute__((aligned(1024))) char smem[kF8Stages][kF8StageBytes];
   __shared__ float amax_x[2][kF8BM];
   const int NT = p.N / kF8BN;
-  int e, mt, nt;
-  if (!decode_tile_prefix(p.tile_prefix, p.E, NT, e, mt, nt)) return;
+  int e, mt, mte, nt;
+  if (!decode_tile(p.tile_prefix, p.E, NT, e, mt, mte, nt)) return;
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
@@ -760,6 +789,19 @@ __global__ __launch_bounds__(256) void ffn_f32_down(const float* __restrict__ H,
 
 // Workspace: H [rows, F] (fp32, bf16 or e4m3) [+ e4m3 H scales [rows, F/128]], then the
 // tile prefix and the active-expert list.
+// Compute units of the current device (cached per device).
+long long cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off,
                  size_t* hs_off = nullptr) {
   const size_t hsz = act_dtype == MOE_F32 ? 4 : act_dtype == MOE_FP8_E4M3 ? 1 : 2;
@@ -767,8 +809,8 @@ size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_o
   size_t end = align_up((size_t)rows * t->d_ff * hsz, 256);
   if (hs_off) *hs_off = end;
   if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)rows * (t->d_ff / 128) * 4, 256);
-  *map_off = end;
-  return *map_off + 2 * align_up((size_t)(t->n_experts + 2) * 4, 256);
+  *map_off = end;   // tile prefix [E+1], active list [E+1], work counters [16]
+  return *map_off + 2 * align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
 }
 
 }  // namespace
@@ -876,15 +918,18 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
       prof_mark(s, MOE_PROF_DEC_DOWN, true);
       return check_launch("moe_grouped_ffn bf16 decode");
     }
+    int32_t* counters = reinterpret_cast<int32_t*>(wsb + map_off + 2 * align_up((size_t)(E + 2) * 4, 256));
     hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
-                       tile_prefix, E, kBM);
+                       tile_prefix, E, kBM, kTallRows, counters, 16);
     const int max_mt = (rows + kBM - 1) / kBM + (E < rows ? E : rows);
+    const long long n_cu = cu_count();
     GemmArgs p{};
     p.a_row_src = a_row_src;
     p.a_row_div = a_row_div;
     p.offsets = offsets;
     p.slot_of_expert = t.slot_of_expert;
     p.tile_prefix = tile_prefix;
+    p.counters = counters;
     p.pool = static_cast<const char*>(t.pool);
     p.slot_stride = t.slot_stride;
     p.E = E;
@@ -895,7 +940,8 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.K = d;
     p.out = H;
     p.out_dtype = MOE_BF16;
-    long long nblk = (long long)max_mt * (p.N / kBN);
+    // persistent: at most one block per CU, a multiple of 8 (one per XCD in turn)
+    long long nblk = std::min((long long)max_mt * (p.N / kBN), n_cu);
     prof_mark(s, MOE_PROF_GATEUP, false);
     hipLaunchKernelGGL(ffn_gemm_bf16<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(64 * kGemmWaves), 0, s, p);
     prof_mark(s, MOE_PROF_GATEUP, true);
@@ -908,7 +954,8 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.K = F;
     p.out = y;
     p.out_dtype = y_dtype;
-    nblk = (long long)max_mt * (p.N / kBN);
+    p.counters = counters + 8;
+    nblk = std::min((long long)max_mt * (p.N / kBN), n_cu);
     prof_mark(s, MOE_PROF_DOWN, false);
     hipLaunchKernelGGL(ffn_gemm_bf16<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(64 * kGemmWaves), 0, s, p);
     prof_mark(s, MOE_PROF_DOWN, true);
@@ -927,7 +974,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     uint8_t* Hq = reinterpret_cast<uint8_t*>(wsb + h_off);
     float* Hs = reinterpret_cast<float*>(wsb + hs_off);
     hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
-                       tile_prefix, E, kF8BM);
+                       tile_prefix, E, kF8BM, 0, nullptr, 0);
     const int max_mt = (rows + kF8BM - 1) / kF8BM + (E < rows ? E : rows);
     Fp8Args p{};
     p.a = static_cast<const uint8_t*>(a);

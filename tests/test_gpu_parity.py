@@ -78,6 +78,16 @@ def test_bf16_layer_reduced(T, d, E, k, F):
     _run_and_check(cfg, layer, w, T)
 
 
+@pytest.mark.parametrize("T", [256, 257, 300, 320, 321, 1088, 1089])
+def test_bf16_last_tile_sizes(T):
+    """E=2, k=2: both experts get all T rows. Around 256 + 64 rows an expert's last m-tile
+    switches between one tile of up to 320 rows and an extra tile; every row is checked."""
+    cfg = synth.get_config("mixtral_prefill_bf16", T=T, d=256, E=2, k=2, F=512, name=f"lasttile_T{T}")
+    layer, w = _build(cfg)
+    g = _run_and_check(cfg, layer, w, T)
+    assert to_np(g["route"]["counts"]).tolist() == [T, T]
+
+
 def test_mixtral_full_size_sampled():
     cfg = synth.get_config("mixtral_prefill_bf16")
     layer, w = _build(cfg)
