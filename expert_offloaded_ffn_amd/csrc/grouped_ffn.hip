@@ -266,7 +266,10 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
     bptr0 += 1024;
     bptr1 += 1024;
   };
-  const int wm = w & 1, wn = w >> 1;   // wave row (MB m-blocks) x wave column (4 n-blocks)
+  // wave row wm (MB m-blocks) x wave column wn (4 n-blocks). Waves w and w + 4 share a
+  // SIMD; they form the two groups that take turns (see the main loop).
+  const int g = w >> 2;
+  const int wm = g, wn = w & 3;
   const int a_slot = 16 * (4 * (lane & 15) + ((lane >> 4) ^ swz(lane & 15)));  // row l%16, chunk l/16
   bf16x8_t fa[MB], fb[4];
   auto read = [&](int s) {
@@ -296,19 +299,32 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : MOEFFN_ACC(acc[i][j]) : "v"(fa[i]), "v"(fb[j]));
   };
 
-  // prologue: the first kStages - 1 stages in flight. Iteration s: stage s is visible
-  // after the barrier, stage s + kStages - 1 goes into the buffer that stage s - 1 used
-  // (every wave is past its reads of it: they completed before the MFMAs of s - 1), the
-  // fragments of stage s are read, then its MFMAs issue. The other wave on the SIMD
-  // covers this wave's LDS read latency.
+  // Main loop: the two wave groups take turns, phase by phase, with a barrier between
+  // phases. In the phase where group 0 reads the fragments of stage s (and issues the DMA
+  // of stage s + kStages - 1), group 1 runs the MFMAs of stage s - 1; in the next phase
+  // group 0 runs the MFMAs of stage s while group 1 reads stage s. So on every SIMD one
+  // wave keeps the matrix core busy while the other waits on LDS. Stage t's DMA goes into
+  // the buffer of stage t - kStages, which both groups finished reading two phases before;
+  // at the end of the phase before a stage is first read, every wave waits for its own
+  // part of that stage to land, and the barrier then makes it visible to all.
   for (int s = 0; s < kStages - 1 && s < KS; ++s) issue(s);
+  wait_vmcnt_le(dma_per_stage * min(KS - 1, kStages - 2));   // stage 0 has landed
+  barrier_no_fence();
+  if (g == 1) barrier_no_fence();   // group 1 sits out the first phase
   for (int s = 0; s < KS; ++s) {
-    wait_vmcnt_le(dma_per_stage * (min(KS - 1, s + kStages - 2) - s));
-    barrier_no_fence();
+    // read phase of stage s
     if (s + kStages - 1 < KS) issue(s + kStages - 1);
     read(s);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // DMA instructions this wave may leave in flight once stage s + 1 has landed
+    const int vm_left = dma_per_stage * (min(KS - 1, s + kStages - 1) - (s + 1));
+    if (g == 1 && s + 1 < KS) wait_vmcnt_le(vm_left);
+    barrier_no_fence();
+    // multiply phase of stage s
     mma();
+    if (g == 0 && s + 1 < KS) wait_vmcnt_le(vm_left);
+    // group 1's last multiply phase needs no closing barrier: group 0 has left the loop
+    if (g == 0 || s + 1 < KS) barrier_no_fence();
   }
   // the last MFMAs must retire before their accumulators are read (the hazard
   // recognizer does not see inside the inline assembly)
