@@ -201,6 +201,11 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 #ifndef MOEFFN_GEMM_STAGES
 #define MOEFFN_GEMM_STAGES 4
 #endif
@@ -299,32 +304,43 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : MOEFFN_ACC(acc[i][j]) : "v"(fa[i]), "v"(fb[j]));
   };
 
-  // Main loop: the two wave groups take turns, phase by phase, with a barrier between
-  // phases. In the phase where group 0 reads the fragments of stage s (and issues the DMA
-  // of stage s + kStages - 1), group 1 runs the MFMAs of stage s - 1; in the next phase
-  // group 0 runs the MFMAs of stage s while group 1 reads stage s. So on every SIMD one
-  // wave keeps the matrix core busy while the other waits on LDS. Stage t's DMA goes into
-  // the buffer of stage t - kStages, which both groups finished reading two phases before;
-  // at the end of the phase before a stage is first read, every wave waits for its own
-  // part of that stage to land, and the barrier then makes it visible to all.
-  for (int s = 0; s < kStages - 1 && s < KS; ++s) issue(s);
-  wait_vmcnt_le(dma_per_stage * min(KS - 1, kStages - 2));   // stage 0 has landed
+  // Main loop, one barrier per stage. Between barrier s and barrier s + 1, group 0 runs
+  // the MFMAs of stage s and then reads the fragments of stage s + 1, while group 1 reads
+  // stage s and then runs its MFMAs; group 0 raises its wave priority for its MFMA burst,
+  // so on every SIMD the two bursts follow each other and each group's LDS reads overlap
+  // the other group's MFMAs. Stages s and s + 1 are read between barriers s and s + 1, so
+  // the DMA of stage s + 3 (issued then) goes into the buffer of stage s - 1, which both
+  // groups finished reading before barrier s. Before barrier s + 1 every wave waits for
+  // its own part of stage s + 2 to land, and the barrier makes it visible to all.
+  static_assert(kStages == 4, "the schedule below keeps stages s - 1 .. s + 2 in the ring");
+  constexpr int kDmaG0 = TALL ? 5 : 4;   // DMA instructions per stage of a group-0 wave
+  for (int s = 0; s < 3 && s < KS; ++s) issue(s);
+  wait_vmcnt_le(dma_per_stage * min(KS - 1, 2));   // stage 0 has landed
   barrier_no_fence();
-  if (g == 1) barrier_no_fence();   // group 1 sits out the first phase
-  for (int s = 0; s < KS; ++s) {
-    // read phase of stage s
-    if (s + kStages - 1 < KS) issue(s + kStages - 1);
-    read(s);
+  if (g == 0) {
+    read(0);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // DMA instructions this wave may leave in flight once stage s + 1 has landed
-    const int vm_left = dma_per_stage * (min(KS - 1, s + kStages - 1) - (s + 1));
-    if (g == 1 && s + 1 < KS) wait_vmcnt_le(vm_left);
-    barrier_no_fence();
-    // multiply phase of stage s
-    mma();
-    if (g == 0 && s + 1 < KS) wait_vmcnt_le(vm_left);
-    // group 1's last multiply phase needs no closing barrier: group 0 has left the loop
-    if (g == 0 || s + 1 < KS) barrier_no_fence();
+  }
+  if (KS > 1) wait_vmcnt_le(dma_per_stage * (min(KS - 1, 2) - 1));   // stage 1 has landed
+  barrier_no_fence();
+  // (one code path for both groups, so a single set of fragment registers is live)
+  for (int s = 0; s < KS; ++s) {
+    if (g == 0) {
+      __builtin_amdgcn_s_setprio(1);
+      mma();
+      __builtin_amdgcn_s_setprio(0);
+    }
+    if (s + 3 < KS) issue(s + 3);
+    if (s + 1 - g < KS) read(s + 1 - g);   // group 0 reads stage s + 1, group 1 stage s
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (g == 1) mma();
+    if (s + 3 < KS) {
+      if (g == 0) wait_vmcnt<kDmaG0>();
+      else wait_vmcnt<4>();
+    } else if (s + 2 < KS) {
+      wait_vmcnt<0>();
+    }
+    if (s + 1 < KS) barrier_no_fence();
   }
   // the last MFMAs must retire before their accumulators are read (the hazard
   // recognizer does not see inside the inline assembly)
