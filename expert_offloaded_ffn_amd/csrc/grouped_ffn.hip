@@ -122,24 +122,10 @@ __device__ __forceinline__ void tile_coords(const int32_t* tile_prefix, int E, i
   mt = local % mte;
 }
 
-// One tile per block. Workgroups are dealt round-robin over the 8 XCDs, so block b runs
-// on XCD b % 8; tile L = (b % 8) * total/8 + b / 8 gives each XCD a contiguous run of
-// tiles (shared weight tiles stay in that XCD's L2). Returns false when the block has no
-// tile.
-__device__ __forceinline__ bool decode_tile(const int32_t* tile_prefix, int E, int NT, int& e, int& mt, int& mte,
-                                            int& nt) {
-  const int total = tile_prefix[E] * NT;
-  const int total_pad = (total + 7) & ~7;
-  const int b = blockIdx.x;
-  if (b >= total_pad) return false;
-  const int L = (b & 7) * (total_pad >> 3) + (b >> 3);
-  if (L >= total) return false;
-  tile_coords(tile_prefix, E, NT, L, e, mt, mte, nt);
-  return true;
-}
-
-// Persistent blocks (one per CU) take tiles from per-XCD queues. The tiles are cut into 8
-// contiguous ranges, one per XCD; block b (on XCD b % 8) takes the next tile of its own
+// Persistent blocks (one per CU) take tiles from per-XCD queues. Workgroups are dealt
+// round-robin over the 8 XCDs, so block b runs on XCD b % 8. The tiles are cut into 8
+// contiguous ranges, one per XCD (tiles that share a weight tile stay in one XCD's L2);
+// block b takes the next tile of its own
 // XCD's range with an atomic counter and, once that range is used up, of the other ranges
 // in turn. Work moves to whichever CU is free, so tiles of unequal cost (an expert's
 // taller last m-tile) and XCDs with more of them do not leave CUs idle. Returns -1 when
@@ -571,6 +557,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
 // layout), the 128 row scales of the stage's block.
 
 constexpr int kF8BM = 128, kF8BN = 256, kF8Stages = 3;
+constexpr int kF8MaxKB = 128;   // K up to 16384 (weight scales of a tile are staged in LDS)
 constexpr int kF8A = 0, kF8B = 16384, kF8S = 49152, kF8StageBytes = 50176;
 
 struct Fp8Args {
@@ -581,6 +568,7 @@ struct Fp8Args {
   const int32_t* offsets;
   const int32_t* slot_of_expert;
   const int32_t* tile_prefix;
+  int32_t* counters;           // [8] per-XCD tile counters (zeroed by ffn_tile_map)
   const char* pool;
   int64_t slot_stride;
   int64_t b_off;
@@ -592,26 +580,41 @@ struct Fp8Args {
   int E;
 };
 
-__device__ __forceinline__ void dma4(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 4, 0, 0);
+// 4 bytes per lane from global into LDS at lds_base + 4 * lane, as inline assembly (see
+// dma16_asm). lds_base must be wave-uniform.
+__device__ __forceinline__ void dma4_asm(const void* g, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
+// One 128 x 256 tile. The weight block scales this tile needs (two per 128-column stage)
+// are staged in LDS first (s_wscale), so the main loop issues no global loads of its own
+// besides the DMA ring.
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
-  __shared__ __attribute__((aligned(1024))) char smem[kF8Stages][kF8StageBytes];
-  __shared__ float amax_x[2][kF8BM];
-  const int NT = p.N / kF8BN;
-  int e, mt, mte, nt;
-  if (!decode_tile(p.tile_prefix, p.E, NT, e, mt, mte, nt)) return;
-
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8StageBytes],
+                                              float (*amax_x)[kF8BM], float (*s_wscale)[kF8MaxKB], int e, int row0,
+                                              int row_end, int n0) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 1, wn = w & 1;
-  const int row0 = p.offsets[e] + mt * kF8BM;
-  const int row_end = p.offsets[e + 1];
-  const int n0 = nt * kF8BN;
   const int KB = p.K / 128;
   const char* bundle = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride;
   const char* B = bundle + p.b_off;
+  // GATEUP: [0] gate and [1] up scales of the tile's 128 hidden rows; DOWN: the scales of
+  // the tile's two 128-column blocks (wave column wn uses [wn])
+  for (int i = threadIdx.x; i < 2 * KB; i += blockDim.x) {
+    const int which = i / KB, s = i - which * KB;
+    const float* grid;
+    int blk;
+    if constexpr (MODE == MODE_GATEUP) {
+      grid = reinterpret_cast<const float*>(bundle + (which ? p.s_off1 : p.s_off0));
+      blk = n0 / 256;
+    } else {
+      grid = reinterpret_cast<const float*>(bundle + p.s_off0);
+      blk = n0 / 128 + which;
+    }
+    s_wscale[which][s] = grid[blk * KB + s];
+  }
+  __syncthreads();
   auto f = [](int r) { return ((r >> 1) + 4 * (r & 1)) & 7; };
   auto src_row = [&](int r) {
     r = r < row_end ? r : row_end - 1;
@@ -634,13 +637,13 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
   auto issue = [&](int s) {
     char* base = smem[s % kF8Stages];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dma16(aptr[t] + s * 128, base + kF8A + (4 * w + t) * 1024);
+    for (int t = 0; t < 4; ++t) dma16_asm(aptr[t] + s * 128, base + kF8A + (4 * w + t) * 1024);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        dma16(bptr + ((int64_t)i * KB + s) * 2048 + h * 1024, base + kF8B + (w * 4 + i) * 2048 + h * 1024);
-    dma4(sptr + s, base + kF8S + w * 256);
+        dma16_asm(bptr + ((int64_t)i * KB + s) * 2048 + h * 1024, base + kF8B + (w * 4 + i) * 2048 + h * 1024);
+    dma4_asm(sptr + s, base + kF8S + w * 256);
   };
   auto wait_dma = [&](bool more) {
     if (more) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
@@ -657,7 +660,6 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
   const int ar = lane & 15, ac = 2 * (lane >> 4);
   const int a_off0 = 16 * (8 * ar + ((ac + 0) ^ f(ar)));
   const int a_off1 = 16 * (8 * ar + ((ac + 1) ^ f(ar)));
-  const int nt16_0 = n0 / 16 + wn * 8;
 
   issue(0);
   if (KB > 1) issue(1);
@@ -675,29 +677,30 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
       const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + a_off1);
       fa[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    f32x4_t sa[4];
+    // combined scales: row scale x weight scale, [m-block][gate/up (GATEUP) or 0 (DOWN)]
+    f32x4_t sc[4][2];
+    {
+      const float sw0 = s_wscale[MODE == MODE_GATEUP ? 0 : wn][s];
+      const float sw1 = s_wscale[MODE == MODE_GATEUP ? 1 : wn][s];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sa[i] = *reinterpret_cast<const f32x4_t*>(base + kF8S + 4 * ((wm * 4 + i) * 16 + 4 * (lane >> 4)));
+      for (int i = 0; i < 4; ++i) {
+        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(base + kF8S + 4 * ((wm * 4 + i) * 16 + 4 * (lane >> 4)));
+        sc[i][0] = sa * sw0;
+        sc[i][1] = sa * sw1;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const char* blk = base + kF8B + (wn * 8 + j) * 2048 + 16 * lane;
       const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
       const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
       const i32x8_t fb = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      const int nt16 = nt16_0 + j;
-      float sw;
-      if constexpr (MODE == MODE_GATEUP) {
-        const float* grid = reinterpret_cast<const float*>(bundle + ((nt16 & 1) ? p.s_off1 : p.s_off0));
-        sw = grid[(nt16 >> 4) * KB + s];
-      } else {
-        sw = reinterpret_cast<const float*>(bundle + p.s_off0)[(nt16 >> 3) * KB + s];
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb, f32x4_t{0.f, 0.f, 0.f, 0.f},
                                                                               0, 0, 0, 127, 0, 127);
-        acc[i][j] += part * (sa[i] * sw);
+        // gate/up rows alternate every 16 (n-block parity); down: one scale block per wave column
+        acc[i][j] += part * sc[i][MODE == MODE_GATEUP ? (j & 1) : 0];
       }
     }
   }
@@ -764,6 +767,29 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
           }
         }
       }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
+  __shared__ __attribute__((aligned(1024))) char smem[kF8Stages][kF8StageBytes];
+  __shared__ float amax_x[2][kF8BM];
+  __shared__ float s_wscale[2][kF8MaxKB];
+  __shared__ int s_tile;
+  const int NT = p.N / kF8BN;
+  const int total = p.tile_prefix[p.E] * NT;
+  int range = 0;   // thread 0: XCD ranges this block has used up
+  for (;;) {
+    if (threadIdx.x == 0) s_tile = take_tile(p.counters, total, range);
+    __syncthreads();
+    const int L = s_tile;
+    if (L < 0) return;
+    int e, mt, mte, nt;
+    tile_coords(p.tile_prefix, p.E, NT, L, e, mt, mte, nt);
+    const int row0 = p.offsets[e] + mt * kF8BM;
+    gemm_fp8_tile<MODE>(p, smem, amax_x, s_wscale, e, row0, p.offsets[e + 1], nt * kF8BN);
+    // every wave is done with the ring, the scale and amax arrays, and has read s_tile
+    __syncthreads();
   }
 }
 
@@ -999,15 +1025,19 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
   MOE_REQUIRE((2 * F) % kF8BN == 0 && d % kF8BN == 0 && d % 128 == 0 && F % 128 == 0, MOE_EUNSUPPORTED,
               "moe_grouped_ffn: fp8 tiles need d and 2F multiples of %d and F a multiple of 128", kF8BN);
   MOE_REQUIRE(aligned(a_scale, 4), MOE_EINVAL, "moe_grouped_ffn: a_scale must be 4-byte aligned");
+  MOE_REQUIRE(d / 128 <= kF8MaxKB && F / 128 <= kF8MaxKB, MOE_EUNSUPPORTED,
+              "moe_grouped_ffn: fp8 tiles need d and F at most %d", 128 * kF8MaxKB);
   {
     size_t hs_off;
     ws_layout(&t, rows, act_dtype, &h_off, &map_off, &hs_off);
     int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
     uint8_t* Hq = reinterpret_cast<uint8_t*>(wsb + h_off);
     float* Hs = reinterpret_cast<float*>(wsb + hs_off);
+    int32_t* counters = reinterpret_cast<int32_t*>(wsb + map_off + 2 * align_up((size_t)(E + 2) * 4, 256));
     hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
-                       tile_prefix, E, kF8BM, 0, nullptr, 0);
+                       tile_prefix, E, kF8BM, 0, counters, 16);
     const int max_mt = (rows + kF8BM - 1) / kF8BM + (E < rows ? E : rows);
+    const long long n_cu = cu_count();
     Fp8Args p{};
     p.a = static_cast<const uint8_t*>(a);
     p.a_scale = a_scale;
@@ -1016,6 +1046,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.offsets = offsets;
     p.slot_of_expert = t.slot_of_expert;
     p.tile_prefix = tile_prefix;
+    p.counters = counters;
     p.pool = static_cast<const char*>(t.pool);
     p.slot_stride = t.slot_stride;
     p.E = E;
@@ -1026,7 +1057,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.K = d;
     p.out = Hq;
     p.out_scale = Hs;
-    long long nblk = (long long)max_mt * (p.N / kF8BN);
+    long long nblk = std::min((long long)max_mt * (p.N / kF8BN), n_cu);
     prof_mark(s, MOE_PROF_GATEUP, false);
     hipLaunchKernelGGL(ffn_gemm_fp8<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
     prof_mark(s, MOE_PROF_GATEUP, true);
@@ -1042,7 +1073,8 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.out = y;
     p.out_scale = nullptr;
     p.out_dtype = y_dtype;
-    nblk = (long long)max_mt * (p.N / kF8BN);
+    p.counters = counters + 8;
+    nblk = std::min((long long)max_mt * (p.N / kF8BN), n_cu);
     prof_mark(s, MOE_PROF_DOWN, false);
     hipLaunchKernelGGL(ffn_gemm_fp8<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
     prof_mark(s, MOE_PROF_DOWN, true);
