@@ -9,9 +9,9 @@
 // Three passes of a counting sort, each a single wavefront per 64-token block:
 //  block_counts  for every expert e, a 64-lane ballot of "this token picked e";
 //                popcount = the block's count for e.
-//  scan          one thread per expert walks the blocks in order (exclusive
-//                scan over blocks), then a block-wide exclusive scan over
-//                experts gives offsets; base[b][e] = offsets[e] + sum_{b'<b}.
+//  scan          one 1024-thread block: chunked sums over the blocks of each
+//                expert, shuffle scans over the chunks and over the experts give
+//                offsets and base[b][e] = offsets[e] + sum_{b'<b} cnt[b'][e].
 //  scatter       the same ballots; a pair's row is base[b][e] plus the number
 //                of lower lanes (= earlier tokens) in the ballot.
 #include <type_traits>
@@ -41,35 +41,57 @@ __global__ __launch_bounds__(64) void permute_block_counts(const int32_t* __rest
   }
 }
 
-// One block of up to 1024 threads; thread e owns expert e.
+// One block of 1024 threads. Each expert's blocks are split into C chunks (C a power of
+// two, at most 64, with C * E <= 1024); thread (e, c) = (tid / C, tid % C) sums the
+// counts of chunk c, the C chunk sums of an expert (adjacent lanes of one wavefront) are
+// scanned with shuffles, the expert totals are scanned across the block into offsets,
+// and every thread then writes base[b][e] for the blocks of its chunk.
 __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__ cnt, int32_t* __restrict__ base,
                                                      int32_t* __restrict__ offsets, int nb, int E) {
-  __shared__ int32_t tot[kMaxE];
-  const int e = threadIdx.x;
-  int running = 0;
-  if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int c = cnt[(size_t)b * E + e];
+  __shared__ int32_t off[kMaxE];
+  __shared__ int32_t wave_sum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int C = 64;
+  while (C > 1 && C * E > 1024) C >>= 1;
+  const int e = tid / C, c = tid % C;
+  const bool on = e < E;
+  const int per = (nb + C - 1) / C;
+  const int b0 = min(nb, c * per), b1 = min(nb, b0 + per);
+  int sum = 0;
+  if (on)
+    for (int b = b0; b < b1; ++b) sum += cnt[(size_t)b * E + e];
+  int inc = sum;   // inclusive scan over the chunks of expert e
+  for (int o = 1; o < C; o <<= 1) {
+    const int v = __shfl_up(inc, o, 64);
+    if (c >= o) inc += v;
+  }
+  if (on && c == C - 1) off[e] = inc;   // expert total
+  __syncthreads();
+  // exclusive scan of the E totals: within each wavefront, then across wavefronts
+  const int t = tid < E ? off[tid] : 0;
+  int ti = t;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(ti, o, 64);
+    if (lane >= o) ti += v;
+  }
+  if (lane == 63) wave_sum[wave] = ti;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wave_sum[w];
+  const int excl = before + ti - t;
+  __syncthreads();   // every thread has read off[] before it is overwritten
+  if (tid < E) {
+    off[tid] = excl;
+    offsets[tid] = excl;
+  }
+  if (tid == E - 1) offsets[E] = excl + t;
+  __syncthreads();
+  if (on) {
+    int running = off[e] + inc - sum;
+    for (int b = b0; b < b1; ++b) {
       base[(size_t)b * E + e] = running;
-      running += c;
+      running += cnt[(size_t)b * E + e];
     }
-    tot[e] = running;
-  }
-  __syncthreads();
-  if (e == 0) {
-    int acc = 0;
-    for (int i = 0; i < E; ++i) {
-      const int c = tot[i];
-      tot[i] = acc;
-      acc += c;
-    }
-    offsets[E] = acc;
-  }
-  __syncthreads();
-  if (e < E) {
-    const int off = tot[e];
-    offsets[e] = off;
-    for (int b = 0; b < nb; ++b) base[(size_t)b * E + e] += off;
   }
 }
 
@@ -200,8 +222,8 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
   hipStream_t s = as_stream(stream);
   if (T == 0) {
     // offsets stay well defined for an empty batch
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, (const int32_t*)nullptr,
-                       (int32_t*)nullptr, offsets, 0, E);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, s, (const int32_t*)nullptr, (int32_t*)nullptr, offsets,
+                       0, E);
     return check_launch("moe_permute scan");
   }
   MOE_REQUIRE(topk_idx && perm_src && perm_dst && ws, MOE_EINVAL, "moe_permute: NULL argument");
@@ -211,7 +233,7 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
   auto sort = [&](auto kmax) {
     constexpr int KM = decltype(kmax)::value;
     hipLaunchKernelGGL(permute_block_counts<KM>, dim3(nb), dim3(64), 0, s, topk_idx, cnt, T, k, E);
-    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, cnt, base, offsets, nb, E);
+    hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, s, cnt, base, offsets, nb, E);
     hipLaunchKernelGGL(permute_scatter<KM>, dim3(nb), dim3(64), 0, s, topk_idx, cnt, base, perm_src, perm_dst, T, k,
                        E);
   };

@@ -26,8 +26,9 @@ constexpr int kMaxGroups = 64;
 // A block owns MT m-tiles of 16 tokens x 64 expert columns (4 n-tiles of 16); its WK
 // waves split K, each accumulating MT x 4 MFMA tiles over its K range; the partials are
 // summed through LDS in wave order (deterministic) by the first wave. Column c < E reads
-// w_router row c; c == E (when w_sg is given) reads w_sg. Small batches use MT = 1 and
-// WK = 16 (a decode step is a few MFMA steps deep); large batches MT = 4, WK = 4.
+// w_router row c; c == E (when w_sg is given) reads w_sg. Small batches, and any batch
+// whose experts fit one 64-column group, use MT = 1 and WK = 16; large batches over many
+// experts MT = 4, WK = 4.
 // Output: raw logits into scores[t, c] for c < E, and into shared_logit[t].
 template <int MT, int WK>
 __global__ __launch_bounds__(64 * WK) void route_logits_mfma(
@@ -353,7 +354,9 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
     const bf16_t* xb = static_cast<const bf16_t*>(x);
     const bf16_t* wb = static_cast<const bf16_t*>(w_router);
     const bf16_t* sgb = static_cast<const bf16_t*>(w_shared_gate);
-    if (c.T <= 256) {
+    // 16-token blocks fill the chip when one 64-column group covers every expert; with
+    // more columns, 64-token blocks re-read x fewer times
+    if (c.T <= 256 || ncols <= 64) {
       dim3 grid((c.T + 15) / 16, (ncols + 63) / 64);
       hipLaunchKernelGGL((route_logits_mfma<1, 16>), grid, dim3(1024), 0, s, xb, wb, sgb, scores, shared_gate, counts,
                          c.T, c.d_model, c.n_experts);
