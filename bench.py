@@ -32,6 +32,29 @@ PEAK_HBM_GBS = 8000.0
 WORKLOADS = ["mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16"]
 
 
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel source changed since it was taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic-record:"):
+                    continue
+                rec = json.loads(line.split(":", 1)[1])
+                if rec.get("workload") != workload or rec.get("kernel") != kernel:
+                    continue
+                src = os.path.join(ROOT, rec["source"])
+                if not os.path.exists(src):
+                    return None
+                with open(src, "rb") as g:
+                    if hashlib.sha256(g.read()).hexdigest() != rec["source_sha256"]:
+                        return None
+                return int(rec["bytes_per_launch"])
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -329,7 +352,7 @@ def main():
         kname = "ffn_gemm_fp8<gate/up+SwiGLU+requant>" if dtype == "fp8" else "ffn_gemm_bf16<gate/up+SwiGLU>"
         result["roofline"] = {"bound": "mfma", "kernel": kname,
                               "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                              "frac": round(achieved / peak, 4), "traffic": None,
+                              "frac": round(achieved / peak, 4), "traffic": recorded_traffic(cfg.name, kname),
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
                               "work_per_launch": f"4*rows*d*F flops, rows = T*k = {int(rows.mean())}"
                               + (f"; plus the shared expert's launch, 4*T*d*F_s" if cfg.F_shared else "")}
