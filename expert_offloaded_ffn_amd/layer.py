@@ -89,6 +89,7 @@ class MoELayer:
             sb = pack_bundles(cfg, [shared], self.d, Fs, threads=1)
             self.shared = ResidentPool(sb, self.d, Fs, self.w_code, self.device)
         self._ws = {}
+        self._side = None
 
     def _buf(self, name, numel, dtype=torch.uint8):
         t = self._ws.get(name)
@@ -112,46 +113,67 @@ class MoELayer:
                     renormalize=c.renormalize, route_scale=c.route_scale, n_groups=c.n_groups,
                     topk_groups=c.topk_groups, group_topn=c.group_topn)
 
+    def _side_stream(self):
+        """The stream the shared expert runs on (default priority, created once)."""
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=self.device)
+        return self._side
+
+    def _shared_ffn(self, T, a, a_scale, a_code, ydt, main):
+        """Launches the shared expert's FFN on the side stream once `a` is ready on `main`; the
+        caller joins the side stream back before the combine."""
+        offs = self._shared_offsets(T)
+        shared_y = torch.empty(T, self.d, device=self.device, dtype=torch.float32 if ydt == B.MOE_F32 else torch.bfloat16)
+        sws = self._buf("shared_ws", B.grouped_ffn_workspace_size(self.shared.table, T, a_code))
+        side = self._side_stream()
+        side.wait_stream(main)
+        B.grouped_ffn(self.shared.table, T, offs, a, a_scale=a_scale, act_dtype=a_code, y=shared_y, y_dtype=ydt,
+                      ws=sws, stream=side)
+        return shared_y
+
     def forward(self, x: torch.Tensor, logit_bias: torch.Tensor | None = None, stream=None) -> dict:
-        """x [T, d] device tensor in the activation dtype. Returns the layer output and routing tensors."""
+        """x [T, d] device tensor in the activation dtype. Returns the layer output and routing tensors.
+        The shared expert (when there is one) runs on a second stream, concurrently with the
+        routing and the routed experts, and is joined before the combine."""
         T = x.shape[0]
         k, E, d = self.k, self.E, self.d
+        main = torch.cuda.current_stream(self.device) if stream is None else stream
+        ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
+        shared_y = None
+        if self.shared is not None and self.w_code != B.MOE_FP8_E4M3:
+            shared_y = self._shared_ffn(T, x, None, self.act_code, ydt, main)
         r = B.route(x, self.w_router_t, logit_bias=logit_bias, select_bias=self.select_bias,
-                    w_shared_gate=self.w_sg, stream=stream, **self.route_args())
+                    w_shared_gate=self.w_sg, stream=main, **self.route_args())
         ws = self._buf("perm_ws", B.permute_workspace_size(T, k, E))
         rows = T * k
-        ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
         y = torch.empty(rows, d, device=self.device, dtype=torch.float32 if ydt == B.MOE_F32 else torch.bfloat16)
         a, a_scale, a_code = x, None, self.act_code
         if self.w_code == B.MOE_FP8_E4M3:
             # grouping plus one e4m3 quantisation of every token (token order); the GEMMs
             # gather rows through perm_src
-            p = B.permute(r["idx"], E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=0, ws=ws, stream=stream)
+            p = B.permute(r["idx"], E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=0, ws=ws, stream=main)
             a, a_scale, a_code = p["x_out"], p["x_out_scale"], B.MOE_FP8_E4M3
+            if self.shared is not None:
+                shared_y = self._shared_ffn(T, a, a_scale, a_code, ydt, main)
         else:
-            p = B.permute(r["idx"], E, ws=ws, stream=stream)
+            p = B.permute(r["idx"], E, ws=ws, stream=main)
         fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
         if self.cache is None:
             B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
-                          a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=stream)
+                          a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=main)
             waves = 0
         else:
-            waves = self.cache.acquire(r["counts"], stream=stream)
+            waves = self.cache.acquire(r["counts"], stream=main)
             for w in range(waves):
                 for part in (0, 1):
-                    n = self.cache.wave(w, part, self.slot_table, stream=stream)
+                    n = self.cache.wave(w, part, self.slot_table, stream=main)
                     if n:
                         B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
-                                      a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=stream)
-                self.cache.release(w, stream=stream)
-        shared_y = None
-        if self.shared is not None:
-            offs = self._shared_offsets(T)
-            shared_y = torch.empty(T, d, device=self.device, dtype=y.dtype)
-            sws = self._buf("shared_ws", B.grouped_ffn_workspace_size(self.shared.table, T, a_code))
-            B.grouped_ffn(self.shared.table, T, offs, a, a_scale=a_scale, act_dtype=a_code, y=shared_y, y_dtype=ydt,
-                          ws=sws, stream=stream)
-        out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"], stream=stream)
+                                      a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=main)
+                self.cache.release(w, stream=main)
+        if shared_y is not None:
+            main.wait_stream(self._side_stream())
+        out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"], stream=main)
         return {"out": out, "route": r, "perm": p, "y": y, "shared_y": shared_y, "waves": waves}
 
     def capture(self, x_static: torch.Tensor, logit_bias_static: torch.Tensor | None = None):
