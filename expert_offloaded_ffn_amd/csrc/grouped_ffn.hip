@@ -147,20 +147,15 @@ __device__ __forceinline__ int take_tile(int32_t* counters, int total, int& rang
   return -1;
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
-// 16 bytes per lane from global straight into LDS at lds_base + 16 * lane.
-__device__ __forceinline__ void dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)g, (lds_void_t*)lds_base, 16, 0, 0);
-}
-
-// The same transfer issued as inline assembly. The compiler then does not track the LDS
-// write, so it adds no "vmcnt(0)" before later LDS reads; the caller orders them with
-// explicit vmcnt waits and barriers. lds_base must be wave-uniform.
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4, with the LDS base in M0), issued as inline assembly: the
+// compiler then does not track the LDS write, so it adds no "vmcnt(0)" before later LDS
+// reads; callers order them with explicit vmcnt waits and barriers. Each asm block sets M0
+// itself; M0 is reserved by the compiler (so it is not listed as clobbered) and the
+// compiled kernels here make no other use of it. lds_base must be wave-uniform.
 __device__ __forceinline__ void dma16_asm(const void* g, const void* lds_base) {
   const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");
 }
 
 // Workgroup barrier without the release fence __syncthreads() carries: that fence
@@ -405,22 +400,26 @@ __global__ __launch_bounds__(64 * kGemmWaves, 1) void ffn_gemm_bf16(GemmArgs p) 
 // is 1 KiB contiguous); A rows (at most 64 per pass, in m-blocks of 16) come from L2.
 // The split-K partials are summed through LDS in wave order (deterministic).
 
-// active[0] = number of experts with rows and a slot; active[1..] = their ids, ascending.
-// One wavefront: 64 experts per step, a ballot and a popcount of lower lanes place each.
-__global__ __launch_bounds__(64) void ffn_active_list(const int32_t* __restrict__ offsets,
-                                                      const int32_t* __restrict__ slot_of_expert,
-                                                      int32_t* __restrict__ active, int E) {
-  const int lane = threadIdx.x;
+// The i-th expert (ascending id) that has rows and a slot, or -1 when there are not that
+// many: one ballot per 64 experts; the result is uniform across the wavefront, and every
+// wavefront of a block computes the same answer.
+__device__ __forceinline__ int nth_active_expert(const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ slot_of_expert, int E, int i) {
+  const int lane = threadIdx.x & 63;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int n = 0;
+  int seen = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
     const bool on = e < E && offsets[e + 1] > offsets[e] && slot_of_expert[e] >= 0;
     const uint64_t m = __ballot(on);
-    if (on) active[1 + n + __popcll(m & below)] = e;
-    n += __popcll(m);
+    const int c = __popcll(m);
+    if (i < seen + c) {
+      const uint64_t hit = __ballot(on && __popcll(m & below) == i - seen);
+      return e0 + __ffsll((unsigned long long)hit) - 1;
+    }
+    seen += c;
   }
-  if (lane == 0) active[0] = n;
+  return -1;
 }
 
 struct DecodeArgs {
@@ -429,7 +428,7 @@ struct DecodeArgs {
   int a_row_div;
   const int32_t* offsets;
   const int32_t* slot_of_expert;
-  const int32_t* active;
+  int E;
   const char* pool;
   int64_t slot_stride;
   int64_t b_off;
@@ -455,8 +454,8 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
   __shared__ f32x4_t red[kDecWaves - 1][4][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
   const int G = p.N / 32;
   const int i = blockIdx.x / G, g = blockIdx.x % G;
-  if (i >= p.active[0]) return;
-  const int e = p.active[1 + i];
+  const int e = nth_active_expert(p.offsets, p.slot_of_expert, p.E, i);
+  if (e < 0) return;
   const int row0 = p.offsets[e];
   const int n_e = p.offsets[e + 1] - row0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -584,7 +583,7 @@ struct Fp8Args {
 // dma16_asm). lds_base must be wave-uniform.
 __device__ __forceinline__ void dma4_asm(const void* g, const void* lds_base) {
   const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
 }
 
 // One 128 x 256 tile. The weight block scales this tile needs (two per 128-column stage)
@@ -845,8 +844,6 @@ __global__ __launch_bounds__(256) void ffn_f32_down(const float* __restrict__ H,
   else static_cast<float*>(y)[(size_t)r * d + c] = s;
 }
 
-// Workspace: H [rows, F] (fp32, bf16 or e4m3) [+ e4m3 H scales [rows, F/128]], then the
-// tile prefix and the active-expert list.
 // Compute units of the current device (cached per device).
 long long cu_count() {
   static int cached[64] = {0};
@@ -860,6 +857,8 @@ long long cu_count() {
   return cached[dev];
 }
 
+// Workspace: H [rows, F] (fp32, bf16 or e4m3) [+ e4m3 H scales [rows, F/128]], then the
+// tile prefix and the per-XCD work counters of the persistent GEMMs.
 size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off,
                  size_t* hs_off = nullptr) {
   const size_t hsz = act_dtype == MOE_F32 ? 4 : act_dtype == MOE_FP8_E4M3 ? 1 : 2;
@@ -867,8 +866,8 @@ size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_o
   size_t end = align_up((size_t)rows * t->d_ff * hsz, 256);
   if (hs_off) *hs_off = end;
   if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)rows * (t->d_ff / 128) * 4, 256);
-  *map_off = end;   // tile prefix [E+1], active list [E+1], work counters [16]
-  return *map_off + 2 * align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
+  *map_off = end;   // tile prefix [E+1], then the work counters [16]
+  return *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
 }
 
 }  // namespace
@@ -938,13 +937,11 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     MOE_REQUIRE((2 * F) % kBN == 0 && d % kBN == 0, MOE_EUNSUPPORTED,
                 "moe_grouped_ffn: bf16 prefill tiles need d and 2F multiples of %d", kBN);
     int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
-    int32_t* active = reinterpret_cast<int32_t*>(wsb + map_off + align_up((size_t)(E + 2) * 4, 256));
     bf16_t* H = reinterpret_cast<bf16_t*>(wsb + h_off);
     // Rows per expert are bounded by the number of distinct source rows: at most
     // rows / a_row_div tokens (each picks an expert once) or all rows.
     const int max_rows_e = a_row_src ? (rows + a_row_div - 1) / a_row_div : rows;
     if (max_rows_e <= 64 && (2 * F) % 32 == 0 && d % 32 == 0) {
-      hipLaunchKernelGGL(ffn_active_list, dim3(1), dim3(64), 0, s, offsets, t.slot_of_expert, active, E);
       const int max_active = E < rows ? E : rows;
       DecodeArgs q{};
       q.a = static_cast<const bf16_t*>(a);
@@ -952,7 +949,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
       q.a_row_div = a_row_div;
       q.offsets = offsets;
       q.slot_of_expert = t.slot_of_expert;
-      q.active = active;
+      q.E = E;
       q.pool = static_cast<const char*>(t.pool);
       q.slot_stride = t.slot_stride;
       q.b_off = g.gu_off;
@@ -976,7 +973,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
       prof_mark(s, MOE_PROF_DEC_DOWN, true);
       return check_launch("moe_grouped_ffn bf16 decode");
     }
-    int32_t* counters = reinterpret_cast<int32_t*>(wsb + map_off + 2 * align_up((size_t)(E + 2) * 4, 256));
+    int32_t* counters = reinterpret_cast<int32_t*>(wsb + map_off + align_up((size_t)(E + 2) * 4, 256));
     hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
                        tile_prefix, E, kBM, kTallRows, counters, 16);
     const int max_mt = (rows + kBM - 1) / kBM + (E < rows ? E : rows);
@@ -1033,7 +1030,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
     uint8_t* Hq = reinterpret_cast<uint8_t*>(wsb + h_off);
     float* Hs = reinterpret_cast<float*>(wsb + hs_off);
-    int32_t* counters = reinterpret_cast<int32_t*>(wsb + map_off + 2 * align_up((size_t)(E + 2) * 4, 256));
+    int32_t* counters = reinterpret_cast<int32_t*>(wsb + map_off + align_up((size_t)(E + 2) * 4, 256));
     hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
                        tile_prefix, E, kF8BM, 0, counters, 16);
     const int max_mt = (rows + kF8BM - 1) / kF8BM + (E < rows ? E : rows);

@@ -63,18 +63,31 @@ __global__ __launch_bounds__(64 * WK) void route_logits_mfma(
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int n = 0; n < 4; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int kt = k0; kt < k1; ++kt) {
-    bf16x8_t b[4], a[MT];
+  // operands of k-step kt + 1 are loaded while the MFMAs of k-step kt run (two register
+  // sets, alternating), so each wave keeps two steps of loads in flight
+  bf16x8_t b0[4], a0[MT], b1[4], a1[MT];
+  auto load = [&](int kt, bf16x8_t* b, bf16x8_t* a) {
 #pragma unroll
     for (int n = 0; n < 4; ++n)
       if (n < ntile) b[n] = *reinterpret_cast<const bf16x8_t*>(brow[n] + kt * 32);
 #pragma unroll
     for (int m = 0; m < MT; ++m) a[m] = *reinterpret_cast<const bf16x8_t*>(arow[m] + kt * 32);
+  };
+  auto mma = [&](const bf16x8_t* b, const bf16x8_t* a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int n = 0; n < 4; ++n)
         if (n < ntile) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
+  };
+  if (k0 < k1) load(k0, b0, a0);
+  for (int kt = k0; kt < k1; kt += 2) {
+    if (kt + 1 < k1) load(kt + 1, b1, a1);
+    mma(b0, a0);
+    if (kt + 1 < k1) {
+      if (kt + 2 < k1) load(kt + 2, b0, a0);
+      mma(b1, a1);
+    }
   }
   if (wave > 0) {
 #pragma unroll
