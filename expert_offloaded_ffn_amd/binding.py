@@ -57,7 +57,7 @@ class CacheStats(ctypes.Structure):
 
 
 class Profile(ctypes.Structure):
-    _fields_ = [("ms", ctypes.c_double * 4), ("launches", ctypes.c_int64 * 4)]
+    _fields_ = [("ms", ctypes.c_double * 8), ("launches", ctypes.c_int64 * 8)]
 
 
 class CacheEntry(ctypes.Structure):
@@ -96,6 +96,7 @@ EXPORTS = {
                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_stats": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheStats)]),
     "moe_profile_enable": (ctypes.c_int32, [ctypes.c_int32]),
+    "moe_profile_label": (ctypes.c_int32, [ctypes.c_int32]),
     "moe_profile_read": (ctypes.c_int32, [ctypes.POINTER(Profile)]),
 }
 
@@ -319,14 +320,20 @@ class SlotCache:
 # ------------------------------------------------------------- profile ---
 
 PROF_GATEUP, PROF_DOWN, PROF_DEC_GATEUP, PROF_DEC_DOWN = 0, 1, 2, 3
+PROF_LABELED = 4   # kind offset of launches made under label 1 (e.g. a shared expert)
 
 
 def profile_enable(on: bool = True):
     _check(lib().moe_profile_enable(int(on)))
 
 
+def profile_label(label: int):
+    """Launches from this thread are recorded under kind + 4 while label is 1."""
+    _check(lib().moe_profile_label(int(label)))
+
+
 def profile_read() -> dict:
-    """{kind: (total_ms, launches)} since the last profile_enable."""
+    """{kind: (total_ms, launches)} since the last profile_enable (kinds 0..7)."""
     p = Profile()
     _check(lib().moe_profile_read(ctypes.byref(p)))
-    return {k: (p.ms[k], p.launches[k]) for k in range(4)}
+    return {k: (p.ms[k], p.launches[k]) for k in range(8)}

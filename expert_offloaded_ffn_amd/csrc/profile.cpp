@@ -22,6 +22,8 @@ Prof& prof() {
   return p;
 }
 
+thread_local int t_label = 0;   // moe_profile_label of the calling thread
+
 hipEvent_t take(Prof& p) {
   if (!p.pool.empty()) {
     hipEvent_t e = p.pool.back();
@@ -38,6 +40,7 @@ hipEvent_t take(Prof& p) {
 void prof_mark(hipStream_t s, int kind, bool end) {
   Prof& p = prof();
   if (!p.on) return;
+  kind += t_label * MOE_PROF_LABELED;
   std::lock_guard<std::mutex> lock(p.mu);
   hipEvent_t e = take(p);
   if (!e) return;
@@ -68,6 +71,13 @@ extern "C" moe_status moe_profile_enable(int32_t on) {
   p.done.clear();
   p.acc = moe_profile{};
   p.on = on != 0;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_profile_label(int32_t label) {
+  clear_error();
+  MOE_REQUIRE(label == 0 || label == 1, MOE_EINVAL, "moe_profile_label: label %d is not 0 or 1", label);
+  t_label = label;
   return MOE_OK;
 }
 

@@ -127,8 +127,12 @@ class MoELayer:
         sws = self._buf("shared_ws", B.grouped_ffn_workspace_size(self.shared.table, T, a_code))
         side = self._side_stream()
         side.wait_stream(main)
-        B.grouped_ffn(self.shared.table, T, offs, a, a_scale=a_scale, act_dtype=a_code, y=shared_y, y_dtype=ydt,
-                      ws=sws, stream=side)
+        B.profile_label(1)   # timed apart from the routed experts when profiling is on
+        try:
+            B.grouped_ffn(self.shared.table, T, offs, a, a_scale=a_scale, act_dtype=a_code, y=shared_y, y_dtype=ydt,
+                          ws=sws, stream=side)
+        finally:
+            B.profile_label(0)
         return shared_y
 
     def forward(self, x: torch.Tensor, logit_bias: torch.Tensor | None = None, stream=None) -> dict:

@@ -325,14 +325,26 @@ moe_status expert_slot_cache_stats(const expert_slot_cache* c, moe_cache_stats* 
  * kernel kind since the last moe_profile_enable call (which also resets).
  * Kinds: 0 gate/up GEMM with the SwiGLU epilogue, 1 down GEMM (many rows per
  * expert), 2 and 3 the same for the decode kernels (at most 64 rows per expert).
- * Errors: MOE_EINVAL for a NULL out, MOE_EHIP if an event cannot be read.
+ * Launches made while the calling thread's label is 1 (moe_profile_label) are
+ * recorded under kind + 4 instead, so a caller can keep, say, a shared expert
+ * running concurrently on another stream apart from the routed experts.
+ * Errors: MOE_EINVAL for a NULL out or a label other than 0 and 1, MOE_EHIP if an
+ * event cannot be read.
  */
-enum { MOE_PROF_GATEUP = 0, MOE_PROF_DOWN = 1, MOE_PROF_DEC_GATEUP = 2, MOE_PROF_DEC_DOWN = 3, MOE_PROF_KINDS = 4 };
+enum {
+  MOE_PROF_GATEUP = 0,
+  MOE_PROF_DOWN = 1,
+  MOE_PROF_DEC_GATEUP = 2,
+  MOE_PROF_DEC_DOWN = 3,
+  MOE_PROF_LABELED = 4, /* offset of the kinds recorded under label 1 */
+  MOE_PROF_KINDS = 8
+};
 typedef struct {
   double ms[MOE_PROF_KINDS];
   int64_t launches[MOE_PROF_KINDS];
 } moe_profile;
 moe_status moe_profile_enable(int32_t on);
+moe_status moe_profile_label(int32_t label);
 moe_status moe_profile_read(moe_profile* out);
 
 #ifdef __cplusplus

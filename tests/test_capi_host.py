@@ -156,3 +156,12 @@ def test_cache_create_validation():
     with pytest.raises(B.MoeError) as ei:
         c.acquire(None)
     assert ei.value.status in (-1, -6)
+
+
+def test_profile_label_validation():
+    L = B.lib()
+    assert L.moe_profile_label(2) == -1
+    assert b"label" in L.moe_last_error()
+    assert L.moe_profile_label(1) == 0
+    assert L.moe_profile_label(0) == 0
+    assert ctypes.sizeof(B.Profile) == 8 * 8 + 8 * 8   # ms[8] doubles, launches[8] int64
