@@ -557,6 +557,9 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
 
 constexpr int kF8BM = 128, kF8BN = 256, kF8Stages = 3;
 constexpr int kF8MaxKB = 128;   // K up to 16384 (weight scales of a tile are staged in LDS)
+#ifndef MOEFFN_F8_PIPE
+#define MOEFFN_F8_PIPE 1
+#endif
 constexpr int kF8A = 0, kF8B = 16384, kF8S = 49152, kF8StageBytes = 50176;
 
 struct Fp8Args {
@@ -660,6 +663,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
   const int a_off0 = 16 * (8 * ar + ((ac + 0) ^ f(ar)));
   const int a_off1 = 16 * (8 * ar + ((ac + 1) ^ f(ar)));
 
+  const int e8m0_one = 127;   // MFMA block scale 2^0: the fp32 block scales are applied in software
   issue(0);
   if (KB > 1) issue(1);
   for (int s = 0; s < KB; ++s) {
@@ -676,6 +680,52 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
       const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + a_off1);
       fa[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+#if MOEFFN_F8_PIPE
+    // Software-pipelined block-scale promotion. The 32 MFMAs of the stage (n-block jj,
+    // m-block i: k = 4 jj + i) write a ring of 6 partial tiles; partial k is promoted
+    // (acc += part * row scale * weight scale) after MFMA k + 4 has been issued, so the
+    // VALU work of one tile runs while the matrix core computes the next ones, and every
+    // partial has had four MFMA issue slots to complete (the hazard recognizer does not
+    // see into the inline-asm MFMAs; the drain waits explicitly). GATEUP walks the gate
+    // n-blocks (even j) before the up n-blocks (odd j), so one set of combined scales is
+    // live at a time.
+    const f32x4_t* sa_p = reinterpret_cast<const f32x4_t*>(base + kF8S + 4 * (wm * 64 + 4 * (lane >> 4)));
+    f32x4_t sc[4];
+    auto make_sc = [&](int which) {
+      const float sw = s_wscale[which][s];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[i] = sa_p[4 * i] * sw;
+    };
+    make_sc(MODE == MODE_GATEUP ? 0 : wn);
+    auto jof = [](int jj) { return MODE == MODE_GATEUP ? ((jj & 3) << 1) | (jj >> 2) : jj; };
+    auto load_b = [&](int jj) {
+      const char* blk = base + kF8B + (wn * 8 + jof(jj)) * 2048 + 16 * lane;
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
+      return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    i32x8_t fbuf[2];
+    fbuf[0] = load_b(0);
+    f32x4_t part[6];
+#pragma unroll
+    for (int k = 0; k < 36; ++k) {
+      if (k < 32) {
+        const int jj = k >> 2, i = k & 3;
+        if (i == 0 && jj + 1 < 8) fbuf[(jj + 1) & 1] = load_b(jj + 1);
+        // ("memory" keeps the compiler from sinking the next n-block's LDS reads to their use)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+                     : "=v"(part[k % 6])
+                     : "v"(fa[i]), "v"(fbuf[jj & 1]), "v"(e8m0_one)
+                     : "memory");
+      }
+      if (k == 32) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      if (k >= 4) {
+        const int kk = k - 4, i = kk & 3, jj = kk >> 2;
+        if (MODE == MODE_GATEUP && kk == 16) make_sc(1);   // the up n-blocks start here
+        acc[i][jof(jj)] += part[kk % 6] * sc[i];
+      }
+    }
+#else
     // combined scales: row scale x weight scale, [m-block][gate/up (GATEUP) or 0 (DOWN)]
     f32x4_t sc[4][2];
     {
@@ -702,6 +752,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
         acc[i][j] += part * sc[i][MODE == MODE_GATEUP ? (j & 1) : 0];
       }
     }
+#endif
   }
 
   const int rbase = row0 + wm * 64 + 4 * (lane >> 4);
