@@ -352,9 +352,9 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
                 "moe_route: group_topn=%d outside [1, min(E/n_groups, 8)]", c.group_topn);
     MOE_REQUIRE(c.top_k <= c.topk_groups * (c.n_experts / G), MOE_EINVAL, "moe_route: top_k exceeds the experts of the kept groups");
   }
+  if (c.T == 0) return MOE_OK;   // nothing to write: empty outputs may have null pointers
   MOE_REQUIRE((w_shared_gate == nullptr) == (shared_gate == nullptr), MOE_EINVAL,
               "moe_route: w_shared_gate and shared_gate go together");
-  if (c.T == 0) return MOE_OK;
   MOE_REQUIRE(x && w_router && scores && topk_idx && topk_gate, MOE_EINVAL, "moe_route: NULL tensor argument");
   MOE_REQUIRE(aligned(x, 16) && aligned(w_router, 16) && (!w_shared_gate || aligned(w_shared_gate, 16)), MOE_EINVAL,
               "moe_route: x, w_router, w_shared_gate must be 16-byte aligned");

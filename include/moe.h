@@ -100,7 +100,8 @@ const char* moe_version(void);
  * Errors: MOE_EINVAL for T < 0, d < 1, E < 1, k outside [1, E], d % 8 != 0,
  *  n_groups not dividing E, topk_groups > n_groups, group_topn outside
  *  [1, E/n_groups], k > topk_groups*E/n_groups, E > 1024, null required pointers,
- *  select_bias with softmax. T = 0 is a no-op.
+ *  select_bias with softmax. T = 0 is a no-op (the configuration is still checked;
+ *  tensor pointers may then be NULL).
  */
 typedef struct {
   int32_t T, d_model, n_experts, top_k;

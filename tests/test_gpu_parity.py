@@ -88,6 +88,34 @@ def test_bf16_last_tile_sizes(T):
     assert to_np(g["route"]["counts"]).tolist() == [T, T]
 
 
+@pytest.mark.parametrize("T,d,E,k,F", [(200, 256, 16, 1, 256), (130, 256, 96, 6, 256)])
+def test_bf16_layer_top1_and_many_experts(T, d, E, k, F):
+    """top-1 routing (gates are 1 after renormalisation), and more experts than one 64-lane group."""
+    cfg = synth.get_config("mixtral_prefill_bf16", T=T, d=d, E=E, k=k, F=F, name=f"bf16b_T{T}_E{E}_k{k}")
+    layer, w = _build(cfg)
+    g = _run_and_check(cfg, layer, w, T)
+    if k == 1:
+        np.testing.assert_allclose(to_np(g["route"]["gate"]), 1.0, rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("config_name", ["mixtral_prefill_bf16", "qwen_decode_bf16", "dsv3_prefill_fp8"])
+def test_empty_batch(config_name):
+    """T = 0 runs through every call of the layer and returns an empty output."""
+    overrides = {"d": 256, "F": 256} if config_name == "mixtral_prefill_bf16" else {}
+    if config_name == "dsv3_prefill_fp8":
+        overrides = dict(d=512, E=32, k=8, F=256, F_shared=256, n_groups=8, topk_groups=4)
+    if config_name == "qwen_decode_bf16":
+        overrides = dict(T=1)
+    cfg = synth.get_config(config_name, name=f"empty_{config_name}", **overrides)
+    layer, _ = _build(cfg)
+    x = torch.empty(0, cfg.d, device=DEV, dtype=torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16)
+    say(f"  case empty batch {config_name}: launching")
+    g = layer.forward(x)
+    torch.cuda.synchronize()
+    assert tuple(g["out"].shape) == (0, cfg.d)
+    assert to_np(g["perm"]["offsets"]).tolist() == [0] * (cfg.E + 1)
+
+
 def test_mixtral_full_size_sampled():
     cfg = synth.get_config("mixtral_prefill_bf16")
     layer, w = _build(cfg)
