@@ -219,12 +219,13 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
   // Per stage this wave loads A blocks 2w, 2w+1 (and 16 + w on a tall tile, waves 0-3)
   // and B blocks 2w, 2w+1. An A block is 16 rows x 32 columns; lane l fetches 16 bytes of
   // row r = l/4, so each quad of lanes reads one row's 64 contiguous bytes. Chunk c of
-  // row r is stored at slot 4r + (c ^ g(r)) with g(r) = (r2 << 1) | (r1 ^ r3) (bits of r):
-  // the MFMA fragment reads (row l%16, chunk l/16) then touch distinct 16-byte bank groups
-  // within every group of 8 lanes and within every group of 16 lanes.
+  // row r is stored at slot 4r + (c ^ g(r)) with g(r) = (r3 << 1) | r2 (bits of r): the
+  // MFMA fragment reads (row l%16, chunk l/16) then touch distinct 16-byte slots modulo 32
+  // within every 32 consecutive lanes, and so also within every 16, whichever of the two
+  // lane groups the LDS serves a 16-byte read in.
   const bool extra_a = TALL && w < 4;
   const int dma_per_stage = 4 + (extra_a ? 1 : 0);
-  auto swz = [](int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); };
+  auto swz = [](int r) { return (((r >> 3) & 1) << 1) | ((r >> 2) & 1); };
   const int a_chunk = (lane & 3) ^ swz(lane >> 2);
   auto a_src = [&](int blk) {
     int r = row0 + blk * 16 + (lane >> 2);
