@@ -2,8 +2,8 @@
 // order, plus the always-resident shared expert ("Running 35B MoE Models on 8GB
 // GPUs", section "Gotcha": shared experts sit outside the routed, cached set).
 //
-// One wavefront per (token, 512-column chunk); each lane owns 8 consecutive
-// columns, reads the k expert rows through perm_dst with 16-byte (bf16) or
+// One wavefront per token (large batches) or per (token, 512-column chunk) (small
+// ones); each lane owns 8 consecutive columns per step, reads the k expert rows through perm_dst with 16-byte (bf16) or
 // 32-byte (fp32) loads, accumulates in fp32 in slot order j = 0..k-1, adds the
 // shared term last and rounds once.
 #include "moe_internal.h"
@@ -35,12 +35,13 @@ template <typename TY, typename TO>
 __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, const int32_t* __restrict__ perm_dst,
                                                       const float* __restrict__ gate, const TY* __restrict__ shared_y,
                                                       const float* __restrict__ shared_gate, TO* __restrict__ out,
-                                                      int T, int k, int d) {
-  // one wavefront per (token, 512-column chunk): every load of a wavefront is issued at
-  // once, and a small batch still spreads over d / 512 wavefronts per token
+                                                      int T, int k, int d, int span) {
+  // one wavefront per (token, span of 512-column chunks): a small batch spreads each token
+  // over d / 512 wavefronts (span 1), a large one gives a wavefront the whole row
   const int nchunk = (d + 511) / 512;
+  const int groups = (nchunk + span - 1) / span;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int t = item / nchunk, chunk = item - t * nchunk;
+  const int t = item / groups, gi = item - t * groups;
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
   int rows[32];
@@ -50,9 +51,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, 
     g[j] = gate[(size_t)t * k + j];
   }
   const float sg = shared_y ? (shared_gate ? shared_gate[t] : 1.0f) : 0.0f;
-  {
-    const int c = chunk * 512 + lane * 8;
-    if (c >= d) return;
+  const int c_end = min(d, (gi + 1) * span * 512);
+  for (int c = gi * span * 512 + lane * 8; c < c_end; c += 512) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       float v[8];
@@ -97,19 +97,21 @@ extern "C" moe_status moe_combine(int32_t T, int32_t k, int32_t d, const void* y
   MOE_REQUIRE(aligned(y, 16) && aligned(out, 16) && (!shared_y || aligned(shared_y, 16)), MOE_EINVAL,
               "moe_combine: y, shared_y and out must be 16-byte aligned");
   hipStream_t s = as_stream(stream);
-  const long long items = (long long)T * ((d + 511) / 512);
+  const int nchunk = (d + 511) / 512;
+  const int span = T >= 512 ? nchunk : 1;   // enough tokens fill the chip with a row each
+  const long long items = (long long)T * ((nchunk + span - 1) / span);
   dim3 grid((unsigned)((items + 3) / 4)), block(256);
   if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16)
     hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), grid, block, 0, s, (const bf16_t*)y, perm_dst, topk_gate,
-                       (const bf16_t*)shared_y, shared_gate, (bf16_t*)out, T, k, d);
+                       (const bf16_t*)shared_y, shared_gate, (bf16_t*)out, T, k, d, span);
   else if (y_dtype == MOE_BF16)
     hipLaunchKernelGGL((combine_kernel<bf16_t, float>), grid, block, 0, s, (const bf16_t*)y, perm_dst, topk_gate,
-                       (const bf16_t*)shared_y, shared_gate, (float*)out, T, k, d);
+                       (const bf16_t*)shared_y, shared_gate, (float*)out, T, k, d, span);
   else if (out_dtype == MOE_BF16)
     hipLaunchKernelGGL((combine_kernel<float, bf16_t>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
-                       (const float*)shared_y, shared_gate, (bf16_t*)out, T, k, d);
+                       (const float*)shared_y, shared_gate, (bf16_t*)out, T, k, d, span);
   else
     hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
-                       (const float*)shared_y, shared_gate, (float*)out, T, k, d);
+                       (const float*)shared_y, shared_gate, (float*)out, T, k, d, span);
   return check_launch("moe_combine");
 }
