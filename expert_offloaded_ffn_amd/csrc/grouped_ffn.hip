@@ -558,9 +558,6 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
 
 constexpr int kF8BM = 128, kF8BN = 256, kF8Stages = 3;
 constexpr int kF8MaxKB = 128;   // K up to 16384 (weight scales of a tile are staged in LDS)
-#ifndef MOEFFN_F8_PIPE
-#define MOEFFN_F8_PIPE 1
-#endif
 constexpr int kF8A = 0, kF8B = 16384, kF8S = 49152, kF8StageBytes = 50176;
 
 struct Fp8Args {
@@ -590,20 +587,21 @@ __device__ __forceinline__ void dma4_asm(const void* g, const void* lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
 }
 
-// One 128 x 256 tile. The weight block scales this tile needs (two per 128-column stage)
-// are staged in LDS first (s_wscale), so the main loop issues no global loads of its own
-// besides the DMA ring.
+// One 128 x 256 tile on 8 waves (2 wave rows of 64 x 4 wave columns of 64, two waves per
+// SIMD, so one wave's block-scale promotion and LDS reads run while the other's MFMAs do).
+// The weight block scales the tile needs (two per 128-column stage) are staged in LDS
+// first (s_wscale), so the main loop issues no global loads of its own besides the ring.
 template <int MODE>
 __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8StageBytes],
                                               float (*amax_x)[kF8BM], float (*s_wscale)[kF8MaxKB], int e, int row0,
                                               int row_end, int n0) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w >> 2, wn = w & 3;   // wave row (4 m-blocks) x wave column (4 n-blocks)
   const int KB = p.K / 128;
   const char* bundle = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride;
   const char* B = bundle + p.b_off;
   // GATEUP: [0] gate and [1] up scales of the tile's 128 hidden rows; DOWN: the scales of
-  // the tile's two 128-column blocks (wave column wn uses [wn])
+  // the tile's two 128-column blocks (wave column wn uses [wn / 2])
   for (int i = threadIdx.x; i < 2 * KB; i += blockDim.x) {
     const int which = i / KB, s = i - which * KB;
     const float* grid;
@@ -624,40 +622,40 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
     return p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
   };
 
-  // A: this wave's 4 DMA instructions per stage cover rows 32w .. 32w+31 of the tile
-  // (8 rows each); lane j loads chunk (j%8) ^ f(r) of row r = (32w + 8t + j/8) % 16 of its block.
-  const uint8_t* aptr[4];
+  // Per stage each wave issues 7 DMA instructions: A rows 16w .. 16w+15 (two of 8 rows;
+  // lane j loads chunk (j%8) ^ f(r) of row r = 16w + 8t + j/8), B n-blocks 2w and 2w+1
+  // (two 1 KiB halves each) and one of the row-scale quarters (rows 64 (w & 1) + lane into
+  // slot w & 3; waves 4-7 repeat 0-3 with the same bytes, so every wave has the same count).
+  const uint8_t* aptr[2];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int tr = 32 * w + 8 * t + (lane >> 3);   // row within the 128-row tile
-    const int r16 = tr & 15;
-    aptr[t] = p.a + (size_t)src_row(row0 + tr) * p.K + 16 * ((lane & 7) ^ f(r16));
+  for (int t = 0; t < 2; ++t) {
+    const int tr = 16 * w + 8 * t + (lane >> 3);   // row within the 128-row tile
+    aptr[t] = p.a + (size_t)src_row(row0 + tr) * p.K + 16 * ((lane & 7) ^ f(tr & 15));
   }
-  // row scales: wave w loads rows 64*(w&1) + lane (waves 2, 3 duplicate into the spare half)
   const float* sptr = p.a_scale + (size_t)src_row(row0 + 64 * (w & 1) + lane) * KB;
-  const char* bptr = B + ((int64_t)(n0 / 16 + w * 4) * KB) * 2048 + 16 * lane;
+  const char* bptr = B + ((int64_t)(n0 / 16 + w * 2) * KB) * 2048 + 16 * lane;
 
   auto issue = [&](int s) {
     char* base = smem[s % kF8Stages];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) dma16_asm(aptr[t] + s * 128, base + kF8A + (4 * w + t) * 1024);
+    for (int t = 0; t < 2; ++t) dma16_asm(aptr[t] + s * 128, base + kF8A + (2 * w + t) * 1024);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        dma16_asm(bptr + ((int64_t)i * KB + s) * 2048 + h * 1024, base + kF8B + (w * 4 + i) * 2048 + h * 1024);
-    dma4_asm(sptr + s, base + kF8S + w * 256);
+        dma16_asm(bptr + ((int64_t)i * KB + s) * 2048 + h * 1024, base + kF8B + (w * 2 + i) * 2048 + h * 1024);
+    dma4_asm(sptr + s, base + kF8S + (w & 3) * 256);
   };
   auto wait_dma = [&](bool more) {
-    if (more) asm volatile("s_waitcnt vmcnt(13)" ::: "memory");
+    if (more) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
 
-  f32x4_t acc[4][8];
+  f32x4_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // fragment read offsets: A (row l%16, chunks 2(l/16) and 2(l/16)+1), B (two halves)
   const int ar = lane & 15, ac = 2 * (lane >> 4);
@@ -681,8 +679,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
       const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + a_off1);
       fa[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-#if MOEFFN_F8_PIPE
-    // Software-pipelined block-scale promotion. The 32 MFMAs of the stage (n-block jj,
+    // Software-pipelined block-scale promotion. The 16 MFMAs of the stage (n-block jj,
     // m-block i: k = 4 jj + i) write a ring of 6 partial tiles; partial k is promoted
     // (acc += part * row scale * weight scale) after MFMA k + 4 has been issued, so the
     // VALU work of one tile runs while the matrix core computes the next ones, and every
@@ -697,10 +694,10 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = sa_p[4 * i] * sw;
     };
-    make_sc(MODE == MODE_GATEUP ? 0 : wn);
-    auto jof = [](int jj) { return MODE == MODE_GATEUP ? ((jj & 3) << 1) | (jj >> 2) : jj; };
+    make_sc(MODE == MODE_GATEUP ? 0 : wn >> 1);
+    auto jof = [](int jj) { return MODE == MODE_GATEUP ? ((jj & 1) << 1) | (jj >> 1) : jj; };
     auto load_b = [&](int jj) {
-      const char* blk = base + kF8B + (wn * 8 + jof(jj)) * 2048 + 16 * lane;
+      const char* blk = base + kF8B + (wn * 4 + jof(jj)) * 2048 + 16 * lane;
       const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
       const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
       return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -709,58 +706,31 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
     fbuf[0] = load_b(0);
     f32x4_t part[6];
 #pragma unroll
-    for (int k = 0; k < 36; ++k) {
-      if (k < 32) {
+    for (int k = 0; k < 20; ++k) {
+      if (k < 16) {
         const int jj = k >> 2, i = k & 3;
-        if (i == 0 && jj + 1 < 8) fbuf[(jj + 1) & 1] = load_b(jj + 1);
+        if (i == 0 && jj + 1 < 4) fbuf[(jj + 1) & 1] = load_b(jj + 1);
         // ("memory" keeps the compiler from sinking the next n-block's LDS reads to their use)
         asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
                      : "=v"(part[k % 6])
                      : "v"(fa[i]), "v"(fbuf[jj & 1]), "v"(e8m0_one)
                      : "memory");
       }
-      if (k == 32) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+      if (k == 16) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
       if (k >= 4) {
         const int kk = k - 4, i = kk & 3, jj = kk >> 2;
-        if (MODE == MODE_GATEUP && kk == 16) make_sc(1);   // the up n-blocks start here
+        if (MODE == MODE_GATEUP && kk == 8) make_sc(1);   // the up n-blocks start here
         acc[i][jof(jj)] += part[kk % 6] * sc[i];
       }
     }
-#else
-    // combined scales: row scale x weight scale, [m-block][gate/up (GATEUP) or 0 (DOWN)]
-    f32x4_t sc[4][2];
-    {
-      const float sw0 = s_wscale[MODE == MODE_GATEUP ? 0 : wn][s];
-      const float sw1 = s_wscale[MODE == MODE_GATEUP ? 1 : wn][s];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(base + kF8S + 4 * ((wm * 4 + i) * 16 + 4 * (lane >> 4)));
-        sc[i][0] = sa * sw0;
-        sc[i][1] = sa * sw1;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const char* blk = base + kF8B + (wn * 8 + j) * 2048 + 16 * lane;
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
-      const i32x8_t fb = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const f32x4_t part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa[i], fb, f32x4_t{0.f, 0.f, 0.f, 0.f},
-                                                                              0, 0, 0, 127, 0, 127);
-        // gate/up rows alternate every 16 (n-block parity); down: one scale block per wave column
-        acc[i][j] += part * sc[i][MODE == MODE_GATEUP ? (j & 1) : 0];
-      }
-    }
-#endif
   }
 
   const int rbase = row0 + wm * 64 + 4 * (lane >> 4);
   if constexpr (MODE == MODE_GATEUP) {
-    // H = silu(G) * U over this tile's 128 hidden columns, then per-row e4m3 quantisation
+    // H = silu(G) * U over this tile's 128 hidden columns (32 per wave column), then per-row
+    // e4m3 quantisation with one scale per row for the 128 columns (amax over the 4 waves)
     const int F = p.N / 2;
-    float h[4][4][4];  // [m-block][pair][row q]
+    float h[4][2][4];  // [m-block][pair][row q]
     float am[4][4];    // [m-block][row q]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -768,7 +738,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
       for (int q = 0; q < 4; ++q) {
         float m = 0.f;
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
+        for (int pp = 0; pp < 2; ++pp) {
           const float v = silu_f32(acc[i][2 * pp][q]) * acc[i][2 * pp + 1][q];
           h[i][pp][q] = v;
           m = fmaxf(m, fabsf(v));
@@ -785,18 +755,18 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
     }
     __syncthreads();
     uint8_t* Hq = static_cast<uint8_t*>(p.out);
-    const int hcol0 = n0 / 2 + wn * 64 + (lane & 15);
+    const int hcol0 = n0 / 2 + wn * 32 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int lr = wm * 64 + i * 16 + 4 * (lane >> 4) + q;
         const int r = row0 + lr;
-        const float a = fmaxf(amax_x[0][lr], amax_x[1][lr]);
+        const float a = fmaxf(fmaxf(amax_x[0][lr], amax_x[1][lr]), fmaxf(amax_x[2][lr], amax_x[3][lr]));
         const float scale = a > 0.f ? a / 448.0f : 1.0f;
         if (r < row_end) {
 #pragma unroll
-          for (int pp = 0; pp < 4; ++pp) {
+          for (int pp = 0; pp < 2; ++pp) {
             const float y = fminf(fmaxf(h[i][pp][q] / scale, -448.0f), 448.0f);
             Hq[(size_t)r * F + hcol0 + pp * 16] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
           }
@@ -807,8 +777,8 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = rbase + i * 16 + q;
@@ -822,9 +792,9 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_fp8(Fp8Args p) {
+__global__ __launch_bounds__(512, 1) void ffn_gemm_fp8(Fp8Args p) {
   __shared__ __attribute__((aligned(1024))) char smem[kF8Stages][kF8StageBytes];
-  __shared__ float amax_x[2][kF8BM];
+  __shared__ float amax_x[4][kF8BM];
   __shared__ float s_wscale[2][kF8MaxKB];
   __shared__ int s_tile;
   const int NT = p.N / kF8BN;
@@ -1108,7 +1078,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.out_scale = Hs;
     long long nblk = std::min((long long)max_mt * (p.N / kF8BN), n_cu);
     prof_mark(s, MOE_PROF_GATEUP, false);
-    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, p);
     prof_mark(s, MOE_PROF_GATEUP, true);
     p.a = Hq;
     p.a_scale = Hs;
@@ -1125,7 +1095,7 @@ extern "C" moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t row
     p.counters = counters + 8;
     nblk = std::min((long long)max_mt * (p.N / kF8BN), n_cu);
     prof_mark(s, MOE_PROF_DOWN, false);
-    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, p);
     prof_mark(s, MOE_PROF_DOWN, true);
   }
   return check_launch("moe_grouped_ffn fp8");
