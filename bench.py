@@ -34,7 +34,8 @@ WORKLOADS = ["mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "ti
 
 def recorded_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
-    when there is none for this workload or the kernel source changed since it was taken."""
+    when there is none for this workload or any source file of the kernel changed since the
+    counters were taken (the record lists the sha256 of each)."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
@@ -45,12 +46,13 @@ def recorded_traffic(workload, kernel):
                 rec = json.loads(line.split(":", 1)[1])
                 if rec.get("workload") != workload or rec.get("kernel") != kernel:
                     continue
-                src = os.path.join(ROOT, rec["source"])
-                if not os.path.exists(src):
-                    return None
-                with open(src, "rb") as g:
-                    if hashlib.sha256(g.read()).hexdigest() != rec["source_sha256"]:
+                for rel, sha in rec["sources"].items():
+                    src = os.path.join(ROOT, rel)
+                    if not os.path.exists(src):
                         return None
+                    with open(src, "rb") as g:
+                        if hashlib.sha256(g.read()).hexdigest() != sha:
+                            return None
                 return int(rec["bytes_per_launch"])
     return None
 
@@ -164,7 +166,9 @@ def bench_offload(args, torch, B, synth, MoELayer):
 
 def bench_decode(args, torch, B, synth, MoELayer):
     """Decode layer (few tokens): each step's time is measured alone with hipEvents, after a
-    512 MiB write that evicts the 256 MB last-level cache, so weights stream from HBM. The
+    512 MiB pass that evicts the 256 MB last-level cache, so weights stream from HBM (a read by
+    default, leaving clean lines as other layers' weight reads would; --mall-flush write leaves
+    dirty lines that the step's own reads must first write back). The
     roofline is HBM bytes: the distinct touched experts' bundles + the shared expert + router
     weights + activations in and out."""
     cfg = synth.get_config(args.workload)
@@ -178,7 +182,8 @@ def bench_decode(args, torch, B, synth, MoELayer):
                      threads=16)
     nb = max(args.batches, 64)
     xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(nb)]
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
+    flush_words = flush.view(torch.int32)
     bundle = B.bundle_bytes(cfg.d, cfg.F, B.MOE_BF16)
     shared_bytes = B.bundle_bytes(cfg.d, cfg.F_shared, B.MOE_BF16) if cfg.F_shared else 0
     act = 2 * cfg.T * cfg.d * 2 + cfg.E * cfg.d * 2 + (cfg.d * 2 if cfg.shared_gate else 0)
@@ -198,7 +203,10 @@ def bench_decode(args, torch, B, synth, MoELayer):
     B.profile_enable(not args.graph)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
-        flush.fill_(i & 255)
+        if args.mall_flush == "write":
+            flush.fill_(i & 255)      # leaves the last-level cache full of dirty lines
+        else:
+            flush_words.max()         # reads 512 MiB: clean lines, as other layers' weight reads leave it
         if graph is not None:
             x_static.copy_(xs[i % nb])
             evs[i][0].record()
@@ -212,7 +220,11 @@ def bench_decode(args, torch, B, synth, MoELayer):
     B.profile_enable(False)
     ms = np.array([a.elapsed_time(b) for a, b in evs])
     step_bytes = np.array([touched[i % nb] * bundle + shared_bytes + act for i in range(args.steps)], np.float64)
-    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * 2 for i in range(args.steps))   # routed experts
+    # the decode gate/up launch streams the touched routed experts' W_gu, and the shared
+    # expert's when the layer runs it inside the same launch
+    merged = layer.shared_in_decode_launch(cfg.T)
+    shared_gu = 2 * cfg.F_shared * cfg.d * 2 if merged else 0
+    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * 2 + shared_gu for i in range(args.steps))
     gu_ms, gu_n = prof[B.PROF_DEC_GATEUP]
     hbm = float(step_bytes.sum() / (ms.sum() / 1e3) / 1e9)
     result = {
@@ -221,7 +233,8 @@ def bench_decode(args, torch, B, synth, MoELayer):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
-                   "d_ff": cfg.F, "d_ff_shared": cfg.F_shared, "mall_flush_MiB": 512, "hip_graph": bool(args.graph)},
+                   "d_ff": cfg.F, "d_ff_shared": cfg.F_shared, "mall_flush_MiB": 512, "mall_flush": args.mall_flush,
+                   "hip_graph": bool(args.graph)},
         "step_ms_p10_p50_p90": [round(float(np.percentile(ms, q)), 4) for q in (10, 50, 90)],
         "touched_experts_mean": round(float(np.mean([touched[i % nb] for i in range(args.steps)])), 2),
         "layer_hbm": {"achieved": round(hbm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
@@ -229,11 +242,12 @@ def bench_decode(args, torch, B, synth, MoELayer):
     }
     if gu_n:
         a = gu_bytes / (gu_ms / 1e3) / 1e9
-        result["roofline"] = {"bound": "hbm", "kernel": "ffn_decode_bf16<gate/up+SwiGLU> (routed experts)",
+        who = "routed experts + shared expert" if merged else "routed experts"
+        result["roofline"] = {"bound": "hbm", "kernel": f"ffn_decode_bf16<gate/up+SwiGLU> ({who})",
                               "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
-                              "work_per_launch": "gate/up weight bytes of the touched routed experts"}
+                              "work_per_launch": f"gate/up weight bytes of the touched {who}"}
     print(json.dumps(result), flush=True)
     return 0
 
@@ -249,6 +263,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="decode: replay the layer as one captured HIP graph")
+    ap.add_argument("--mall-flush", choices=["read", "write"], default="read",
+                    help="decode: evict the last-level cache before each step by reading (default) or writing 512 MiB")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (HBM ceiling and the "
                          "reference for the FETCH_SIZE/WRITE_SIZE counters), then exit")

@@ -44,6 +44,13 @@ class ExpertTable(ctypes.Structure):
                 ("w_dtype", ctypes.c_int32)]
 
 
+class FfnProblem(ctypes.Structure):
+    _fields_ = [("table", ctypes.POINTER(ExpertTable)), ("rows", ctypes.c_int32), ("offsets", ctypes.c_void_p),
+                ("a", ctypes.c_void_p), ("a_scale", ctypes.c_void_p), ("act_dtype", ctypes.c_int32),
+                ("a_row_src", ctypes.c_void_p), ("a_row_div", ctypes.c_int32), ("y", ctypes.c_void_p),
+                ("y_dtype", ctypes.c_int32)]
+
+
 class CacheCfg(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("bundle_bytes", ctypes.c_int64),
                 ("slot_stride", ctypes.c_int64), ("bundles_host", ctypes.c_void_p), ("pool", ctypes.c_void_p),
@@ -70,6 +77,8 @@ EXPORTS = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_version": (ctypes.c_char_p, []),
     "moe_route": (ctypes.c_int32, [ctypes.POINTER(RouteCfg)] + [ctypes.c_void_p] * 11),
+    "moe_route_permute": (ctypes.c_int32, [ctypes.POINTER(RouteCfg)] + [ctypes.c_void_p] * 14 +
+                          [ctypes.c_size_t, ctypes.c_void_p]),
     "moe_permute_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
     "moe_permute": (ctypes.c_int32, [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p,
                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
@@ -80,6 +89,9 @@ EXPORTS = {
     "moe_grouped_ffn": (ctypes.c_int32, [ctypes.POINTER(ExpertTable), ctypes.c_int32, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_grouped_ffn_batch_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(FfnProblem), ctypes.c_int32]),
+    "moe_grouped_ffn_batch": (ctypes.c_int32, [ctypes.POINTER(FfnProblem), ctypes.c_int32, ctypes.c_void_p,
+                              ctypes.c_size_t, ctypes.c_void_p]),
     "moe_combine": (ctypes.c_int32, [ctypes.c_int32] * 3 + [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                     ctypes.c_void_p]),
@@ -196,6 +208,38 @@ def permute(idx, E, *, x=None, out_dtype=None, gather=1, ws=None, out=None, stre
     return {"offsets": offsets, "perm_src": src, "perm_dst": dst, "x_out": x_out, "x_out_scale": xs}
 
 
+def route_permute(x, w_router_t, *, k, score_fn=MOE_SOFTMAX, renormalize=1, route_scale=1.0, n_groups=1,
+                  topk_groups=1, group_topn=0, logit_bias=None, select_bias=None, w_shared_gate=None, ws=None,
+                  out=None, stream=None):
+    """moe_route_permute. Returns the dicts of route() and permute() (without x_out) merged."""
+    T, d = x.shape
+    E = w_router_t.shape[0]
+    dev = x.device
+    o = out or {}
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        return t if t is not None else torch.empty(*shape, device=dev, dtype=dtype)
+
+    scores = get("scores", (T, E), torch.float32)
+    idx = get("idx", (T, k), torch.int32)
+    gate = get("gate", (T, k), torch.float32)
+    counts = get("counts", (E,), torch.int32)
+    sg = get("shared_gate", (T,), torch.float32) if w_shared_gate is not None else None
+    offsets = get("offsets", (E + 1,), torch.int32)
+    src = get("perm_src", (T * k,), torch.int32)
+    dst = get("perm_dst", (T * k,), torch.int32)
+    if ws is None:
+        ws = torch.empty(max(permute_workspace_size(T, k, E), 256), device=dev, dtype=torch.uint8)
+    cfg = RouteCfg(T, d, E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn,
+                   DTYPE_CODE[x.dtype])
+    _check(lib().moe_route_permute(ctypes.byref(cfg), ptr(x), ptr(w_router_t), ptr(logit_bias), ptr(select_bias),
+                                   ptr(w_shared_gate), ptr(sg), ptr(scores), ptr(idx), ptr(gate), ptr(counts),
+                                   ptr(offsets), ptr(src), ptr(dst), ptr(ws), ws.numel(), stream_ptr(stream)))
+    return {"scores": scores, "idx": idx, "gate": gate, "counts": counts, "shared_gate": sg,
+            "offsets": offsets, "perm_src": src, "perm_dst": dst, "x_out": None, "x_out_scale": None}
+
+
 def bundle_bytes(d, F, w_dtype) -> int:
     return int(lib().moe_bundle_bytes(d, F, w_dtype))
 
@@ -235,6 +279,35 @@ def grouped_ffn(table: ExpertTable, rows, offsets, a, *, a_scale=None, act_dtype
     _check(lib().moe_grouped_ffn(ctypes.byref(table), rows, ptr(offsets), ptr(a), ptr(a_scale), act, ptr(a_row_src),
                                  int(a_row_div), ptr(y), y_dtype, ptr(ws), ws.numel(), stream_ptr(stream)))
     return y
+
+
+def ffn_problem(table: ExpertTable, rows, offsets, a, *, a_scale=None, act_dtype=None, a_row_src=None, a_row_div=1,
+                y=None, y_dtype=MOE_BF16) -> FfnProblem:
+    """The fields of one moe_grouped_ffn call; `y` is allocated when not given (read it back as .y_tensor)."""
+    act = DTYPE_CODE[a.dtype] if act_dtype is None else act_dtype
+    if y is None:
+        y = torch.empty(rows, table.d_model, device=a.device,
+                        dtype=torch.bfloat16 if y_dtype == MOE_BF16 else torch.float32)
+    pr = FfnProblem(ctypes.pointer(table), rows, ptr(offsets), ptr(a), ptr(a_scale), act, ptr(a_row_src),
+                    int(a_row_div), ptr(y), y_dtype)
+    pr.y_tensor = y
+    pr.keep = (table, offsets, a, a_scale, a_row_src)   # the tensors stay alive with the struct
+    return pr
+
+
+def grouped_ffn_batch_workspace_size(problems) -> int:
+    arr = (FfnProblem * len(problems))(*problems)
+    return int(lib().moe_grouped_ffn_batch_workspace_size(arr, len(problems)))
+
+
+def grouped_ffn_batch(problems, *, ws=None, stream=None):
+    """moe_grouped_ffn_batch over 1 or 2 FfnProblem structs (see ffn_problem). Returns their y tensors."""
+    arr = (FfnProblem * len(problems))(*problems)
+    dev = problems[0].y_tensor.device
+    if ws is None:
+        ws = torch.empty(max(grouped_ffn_batch_workspace_size(problems), 256), device=dev, dtype=torch.uint8)
+    _check(lib().moe_grouped_ffn_batch(arr, len(problems), ptr(ws), ws.numel(), stream_ptr(stream)))
+    return [pr.y_tensor for pr in problems]
 
 
 def combine(y, perm_dst, gate, *, shared_y=None, shared_gate=None, out=None, out_dtype=None, stream=None):

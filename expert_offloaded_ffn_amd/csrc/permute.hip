@@ -17,6 +17,7 @@
 // A batch of at most 64 tokens runs all three passes in one workgroup (permute_small).
 #include <type_traits>
 
+#include "group_small.h"
 #include "moe_internal.h"
 
 namespace moeffn {
@@ -97,59 +98,14 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
 }
 
 // T <= 64 (a single block of tokens): the three passes in one workgroup of 16 wavefronts.
-// Every wavefront holds all tokens (lane = token) and takes experts w, w + 16, ...: a
-// ballot per expert gives its count, a block-wide scan over the experts gives the
-// offsets, and a second ballot per expert ranks each pair by token.
+// One block of at most 64 tokens: the whole counting sort in one workgroup.
 template <int KMAX>
 __global__ __launch_bounds__(1024) void permute_small(const int32_t* __restrict__ idx, int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm_src, int32_t* __restrict__ perm_dst,
                                                       int T, int k, int E) {
   __shared__ int32_t off[kMaxE];
   __shared__ int32_t wave_sum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int mine[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) mine[j] = (lane < T && j < k) ? idx[(size_t)lane * k + j] : -1;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = wave; e < E; e += 16) {
-    bool has = false;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) has |= (mine[j] == e);
-    const uint64_t m = __ballot(has);
-    if (lane == 0) off[e] = __popcll(m);
-  }
-  __syncthreads();
-  // exclusive scan of the counts over the experts (thread e holds expert e)
-  const int c = tid < E ? off[tid] : 0;
-  int inc = c;
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += v;
-  }
-  if (lane == 63) wave_sum[wave] = inc;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wave; ++w) before += wave_sum[w];
-  const int excl = before + inc - c;
-  __syncthreads();   // every count has been read before it is overwritten
-  if (tid < E) {
-    off[tid] = excl;
-    offsets[tid] = excl;
-  }
-  if (tid == E - 1) offsets[E] = excl + c;
-  __syncthreads();
-  for (int e = wave; e < E; e += 16) {
-    int slot = -1;
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j)
-      if (mine[j] == e) slot = j;
-    const uint64_t m = __ballot(slot >= 0);
-    if (slot >= 0) {
-      const int pos = off[e] + __popcll(m & below);
-      perm_src[pos] = lane * k + slot;
-      perm_dst[lane * k + slot] = pos;
-    }
-  }
+  group_small<KMAX>(idx, nullptr, offsets, perm_src, perm_dst, T, k, E, off, wave_sum);
 }
 
 template <int KMAX>

@@ -13,6 +13,9 @@
 //  route_select       one wavefront per token: keys, group limit, k rounds of a
 //                     64-lane arg-max over packed (key, ~index) words, gates, and
 //                     a per-block LDS histogram flushed with one atomic per bin.
+#include <type_traits>
+
+#include "group_small.h"
 #include "moe_internal.h"
 
 namespace moeffn {
@@ -171,6 +174,139 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 constexpr int kSelWaves = 4;     // waves per block
 
+// Selection for token t by one wavefront: keys, the group limit, k rounds of a wave-wide
+// arg-max, the gates, and the sigmoid of the shared gate's logit. Reads the token's raw
+// logits from scores and writes its keys back; wk is LDS scratch of E floats owned by
+// this wavefront; hist (LDS, may be NULL) counts the selected experts.
+template <int PER_LANE>
+__device__ __forceinline__ void select_token(
+    int t, float* __restrict__ scores, const float* __restrict__ logit_bias, const float* __restrict__ select_bias,
+    float* __restrict__ shared_gate, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int* hist,
+    float* wk, int E, int k, int score_fn, int renormalize, float route_scale, int n_groups, int topk_groups,
+    int group_topn) {
+  const int lane = threadIdx.x & 63;
+  const int gsz = n_groups > 0 ? E / n_groups : E;
+  float logit[PER_LANE], key[PER_LANE];
+  bool live[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    float l = 0.f;
+    if (live[i]) {
+      l = scores[(size_t)t * E + e];
+      if (logit_bias) l += logit_bias[e];
+    }
+    logit[i] = l;
+    float kv = l;
+    if (score_fn == MOE_SIGMOID) {
+      const float s = 1.0f / (1.0f + expf(-l));
+      logit[i] = s;  // for sigmoid routing keep s for the gates
+      kv = s;
+      if (select_bias && live[i]) kv = s + select_bias[e];
+    }
+    key[i] = kv;
+    if (live[i]) scores[(size_t)t * E + e] = kv;
+  }
+
+  // group limit: lanes g < n_groups score their group from the keys in LDS
+  if (n_groups > 1 && topk_groups < n_groups) {
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i)
+      if (live[i]) wk[lane + 64 * i] = key[i];
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint64_t gword = 0;
+    if (lane < n_groups) {
+      // the group's group_topn largest keys, summed largest first in fp32
+      float top[8];
+      const int nt = min(group_topn, 8);
+      for (int i = 0; i < nt; ++i) top[i] = -INFINITY;
+      for (int m = 0; m < gsz; ++m) {
+        float v = wk[lane * gsz + m];
+        for (int i = 0; i < nt; ++i) {
+          if (v > top[i]) { float tmp = top[i]; top[i] = v; v = tmp; }
+        }
+      }
+      float sum = top[0];
+      for (int i = 1; i < nt; ++i) sum = sum + top[i];
+      gword = pack_key(sum, lane);
+    }
+    uint64_t keep_mask = 0;
+    for (int r = 0; r < topk_groups; ++r) {
+      const uint64_t best = wave_max_u64(gword);
+      const int g = unpack_idx(best);
+      keep_mask |= 1ull << g;
+      if (lane == g) gword = 0;
+    }
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      const int e = lane + 64 * i;
+      if (live[i] && !((keep_mask >> (e / gsz)) & 1ull)) live[i] = false;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // top-k: k rounds of a wave-wide arg-max
+  int sel_idx = 0;
+  float sel_val = 0.f;  // logit (softmax) or s (sigmoid) of the lane-th winner
+  for (int r = 0; r < k; ++r) {
+    uint64_t mine = 0;
+    int mine_i = -1;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      if (live[i]) {
+        const uint64_t w = pack_key(key[i], lane + 64 * i);
+        if (w > mine) { mine = w; mine_i = i; }
+      }
+    }
+    const uint64_t best = wave_max_u64(mine);
+    const int e = unpack_idx(best);
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      if (lane + 64 * i == e) { live[i] = false; v = logit[i]; }
+    }
+    // broadcast the winner's value from its owner lane
+    const int owner = e & 63;
+    v = __shfl(v, owner, 64);
+    if (lane == r) { sel_idx = e; sel_val = v; }
+    (void)mine_i;
+  }
+
+  // gates (lanes r < k hold winner r)
+  float g = 0.f;
+  if (score_fn == MOE_SOFTMAX) {
+    const float m = __shfl(sel_val, 0, 64);  // the best key is the largest selected logit
+    if (renormalize) {
+      const float z = lane < k ? expf(sel_val - m) : 0.f;
+      const float denom = wave_sum_f32(z);
+      g = z / denom;
+    } else {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i)
+        if (lane + 64 * i < E) part += expf(logit[i] - m);
+      const float denom = wave_sum_f32(part);
+      g = lane < k ? expf(sel_val - m) / denom : 0.f;
+    }
+  } else {
+    const float s = lane < k ? sel_val : 0.f;
+    if (renormalize) g = s / wave_sum_f32(s);
+    else g = s;
+  }
+  g *= route_scale;
+  if (lane < k) {
+    topk_idx[(size_t)t * k + lane] = sel_idx;
+    topk_gate[(size_t)t * k + lane] = g;
+    if (hist) atomicAdd(&hist[sel_idx], 1);
+  }
+  if (shared_gate && lane == 0) {
+    const float l = shared_gate[t];
+    shared_gate[t] = 1.0f / (1.0f + expf(-l));
+  }
+}
+
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void route_select(
     float* __restrict__ scores, const float* __restrict__ logit_bias, const float* __restrict__ select_bias,
@@ -179,134 +315,16 @@ __global__ __launch_bounds__(256) void route_select(
     int n_groups, int topk_groups, int group_topn, int tok_per_wave) {
   __shared__ int hist[kMaxE];
   __shared__ float wkeys[kSelWaves][kMaxE];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   if (counts != nullptr)
     for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
   __syncthreads();
-
-  const int gsz = n_groups > 0 ? E / n_groups : E;
   for (int it = 0; it < tok_per_wave; ++it) {
     const int t = (blockIdx.x * kSelWaves + wave) * tok_per_wave + it;
     if (t >= T) break;
-    float logit[PER_LANE], key[PER_LANE];
-    bool live[PER_LANE];
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-      const int e = lane + 64 * i;
-      live[i] = e < E;
-      float l = 0.f;
-      if (live[i]) {
-        l = scores[(size_t)t * E + e];
-        if (logit_bias) l += logit_bias[e];
-      }
-      logit[i] = l;
-      float kv = l;
-      if (score_fn == MOE_SIGMOID) {
-        const float s = 1.0f / (1.0f + expf(-l));
-        logit[i] = s;  // for sigmoid routing keep s for the gates
-        kv = s;
-        if (select_bias && live[i]) kv = s + select_bias[e];
-      }
-      key[i] = kv;
-      if (live[i]) scores[(size_t)t * E + e] = kv;
-    }
-
-    // group limit: lanes g < n_groups score their group from the keys in LDS
-    if (n_groups > 1 && topk_groups < n_groups) {
-#pragma unroll
-      for (int i = 0; i < PER_LANE; ++i)
-        if (live[i]) wkeys[wave][lane + 64 * i] = key[i];
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      uint64_t gword = 0;
-      if (lane < n_groups) {
-        // the group's group_topn largest keys, summed largest first in fp32
-        float top[8];
-        const int nt = min(group_topn, 8);
-        for (int i = 0; i < nt; ++i) top[i] = -INFINITY;
-        for (int m = 0; m < gsz; ++m) {
-          float v = wkeys[wave][lane * gsz + m];
-          for (int i = 0; i < nt; ++i) {
-            if (v > top[i]) { float tmp = top[i]; top[i] = v; v = tmp; }
-          }
-        }
-        float sum = top[0];
-        for (int i = 1; i < nt; ++i) sum = sum + top[i];
-        gword = pack_key(sum, lane);
-      }
-      uint64_t keep_mask = 0;
-      for (int r = 0; r < topk_groups; ++r) {
-        const uint64_t best = wave_max_u64(gword);
-        const int g = unpack_idx(best);
-        keep_mask |= 1ull << g;
-        if (lane == g) gword = 0;
-      }
-#pragma unroll
-      for (int i = 0; i < PER_LANE; ++i) {
-        const int e = lane + 64 * i;
-        if (live[i] && !((keep_mask >> (e / gsz)) & 1ull)) live[i] = false;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-
-    // top-k: k rounds of a wave-wide arg-max
-    int sel_idx = 0;
-    float sel_val = 0.f;  // logit (softmax) or s (sigmoid) of the lane-th winner
-    for (int r = 0; r < k; ++r) {
-      uint64_t mine = 0;
-      int mine_i = -1;
-#pragma unroll
-      for (int i = 0; i < PER_LANE; ++i) {
-        if (live[i]) {
-          const uint64_t w = pack_key(key[i], lane + 64 * i);
-          if (w > mine) { mine = w; mine_i = i; }
-        }
-      }
-      const uint64_t best = wave_max_u64(mine);
-      const int e = unpack_idx(best);
-      float v = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER_LANE; ++i) {
-        if (lane + 64 * i == e) { live[i] = false; v = logit[i]; }
-      }
-      // broadcast the winner's value from its owner lane
-      const int owner = e & 63;
-      v = __shfl(v, owner, 64);
-      if (lane == r) { sel_idx = e; sel_val = v; }
-      (void)mine_i;
-    }
-
-    // gates (lanes r < k hold winner r)
-    float g = 0.f;
-    if (score_fn == MOE_SOFTMAX) {
-      const float m = __shfl(sel_val, 0, 64);  // the best key is the largest selected logit
-      if (renormalize) {
-        const float z = lane < k ? expf(sel_val - m) : 0.f;
-        const float denom = wave_sum_f32(z);
-        g = z / denom;
-      } else {
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i)
-          if (lane + 64 * i < E) part += expf(logit[i] - m);
-        const float denom = wave_sum_f32(part);
-        g = lane < k ? expf(sel_val - m) / denom : 0.f;
-      }
-    } else {
-      const float s = lane < k ? sel_val : 0.f;
-      if (renormalize) g = s / wave_sum_f32(s);
-      else g = s;
-    }
-    g *= route_scale;
-    if (lane < k) {
-      topk_idx[(size_t)t * k + lane] = sel_idx;
-      topk_gate[(size_t)t * k + lane] = g;
-      if (counts) atomicAdd(&hist[sel_idx], 1);
-    }
-    if (shared_gate && lane == 0) {
-      const float l = shared_gate[t];
-      shared_gate[t] = 1.0f / (1.0f + expf(-l));
-    }
+    select_token<PER_LANE>(t, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
+                           counts != nullptr ? hist : nullptr, wkeys[wave], E, k, score_fn, renormalize,
+                           route_scale, n_groups, topk_groups, group_topn);
   }
   if (counts != nullptr) {
     __syncthreads();
@@ -324,6 +342,121 @@ void launch_select(int tpw, hipStream_t s, float* scores, const float* lb, const
                      c.topk_groups, c.group_topn, tpw);
 }
 
+// -------------------------------------------------------- small batches ---
+// A decode step routes a handful of tokens. One workgroup computes their logits, selects
+// and groups them, so the three steps cost one launch instead of three. The logits use
+// the tiling of route_logits_mfma<1, 16> (16 waves split K; every wave keeps 1 m-tile x
+// 4 n-tiles of 16 and sums its K range in order; the partials are added in wave order),
+// except that a wave issues the loads of up to kFuseChunk k-steps at once. The selection
+// is select_token and the grouping group_small, so the outputs equal those of moe_route
+// followed by moe_permute bit for bit.
+constexpr int kFuseMaxT = 16;
+constexpr int kFuseMaxE = 256;
+constexpr int kFuseChunk = 2;
+
+template <int PER_LANE, int KMAX>
+__global__ __launch_bounds__(1024) void route_permute_small(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_router, const bf16_t* __restrict__ w_sg,
+    const float* __restrict__ logit_bias, const float* __restrict__ select_bias, float* __restrict__ shared_gate,
+    float* __restrict__ scores, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+    int32_t* __restrict__ perm_dst, int T, int d, int E, int k, int score_fn, int renormalize, float route_scale,
+    int n_groups, int topk_groups, int group_topn) {
+  __shared__ f32x4_t red[16][4][64];   // every wave's partial: [wave][n-tile][lane]
+  __shared__ float wkeys[16][kFuseMaxE];
+  __shared__ int32_t off[kFuseMaxE];
+  __shared__ int32_t wave_sum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ncols = E + (w_sg != nullptr ? 1 : 0);
+  const int KT = d / 32;
+  const int k0 = (KT * wave) / 16, k1 = (KT * (wave + 1)) / 16;
+  const int koff = 8 * (lane >> 4);
+  const bf16_t* arow = x + (size_t)min(lane & 15, T - 1) * d + koff;
+  for (int c0 = 0; c0 < ncols; c0 += 64) {
+    const int ntile = min(4, (ncols - c0 + 15) / 16);
+    const bf16_t* brow[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const int c = min(c0 + n * 16 + (lane & 15), ncols - 1);
+      brow[n] = (c < E ? w_router + (size_t)c * d : w_sg) + koff;
+    }
+    f32x4_t acc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int kc = k0; kc < k1; kc += kFuseChunk) {
+      bf16x8_t b[kFuseChunk][4], a[kFuseChunk];
+#pragma unroll
+      for (int c = 0; c < kFuseChunk; ++c) {
+        if (kc + c < k1) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            if (n < ntile) b[c][n] = *reinterpret_cast<const bf16x8_t*>(brow[n] + (kc + c) * 32);
+          a[c] = *reinterpret_cast<const bf16x8_t*>(arow + (kc + c) * 32);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kFuseChunk; ++c) {
+        if (kc + c < k1) {
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            if (n < ntile) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], b[c][n], acc[n], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) red[wave][n][lane] = acc[n];
+    __syncthreads();
+    {
+      // thread -> (n-tile, lane, row of the lane's 4): 4 x 64 x 4 = 1024 values
+      const int n = threadIdx.x >> 8, l = (threadIdx.x >> 2) & 63, i = threadIdx.x & 3;
+      if (n < ntile) {
+        float v = red[0][n][l][i];
+        for (int w = 1; w < 16; ++w) v += red[w][n][l][i];
+        // D layout: lane l holds rows 4*(l/16)+i, column l%16
+        const int c = c0 + n * 16 + (l & 15);
+        const int t = 4 * (l >> 4) + i;
+        if (t < T && c < ncols) {
+          if (c < E) scores[(size_t)t * E + c] = v;
+          else shared_gate[t] = v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (wave < T)
+    select_token<PER_LANE>(wave, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, nullptr,
+                           wkeys[wave], E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn);
+  __syncthreads();
+  group_small<KMAX>(topk_idx, counts, offsets, perm_src, perm_dst, T, k, E, off, wave_sum);
+}
+
+// Configuration checks shared by moe_route and moe_route_permute.
+moe_status check_route_cfg(const moe_route_cfg& c, const char* who) {
+  MOE_REQUIRE(c.T >= 0, MOE_EINVAL, "%s: T=%d < 0", who, c.T);
+  MOE_REQUIRE(c.d_model >= 1 && c.d_model % 8 == 0, MOE_EINVAL, "%s: d_model=%d must be a positive multiple of 8", who,
+              c.d_model);
+  MOE_REQUIRE(c.n_experts >= 1 && c.n_experts <= kMaxE, MOE_EINVAL, "%s: n_experts=%d outside [1, %d]", who,
+              c.n_experts, kMaxE);
+  MOE_REQUIRE(c.top_k >= 1 && c.top_k <= c.n_experts && c.top_k <= kMaxK, MOE_EINVAL,
+              "%s: top_k=%d outside [1, min(E, %d)]", who, c.top_k, kMaxK);
+  MOE_REQUIRE(c.score_fn == MOE_SOFTMAX || c.score_fn == MOE_SIGMOID, MOE_EINVAL, "%s: bad score_fn %d", who,
+              c.score_fn);
+  MOE_REQUIRE(c.act_dtype == MOE_F32 || c.act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "%s: act_dtype %d unsupported", who,
+              c.act_dtype);
+  const int G = c.n_groups < 1 ? 1 : c.n_groups;
+  if (G > 1) {
+    MOE_REQUIRE(G <= kMaxGroups && c.n_experts % G == 0, MOE_EINVAL, "%s: n_groups=%d must divide E=%d (max %d)", who,
+                G, c.n_experts, kMaxGroups);
+    MOE_REQUIRE(c.topk_groups >= 1 && c.topk_groups <= G, MOE_EINVAL, "%s: topk_groups=%d outside [1, n_groups]", who,
+                c.topk_groups);
+    MOE_REQUIRE(c.group_topn >= 1 && c.group_topn <= c.n_experts / G && c.group_topn <= 8, MOE_EINVAL,
+                "%s: group_topn=%d outside [1, min(E/n_groups, 8)]", who, c.group_topn);
+    MOE_REQUIRE(c.top_k <= c.topk_groups * (c.n_experts / G), MOE_EINVAL, "%s: top_k exceeds the experts of the kept groups",
+                who);
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moeffn
 
@@ -336,22 +469,9 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
   clear_error();
   MOE_REQUIRE(cfg != nullptr, MOE_EINVAL, "moe_route: cfg is NULL");
   const moe_route_cfg c = *cfg;
-  MOE_REQUIRE(c.T >= 0, MOE_EINVAL, "moe_route: T=%d < 0", c.T);
-  MOE_REQUIRE(c.d_model >= 1 && c.d_model % 8 == 0, MOE_EINVAL, "moe_route: d_model=%d must be a positive multiple of 8", c.d_model);
-  MOE_REQUIRE(c.n_experts >= 1 && c.n_experts <= kMaxE, MOE_EINVAL, "moe_route: n_experts=%d outside [1, %d]", c.n_experts, kMaxE);
-  MOE_REQUIRE(c.top_k >= 1 && c.top_k <= c.n_experts && c.top_k <= kMaxK, MOE_EINVAL,
-              "moe_route: top_k=%d outside [1, min(E, %d)]", c.top_k, kMaxK);
-  MOE_REQUIRE(c.score_fn == MOE_SOFTMAX || c.score_fn == MOE_SIGMOID, MOE_EINVAL, "moe_route: bad score_fn %d", c.score_fn);
-  MOE_REQUIRE(c.act_dtype == MOE_F32 || c.act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_route: act_dtype %d unsupported", c.act_dtype);
+  if (moe_status st = check_route_cfg(c, "moe_route")) return st;
   MOE_REQUIRE(!(select_bias && c.score_fn == MOE_SOFTMAX), MOE_EINVAL, "moe_route: select_bias needs sigmoid scoring");
   const int G = c.n_groups < 1 ? 1 : c.n_groups;
-  if (G > 1) {
-    MOE_REQUIRE(G <= kMaxGroups && c.n_experts % G == 0, MOE_EINVAL, "moe_route: n_groups=%d must divide E=%d (max %d)", G, c.n_experts, kMaxGroups);
-    MOE_REQUIRE(c.topk_groups >= 1 && c.topk_groups <= G, MOE_EINVAL, "moe_route: topk_groups=%d outside [1, n_groups]", c.topk_groups);
-    MOE_REQUIRE(c.group_topn >= 1 && c.group_topn <= c.n_experts / G && c.group_topn <= 8, MOE_EINVAL,
-                "moe_route: group_topn=%d outside [1, min(E/n_groups, 8)]", c.group_topn);
-    MOE_REQUIRE(c.top_k <= c.topk_groups * (c.n_experts / G), MOE_EINVAL, "moe_route: top_k exceeds the experts of the kept groups");
-  }
   if (c.T == 0) return MOE_OK;   // nothing to write: empty outputs may have null pointers
   MOE_REQUIRE((w_shared_gate == nullptr) == (shared_gate == nullptr), MOE_EINVAL,
               "moe_route: w_shared_gate and shared_gate go together");
@@ -398,4 +518,57 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
   else if (per_lane <= 4) launch_select<4>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
   else launch_select<16>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
   return check_launch("moe_route select");
+}
+
+extern "C" moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x, const void* w_router,
+                                        const float* logit_bias, const float* select_bias,
+                                        const void* w_shared_gate, float* shared_gate, float* scores,
+                                        int32_t* topk_idx, float* topk_gate, int32_t* counts, int32_t* offsets,
+                                        int32_t* perm_src, int32_t* perm_dst, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  clear_error();
+  MOE_REQUIRE(cfg != nullptr, MOE_EINVAL, "moe_route_permute: cfg is NULL");
+  const moe_route_cfg c = *cfg;
+  if (moe_status st = check_route_cfg(c, "moe_route_permute")) return st;
+  const bool fused = c.T >= 1 && c.T <= kFuseMaxT && c.n_experts <= kFuseMaxE && c.act_dtype == MOE_BF16 &&
+                     c.d_model % 32 == 0;
+  if (!fused) {
+    if (moe_status st = moe_route(cfg, x, w_router, logit_bias, select_bias, w_shared_gate, shared_gate, scores,
+                                  topk_idx, topk_gate, counts, stream))
+      return st;
+    return moe_permute(c.T, c.top_k, c.n_experts, topk_idx, offsets, perm_src, perm_dst, 0, nullptr, 0, nullptr, 0,
+                       nullptr, 0, ws, ws_bytes, stream);
+  }
+  MOE_REQUIRE(!(select_bias && c.score_fn == MOE_SOFTMAX), MOE_EINVAL,
+              "moe_route_permute: select_bias needs sigmoid scoring");
+  MOE_REQUIRE((w_shared_gate == nullptr) == (shared_gate == nullptr), MOE_EINVAL,
+              "moe_route_permute: w_shared_gate and shared_gate go together");
+  MOE_REQUIRE(x && w_router && scores && topk_idx && topk_gate && offsets && perm_src && perm_dst && ws, MOE_EINVAL,
+              "moe_route_permute: NULL tensor argument");
+  MOE_REQUIRE(aligned(x, 16) && aligned(w_router, 16) && (!w_shared_gate || aligned(w_shared_gate, 16)), MOE_EINVAL,
+              "moe_route_permute: x, w_router, w_shared_gate must be 16-byte aligned");
+  const size_t need = moe_permute_workspace_size(c.T, c.top_k, c.n_experts);
+  MOE_REQUIRE(ws_bytes >= need, MOE_ECAPACITY, "moe_route_permute: workspace %zu < %zu bytes", ws_bytes, need);
+  hipStream_t s = as_stream(stream);
+  const int G = c.n_groups < 1 ? 1 : c.n_groups;
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const bf16_t* wb = static_cast<const bf16_t*>(w_router);
+  const bf16_t* sgb = static_cast<const bf16_t*>(w_shared_gate);
+  auto go = [&](auto pl, auto km) {
+    constexpr int PL = decltype(pl)::value, KM = decltype(km)::value;
+    hipLaunchKernelGGL((route_permute_small<PL, KM>), dim3(1), dim3(1024), 0, s, xb, wb, sgb, logit_bias,
+                       select_bias, shared_gate, scores, topk_idx, topk_gate, counts, offsets, perm_src, perm_dst,
+                       c.T, c.d_model, c.n_experts, c.top_k, c.score_fn, c.renormalize, c.route_scale, G,
+                       c.topk_groups, c.group_topn);
+  };
+  auto by_k = [&](auto pl) {
+    if (c.top_k <= 2) go(pl, std::integral_constant<int, 2>{});
+    else if (c.top_k <= 4) go(pl, std::integral_constant<int, 4>{});
+    else if (c.top_k <= 8) go(pl, std::integral_constant<int, 8>{});
+    else go(pl, std::integral_constant<int, 32>{});
+  };
+  if (c.n_experts <= 64) by_k(std::integral_constant<int, 1>{});
+  else if (c.n_experts <= 128) by_k(std::integral_constant<int, 2>{});
+  else by_k(std::integral_constant<int, 4>{});
+  return check_launch("moe_route_permute");
 }

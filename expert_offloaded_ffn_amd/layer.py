@@ -2,8 +2,8 @@
 
 Holds the packed expert bundles (a resident pool with an identity slot table, or
 an expert slot pool fed from pinned host bundles), the router weights and the
-workspaces, and runs route -> permute -> grouped FFN (routed, then shared) ->
-combine as calls into libmoeffn. No arithmetic of the layer happens here.
+workspaces, and runs route + permute -> grouped FFN (routed, and the shared expert on a side
+stream) -> combine as calls into libmoeffn. No arithmetic of the layer happens here.
 """
 from __future__ import annotations
 
@@ -119,6 +119,11 @@ class MoELayer:
             self._side = torch.cuda.Stream(device=self.device)
         return self._side
 
+    def shared_in_decode_launch(self, T: int) -> bool:
+        """Whether a T-token forward runs the shared expert inside the routed experts' decode
+        launches (bf16, resident experts, at most 64 rows per expert) instead of on a side stream."""
+        return (self.shared is not None and self.cache is None and self.w_code == B.MOE_BF16 and 0 < T <= 64)
+
     def _shared_ffn(self, T, a, a_scale, a_code, ydt, main):
         """Launches the shared expert's FFN on the side stream once `a` is ready on `main`; the
         caller joins the side stream back before the combine."""
@@ -137,22 +142,22 @@ class MoELayer:
 
     def forward(self, x: torch.Tensor, logit_bias: torch.Tensor | None = None, stream=None) -> dict:
         """x [T, d] device tensor in the activation dtype. Returns the layer output and routing tensors.
-        The shared expert (when there is one) runs on a second stream, concurrently with the
-        routing and the routed experts, and is joined before the combine."""
+        The shared expert (when there is one) runs inside the routed experts' launches for a
+        decode step (shared_in_decode_launch), else on a second stream, forked once the routing
+        is issued, concurrently with the routed experts, and joined before the combine."""
         T = x.shape[0]
         k, E, d = self.k, self.E, self.d
         main = torch.cuda.current_stream(self.device) if stream is None else stream
         ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
         shared_y = None
-        if self.shared is not None and self.w_code != B.MOE_FP8_E4M3:
-            shared_y = self._shared_ffn(T, x, None, self.act_code, ydt, main)
-        r = B.route(x, self.w_router_t, logit_bias=logit_bias, select_bias=self.select_bias,
-                    w_shared_gate=self.w_sg, stream=main, **self.route_args())
+        merged = self.shared_in_decode_launch(T)
         ws = self._buf("perm_ws", B.permute_workspace_size(T, k, E))
         rows = T * k
         y = torch.empty(rows, d, device=self.device, dtype=torch.float32 if ydt == B.MOE_F32 else torch.bfloat16)
         a, a_scale, a_code = x, None, self.act_code
         if self.w_code == B.MOE_FP8_E4M3:
+            r = B.route(x, self.w_router_t, logit_bias=logit_bias, select_bias=self.select_bias,
+                        w_shared_gate=self.w_sg, stream=main, **self.route_args())
             # grouping plus one e4m3 quantisation of every token (token order); the GEMMs
             # gather rows through perm_src
             p = B.permute(r["idx"], E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=0, ws=ws, stream=main)
@@ -160,13 +165,30 @@ class MoELayer:
             if self.shared is not None:
                 shared_y = self._shared_ffn(T, a, a_scale, a_code, ydt, main)
         else:
-            p = B.permute(r["idx"], E, ws=ws, stream=main)
-        fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
-        if self.cache is None:
+            # routing and grouping in one call; the routed chain is the critical path, so it
+            # is issued first and the shared expert forks off behind it
+            r = p = B.route_permute(x, self.w_router_t, logit_bias=logit_bias, select_bias=self.select_bias,
+                                    w_shared_gate=self.w_sg, ws=ws, stream=main, **self.route_args())
+            if self.shared is not None and not merged:
+                shared_y = self._shared_ffn(T, x, None, self.act_code, ydt, main)
+        if merged:
+            # a decode step: the shared expert's blocks (dispatched first, they carry the longer
+            # rows of its down projection) and the routed experts' share one launch per GEMM
+            shared_y = torch.empty(T, d, device=self.device, dtype=y.dtype)
+            probs = [B.ffn_problem(self.shared.table, T, self._shared_offsets(T), x, act_dtype=self.act_code,
+                                   y=shared_y, y_dtype=ydt),
+                     B.ffn_problem(self.table, rows, p["offsets"], a, act_dtype=a_code, a_row_src=p["perm_src"],
+                                   a_row_div=k, y=y, y_dtype=ydt)]
+            bws = self._buf("batch_ws", B.grouped_ffn_batch_workspace_size(probs))
+            B.grouped_ffn_batch(probs, ws=bws, stream=main)
+            waves = 0
+        elif self.cache is None:
+            fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
             B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
                           a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=main)
             waves = 0
         else:
+            fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
             waves = self.cache.acquire(r["counts"], stream=main)
             for w in range(waves):
                 for part in (0, 1):
@@ -175,7 +197,7 @@ class MoELayer:
                         B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
                                       a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=main)
                 self.cache.release(w, stream=main)
-        if shared_y is not None:
+        if shared_y is not None and not merged:
             main.wait_stream(self._side_stream())
         out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"], stream=main)
         return {"out": out, "route": r, "perm": p, "y": y, "shared_y": shared_y, "waves": waves}

@@ -148,6 +148,24 @@ moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_idx,
                        int32_t out_dtype, float* x_out_scale, int32_t gather,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------ route + permute --
+ * moe_route followed by moe_permute without row materialisation (x_out NULL), as
+ * one call: the router's expert list goes straight to the grouping that decides
+ * which experts run ([VVLLM] "Technical Insight": the expert list is intercepted
+ * between the router and the expert kernels). The outputs and their meaning are
+ * exactly those of the two calls (same arguments, same errors); counts may be NULL.
+ * Batches of 1..16 bf16 tokens with d % 32 == 0 and E <= 256 (a decode step) run as
+ * a single workgroup launch whose outputs equal the two calls' bit for bit; other
+ * batches make the two calls.
+ * Workspace: moe_permute_workspace_size(T, k, E) bytes at `ws` (256-B aligned).
+ */
+moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x, const void* w_router,
+                             const float* logit_bias, const float* select_bias,
+                             const void* w_shared_gate, float* shared_gate, float* scores,
+                             int32_t* topk_idx, float* topk_gate, int32_t* counts,
+                             int32_t* offsets, int32_t* perm_src, int32_t* perm_dst,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------ expert table --
  * Where each expert's bundle lives. A bundle is one contiguous block holding an
  * expert's three matrices and, for fp8, their scales: the atomic unit of
@@ -225,6 +243,37 @@ moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t rows, const in
                            const void* a, const float* a_scale, int32_t act_dtype,
                            const int32_t* a_row_src, int32_t a_row_div,
                            void* y, int32_t y_dtype, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------- grouped FFN batch --
+ * One or two independent grouped FFN problems, each with exactly the meaning,
+ * argument rules and errors of a moe_grouped_ffn call with the same fields (the
+ * problem's index is named in error messages). Meant for the routed experts and
+ * the always-resident shared expert of one layer ([VVLLM] "Gotcha": shared
+ * experts sit outside the routed set): when both problems are bf16 with at most
+ * 64 rows per expert (a decode step), they share one gate/up launch and one down
+ * launch, with the first problem's work dispatched first, instead of running
+ * on two streams that a graph must fork and join. Otherwise the problems run one
+ * after the other on `stream`. n must be 1 or 2.
+ * Workspace: moe_grouped_ffn_batch_workspace_size(problems, n) bytes at `ws`
+ * (256-B aligned): each problem's moe_grouped_ffn workspace, in order, each
+ * rounded up to a multiple of 256 B.
+ */
+typedef struct {
+  const moe_expert_table* table;
+  int32_t rows;
+  const int32_t* offsets;
+  const void* a;
+  const float* a_scale;
+  int32_t act_dtype;
+  const int32_t* a_row_src;
+  int32_t a_row_div;
+  void* y;
+  int32_t y_dtype;
+} moe_ffn_problem;
+
+size_t moe_grouped_ffn_batch_workspace_size(const moe_ffn_problem* problems, int32_t n);
+moe_status moe_grouped_ffn_batch(const moe_ffn_problem* problems, int32_t n, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* ---------------------------------------------------------------- combine --
  * Gate-weighted sum of each token's expert outputs back in token order, plus

@@ -1,5 +1,5 @@
 """bench.py host logic: the traffic figure comes from the committed counter summary only while
-the kernel source still has the recorded hash."""
+every source file of the kernel still has the recorded hash."""
 import hashlib
 import json
 import os
@@ -24,13 +24,17 @@ def test_traffic_records_are_well_formed():
     assert recs, "no traffic record under profiles/"
     for r in recs:
         assert r["bytes_per_launch"] == r["fetch_bytes_per_launch"] + r["write_bytes_per_launch"]
-        assert os.path.exists(os.path.join(ROOT, r["source"]))
+        assert r["sources"], "a record names the files its kernel is built from"
+        for rel in r["sources"]:
+            assert os.path.exists(os.path.join(ROOT, rel)), rel
 
 
 def test_traffic_follows_source_hash():
     for r in _records():
-        with open(os.path.join(ROOT, r["source"]), "rb") as f:
-            same = hashlib.sha256(f.read()).hexdigest() == r["source_sha256"]
+        same = True
+        for rel, sha in r["sources"].items():
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                same &= hashlib.sha256(f.read()).hexdigest() == sha
         got = bench.recorded_traffic(r["workload"], r["kernel"])
         assert got == (r["bytes_per_launch"] if same else None)
     assert bench.recorded_traffic("no_such_workload", "no_such_kernel") is None

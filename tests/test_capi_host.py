@@ -5,6 +5,7 @@ device, the bundle packer writes the documented layout, and the slot-pool planne
 import ctypes
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -75,6 +76,63 @@ def test_grouped_ffn_validation_codes():
     t = B.ExpertTable(ctypes.c_void_p(256), nb - 256, ctypes.c_void_p(256), 8, 4096, 14336, B.MOE_BF16)
     assert L.moe_grouped_ffn(ctypes.byref(t), 16, *([None] * 3), 1, None, 1, None, 1, None, 0, None) == -1
     assert b"slot_stride" in L.moe_last_error()
+
+
+_STRUCTS = [("moe_route_cfg", B.RouteCfg), ("moe_expert_table", B.ExpertTable), ("moe_ffn_problem", B.FfnProblem),
+            ("moe_cache_cfg", B.CacheCfg), ("moe_cache_stats", B.CacheStats), ("moe_cache_entry", B.CacheEntry),
+            ("moe_profile", B.Profile)]
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """Every ctypes mirror has the size and field offsets the C compiler gives the header's struct."""
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "moe.h"', "int main(void) {"]
+    for cname, py in _STRUCTS:
+        lines.append(f'  printf("{cname} %zu\\n", sizeof({cname}));')
+        for f, _ in py._fields_:
+            lines.append(f'  printf("{cname}.{f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = dict(line.split() for line in subprocess.run([str(exe)], check=True, capture_output=True,
+                                                           text=True).stdout.splitlines())
+    for cname, py in _STRUCTS:
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for f, _ in py._fields_:
+            assert int(got[f"{cname}.{f}"]) == getattr(py, f).offset, f"{cname}.{f}"
+
+
+def test_batch_and_route_permute_validation_codes():
+    L = B.lib()
+    assert L.moe_grouped_ffn_batch(None, 1, None, 0, None) == -1
+    t = B.ExpertTable(ctypes.c_void_p(256), B.bundle_bytes(256, 512, B.MOE_BF16), ctypes.c_void_p(256), 8, 256, 512,
+                      B.MOE_BF16)
+    fake = ctypes.c_void_p(0x1000)
+    pr = B.FfnProblem(ctypes.pointer(t), 16, fake, fake, None, B.MOE_BF16, None, 1, fake, B.MOE_BF16)
+    arr = (B.FfnProblem * 3)(pr, pr, pr)
+    assert L.moe_grouped_ffn_batch(arr, 3, fake, 1 << 20, None) == -1               # n outside [1, 2]
+    one = L.moe_grouped_ffn_workspace_size(ctypes.byref(t), 16, B.MOE_BF16)
+    need = L.moe_grouped_ffn_batch_workspace_size(arr, 2)
+    assert need == 2 * ((one + 255) // 256 * 256)
+    assert L.moe_grouped_ffn_batch(arr, 2, None, need, None) == -1                 # no workspace
+    assert L.moe_grouped_ffn_batch(arr, 2, fake, need - 1, None) == -4             # short workspace
+    empty = B.FfnProblem(ctypes.pointer(t), 0, None, None, None, B.MOE_BF16, None, 1, None, B.MOE_BF16)
+    assert L.moe_grouped_ffn_batch((B.FfnProblem * 2)(empty, empty), 2, None, 0, None) == 0
+    nul = B.FfnProblem(None, 4, None, None, None, B.MOE_BF16, None, 1, None, B.MOE_BF16)
+    assert L.moe_grouped_ffn_batch((B.FfnProblem * 1)(nul), 1, fake, need, None) == -1
+    assert b"no table" in L.moe_last_error()
+    null = None
+    assert L.moe_route_permute(None, *([null] * 14), 0, null) == -1
+    bad = B.RouteCfg(4, 128, 8, 9, 0, 1, 1.0, 1, 1, 0, B.MOE_BF16)                # k > E
+    assert L.moe_route_permute(ctypes.byref(bad), *([null] * 14), 0, null) == -1
+    assert b"moe_route_permute" in L.moe_last_error()
+    cfg = B.RouteCfg(4, 128, 8, 2, 0, 1, 1.0, 1, 1, 0, B.MOE_BF16)
+    args = [fake] * 14                                                              # 13 tensors and ws
+    args[3] = None                                                                  # select_bias: softmax has none
+    assert L.moe_route_permute(ctypes.byref(cfg), *args, 0, null) == -4             # short workspace
+    args[1] = ctypes.c_void_p(0x1001)                                               # misaligned router weights
+    assert L.moe_route_permute(ctypes.byref(cfg), *args, 1 << 16, null) == -1
 
 
 def test_pack_bf16_layout():

@@ -233,3 +233,91 @@ def test_decode_graph_replay_matches_eager(T):
         assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {i} differs from eager"
     # and the replayed output still matches the oracle
     _run_and_check(cfg, layer, w, T, 13)
+
+
+_RP_CASES = [
+    # config, overrides, T: the fused single-workgroup path (T <= 16, E <= 256) and the two-call path
+    ("qwen_decode_bf16", {}, 1),
+    ("qwen_decode_bf16", {}, 8),
+    ("qwen_decode_bf16", {}, 16),
+    ("qwen_decode_bf16", {}, 17),
+    ("qwen_decode_bf16", {}, 64),
+    ("dsv3_prefill_fp8", dict(d=512, E=256, k=8), 16),                  # grouped sigmoid, E = 256
+    ("dsv3_prefill_fp8", dict(d=256, E=64, k=8, n_groups=8, topk_groups=3), 5),
+    ("offload_decode_bf16", dict(d=512), 7),                              # E = 128, logit prior
+    ("offload_decode_bf16", dict(d=512), 32),
+    ("mixtral_prefill_bf16", dict(d=96, k=1), 3),                         # fewer k-steps than waves, top-1
+    ("mixtral_prefill_bf16", dict(d=256, E=40, k=12), 9),                 # k > 8
+]
+
+
+@pytest.mark.parametrize("name,over,T", _RP_CASES)
+def test_route_permute_equals_route_then_permute(name, over, T):
+    """moe_route_permute gives exactly the outputs of moe_route followed by moe_permute, and both
+    meet the routing contract against the oracle."""
+    cfg = synth.get_config(name, T=T, **over)
+    router = synth.gen_router(cfg)
+    w_sg = synth.gen_shared_gate(cfg) if cfg.shared_gate else None
+    sb = synth.gen_select_bias(cfg) if cfg.select_bias else None
+    lb = np.random.default_rng([7, T]).normal(0, 2.0, cfg.E).astype(np.float32) if name.startswith("offload") else None
+    x_store = synth.gen_x(cfg, 0, T=T)
+    x = _x_dev(cfg, x_store)
+    wr = torch.from_numpy(np.ascontiguousarray(router.T).view(np.int16)).view(torch.bfloat16).to(DEV)
+    sg_dev = None if w_sg is None else torch.from_numpy(w_sg.view(np.int16)).view(torch.bfloat16).to(DEV)
+    kw = dict(k=cfg.k, score_fn=B.MOE_SIGMOID if cfg.score_fn == "sigmoid" else B.MOE_SOFTMAX,
+              renormalize=cfg.renormalize, route_scale=cfg.route_scale, n_groups=cfg.n_groups,
+              topk_groups=cfg.topk_groups, group_topn=cfg.group_topn,
+              logit_bias=None if lb is None else torch.from_numpy(lb).to(DEV),
+              select_bias=None if sb is None else torch.from_numpy(sb).to(DEV), w_shared_gate=sg_dev)
+    say(f"  case route_permute {name} {over} T={T}: launching")
+    fused = B.route_permute(x, wr, **kw)
+    r = B.route(x, wr, **kw)
+    p = B.permute(r["idx"], cfg.E)
+    torch.cuda.synchronize()
+    say("    done")
+    for key, ref in [("scores", r), ("idx", r), ("gate", r), ("counts", r), ("shared_gate", r), ("offsets", p),
+                     ("perm_src", p), ("perm_dst", p)]:
+        if ref[key] is None:
+            assert fused[key] is None
+            continue
+        a, b = fused[key].cpu(), ref[key].cpu()
+        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                           b.view(torch.int32) if b.dtype == torch.float32 else b), f"{key} differs"
+    check_exact_indices(cfg, fused, fused, T)
+    r_ref = oracle_route(cfg, x_store, router, w_sg, sb, lb)
+    route_agreement(cfg, r_ref, fused, key_tol=1e-4)
+
+
+def test_route_permute_empty_batch():
+    cfg = synth.get_config("qwen_decode_bf16", T=0)
+    wr = torch.zeros(cfg.E, cfg.d, device=DEV, dtype=torch.bfloat16)
+    x = torch.zeros(0, cfg.d, device=DEV, dtype=torch.bfloat16)
+    out = B.route_permute(x, wr, k=cfg.k)
+    torch.cuda.synchronize()
+    assert out["offsets"].cpu().eq(0).all()
+
+
+@pytest.mark.parametrize("T", [1, 5, 64, 100])
+def test_grouped_ffn_batch_equals_separate_calls(T):
+    """The shared and the routed experts through moe_grouped_ffn_batch (one launch per GEMM for a
+    decode step, else one call after the other) give exactly the outputs of two moe_grouped_ffn calls."""
+    cfg = synth.get_config("qwen_decode_bf16", T=T, d=256, E=16, k=4, F=256, F_shared=512)
+    layer, w = _build(cfg)
+    x = _x_dev(cfg, synth.gen_x(cfg, 0, T=T))
+    say(f"  case grouped_ffn_batch T={T}: launching")
+    r = B.route_permute(x, layer.w_router_t, w_shared_gate=layer.w_sg, **layer.route_args())
+    rows = T * cfg.k
+    offs = torch.tensor([0, T], dtype=torch.int32).to(DEV)
+    y_sep = B.grouped_ffn(layer.table, rows, r["offsets"], x, a_row_src=r["perm_src"], a_row_div=cfg.k)
+    s_sep = B.grouped_ffn(layer.shared.table, T, offs, x)
+    probs = [B.ffn_problem(layer.shared.table, T, offs, x),
+             B.ffn_problem(layer.table, rows, r["offsets"], x, a_row_src=r["perm_src"], a_row_div=cfg.k)]
+    s_bat, y_bat = B.grouped_ffn_batch(probs)
+    torch.cuda.synchronize()
+    say("    done")
+    assert torch.equal(y_bat.view(torch.int16).cpu(), y_sep.view(torch.int16).cpu())
+    assert torch.equal(s_bat.view(torch.int16).cpu(), s_sep.view(torch.int16).cpu())
+    # and the shared expert's output against the oracle
+    shared = oracle_expert(cfg, w["shared"])
+    ref = moe.swiglu_ffn(decode(synth.gen_x(cfg, 0, T=T), cfg.act_dtype), shared.w_gate, shared.w_up, shared.w_down)
+    assert_close(to_np(s_bat), ref, cfg.dtype, "shared expert")
