@@ -11,7 +11,9 @@ namespace {
 // Few rows per expert (decode batches): the layer is bound by streaming each active
 // expert's weights once from HBM. A workgroup owns one active expert and one group of
 // 32 weight rows (GATEUP: 16 gate + 16 up rows -> 16 hidden columns; DOWN: 32 output
-// columns); its 8 waves split K. Weight tiles go straight from global memory into MFMA
+// columns); its 8 waves split K. A long down projection over at most 64 rows (a shared
+// expert's) is also split over K across workgroups, whose fp32 partials the last one to
+// arrive adds in a fixed order. Weight tiles go straight from global memory into MFMA
 // B fragments (the bundle's 1 KiB tile layout is the fragment layout, so every wave load
 // is 1 KiB contiguous); A rows (at most 64 per pass, in m-blocks of 16) come from L2.
 // The split-K partials are summed through LDS in wave order (deterministic).
@@ -51,6 +53,12 @@ struct DecodeArgs {
   int N, K;
   void* out;
   int out_dtype;
+  int rows;          // the problem's rows (indexing of the split partials)
+  int splits;        // DOWN: workgroups sharing one (expert, group)'s K range; 1 otherwise
+  float* part;       // DOWN with splits > 1: fp32 partials [splits][rows][N]
+  int32_t* arrived;  // DOWN with splits > 1: per (active expert, group) arrival counts
+  int32_t* clear;    // GATEUP: the arrival counts of the down launch that follows, cleared here
+  int clear_n;
 };
 
 #ifndef MOEFFN_DEC_CHUNK
@@ -64,25 +72,40 @@ struct DecodeArgs {
 #endif
 constexpr int kDecChunk = MOEFFN_DEC_CHUNK;   // k-tiles whose loads are issued together
 constexpr int kDecWaves = MOEFFN_DEC_WAVES;   // waves per workgroup (split-K)
+constexpr int kDecMaxSplits = 8;              // workgroups per (expert, group) of a split down GEMM
 
 // Blocks [0, nb0) work on problem p0, the rest on p1 (two independent grouped FFNs, e.g.
-// the routed experts and the shared expert, in one launch).
-template <int MODE>
+// the routed experts and the shared expert, in one launch). SPLIT launches carry a down
+// projection split over K (and, for GATEUP, clear its arrival counts); the others compile
+// without that code.
+template <int MODE, bool SPLIT>
 __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(DecodeArgs p0, DecodeArgs p1,
                                                                                        int nb0) {
   __shared__ f32x4_t red[kDecWaves - 1][4][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
+  __shared__ int s_last;                               // split K: this workgroup arrived last
   const bool second = (int)blockIdx.x >= nb0;
   const DecodeArgs p = second ? p1 : p0;
   const int bid = second ? (int)blockIdx.x - nb0 : (int)blockIdx.x;
+  if constexpr (SPLIT && MODE == MODE_GATEUP) {
+    if (bid == 0 && p.clear != nullptr)
+      for (int j = threadIdx.x; j < p.clear_n; j += blockDim.x) p.clear[j] = 0;
+  }
+  // The block's coordinates are uniform; integer division runs on the vector unit, so they
+  // are moved back to scalar registers, which keeps the expert's offsets and slot on scalar loads.
   const int G = p.N / 32;
-  const int i = bid / G, g = bid % G;
-  const int e = nth_active_expert(p.offsets, p.slot_of_expert, p.E, i);
+  const int S = (SPLIT && MODE == MODE_DOWN) ? p.splits : 1;
+  const int unit = __builtin_amdgcn_readfirstlane(bid / S);   // (active expert, group)
+  const int s = bid - unit * S;                               // K split
+  const int i = __builtin_amdgcn_readfirstlane(unit / G);
+  const int g = unit - i * G;
+  const int e = __builtin_amdgcn_readfirstlane(nth_active_expert(p.offsets, p.slot_of_expert, p.E, i));
   if (e < 0) return;
   const int row0 = p.offsets[e];
   const int n_e = p.offsets[e + 1] - row0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int KT = p.K / 32;
-  const int kt0 = (KT * w) / kDecWaves, kt1 = (KT * (w + 1)) / kDecWaves;
+  const int ks0 = (KT * s) / S, ks = (KT * (s + 1)) / S - ks0;   // this split's k-steps
+  const int kt0 = ks0 + (ks * w) / kDecWaves, kt1 = ks0 + (ks * (w + 1)) / kDecWaves;
   const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
   const char* b0 = B + ((int64_t)(2 * g) * KT) * 1024 + 16 * lane;      // n-tile 2g
   const char* b1 = B + ((int64_t)(2 * g + 1) * KT) * 1024 + 16 * lane;  // n-tile 2g+1
@@ -102,21 +125,26 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
     for (int m = 0; m < 4; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int k0 = kt0; k0 < kt1; k0 += kDecChunk) {
       const int nk = min(kDecChunk, kt1 - k0);
+      // the chunk's tiles as constant offsets from one pointer per n-tile, so the loads issue
+      // back to back with immediate offsets
+      const char* q0 = b0 + (int64_t)k0 * 1024;
+      const char* q1 = b1 + (int64_t)k0 * 1024;
       bf16x8_t fb[kDecChunk][2];
 #pragma unroll
       for (int c = 0; c < kDecChunk; ++c) {
         if (c < nk) {
-          fb[c][0] = *reinterpret_cast<const bf16x8_t*>(b0 + (int64_t)(k0 + c) * 1024);
-          fb[c][1] = *reinterpret_cast<const bf16x8_t*>(b1 + (int64_t)(k0 + c) * 1024);
+          fb[c][0] = *reinterpret_cast<const bf16x8_t*>(q0 + c * 1024);
+          fb[c][1] = *reinterpret_cast<const bf16x8_t*>(q1 + c * 1024);
         }
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         if (m < mbn) {
+          const bf16_t* qa = arow[m] + (int64_t)k0 * 32;
 #pragma unroll
           for (int c = 0; c < kDecChunk; ++c) {
             if (c < nk) {
-              const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(arow[m] + (k0 + c) * 32);
+              const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(qa + c * 32);
               acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c][0], acc[m][0], 0, 0, 0);
               acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, fb[c][1], acc[m][1], 0, 0, 0);
             }
@@ -149,14 +177,57 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
             const int F = p.N / 2;
             static_cast<bf16_t*>(p.out)[(size_t)(row0 + r) * F + g * 16 + (lane & 15)] =
                 f32_to_bf16(silu_fast(acc[m][0][q]) * acc[m][1][q]);
-          } else {
+          } else if (S == 1) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const size_t o = (size_t)(row0 + r) * p.N + (2 * g + j) * 16 + (lane & 15);
               if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[o] = f32_to_bf16(acc[m][j][q]);
               else static_cast<float*>(p.out)[o] = acc[m][j][q];
             }
+          } else if constexpr (SPLIT) {
+            // device-scope stores (written through to the coherent level, not left in this
+            // XCD's L2), so no cache-wide write-back is needed to publish them
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              __hip_atomic_store(&p.part[((size_t)s * p.rows + row0 + r) * p.N + (2 * g + j) * 16 + (lane & 15)],
+                                 acc[m][j][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
+        }
+      }
+    }
+    if (SPLIT && MODE == MODE_DOWN && S > 1) {
+      // K split over S workgroups (at most 64 rows, so one pass of mc): the last to arrive
+      // adds the S partials in split order, so the sum does not depend on arrival order.
+      // The partial's stores have completed (stores count in vmcnt) before this split is
+      // counted. A full release fence would also write back the whole L2 of this XCD, and the
+      // matching acquire would invalidate it, evicting the rows the other groups re-read.
+      if (w == 0) {
+        wait_vmcnt<0>();
+        int last = 0;
+        if (lane == 0) last = atomicAdd(&p.arrived[unit], 1) == S - 1;
+        if (lane == 0) s_last = last;
+      }
+      __syncthreads();
+      if (s_last) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // no load moves above the count
+        // the group's n_e x 32 outputs over the whole workgroup (one pass for up to 16 rows,
+        // four for 64), a pass's S loads issued before the first add; device-scope loads never
+        // see a stale line of this XCD's L2
+#pragma unroll 1
+        for (int x = threadIdx.x; x < n_e * 32; x += 64 * kDecWaves) {
+          const size_t o = (size_t)(row0 + (x >> 5)) * p.N + 32 * g + (x & 31);
+          float v[kDecMaxSplits];
+#pragma unroll
+          for (int t = 0; t < kDecMaxSplits; ++t)
+            if (t < S)
+              v[t] = __hip_atomic_load(&p.part[(size_t)t * p.rows * p.N + o], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+          float acc_v = v[0];
+#pragma unroll
+          for (int t = 1; t < kDecMaxSplits; ++t)
+            if (t < S) acc_v += v[t];
+          if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[o] = f32_to_bf16(acc_v);
+          else static_cast<float*>(p.out)[o] = acc_v;
         }
       }
     }

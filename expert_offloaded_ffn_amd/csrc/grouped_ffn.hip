@@ -90,17 +90,36 @@ long long cu_count() {
   return cached[dev];
 }
 
+// K splits of a decode down projection. With at most 4 rows (one or a few tokens: the
+// routed experts touched are few, so their short workgroups end early) a down GEMM longer
+// than 64 k-steps of 32 spreads each (expert, 32-column group) over workgroups of about 48
+// k-steps (a shared expert's F is several routed experts' F), so its few long workgroups do
+// not set the launch's length. The choice depends on the problem alone, so a problem gives
+// the same bits alone or batched.
+int decode_down_splits(const moe_expert_table* t, int rows) {
+  if (t->w_dtype != MOE_BF16 || rows > 4) return 1;
+  const int kt = t->d_ff / 32;
+  return kt > 64 ? std::min(8, (kt + 47) / 48) : 1;
+}
+
 // Workspace: H [rows, F] (fp32, bf16 or e4m3) [+ e4m3 H scales [rows, F/128]], then the
-// tile prefix and the per-XCD work counters of the persistent GEMMs.
+// tile prefix and the per-XCD work counters of the persistent GEMMs, then (for a split
+// decode down projection) the fp32 partials [splits][rows][d] and the arrival counts.
 size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off,
-                 size_t* hs_off = nullptr) {
+                 size_t* hs_off = nullptr, size_t* part_off = nullptr, size_t* arrived_off = nullptr) {
   const size_t hsz = act_dtype == MOE_F32 ? 4 : act_dtype == MOE_FP8_E4M3 ? 1 : 2;
   *h_off = 0;
   size_t end = align_up((size_t)rows * t->d_ff * hsz, 256);
   if (hs_off) *hs_off = end;
   if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)rows * (t->d_ff / 128) * 4, 256);
   *map_off = end;   // tile prefix [E+1], then the work counters [16]
-  return *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
+  end = *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
+  const int S = decode_down_splits(t, rows);
+  if (part_off) *part_off = end;
+  if (S > 1) end += align_up((size_t)S * rows * t->d_model * 4, 256);
+  if (arrived_off) *arrived_off = end;
+  if (S > 1) end += align_up((size_t)std::min(t->n_experts, rows) * (t->d_model / 32) * 4, 256);
+  return end;
 }
 
 }  // namespace
@@ -192,10 +211,10 @@ bool decode_path(const FfnCall& c) {
 }
 
 // The decode kernels' arguments and block counts for one problem: gate/up + SwiGLU into
-// H (in the problem's workspace), then down into y.
-void decode_args(const FfnCall& c, DecodeArgs* gu, DecodeArgs* dn, int* nb_gu, int* nb_dn) {
-  size_t h_off, map_off;
-  ws_layout(&c.t, c.rows, c.act_dtype, &h_off, &map_off);
+// H (in the problem's workspace), then down into y over S K splits.
+void decode_args(const FfnCall& c, int S, DecodeArgs* gu, DecodeArgs* dn, int* nb_gu, int* nb_dn) {
+  size_t h_off, map_off, hs_off, part_off, arrived_off;
+  ws_layout(&c.t, c.rows, c.act_dtype, &h_off, &map_off, &hs_off, &part_off, &arrived_off);
   const BundleGeom g = bundle_geom(c.t.d_model, c.t.d_ff, c.t.w_dtype);
   bf16_t* H = reinterpret_cast<bf16_t*>(c.ws + h_off);
   const int E = c.t.n_experts, d = c.t.d_model, F = c.t.d_ff;
@@ -214,6 +233,10 @@ void decode_args(const FfnCall& c, DecodeArgs* gu, DecodeArgs* dn, int* nb_gu, i
   q.K = d;
   q.out = H;
   q.out_dtype = MOE_BF16;
+  q.rows = c.rows;
+  q.splits = 1;
+  q.clear = S > 1 ? reinterpret_cast<int32_t*>(c.ws + arrived_off) : nullptr;
+  q.clear_n = S > 1 ? max_active * (d / 32) : 0;
   *gu = q;
   *nb_gu = max_active * (q.N / 32);
   q.a = H;
@@ -224,8 +247,13 @@ void decode_args(const FfnCall& c, DecodeArgs* gu, DecodeArgs* dn, int* nb_gu, i
   q.K = F;
   q.out = c.y;
   q.out_dtype = c.y_dtype;
+  q.splits = S;
+  q.part = S > 1 ? reinterpret_cast<float*>(c.ws + part_off) : nullptr;
+  q.arrived = S > 1 ? reinterpret_cast<int32_t*>(c.ws + arrived_off) : nullptr;
+  q.clear = nullptr;
+  q.clear_n = 0;
   *dn = q;
-  *nb_dn = max_active * (q.N / 32);
+  *nb_dn = max_active * (q.N / 32) * S;
 }
 
 // One or two decode problems in one gate/up launch and one down launch; the blocks of the
@@ -233,18 +261,25 @@ void decode_args(const FfnCall& c, DecodeArgs* gu, DecodeArgs* dn, int* nb_gu, i
 moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s) {
   DecodeArgs gu[2], dn[2];
   int ngu[2] = {0, 0}, ndn[2] = {0, 0};
-  for (int i = 0; i < n; ++i) decode_args(calls[i], &gu[i], &dn[i], &ngu[i], &ndn[i]);
+  for (int i = 0; i < n; ++i)
+    decode_args(calls[i], decode_down_splits(&calls[i].t, calls[i].rows), &gu[i], &dn[i], &ngu[i], &ndn[i]);
   if (n == 1) {
     gu[1] = gu[0];
     dn[1] = dn[0];
   }
+  const bool split = dn[0].splits > 1 || (n == 2 && dn[1].splits > 1);
+  const dim3 block(64 * kDecWaves);
   prof_mark(s, MOE_PROF_DEC_GATEUP, false);
-  hipLaunchKernelGGL(ffn_decode_bf16<MODE_GATEUP>, dim3(ngu[0] + ngu[1]), dim3(64 * kDecWaves), 0, s, gu[0], gu[1],
-                     ngu[0]);
+  if (split)
+    hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, true>), dim3(ngu[0] + ngu[1]), block, 0, s, gu[0], gu[1], ngu[0]);
+  else
+    hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, false>), dim3(ngu[0] + ngu[1]), block, 0, s, gu[0], gu[1], ngu[0]);
   prof_mark(s, MOE_PROF_DEC_GATEUP, true);
   prof_mark(s, MOE_PROF_DEC_DOWN, false);
-  hipLaunchKernelGGL(ffn_decode_bf16<MODE_DOWN>, dim3(ndn[0] + ndn[1]), dim3(64 * kDecWaves), 0, s, dn[0], dn[1],
-                     ndn[0]);
+  if (split)
+    hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, true>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1], ndn[0]);
+  else
+    hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, false>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1], ndn[0]);
   prof_mark(s, MOE_PROF_DEC_DOWN, true);
   return check_launch("moe_grouped_ffn bf16 decode");
 }

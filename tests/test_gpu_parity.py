@@ -297,11 +297,15 @@ def test_route_permute_empty_batch():
     assert out["offsets"].cpu().eq(0).all()
 
 
-@pytest.mark.parametrize("T", [1, 5, 64, 100])
-def test_grouped_ffn_batch_equals_separate_calls(T):
+@pytest.mark.parametrize("T,Fs", [(1, 512), (5, 512), (64, 512), (100, 512), (1, 5632), (3, 5632), (7, 5632),
+                                  (64, 5632), (100, 5632)])
+def test_grouped_ffn_batch_equals_separate_calls(T, Fs):
     """The shared and the routed experts through moe_grouped_ffn_batch (one launch per GEMM for a
-    decode step, else one call after the other) give exactly the outputs of two moe_grouped_ffn calls."""
-    cfg = synth.get_config("qwen_decode_bf16", T=T, d=256, E=16, k=4, F=256, F_shared=512)
+    decode step, else one call after the other) give exactly the outputs of two moe_grouped_ffn calls.
+    With F_shared = 5632 and at most 4 rows the shared expert's down projection is split over K
+    across workgroups (fp32 partials added by the last to arrive); repeating the calls over a
+    workspace filled with stale bytes checks that the arrival counts start from zero every time."""
+    cfg = synth.get_config("qwen_decode_bf16", T=T, d=256, E=16, k=4, F=256, F_shared=Fs)
     layer, w = _build(cfg)
     x = _x_dev(cfg, synth.gen_x(cfg, 0, T=T))
     say(f"  case grouped_ffn_batch T={T}: launching")
@@ -312,11 +316,21 @@ def test_grouped_ffn_batch_equals_separate_calls(T):
     s_sep = B.grouped_ffn(layer.shared.table, T, offs, x)
     probs = [B.ffn_problem(layer.shared.table, T, offs, x),
              B.ffn_problem(layer.table, rows, r["offsets"], x, a_row_src=r["perm_src"], a_row_div=cfg.k)]
-    s_bat, y_bat = B.grouped_ffn_batch(probs)
+    ws = torch.empty(B.grouped_ffn_batch_workspace_size(probs), device=DEV, dtype=torch.uint8)
+    s_bat, y_bat = B.grouped_ffn_batch(probs, ws=ws)
+    torch.cuda.synchronize()
+    s_first, y_first = s_bat.clone(), y_bat.clone()
+    ws.fill_(0x5A)   # stale bytes everywhere, arrival counts included
+    for _ in range(2):
+        s_bat, y_bat = B.grouped_ffn_batch(probs, ws=ws)
+        s_sep2 = B.grouped_ffn(layer.shared.table, T, offs, x)
     torch.cuda.synchronize()
     say("    done")
     assert torch.equal(y_bat.view(torch.int16).cpu(), y_sep.view(torch.int16).cpu())
     assert torch.equal(s_bat.view(torch.int16).cpu(), s_sep.view(torch.int16).cpu())
+    assert torch.equal(s_first.view(torch.int16).cpu(), s_sep.view(torch.int16).cpu())
+    assert torch.equal(y_first.view(torch.int16).cpu(), y_sep.view(torch.int16).cpu())
+    assert torch.equal(s_sep2.view(torch.int16).cpu(), s_sep.view(torch.int16).cpu())
     # and the shared expert's output against the oracle
     shared = oracle_expert(cfg, w["shared"])
     ref = moe.swiglu_ffn(decode(synth.gen_x(cfg, 0, T=T), cfg.act_dtype), shared.w_gate, shared.w_up, shared.w_down)
