@@ -79,6 +79,7 @@ EXPORTS = {
     "moe_route": (ctypes.c_int32, [ctypes.POINTER(RouteCfg)] + [ctypes.c_void_p] * 11),
     "moe_route_permute": (ctypes.c_int32, [ctypes.POINTER(RouteCfg)] + [ctypes.c_void_p] * 14 +
                           [ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_route_permute_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 4),
     "moe_permute_workspace_size": (ctypes.c_size_t, [ctypes.c_int32] * 3),
     "moe_permute": (ctypes.c_int32, [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p,
                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
@@ -208,6 +209,10 @@ def permute(idx, E, *, x=None, out_dtype=None, gather=1, ws=None, out=None, stre
     return {"offsets": offsets, "perm_src": src, "perm_dst": dst, "x_out": x_out, "x_out_scale": xs}
 
 
+def route_permute_workspace_size(T, k, E, d) -> int:
+    return int(lib().moe_route_permute_workspace_size(T, k, E, d))
+
+
 def route_permute(x, w_router_t, *, k, score_fn=MOE_SOFTMAX, renormalize=1, route_scale=1.0, n_groups=1,
                   topk_groups=1, group_topn=0, logit_bias=None, select_bias=None, w_shared_gate=None, ws=None,
                   out=None, stream=None):
@@ -230,7 +235,7 @@ def route_permute(x, w_router_t, *, k, score_fn=MOE_SOFTMAX, renormalize=1, rout
     src = get("perm_src", (T * k,), torch.int32)
     dst = get("perm_dst", (T * k,), torch.int32)
     if ws is None:
-        ws = torch.empty(max(permute_workspace_size(T, k, E), 256), device=dev, dtype=torch.uint8)
+        ws = torch.empty(max(route_permute_workspace_size(T, k, E, d), 256), device=dev, dtype=torch.uint8)
     cfg = RouteCfg(T, d, E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn,
                    DTYPE_CODE[x.dtype])
     _check(lib().moe_route_permute(ctypes.byref(cfg), ptr(x), ptr(w_router_t), ptr(logit_bias), ptr(select_bias),

@@ -13,6 +13,10 @@
 //  route_select       one wavefront per token: keys, group limit, k rounds of a
 //                     64-lane arg-max over packed (key, ~index) words, gates, and
 //                     a per-block LDS histogram flushed with one atomic per bin.
+//  route_logit_slices logits of up to 16 tokens split over K across many workgroups
+//                     (moe_route_permute).
+//  route_finish_small the slices' sum, then selection and grouping of those tokens in
+//                     one workgroup (moe_route_permute).
 #include <type_traits>
 
 #include "group_small.h"
@@ -176,11 +180,13 @@ constexpr int kSelWaves = 4;     // waves per block
 
 // Selection for token t by one wavefront: keys, the group limit, k rounds of a wave-wide
 // arg-max, the gates, and the sigmoid of the shared gate's logit. Reads the token's raw
-// logits from scores and writes its keys back; wk is LDS scratch of E floats owned by
-// this wavefront; hist (LDS, may be NULL) counts the selected experts.
+// logits from src (row t at src + t * src_stride: scores itself, or a copy in LDS) and
+// writes its keys to scores; wk is LDS scratch of E floats owned by this wavefront; hist
+// (LDS, may be NULL) counts the selected experts.
 template <int PER_LANE>
 __device__ __forceinline__ void select_token(
-    int t, float* __restrict__ scores, const float* __restrict__ logit_bias, const float* __restrict__ select_bias,
+    int t, const float* src, int src_stride, float* __restrict__ scores, const float* __restrict__ logit_bias,
+    const float* __restrict__ select_bias,
     float* __restrict__ shared_gate, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int* hist,
     float* wk, int E, int k, int score_fn, int renormalize, float route_scale, int n_groups, int topk_groups,
     int group_topn) {
@@ -194,7 +200,7 @@ __device__ __forceinline__ void select_token(
     live[i] = e < E;
     float l = 0.f;
     if (live[i]) {
-      l = scores[(size_t)t * E + e];
+      l = src[(size_t)t * src_stride + e];
       if (logit_bias) l += logit_bias[e];
     }
     logit[i] = l;
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(256) void route_select(
   for (int it = 0; it < tok_per_wave; ++it) {
     const int t = (blockIdx.x * kSelWaves + wave) * tok_per_wave + it;
     if (t >= T) break;
-    select_token<PER_LANE>(t, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
+    select_token<PER_LANE>(t, scores, E, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
                            counts != nullptr ? hist : nullptr, wkeys[wave], E, k, score_fn, renormalize,
                            route_scale, n_groups, topk_groups, group_topn);
   }
@@ -343,88 +349,104 @@ void launch_select(int tpw, hipStream_t s, float* scores, const float* lb, const
 }
 
 // -------------------------------------------------------- small batches ---
-// A decode step routes a handful of tokens. One workgroup computes their logits, selects
-// and groups them, so the three steps cost one launch instead of three. The logits use
-// the tiling of route_logits_mfma<1, 16> (16 waves split K; every wave keeps 1 m-tile x
-// 4 n-tiles of 16 and sums its K range in order; the partials are added in wave order),
-// except that a wave issues the loads of up to kFuseChunk k-steps at once. The selection
-// is select_token and the grouping group_small, so the outputs equal those of moe_route
-// followed by moe_permute bit for bit.
+// A decode step routes at most 16 tokens. One workgroup could hold all of their logits, but
+// a single CU pulls the router weights from HBM slowly, so the logits are split over K into
+// slices of kSliceSteps k-steps of 32 that many workgroups compute at once
+// (route_logit_slices: one wave per slice, n-tile of 16 columns and m-tile of 16 tokens,
+// every load of the slice issued at once); one workgroup then adds each logit's slices in
+// slice order, selects and groups (route_finish_small: select_token, group_small). The
+// slices of more tokens would be as many bytes as the router weights, read back by that one
+// workgroup, so larger batches take the route and permute kernels instead.
 constexpr int kFuseMaxT = 16;
 constexpr int kFuseMaxE = 256;
-constexpr int kFuseChunk = 2;
+constexpr int kSliceSteps = 4;
+
+int route_slices(int d) { return (d / 32 + kSliceSteps - 1) / kSliceSteps; }
+
+// grid (slices, column groups of 64, m-tiles of 16), 4 waves: wave w takes n-tile w of the
+// group. Output: part[slice][t][c] fp32 for t < T, c < E (+1 with the shared gate column).
+__global__ __launch_bounds__(256) void route_logit_slices(const bf16_t* __restrict__ x,
+                                                          const bf16_t* __restrict__ w_router,
+                                                          const bf16_t* __restrict__ w_sg, float* __restrict__ part,
+                                                          int T, int d, int E) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ncols = E + (w_sg != nullptr ? 1 : 0);
+  const int sl = blockIdx.x, c0 = blockIdx.y * 64 + wave * 16, t0 = blockIdx.z * 16;
+  if (c0 >= ncols) return;   // the whole wave: its n-tile lies past the last column
+  const int KT = d / 32;
+  const int k0 = sl * kSliceSteps, nk = min(KT - k0, kSliceSteps);
+  const int koff = 8 * (lane >> 4);
+  const int c = min(c0 + (lane & 15), ncols - 1);
+  const bf16_t* brow = (c < E ? w_router + (size_t)c * d : w_sg) + koff + k0 * 32;
+  const bf16_t* arow = x + (size_t)min(t0 + (lane & 15), T - 1) * d + koff + k0 * 32;
+  bf16x8_t b[kSliceSteps], a[kSliceSteps];
+#pragma unroll
+  for (int j = 0; j < kSliceSteps; ++j) {
+    if (j < nk) {
+      b[j] = *reinterpret_cast<const bf16x8_t*>(brow + j * 32);
+      a[j] = *reinterpret_cast<const bf16x8_t*>(arow + j * 32);
+    }
+  }
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kSliceSteps; ++j)
+    if (j < nk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j], acc, 0, 0, 0);
+  // D layout: lane l holds rows 4*(l/16)+i, column l%16
+  const int col = c0 + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 4 * (lane >> 4) + i;
+    if (t < T && col < ncols) part[((size_t)sl * T + t) * ncols + col] = acc[i];
+  }
+}
 
 template <int PER_LANE, int KMAX>
-__global__ __launch_bounds__(1024) void route_permute_small(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w_router, const bf16_t* __restrict__ w_sg,
-    const float* __restrict__ logit_bias, const float* __restrict__ select_bias, float* __restrict__ shared_gate,
-    float* __restrict__ scores, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
-    int32_t* __restrict__ perm_dst, int T, int d, int E, int k, int score_fn, int renormalize, float route_scale,
-    int n_groups, int topk_groups, int group_topn) {
-  __shared__ f32x4_t red[16][4][64];   // every wave's partial: [wave][n-tile][lane]
+__global__ __launch_bounds__(1024) void route_finish_small(
+    const float* __restrict__ part, int nsl, const float* __restrict__ logit_bias,
+    const float* __restrict__ select_bias, float* __restrict__ shared_gate, float* __restrict__ scores,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ perm_dst, int T, int E,
+    int ncols, int k, int score_fn, int renormalize, float route_scale, int n_groups, int topk_groups,
+    int group_topn) {
+  __shared__ float lg[kFuseMaxT * (kFuseMaxE + 1)];   // the summed logits, [t][ncols]
   __shared__ float wkeys[16][kFuseMaxE];
   __shared__ int32_t off[kFuseMaxE];
   __shared__ int32_t wave_sum[16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ncols = E + (w_sg != nullptr ? 1 : 0);
-  const int KT = d / 32;
-  const int k0 = (KT * wave) / 16, k1 = (KT * (wave + 1)) / 16;
-  const int koff = 8 * (lane >> 4);
-  const bf16_t* arow = x + (size_t)min(lane & 15, T - 1) * d + koff;
-  for (int c0 = 0; c0 < ncols; c0 += 64) {
-    const int ntile = min(4, (ncols - c0 + 15) / 16);
-    const bf16_t* brow[4];
+  const int wave = threadIdx.x >> 6;
+  const int n = T * ncols;
+  // Each logit is the sum of its slices in slice order. A thread takes up to 4 logits at a
+  // time and issues 8 slices of each (32 loads) before the first add.
+  constexpr int kE = 4, kS = 8;
+  for (int j0 = threadIdx.x; j0 < n; j0 += kE * blockDim.x) {
+    float v[kE];
+    for (int s0 = 0; s0 < nsl; s0 += kS) {
+      float buf[kE][kS];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int c = min(c0 + n * 16 + (lane & 15), ncols - 1);
-      brow[n] = (c < E ? w_router + (size_t)c * d : w_sg) + koff;
-    }
-    f32x4_t acc[4];
+      for (int u = 0; u < kE; ++u) {
+        const int j = j0 + u * blockDim.x;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int kc = k0; kc < k1; kc += kFuseChunk) {
-      bf16x8_t b[kFuseChunk][4], a[kFuseChunk];
-#pragma unroll
-      for (int c = 0; c < kFuseChunk; ++c) {
-        if (kc + c < k1) {
-#pragma unroll
-          for (int n = 0; n < 4; ++n)
-            if (n < ntile) b[c][n] = *reinterpret_cast<const bf16x8_t*>(brow[n] + (kc + c) * 32);
-          a[c] = *reinterpret_cast<const bf16x8_t*>(arow + (kc + c) * 32);
-        }
+        for (int q = 0; q < kS; ++q)
+          if (j < n && s0 + q < nsl) buf[u][q] = part[(size_t)(s0 + q) * n + j];
       }
 #pragma unroll
-      for (int c = 0; c < kFuseChunk; ++c) {
-        if (kc + c < k1) {
+      for (int u = 0; u < kE; ++u)
 #pragma unroll
-          for (int n = 0; n < 4; ++n)
-            if (n < ntile) acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c], b[c][n], acc[n], 0, 0, 0);
-        }
-      }
+        for (int q = 0; q < kS; ++q)
+          if (s0 + q < nsl) v[u] = (s0 + q == 0) ? buf[u][q] : v[u] + buf[u][q];
     }
 #pragma unroll
-    for (int n = 0; n < 4; ++n) red[wave][n][lane] = acc[n];
-    __syncthreads();
-    {
-      // thread -> (n-tile, lane, row of the lane's 4): 4 x 64 x 4 = 1024 values
-      const int n = threadIdx.x >> 8, l = (threadIdx.x >> 2) & 63, i = threadIdx.x & 3;
-      if (n < ntile) {
-        float v = red[0][n][l][i];
-        for (int w = 1; w < 16; ++w) v += red[w][n][l][i];
-        // D layout: lane l holds rows 4*(l/16)+i, column l%16
-        const int c = c0 + n * 16 + (l & 15);
-        const int t = 4 * (l >> 4) + i;
-        if (t < T && c < ncols) {
-          if (c < E) scores[(size_t)t * E + c] = v;
-          else shared_gate[t] = v;
-        }
-      }
+    for (int u = 0; u < kE; ++u) {
+      const int j = j0 + u * blockDim.x;
+      if (j >= n) continue;
+      lg[j] = v[u];
+      const int t = j / ncols, c = j - t * ncols;
+      if (c < E) scores[(size_t)t * E + c] = v[u];
+      else shared_gate[t] = v[u];
     }
-    __syncthreads();
   }
-  if (wave < T)
-    select_token<PER_LANE>(wave, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, nullptr,
+  __syncthreads();
+  for (int t = wave; t < T; t += 16)
+    select_token<PER_LANE>(t, lg, ncols, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, nullptr,
                            wkeys[wave], E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn);
   __syncthreads();
   group_small<KMAX>(topk_idx, counts, offsets, perm_src, perm_dst, T, k, E, off, wave_sum);
@@ -520,6 +542,13 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
   return check_launch("moe_route select");
 }
 
+extern "C" size_t moe_route_permute_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d_model) {
+  if (T < 0 || E < 1 || d_model < 1) return 0;
+  const size_t grouping = moe_permute_workspace_size(T, k, E);
+  const size_t slices = align_up((size_t)route_slices(d_model) * T * (E + 1) * sizeof(float), 256);
+  return grouping > slices ? grouping : slices;
+}
+
 extern "C" moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x, const void* w_router,
                                         const float* logit_bias, const float* select_bias,
                                         const void* w_shared_gate, float* shared_gate, float* scores,
@@ -530,6 +559,8 @@ extern "C" moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x,
   MOE_REQUIRE(cfg != nullptr, MOE_EINVAL, "moe_route_permute: cfg is NULL");
   const moe_route_cfg c = *cfg;
   if (moe_status st = check_route_cfg(c, "moe_route_permute")) return st;
+  const size_t need = moe_route_permute_workspace_size(c.T, c.top_k, c.n_experts, c.d_model);
+  MOE_REQUIRE(ws_bytes >= need, MOE_ECAPACITY, "moe_route_permute: workspace %zu < %zu bytes", ws_bytes, need);
   const bool fused = c.T >= 1 && c.T <= kFuseMaxT && c.n_experts <= kFuseMaxE && c.act_dtype == MOE_BF16 &&
                      c.d_model % 32 == 0;
   if (!fused) {
@@ -545,21 +576,23 @@ extern "C" moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x,
               "moe_route_permute: w_shared_gate and shared_gate go together");
   MOE_REQUIRE(x && w_router && scores && topk_idx && topk_gate && offsets && perm_src && perm_dst && ws, MOE_EINVAL,
               "moe_route_permute: NULL tensor argument");
-  MOE_REQUIRE(aligned(x, 16) && aligned(w_router, 16) && (!w_shared_gate || aligned(w_shared_gate, 16)), MOE_EINVAL,
-              "moe_route_permute: x, w_router, w_shared_gate must be 16-byte aligned");
-  const size_t need = moe_permute_workspace_size(c.T, c.top_k, c.n_experts);
-  MOE_REQUIRE(ws_bytes >= need, MOE_ECAPACITY, "moe_route_permute: workspace %zu < %zu bytes", ws_bytes, need);
+  MOE_REQUIRE(aligned(x, 16) && aligned(w_router, 16) && (!w_shared_gate || aligned(w_shared_gate, 16)) &&
+                  aligned(ws, 16),
+              MOE_EINVAL, "moe_route_permute: x, w_router, w_shared_gate and ws must be 16-byte aligned");
   hipStream_t s = as_stream(stream);
   const int G = c.n_groups < 1 ? 1 : c.n_groups;
-  const bf16_t* xb = static_cast<const bf16_t*>(x);
-  const bf16_t* wb = static_cast<const bf16_t*>(w_router);
-  const bf16_t* sgb = static_cast<const bf16_t*>(w_shared_gate);
+  const int ncols = c.n_experts + (w_shared_gate ? 1 : 0);
+  const int nsl = route_slices(c.d_model);
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL(route_logit_slices, dim3(nsl, (ncols + 63) / 64, (c.T + 15) / 16), dim3(256), 0, s,
+                     static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router),
+                     static_cast<const bf16_t*>(w_shared_gate), part, c.T, c.d_model, c.n_experts);
   auto go = [&](auto pl, auto km) {
     constexpr int PL = decltype(pl)::value, KM = decltype(km)::value;
-    hipLaunchKernelGGL((route_permute_small<PL, KM>), dim3(1), dim3(1024), 0, s, xb, wb, sgb, logit_bias,
-                       select_bias, shared_gate, scores, topk_idx, topk_gate, counts, offsets, perm_src, perm_dst,
-                       c.T, c.d_model, c.n_experts, c.top_k, c.score_fn, c.renormalize, c.route_scale, G,
-                       c.topk_groups, c.group_topn);
+    hipLaunchKernelGGL((route_finish_small<PL, KM>), dim3(1), dim3(1024), 0, s, part, nsl, logit_bias, select_bias,
+                       shared_gate, scores, topk_idx, topk_gate, counts, offsets, perm_src, perm_dst, c.T,
+                       c.n_experts, ncols, c.top_k, c.score_fn, c.renormalize, c.route_scale, G, c.topk_groups,
+                       c.group_topn);
   };
   auto by_k = [&](auto pl) {
     if (c.top_k <= 2) go(pl, std::integral_constant<int, 2>{});

@@ -151,7 +151,7 @@ class MoELayer:
         ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
         shared_y = None
         merged = self.shared_in_decode_launch(T)
-        ws = self._buf("perm_ws", B.permute_workspace_size(T, k, E))
+        ws = self._buf("perm_ws", B.route_permute_workspace_size(T, k, E, d))
         rows = T * k
         y = torch.empty(rows, d, device=self.device, dtype=torch.float32 if ydt == B.MOE_F32 else torch.bfloat16)
         a, a_scale, a_code = x, None, self.act_code

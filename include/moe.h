@@ -152,13 +152,18 @@ moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_idx,
  * moe_route followed by moe_permute without row materialisation (x_out NULL), as
  * one call: the router's expert list goes straight to the grouping that decides
  * which experts run ([VVLLM] "Technical Insight": the expert list is intercepted
- * between the router and the expert kernels). The outputs and their meaning are
- * exactly those of the two calls (same arguments, same errors); counts may be NULL.
- * Batches of 1..16 bf16 tokens with d % 32 == 0 and E <= 256 (a decode step) run as
- * a single workgroup launch whose outputs equal the two calls' bit for bit; other
- * batches make the two calls.
- * Workspace: moe_permute_workspace_size(T, k, E) bytes at `ws` (256-B aligned).
+ * between the router and the expert kernels). The outputs, their meaning, the
+ * routing contract and the errors are those of the two calls; counts may be NULL.
+ * Batches of 1..16 bf16 tokens with d % 32 == 0 and E <= 256 (a decode step) run
+ * as two launches: the logits split over K across many workgroups (so the router
+ * weights stream through many CUs), then one workgroup that adds the K slices in
+ * order, selects and groups. Their logits are therefore summed in another order
+ * than moe_route's and can differ from them in the last bits. Other batches make
+ * the two calls.
+ * Workspace: moe_route_permute_workspace_size(T, k, E, d_model) bytes at `ws`
+ * (256-B aligned); MOE_ECAPACITY if short.
  */
+size_t moe_route_permute_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d_model);
 moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x, const void* w_router,
                              const float* logit_bias, const float* select_bias,
                              const void* w_shared_gate, float* shared_gate, float* scores,

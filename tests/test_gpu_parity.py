@@ -236,25 +236,28 @@ def test_decode_graph_replay_matches_eager(T):
 
 
 _RP_CASES = [
-    # config, overrides, T: the fused single-workgroup path (T <= 16, E <= 256) and the two-call path
+    # config, overrides, T: the sliced-logits path (T <= 16, E <= 256, bf16) and the two-call path
     ("qwen_decode_bf16", {}, 1),
     ("qwen_decode_bf16", {}, 8),
-    ("qwen_decode_bf16", {}, 16),
     ("qwen_decode_bf16", {}, 17),
     ("qwen_decode_bf16", {}, 64),
+    ("qwen_decode_bf16", {}, 16),
     ("dsv3_prefill_fp8", dict(d=512, E=256, k=8), 16),                  # grouped sigmoid, E = 256
     ("dsv3_prefill_fp8", dict(d=256, E=64, k=8, n_groups=8, topk_groups=3), 5),
     ("offload_decode_bf16", dict(d=512), 7),                              # E = 128, logit prior
-    ("offload_decode_bf16", dict(d=512), 32),
-    ("mixtral_prefill_bf16", dict(d=96, k=1), 3),                         # fewer k-steps than waves, top-1
+    ("offload_decode_bf16", {}, 12),                                      # d = 4096
+    ("offload_decode_bf16", {}, 32),                                      # two calls
+    ("mixtral_prefill_bf16", dict(d=96, k=1), 3),                         # a partial K slice, top-1
     ("mixtral_prefill_bf16", dict(d=256, E=40, k=12), 9),                 # k > 8
+    ("mixtral_prefill_bf16", dict(d=256), 200),                           # two calls
 ]
 
 
 @pytest.mark.parametrize("name,over,T", _RP_CASES)
-def test_route_permute_equals_route_then_permute(name, over, T):
-    """moe_route_permute gives exactly the outputs of moe_route followed by moe_permute, and both
-    meet the routing contract against the oracle."""
+def test_route_permute_against_route_then_permute(name, over, T):
+    """moe_route_permute meets the routing contract against the oracle. Where it makes the two
+    calls it equals moe_route followed by moe_permute bit for bit; on the sliced-logits path its
+    keys (summed over K slices in another order) agree with theirs to rounding."""
     cfg = synth.get_config(name, T=T, **over)
     router = synth.gen_router(cfg)
     w_sg = synth.gen_shared_gate(cfg) if cfg.shared_gate else None
@@ -275,17 +278,24 @@ def test_route_permute_equals_route_then_permute(name, over, T):
     p = B.permute(r["idx"], cfg.E)
     torch.cuda.synchronize()
     say("    done")
-    for key, ref in [("scores", r), ("idx", r), ("gate", r), ("counts", r), ("shared_gate", r), ("offsets", p),
-                     ("perm_src", p), ("perm_dst", p)]:
-        if ref[key] is None:
-            assert fused[key] is None
-            continue
-        a, b = fused[key].cpu(), ref[key].cpu()
-        assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
-                           b.view(torch.int32) if b.dtype == torch.float32 else b), f"{key} differs"
     check_exact_indices(cfg, fused, fused, T)
     r_ref = oracle_route(cfg, x_store, router, w_sg, sb, lb)
     route_agreement(cfg, r_ref, fused, key_tol=1e-4)
+    sliced = T <= 16 and cfg.E <= 256
+    if not sliced:
+        for key, ref in [("scores", r), ("idx", r), ("gate", r), ("counts", r), ("shared_gate", r),
+                         ("offsets", p), ("perm_src", p), ("perm_dst", p)]:
+            if ref[key] is None:
+                assert fused[key] is None
+                continue
+            a, b = fused[key].cpu(), ref[key].cpu()
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                               b.view(torch.int32) if b.dtype == torch.float32 else b), f"{key} differs"
+        return
+    kf, ks = to_np(fused["scores"]), to_np(r["scores"])
+    assert np.abs(kf - ks).max() <= 1e-5 * max(1.0, np.abs(ks).max())
+    if cfg.shared_gate:
+        assert np.abs(to_np(fused["shared_gate"]) - to_np(r["shared_gate"])).max() <= 1e-6
 
 
 def test_route_permute_empty_batch():
