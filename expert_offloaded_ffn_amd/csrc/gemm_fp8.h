@@ -127,6 +127,11 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
   const int a_off1 = 16 * (8 * ar + ((ac + 1) ^ f(ar)));
 
   const int e8m0_one = 127;   // MFMA block scale 2^0: the fp32 block scales are applied in software
+  // A wave row whose 64 rows all lie past the expert's last row (the short last m-tile of an
+  // expert whose rows just pass a multiple of 128) only moves data: it issues its share of
+  // the DMA and joins the barriers, but reads no fragments and issues no MFMAs; its
+  // accumulators stay zero and the epilogue stores no row of it.
+  const bool idle = row0 + wm * 64 >= row_end;
   issue(0);
   if (KB > 1) issue(1);
   for (int s = 0; s < KB; ++s) {
@@ -134,6 +139,7 @@ __device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     barrier_no_fence();
     if (s + 2 < KB) issue(s + 2);
+    if (idle) continue;
     const char* base = smem[s % kF8Stages];
     i32x8_t fa[4];
 #pragma unroll
