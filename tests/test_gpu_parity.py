@@ -345,3 +345,33 @@ def test_grouped_ffn_batch_equals_separate_calls(T, Fs):
     shared = oracle_expert(cfg, w["shared"])
     ref = moe.swiglu_ffn(decode(synth.gen_x(cfg, 0, T=T), cfg.act_dtype), shared.w_gate, shared.w_up, shared.w_down)
     assert_close(to_np(s_bat), ref, cfg.dtype, "shared expert")
+
+
+@pytest.mark.parametrize("T", [64, 300])
+def test_max_experts_and_top_k(T):
+    """The largest routing the ABI takes: 1024 experts, top-32. T = 64 takes the decode kernels
+    (at most 64 rows per expert), T = 300 the prefill tile map over 1024 experts."""
+    cfg = synth.get_config("mixtral_prefill_bf16", T=T, d=256, F=256, E=1024, k=32, name="maxE")
+    layer, w = _build(cfg)
+    _run_and_check(cfg, layer, w, T, 0)
+
+
+def test_grouped_routing_at_64_groups():
+    """Group-limited sigmoid routing with selection bias at 1024 experts in 64 groups (8 kept,
+    top-2 sum per group), top-16, against the oracle's routing contract."""
+    cfg = synth.get_config("dsv3_prefill_fp8", T=200, d=256, E=1024, k=16, n_groups=64, topk_groups=8,
+                           group_topn=2)
+    router = synth.gen_router(cfg)
+    sb = synth.gen_select_bias(cfg)
+    x_store = synth.gen_x(cfg, 0, T=cfg.T)
+    x = _x_dev(cfg, x_store)
+    wr = torch.from_numpy(np.ascontiguousarray(router.T).view(np.int16)).view(torch.bfloat16).to(DEV)
+    say("  case grouped routing 1024 experts / 64 groups: launching")
+    r = B.route(x, wr, k=cfg.k, score_fn=B.MOE_SIGMOID, route_scale=cfg.route_scale, n_groups=64, topk_groups=8,
+                group_topn=2, select_bias=torch.from_numpy(sb).to(DEV))
+    p = B.permute(r["idx"], cfg.E)
+    torch.cuda.synchronize()
+    say("    done")
+    check_exact_indices(cfg, r, p, cfg.T)
+    r_ref = oracle_route(cfg, x_store, router, select_bias=sb)
+    route_agreement(cfg, r_ref, r, key_tol=1e-5)
