@@ -13,8 +13,9 @@
 //  route_select       one wavefront per token: keys, group limit, k rounds of a
 //                     64-lane arg-max over packed (key, ~index) words, gates, and
 //                     a per-block LDS histogram flushed with one atomic per bin.
-//  route_logit_slices logits of up to 16 tokens split over K across many workgroups
+//  route_logit_slices logits of up to 64 tokens split over K across many workgroups
 //                     (moe_route_permute).
+//  route_select_slices a wavefront per token: the sum of its slices, then its selection.
 //  route_finish_small the slices' sum, then selection and grouping of those tokens in
 //                     one workgroup (moe_route_permute).
 #include <type_traits>
@@ -349,14 +350,15 @@ void launch_select(int tpw, hipStream_t s, float* scores, const float* lb, const
 }
 
 // -------------------------------------------------------- small batches ---
-// A decode step routes at most 16 tokens. One workgroup could hold all of their logits, but
+// A decode step routes at most 64 tokens. One workgroup could hold all of their logits, but
 // a single CU pulls the router weights from HBM slowly, so the logits are split over K into
 // slices of kSliceSteps k-steps of 32 that many workgroups compute at once
 // (route_logit_slices: one wave per slice, n-tile of 16 columns and m-tile of 16 tokens,
-// every load of the slice issued at once); one workgroup then adds each logit's slices in
-// slice order, selects and groups (route_finish_small: select_token, group_small). The
-// slices of more tokens would be as many bytes as the router weights, read back by that one
-// workgroup, so larger batches take the route and permute kernels instead.
+// every load of the slice issued at once). Up to 16 tokens, one workgroup then adds each
+// logit's slices in slice order, selects and groups (route_finish_small: select_token,
+// group_small); for more tokens the slices would be as many bytes as the router weights,
+// too many for one workgroup to read back, so a wavefront per token sums and selects
+// (route_select_slices) and the one-workgroup grouping follows.
 constexpr int kFuseMaxT = 16;
 constexpr int kFuseMaxE = 256;
 constexpr int kSliceSteps = 4;
@@ -368,8 +370,10 @@ int route_slices(int d) { return (d / 32 + kSliceSteps - 1) / kSliceSteps; }
 __global__ __launch_bounds__(256) void route_logit_slices(const bf16_t* __restrict__ x,
                                                           const bf16_t* __restrict__ w_router,
                                                           const bf16_t* __restrict__ w_sg, float* __restrict__ part,
-                                                          int T, int d, int E) {
+                                                          int32_t* __restrict__ counts, int T, int d, int E) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (counts != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)   // route_select_slices adds to them
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
   const int ncols = E + (w_sg != nullptr ? 1 : 0);
   const int sl = blockIdx.x, c0 = blockIdx.y * 64 + wave * 16, t0 = blockIdx.z * 16;
   if (c0 >= ncols) return;   // the whole wave: its n-tile lies past the last column
@@ -450,6 +454,53 @@ __global__ __launch_bounds__(1024) void route_finish_small(
                            wkeys[wave], E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn);
   __syncthreads();
   group_small<KMAX>(topk_idx, counts, offsets, perm_src, perm_dst, T, k, E, off, wave_sum);
+}
+
+// 17..64 tokens: one wavefront per token sums the token's slices (slice order, 8 slice loads
+// in flight per column) into an LDS row, then selects on it like route_select (the
+// expert histogram included); moe_permute's one-workgroup grouping follows.
+constexpr int kSliceMaxT = 64;
+
+template <int PER_LANE>
+__global__ __launch_bounds__(64 * kSelWaves) void route_select_slices(
+    const float* __restrict__ part, int nsl, int ncols, const float* __restrict__ logit_bias,
+    const float* __restrict__ select_bias, float* __restrict__ shared_gate, float* __restrict__ scores,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int32_t* __restrict__ counts, int T, int E, int k,
+    int score_fn, int renormalize, float route_scale, int n_groups, int topk_groups, int group_topn) {
+  __shared__ int hist[kFuseMaxE];
+  __shared__ float wkeys[kSelWaves][kFuseMaxE];
+  __shared__ float lg[kSelWaves][kFuseMaxE + 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (counts != nullptr)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kSelWaves + wave;
+  if (t < T) {
+    for (int c = lane; c < ncols; c += 64) {
+      float v = 0.f;
+      for (int s0 = 0; s0 < nsl; s0 += 8) {
+        float buf[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (s0 + q < nsl) buf[q] = part[((size_t)(s0 + q) * T + t) * ncols + c];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (s0 + q < nsl) v = (s0 + q == 0) ? buf[q] : v + buf[q];
+      }
+      lg[wave][c] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    if (shared_gate != nullptr && lane == 0) shared_gate[t] = lg[wave][E];   // the raw logit; sigmoid below
+    select_token<PER_LANE>(t, lg[wave], 0, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
+                           counts != nullptr ? hist : nullptr, wkeys[wave], E, k, score_fn, renormalize,
+                           route_scale, n_groups, topk_groups, group_topn);
+  }
+  if (counts != nullptr) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += blockDim.x)
+      if (hist[e]) atomicAdd(&counts[e], hist[e]);
+  }
 }
 
 // Configuration checks shared by moe_route and moe_route_permute.
@@ -561,9 +612,9 @@ extern "C" moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x,
   if (moe_status st = check_route_cfg(c, "moe_route_permute")) return st;
   const size_t need = moe_route_permute_workspace_size(c.T, c.top_k, c.n_experts, c.d_model);
   MOE_REQUIRE(ws_bytes >= need, MOE_ECAPACITY, "moe_route_permute: workspace %zu < %zu bytes", ws_bytes, need);
-  const bool fused = c.T >= 1 && c.T <= kFuseMaxT && c.n_experts <= kFuseMaxE && c.act_dtype == MOE_BF16 &&
-                     c.d_model % 32 == 0;
-  if (!fused) {
+  const bool sliced = c.T >= 1 && c.T <= kSliceMaxT && c.n_experts <= kFuseMaxE && c.act_dtype == MOE_BF16 &&
+                      c.d_model % 32 == 0;
+  if (!sliced) {
     if (moe_status st = moe_route(cfg, x, w_router, logit_bias, select_bias, w_shared_gate, shared_gate, scores,
                                   topk_idx, topk_gate, counts, stream))
       return st;
@@ -586,7 +637,23 @@ extern "C" moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x,
   float* part = static_cast<float*>(ws);
   hipLaunchKernelGGL(route_logit_slices, dim3(nsl, (ncols + 63) / 64, (c.T + 15) / 16), dim3(256), 0, s,
                      static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w_router),
-                     static_cast<const bf16_t*>(w_shared_gate), part, c.T, c.d_model, c.n_experts);
+                     static_cast<const bf16_t*>(w_shared_gate), part, counts, c.T, c.d_model, c.n_experts);
+  if (c.T > kFuseMaxT) {
+    auto sel = [&](auto pl) {
+      constexpr int PL = decltype(pl)::value;
+      hipLaunchKernelGGL((route_select_slices<PL>), dim3((c.T + kSelWaves - 1) / kSelWaves), dim3(64 * kSelWaves), 0,
+                         s, part, nsl, ncols, logit_bias, select_bias, shared_gate, scores, topk_idx, topk_gate, counts,
+                         c.T, c.n_experts, c.top_k, c.score_fn, c.renormalize, c.route_scale, G, c.topk_groups,
+                         c.group_topn);
+    };
+    if (c.n_experts <= 64) sel(std::integral_constant<int, 1>{});
+    else if (c.n_experts <= 128) sel(std::integral_constant<int, 2>{});
+    else sel(std::integral_constant<int, 4>{});
+    if (moe_status st = check_launch("moe_route_permute select")) return st;
+    // at most 64 tokens: the one-workgroup grouping, which leaves the partials in ws alone
+    return moe_permute(c.T, c.top_k, c.n_experts, topk_idx, offsets, perm_src, perm_dst, 0, nullptr, 0, nullptr, 0,
+                       nullptr, 0, ws, ws_bytes, stream);
+  }
   auto go = [&](auto pl, auto km) {
     constexpr int PL = decltype(pl)::value, KM = decltype(km)::value;
     hipLaunchKernelGGL((route_finish_small<PL, KM>), dim3(1), dim3(1024), 0, s, part, nsl, logit_bias, select_bias,

@@ -154,12 +154,13 @@ moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t* topk_idx,
  * which experts run ([VVLLM] "Technical Insight": the expert list is intercepted
  * between the router and the expert kernels). The outputs, their meaning, the
  * routing contract and the errors are those of the two calls; counts may be NULL.
- * Batches of 1..16 bf16 tokens with d % 32 == 0 and E <= 256 (a decode step) run
- * as two launches: the logits split over K across many workgroups (so the router
- * weights stream through many CUs), then one workgroup that adds the K slices in
- * order, selects and groups. Their logits are therefore summed in another order
- * than moe_route's and can differ from them in the last bits. Other batches make
- * the two calls.
+ * Batches of 1..64 bf16 tokens with d % 32 == 0 and E <= 256 (a decode step) split
+ * the logits over K across many workgroups (so the router weights stream through
+ * many CUs); for up to 16 tokens one workgroup then adds the K slices in order,
+ * selects and groups, for 17..64 a wavefront per token adds and selects and the
+ * grouping follows. Their logits are therefore summed in another order than
+ * moe_route's and can differ from them in the last bits. Other batches make the
+ * two calls.
  * Workspace: moe_route_permute_workspace_size(T, k, E, d_model) bytes at `ws`
  * (256-B aligned); MOE_ECAPACITY if short.
  */

@@ -236,19 +236,22 @@ def test_decode_graph_replay_matches_eager(T):
 
 
 _RP_CASES = [
-    # config, overrides, T: the sliced-logits path (T <= 16, E <= 256, bf16) and the two-call path
+    # config, overrides, T: the sliced-logits paths (T <= 16 and 17..64, E <= 256, bf16) and the
+    # two-call path
     ("qwen_decode_bf16", {}, 1),
     ("qwen_decode_bf16", {}, 8),
     ("qwen_decode_bf16", {}, 17),
     ("qwen_decode_bf16", {}, 64),
+    ("qwen_decode_bf16", {}, 65),                                         # two calls
     ("qwen_decode_bf16", {}, 16),
     ("dsv3_prefill_fp8", dict(d=512, E=256, k=8), 16),                  # grouped sigmoid, E = 256
     ("dsv3_prefill_fp8", dict(d=256, E=64, k=8, n_groups=8, topk_groups=3), 5),
     ("offload_decode_bf16", dict(d=512), 7),                              # E = 128, logit prior
     ("offload_decode_bf16", {}, 12),                                      # d = 4096
-    ("offload_decode_bf16", {}, 32),                                      # two calls
+    ("offload_decode_bf16", {}, 32),                                      # d = 4096, 17..64 tokens
     ("mixtral_prefill_bf16", dict(d=96, k=1), 3),                         # a partial K slice, top-1
     ("mixtral_prefill_bf16", dict(d=256, E=40, k=12), 9),                 # k > 8
+    ("dsv3_prefill_fp8", dict(d=512, E=256, k=8), 40),                  # grouped sigmoid, 17..64 tokens
     ("mixtral_prefill_bf16", dict(d=256), 200),                           # two calls
 ]
 
@@ -281,7 +284,7 @@ def test_route_permute_against_route_then_permute(name, over, T):
     check_exact_indices(cfg, fused, fused, T)
     r_ref = oracle_route(cfg, x_store, router, w_sg, sb, lb)
     route_agreement(cfg, r_ref, fused, key_tol=1e-4)
-    sliced = T <= 16 and cfg.E <= 256
+    sliced = T <= 64 and cfg.E <= 256
     if not sliced:
         for key, ref in [("scores", r), ("idx", r), ("gate", r), ("counts", r), ("shared_gate", r),
                          ("offsets", p), ("perm_src", p), ("perm_dst", p)]:
