@@ -263,6 +263,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="decode: replay the layer as one captured HIP graph")
+    ap.add_argument("--skew-zipf", type=float, default=0.0,
+                    help="prefill: add a Zipf(alpha) log-prior to the routing logits (0 = unskewed)")
     ap.add_argument("--mall-flush", choices=["read", "write"], default="read",
                     help="decode: evict the last-level cache before each step by reading (default) or writing 512 MiB")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -313,15 +315,22 @@ def main():
     layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
                      select_bias=w["sb"], threads=16)
     xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(args.batches)]
+    # skewed prefill: a Zipf(alpha) log-prior over a seeded permutation of the experts added to
+    # every token's logits, so a few experts get several times the average rows
+    lb = None
+    if args.skew_zipf > 0:
+        import dataclasses
+        zcfg = dataclasses.replace(cfg, zipf_alpha=args.skew_zipf, zipf_epoch=1)
+        lb = torch.from_numpy(synth.zipf_logit_bias(zcfg, 0)).to("cuda")
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup}")
     for i in range(args.warmup):
-        layer.forward(xs[i % len(xs)])
+        layer.forward(xs[i % len(xs)], logit_bias=lb)
     torch.cuda.synchronize()
     # rows per expert of each batch (real rows only; used for the algorithmic work)
     rows_e = []
     for x in xs:
-        rows_e.append(B.route(x, layer.w_router_t, **layer.route_args())["counts"].cpu().numpy())
+        rows_e.append(B.route(x, layer.w_router_t, logit_bias=lb, **layer.route_args())["counts"].cpu().numpy())
     torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps")
@@ -331,7 +340,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record()
     for i in range(args.steps):
-        layer.forward(xs[i % len(xs)])
+        layer.forward(xs[i % len(xs)], logit_bias=lb)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -364,6 +373,11 @@ def main():
         "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
                    "d_ff_shared": cfg.F_shared, "score_fn": cfg.score_fn, "all_experts_resident": True},
     }
+    if lb is not None:
+        re = np.stack(rows_e)
+        result["config"]["zipf_skew_alpha"] = args.skew_zipf
+        result["data"] += f"; routing skewed by a Zipf({args.skew_zipf}) log-prior"
+        result["rows_per_expert"] = {"max": int(re.max()), "mean": round(float(re.mean()), 1), "min": int(re.min())}
     if gu_n:
         gu_avg_s = gu_ms / gu_n / 1e3
         achieved = float(gateup_flops.mean()) / (gu_avg_s * launches) / 1e12
