@@ -596,7 +596,9 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
 extern "C" size_t moe_route_permute_workspace_size(int32_t T, int32_t k, int32_t E, int32_t d_model) {
   if (T < 0 || E < 1 || d_model < 1) return 0;
   const size_t grouping = moe_permute_workspace_size(T, k, E);
-  const size_t slices = align_up((size_t)route_slices(d_model) * T * (E + 1) * sizeof(float), 256);
+  // the logit slices exist only on the sliced path (bf16 is checked at the call)
+  const bool sliced = T >= 1 && T <= kSliceMaxT && E <= kFuseMaxE && d_model % 32 == 0;
+  const size_t slices = sliced ? align_up((size_t)route_slices(d_model) * T * (E + 1) * sizeof(float), 256) : 0;
   return grouping > slices ? grouping : slices;
 }
 

@@ -135,6 +135,17 @@ def test_batch_and_route_permute_validation_codes():
     assert L.moe_route_permute(ctypes.byref(cfg), *args, 1 << 16, null) == -1
 
 
+def test_route_permute_workspace_only_holds_slices_when_used():
+    """The logit slices (K slices x T x (E + 1) fp32) are part of the workspace only for the
+    batches that take the sliced path (1..64 tokens, E <= 256, d % 32 == 0)."""
+    assert B.route_permute_workspace_size(8192, 8, 256, 7168) == B.permute_workspace_size(8192, 8, 256)
+    assert B.route_permute_workspace_size(65, 4, 60, 2048) == B.permute_workspace_size(65, 4, 60)
+    assert B.route_permute_workspace_size(64, 4, 300, 2048) == B.permute_workspace_size(64, 4, 300)
+    slices = (2048 // 32 + 3) // 4           # 4 k-steps of 32 per slice
+    assert B.route_permute_workspace_size(64, 4, 60, 2048) >= slices * 64 * 61 * 4
+    assert B.route_permute_workspace_size(1, 4, 60, 2048) >= slices * 1 * 61 * 4
+
+
 def test_pack_bf16_layout():
     d, F = 64, 32
     rng = np.random.default_rng(0)
