@@ -393,3 +393,14 @@ def test_prefill_under_zipf_skew(name, over):
     g = _run_and_check(cfg, layer, w, cfg.T, 0, tokens=np.arange(0, cfg.T, 3), logit_bias=lb)
     counts = to_np(g["route"]["counts"])
     assert counts.max() >= 2 * counts.mean()   # the skew is real
+
+
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_decode_routed_down_split(T):
+    """A Mixtral-shaped expert (F = 14336) serving 1-3 tokens: the routed problem has at most 4
+    rows, so its down projection is split over K across 8 workgroups per 32-column group, and
+    the last to arrive adds the partials (T = 3 has 6 rows and is not split)."""
+    cfg = synth.get_config("mixtral_prefill_bf16", T=T, d=256, name="decode_split")
+    layer, w = _build(cfg)
+    for xi in range(2):
+        _run_and_check(cfg, layer, w, T, xi)
