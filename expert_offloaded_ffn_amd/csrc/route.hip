@@ -584,7 +584,7 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
                          shared_gate, counts, c.T, c.d_model, c.n_experts);
   }
   if (moe_status st = check_launch("moe_route logits")) return st;
-  const int tpw = c.T >= 16384 ? 4 : 1;  // tokens per wavefront
+  const int tpw = c.T >= 2048 ? 4 : 1;  // tokens per wavefront (fewer, fuller workgroups for large batches)
   const int per_lane = (c.n_experts + 63) / 64;
   if (per_lane <= 1) launch_select<1>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
   else if (per_lane <= 2) launch_select<2>(tpw, s, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, counts, cc);
