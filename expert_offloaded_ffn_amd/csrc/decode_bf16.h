@@ -78,10 +78,13 @@ constexpr int kDecMaxSplits = 8;              // workgroups per (expert, group) 
 // the routed experts and the shared expert, in one launch). SPLIT launches carry a down
 // projection split over K (and, for GATEUP, clear its arrival counts); the others compile
 // without that code.
-template <int MODE, bool SPLIT>
-__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(DecodeArgs p0, DecodeArgs p1,
-                                                                                       int nb0) {
-  __shared__ f32x4_t red[kDecWaves - 1][4][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
+// MB is the number of 16-row m-blocks a pass covers: 4 in general, 1 when no expert has more
+// than 16 rows, which needs a quarter of the accumulators and of the reduction LDS, so more
+// workgroups (and more loads in flight) fit on a CU.
+template <int MODE, bool SPLIT, int MB>
+__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
+    DecodeArgs p0, DecodeArgs p1, int nb0) {
+  __shared__ f32x4_t red[kDecWaves - 1][MB][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
   __shared__ int s_last;                               // split K: this workgroup arrived last
   const bool second = (int)blockIdx.x >= nb0;
   const DecodeArgs p = second ? p1 : p0;
@@ -110,19 +113,19 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
   const char* b0 = B + ((int64_t)(2 * g) * KT) * 1024 + 16 * lane;      // n-tile 2g
   const char* b1 = B + ((int64_t)(2 * g + 1) * KT) * 1024 + 16 * lane;  // n-tile 2g+1
 
-  for (int mc = 0; mc < n_e; mc += 64) {
-    const int mbn = min(4, (n_e - mc + 15) / 16);
-    const bf16_t* arow[4];
+  for (int mc = 0; mc < n_e; mc += 16 * MB) {
+    const int mbn = min(MB, (n_e - mc + 15) / 16);
+    const bf16_t* arow[MB];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MB; ++m) {
       int r = mc + m * 16 + (lane & 15);
       r = r < n_e ? r : n_e - 1;
       const int src = p.a_row_src ? p.a_row_src[row0 + r] / p.a_row_div : row0 + r;
       arow[m] = p.a + (size_t)src * p.K + 8 * (lane >> 4);
     }
-    f32x4_t acc[4][2];
+    f32x4_t acc[MB][2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MB; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int k0 = kt0; k0 < kt1; k0 += kDecChunk) {
       const int nk = min(kDecChunk, kt1 - k0);
       // the chunk's tiles as constant offsets from one pointer per n-tile, so the loads issue
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
         }
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < MB; ++m) {
         if (m < mbn) {
           const bf16_t* qa = arow[m] + (int64_t)k0 * 32;
 #pragma unroll
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
     }
     if (w > 0) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+      for (int m = 0; m < MB; ++m)
         if (m < mbn) {
           red[w - 1][m][0][lane] = acc[m][0];
           red[w - 1][m][1][lane] = acc[m][1];
@@ -163,7 +166,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
     __syncthreads();
     if (w == 0) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < MB; ++m) {
         if (m >= mbn) continue;
         for (int ww = 0; ww < kDecWaves - 1; ++ww) {
           acc[m][0] += red[ww][m][0][lane];
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
       }
     }
     if (SPLIT && MODE == MODE_DOWN && S > 1) {
-      // K split over S workgroups (at most 64 rows, so one pass of mc): the last to arrive
+      // K split over S workgroups (at most 4 rows, so one pass of mc): the last to arrive
       // adds the S partials in split order, so the sum does not depend on arrival order.
       // The partial's stores have completed (stores count in vmcnt) before this split is
       // counted. A full release fence would also write back the whole L2 of this XCD, and the
@@ -210,8 +213,8 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
       __syncthreads();
       if (s_last) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // no load moves above the count
-        // the group's n_e x 32 outputs over the whole workgroup (one pass for up to 16 rows,
-        // four for 64), a pass's S loads issued before the first add; device-scope loads never
+        // the group's n_e x 32 outputs over the whole workgroup (one pass), the S loads
+        // issued before the first add; device-scope loads never
         // see a stale line of this XCD's L2
 #pragma unroll 1
         for (int x = threadIdx.x; x < n_e * 32; x += 64 * kDecWaves) {

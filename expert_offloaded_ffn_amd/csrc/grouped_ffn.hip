@@ -16,6 +16,7 @@
 //  this file      ffn_f32_* (fp32 VALU path, one thread per output element) and the host
 //                 side: argument checks, workspace layout, launches
 #include <algorithm>
+#include <type_traits>
 
 #include "decode_bf16.h"
 #include "ffn_common.h"
@@ -268,19 +269,38 @@ moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s) {
     dn[1] = dn[0];
   }
   const bool split = dn[0].splits > 1 || (n == 2 && dn[1].splits > 1);
+  // one 16-row m-block per pass while every expert holds at most 16 rows (71 VGPRs, so more
+  // workgroups fit on a CU), else 4 (112 VGPRs; a 2-block pass at the 6-wave cap spills and
+  // measured slower than 4 blocks at 17..32 rows)
+  int max_rows_e = 0;
+  for (int i = 0; i < n; ++i) {
+    const FfnCall& c = calls[i];
+    max_rows_e = std::max(max_rows_e, c.a_row_src ? (c.rows + c.a_row_div - 1) / c.a_row_div : c.rows);
+  }
   const dim3 block(64 * kDecWaves);
-  prof_mark(s, MOE_PROF_DEC_GATEUP, false);
-  if (split)
-    hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, true>), dim3(ngu[0] + ngu[1]), block, 0, s, gu[0], gu[1], ngu[0]);
-  else
-    hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, false>), dim3(ngu[0] + ngu[1]), block, 0, s, gu[0], gu[1], ngu[0]);
-  prof_mark(s, MOE_PROF_DEC_GATEUP, true);
-  prof_mark(s, MOE_PROF_DEC_DOWN, false);
-  if (split)
-    hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, true>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1], ndn[0]);
-  else
-    hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, false>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1], ndn[0]);
-  prof_mark(s, MOE_PROF_DEC_DOWN, true);
+  auto go = [&](auto sp, auto mb) {
+    constexpr bool SP = decltype(sp)::value;
+    constexpr int MB = decltype(mb)::value;
+    prof_mark(s, MOE_PROF_DEC_GATEUP, false);
+    hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, SP, MB>), dim3(ngu[0] + ngu[1]), block, 0, s, gu[0], gu[1],
+                       ngu[0]);
+    prof_mark(s, MOE_PROF_DEC_GATEUP, true);
+    prof_mark(s, MOE_PROF_DEC_DOWN, false);
+    hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1],
+                       ndn[0]);
+    prof_mark(s, MOE_PROF_DEC_DOWN, true);
+  };
+  using T1 = std::true_type;
+  using F0 = std::false_type;
+  using M1 = std::integral_constant<int, 1>;
+  using M4 = std::integral_constant<int, 4>;
+  if (split) {   // at most 4 rows
+    go(T1{}, M1{});
+  } else if (max_rows_e <= 16) {
+    go(F0{}, M1{});
+  } else {
+    go(F0{}, M4{});
+  }
   return check_launch("moe_grouped_ffn bf16 decode");
 }
 

@@ -350,6 +350,38 @@ def test_grouped_ffn_batch_equals_separate_calls(T, Fs):
     assert_close(to_np(s_bat), ref, cfg.dtype, "shared expert")
 
 
+def test_grouped_ffn_batch_split_beside_wide_routed():
+    """A batch whose first problem splits its down projection over K (2 rows of the 5632-wide
+    shared expert) beside a routed problem of another batch with more than 16 rows per expert:
+    the shared launch then covers the routed experts in several 16-row passes, and both outputs
+    must equal those of separate calls bit for bit."""
+    cfg = synth.get_config("qwen_decode_bf16", T=2, d=256, E=4, k=2, F=256, F_shared=5632)
+    layer, w = _build(cfg)
+    T2 = 48
+    x1 = _x_dev(cfg, synth.gen_x(cfg, 0, T=2))
+    x2 = _x_dev(cfg, synth.gen_x(cfg, 1, T=T2))
+    say("  case grouped_ffn_batch split + 48-token routed: launching")
+    r = B.route_permute(x2, layer.w_router_t, w_shared_gate=layer.w_sg, **layer.route_args())
+    counts = r["offsets"].cpu().diff()
+    assert int(counts.max()) > 16
+    rows = T2 * cfg.k
+    offs = torch.tensor([0, 2], dtype=torch.int32).to(DEV)
+    y_sep = B.grouped_ffn(layer.table, rows, r["offsets"], x2, a_row_src=r["perm_src"], a_row_div=cfg.k)
+    s_sep = B.grouped_ffn(layer.shared.table, 2, offs, x1)
+    probs = [B.ffn_problem(layer.shared.table, 2, offs, x1),
+             B.ffn_problem(layer.table, rows, r["offsets"], x2, a_row_src=r["perm_src"], a_row_div=cfg.k)]
+    ws = torch.empty(B.grouped_ffn_batch_workspace_size(probs), device=DEV, dtype=torch.uint8)
+    ws.fill_(0x5A)
+    s_bat, y_bat = B.grouped_ffn_batch(probs, ws=ws)
+    torch.cuda.synchronize()
+    say("    done")
+    assert torch.equal(y_bat.view(torch.int16).cpu(), y_sep.view(torch.int16).cpu())
+    assert torch.equal(s_bat.view(torch.int16).cpu(), s_sep.view(torch.int16).cpu())
+    shared = oracle_expert(cfg, w["shared"])
+    ref = moe.swiglu_ffn(decode(synth.gen_x(cfg, 0, T=2), cfg.act_dtype), shared.w_gate, shared.w_up, shared.w_down)
+    assert_close(to_np(s_bat), ref, cfg.dtype, "shared expert")
+
+
 @pytest.mark.parametrize("T", [64, 300])
 def test_max_experts_and_top_k(T):
     """The largest routing the ABI takes: 1024 experts, top-32. T = 64 takes the decode kernels
