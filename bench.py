@@ -171,6 +171,7 @@ def bench_decode(args, torch, B, synth, MoELayer):
     dirty lines that the step's own reads must first write back). The
     roofline is HBM bytes: the distinct touched experts' bundles + the shared expert + router
     weights + activations in and out."""
+    from expert_offloaded_ffn_amd.layer import FUSE_COMBINE_MAX_T
     cfg = synth.get_config(args.workload)
     if args.tokens:
         cfg = cfg.with_T(args.tokens)
@@ -179,7 +180,7 @@ def bench_decode(args, torch, B, synth, MoELayer):
              shared=synth.gen_shared(cfg) if cfg.F_shared else None,
              w_sg=synth.gen_shared_gate(cfg) if cfg.shared_gate else None)
     layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
-                     threads=16)
+                     threads=16, fuse_combine=not args.no_fuse_combine)
     nb = max(args.batches, 64)
     xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(nb)]
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
@@ -234,7 +235,9 @@ def bench_decode(args, torch, B, synth, MoELayer):
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
                    "d_ff": cfg.F, "d_ff_shared": cfg.F_shared, "mall_flush_MiB": 512, "mall_flush": args.mall_flush,
-                   "hip_graph": bool(args.graph)},
+                   "hip_graph": bool(args.graph),
+                   "combine_in_down_launch": bool(layer.fuse_combine and layer.shared_in_decode_launch(cfg.T)
+                                                  and cfg.T <= FUSE_COMBINE_MAX_T)},
         "step_ms_p10_p50_p90": [round(float(np.percentile(ms, q)), 4) for q in (10, 50, 90)],
         "touched_experts_mean": round(float(np.mean([touched[i % nb] for i in range(args.steps)])), 2),
         "layer_hbm": {"achieved": round(hbm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
@@ -263,6 +266,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="decode: replay the layer as one captured HIP graph")
+    ap.add_argument("--no-fuse-combine", action="store_true",
+                    help="decode: run the combine as its own launch instead of inside the down launch")
     ap.add_argument("--skew-zipf", type=float, default=0.0,
                     help="prefill: add a Zipf(alpha) log-prior to the routing logits (0 = unskewed)")
     ap.add_argument("--mall-flush", choices=["read", "write"], default="read",

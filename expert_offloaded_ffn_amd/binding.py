@@ -51,6 +51,12 @@ class FfnProblem(ctypes.Structure):
                 ("y_dtype", ctypes.c_int32)]
 
 
+class CombineArgs(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("k", ctypes.c_int32), ("perm_dst", ctypes.c_void_p),
+                ("topk_gate", ctypes.c_void_p), ("shared_gate", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("out_dtype", ctypes.c_int32)]
+
+
 class CacheCfg(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("bundle_bytes", ctypes.c_int64),
                 ("slot_stride", ctypes.c_int64), ("bundles_host", ctypes.c_void_p), ("pool", ctypes.c_void_p),
@@ -96,6 +102,10 @@ EXPORTS = {
     "moe_combine": (ctypes.c_int32, [ctypes.c_int32] * 3 + [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                     ctypes.c_void_p]),
+    "moe_grouped_ffn_combine_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(FfnProblem),
+                                               ctypes.POINTER(FfnProblem)]),
+    "moe_grouped_ffn_combine": (ctypes.c_int32, [ctypes.POINTER(FfnProblem), ctypes.POINTER(FfnProblem),
+                                ctypes.POINTER(CombineArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "expert_slot_cache_create": (ctypes.c_int32, [ctypes.POINTER(CacheCfg), ctypes.POINTER(ctypes.c_void_p)]),
     "expert_slot_cache_destroy": (ctypes.c_int32, [ctypes.c_void_p]),
     "expert_slot_cache_reset": (ctypes.c_int32, [ctypes.c_void_p]),
@@ -324,6 +334,28 @@ def combine(y, perm_dst, gate, *, shared_y=None, shared_gate=None, out=None, out
         out = torch.empty(T, d, device=y.device, dtype=torch.bfloat16 if odt == MOE_BF16 else torch.float32)
     _check(lib().moe_combine(T, k, d, ptr(y), ydt, ptr(perm_dst), ptr(gate), ptr(shared_y), ptr(shared_gate),
                              ptr(out), odt, stream_ptr(stream)))
+    return out
+
+
+def grouped_ffn_combine_workspace_size(routed: FfnProblem, shared: FfnProblem | None = None) -> int:
+    return int(lib().moe_grouped_ffn_combine_workspace_size(ctypes.byref(routed),
+                                                             ctypes.byref(shared) if shared is not None else None))
+
+
+def grouped_ffn_combine(routed: FfnProblem, shared, perm_dst, gate, *, shared_gate=None, out=None, out_dtype=MOE_BF16,
+                        ws=None, stream=None):
+    """moe_grouped_ffn_combine: the decode FFN of the routed (and shared) problem with the combine
+    folded into its down launch. Returns out [T, d]."""
+    T, k = gate.shape
+    d = routed.table.contents.d_model
+    dev = gate.device
+    if out is None:
+        out = torch.empty(T, d, device=dev, dtype=torch.bfloat16 if out_dtype == MOE_BF16 else torch.float32)
+    if ws is None:
+        ws = torch.empty(max(grouped_ffn_combine_workspace_size(routed, shared), 256), device=dev, dtype=torch.uint8)
+    cb = CombineArgs(T, k, ptr(perm_dst), ptr(gate), ptr(shared_gate), ptr(out), out_dtype)
+    _check(lib().moe_grouped_ffn_combine(ctypes.byref(routed), ctypes.byref(shared) if shared is not None else None,
+                                         ctypes.byref(cb), ptr(ws), ws.numel(), stream_ptr(stream)))
     return out
 
 

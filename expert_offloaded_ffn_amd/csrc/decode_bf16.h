@@ -59,7 +59,123 @@ struct DecodeArgs {
   int32_t* arrived;  // DOWN with splits > 1: per (active expert, group) arrival counts
   int32_t* clear;    // GATEUP: the arrival counts of the down launch that follows, cleared here
   int clear_n;
+  int32_t* clear2;   // GATEUP: the combine's per-group arrival counts of that launch, cleared here
+  int clear2_n;
 };
+
+// The combine folded into a decode down launch: once every (expert, 32-column group) unit of
+// both problems has stored its outputs for group g, the last workgroup to finish one adds,
+// for every token, the gate-weighted rows of its k experts and the gated shared-expert row
+// over those 32 columns, exactly as moe_combine does (fp32, j ascending, shared term last,
+// one rounding). The expert outputs are fp32 values (already rounded to the problem's y
+// dtype) in the workspace, written and read with device-scope accesses.
+struct DecodeCombine {
+  int T, k, d;
+  const int32_t* perm_dst;   // [T*k] -> row of y_routed
+  const float* gate;         // [T*k]
+  const float* shared_gate;  // [T] or NULL (= 1 when y_shared is given)
+  const float* y_routed;     // [T*k, d]
+  const float* y_shared;     // [T, d] or NULL
+  void* out;                 // [T, d] out_dtype
+  int out_dtype;
+  int32_t* arrived;          // [d / 32], zero when the launch starts
+  int nprob;                 // problems in the launch (units of both count)
+};
+
+// Number of experts that have rows and a slot (the units of one 32-column group).
+__device__ __forceinline__ int count_active_experts(const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ slot_of_expert, int E) {
+  const int lane = threadIdx.x & 63;
+  int n = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    n += __popcll(__ballot(e < E && offsets[e + 1] > offsets[e] && slot_of_expert[e] >= 0));
+  }
+  return n;
+}
+
+// The part of the combine a thread can load before its group is complete: the rows and
+// gates of the first 8 experts of its (token, 4 columns) item (T <= 64, so one item per
+// thread of a 512-thread workgroup) and the shared gate.
+struct CombinePre {
+  int rr[8];
+  float gg[8];
+  float sg;
+};
+
+__device__ __forceinline__ void decode_combine_preload(const DecodeCombine& cb, CombinePre& pre) {
+  const int it = threadIdx.x;
+  if (it >= cb.T * 8) return;
+  const int t = it >> 3, k = cb.k;
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if (u < k) {
+      pre.rr[u] = cb.perm_dst[(size_t)t * k + u];
+      pre.gg[u] = cb.gate[(size_t)t * k + u];
+    }
+  pre.sg = cb.y_shared ? (cb.shared_gate ? cb.shared_gate[t] : 1.0f) : 0.0f;
+}
+
+// Columns 32 g .. 32 g + 31 of out for every token, from the expert outputs (see
+// DecodeCombine); one (token, 4 columns) item per thread, the loads of up to 8 expert rows
+// issued before the first add.
+__device__ __forceinline__ void decode_combine_group(const DecodeCombine& cb, int g, const CombinePre& pre) {
+  const int k = cb.k, d = cb.d;
+  const int it = threadIdx.x;
+  if (it >= cb.T * 8) return;
+  const int t = it >> 3, c = 32 * g + 4 * (it & 7);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int rr[8];
+    float gg[8], v[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < k) {
+        rr[u] = j0 == 0 ? pre.rr[u] : cb.perm_dst[(size_t)t * k + j0 + u];
+        gg[u] = j0 == 0 ? pre.gg[u] : cb.gate[(size_t)t * k + j0 + u];
+      }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[u][q] = __hip_atomic_load(cb.y_routed + (size_t)rr[u] * d + c + q, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (j0 + u < k)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(gg[u], v[u][q], acc[q]);
+  }
+  if (cb.y_shared) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      acc[q] = fmaf(pre.sg, __hip_atomic_load(cb.y_shared + (size_t)t * d + c + q, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT), acc[q]);
+  }
+  if (cb.out_dtype == MOE_BF16) {
+    const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<bf16_t*>(cb.out) + (size_t)t * d + c) = make_uint2(w0, w1);
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(cb.out) + (size_t)t * d + c) =
+        make_float4(acc[0], acc[1], acc[2], acc[3]);
+  }
+}
+
+// An output value of the down projection: stored as y_dtype, or (folded combine) as the
+// fp32 value of that rounding with a device-scope store, so the combining workgroup, on any
+// XCD, reads it without a cache-wide write-back.
+template <bool COMB>
+__device__ __forceinline__ void store_y(const DecodeArgs& p, size_t o, float v) {
+  if constexpr (COMB) {
+    const float r = p.out_dtype == MOE_BF16 ? bf16_to_f32(f32_to_bf16(v)) : v;
+    __hip_atomic_store(static_cast<float*>(p.out) + o, r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[o] = f32_to_bf16(v);
+    else static_cast<float*>(p.out)[o] = v;
+  }
+}
 
 #ifndef MOEFFN_DEC_CHUNK
 #define MOEFFN_DEC_CHUNK 4
@@ -81,17 +197,22 @@ constexpr int kDecMaxSplits = 8;              // workgroups per (expert, group) 
 // MB is the number of 16-row m-blocks a pass covers: 4 in general, 1 when no expert has more
 // than 16 rows, which needs a quarter of the accumulators and of the reduction LDS, so more
 // workgroups (and more loads in flight) fit on a CU.
-template <int MODE, bool SPLIT, int MB>
+// COMB (DOWN only) folds the combine into the launch (DecodeCombine).
+template <int MODE, bool SPLIT, int MB, bool COMB = false>
 __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
-    DecodeArgs p0, DecodeArgs p1, int nb0) {
+    DecodeArgs p0, DecodeArgs p1, int nb0, DecodeCombine cb) {
+  static_assert(!COMB || MODE == MODE_DOWN, "the combine follows the down projection");
   __shared__ f32x4_t red[kDecWaves - 1][MB][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
   __shared__ int s_last;                               // split K: this workgroup arrived last
+  __shared__ int s_glast;                              // COMB: last unit of its column group
   const bool second = (int)blockIdx.x >= nb0;
   const DecodeArgs p = second ? p1 : p0;
   const int bid = second ? (int)blockIdx.x - nb0 : (int)blockIdx.x;
-  if constexpr (SPLIT && MODE == MODE_GATEUP) {
+  if constexpr (MODE == MODE_GATEUP) {
     if (bid == 0 && p.clear != nullptr)
       for (int j = threadIdx.x; j < p.clear_n; j += blockDim.x) p.clear[j] = 0;
+    if (bid == 0 && p.clear2 != nullptr)
+      for (int j = threadIdx.x; j < p.clear2_n; j += blockDim.x) p.clear2[j] = 0;
   }
   // The block's coordinates are uniform; integer division runs on the vector unit, so they
   // are moved back to scalar registers, which keeps the expert's offsets and slot on scalar loads.
@@ -182,11 +303,8 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
                 f32_to_bf16(silu_fast(acc[m][0][q]) * acc[m][1][q]);
           } else if (S == 1) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const size_t o = (size_t)(row0 + r) * p.N + (2 * g + j) * 16 + (lane & 15);
-              if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[o] = f32_to_bf16(acc[m][j][q]);
-              else static_cast<float*>(p.out)[o] = acc[m][j][q];
-            }
+            for (int j = 0; j < 2; ++j)
+              store_y<COMB>(p, (size_t)(row0 + r) * p.N + (2 * g + j) * 16 + (lane & 15), acc[m][j][q]);
           } else if constexpr (SPLIT) {
             // device-scope stores (written through to the coherent level, not left in this
             // XCD's L2), so no cache-wide write-back is needed to publish them
@@ -229,12 +347,34 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
 #pragma unroll
           for (int t = 1; t < kDecMaxSplits; ++t)
             if (t < S) acc_v += v[t];
-          if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[o] = f32_to_bf16(acc_v);
-          else static_cast<float*>(p.out)[o] = acc_v;
+          store_y<COMB>(p, o, acc_v);
         }
       }
     }
     __syncthreads();
+  }
+  if constexpr (COMB) {
+    // This workgroup finished a unit (expert e, group g) when it ran the whole K range or
+    // was the last of its K splits. Its stores have completed before the unit is counted;
+    // the workgroup that counts the group's last unit combines the group's columns.
+    bool done = true;
+    if constexpr (SPLIT) done = S == 1 || s_last;
+    if (done) {
+      CombinePre pre;
+      decode_combine_preload(cb, pre);   // overlaps the wait for this workgroup's stores
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (w == 0) {
+        const int units = count_active_experts(p0.offsets, p0.slot_of_expert, p0.E) +
+                          (cb.nprob > 1 ? count_active_experts(p1.offsets, p1.slot_of_expert, p1.E) : 0);
+        if (lane == 0) s_glast = atomicAdd(&cb.arrived[g], 1) == units - 1;
+      }
+      __syncthreads();
+      if (s_glast) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // no load moves above the count
+        decode_combine_group(cb, g, pre);
+      }
+    }
   }
 }
 

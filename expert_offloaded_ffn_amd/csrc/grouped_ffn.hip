@@ -258,12 +258,19 @@ void decode_args(const FfnCall& c, int S, DecodeArgs* gu, DecodeArgs* dn, int* n
 }
 
 // One or two decode problems in one gate/up launch and one down launch; the blocks of the
-// first problem come first in dispatch order.
-moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s) {
+// first problem come first in dispatch order. With cb, the down launch also combines (the
+// problems' y are then the fp32 buffers cb reads, and cb->arrived is cleared by the gate/up
+// launch).
+moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s, const DecodeCombine* cb = nullptr) {
   DecodeArgs gu[2], dn[2];
   int ngu[2] = {0, 0}, ndn[2] = {0, 0};
   for (int i = 0; i < n; ++i)
     decode_args(calls[i], decode_down_splits(&calls[i].t, calls[i].rows), &gu[i], &dn[i], &ngu[i], &ndn[i]);
+  if (cb != nullptr) {
+    gu[0].clear2 = cb->arrived;
+    gu[0].clear2_n = cb->d / 32;
+  }
+  const DecodeCombine no_cb{};
   if (n == 1) {
     gu[1] = gu[0];
     dn[1] = dn[0];
@@ -283,11 +290,15 @@ moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s) {
     constexpr int MB = decltype(mb)::value;
     prof_mark(s, MOE_PROF_DEC_GATEUP, false);
     hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, SP, MB>), dim3(ngu[0] + ngu[1]), block, 0, s, gu[0], gu[1],
-                       ngu[0]);
+                       ngu[0], no_cb);
     prof_mark(s, MOE_PROF_DEC_GATEUP, true);
     prof_mark(s, MOE_PROF_DEC_DOWN, false);
-    hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1],
-                       ndn[0]);
+    if (cb != nullptr)
+      hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB, true>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0],
+                         dn[1], ndn[0], *cb);
+    else
+      hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1],
+                         ndn[0], no_cb);
     prof_mark(s, MOE_PROF_DEC_DOWN, true);
   };
   using T1 = std::true_type;
@@ -490,4 +501,97 @@ extern "C" moe_status moe_grouped_ffn_batch(const moe_ffn_problem* problems, int
   for (int i = 0; i < n; ++i)
     if (moe_status st = run_call(c[i], s)) return st;
   return MOE_OK;
+}
+
+// The fused decode FFN + combine: the problems as in moe_grouped_ffn_batch (shared first),
+// the expert outputs in fp32 buffers after the batch workspace, then the combine's group
+// arrival counts.
+namespace moeffn {
+namespace {
+struct FusedLayout {
+  size_t batch, y_routed, y_shared, arrived, total;
+};
+FusedLayout fused_layout(const moe_ffn_problem* routed, const moe_ffn_problem* shared) {
+  FusedLayout L{};
+  size_t h, m;
+  if (shared) L.batch += align_up(ws_layout(shared->table, shared->rows, shared->act_dtype, &h, &m), 256);
+  L.batch += align_up(ws_layout(routed->table, routed->rows, routed->act_dtype, &h, &m), 256);
+  const size_t d = routed->table->d_model;
+  L.y_routed = L.batch;
+  L.y_shared = L.y_routed + align_up((size_t)routed->rows * d * 4, 256);
+  L.arrived = L.y_shared + (shared ? align_up((size_t)shared->rows * d * 4, 256) : 0);
+  L.total = L.arrived + align_up(d / 32 * 4, 256);
+  return L;
+}
+}  // namespace
+}  // namespace moeffn
+
+extern "C" size_t moe_grouped_ffn_combine_workspace_size(const moe_ffn_problem* routed,
+                                                          const moe_ffn_problem* shared) {
+  if (!routed || !routed->table || routed->rows < 0) return 0;
+  if (shared && (!shared->table || shared->rows < 0 || shared->table->d_model != routed->table->d_model)) return 0;
+  return fused_layout(routed, shared).total;
+}
+
+extern "C" moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, const moe_ffn_problem* shared,
+                                              const moe_combine_args* comb, void* ws, size_t ws_bytes,
+                                              void* stream) {
+  clear_error();
+  MOE_REQUIRE(routed != nullptr && routed->table != nullptr && comb != nullptr, MOE_EINVAL,
+              "moe_grouped_ffn_combine: routed problem, its table and comb must not be NULL");
+  MOE_REQUIRE(!shared || shared->table != nullptr, MOE_EINVAL, "moe_grouped_ffn_combine: shared problem has no table");
+  const int T = comb->T, k = comb->k, d = routed->table->d_model;
+  MOE_REQUIRE(T >= 0 && k >= 1 && k <= 32, MOE_EINVAL, "moe_grouped_ffn_combine: need T >= 0 and 1 <= k <= 32 (T=%d k=%d)",
+              T, k);
+  MOE_REQUIRE(T <= 64, MOE_EUNSUPPORTED, "moe_grouped_ffn_combine: T=%d > 64 (decode batches only)", T);
+  MOE_REQUIRE(routed->rows == T * k, MOE_EINVAL, "moe_grouped_ffn_combine: routed rows %d != T*k = %d", routed->rows,
+              T * k);
+  if (shared) {
+    MOE_REQUIRE(shared->rows == T, MOE_EINVAL, "moe_grouped_ffn_combine: shared rows %d != T = %d", shared->rows, T);
+    MOE_REQUIRE(shared->table->d_model == d, MOE_EINVAL, "moe_grouped_ffn_combine: shared d_model %d != %d",
+                shared->table->d_model, d);
+  }
+  MOE_REQUIRE(comb->out_dtype == MOE_F32 || comb->out_dtype == MOE_BF16, MOE_EUNSUPPORTED,
+              "moe_grouped_ffn_combine: out_dtype %d", comb->out_dtype);
+  if (T == 0) return MOE_OK;
+  MOE_REQUIRE(comb->perm_dst && comb->topk_gate && comb->out && ws, MOE_EINVAL,
+              "moe_grouped_ffn_combine: NULL perm_dst, topk_gate, out or workspace");
+  MOE_REQUIRE(aligned(comb->out, 16) && aligned(ws, 256), MOE_EINVAL,
+              "moe_grouped_ffn_combine: out needs 16-B and ws 256-B alignment");
+  const FusedLayout L = fused_layout(routed, shared);
+  MOE_REQUIRE(ws_bytes >= L.total, MOE_ECAPACITY, "moe_grouped_ffn_combine: workspace %zu < %zu bytes", ws_bytes,
+              L.total);
+  char* w = static_cast<char*>(ws);
+  float* y_routed = reinterpret_cast<float*>(w + L.y_routed);
+  float* y_shared = shared ? reinterpret_cast<float*>(w + L.y_shared) : nullptr;
+  FfnCall c[2];
+  int n = 0;
+  size_t off = 0;
+  size_t h, m;
+  for (const moe_ffn_problem* q : {shared, routed}) {
+    if (!q) continue;
+    const size_t need = ws_layout(q->table, q->rows, q->act_dtype, &h, &m);
+    c[n] = FfnCall{*q->table, q->rows, q->offsets, q->a, q->a_scale, q->act_dtype, q->a_row_src, q->a_row_div,
+                   q == routed ? (void*)y_routed : (void*)y_shared, q->y_dtype, w + off, need};
+    off += align_up(need, 256);
+    if (moe_status st = check_call(c[n], "moe_grouped_ffn_combine")) return st;
+    MOE_REQUIRE(decode_path(c[n]), MOE_EUNSUPPORTED,
+                "moe_grouped_ffn_combine: the %s problem is not a decode problem (bf16 weights, at most 64 rows per "
+                "expert)", q == routed ? "routed" : "shared");
+    ++n;
+  }
+  DecodeCombine cb{};
+  cb.T = T;
+  cb.k = k;
+  cb.d = d;
+  cb.perm_dst = comb->perm_dst;
+  cb.gate = comb->topk_gate;
+  cb.shared_gate = shared ? comb->shared_gate : nullptr;
+  cb.y_routed = y_routed;
+  cb.y_shared = y_shared;
+  cb.out = comb->out;
+  cb.out_dtype = comb->out_dtype;
+  cb.arrived = reinterpret_cast<int32_t*>(w + L.arrived);
+  cb.nprob = n;
+  return launch_decode(c, n, as_stream(stream), &cb);
 }

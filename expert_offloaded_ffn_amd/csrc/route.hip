@@ -190,7 +190,7 @@ __device__ __forceinline__ void select_token(
     const float* __restrict__ select_bias,
     float* __restrict__ shared_gate, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int* hist,
     float* wk, int E, int k, int score_fn, int renormalize, float route_scale, int n_groups, int topk_groups,
-    int group_topn) {
+    int group_topn, int32_t* idx_copy = nullptr) {
   const int lane = threadIdx.x & 63;
   const int gsz = n_groups > 0 ? E / n_groups : E;
   float logit[PER_LANE], key[PER_LANE];
@@ -305,6 +305,7 @@ __device__ __forceinline__ void select_token(
   g *= route_scale;
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = sel_idx;
+    if (idx_copy) idx_copy[t * k + lane] = sel_idx;   // (LDS) for a grouping in the same workgroup
     topk_gate[(size_t)t * k + lane] = g;
     if (hist) atomicAdd(&hist[sel_idx], 1);
   }
@@ -416,11 +417,13 @@ __global__ __launch_bounds__(1024) void route_finish_small(
   __shared__ float wkeys[16][kFuseMaxE];
   __shared__ int32_t off[kFuseMaxE];
   __shared__ int32_t wave_sum[16];
+  __shared__ int32_t idx_lds[kFuseMaxT * 32];   // the selection, read back by the grouping
   const int wave = threadIdx.x >> 6;
   const int n = T * ncols;
-  // Each logit is the sum of its slices in slice order. A thread takes up to 4 logits at a
-  // time and issues 8 slices of each (32 loads) before the first add.
-  constexpr int kE = 4, kS = 8;
+  // Each logit is the sum of its slices in slice order. A thread takes up to 2 logits at a
+  // time and issues 16 slices of each (32 loads; 16 slices cover d = 2048) before the
+  // first add.
+  constexpr int kE = 2, kS = 16;
   for (int j0 = threadIdx.x; j0 < n; j0 += kE * blockDim.x) {
     float v[kE];
     for (int s0 = 0; s0 < nsl; s0 += kS) {
@@ -451,9 +454,10 @@ __global__ __launch_bounds__(1024) void route_finish_small(
   __syncthreads();
   for (int t = wave; t < T; t += 16)
     select_token<PER_LANE>(t, lg, ncols, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, nullptr,
-                           wkeys[wave], E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn);
+                           wkeys[wave], E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn,
+                           idx_lds);
   __syncthreads();
-  group_small<KMAX>(topk_idx, counts, offsets, perm_src, perm_dst, T, k, E, off, wave_sum);
+  group_small<KMAX>(idx_lds, counts, offsets, perm_src, perm_dst, T, k, E, off, wave_sum);
 }
 
 // 17..64 tokens: one wavefront per token sums the token's slices (slice order, 8 slice loads

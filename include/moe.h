@@ -296,6 +296,42 @@ moe_status moe_combine(int32_t T, int32_t k, int32_t d, const void* y, int32_t y
                        const void* shared_y, const float* shared_gate,
                        void* out, int32_t out_dtype, void* stream);
 
+/* ------------------------------------------- decode FFN with the combine --
+ * A decode step's grouped FFN and combine in one call (two launches): the
+ * routed experts and, optionally, the always-resident shared expert ([VVLLM]
+ * "Gotcha": shared experts sit outside the routed set), then the gate-weighted
+ * sum back to token order, which the last workgroup to finish each 32-column
+ * group of the down projection computes for that group ([NOVA] section 3,
+ * Optimization #3: fewer launches per decode step).
+ * The result equals, bit for bit, moe_grouped_ffn_batch over {shared, routed}
+ * (or {routed}) followed by moe_combine(T, k, d, routed.y, routed.y_dtype,
+ * perm_dst, topk_gate, shared.y, shared_gate, out, out_dtype): each expert
+ * output is rounded to its problem's y_dtype and the sum runs in fp32, j
+ * ascending, shared term last, rounded once to out_dtype.
+ *  routed  the routed problem: rows = T*k, a_row_src = perm_src, a_row_div = k
+ *  shared  NULL or the shared expert: one group, offsets [0, T], rows = T
+ *  The problems' y pointers are not used (may be NULL): the expert outputs
+ *  stay in the workspace. Only out [T, d] (16-B aligned) is written.
+ * Both problems must be decode problems (bf16 weights and activations, T <= 64
+ * tokens); otherwise MOE_EUNSUPPORTED (use the batch call and moe_combine).
+ * Workspace: moe_grouped_ffn_combine_workspace_size(routed, shared) bytes,
+ * 256-B aligned. Calls that share a workspace must not overlap.
+ * Errors: as moe_grouped_ffn for each problem; MOE_EINVAL for rows that do
+ * not match T and k, MOE_ECAPACITY for a short workspace. T = 0 is a no-op.
+ */
+typedef struct {
+  int32_t T, k;
+  const int32_t* perm_dst;   /* [T*k] device: row of the routed outputs */
+  const float* topk_gate;    /* [T*k] device */
+  const float* shared_gate;  /* [T] device, or NULL = 1 (used only with a shared problem) */
+  void* out;                 /* [T, d] device, out_dtype */
+  int32_t out_dtype;         /* MOE_F32 or MOE_BF16 */
+} moe_combine_args;
+
+size_t moe_grouped_ffn_combine_workspace_size(const moe_ffn_problem* routed, const moe_ffn_problem* shared);
+moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, const moe_ffn_problem* shared,
+                                   const moe_combine_args* comb, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- expert slot cache --
  * Expert-granular residency: a fixed pool of n_slots bundle slots in HBM backed
  * by every expert's bundle in pinned host memory ([NOVA] section 3,

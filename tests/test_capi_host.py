@@ -80,7 +80,7 @@ def test_grouped_ffn_validation_codes():
 
 _STRUCTS = [("moe_route_cfg", B.RouteCfg), ("moe_expert_table", B.ExpertTable), ("moe_ffn_problem", B.FfnProblem),
             ("moe_cache_cfg", B.CacheCfg), ("moe_cache_stats", B.CacheStats), ("moe_cache_entry", B.CacheEntry),
-            ("moe_profile", B.Profile)]
+            ("moe_profile", B.Profile), ("moe_combine_args", B.CombineArgs)]
 
 
 def test_struct_layouts_match_header(tmp_path):
@@ -133,6 +133,42 @@ def test_batch_and_route_permute_validation_codes():
     assert L.moe_route_permute(ctypes.byref(cfg), *args, 0, null) == -4             # short workspace
     args[1] = ctypes.c_void_p(0x1001)                                               # misaligned router weights
     assert L.moe_route_permute(ctypes.byref(cfg), *args, 1 << 16, null) == -1
+
+
+def test_grouped_ffn_combine_validation_codes():
+    """The fused decode FFN + combine rejects, before any launch, what the two-call sequence would
+    reject, rows that do not match T and k, non-decode problems and short workspaces."""
+    L = B.lib()
+    t = B.ExpertTable(ctypes.c_void_p(256), B.bundle_bytes(256, 512, B.MOE_BF16), ctypes.c_void_p(256), 8, 256, 512,
+                      B.MOE_BF16)
+    fake = ctypes.c_void_p(0x1000)
+    T, k = 4, 2
+    routed = B.FfnProblem(ctypes.pointer(t), T * k, fake, fake, None, B.MOE_BF16, fake, k, None, B.MOE_BF16)
+    shared = B.FfnProblem(ctypes.pointer(t), T, fake, fake, None, B.MOE_BF16, None, 1, None, B.MOE_BF16)
+    cb = B.CombineArgs(T, k, fake, fake, fake, fake, B.MOE_BF16)
+    need = L.moe_grouped_ffn_combine_workspace_size(ctypes.byref(routed), ctypes.byref(shared))
+    batch = L.moe_grouped_ffn_batch_workspace_size((B.FfnProblem * 2)(shared, routed), 2)
+    # the batch workspace, fp32 expert outputs of both problems, then the group counts
+    assert need == batch + T * k * 256 * 4 + T * 256 * 4 + 256
+    assert L.moe_grouped_ffn_combine(None, None, ctypes.byref(cb), fake, need, None) == -1
+    assert L.moe_grouped_ffn_combine(ctypes.byref(routed), None, None, fake, need, None) == -1
+    assert L.moe_grouped_ffn_combine(ctypes.byref(routed), ctypes.byref(shared), ctypes.byref(cb), fake, need - 1,
+                                     None) == -4
+    bad_rows = B.CombineArgs(T + 1, k, fake, fake, fake, fake, B.MOE_BF16)
+    assert L.moe_grouped_ffn_combine(ctypes.byref(routed), None, ctypes.byref(bad_rows), fake, need, None) == -1
+    assert b"routed rows" in L.moe_last_error()
+    big = B.CombineArgs(65, 1, fake, fake, fake, fake, B.MOE_BF16)
+    assert L.moe_grouped_ffn_combine(ctypes.byref(routed), None, ctypes.byref(big), fake, need, None) == -2
+    t32 = B.ExpertTable(ctypes.c_void_p(256), B.bundle_bytes(256, 512, B.MOE_F32), ctypes.c_void_p(256), 8, 256, 512,
+                        B.MOE_F32)
+    r32 = B.FfnProblem(ctypes.pointer(t32), T * k, fake, fake, None, B.MOE_F32, fake, k, None, B.MOE_F32)
+    need32 = L.moe_grouped_ffn_combine_workspace_size(ctypes.byref(r32), None)
+    assert L.moe_grouped_ffn_combine(ctypes.byref(r32), None, ctypes.byref(cb), ctypes.c_void_p(0x10000), need32,
+                                     None) == -2
+    assert b"not a decode problem" in L.moe_last_error()
+    empty = B.CombineArgs(0, k, None, None, None, None, B.MOE_BF16)
+    r0 = B.FfnProblem(ctypes.pointer(t), 0, None, None, None, B.MOE_BF16, None, k, None, B.MOE_BF16)
+    assert L.moe_grouped_ffn_combine(ctypes.byref(r0), None, ctypes.byref(empty), None, 0, None) == 0
 
 
 def test_route_permute_workspace_only_holds_slices_when_used():
