@@ -61,6 +61,7 @@ struct DecodeArgs {
   int clear_n;
   int32_t* clear2;   // GATEUP: the combine's per-group arrival counts of that launch, cleared here
   int clear2_n;
+  int rchunks;       // workgroups per (expert, group), each taking 16 rows (1: one takes all rows)
 };
 
 // The combine folded into a decode down launch: once every (expert, 32-column group) unit of
@@ -194,9 +195,10 @@ constexpr int kDecMaxSplits = 8;              // workgroups per (expert, group) 
 // the routed experts and the shared expert, in one launch). SPLIT launches carry a down
 // projection split over K (and, for GATEUP, clear its arrival counts); the others compile
 // without that code.
-// MB is the number of 16-row m-blocks a pass covers: 4 in general, 1 when no expert has more
-// than 16 rows, which needs a quarter of the accumulators and of the reduction LDS, so more
-// workgroups (and more loads in flight) fit on a CU.
+// MB is the number of 16-row m-blocks a pass covers: 1 for decode batches (a quarter of the
+// accumulators and of the reduction LDS of 4, so more workgroups and more loads in flight fit
+// on a CU; an expert with more rows takes several passes, a one-expert problem several
+// workgroups, see rchunks), 4 for larger ones.
 // COMB (DOWN only) folds the combine into the launch (DecodeCombine).
 template <int MODE, bool SPLIT, int MB, bool COMB = false>
 __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
@@ -218,8 +220,21 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
   // are moved back to scalar registers, which keeps the expert's offsets and slot on scalar loads.
   const int G = p.N / 32;
   const int S = (SPLIT && MODE == MODE_DOWN) ? p.splits : 1;
-  const int unit = __builtin_amdgcn_readfirstlane(bid / S);   // (active expert, group)
-  const int s = bid - unit * S;                               // K split
+  const int R = p.rchunks;
+  int unit, s = 0, c = 0;   // (active expert, group), K split, 16-row chunk
+  if (R > 1) {
+    // the R chunks of units 8q .. 8q + 7 are blocks 8Rq .. 8Rq + 8R - 1, chunk c of unit
+    // 8q + x at 8Rq + 8c + x: the blocks that read one weight group run on one XCD
+    // (block b on XCD b % 8) at about the same time, so the chunks after the first find it in L2
+    const int q = bid / (8 * R), rem = bid - q * 8 * R;
+    c = rem >> 3;
+    unit = q * 8 + (rem & 7);
+  } else {
+    unit = bid / S;
+    s = bid - unit * S;
+  }
+  unit = __builtin_amdgcn_readfirstlane(unit);
+  c = __builtin_amdgcn_readfirstlane(c);
   const int i = __builtin_amdgcn_readfirstlane(unit / G);
   const int g = unit - i * G;
   const int e = __builtin_amdgcn_readfirstlane(nth_active_expert(p.offsets, p.slot_of_expert, p.E, i));
@@ -234,7 +249,8 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
   const char* b0 = B + ((int64_t)(2 * g) * KT) * 1024 + 16 * lane;      // n-tile 2g
   const char* b1 = B + ((int64_t)(2 * g + 1) * KT) * 1024 + 16 * lane;  // n-tile 2g+1
 
-  for (int mc = 0; mc < n_e; mc += 16 * MB) {
+  const int mc_end = R > 1 ? min(n_e, 16 * c + 16) : n_e;
+  for (int mc = 16 * c; mc < mc_end; mc += 16 * MB) {
     const int mbn = min(MB, (n_e - mc + 15) / 16);
     const bf16_t* arow[MB];
 #pragma unroll
@@ -365,8 +381,8 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
       wait_vmcnt<0>();
       __syncthreads();
       if (w == 0) {
-        const int units = count_active_experts(p0.offsets, p0.slot_of_expert, p0.E) +
-                          (cb.nprob > 1 ? count_active_experts(p1.offsets, p1.slot_of_expert, p1.E) : 0);
+        const int units = count_active_experts(p0.offsets, p0.slot_of_expert, p0.E) * p0.rchunks +
+                          (cb.nprob > 1 ? count_active_experts(p1.offsets, p1.slot_of_expert, p1.E) * p1.rchunks : 0);
         if (lane == 0) s_glast = atomicAdd(&cb.arrived[g], 1) == units - 1;
       }
       __syncthreads();

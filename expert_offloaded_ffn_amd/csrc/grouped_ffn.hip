@@ -213,7 +213,8 @@ bool decode_path(const FfnCall& c) {
 
 // The decode kernels' arguments and block counts for one problem: gate/up + SwiGLU into
 // H (in the problem's workspace), then down into y over S K splits.
-void decode_args(const FfnCall& c, int S, DecodeArgs* gu, DecodeArgs* dn, int* nb_gu, int* nb_dn) {
+// R > 1 gives each (expert, 32-row group) R workgroups of 16 rows each (see ffn_decode_bf16).
+void decode_args(const FfnCall& c, int S, int R, DecodeArgs* gu, DecodeArgs* dn, int* nb_gu, int* nb_dn) {
   size_t h_off, map_off, hs_off, part_off, arrived_off;
   ws_layout(&c.t, c.rows, c.act_dtype, &h_off, &map_off, &hs_off, &part_off, &arrived_off);
   const BundleGeom g = bundle_geom(c.t.d_model, c.t.d_ff, c.t.w_dtype);
@@ -236,10 +237,13 @@ void decode_args(const FfnCall& c, int S, DecodeArgs* gu, DecodeArgs* dn, int* n
   q.out_dtype = MOE_BF16;
   q.rows = c.rows;
   q.splits = 1;
+  q.rchunks = R;
   q.clear = S > 1 ? reinterpret_cast<int32_t*>(c.ws + arrived_off) : nullptr;
   q.clear_n = S > 1 ? max_active * (d / 32) : 0;
   *gu = q;
-  *nb_gu = max_active * (q.N / 32);
+  // R > 1: the units padded to a multiple of 8, each with R workgroups
+  auto blocks = [&](int units) { return R > 1 ? (units + 7) / 8 * 8 * R : units; };
+  *nb_gu = blocks(max_active * (q.N / 32));
   q.a = H;
   q.a_row_src = nullptr;
   q.a_row_div = 1;
@@ -254,8 +258,12 @@ void decode_args(const FfnCall& c, int S, DecodeArgs* gu, DecodeArgs* dn, int* n
   q.clear = nullptr;
   q.clear_n = 0;
   *dn = q;
-  *nb_dn = max_active * (q.N / 32) * S;
+  *nb_dn = blocks(max_active * (q.N / 32) * S);
 }
+
+#ifndef MOEFFN_DEC_MB1_MAX_ROWS
+#define MOEFFN_DEC_MB1_MAX_ROWS 64
+#endif
 
 // One or two decode problems in one gate/up launch and one down launch; the blocks of the
 // first problem come first in dispatch order. With cb, the down launch also combines (the
@@ -264,8 +272,23 @@ void decode_args(const FfnCall& c, int S, DecodeArgs* gu, DecodeArgs* dn, int* n
 moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s, const DecodeCombine* cb = nullptr) {
   DecodeArgs gu[2], dn[2];
   int ngu[2] = {0, 0}, ndn[2] = {0, 0};
-  for (int i = 0; i < n; ++i)
-    decode_args(calls[i], decode_down_splits(&calls[i].t, calls[i].rows), &gu[i], &dn[i], &ngu[i], &ndn[i]);
+  // One 16-row m-block per pass (71 VGPRs, so more workgroups fit on a CU) while no expert of
+  // a routed problem can hold more than MOEFFN_DEC_MB1_MAX_ROWS rows; a one-expert problem (a
+  // shared expert) with more than 16 rows then takes one workgroup per 16 rows. Else 4 m-blocks
+  // per pass (112 VGPRs; a 2-block pass at the 6-wave cap spills and measured slower).
+  int max_rows_e = 0;
+  bool split = false;
+  for (int i = 0; i < n; ++i) {
+    const FfnCall& c = calls[i];
+    if (c.t.n_experts > 1) max_rows_e = std::max(max_rows_e, c.a_row_src ? (c.rows + c.a_row_div - 1) / c.a_row_div : c.rows);
+    split |= decode_down_splits(&c.t, c.rows) > 1;
+  }
+  const bool mb1 = split || max_rows_e <= MOEFFN_DEC_MB1_MAX_ROWS;
+  for (int i = 0; i < n; ++i) {
+    const FfnCall& c = calls[i];
+    const int R = (mb1 && c.t.n_experts == 1 && c.rows > 16) ? (c.rows + 15) / 16 : 1;
+    decode_args(c, decode_down_splits(&c.t, c.rows), R, &gu[i], &dn[i], &ngu[i], &ndn[i]);
+  }
   if (cb != nullptr) {
     gu[0].clear2 = cb->arrived;
     gu[0].clear2_n = cb->d / 32;
@@ -274,15 +297,6 @@ moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s, const Decod
   if (n == 1) {
     gu[1] = gu[0];
     dn[1] = dn[0];
-  }
-  const bool split = dn[0].splits > 1 || (n == 2 && dn[1].splits > 1);
-  // one 16-row m-block per pass while every expert holds at most 16 rows (71 VGPRs, so more
-  // workgroups fit on a CU), else 4 (112 VGPRs; a 2-block pass at the 6-wave cap spills and
-  // measured slower than 4 blocks at 17..32 rows)
-  int max_rows_e = 0;
-  for (int i = 0; i < n; ++i) {
-    const FfnCall& c = calls[i];
-    max_rows_e = std::max(max_rows_e, c.a_row_src ? (c.rows + c.a_row_div - 1) / c.a_row_div : c.rows);
   }
   const dim3 block(64 * kDecWaves);
   auto go = [&](auto sp, auto mb) {
@@ -307,7 +321,7 @@ moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s, const Decod
   using M4 = std::integral_constant<int, 4>;
   if (split) {   // at most 4 rows
     go(T1{}, M1{});
-  } else if (max_rows_e <= 16) {
+  } else if (mb1) {
     go(F0{}, M1{});
   } else {
     go(F0{}, M4{});
