@@ -360,6 +360,8 @@ void launch_select(int tpw, hipStream_t s, float* scores, const float* lb, const
 // group_small); for more tokens the slices would be as many bytes as the router weights,
 // too many for one workgroup to read back, so a wavefront per token sums and selects
 // (route_select_slices) and the one-workgroup grouping follows.
+// (one workgroup reading back the slices of 17..64 tokens measured slower than the two
+// launches: 0.244 vs 0.231 ms per Qwen-shaped step at 64 tokens)
 constexpr int kFuseMaxT = 16;
 constexpr int kFuseMaxE = 256;
 constexpr int kSliceSteps = 4;
