@@ -77,6 +77,8 @@ def cpu_baseline(cfg, w, sample_tokens):
     def dec_w(m):
         if cfg.dtype == "fp8":
             return formats.dequantize_weight_blocks(*m)
+        if cfg.dtype == "mxfp4":
+            return formats.dequantize_mxfp4_weight(*m)
         return dec(m)
 
     threads = len(os.sched_getaffinity(0))

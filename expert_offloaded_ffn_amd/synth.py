@@ -1,7 +1,8 @@
 """Seeded synthetic inputs for one Mixture-of-Experts FFN layer.
 
 This module only draws random tensors and stores them in the formats the layer
-consumes (fp32, bf16 bit patterns, OCP e4m3 codes with fp32 block scales). It
+consumes (fp32, bf16 bit patterns, OCP e4m3 codes with fp32 block scales, OCP MXFP4
+codes with E8M0 scales per 32 inputs). It
 holds none of the layer's arithmetic: routing, grouping, the expert FFN and the
 combine live in the HIP library and, independently, in the CPU oracle. Both
 sides read the exact bytes produced here.
@@ -23,6 +24,9 @@ Mixtral, Qwen-MoE and DeepSeek-family models without fixing their shapes):
                            T=32 tokens per step for 256 steps; router logits
                            biased by a Zipf(1.1) log-prior over a seed-permuted
                            expert order that is re-drawn every 64 steps.
+* ``offload_decode_mxfp4`` the same layer and stream with MXFP4 expert weights
+                           (FP4 E2M1 codes, one E8M0 scale per 32 inputs of an
+                           output column), bf16 router and activations.
 
 Draws: ``numpy.random.default_rng([seed, stream, index])``. Stream 0 holds the
 weights (one index per tensor, so any expert can be drawn on its own), stream 1
@@ -40,7 +44,7 @@ from dataclasses import dataclass, replace
 import numpy as np
 
 __all__ = [
-    "LayerConfig", "CONFIGS", "get_config", "to_bf16_bits", "quantize_e4m3_blocks",
+    "LayerConfig", "CONFIGS", "get_config", "to_bf16_bits", "quantize_e4m3_blocks", "quantize_mxfp4",
     "gen_router", "gen_shared_gate", "gen_select_bias", "gen_expert", "gen_experts",
     "gen_shared", "gen_x", "zipf_logit_bias",
 ]
@@ -57,7 +61,7 @@ class LayerConfig:
     E: int
     k: int
     F: int
-    dtype: str                 # "f32" | "bf16" | "fp8"
+    dtype: str                 # "f32" | "bf16" | "fp8" | "mxfp4"
     score_fn: str              # "softmax" | "sigmoid"
     seed: int
     renormalize: int = 1
@@ -97,6 +101,9 @@ CONFIGS = {
     "offload_decode_bf16": LayerConfig("offload_decode_bf16", T=32, d=4096, E=128, k=8, F=1536,
                                        dtype="bf16", score_fn="softmax", seed=5, n_slots=32,
                                        steps=256, zipf_alpha=1.1, zipf_epoch=64),
+    "offload_decode_mxfp4": LayerConfig("offload_decode_mxfp4", T=32, d=4096, E=128, k=8, F=1536,
+                                        dtype="mxfp4", score_fn="softmax", seed=5, n_slots=32,
+                                        steps=256, zipf_alpha=1.1, zipf_epoch=64),
 }
 
 
@@ -130,6 +137,34 @@ def quantize_e4m3_blocks(w: np.ndarray, block: int = 128):
     return codes.view(torch.uint8).numpy(), scale
 
 
+# FP4 E2M1 magnitudes of the codes 0..7 (sign in bit 3)
+_FP4_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
+
+
+def quantize_mxfp4(w: np.ndarray, block: int = 32):
+    """Weight storage for the MXFP4 workload (the OCP MX conversion): per output column and
+    block of `block` consecutive inputs, shared exponent X = floor(log2(amax)) - 2 (the
+    largest E2M1 exponent), clamped to the E8M0 range (X = -127 for an all-zero block);
+    codes = E2M1(w / 2^X) rounded to the nearest magnitude, ties to the even code, saturated
+    at 6. Returns (uint8 codes [in, out], one code per byte, uint8 E8M0 scales [in/b, out])."""
+    n_in, n_out = w.shape
+    assert n_in % block == 0
+    wb = w.astype(np.float64).reshape(n_in // block, block, n_out)
+    amax = np.abs(wb).max(axis=1)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, -127)
+    X = np.clip(X, -127, 127).astype(np.int64)
+    y = np.abs(wb) / np.ldexp(1.0, X)[:, None, :]
+    y = np.minimum(y, 6.0)
+    hi = np.minimum(np.searchsorted(_FP4_MAG, y, side="left"), 7)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = y - _FP4_MAG[lo], _FP4_MAG[hi] - y
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(_FP4_MAG[hi] == y, hi, code)
+    code = code | (np.signbit(wb).astype(np.int64) << 3)
+    return code.reshape(n_in, n_out).astype(np.uint8), (X + 127).astype(np.uint8)
+
+
 def _store(w32: np.ndarray, dtype: str):
     if dtype == "f32":
         return w32.astype(np.float32)
@@ -137,6 +172,8 @@ def _store(w32: np.ndarray, dtype: str):
         return to_bf16_bits(w32)
     if dtype == "fp8":
         return quantize_e4m3_blocks(w32)
+    if dtype == "mxfp4":
+        return quantize_mxfp4(w32)
     raise ValueError(dtype)
 
 
@@ -169,8 +206,8 @@ def _ffn_weights(cfg: LayerConfig, F: int, base_id: int):
 
 
 def gen_expert(cfg: LayerConfig, e: int):
-    """Expert e's (W_gate [d,F], W_up [d,F], W_down [F,d]) in storage format. For fp8 each
-    entry is a (codes, scales) pair."""
+    """Expert e's (W_gate [d,F], W_up [d,F], W_down [F,d]) in storage format. For fp8 and
+    mxfp4 each entry is a (codes, scales) pair."""
     return _ffn_weights(cfg, cfg.F, ID_EXPERT0 + 3 * e)
 
 

@@ -9,10 +9,18 @@ S.1111.111 is NaN; there are no infinities; the largest finite magnitude is
 1.75 * 2^8 = 448. Encoding here is round-to-nearest-even with saturation to
 +-448, the conversion the fp8 workload uses for activations.
 
+OCP MXFP4 (the OCP Microscaling Formats specification, as used for 4-bit MoE
+expert weights): elements are FP4 E2M1, 1 sign bit, 2 exponent bits with bias 1
+and 1 mantissa bit, exponent field 0 being subnormal (m/2), so the magnitudes are
+0, 0.5, 1, 1.5, 2, 3, 4 and 6; every 32 consecutive elements along the reduction
+axis share one E8M0 scale, the power of two 2^(e-127) (e = 255 is NaN).
+
 The pages list FP8 among the weight formats an MoE offload engine must carry
 ("guqiong96/Lvllm", section "Highlights") and require the quantisation scales
 to travel with the weights as one unit ("Running 35B MoE Models on 8GB GPUs",
-section "Technical Insight"); the exact format is the reading above.
+section "Technical Insight"); the exact format is the reading above. They also
+name 4-bit weights (MXFP4 and NVFP4, "guqiong96/Lvllm", section "Highlights"), of
+which MXFP4 is the one taken here.
 """
 from __future__ import annotations
 
@@ -114,3 +122,50 @@ def dequantize_weight_blocks(codes: np.ndarray, scales: np.ndarray, block: int =
     n_in, n_out = v.shape
     s = scales.astype(np.float64)
     return (v.reshape(n_in // block, block, n_out // block, block) * s[:, None, :, None]).reshape(n_in, n_out)
+
+
+# ------------------------------------------------------------------ MXFP4 --
+MX_BLOCK = 32
+
+
+def _e2m1_magnitude(code: int) -> float:
+    """Value of the 3-bit magnitude field (sign stripped) per the E2M1 definition."""
+    e = (code >> 1) & 3
+    m = code & 1
+    if e == 0:
+        return 0.5 * m                       # subnormal: m/2 * 2^(1 - bias)
+    return (1.0 + 0.5 * m) * 2.0 ** (e - 1)  # normal: (1 + m/2) * 2^(e - bias)
+
+
+def e2m1_table() -> np.ndarray:
+    """float64 value of each of the 16 FP4 E2M1 codes (code 8 is -0.0)."""
+    return np.array([(-1.0 if c & 8 else 1.0) * _e2m1_magnitude(c & 7) for c in range(16)], dtype=np.float64)
+
+
+_E2M1_TABLE = e2m1_table()
+
+
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """FP4 codes (one per uint8, values 0..15) -> float64."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if (c > 15).any():
+        raise ValueError("decode_e2m1: codes are 4-bit")
+    return _E2M1_TABLE[c]
+
+
+def decode_e8m0(e: np.ndarray) -> np.ndarray:
+    """E8M0 scale bytes -> float64 2^(e - 127); 255 is NaN."""
+    e = np.asarray(e, dtype=np.uint8).astype(np.int64)
+    v = np.ldexp(1.0, e - 127)
+    return np.where(e == 255, np.nan, v)
+
+
+def dequantize_mxfp4_weight(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Weights stored as FP4 codes [in, out] (one code per byte) with one E8M0 scale per
+    32 consecutive inputs of an output column, scales [in/32, out] -> float64 [in, out]."""
+    v = decode_e2m1(codes)
+    n_in, n_out = v.shape
+    if n_in % MX_BLOCK:
+        raise ValueError("dequantize_mxfp4_weight: the input dimension must be a multiple of 32")
+    s = decode_e8m0(scales)
+    return (v.reshape(n_in // MX_BLOCK, MX_BLOCK, n_out) * s[:, None, :]).reshape(n_in, n_out)

@@ -37,6 +37,8 @@ def oracle_expert(cfg, w):
     """synth storage tuple -> oracle.moe.ExpertWeights (float64)."""
     if cfg.dtype == "fp8":
         return moe.ExpertWeights(*[formats.dequantize_weight_blocks(q, s) for q, s in w])
+    if cfg.dtype == "mxfp4":
+        return moe.ExpertWeights(*[formats.dequantize_mxfp4_weight(q, s) for q, s in w])
     return moe.ExpertWeights(*[decode(m, cfg.dtype) for m in w])
 
 

@@ -131,3 +131,75 @@ def test_dequantize_weight_blocks():
     assert w[0, 0] == t[codes[0, 0]] * np.float64(scales[0, 0])
     assert w[200, 300] == t[codes[200, 300]] * np.float64(scales[1, 2])
     assert w[127, 129] == t[codes[127, 129]] * np.float64(scales[0, 1])
+
+
+# ------------------------------------------------------------------ MXFP4 --
+
+def _golden_e2m1():
+    path = os.path.join(os.path.dirname(__file__), "golden", "e2m1_points.txt")
+    pts = []
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            code, val = line.split()
+            pts.append((int(code, 2), float(val)))
+    return pts
+
+
+def test_e2m1_table_matches_the_specification():
+    """All 16 FP4 E2M1 encodings against the OCP MX specification's table (golden file)."""
+    pts = _golden_e2m1()
+    assert [c for c, _ in pts] == list(range(16))
+    got = formats.decode_e2m1(np.arange(16, dtype=np.uint8))
+    for c, v in pts:
+        assert got[c] == v and np.signbit(got[c]) == np.signbit(v), (c, got[c], v)
+    with pytest.raises(ValueError):
+        formats.decode_e2m1(np.array([16], dtype=np.uint8))
+
+
+def test_e8m0_points():
+    e = np.array([0, 1, 126, 127, 128, 254, 255], dtype=np.uint8)
+    v = formats.decode_e8m0(e)
+    assert v[0] == 2.0 ** -127 and v[1] == 2.0 ** -126 and v[2] == 0.5 and v[3] == 1.0 and v[4] == 2.0
+    assert v[5] == 2.0 ** 127 and np.isnan(v[6])
+
+
+def test_dequantize_mxfp4_brute_force():
+    """Every element is its code's value times the E8M0 scale of its own 32-input block and
+    output column (explicit loops against the vectorised form, with distinct scales)."""
+    rng = np.random.default_rng(7)
+    n_in, n_out = 96, 5
+    codes = rng.integers(0, 16, (n_in, n_out), dtype=np.uint8)
+    scales = rng.integers(100, 150, (n_in // 32, n_out), dtype=np.uint8)
+    got = formats.dequantize_mxfp4_weight(codes, scales)
+    table = {c: v for c, v in _golden_e2m1()}
+    for i in range(n_in):
+        for o in range(n_out):
+            assert got[i, o] == table[int(codes[i, o])] * 2.0 ** (int(scales[i // 32, o]) - 127)
+
+
+def test_mxfp4_storage_decodes_within_the_rounding_bound():
+    """The workload's MXFP4 weights (seeded draws quantised with the OCP MX conversion) decode,
+    through the oracle, to within half a grid step of the fp32 draws where |w| / 2^X <= 6 (the
+    E2M1 spacing is 0.5, 1 and 2 times 2^X on [0, 2], [2, 4] and [4, 6]), and to 6 * 2^X above (the
+    conversion saturates: a block's largest element can reach 8 * 2^X); the block's largest
+    element maps to a magnitude in [4, 6] * 2^X."""
+    from expert_offloaded_ffn_amd import synth
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((128, 64)) * 0.05).astype(np.float32)
+    codes, scales = synth.quantize_mxfp4(w)
+    q = formats.dequantize_mxfp4_weight(codes, scales)
+    X = scales.astype(np.int64) - 127
+    step = np.ldexp(1.0, np.repeat(X, 32, axis=0))           # 2^X per element
+    err, a = np.abs(q - w), np.abs(w)
+    inside = a <= 6 * step
+    for lo, hi, half in ((0, 2, 0.25), (2, 4, 0.5), (4, 6, 1.0)):
+        m = (a >= lo * step) & (a <= hi * step)
+        assert m.any() and (err[m] <= half * step[m] + 1e-12).all(), (lo, hi)
+    sat = ~inside
+    assert (np.abs(q[sat]) == 6 * step[sat]).all() and (np.sign(q[sat]) == np.sign(w[sat])).all()
+    amax_q = np.abs(q).reshape(4, 32, 64).max(axis=1)
+    assert ((amax_q >= 4 * np.ldexp(1.0, X)) & (amax_q <= 6 * np.ldexp(1.0, X))).all()
+    # all-zero block: scale 2^-127, codes 0
+    c0, s0 = synth.quantize_mxfp4(np.zeros((32, 2), np.float32))
+    assert (c0 == 0).all() and (s0 == 0).all()
