@@ -16,7 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoeffn.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP", -4: "MOE_ECAPACITY",
           -5: "MOE_ENOMEM", -6: "MOE_ESTATE"}
@@ -260,8 +260,9 @@ def bundle_bytes(d, F, w_dtype) -> int:
 
 
 def pack_expert(d, F, w_dtype, wg, wu, wd, sg=None, su=None, sd=None, out=None):
-    """Packs one expert (numpy arrays in storage format: f32, bf16 bits as uint16, e4m3 codes as uint8)
-    into a host bundle (a uint8 tensor, pinned if `out` is pinned)."""
+    """Packs one expert (numpy arrays in storage format: f32, bf16 bits as uint16, e4m3 codes as uint8,
+    FP4 codes as one uint8 each; fp8 block scales or MXFP4 power-of-two scales as fp32 grids) into a
+    host bundle (a uint8 tensor, pinned if `out` is pinned)."""
     import numpy as np
 
     nb = bundle_bytes(d, F, w_dtype)

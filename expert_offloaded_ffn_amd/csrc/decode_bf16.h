@@ -62,7 +62,21 @@ struct DecodeArgs {
   int32_t* clear2;   // GATEUP: the combine's per-group arrival counts of that launch, cleared here
   int clear2_n;
   int rchunks;       // workgroups per (expert, group), each taking 16 rows (1: one takes all rows)
+  int64_t s_off;     // MXFP4: byte offset of the matrix's E8M0 scales inside a bundle
 };
+
+// Eight FP4 E2M1 codes (two per byte, element 2j in the low nibble of byte j) times the
+// E8M0 scale 2^(e-127) as bf16, exactly (an E2M1 value times a power of two is a bf16 value),
+// with the gfx950 scaled conversion (two codes per instruction).
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t codes, uint32_t e) {
+  const float scale = e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);   // 2^(e-127)
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  return bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
 
 // The combine folded into a decode down launch: once every (expert, 32-column group) unit of
 // both problems has stored its outputs for group g, the last workgroup to finish one adds,
@@ -199,8 +213,10 @@ constexpr int kDecMaxSplits = 8;              // workgroups per (expert, group) 
 // accumulators and of the reduction LDS of 4, so more workgroups and more loads in flight fit
 // on a CU; an expert with more rows takes several passes, a one-expert problem several
 // workgroups, see rchunks), 4 for larger ones.
-// COMB (DOWN only) folds the combine into the launch (DecodeCombine).
-template <int MODE, bool SPLIT, int MB, bool COMB = false>
+// COMB (DOWN only) folds the combine into the launch (DecodeCombine). WF is the weight
+// format: 0 bf16 tiles, 1 MXFP4 chunks (codes and scales of 4 k-steps per load, decoded to
+// bf16 in registers; the waves split K in whole chunks).
+template <int MODE, bool SPLIT, int MB, bool COMB = false, int WF = 0>
 __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
     DecodeArgs p0, DecodeArgs p1, int nb0, DecodeCombine cb) {
   static_assert(!COMB || MODE == MODE_DOWN, "the combine follows the down projection");
@@ -244,10 +260,24 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int KT = p.K / 32;
   const int ks0 = (KT * s) / S, ks = (KT * (s + 1)) / S - ks0;   // this split's k-steps
-  const int kt0 = ks0 + (ks * w) / kDecWaves, kt1 = ks0 + (ks * (w + 1)) / kDecWaves;
-  const char* B = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride + p.b_off;
+  int kt0 = ks0 + (ks * w) / kDecWaves, kt1 = ks0 + (ks * (w + 1)) / kDecWaves;
+  const char* bundle = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride;
+  const char* B = bundle + p.b_off;
   const char* b0 = B + ((int64_t)(2 * g) * KT) * 1024 + 16 * lane;      // n-tile 2g
   const char* b1 = B + ((int64_t)(2 * g + 1) * KT) * 1024 + 16 * lane;  // n-tile 2g+1
+  const char* sc0 = nullptr;
+  const char* sc1 = nullptr;
+  if constexpr (WF == 1) {
+    // MXFP4 (no K split): chunks of 4 k-steps, 1 KiB of codes and 64 bytes of scales each
+    const int KC = KT / 4;
+    kt0 = 4 * ((KC * w) / kDecWaves);
+    kt1 = 4 * ((KC * (w + 1)) / kDecWaves);
+    b0 = B + ((int64_t)(2 * g) * KC) * 1024 + 16 * lane;
+    b1 = B + ((int64_t)(2 * g + 1) * KC) * 1024 + 16 * lane;
+    const char* Sg = bundle + p.s_off;
+    sc0 = Sg + ((int64_t)(2 * g) * KC) * 64 + 4 * (lane & 15);
+    sc1 = Sg + ((int64_t)(2 * g + 1) * KC) * 64 + 4 * (lane & 15);
+  }
 
   const int mc_end = R > 1 ? min(n_e, 16 * c + 16) : n_e;
   for (int mc = 16 * c; mc < mc_end; mc += 16 * MB) {
@@ -267,14 +297,28 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
       const int nk = min(kDecChunk, kt1 - k0);
       // the chunk's tiles as constant offsets from one pointer per n-tile, so the loads issue
       // back to back with immediate offsets
-      const char* q0 = b0 + (int64_t)k0 * 1024;
-      const char* q1 = b1 + (int64_t)k0 * 1024;
       bf16x8_t fb[kDecChunk][2];
+      if constexpr (WF == 1) {
+        static_assert(kDecChunk == 4, "an MXFP4 chunk is 4 k-steps");
+        const uint4 w0 = *reinterpret_cast<const uint4*>(b0 + (int64_t)(k0 / 4) * 1024);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(b1 + (int64_t)(k0 / 4) * 1024);
+        const uint32_t e0 = *reinterpret_cast<const uint32_t*>(sc0 + (int64_t)(k0 / 4) * 64);
+        const uint32_t e1 = *reinterpret_cast<const uint32_t*>(sc1 + (int64_t)(k0 / 4) * 64);
+        const uint32_t c0w[4] = {w0.x, w0.y, w0.z, w0.w}, c1w[4] = {w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
-      for (int c = 0; c < kDecChunk; ++c) {
-        if (c < nk) {
-          fb[c][0] = *reinterpret_cast<const bf16x8_t*>(q0 + c * 1024);
-          fb[c][1] = *reinterpret_cast<const bf16x8_t*>(q1 + c * 1024);
+        for (int c = 0; c < 4; ++c) {
+          fb[c][0] = fp4x8_to_bf16(c0w[c], (e0 >> (8 * c)) & 255u);
+          fb[c][1] = fp4x8_to_bf16(c1w[c], (e1 >> (8 * c)) & 255u);
+        }
+      } else {
+        const char* q0 = b0 + (int64_t)k0 * 1024;
+        const char* q1 = b1 + (int64_t)k0 * 1024;
+#pragma unroll
+        for (int c = 0; c < kDecChunk; ++c) {
+          if (c < nk) {
+            fb[c][0] = *reinterpret_cast<const bf16x8_t*>(q0 + c * 1024);
+            fb[c][1] = *reinterpret_cast<const bf16x8_t*>(q1 + c * 1024);
+          }
         }
       }
 #pragma unroll

@@ -25,6 +25,13 @@ __host__ __device__ inline BundleGeom bundle_geom(int d, int F, int dt) {
     g.gu_off = 0;
     g.dn_off = al((int64_t)2 * F * d * 2);
     g.bytes = g.dn_off + al((int64_t)d * F * 2);
+  } else if (dt == MOE_MXFP4) {
+    // codes (two per byte) then E8M0 scales (one per 32 inputs of a row), per matrix
+    g.gu_off = 0;
+    g.sg_off = al((int64_t)2 * F * d / 2);
+    g.dn_off = g.sg_off + al((int64_t)2 * F * (d / 32));
+    g.sd_off = g.dn_off + al((int64_t)d * F / 2);
+    g.bytes = g.sd_off + al((int64_t)d * (F / 32));
   } else if (dt == MOE_FP8_E4M3) {
     g.gu_off = 0;
     g.dn_off = al((int64_t)2 * F * d);

@@ -131,9 +131,9 @@ using namespace moeffn;
 extern "C" size_t moe_bundle_bytes(int32_t d_model, int32_t d_ff, int32_t w_dtype) {
   if (d_model < 1 || d_ff < 1) return 0;
   if (w_dtype == MOE_BF16 && (d_model % 32 || d_ff % 32)) return 0;
-  if (w_dtype == MOE_FP8_E4M3 && (d_model % 128 || d_ff % 128)) return 0;
+  if ((w_dtype == MOE_FP8_E4M3 || w_dtype == MOE_MXFP4) && (d_model % 128 || d_ff % 128)) return 0;
   if (w_dtype == MOE_F32 && d_model % 4) return 0;
-  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3) return 0;
+  if (w_dtype != MOE_F32 && w_dtype != MOE_BF16 && w_dtype != MOE_FP8_E4M3 && w_dtype != MOE_MXFP4) return 0;
   return (size_t)bundle_geom(d_model, d_ff, w_dtype).bytes;
 }
 
@@ -186,6 +186,12 @@ moe_status check_call(const FfnCall& c, const char* who) {
   const int d = t.d_model, F = t.d_ff;
   if (t.w_dtype == MOE_F32) {
     MOE_REQUIRE(act_dtype == MOE_F32, MOE_EUNSUPPORTED, "%s: fp32 weights need fp32 activations", who);
+  } else if (t.w_dtype == MOE_MXFP4) {
+    MOE_REQUIRE(act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "%s: mxfp4 weights need bf16 activations", who);
+    const int max_rows_e = c.a_row_src ? (rows + c.a_row_div - 1) / c.a_row_div : rows;
+    MOE_REQUIRE(max_rows_e <= 64, MOE_EUNSUPPORTED,
+                "%s: mxfp4 weights run on the decode kernels (at most 64 rows per expert, here up to %d)", who,
+                max_rows_e);
   } else if (t.w_dtype == MOE_BF16) {
     MOE_REQUIRE(act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "%s: bf16 weights need bf16 activations", who);
     MOE_REQUIRE((2 * F) % kBN == 0 && d % kBN == 0, MOE_EUNSUPPORTED,
@@ -202,11 +208,11 @@ moe_status check_call(const FfnCall& c, const char* who) {
   return MOE_OK;
 }
 
-// bf16 problems whose experts get at most 64 rows each take the weight-streaming decode
-// kernels. Rows per expert are bounded by the number of distinct source rows: at most
+// bf16 and MXFP4 problems whose experts get at most 64 rows each take the weight-streaming
+// decode kernels (MXFP4 only those). Rows per expert are bounded by the number of distinct source rows: at most
 // rows / a_row_div tokens (each picks an expert once) or all rows.
 bool decode_path(const FfnCall& c) {
-  if (c.t.w_dtype != MOE_BF16 || c.rows == 0) return false;
+  if ((c.t.w_dtype != MOE_BF16 && c.t.w_dtype != MOE_MXFP4) || c.rows == 0) return false;
   const int max_rows_e = c.a_row_src ? (c.rows + c.a_row_div - 1) / c.a_row_div : c.rows;
   return max_rows_e <= 64;
 }
@@ -231,6 +237,7 @@ void decode_args(const FfnCall& c, int S, int R, DecodeArgs* gu, DecodeArgs* dn,
   q.pool = static_cast<const char*>(c.t.pool);
   q.slot_stride = c.t.slot_stride;
   q.b_off = g.gu_off;
+  q.s_off = g.sg_off;   // MXFP4 scales of W_gu (unused for bf16)
   q.N = 2 * F;
   q.K = d;
   q.out = H;
@@ -248,6 +255,7 @@ void decode_args(const FfnCall& c, int S, int R, DecodeArgs* gu, DecodeArgs* dn,
   q.a_row_src = nullptr;
   q.a_row_div = 1;
   q.b_off = g.dn_off;
+  q.s_off = g.sd_off;
   q.N = d;
   q.K = F;
   q.out = c.y;
@@ -299,32 +307,38 @@ moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s, const Decod
     dn[1] = dn[0];
   }
   const dim3 block(64 * kDecWaves);
-  auto go = [&](auto sp, auto mb) {
+  auto go = [&](auto sp, auto mb, auto wf) {
     constexpr bool SP = decltype(sp)::value;
     constexpr int MB = decltype(mb)::value;
+    constexpr int WF = decltype(wf)::value;
     prof_mark(s, MOE_PROF_DEC_GATEUP, false);
-    hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, SP, MB>), dim3(ngu[0] + ngu[1]), block, 0, s, gu[0], gu[1],
-                       ngu[0], no_cb);
+    hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, SP, MB, false, WF>), dim3(ngu[0] + ngu[1]), block, 0, s,
+                       gu[0], gu[1], ngu[0], no_cb);
     prof_mark(s, MOE_PROF_DEC_GATEUP, true);
     prof_mark(s, MOE_PROF_DEC_DOWN, false);
     if (cb != nullptr)
-      hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB, true>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0],
+      hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB, true, WF>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0],
                          dn[1], ndn[0], *cb);
     else
-      hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB>), dim3(ndn[0] + ndn[1]), block, 0, s, dn[0], dn[1],
-                         ndn[0], no_cb);
+      hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, MB, false, WF>), dim3(ndn[0] + ndn[1]), block, 0, s,
+                         dn[0], dn[1], ndn[0], no_cb);
     prof_mark(s, MOE_PROF_DEC_DOWN, true);
   };
   using T1 = std::true_type;
   using F0 = std::false_type;
   using M1 = std::integral_constant<int, 1>;
   using M4 = std::integral_constant<int, 4>;
-  if (split) {   // at most 4 rows
-    go(T1{}, M1{});
+  using BF = std::integral_constant<int, 0>;
+  using FP4 = std::integral_constant<int, 1>;
+  if (calls[0].t.w_dtype == MOE_MXFP4) {   // (the callers launch only same-format problems together)
+    if (mb1) go(F0{}, M1{}, FP4{});
+    else go(F0{}, M4{}, FP4{});
+  } else if (split) {   // at most 4 rows
+    go(T1{}, M1{}, BF{});
   } else if (mb1) {
-    go(F0{}, M1{});
+    go(F0{}, M1{}, BF{});
   } else {
-    go(F0{}, M4{});
+    go(F0{}, M4{}, BF{});
   }
   return check_launch("moe_grouped_ffn bf16 decode");
 }
@@ -356,6 +370,7 @@ moe_status run_call(const FfnCall& c, hipStream_t s) {
                        d, F, E);
     return check_launch("moe_grouped_ffn f32");
   }
+  if (t.w_dtype == MOE_MXFP4) return launch_decode(&c, 1, s);   // (check_call admits decode problems only)
   if (t.w_dtype == MOE_BF16) {
     int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
     bf16_t* H = reinterpret_cast<bf16_t*>(wsb + h_off);
@@ -511,7 +526,8 @@ extern "C" moe_status moe_grouped_ffn_batch(const moe_ffn_problem* problems, int
   for (int i = 0; i < n; ++i)
     if (moe_status st = check_call(c[i], "moe_grouped_ffn_batch")) return st;
   hipStream_t s = as_stream(stream);
-  if (n == 2 && decode_path(c[0]) && decode_path(c[1])) return launch_decode(c, 2, s);
+  if (n == 2 && decode_path(c[0]) && decode_path(c[1]) && c[0].t.w_dtype == c[1].t.w_dtype)
+    return launch_decode(c, 2, s);
   for (int i = 0; i < n; ++i)
     if (moe_status st = run_call(c[i], s)) return st;
   return MOE_OK;
@@ -594,6 +610,8 @@ extern "C" moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, con
                 "expert)", q == routed ? "routed" : "shared");
     ++n;
   }
+  MOE_REQUIRE(n == 1 || c[0].t.w_dtype == c[1].t.w_dtype, MOE_EUNSUPPORTED,
+              "moe_grouped_ffn_combine: the shared and routed experts must have the same weight format");
   DecodeCombine cb{};
   cb.T = T;
   cb.k = k;

@@ -14,7 +14,7 @@ import torch
 
 from . import binding as B
 
-W_CODE = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_FP8_E4M3}
+W_CODE = {"f32": B.MOE_F32, "bf16": B.MOE_BF16, "fp8": B.MOE_FP8_E4M3, "mxfp4": B.MOE_MXFP4}
 
 
 def _bits_to_tensor(a: np.ndarray, act: str, device) -> torch.Tensor:
@@ -35,6 +35,10 @@ def pack_bundles(cfg, expert_weights, d, F, pin=False, threads=8):
         if cfg.dtype == "fp8":
             (gq, gs), (uq, us), (dq, ds) = ws
             return B.pack_expert(d, F, w, gq, uq, dq, gs, us, ds, out=out)
+        if cfg.dtype == "mxfp4":   # E8M0 exponents -> the fp32 powers of two the packer takes
+            (gq, gs), (uq, us), (dq, ds) = ws
+            p2 = lambda e: np.ldexp(np.float32(1.0), e.astype(np.int32) - 127).astype(np.float32)
+            return B.pack_expert(d, F, w, gq, uq, dq, p2(gs), p2(us), p2(ds), out=out)
         return B.pack_expert(d, F, w, ws[0], ws[1], ws[2], out=out)
 
     with ThreadPoolExecutor(max(1, threads)) as ex:

@@ -61,8 +61,12 @@ enum {
 };
 
 /* Element types. MOE_FP8_E4M3 is the OCP 8-bit E4M3 ("fn": bias 7, max 448,
- * no infinities), always paired with fp32 scales as described per call. */
-enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 };
+ * no infinities), always paired with fp32 scales as described per call.
+ * MOE_MXFP4 (expert weights only) is OCP MXFP4: FP4 E2M1 codes (bias 1, values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) with one E8M0 scale 2^(e-127)
+ * per 32 consecutive inputs of an output column ([LVLLM] "Highlights" names
+ * MXFP4 among the expert formats to carry). */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 };
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
 
 /* Human-readable message for the last failing call on this thread ("" if none). */
@@ -194,16 +198,24 @@ moe_status moe_route_permute(const moe_route_cfg* cfg, const void* x, const void
  *   16h + b (each half is one contiguous 1 KiB wave load of 16 bytes per lane);
  *   then three fp32 scale grids: gate [F/128][d/128], up [F/128][d/128],
  *   down [d/128][F/128] (one scale per 128x128 block of the original matrix).
+ *  MOE_MXFP4: same row orders; each matrix [N, K] as codes then scales. Codes:
+ *   chunks of 16 rows x 128 columns at ((nb * K/128) + kc) * 1024 bytes; byte
+ *   16*l + 4*c + j (lane l = 0..63, k-step c = 0..3, j = 0..3) holds row
+ *   16nb + l%16, columns 128kc + 32c + 8*(l/16) + 2j (low nibble) and + 1 (high
+ *   nibble). Scales (256 B after the codes): 64 bytes per chunk at
+ *   ((nb * K/128) + kc) * 64, byte 4r + c the E8M0 exponent of row 16nb + r,
+ *   columns 128kc + 32c .. + 31. Order: W_gu codes, W_gu scales, W_dn codes,
+ *   W_dn scales.
  *  MOE_F32: W_gate^T [F, d], W_up^T [F, d], W_down^T [d, F], plain row-major.
  * Requirements: d % 32 == 0 and F % 32 == 0 (bf16); d % 128 == 0 and
- *  F % 128 == 0 (fp8); d % 4 == 0 (f32).
+ *  F % 128 == 0 (fp8, mxfp4); d % 4 == 0 (f32).
  */
 typedef struct {
   const void* pool;               /* device base address of slot 0 */
   int64_t slot_stride;            /* bytes between slots, >= bundle bytes, % 256 == 0 */
   const int32_t* slot_of_expert;  /* device [n_experts]: slot or -1 (skip) */
   int32_t n_experts, d_model, d_ff;
-  int32_t w_dtype;                /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 */
+  int32_t w_dtype;                /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 | MOE_MXFP4 */
 } moe_expert_table;
 
 /* Bytes of one expert bundle for this layout (0 on invalid sizes). */
@@ -212,7 +224,10 @@ size_t moe_bundle_bytes(int32_t d_model, int32_t d_ff, int32_t w_dtype);
 /* Host-side packer: writes one bundle from the expert's matrices in their
  * natural layouts, W_gate and W_up [d, F], W_down [F, d] (element type w_dtype;
  * fp8 codes as uint8), plus for fp8 the block scales gate/up [d/128][F/128] and
- * down [F/128][d/128] (fp32). bundle_host must hold moe_bundle_bytes(...) bytes.
+ * down [F/128][d/128] (fp32). For MXFP4 the matrices hold one FP4 code (0..15)
+ * per uint8 and the scales are gate/up [d/32][F] and down [F/32][d], fp32 powers
+ * of two 2^(e-127), e in 0..254 (MOE_EINVAL for any other value or a code above
+ * 15). bundle_host must hold moe_bundle_bytes(...) bytes.
  * Pure host code; no device is touched. */
 moe_status moe_pack_expert(int32_t d_model, int32_t d_ff, int32_t w_dtype,
                            const void* w_gate_host, const void* w_up_host,
@@ -232,8 +247,11 @@ moe_status moe_pack_expert(int32_t d_model, int32_t d_ff, int32_t w_dtype,
  *         bf16 for bf16 weights, re-quantised per row per 128 to e4m3 for fp8)
  *   y_r = H_r W_down_e                          (fp32 accumulation, y_dtype)
  * Rows of skipped experts are left untouched in y.
- *  a        [*, d] act_dtype: MOE_F32 (f32 weights), MOE_BF16 (bf16 weights) or
- *           MOE_FP8_E4M3 codes (fp8 weights) with a_scale [*, d/128] fp32
+ *  a        [*, d] act_dtype: MOE_F32 (f32 weights), MOE_BF16 (bf16 or MXFP4
+ *           weights) or MOE_FP8_E4M3 codes (fp8 weights) with a_scale [*, d/128]
+ *           fp32. MXFP4 weights are decoded exactly to bf16 (E2M1 times a power of
+ *           two) for bf16 MFMAs; they run at most 64 rows per expert (decode
+ *           batches; more is MOE_EUNSUPPORTED).
  *  offsets  device [n_experts + 1] int32 (from moe_permute, or [0, rows] for a
  *           single dense expert such as a shared expert)
  *  y        [rows, d] y_dtype (MOE_F32 or MOE_BF16)

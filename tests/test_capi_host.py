@@ -207,6 +207,52 @@ def test_pack_bf16_layout():
         assert tiled(dn, n, f, F) == wd[f, n]
 
 
+def test_pack_mxfp4_layout_and_scales():
+    """MXFP4 bundle: two codes per byte in 16 x 128 chunks and E8M0 exponents per 32-input
+    block, as the header lays them out; bad codes and non-power-of-two scales are refused."""
+    d, F = 256, 128
+    rng = np.random.default_rng(2)
+    wg, wu = rng.integers(0, 16, (d, F), dtype=np.uint8), rng.integers(0, 16, (d, F), dtype=np.uint8)
+    wd = rng.integers(0, 16, (F, d), dtype=np.uint8)
+    eg, eu = rng.integers(100, 150, (d // 32, F)), rng.integers(100, 150, (d // 32, F))
+    ed = rng.integers(100, 150, (F // 32, d))
+    p2 = lambda e: np.ldexp(np.float32(1.0), e - 127).astype(np.float32)
+    b = B.pack_expert(d, F, B.MOE_MXFP4, wg, wu, wd, p2(eg), p2(eu), p2(ed)).numpy()
+    al = lambda v: (v + 255) // 256 * 256
+    gu_s = al(2 * F * d // 2)
+    dn_c = gu_s + al(2 * F * d // 32)
+    dn_s = dn_c + al(d * F // 2)
+    assert b.size == dn_s + al(d * F // 32) == B.bundle_bytes(d, F, B.MOE_MXFP4)
+
+    def code_at(base, n, k, K):
+        kc, c, q, j = k // 128, (k % 128) // 32, (k % 32) // 8, (k % 8) // 2
+        lane = n % 16 + 16 * q
+        byte = b[base + ((n // 16) * (K // 128) + kc) * 1024 + 16 * lane + 4 * c + j]
+        return (byte >> 4) if k % 2 else (byte & 15)
+
+    def exp_at(base, n, k, K):
+        kc, c = k // 128, (k % 128) // 32
+        return b[base + ((n // 16) * (K // 128) + kc) * 64 + 4 * (n % 16) + c]
+
+    for _ in range(300):
+        R, kk = rng.integers(0, 2 * F), rng.integers(0, d)
+        j, rr = R // 32, R % 32
+        up, col = rr >= 16, 16 * j + rr % 16
+        assert code_at(0, R, kk, d) == (wu if up else wg)[kk, col]
+        assert exp_at(gu_s, R, kk, d) == (eu if up else eg)[kk // 32, col]
+        n, f = rng.integers(0, d), rng.integers(0, F)
+        assert code_at(dn_c, n, f, F) == wd[f, n]
+        assert exp_at(dn_s, n, f, F) == ed[f // 32, n]
+    bad = wg.copy()
+    bad[3, 4] = 16
+    with pytest.raises(B.MoeError):
+        B.pack_expert(d, F, B.MOE_MXFP4, bad, wu, wd, p2(eg), p2(eu), p2(ed))
+    s_bad = p2(eg)
+    s_bad[0, 0] = 0.75
+    with pytest.raises(B.MoeError):
+        B.pack_expert(d, F, B.MOE_MXFP4, wg, wu, wd, s_bad, p2(eu), p2(ed))
+
+
 def test_pack_fp8_layout_and_scales():
     d, F = 256, 128
     rng = np.random.default_rng(1)

@@ -1,0 +1,84 @@
+"""MXFP4 expert weights (FP4 E2M1 codes with an E8M0 scale per 32 inputs) through the decode
+kernels, against the float64 oracle on the decoded weights: resident layers at reduced and at
+full offload-workload size, and the expert slot pool."""
+import numpy as np
+import pytest
+import torch
+
+from expert_offloaded_ffn_amd import binding as B
+from expert_offloaded_ffn_amd import synth
+from expert_offloaded_ffn_amd.layer import MoELayer
+from oracle import moe
+from parity_util import (assert_close, check_exact_indices, decode, oracle_expert, oracle_route, route_agreement,
+                         say, to_np)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _x(cfg, xs):
+    return torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _check(cfg, layer, router, experts, T, xi, logit_bias=None, tokens=None):
+    xs = synth.gen_x(cfg, xi, T=T)
+    lb = None if logit_bias is None else torch.from_numpy(logit_bias).to(DEV)
+    say(f"  case {cfg.name} T={T} x={xi}: launching")
+    g = layer.forward(_x(cfg, xs), logit_bias=lb)
+    torch.cuda.synchronize()
+    say("    done")
+    check_exact_indices(cfg, g["route"], g["perm"], T)
+    r_ref = oracle_route(cfg, xs, router, logit_bias=logit_bias)
+    same = route_agreement(cfg, r_ref, g["route"], key_tol=1e-4)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    toks = toks[same[toks]]
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = oracle_expert(cfg, experts[e])
+        return cache[e]
+
+    ref = moe.moe_layer(decode(xs, "bf16"), r_ref, expert, cfg.E, tokens=toks)
+    assert_close(to_np(g["out"])[toks], ref, "bf16", f"{cfg.name} T={T}")
+    return g
+
+
+@pytest.mark.parametrize("T,d,E,k,F", [(1, 256, 16, 4, 256), (5, 256, 16, 4, 384), (32, 512, 32, 8, 256),
+                                       (64, 256, 8, 2, 128)])
+def test_mxfp4_decode_layer_reduced(T, d, E, k, F):
+    cfg = synth.get_config("offload_decode_mxfp4", T=T, d=d, E=E, k=k, F=F, name=f"mxfp4_T{T}_d{d}_E{E}_k{k}_F{F}")
+    router, experts = synth.gen_router(cfg), synth.gen_experts(cfg)
+    layer = MoELayer(cfg, router=router, experts=experts, device=DEV)
+    for xi in range(2):
+        _check(cfg, layer, router, experts, T, xi)
+
+
+def test_mxfp4_offload_workload_resident():
+    """The full offload workload shape (E=128, d=4096, F=1536, top-8, T=32) with every expert
+    resident, under the Zipf prior of step 0."""
+    cfg = synth.get_config("offload_decode_mxfp4")
+    router, experts = synth.gen_router(cfg), synth.gen_experts(cfg, threads=16)
+    layer = MoELayer(cfg, router=router, experts=experts, device=DEV, threads=16)
+    _check(cfg, layer, router, experts, cfg.T, 0, logit_bias=synth.zipf_logit_bias(cfg, 0), tokens=[0, 7, 31])
+
+
+def test_mxfp4_slot_pool_matches_resident():
+    """MXFP4 bundles through the expert slot pool (8 slots for 32 experts): every step equals the
+    resident layer bit for bit, and the hit/miss counts follow the pool."""
+    cfg = synth.get_config("offload_decode_mxfp4", d=512, F=256, E=32, k=4, T=16, n_slots=8)
+    router, experts = synth.gen_router(cfg), synth.gen_experts(cfg)
+    res = MoELayer(cfg, router=router, experts=experts, device=DEV)
+    pool = MoELayer(cfg, router=router, experts=experts, device=DEV, pool_slots=cfg.n_slots)
+    for step in range(6):
+        x = _x(cfg, synth.gen_x(cfg, step))
+        lb = torch.from_numpy(synth.zipf_logit_bias(cfg, step)).to(DEV)
+        say(f"  case mxfp4 slot pool step {step}: launching")
+        a = res.forward(x, logit_bias=lb)["out"]
+        b = pool.forward(x, logit_bias=lb)["out"]
+        torch.cuda.synchronize()
+        say("    done")
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"step {step}"
+    st = pool.cache.stats()
+    assert st["misses"] > 0 and st["h2d_bytes"] == st["misses"] * B.bundle_bytes(cfg.d, cfg.F, B.MOE_MXFP4)
+    pool.cache.close()
