@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; HBM TB/s (decode) & MFMA TFLOP/s (prefill) vs peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = ["mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16"]
+WORKLOADS = ["mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16",
+             "offload_decode_mxfp4"]
 
 
 def recorded_traffic(workload, kernel):
@@ -114,7 +115,8 @@ def bench_offload(args, torch, B, synth, MoELayer):
     """Expert-offload decode: T tokens per step through an n_slots HBM slot pool fed from pinned host
     bundles, Zipf-biased routing re-drawn every zipf_epoch steps. The same steps run three ways: all
     experts resident (compute time), slot pool with overlapped copies, slot pool in blocking mode."""
-    cfg = synth.get_config("offload_decode_bf16")
+    from expert_offloaded_ffn_amd.layer import W_CODE
+    cfg = synth.get_config(args.workload)
     if args.tokens:
         cfg = cfg.with_T(args.tokens)
     steps = args.steps
@@ -159,7 +161,8 @@ def bench_offload(args, torch, B, synth, MoELayer):
         "ms_per_step": round(o["wall_s"] / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; Zipf(1.1) log-prior re-drawn every 64 steps)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
-                   "d_ff": cfg.F, "n_slots": cfg.n_slots, "bundle_bytes": B.bundle_bytes(cfg.d, cfg.F, B.MOE_BF16)},
+                   "d_ff": cfg.F, "n_slots": cfg.n_slots, "weights": cfg.dtype,
+                   "bundle_bytes": B.bundle_bytes(cfg.d, cfg.F, W_CODE[cfg.dtype])},
         "resident_compute_s": round(t_comp, 4), "offload": out,
     }
     print(json.dumps(result), flush=True)
@@ -173,7 +176,7 @@ def bench_decode(args, torch, B, synth, MoELayer):
     dirty lines that the step's own reads must first write back). The
     roofline is HBM bytes: the distinct touched experts' bundles + the shared expert + router
     weights + activations in and out."""
-    from expert_offloaded_ffn_amd.layer import FUSE_COMBINE_MAX_T
+    from expert_offloaded_ffn_amd.layer import FUSE_COMBINE_MAX_T, W_CODE
     cfg = synth.get_config(args.workload)
     if args.tokens:
         cfg = cfg.with_T(args.tokens)
@@ -187,8 +190,8 @@ def bench_decode(args, torch, B, synth, MoELayer):
     xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(nb)]
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
     flush_words = flush.view(torch.int32)
-    bundle = B.bundle_bytes(cfg.d, cfg.F, B.MOE_BF16)
-    shared_bytes = B.bundle_bytes(cfg.d, cfg.F_shared, B.MOE_BF16) if cfg.F_shared else 0
+    bundle = B.bundle_bytes(cfg.d, cfg.F, W_CODE[cfg.dtype])
+    shared_bytes = B.bundle_bytes(cfg.d, cfg.F_shared, W_CODE[cfg.dtype]) if cfg.F_shared else 0
     act = 2 * cfg.T * cfg.d * 2 + cfg.E * cfg.d * 2 + (cfg.d * 2 if cfg.shared_gate else 0)
     touched = []
     for x in xs:
@@ -226,8 +229,9 @@ def bench_decode(args, torch, B, synth, MoELayer):
     # the decode gate/up launch streams the touched routed experts' W_gu, and the shared
     # expert's when the layer runs it inside the same launch
     merged = layer.shared_in_decode_launch(cfg.T)
-    shared_gu = 2 * cfg.F_shared * cfg.d * 2 if merged else 0
-    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * 2 + shared_gu for i in range(args.steps))
+    wbytes = 0.5 + 1 / 32 if cfg.dtype == "mxfp4" else 2.0   # bytes per weight (codes and scales)
+    shared_gu = 2 * cfg.F_shared * cfg.d * wbytes if merged else 0
+    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * wbytes + shared_gu for i in range(args.steps))
     gu_ms, gu_n = prof[B.PROF_DEC_GATEUP]
     hbm = float(step_bytes.sum() / (ms.sum() / 1e3) / 1e9)
     result = {
@@ -268,6 +272,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="decode: replay the layer as one captured HIP graph")
+    ap.add_argument("--resident", action="store_true",
+                    help="offload workloads: every expert resident in HBM (the decode bench, weights streamed "
+                         "from HBM each step) instead of the slot pool")
     ap.add_argument("--no-fuse-combine", action="store_true",
                     help="decode: run the combine as its own launch instead of inside the down launch")
     ap.add_argument("--skew-zipf", type=float, default=0.0,
@@ -306,9 +313,9 @@ def main():
                           "hbm_read_plus_write_GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}), flush=True)
         return 0
 
-    if args.workload == "offload_decode_bf16":
+    if args.workload.startswith("offload_decode") and not args.resident:
         return bench_offload(args, torch, B, synth, MoELayer)
-    if args.workload == "qwen_decode_bf16":
+    if args.workload == "qwen_decode_bf16" or args.workload.startswith("offload_decode"):
         return bench_decode(args, torch, B, synth, MoELayer)
 
     cfg = synth.get_config(args.workload)
