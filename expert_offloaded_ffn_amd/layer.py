@@ -136,8 +136,10 @@ class MoELayer:
 
     def shared_in_decode_launch(self, T: int) -> bool:
         """Whether a T-token forward runs the shared expert inside the routed experts' decode
-        launches (bf16, resident experts, at most 64 rows per expert) instead of on a side stream."""
-        return (self.shared is not None and self.cache is None and self.w_code == B.MOE_BF16 and 0 < T <= 64)
+        launches (bf16 or MXFP4, resident experts, at most 64 rows per expert) instead of on a side
+        stream."""
+        return (self.shared is not None and self.cache is None and self.w_code in (B.MOE_BF16, B.MOE_MXFP4)
+                and 0 < T <= 64)
 
     def _shared_ffn(self, T, a, a_scale, a_code, ydt, main):
         """Launches the shared expert's FFN on the side stream once `a` is ready on `main`; the

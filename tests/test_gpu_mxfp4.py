@@ -82,3 +82,45 @@ def test_mxfp4_slot_pool_matches_resident():
     st = pool.cache.stats()
     assert st["misses"] > 0 and st["h2d_bytes"] == st["misses"] * B.bundle_bytes(cfg.d, cfg.F, B.MOE_MXFP4)
     pool.cache.close()
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 40])
+def test_mxfp4_with_shared_expert(T):
+    """A Qwen1.5-MoE-shaped layer (E=60 top-4, F=1408, gated shared expert F=5632) with MXFP4
+    weights: the shared expert runs in the routed experts' decode launches (and, for 1-4 tokens,
+    the combine in the down launch); against the oracle."""
+    cfg = synth.get_config("qwen_decode_bf16", dtype="mxfp4", T=T, name=f"qwen_mxfp4_T{T}")
+    router, experts, shared = synth.gen_router(cfg), synth.gen_experts(cfg), synth.gen_shared(cfg)
+    w_sg = synth.gen_shared_gate(cfg)
+    layer = MoELayer(cfg, router=router, experts=experts, shared=shared, w_shared_gate=w_sg, device=DEV)
+    assert layer.shared_in_decode_launch(T)
+    xs = synth.gen_x(cfg, 0, T=T)
+    say(f"  case {cfg.name}: launching")
+    g = layer.forward(_x(cfg, xs))
+    torch.cuda.synchronize()
+    say("    done")
+    check_exact_indices(cfg, g["route"], g["perm"], T)
+    r_ref = oracle_route(cfg, xs, router, w_sg)
+    same = route_agreement(cfg, r_ref, g["route"], key_tol=1e-4)
+    toks = np.arange(T)[same]
+    ref = moe.moe_layer(decode(xs, "bf16"), r_ref, lambda e: oracle_expert(cfg, experts[e]), cfg.E,
+                        shared=oracle_expert(cfg, shared), tokens=toks)
+    assert_close(to_np(g["out"])[toks], ref, "bf16", cfg.name)
+
+
+def test_mxfp4_fused_combine_bit_equal():
+    """moe_grouped_ffn_combine on MXFP4 problems equals the batch call plus moe_combine."""
+    cfg = synth.get_config("offload_decode_mxfp4", d=512, F=256, E=32, k=4, T=12)
+    layer = MoELayer(cfg, router=synth.gen_router(cfg), experts=synth.gen_experts(cfg), device=DEV)
+    x = _x(cfg, synth.gen_x(cfg, 0))
+    p = B.route_permute(x, layer.w_router_t, **layer.route_args())
+    rows = cfg.T * cfg.k
+    pr = B.ffn_problem(layer.table, rows, p["offsets"], x, a_row_src=p["perm_src"], a_row_div=cfg.k)
+    y = B.grouped_ffn_batch([pr])[0]
+    ref = B.combine(y, p["perm_dst"], p["gate"])
+    pr2 = B.ffn_problem(layer.table, rows, p["offsets"], x, a_row_src=p["perm_src"], a_row_div=cfg.k)
+    say("  case mxfp4 fused combine: launching")
+    got = B.grouped_ffn_combine(pr2, None, p["perm_dst"], p["gate"])
+    torch.cuda.synchronize()
+    say("    done")
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
