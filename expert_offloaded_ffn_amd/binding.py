@@ -66,7 +66,8 @@ class CacheCfg(ctypes.Structure):
 class CacheStats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
                 ("evictions", ctypes.c_int64), ("waves", ctypes.c_int64), ("h2d_bytes", ctypes.c_int64),
-                ("d2h_bytes", ctypes.c_int64), ("copy_ms", ctypes.c_double)]
+                ("d2h_bytes", ctypes.c_int64), ("copy_ms", ctypes.c_double), ("prefetches", ctypes.c_int64),
+                ("prefetch_used", ctypes.c_int64)]
 
 
 class Profile(ctypes.Structure):
@@ -115,6 +116,8 @@ EXPORTS = {
     "expert_slot_cache_wave": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_release": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "expert_slot_cache_prefetch": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_wave_plan": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(CacheEntry),
                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_stats": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheStats)]),
@@ -414,6 +417,16 @@ class SlotCache:
 
     def release(self, w, stream=None):
         _check(lib().expert_slot_cache_release(self.h, w, stream_ptr(stream)))
+
+    def prefetch(self, experts) -> int:
+        """Copies the listed (predicted) experts ahead of their step; returns the copies issued."""
+        import numpy as np
+
+        e = np.ascontiguousarray(experts, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(lib().expert_slot_cache_prefetch(self.h, e.ctypes.data if e.size else None, int(e.size),
+                                                ctypes.byref(n)))
+        return n.value
 
     def wave_plan(self, w):
         n = ctypes.c_int32()

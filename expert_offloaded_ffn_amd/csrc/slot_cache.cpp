@@ -11,15 +11,26 @@
 // host-to-HBM copies issued only for non-resident experts ("The Billion-Token
 // Bottleneck", section "Predictive Prefetching").
 //
+// Prefetch: a background reader fetches the next layer ahead of its compute
+// ("NovaLLM", section 3, Optimization #1); predicted experts that are not
+// resident are copied asynchronously before the model reaches their layer,
+// highest expected demand first ("The Billion-Token Bottleneck", sections
+// "Predictive Prefetching" and "The Orchestration Layer").
+//
 // Two halves:
 //  planner   pure host code: per step, the touched set (from the expert
 //            histogram), the access order (resident ascending, then
 //            non-resident ascending), waves of <= n_slots, LRU with the lowest
-//            free slot first. Runs without a device (dry_run) for tests.
+//            free slot first; prefetch inserts predicted experts between steps
+//            without evicting an expert of the step last planned. Runs without
+//            a device (dry_run) for tests.
 //  executor  a side stream for host->HBM bundle copies; per-slot "last read"
 //            events recorded on the compute stream (a copy into a slot waits for
 //            the last kernel that read it); per-wave "copies done" events that
-//            the compute stream waits on before the wave's miss experts run.
+//            the compute stream waits on before the wave's miss experts run;
+//            per-slot "filled" events of prefetch copies, which the compute
+//            stream waits on before a wave's hits run when one of them is still
+//            in flight.
 #include <algorithm>
 #include <cstring>
 #include <new>
@@ -36,6 +47,8 @@ struct expert_slot_cache {
   std::vector<int32_t> slot_of, owner;
   std::vector<int64_t> last;
   int64_t clock = 0;
+  int64_t step_clock = 0;                // clock before the last planned step's first access
+  std::vector<char> prefetched;          // per expert: brought in by prefetch, not yet used by a step
   std::vector<std::vector<moe_cache_entry>> waves;
   bool planned = false;
   moe_cache_stats st{};
@@ -47,6 +60,8 @@ struct expert_slot_cache {
   std::vector<hipEvent_t> copy_begin, copy_done;  // per wave
   std::vector<char> wave_copied;         // copies issued for the wave this step
   std::vector<char> timing_pending;      // copy span events to be added to copy_ms
+  std::vector<hipEvent_t> fill_done;     // per slot: end of its last prefetch copy
+  std::vector<char> fill_pending;        // per slot: the compute stream has not waited for it
   hipEvent_t compute_mark = nullptr;     // blocking mode: all compute enqueued before a wave
   int32_t* counts_pinned = nullptr;
   int32_t* tables_pinned = nullptr;      // [max_waves][2][E]
@@ -60,7 +75,9 @@ void plan_reset(expert_slot_cache* c) {
   c->slot_of.assign(E, -1);
   c->owner.assign(S, -1);
   c->last.assign(E, 0);
+  c->prefetched.assign(E, 0);
   c->clock = 0;
+  c->step_clock = 0;
   c->waves.clear();
   c->planned = false;
   c->st = moe_cache_stats{};
@@ -72,6 +89,10 @@ moe_cache_entry access(expert_slot_cache* c, int e) {
   if (c->slot_of[e] >= 0) {
     c->last[e] = c->clock;
     c->st.hits += 1;
+    if (c->prefetched[e]) {
+      c->st.prefetch_used += 1;
+      c->prefetched[e] = 0;
+    }
     r.slot = c->slot_of[e];
     r.hit = 1;
     return r;
@@ -88,6 +109,7 @@ moe_cache_entry access(expert_slot_cache* c, int e) {
     }
     slot = c->slot_of[victim];
     c->slot_of[victim] = -1;
+    c->prefetched[victim] = 0;
     c->st.evictions += 1;
     r.evicted = victim;
   }
@@ -98,8 +120,52 @@ moe_cache_entry access(expert_slot_cache* c, int e) {
   return r;
 }
 
+// One predicted expert. Resident: its recency is refreshed (no copy; slot < 0
+// in the result). Otherwise it takes the lowest free slot, else the slot of the
+// least recently used expert last used before the last planned step began:
+// experts of that step may still be read by its kernels, and experts named by
+// a prefetch since then are the prediction itself. With no such victim nothing
+// changes and r.expert is -1.
+moe_cache_entry prefetch_one(expert_slot_cache* c, int e) {
+  moe_cache_entry r{e, -1, 0, -1};
+  if (c->slot_of[e] >= 0) {
+    c->clock += 1;
+    c->last[e] = c->clock;
+    return r;
+  }
+  int slot = -1;
+  for (int s = 0; s < c->cfg.n_slots; ++s)
+    if (c->owner[s] < 0) { slot = s; break; }
+  if (slot < 0) {
+    int victim = -1;
+    for (int s = 0; s < c->cfg.n_slots; ++s) {
+      const int v = c->owner[s];
+      if (c->last[v] > c->step_clock) continue;
+      if (victim < 0 || c->last[v] < c->last[victim]) victim = v;
+    }
+    if (victim < 0) {
+      r.expert = -1;
+      return r;
+    }
+    slot = c->slot_of[victim];
+    c->slot_of[victim] = -1;
+    c->prefetched[victim] = 0;
+    c->st.evictions += 1;
+    r.evicted = victim;
+  }
+  c->clock += 1;
+  c->owner[slot] = e;
+  c->slot_of[e] = slot;
+  c->last[e] = c->clock;
+  c->prefetched[e] = 1;
+  c->st.prefetches += 1;
+  r.slot = slot;
+  return r;
+}
+
 void plan_step(expert_slot_cache* c, const int32_t* counts) {
   const int E = c->cfg.n_experts, S = c->cfg.n_slots;
+  c->step_clock = c->clock;
   std::vector<int> order;
   for (int e = 0; e < E; ++e)
     if (counts[e] > 0 && c->slot_of[e] >= 0) order.push_back(e);
@@ -134,6 +200,7 @@ void destroy_device(expert_slot_cache* c) {
   for (auto& e : c->last_read) if (e) (void)hipEventDestroy(e);
   for (auto& e : c->copy_begin) if (e) (void)hipEventDestroy(e);
   for (auto& e : c->copy_done) if (e) (void)hipEventDestroy(e);
+  for (auto& e : c->fill_done) if (e) (void)hipEventDestroy(e);
   if (c->compute_mark) (void)hipEventDestroy(c->compute_mark);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->counts_pinned) (void)hipHostFree(c->counts_pinned);
@@ -186,6 +253,10 @@ extern "C" moe_status expert_slot_cache_create(const moe_cache_cfg* cfg, expert_
     c->last_read_valid.assign(k.n_slots, 0);
     for (auto& ev : c->last_read)
       if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+    c->fill_done.assign(k.n_slots, nullptr);
+    c->fill_pending.assign(k.n_slots, 0);
+    for (auto& ev : c->fill_done)
+      if ((e = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
     if ((e = hipEventCreateWithFlags(&c->compute_mark, hipEventDisableTiming)) != hipSuccess)
       return fail("hipEventCreate", e);
     c->copy_begin.assign(c->max_waves, nullptr);
@@ -222,6 +293,7 @@ extern "C" moe_status expert_slot_cache_reset(expert_slot_cache* c) {
     MOE_HIP(hipStreamSynchronize(c->side));
     std::fill(c->last_read_valid.begin(), c->last_read_valid.end(), 0);
     std::fill(c->timing_pending.begin(), c->timing_pending.end(), 0);
+    std::fill(c->fill_pending.begin(), c->fill_pending.end(), 0);
   }
   plan_reset(c);
   return MOE_OK;
@@ -270,6 +342,7 @@ moe_status issue_copies(expert_slot_cache* c, int w, hipStream_t compute) {
       any = true;
     }
     if (c->last_read_valid[en.slot]) MOE_HIP(hipStreamWaitEvent(c->side, c->last_read[en.slot], 0));
+    c->fill_pending[en.slot] = 0;  // the wave's copy_done covers the slot from now on
     char* dst = static_cast<char*>(c->cfg.pool) + (int64_t)en.slot * c->cfg.slot_stride;
     const hipError_t err = hipMemcpyAsync(dst, c->bundles[en.expert], (size_t)c->cfg.bundle_bytes,
                                           hipMemcpyHostToDevice, c->side);
@@ -311,6 +384,11 @@ extern "C" moe_status expert_slot_cache_wave(expert_slot_cache* c, int32_t wave,
     if (take) {
       table[en.expert] = en.slot;
       ++n;
+      if (en.hit && c->fill_pending[en.slot]) {
+        // a prefetched bundle: its copy may still be in flight
+        MOE_HIP(hipStreamWaitEvent(s, c->fill_done[en.slot], 0));
+        c->fill_pending[en.slot] = 0;
+      }
     }
   }
   MOE_HIP(hipMemcpyAsync(slot_of_expert, table, sizeof(int32_t) * E, hipMemcpyHostToDevice, s));
@@ -329,6 +407,43 @@ extern "C" moe_status expert_slot_cache_release(expert_slot_cache* c, int32_t wa
     MOE_HIP(hipEventRecord(c->last_read[en.slot], s));
     c->last_read_valid[en.slot] = 1;
   }
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_prefetch(expert_slot_cache* c, const int32_t* experts_host, int32_t n,
+                                                 int32_t* n_copies_out) {
+  clear_error();
+  MOE_REQUIRE(c && (experts_host || n == 0), MOE_EINVAL, "expert_slot_cache_prefetch: NULL argument");
+  MOE_REQUIRE(n >= 0, MOE_EINVAL, "expert_slot_cache_prefetch: n=%d < 0", n);
+  MOE_REQUIRE(!c->cfg.blocking, MOE_ESTATE,
+              "expert_slot_cache_prefetch: a blocking cache transfers only what a step needs");
+  for (int i = 0; i < n; ++i)
+    MOE_REQUIRE(experts_host[i] >= 0 && experts_host[i] < c->cfg.n_experts, MOE_EINVAL,
+                "expert_slot_cache_prefetch: expert %d outside [0, %d)", experts_host[i], c->cfg.n_experts);
+  int copies = 0;
+  for (int i = 0; i < n; ++i) {
+    const moe_cache_entry en = prefetch_one(c, experts_host[i]);
+    if (en.expert < 0) break;  // every slot holds an expert of the last planned step
+    if (en.slot < 0) continue;  // already resident
+    ++copies;
+    if (c->cfg.dry_run) continue;
+    if (c->last_read_valid[en.slot]) MOE_HIP(hipStreamWaitEvent(c->side, c->last_read[en.slot], 0));
+    char* dst = static_cast<char*>(c->cfg.pool) + (int64_t)en.slot * c->cfg.slot_stride;
+    const hipError_t err = hipMemcpyAsync(dst, c->bundles[en.expert], (size_t)c->cfg.bundle_bytes,
+                                          hipMemcpyHostToDevice, c->side);
+    if (err != hipSuccess) {
+      c->slot_of[en.expert] = -1;
+      c->owner[en.slot] = -1;
+      c->prefetched[en.expert] = 0;
+      set_error("expert_slot_cache_prefetch: copy of expert %d into slot %d failed: %s", en.expert, en.slot,
+                hipGetErrorString(err));
+      return MOE_EHIP;
+    }
+    MOE_HIP(hipEventRecord(c->fill_done[en.slot], c->side));
+    c->fill_pending[en.slot] = 1;
+    c->st.h2d_bytes += c->cfg.bundle_bytes;
+  }
+  if (n_copies_out) *n_copies_out = copies;
   return MOE_OK;
 }
 

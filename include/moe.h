@@ -403,8 +403,10 @@ typedef struct {
 
 typedef struct {
   int64_t steps, hits, misses, evictions, waves;
-  int64_t h2d_bytes, d2h_bytes;
-  double copy_ms;   /* sum over steps of side-stream copy spans (events) */
+  int64_t h2d_bytes, d2h_bytes;   /* h2d includes prefetch copies */
+  double copy_ms;   /* sum over steps of side-stream copy spans of the steps' misses (events) */
+  int64_t prefetches;     /* bundles copied by expert_slot_cache_prefetch */
+  int64_t prefetch_used;  /* of those, bundles a later step hit before they were evicted */
 } moe_cache_stats;
 
 /* One entry of a wave's plan (host query for tests and tools). */
@@ -422,6 +424,36 @@ moe_status expert_slot_cache_plan_host(expert_slot_cache* c, const int32_t* coun
 moe_status expert_slot_cache_wave(expert_slot_cache* c, int32_t wave, int32_t part, void* stream,
                                   int32_t* slot_of_expert, int32_t* n_experts_in_part);
 moe_status expert_slot_cache_release(expert_slot_cache* c, int32_t wave, void* stream);
+/* Prefetch of predicted experts ahead of the step that routes to them.
+ * The pages: a background reader fetches the next layer while the current one
+ * computes ("NovaLLM: Running Massive MoE Models Fully In-Memory", section 3,
+ * Optimization #1); predicted experts that are not resident are copied
+ * host -> HBM asynchronously before the model reaches their layer, the experts
+ * most in demand first ("The Billion-Token Bottleneck", sections "Predictive
+ * Prefetching: Looking into the Future" and "The Orchestration Layer").
+ * The prediction itself is the caller's (a list of expert ids, highest
+ * priority first). Readings implemented, in list order:
+ *  - a resident expert has its recency refreshed, and is not copied;
+ *  - a non-resident expert takes the lowest free slot, else the slot of the
+ *    least recently used expert that neither the last planned step (acquire or
+ *    plan_host) accessed nor a prefetch since then named: a prefetch never
+ *    evicts an expert of that step, whose kernels may still read it, nor one
+ *    it has just brought in. If every slot holds such an expert, the rest of
+ *    the list is dropped;
+ *  - a prefetched expert is resident for the planner: the next step that
+ *    touches it counts a hit (stats.prefetch_used) and runs it with the wave's
+ *    hits (part 0), after `stream`-side waits for its copy if that copy may
+ *    still be in flight.
+ * Copies go on the cache's side stream, after every copy issued before (so
+ * call this after the current step's waves have been issued, or its miss
+ * copies queue behind the prediction), each after the last compute read of
+ * its victim slot. Under dry_run only the plan changes.
+ * n_copies_out (optional) = bundles copied by this call.
+ * Errors: MOE_EINVAL (an id outside [0, n_experts), n < 0, NULL list with
+ *  n > 0), MOE_ESTATE (a blocking cache, which only transfers what a step
+ *  needs), MOE_EHIP (a copy failed; that expert is left non-resident). */
+moe_status expert_slot_cache_prefetch(expert_slot_cache* c, const int32_t* experts_host, int32_t n,
+                                      int32_t* n_copies_out);
 moe_status expert_slot_cache_wave_plan(const expert_slot_cache* c, int32_t wave,
                                        moe_cache_entry* entries_host, int32_t capacity,
                                        int32_t* n_entries);

@@ -24,6 +24,23 @@ Readings taken where the pages are silent:
 Under this order an eviction never removes an expert of the wave being formed:
 every expert accessed in the wave is more recent than any candidate victim,
 and a wave holds at most n_slots experts.
+
+Prefetch (the "next" row of the residency design): predicted experts are
+fetched ahead of the layer that will run them, in the background while the
+current layer computes ("NovaLLM", section 3, Optimization #1), only when not
+already resident, the experts most in demand first ("The Billion-Token
+Bottleneck", sections "Predictive Prefetching: Looking into the Future" and
+"The Orchestration Layer"). The prediction is an input (a priority-ordered
+list). Readings taken:
+
+* a predicted expert that is resident only has its recency refreshed;
+* a non-resident one takes the lowest free slot, else the slot of the least
+  recently used expert that neither the most recent step touched (that step's
+  kernels may still be reading its experts) nor a prediction since that step
+  named (a prediction does not undo itself); when no such expert exists the
+  rest of the prediction is dropped;
+* a prefetch is neither a hit nor a miss; a later step that touches a
+  prefetched expert before it is evicted counts a hit and a "prefetch used".
 """
 from __future__ import annotations
 
@@ -50,6 +67,8 @@ class CacheStats:
     evictions: int = 0
     waves: int = 0
     steps: int = 0
+    prefetches: int = 0
+    prefetch_used: int = 0
 
 
 class LRUSlotCache:
@@ -64,6 +83,8 @@ class LRUSlotCache:
         self.owner = [-1] * self.S
         self.last = [0] * self.E
         self.clock = 0
+        self.step_touched = set()     # experts the most recent step accessed, or predicted since
+        self.from_prefetch = set()    # prefetched, not yet touched by a step
         self.stats = CacheStats()
 
     def resident(self):
@@ -71,9 +92,13 @@ class LRUSlotCache:
 
     def _access(self, e: int) -> WaveEntry:
         self.clock += 1
+        self.step_touched.add(e)
         if self.slot_of[e] >= 0:
             self.last[e] = self.clock
             self.stats.hits += 1
+            if e in self.from_prefetch:
+                self.from_prefetch.discard(e)
+                self.stats.prefetch_used += 1
             return WaveEntry(e, self.slot_of[e], True, -1)
         self.stats.misses += 1
         evicted = -1
@@ -84,6 +109,7 @@ class LRUSlotCache:
             evicted = min(self.resident(), key=lambda v: self.last[v])
             slot = self.slot_of[evicted]
             self.slot_of[evicted] = -1
+            self.from_prefetch.discard(evicted)
             self.stats.evictions += 1
         self.owner[slot] = e
         self.slot_of[e] = slot
@@ -92,6 +118,7 @@ class LRUSlotCache:
 
     def step(self, touched_experts) -> StepPlan:
         touched = sorted(set(int(e) for e in touched_experts))
+        self.step_touched = set()
         order = [e for e in touched if self.slot_of[e] >= 0] + [e for e in touched if self.slot_of[e] < 0]
         plan = StepPlan()
         for w0 in range(0, len(order), self.S):
@@ -99,3 +126,36 @@ class LRUSlotCache:
         self.stats.waves += len(plan.waves)
         self.stats.steps += 1
         return plan
+
+    def prefetch(self, predicted):
+        """Inserts the predicted experts (priority order) between steps. Returns the copies it
+        implies as (expert, slot, evicted) in issue order."""
+        copies = []
+        for e in (int(v) for v in predicted):
+            if self.slot_of[e] >= 0:
+                self.clock += 1
+                self.last[e] = self.clock
+                self.step_touched.add(e)
+                continue
+            free = [s for s in range(self.S) if self.owner[s] < 0]
+            evicted = -1
+            if free:
+                slot = free[0]
+            else:
+                candidates = [v for v in self.resident() if v not in self.step_touched]
+                if not candidates:
+                    break
+                evicted = min(candidates, key=lambda v: self.last[v])
+                slot = self.slot_of[evicted]
+                self.slot_of[evicted] = -1
+                self.from_prefetch.discard(evicted)
+                self.stats.evictions += 1
+            self.clock += 1
+            self.owner[slot] = e
+            self.slot_of[e] = slot
+            self.last[e] = self.clock
+            self.step_touched.add(e)
+            self.from_prefetch.add(e)
+            self.stats.prefetches += 1
+            copies.append((e, slot, evicted))
+        return copies

@@ -296,6 +296,44 @@ def test_planner_matches_oracle_simulation(E, S, k, T):
     c.close()
 
 
+@pytest.mark.parametrize("E,S,k,T", [(8, 5, 2, 2), (60, 24, 4, 4), (128, 48, 8, 4), (128, 32, 8, 32)])
+def test_planner_prefetch_matches_oracle_simulation(E, S, k, T):
+    """Steps interleaved with predictions (the previous step's set, random lists, resident
+    experts): the library's plans, copy counts and counters equal the oracle's."""
+    rng = np.random.default_rng(7 * E + S)
+    c = B.SlotCache(E, S, 1 << 20, 1 << 20, dry_run=True)
+    sim = LRUSlotCache(E, S)
+    prev = None
+    for step in range(60):
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+        counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+        n = c.plan_host(counts)
+        plan = sim.step(idx.ravel())
+        assert n == len(plan.waves)
+        for w, wave in enumerate(plan.waves):
+            assert c.wave_plan(w) == [(en.expert, en.slot, int(en.hit), en.evicted) for en in wave]
+        pred = rng.choice(E, size=rng.integers(0, S + 4)).tolist()
+        if prev is not None and step % 2:
+            pred = np.flatnonzero(prev).tolist() + pred
+        assert c.prefetch(pred) == len(sim.prefetch(pred))
+        prev = counts
+    st = c.stats()
+    s = sim.stats
+    assert (st["hits"], st["misses"], st["evictions"], st["prefetches"], st["prefetch_used"]) == \
+        (s.hits, s.misses, s.evictions, s.prefetches, s.prefetch_used)
+    if S > T * k:   # else every slot holds an expert of the last step and nothing is copied
+        assert s.prefetches > 0 and s.prefetch_used > 0
+    with pytest.raises(B.MoeError) as ei:
+        c.prefetch([E])
+    assert ei.value.status == -1
+    c.close()
+    blocking = B.SlotCache(E, S, 1 << 20, 1 << 20, blocking=True, dry_run=True)
+    with pytest.raises(B.MoeError) as ei:
+        blocking.prefetch([0])
+    assert ei.value.status == -6
+    blocking.close()
+
+
 def test_cache_create_validation():
     with pytest.raises(B.MoeError) as ei:
         B.SlotCache(8, 0, 1024, 1024, dry_run=True)

@@ -90,3 +90,141 @@ def test_pool_holding_all_experts_only_cold_misses():
         c.step(st)
     assert c.stats.misses == len(set(np.concatenate(steps).tolist()))
     assert c.stats.evictions == 0
+
+
+# ---------------------------------------------------------------- prefetch --
+
+def _prefetch_sequence():
+    return [("S", {0, 1}), ("P", [2, 3, 4]), ("S", {2, 3}), ("P", [4, 5, 1]), ("S", {1, 4})]
+
+
+def test_prefetch_hand_worked_trace():
+    want_s, want_p, want_t = [], [], None
+    for line in open(os.path.join(GOLDEN, "lru_prefetch_trace.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        tag, *vals = line.split()
+        vals = tuple(int(v) for v in vals)
+        {"S": want_s, "P": want_p}.get(tag, []).append(vals)
+        if tag == "T":
+            want_t = vals
+    c = LRUSlotCache(6, 3)
+    got_s, got_p = [], []
+    n_s = n_p = 0
+    for kind, arg in _prefetch_sequence():
+        if kind == "S":
+            n_s += 1
+            for w, wave in enumerate(c.step(arg).waves):
+                got_s += [(n_s, w, en.expert, en.slot, int(en.hit), en.evicted) for en in wave]
+        else:
+            n_p += 1
+            got_p += [(n_p,) + cp for cp in c.prefetch(arg)]
+    assert got_s == want_s and got_p == want_p
+    st = c.stats
+    assert (st.hits, st.misses, st.evictions, st.prefetches, st.prefetch_used) == want_t
+
+
+def _mtf_prefetch_run(ops, S):
+    """Move-to-front list (index 0 = most recent) with prefetch: a prediction goes to the
+    front; its victim is the deepest entry outside the protected set (the last step's
+    experts and everything predicted since)."""
+    lst, protected, from_pf = [], set(), set()
+    hits = misses = ev = pf = used = 0
+    for kind, arg in ops:
+        if kind == "S":
+            touched = sorted(set(arg))
+            protected = set()
+            for e in [e for e in touched if e in lst] + [e for e in touched if e not in lst]:
+                protected.add(e)
+                if e in lst:
+                    hits += 1
+                    used += e in from_pf
+                    from_pf.discard(e)
+                    lst.remove(e)
+                else:
+                    misses += 1
+                    if len(lst) == S:
+                        from_pf.discard(lst.pop())
+                        ev += 1
+                lst.insert(0, e)
+        else:
+            for e in arg:
+                if e in lst:
+                    lst.remove(e)
+                    lst.insert(0, e)
+                    protected.add(e)
+                    continue
+                if len(lst) == S:
+                    free = [i for i, v in enumerate(lst) if v not in protected]
+                    if not free:
+                        break
+                    from_pf.discard(lst.pop(free[-1]))
+                    ev += 1
+                lst.insert(0, e)
+                protected.add(e)
+                from_pf.add(e)
+                pf += 1
+    return (hits, misses, ev, pf, used), sorted(lst)
+
+
+@pytest.mark.parametrize("E,S,k", [(8, 3, 2), (16, 5, 3), (64, 16, 8), (128, 32, 8)])
+def test_prefetch_matches_move_to_front(E, S, k):
+    rng = np.random.default_rng(E + S)
+    ops, prev = [], None
+    for i in range(120):
+        touched = rng.choice(E, size=(rng.integers(1, 5), k)).ravel()
+        ops.append(("S", touched))
+        if i % 3 != 2:
+            pred = rng.choice(E, size=rng.integers(0, S + 3)).tolist()
+            if prev is not None and i % 2:
+                pred = sorted(set(prev.tolist()))[:S] + pred   # previous step's set first
+            ops.append(("P", pred))
+        prev = touched
+    c = LRUSlotCache(E, S)
+    for kind, arg in ops:
+        if kind == "S":
+            before = set(c.resident())
+            plan = c.step(arg)
+            for wave in plan.waves:
+                for en in wave:
+                    assert bool(en.hit) == (en.expert in before)
+        else:
+            last_step = {en.expert for wave in plan.waves for en in wave if c.slot_of[en.expert] >= 0}
+            c.prefetch(arg)
+            # a prefetch never evicts an expert the last step ran
+            assert last_step <= set(c.resident())
+    st = c.stats
+    want, res = _mtf_prefetch_run(ops, S)
+    assert (st.hits, st.misses, st.evictions, st.prefetches, st.prefetch_used) == want
+    assert c.resident() == res
+    for e in range(E):
+        if c.slot_of[e] >= 0:
+            assert c.owner[c.slot_of[e]] == e
+
+
+def test_prefetch_of_the_next_set_removes_its_misses():
+    """A perfect prediction with room for it: the next step is all hits, each one used."""
+    rng = np.random.default_rng(21)
+    E, S = 64, 40
+    c = LRUSlotCache(E, S)
+    steps = [rng.choice(E, size=16, replace=False) for _ in range(30)]
+    for cur, nxt in zip(steps, steps[1:]):
+        c.step(cur)
+        pf0 = c.stats.prefetches
+        c.prefetch(sorted(set(nxt.tolist())))
+        h0, m0, u0 = c.stats.hits, c.stats.misses, c.stats.prefetch_used
+        c.step(nxt)
+        assert c.stats.misses == m0
+        assert c.stats.hits - h0 == len(set(nxt.tolist()))
+        # every bundle the last prefetch copied was used by this step
+        assert c.stats.prefetch_used - u0 == c.stats.prefetches - pf0
+    assert c.stats.prefetch_used == c.stats.prefetches
+
+
+def test_prefetch_of_resident_or_nothing_changes_no_residency():
+    c = LRUSlotCache(10, 4)
+    c.step([1, 2, 3])
+    slots = list(c.slot_of)
+    assert c.prefetch([]) == [] and c.prefetch([3, 1]) == []
+    assert c.slot_of == slots and c.stats.prefetches == 0 and c.stats.evictions == 0
