@@ -169,6 +169,89 @@ def bench_offload(args, torch, B, synth, MoELayer):
     return 0
 
 
+def bench_stack(args, torch, B, synth, MoELayer):
+    """Expert-offload decode through a synthetic stack of L layers whose experts share one HBM slot
+    pool (entry l*E + e), so the layers compete for the same slots. Each layer step may prefetch the
+    next layer's predicted experts once its own waves are issued: "prev" predicts the experts that
+    layer touched in the previous step, "zipf" the top-N experts of its routing prior for the step
+    (the synthetic stand-in for a shadow router). The layers share expert weights (distinct cache
+    entries, real copies) and take independent inputs; the same steps also run with every expert
+    resident (compute time) and with no prefetch."""
+    from expert_offloaded_ffn_amd.layer import W_CODE, SharedSlotPool, pack_bundles
+    cfg = synth.get_config(args.workload)
+    if args.tokens:
+        cfg = cfg.with_T(args.tokens)
+    L, steps, E = args.layers, args.steps, cfg.E
+    n_slots = args.slots or cfg.n_slots * L
+    cfgs = synth.stack_configs(cfg, L)
+    log(f"[bench] stack: {L} layers, {n_slots} shared slots, generating {E} experts")
+    experts = synth.gen_experts(cfg, threads=16)
+    routers = [synth.gen_router(c) for c in cfgs]
+    xs = [[_x_dev(c, synth.gen_x(c, s), torch) for s in range(steps)] for c in cfgs]
+    priors = [[synth.zipf_logit_bias(c, s) for s in range(steps + 1)] for c in cfgs]
+    lbs = [[torch.from_numpy(p).to("cuda") for p in pl[:steps]] for pl in priors]
+
+    def run(layers, pool=None, predictor="none"):
+        prev = [[] for _ in range(L)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            for l in range(L):
+                nl, ns = (l + 1) % L, s + (l + 1) // L
+                pred = None
+                if predictor == "prev":
+                    pred = [nl * E + e for e in prev[nl]]
+                elif predictor == "zipf":
+                    pred = [nl * E + int(e) for e in np.argsort(-priors[nl][ns], kind="stable")[:args.prefetch_n]]
+                g = layers[l].forward(xs[l][s], logit_bias=lbs[l][s], prefetch=pred)
+                if pool is not None and predictor == "prev":
+                    prev[l] = sorted({en[0] - l * E for w in range(g["waves"]) for en in pool.cache.wave_plan(w)})
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    res = [MoELayer(c, router=r, experts=experts, threads=16) for c, r in zip(cfgs, routers)]
+    for l in range(L):
+        res[l].forward(xs[l][0], logit_bias=lbs[l][0])
+    t_comp = run(res)
+    del res
+    torch.cuda.empty_cache()
+    bundles = pack_bundles(cfg, experts, cfg.d, cfg.F, pin=True, threads=16)
+    out = {}
+    for predictor in ["none"] + [p for p in args.prefetch.split(",") if p != "none"]:
+        pool = SharedSlotPool([bundles] * L, n_slots, cfg.d, cfg.F, W_CODE[cfg.dtype])
+        layers = [MoELayer(c, router=r, experts=None, shared_pool=pool, layer_index=l)
+                  for l, (c, r) in enumerate(zip(cfgs, routers))]
+        t_wall = run(layers, pool, predictor)
+        st = pool.cache.stats()
+        acc = st["hits"] + st["misses"]
+        out[predictor] = {"wall_s": round(t_wall, 4), "tokens_per_s": round(cfg.T * steps / t_wall, 1),
+                          "ms_per_step": round(t_wall / steps * 1e3, 3),
+                          "hit_rate": round(st["hits"] / max(acc, 1), 4), "hits": st["hits"],
+                          "misses": st["misses"], "prefetches": st["prefetches"],
+                          "prefetch_used": st["prefetch_used"],
+                          "prefetch_accuracy": round(st["prefetch_used"] / max(st["prefetches"], 1), 4),
+                          "h2d_GB": round(st["h2d_bytes"] / 1e9, 3),
+                          "h2d_GBps_wall": round(st["h2d_bytes"] / t_wall / 1e9, 2)}
+        log(f"[bench] stack predictor={predictor}: {out[predictor]}")
+        pool.cache.close()
+        del layers, pool
+        torch.cuda.empty_cache()
+    best = max(out, key=lambda k: out[k]["tokens_per_s"])
+    result = {
+        "metric": METRIC, "value": out[best]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": 0, "ms_per_step": out[best]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded; per-layer routers and Zipf(1.1) priors, expert weights shared by the layers)",
+        "config": {"workload": cfg.name + "_stack", "layers": L, "T": cfg.T, "d_model": cfg.d, "n_experts": E,
+                   "top_k": cfg.k, "d_ff": cfg.F, "n_slots_shared": n_slots, "weights": cfg.dtype,
+                   "prefetch_n_zipf": args.prefetch_n, "best": best,
+                   "bundle_bytes": B.bundle_bytes(cfg.d, cfg.F, W_CODE[cfg.dtype])},
+        "resident_compute_s": round(t_comp, 4), "stack": out,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def bench_decode(args, torch, B, synth, MoELayer):
     """Decode layer (few tokens): each step's time is measured alone with hipEvents, after a
     512 MiB pass that evicts the 256 MB last-level cache, so weights stream from HBM (a read by
@@ -281,6 +364,13 @@ def main():
                     help="prefill: add a Zipf(alpha) log-prior to the routing logits (0 = unskewed)")
     ap.add_argument("--mall-flush", choices=["read", "write"], default="read",
                     help="decode: evict the last-level cache before each step by reading (default) or writing 512 MiB")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="offload workloads: a stack of this many layers sharing one slot pool")
+    ap.add_argument("--slots", type=int, default=0, help="stack: shared slots (default n_slots per layer x layers)")
+    ap.add_argument("--prefetch", default="prev,zipf",
+                    help="stack: predictors to run besides none (prev = the layer's previous step, "
+                         "zipf = top-N of its routing prior)")
+    ap.add_argument("--prefetch-n", type=int, default=16, help="stack: experts the zipf predictor names")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (HBM ceiling and the "
                          "reference for the FETCH_SIZE/WRITE_SIZE counters), then exit")
@@ -313,6 +403,8 @@ def main():
                           "hbm_read_plus_write_GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}), flush=True)
         return 0
 
+    if args.workload.startswith("offload_decode") and args.layers > 1:
+        return bench_stack(args, torch, B, synth, MoELayer)
     if args.workload.startswith("offload_decode") and not args.resident:
         return bench_offload(args, torch, B, synth, MoELayer)
     if args.workload == "qwen_decode_bf16" or args.workload.startswith("offload_decode"):

@@ -59,6 +59,31 @@ class ResidentPool:
         self.table = B.expert_table(self.pool, self.stride, self.slots, self.n, d, F, w_dtype)
 
 
+class SharedSlotPool:
+    """One expert slot pool, and one LRU over it, for the layers of a stack: expert e of layer l
+    is entry l*E + e of the cache, so the layers compete for the same HBM slots and one layer's
+    step can prefetch the next layer's predicted experts (expert_slot_cache_prefetch).
+    bundles_per_layer: [L] lists of E pinned host bundles (layers may share bundle tensors)."""
+
+    def __init__(self, bundles_per_layer, n_slots, d, F, w_dtype, device="cuda"):
+        self.L = len(bundles_per_layer)
+        self.E = len(bundles_per_layer[0])
+        self.d, self.F, self.w_code = d, F, w_dtype
+        self.device = torch.device(device)
+        flat = [b for layer in bundles_per_layer for b in layer]
+        self.bundle_bytes = flat[0].numel()
+        self.stride = (self.bundle_bytes + 255) // 256 * 256
+        self.slot_pool = torch.empty(n_slots, self.stride, dtype=torch.uint8, device=self.device)
+        self.slot_table = torch.full((self.L * self.E,), -1, dtype=torch.int32, device=self.device)
+        self.counts = torch.zeros(self.L * self.E, dtype=torch.int32, device=self.device)
+        self.cache = B.SlotCache(self.L * self.E, n_slots, self.bundle_bytes, self.stride, flat, self.slot_pool)
+
+    def table(self, layer: int):
+        """The expert table of one layer: its E entries of the shared slot table."""
+        view = self.slot_table[layer * self.E:(layer + 1) * self.E]
+        return B.expert_table(self.slot_pool, self.stride, view, self.E, self.d, self.F, self.w_code)
+
+
 # Largest decode batch whose combine runs inside the down launch. Each workgroup that finishes
 # a unit then waits for its stores and an arrival count before it exits; that pays off only
 # while the down launch is about one round of workgroups (1-4 tokens: MI355X, Qwen1.5-MoE
@@ -68,9 +93,11 @@ FUSE_COMBINE_MAX_T = 4
 
 class MoELayer:
     def __init__(self, cfg, *, router, experts, shared=None, w_shared_gate=None, select_bias=None, device="cuda",
-                 pool_slots=None, blocking=False, threads=8, fuse_combine=True):
+                 pool_slots=None, blocking=False, threads=8, fuse_combine=True, shared_pool=None, layer_index=0):
         """router: W_r [d, E] storage; experts: list of synth expert tuples; shared: synth tuple or None.
         pool_slots: None = every expert resident; an int = expert slot pool of that many slots.
+        shared_pool: a SharedSlotPool this layer's experts live in (entry layer_index*E + e);
+        experts is then unused.
         fuse_combine: a decode step of at most FUSE_COMBINE_MAX_T tokens that runs the shared expert
         in the routed experts' launches combines inside the down launch (moe_grouped_ffn_combine)
         instead of a moe_combine call."""
@@ -84,10 +111,21 @@ class MoELayer:
         self.w_router_t = _bits_to_tensor(np.ascontiguousarray(np.asarray(router).T), self.act, self.device)
         self.w_sg = None if w_shared_gate is None else _bits_to_tensor(w_shared_gate, self.act, self.device)
         self.select_bias = None if select_bias is None else torch.from_numpy(select_bias).to(self.device)
-        bundles = pack_bundles(cfg, experts, self.d, self.F, pin=pool_slots is not None, threads=threads)
-        self.bundle_bytes = bundles[0].numel()
         self.cache = None
-        if pool_slots is None:
+        self.cache_base = None
+        if shared_pool is not None:
+            self.cache = shared_pool.cache
+            self.cache_base = layer_index * self.E
+            self.slot_table = shared_pool.slot_table
+            self.counts_all = shared_pool.counts
+            self.table = shared_pool.table(layer_index)
+            self.bundle_bytes = shared_pool.bundle_bytes
+        else:
+            bundles = pack_bundles(cfg, experts, self.d, self.F, pin=pool_slots is not None, threads=threads)
+            self.bundle_bytes = bundles[0].numel()
+        if shared_pool is not None:
+            pass   # the stack's pool holds this layer's bundles
+        elif pool_slots is None:
             self.pool = ResidentPool(bundles, self.d, self.F, self.w_code, self.device)
             self.table = self.pool.table
         else:
@@ -157,8 +195,10 @@ class MoELayer:
             B.profile_label(0)
         return shared_y
 
-    def forward(self, x: torch.Tensor, logit_bias: torch.Tensor | None = None, stream=None) -> dict:
+    def forward(self, x: torch.Tensor, logit_bias: torch.Tensor | None = None, stream=None, prefetch=None) -> dict:
         """x [T, d] device tensor in the activation dtype. Returns the layer output and routing tensors.
+        prefetch (slot pool only): cache entries predicted for a later step, handed to
+        expert_slot_cache_prefetch once this step's waves are issued.
         The shared expert (when there is one) runs inside the routed experts' launches for a
         decode step (shared_in_decode_launch), else on a second stream, forked once the routing
         is issued, concurrently with the routed experts, and joined before the combine."""
@@ -212,7 +252,12 @@ class MoELayer:
             waves = 0
         else:
             fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
-            waves = self.cache.acquire(r["counts"], stream=main)
+            counts = r["counts"]
+            if self.cache_base is not None:   # this layer's histogram into the stack-wide one
+                self.counts_all.zero_()
+                self.counts_all[self.cache_base:self.cache_base + E].copy_(counts)
+                counts = self.counts_all
+            waves = self.cache.acquire(counts, stream=main)
             for w in range(waves):
                 for part in (0, 1):
                     n = self.cache.wave(w, part, self.slot_table, stream=main)
@@ -220,6 +265,8 @@ class MoELayer:
                         B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
                                       a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=main)
                 self.cache.release(w, stream=main)
+            if prefetch is not None:
+                self.cache.prefetch(prefetch)
         if shared_y is not None and not merged:
             main.wait_stream(self._side_stream())
         out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"], stream=main)

@@ -111,6 +111,12 @@ def get_config(config_name: str, **overrides) -> LayerConfig:
     return replace(CONFIGS[config_name], **overrides)
 
 
+def stack_configs(cfg: LayerConfig, n_layers: int) -> list:
+    """Per-layer configs of a synthetic stack of n_layers copies of cfg: layer l draws its router,
+    activations and Zipf epochs from seed cfg.seed + 101*l (the expert weights may be shared)."""
+    return [replace(cfg, seed=cfg.seed + 101 * l) for l in range(n_layers)]
+
+
 def _rng(*key: int) -> np.random.Generator:
     return np.random.default_rng([int(v) for v in key])
 
