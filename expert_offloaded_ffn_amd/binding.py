@@ -121,6 +121,13 @@ EXPORTS = {
     "expert_slot_cache_wave_plan": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(CacheEntry),
                                     ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_stats": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheStats)]),
+    "expert_slot_cache_dev_create": (ctypes.c_int32, [ctypes.POINTER(CacheCfg), ctypes.POINTER(ctypes.c_void_p)]),
+    "expert_slot_cache_dev_destroy": (ctypes.c_int32, [ctypes.c_void_p]),
+    "expert_slot_cache_dev_reset": (ctypes.c_int32, [ctypes.c_void_p]),
+    "expert_slot_cache_dev_step": (ctypes.c_int32, [ctypes.c_void_p] * 5),
+    "expert_slot_cache_dev_join": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p]),
+    "expert_slot_cache_dev_stats": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheStats),
+                                    ctypes.POINTER(ctypes.c_int64)]),
     "moe_profile_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "moe_profile_label": (ctypes.c_int32, [ctypes.c_int32]),
     "moe_profile_read": (ctypes.c_int32, [ctypes.POINTER(Profile)]),
@@ -439,6 +446,49 @@ class SlotCache:
         s = CacheStats()
         _check(lib().expert_slot_cache_stats(self.h, ctypes.byref(s)))
         return {f: getattr(s, f) for f, _ in CacheStats._fields_}
+
+
+class DeviceSlotCache:
+    """expert_slot_cache_dev: the slot pool planned on the device (no host synchronisation)."""
+
+    def __init__(self, n_experts, n_slots, bundle_bytes_, slot_stride, bundles_host, pool):
+        self._keep = bundles_host
+        self._arr = (ctypes.c_void_p * n_experts)(*[b.data_ptr() for b in bundles_host])
+        cfg = CacheCfg(n_experts, n_slots, int(bundle_bytes_), int(slot_stride),
+                       ctypes.cast(self._arr, ctypes.c_void_p), ptr(pool), 0, 0)
+        h = ctypes.c_void_p()
+        _check(lib().expert_slot_cache_dev_create(ctypes.byref(cfg), ctypes.byref(h)))
+        self.h = h
+        self.E = n_experts
+
+    def close(self):
+        if self.h:
+            lib().expert_slot_cache_dev_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self):
+        _check(lib().expert_slot_cache_dev_reset(self.h))
+
+    def step(self, counts, hit_table, miss_table, stream=None):
+        _check(lib().expert_slot_cache_dev_step(self.h, ptr(counts), stream_ptr(stream), ptr(hit_table),
+                                                ptr(miss_table)))
+
+    def join(self, stream=None):
+        _check(lib().expert_slot_cache_dev_join(self.h, stream_ptr(stream)))
+
+    def stats(self) -> dict:
+        s = CacheStats()
+        ov = ctypes.c_int64()
+        _check(lib().expert_slot_cache_dev_stats(self.h, ctypes.byref(s), ctypes.byref(ov)))
+        d = {f: getattr(s, f) for f, _ in CacheStats._fields_}
+        d["overflow_steps"] = ov.value
+        return d
 
 
 # ------------------------------------------------------------- profile ---

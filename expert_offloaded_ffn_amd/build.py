@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoeffn.so")
-SOURCES = ["capi.cpp", "profile.cpp", "pack.cpp", "slot_cache.cpp", "route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip"]
+SOURCES = ["capi.cpp", "profile.cpp", "pack.cpp", "slot_cache.cpp", "slot_cache_device.hip", "route.hip", "permute.hip", "grouped_ffn.hip", "combine.hip"]
 ARCH = os.environ.get("MOEFFN_ARCH", "gfx950")
 
 FLAGS = [

@@ -1,0 +1,367 @@
+// expert_slot_cache_dev: the expert slot pool with its plan made on the device.
+//
+// The pages intercept the router's expert list on the host before the experts
+// run ("Running 35B MoE Models on 8GB GPUs", section "Technical Insight"), a
+// synchronisation they also name as a cost, next to the launch overhead that
+// graph capture removes ("NovaLLM", section 3). Here the same residency step
+// runs without the host: one workgroup reads the expert histogram, checks
+// residency and plans the LRU accesses of the step (the rules of the host
+// planner: resident experts first, then the others, each in ascending id; the
+// lowest free slot, else the least recently used expert), then a copy kernel on
+// a side stream pulls the missed bundles from pinned host memory over PCIe
+// while the step's hits compute. Nothing waits on the host, so a whole decode
+// step (routing, plan, copies, expert FFN, combine) can be one captured graph.
+//
+// Limit: a step that touches more experts than there are slots (the host
+// planner's several waves) is not planned: both tables come back all -1, no
+// copy is made, and the step is counted in `overflow_steps`. Size the pool for
+// the largest touched set, or use the host-planned cache.
+#include <climits>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "moe_internal.h"
+
+using namespace moeffn;
+
+namespace {
+
+constexpr int kPlanThreads = 1024;   // one thread per expert and per slot
+constexpr int kCopyThreads = 256;
+constexpr int kCopyBlocksPerBundle = 16;
+
+enum Ctl { kClock = 0, kSteps, kHits, kMisses, kEvictions, kOverflow, kCopies, kBad, kCtlN };
+
+struct DevState {
+  int32_t* slot_of;   // [E]
+  int32_t* owner;     // [S]
+  int64_t* last;      // [E] recency stamps
+  int64_t* ctl;       // [kCtlN]
+  int2* copies;       // [S] (expert, slot) of the last step's misses
+};
+
+// Rank of this thread's flag among the block's set flags (ascending thread
+// index) and, in *total, how many are set. Every thread of the block calls it.
+__device__ int block_rank(bool flag, int* wave_cnt, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t b = __ballot(flag);
+  const int in_wave = __popcll(b & ((1ull << lane) - 1ull));
+  if (lane == 0) wave_cnt[wave] = __popcll(b);
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const int c = wave_cnt[w];
+    before += w < wave ? c : 0;
+    all += c;
+  }
+  __syncthreads();
+  *total = all;
+  return before + in_wave;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t* __restrict__ counts, DevState st,
+                                                                  int E, int S, int32_t* __restrict__ hit_table,
+                                                                  int32_t* __restrict__ miss_table) {
+  __shared__ int wave_cnt[kPlanThreads / 64];
+  __shared__ int victims[kPlanThreads];
+  __shared__ int old_owner[kPlanThreads];
+  __shared__ long long slot_last[kPlanThreads];
+  const int t = threadIdx.x;
+  bool touched = false, resident = false;
+  int my_slot = -1;
+  if (t < E) {
+    touched = counts[t] > 0;
+    my_slot = st.slot_of[t];
+    resident = my_slot >= 0;
+  }
+  int n_hit = 0, n_miss = 0;
+  const int hit_rank = block_rank(touched && resident, wave_cnt, &n_hit);
+  const int miss_rank = block_rank(touched && !resident, wave_cnt, &n_miss);
+  const long long clock = st.ctl[kClock];
+  if (n_hit + n_miss > S) {  // block-uniform: more touched experts than slots
+    if (t < E) {
+      hit_table[t] = -1;
+      miss_table[t] = -1;
+    }
+    if (t == 0) {
+      st.ctl[kSteps] += 1;
+      st.ctl[kOverflow] += 1;
+      st.ctl[kCopies] = 0;
+    }
+    return;
+  }
+  // Victims in the order sequential LRU takes them: free slots ascending, then
+  // slots of experts this step does not touch, oldest first. Touched experts
+  // are never victims: misses <= S - hits = free + untouched-resident slots.
+  int owner = -1;
+  bool is_free = false, evictable = false;
+  long long lst = LLONG_MAX;
+  if (t < S) {
+    owner = st.owner[t];
+    if (owner >= E) owner = -1;  // ids are < E in a consistent state; never index with another
+    is_free = owner < 0;
+    if (!is_free && counts[owner] == 0) {
+      evictable = true;
+      lst = st.last[owner];
+    }
+  }
+  int n_free = 0;
+  const int free_rank = block_rank(is_free, wave_cnt, &n_free);
+  if (t < S) {
+    slot_last[t] = lst;
+    old_owner[t] = owner;
+    victims[t] = -1;
+  }
+  __syncthreads();
+  if (is_free) victims[free_rank] = t;
+  if (evictable) {
+    int older = 0;  // stamps are distinct
+    for (int s = 0; s < S; ++s) older += slot_last[s] < lst ? 1 : 0;
+    victims[n_free + older] = t;
+  }
+  __syncthreads();
+  if (t < E) {
+    int hs = -1, ms = -1;
+    if (touched && resident) {
+      hs = my_slot;
+      st.last[t] = clock + 1 + hit_rank;
+    } else if (touched) {
+      const int slot = victims[miss_rank];
+      if (slot < 0 || slot >= S) {  // not reachable when the state is consistent; never index with it
+        atomicAdd(reinterpret_cast<unsigned long long*>(st.ctl + kBad), 1ull);
+        hit_table[t] = -1;
+        miss_table[t] = -1;
+        return;
+      }
+      const int old = old_owner[slot];
+      if (old >= 0) st.slot_of[old] = -1;  // an untouched expert: no other thread writes it
+      st.slot_of[t] = slot;
+      st.owner[slot] = t;
+      st.last[t] = clock + 1 + n_hit + miss_rank;
+      st.copies[miss_rank] = make_int2(t, slot);
+      ms = slot;
+    }
+    hit_table[t] = hs;
+    miss_table[t] = ms;
+  }
+  if (t == 0) {
+    st.ctl[kClock] = clock + n_hit + n_miss;
+    st.ctl[kSteps] += 1;
+    st.ctl[kHits] += n_hit;
+    st.ctl[kMisses] += n_miss;
+    st.ctl[kEvictions] += n_miss > n_free ? n_miss - n_free : 0;
+    st.ctl[kCopies] = n_miss;
+  }
+}
+
+// Copies the last step's missed bundles host -> slot. blockIdx.y = copy index
+// (blocks past the step's copy count exit at once); the x blocks of one bundle
+// stride over its 16-byte words, four loads in flight per thread.
+__global__ __launch_bounds__(kCopyThreads) void cache_copy_kernel(const int64_t* __restrict__ ctl,
+                                                                 const int2* __restrict__ copies,
+                                                                 const uint4* const* __restrict__ src,
+                                                                 uint8_t* __restrict__ pool, int64_t stride,
+                                                                 int64_t n16, int n_experts, int n_slots) {
+  const int c = blockIdx.y;
+  if (c >= (int)ctl[kCopies]) return;
+  const int2 cp = copies[c];
+  if (cp.x < 0 || cp.x >= n_experts || cp.y < 0 || cp.y >= n_slots) return;
+  const uint4* __restrict__ from = src[cp.x];
+  uint4* __restrict__ to = reinterpret_cast<uint4*>(pool + (int64_t)cp.y * stride);
+  const int64_t step = (int64_t)gridDim.x * kCopyThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kCopyThreads + threadIdx.x; i < n16; i += 4 * step) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * step < n16) v[u] = from[i + u * step];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i + u * step < n16) to[i + u * step] = v[u];
+  }
+}
+
+}  // namespace
+
+struct expert_slot_cache_dev {
+  moe_cache_cfg cfg{};
+  int device = -1;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  void* block = nullptr;  // device: state, copy list and source pointers
+  DevState st{};
+  const uint4** src = nullptr;
+  bool stepped = false;
+};
+
+namespace {
+
+size_t state_bytes(int E, int S) {
+  return align_up(sizeof(int32_t) * E, 256) + align_up(sizeof(int32_t) * S, 256) +
+         align_up(sizeof(int64_t) * E, 256) + align_up(sizeof(int64_t) * kCtlN, 256) +
+         align_up(sizeof(int2) * S, 256) + align_up(sizeof(void*) * E, 256);
+}
+
+// Empty pool, zero counters (synchronous; not for use under capture).
+moe_status init_state(expert_slot_cache_dev* c) {
+  const int E = c->cfg.n_experts, S = c->cfg.n_slots;
+  std::vector<int32_t> neg(std::max(E, S), -1);
+  std::vector<int64_t> zero(std::max(E, (int)kCtlN), 0);
+  MOE_HIP(hipMemcpy(c->st.slot_of, neg.data(), sizeof(int32_t) * E, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(c->st.owner, neg.data(), sizeof(int32_t) * S, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(c->st.last, zero.data(), sizeof(int64_t) * E, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(c->st.ctl, zero.data(), sizeof(int64_t) * kCtlN, hipMemcpyHostToDevice));
+  c->stepped = false;
+  return MOE_OK;
+}
+
+void destroy_dev(expert_slot_cache_dev* c) {
+  if (c->side) (void)hipStreamSynchronize(c->side);
+  if (c->fork) (void)hipEventDestroy(c->fork);
+  if (c->join) (void)hipEventDestroy(c->join);
+  if (c->side) (void)hipStreamDestroy(c->side);
+  if (c->block) (void)hipFree(c->block);
+}
+
+}  // namespace
+
+extern "C" moe_status expert_slot_cache_dev_create(const moe_cache_cfg* cfg, expert_slot_cache_dev** out) {
+  clear_error();
+  MOE_REQUIRE(cfg && out, MOE_EINVAL, "expert_slot_cache_dev_create: NULL argument");
+  *out = nullptr;
+  const moe_cache_cfg k = *cfg;
+  MOE_REQUIRE(!k.blocking && !k.dry_run, MOE_EINVAL,
+              "expert_slot_cache_dev_create: blocking and dry_run are host-planner modes");
+  MOE_REQUIRE(k.n_experts >= 1 && k.n_experts <= kPlanThreads, MOE_EINVAL,
+              "expert_slot_cache_dev_create: n_experts=%d outside [1, %d]", k.n_experts, kPlanThreads);
+  MOE_REQUIRE(k.n_slots >= 1 && k.n_slots <= kPlanThreads, MOE_ECAPACITY,
+              "expert_slot_cache_dev_create: n_slots=%d outside [1, %d]", k.n_slots, kPlanThreads);
+  MOE_REQUIRE(k.bundle_bytes > 0 && k.bundle_bytes % 16 == 0, MOE_EINVAL,
+              "expert_slot_cache_dev_create: bundle_bytes %lld must be a positive multiple of 16",
+              (long long)k.bundle_bytes);
+  MOE_REQUIRE(k.slot_stride >= k.bundle_bytes && k.slot_stride % 256 == 0, MOE_ECAPACITY,
+              "expert_slot_cache_dev_create: slot_stride %lld must be >= bundle_bytes %lld and a multiple of 256",
+              (long long)k.slot_stride, (long long)k.bundle_bytes);
+  MOE_REQUIRE(k.bundles_host && k.pool, MOE_EINVAL, "expert_slot_cache_dev_create: bundles_host and pool are required");
+  MOE_REQUIRE(aligned(k.pool, 256), MOE_EINVAL, "expert_slot_cache_dev_create: pool must be 256-byte aligned");
+  std::vector<const void*> src(k.n_experts);
+  for (int e = 0; e < k.n_experts; ++e) {
+    const void* h = k.bundles_host[e];
+    MOE_REQUIRE(h != nullptr && aligned(h, 16), MOE_EINVAL,
+                "expert_slot_cache_dev_create: bundle %d is NULL or not 16-byte aligned", e);
+    hipPointerAttribute_t attr;
+    std::memset(&attr, 0, sizeof(attr));
+    hipError_t err = hipPointerGetAttributes(&attr, h);
+    if (err != hipSuccess) (void)hipGetLastError();
+    MOE_REQUIRE(err == hipSuccess && attr.type == hipMemoryTypeHost, MOE_EINVAL,
+                "expert_slot_cache_dev_create: bundle %d is not in pinned host memory", e);
+    void* dptr = nullptr;
+    err = hipHostGetDevicePointer(&dptr, const_cast<void*>(h), 0);
+    if (err != hipSuccess) (void)hipGetLastError();
+    MOE_REQUIRE(err == hipSuccess && dptr != nullptr, MOE_EINVAL,
+                "expert_slot_cache_dev_create: bundle %d has no device mapping", e);
+    src[e] = dptr;
+  }
+  auto* c = new (std::nothrow) expert_slot_cache_dev();
+  MOE_REQUIRE(c != nullptr, MOE_ENOMEM, "expert_slot_cache_dev_create: out of host memory");
+  c->cfg = k;
+  auto fail = [&](const char* what, hipError_t e) {
+    set_error("expert_slot_cache_dev_create: %s: %s", what, hipGetErrorString(e));
+    destroy_dev(c);
+    delete c;
+    return MOE_EHIP;
+  };
+  hipError_t e;
+  const int E = k.n_experts, S = k.n_slots;
+  if ((e = hipGetDevice(&c->device)) != hipSuccess) return fail("hipGetDevice", e);
+  if ((e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess) return fail("hipStreamCreate", e);
+  if ((e = hipEventCreateWithFlags(&c->fork, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+  if ((e = hipEventCreateWithFlags(&c->join, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+  if ((e = hipMalloc(&c->block, state_bytes(E, S))) != hipSuccess) return fail("hipMalloc", e);
+  char* p = static_cast<char*>(c->block);
+  c->st.slot_of = reinterpret_cast<int32_t*>(p);
+  p += align_up(sizeof(int32_t) * E, 256);
+  c->st.owner = reinterpret_cast<int32_t*>(p);
+  p += align_up(sizeof(int32_t) * S, 256);
+  c->st.last = reinterpret_cast<int64_t*>(p);
+  p += align_up(sizeof(int64_t) * E, 256);
+  c->st.ctl = reinterpret_cast<int64_t*>(p);
+  p += align_up(sizeof(int64_t) * kCtlN, 256);
+  c->st.copies = reinterpret_cast<int2*>(p);
+  p += align_up(sizeof(int2) * S, 256);
+  c->src = reinterpret_cast<const uint4**>(p);
+  if ((e = hipMemcpy(c->src, src.data(), sizeof(void*) * E, hipMemcpyHostToDevice)) != hipSuccess)
+    return fail("hipMemcpy", e);
+  if (moe_status s = init_state(c)) {
+    destroy_dev(c);
+    delete c;
+    return s;
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_dev_destroy(expert_slot_cache_dev* c) {
+  clear_error();
+  if (!c) return MOE_OK;
+  destroy_dev(c);
+  delete c;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_dev_reset(expert_slot_cache_dev* c) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_reset: NULL cache");
+  MOE_HIP(hipDeviceSynchronize());
+  return init_state(c);
+}
+
+extern "C" moe_status expert_slot_cache_dev_step(expert_slot_cache_dev* c, const int32_t* counts, void* stream,
+                                                 int32_t* hit_table, int32_t* miss_table) {
+  clear_error();
+  MOE_REQUIRE(c && counts && hit_table && miss_table, MOE_EINVAL, "expert_slot_cache_dev_step: NULL argument");
+  MOE_REQUIRE(aligned(counts, 4) && aligned(hit_table, 4) && aligned(miss_table, 4), MOE_EINVAL,
+              "expert_slot_cache_dev_step: misaligned table");
+  if (moe_status s = check_launch("expert_slot_cache_dev_step (earlier work)")) return s;
+  hipStream_t s = as_stream(stream);
+  const int E = c->cfg.n_experts, S = c->cfg.n_slots;
+  hipLaunchKernelGGL(cache_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, counts, c->st, E, S, hit_table, miss_table);
+  if (moe_status r = check_launch("cache_plan_kernel")) return r;
+  MOE_HIP(hipEventRecord(c->fork, s));
+  MOE_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
+  hipLaunchKernelGGL(cache_copy_kernel, dim3(kCopyBlocksPerBundle, S), dim3(kCopyThreads), 0, c->side,
+                     c->st.ctl, c->st.copies, c->src, static_cast<uint8_t*>(c->cfg.pool), (int64_t)c->cfg.slot_stride,
+                     (int64_t)(c->cfg.bundle_bytes / 16), E, S);
+  if (moe_status r = check_launch("cache_copy_kernel")) return r;
+  MOE_HIP(hipEventRecord(c->join, c->side));
+  c->stepped = true;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_dev_join(expert_slot_cache_dev* c, void* stream) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_join: NULL cache");
+  MOE_REQUIRE(c->stepped, MOE_ESTATE, "expert_slot_cache_dev_join: no step was issued");
+  MOE_HIP(hipStreamWaitEvent(as_stream(stream), c->join, 0));
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_dev_stats(expert_slot_cache_dev* c, moe_cache_stats* out,
+                                                  int64_t* overflow_steps) {
+  clear_error();
+  MOE_REQUIRE(c && out, MOE_EINVAL, "expert_slot_cache_dev_stats: NULL argument");
+  MOE_HIP(hipDeviceSynchronize());
+  int64_t ctl[kCtlN];
+  MOE_HIP(hipMemcpy(ctl, c->st.ctl, sizeof(ctl), hipMemcpyDeviceToHost));
+  *out = moe_cache_stats{};
+  out->steps = ctl[kSteps];
+  out->hits = ctl[kHits];
+  out->misses = ctl[kMisses];
+  out->evictions = ctl[kEvictions];
+  out->waves = ctl[kSteps] - ctl[kOverflow];
+  out->h2d_bytes = ctl[kMisses] * c->cfg.bundle_bytes;
+  if (overflow_steps) *overflow_steps = ctl[kOverflow];
+  MOE_REQUIRE(ctl[kBad] == 0, MOE_ESTATE, "expert_slot_cache_dev_stats: the device plan found no victim slot %lld times",
+              (long long)ctl[kBad]);
+  return MOE_OK;
+}

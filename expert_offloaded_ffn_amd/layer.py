@@ -93,11 +93,14 @@ FUSE_COMBINE_MAX_T = 4
 
 class MoELayer:
     def __init__(self, cfg, *, router, experts, shared=None, w_shared_gate=None, select_bias=None, device="cuda",
-                 pool_slots=None, blocking=False, threads=8, fuse_combine=True, shared_pool=None, layer_index=0):
+                 pool_slots=None, blocking=False, threads=8, fuse_combine=True, shared_pool=None, layer_index=0,
+                 device_plan=False):
         """router: W_r [d, E] storage; experts: list of synth expert tuples; shared: synth tuple or None.
         pool_slots: None = every expert resident; an int = expert slot pool of that many slots.
         shared_pool: a SharedSlotPool this layer's experts live in (entry layer_index*E + e);
         experts is then unused.
+        device_plan: with pool_slots, plan residency and copy missed bundles on the device
+        (expert_slot_cache_dev): no host synchronisation, and capture() works.
         fuse_combine: a decode step of at most FUSE_COMBINE_MAX_T tokens that runs the shared expert
         in the routed experts' launches combines inside the down launch (moe_grouped_ffn_combine)
         instead of a moe_combine call."""
@@ -112,6 +115,7 @@ class MoELayer:
         self.w_sg = None if w_shared_gate is None else _bits_to_tensor(w_shared_gate, self.act, self.device)
         self.select_bias = None if select_bias is None else torch.from_numpy(select_bias).to(self.device)
         self.cache = None
+        self.cache_dev = None
         self.cache_base = None
         if shared_pool is not None:
             self.cache = shared_pool.cache
@@ -133,8 +137,15 @@ class MoELayer:
             stride = (self.bundle_bytes + 255) // 256 * 256
             self.slot_pool = torch.empty(pool_slots, stride, dtype=torch.uint8, device=self.device)
             self.slot_table = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
-            self.cache = B.SlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles, self.slot_pool,
-                                     blocking=blocking)
+            if device_plan:
+                self.miss_slot_table = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
+                self.cache_dev = B.DeviceSlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles,
+                                                   self.slot_pool)
+                self.miss_table = B.expert_table(self.slot_pool, stride, self.miss_slot_table, self.E, self.d,
+                                                 self.F, self.w_code)
+            else:
+                self.cache = B.SlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles, self.slot_pool,
+                                         blocking=blocking)
             self.table = B.expert_table(self.slot_pool, stride, self.slot_table, self.E, self.d, self.F, self.w_code)
         self.shared = None
         if shared is not None:
@@ -245,6 +256,16 @@ class MoELayer:
             bws = self._buf("batch_ws", B.grouped_ffn_batch_workspace_size(probs))
             B.grouped_ffn_batch(probs, ws=bws, stream=main)
             waves = 0
+        elif self.cache_dev is not None:
+            # plan on the device; the hits run while the misses' copy kernel reads host memory
+            fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
+            self.cache_dev.step(r["counts"], self.slot_table, self.miss_slot_table, stream=main)
+            for part, table in enumerate((self.table, self.miss_table)):
+                if part == 1:
+                    self.cache_dev.join(stream=main)
+                B.grouped_ffn(table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
+                              a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=main)
+            waves = 1
         elif self.cache is None:
             fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
             B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
@@ -273,11 +294,14 @@ class MoELayer:
         return {"out": out, "route": r, "perm": p, "y": y, "shared_y": shared_y, "waves": waves}
 
     def capture(self, x_static: torch.Tensor, logit_bias_static: torch.Tensor | None = None):
-        """Records forward() for fixed input buffers as one HIP graph (resident layers only: the
-        slot pool synchronises with the host every step). Returns (graph, outputs); refill
-        x_static (and logit_bias_static) in place, then graph.replay() recomputes outputs."""
+        """Records forward() for fixed input buffers as one HIP graph (resident layers, or a slot
+        pool planned on the device; the host-planned pool synchronises with the host every step).
+        Returns (graph, outputs); refill x_static (and logit_bias_static) in place, then
+        graph.replay() recomputes outputs. The warm-up runs before capture are real steps: a
+        device-planned pool's residency and counters include them."""
         if self.cache is not None:
-            raise RuntimeError("capture() needs a resident layer; the slot pool plans on the host each step")
+            raise RuntimeError("capture() needs a resident layer or device_plan=True; the host-planned slot pool "
+                               "synchronises with the host each step")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
