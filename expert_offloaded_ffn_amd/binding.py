@@ -124,10 +124,11 @@ EXPORTS = {
     "expert_slot_cache_dev_create": (ctypes.c_int32, [ctypes.POINTER(CacheCfg), ctypes.POINTER(ctypes.c_void_p)]),
     "expert_slot_cache_dev_destroy": (ctypes.c_int32, [ctypes.c_void_p]),
     "expert_slot_cache_dev_reset": (ctypes.c_int32, [ctypes.c_void_p]),
+    "expert_slot_cache_dev_max_waves": (ctypes.c_int32, [ctypes.c_void_p]),
     "expert_slot_cache_dev_step": (ctypes.c_int32, [ctypes.c_void_p] * 5),
-    "expert_slot_cache_dev_join": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p]),
-    "expert_slot_cache_dev_stats": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheStats),
-                                    ctypes.POINTER(ctypes.c_int64)]),
+    "expert_slot_cache_dev_copy": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "expert_slot_cache_dev_join": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "expert_slot_cache_dev_stats": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheStats)]),
     "moe_profile_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "moe_profile_label": (ctypes.c_int32, [ctypes.c_int32]),
     "moe_profile_read": (ctypes.c_int32, [ctypes.POINTER(Profile)]),
@@ -475,20 +476,24 @@ class DeviceSlotCache:
     def reset(self):
         _check(lib().expert_slot_cache_dev_reset(self.h))
 
-    def step(self, counts, hit_table, miss_table, stream=None):
-        _check(lib().expert_slot_cache_dev_step(self.h, ptr(counts), stream_ptr(stream), ptr(hit_table),
-                                                ptr(miss_table)))
+    @property
+    def max_waves(self) -> int:
+        return int(lib().expert_slot_cache_dev_max_waves(self.h))
 
-    def join(self, stream=None):
-        _check(lib().expert_slot_cache_dev_join(self.h, stream_ptr(stream)))
+    def step(self, counts, hit_table, miss_tables, stream=None):
+        _check(lib().expert_slot_cache_dev_step(self.h, ptr(counts), stream_ptr(stream), ptr(hit_table),
+                                                ptr(miss_tables)))
+
+    def copy(self, wave, stream=None):
+        _check(lib().expert_slot_cache_dev_copy(self.h, int(wave), stream_ptr(stream)))
+
+    def join(self, wave, stream=None):
+        _check(lib().expert_slot_cache_dev_join(self.h, int(wave), stream_ptr(stream)))
 
     def stats(self) -> dict:
         s = CacheStats()
-        ov = ctypes.c_int64()
-        _check(lib().expert_slot_cache_dev_stats(self.h, ctypes.byref(s), ctypes.byref(ov)))
-        d = {f: getattr(s, f) for f, _ in CacheStats._fields_}
-        d["overflow_steps"] = ov.value
-        return d
+        _check(lib().expert_slot_cache_dev_stats(self.h, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in CacheStats._fields_}
 
 
 # ------------------------------------------------------------- profile ---

@@ -12,10 +12,9 @@
 // while the step's hits compute. Nothing waits on the host, so a whole decode
 // step (routing, plan, copies, expert FFN, combine) can be one captured graph.
 //
-// Limit: a step that touches more experts than there are slots (the host
-// planner's several waves) is not planned: both tables come back all -1, no
-// copy is made, and the step is counted in `overflow_steps`. Size the pool for
-// the largest touched set, or use the host-planned cache.
+// A step that touches more experts than there are slots runs in waves, as on
+// the host: the plan writes one miss table per wave, and wave w's copies start
+// only after the caller's kernels of wave w-1 (they may reuse its slots).
 #include <climits>
 #include <cstring>
 #include <new>
@@ -31,14 +30,14 @@ constexpr int kPlanThreads = 1024;   // one thread per expert and per slot
 constexpr int kCopyThreads = 256;
 constexpr int kCopyBlocksPerBundle = 16;
 
-enum Ctl { kClock = 0, kSteps, kHits, kMisses, kEvictions, kOverflow, kCopies, kBad, kCtlN };
+enum Ctl { kClock = 0, kSteps, kHits, kMisses, kEvictions, kWaves, kStepHits, kCopies, kCtlN };
 
 struct DevState {
   int32_t* slot_of;   // [E]
   int32_t* owner;     // [S]
   int64_t* last;      // [E] recency stamps
   int64_t* ctl;       // [kCtlN]
-  int2* copies;       // [S] (expert, slot) of the last step's misses
+  int2* copies;       // [E] (expert, slot) of the last step's misses, in miss order (up to E of them)
 };
 
 // Rank of this thread's flag among the block's set flags (ascending thread
@@ -60,111 +59,118 @@ __device__ int block_rank(bool flag, int* wave_cnt, int* total) {
   return before + in_wave;
 }
 
+// Smallest 64-bit key over the block (every thread calls it; t >= S passes LLONG_MAX).
+__device__ long long block_min(long long v, long long* wave_min) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const long long o = __shfl_xor(v, off);
+    v = o < v ? o : v;
+  }
+  if ((threadIdx.x & 63) == 0) wave_min[threadIdx.x >> 6] = v;
+  __syncthreads();
+  long long m = wave_min[0];
+  for (int w = 1; w < kPlanThreads / 64; ++w) m = wave_min[w] < m ? wave_min[w] : m;
+  __syncthreads();
+  return m;
+}
+
+// Plans one step as the sequential LRU does: accesses in the order resident
+// touched experts (ascending id), then the others (ascending id), in waves of
+// at most S. A hit restamps its expert; a miss takes the lowest free slot, else
+// the slot whose expert has the oldest stamp (an expert used earlier in this
+// step can go in a later wave; one of the current wave cannot, it is newer).
+// Resident experts are all hits and all fall in wave 0 (there are at most S).
+// Outputs: hit_table[E] (wave 0's hits), miss_tables[w][E] for w < max_waves,
+// the copy list in miss order, and per-step counts in ctl.
 __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t* __restrict__ counts, DevState st,
-                                                                  int E, int S, int32_t* __restrict__ hit_table,
-                                                                  int32_t* __restrict__ miss_table) {
+                                                                  int E, int S, int max_waves,
+                                                                  int32_t* __restrict__ hit_table,
+                                                                  int32_t* __restrict__ miss_tables) {
   __shared__ int wave_cnt[kPlanThreads / 64];
-  __shared__ int victims[kPlanThreads];
-  __shared__ int old_owner[kPlanThreads];
-  __shared__ long long slot_last[kPlanThreads];
+  __shared__ long long wave_min[kPlanThreads / 64];
+  __shared__ int miss_list[kPlanThreads];     // missed experts, ascending
+  __shared__ int slot_owner[kPlanThreads];
+  __shared__ long long slot_stamp[kPlanThreads];
   const int t = threadIdx.x;
   bool touched = false, resident = false;
   int my_slot = -1;
   if (t < E) {
     touched = counts[t] > 0;
     my_slot = st.slot_of[t];
+    if (my_slot >= S) my_slot = -1;  // slots are < S in a consistent table; never index with another
     resident = my_slot >= 0;
   }
   int n_hit = 0, n_miss = 0;
   const int hit_rank = block_rank(touched && resident, wave_cnt, &n_hit);
   const int miss_rank = block_rank(touched && !resident, wave_cnt, &n_miss);
   const long long clock = st.ctl[kClock];
-  if (n_hit + n_miss > S) {  // block-uniform: more touched experts than slots
-    if (t < E) {
-      hit_table[t] = -1;
-      miss_table[t] = -1;
-    }
-    if (t == 0) {
-      st.ctl[kSteps] += 1;
-      st.ctl[kOverflow] += 1;
-      st.ctl[kCopies] = 0;
-    }
-    return;
-  }
-  // Victims in the order sequential LRU takes them: free slots ascending, then
-  // slots of experts this step does not touch, oldest first. Touched experts
-  // are never victims: misses <= S - hits = free + untouched-resident slots.
-  int owner = -1;
-  bool is_free = false, evictable = false;
-  long long lst = LLONG_MAX;
   if (t < S) {
-    owner = st.owner[t];
-    if (owner >= E) owner = -1;  // ids are < E in a consistent state; never index with another
-    is_free = owner < 0;
-    if (!is_free && counts[owner] == 0) {
-      evictable = true;
-      lst = st.last[owner];
+    int o = st.owner[t];
+    if (o >= E) o = -1;
+    slot_owner[t] = o;
+    slot_stamp[t] = o >= 0 ? (long long)st.last[o] : 0;
+  }
+  if (touched && !resident) miss_list[miss_rank] = t;
+  __syncthreads();
+  if (touched && resident) slot_stamp[my_slot] = clock + 1 + hit_rank;  // the hits, in access order
+  __syncthreads();
+  // misses one at a time: free slots (key = slot index) before occupied ones (key above all slot indices)
+  for (int j = 0; j < n_miss; ++j) {
+    long long key = LLONG_MAX;
+    if (t < S) key = slot_owner[t] < 0 ? (long long)t : (1ll << 40) + slot_stamp[t];
+    const long long m = block_min(key, wave_min);
+    if (t < S && key == m) {  // stamps and slot indices are distinct: one thread matches
+      const int e = miss_list[j];
+      const int wave = (n_hit + j) / S;
+      if (wave < max_waves) miss_tables[(size_t)wave * E + e] = t;
+      st.copies[j] = make_int2(e, t);
+      if (slot_owner[t] >= 0) atomicAdd(reinterpret_cast<unsigned long long*>(st.ctl + kEvictions), 1ull);
+      slot_owner[t] = e;
+      slot_stamp[t] = clock + 1 + n_hit + j;
     }
+    __syncthreads();
   }
-  int n_free = 0;
-  const int free_rank = block_rank(is_free, wave_cnt, &n_free);
-  if (t < S) {
-    slot_last[t] = lst;
-    old_owner[t] = owner;
-    victims[t] = -1;
-  }
-  __syncthreads();
-  if (is_free) victims[free_rank] = t;
-  if (evictable) {
-    int older = 0;  // stamps are distinct
-    for (int s = 0; s < S; ++s) older += slot_last[s] < lst ? 1 : 0;
-    victims[n_free + older] = t;
-  }
-  __syncthreads();
+  // tables: -1 for every expert a table does not name
   if (t < E) {
-    int hs = -1, ms = -1;
-    if (touched && resident) {
-      hs = my_slot;
-      st.last[t] = clock + 1 + hit_rank;
-    } else if (touched) {
-      const int slot = victims[miss_rank];
-      if (slot < 0 || slot >= S) {  // not reachable when the state is consistent; never index with it
-        atomicAdd(reinterpret_cast<unsigned long long*>(st.ctl + kBad), 1ull);
-        hit_table[t] = -1;
-        miss_table[t] = -1;
-        return;
-      }
-      const int old = old_owner[slot];
-      if (old >= 0) st.slot_of[old] = -1;  // an untouched expert: no other thread writes it
-      st.slot_of[t] = slot;
-      st.owner[slot] = t;
-      st.last[t] = clock + 1 + n_hit + miss_rank;
-      st.copies[miss_rank] = make_int2(t, slot);
-      ms = slot;
+    hit_table[t] = touched && resident ? my_slot : -1;
+    for (int w = 0; w < max_waves; ++w) {
+      const bool mine = touched && !resident && (n_hit + miss_rank) / S == w;
+      if (!mine) miss_tables[(size_t)w * E + t] = -1;
     }
-    hit_table[t] = hs;
-    miss_table[t] = ms;
+    if (my_slot >= 0 && slot_owner[my_slot] != t) st.slot_of[t] = -1;  // evicted this step
+  }
+  __syncthreads();
+  if (t < S) {
+    const int o = slot_owner[t];
+    st.owner[t] = o;
+    if (o >= 0) {
+      st.slot_of[o] = t;
+      st.last[o] = slot_stamp[t];
+    }
   }
   if (t == 0) {
     st.ctl[kClock] = clock + n_hit + n_miss;
     st.ctl[kSteps] += 1;
     st.ctl[kHits] += n_hit;
     st.ctl[kMisses] += n_miss;
-    st.ctl[kEvictions] += n_miss > n_free ? n_miss - n_free : 0;
+    st.ctl[kWaves] += (n_hit + n_miss + S - 1) / S;
+    st.ctl[kStepHits] = n_hit;
     st.ctl[kCopies] = n_miss;
   }
 }
 
-// Copies the last step's missed bundles host -> slot. blockIdx.y = copy index
-// (blocks past the step's copy count exit at once); the x blocks of one bundle
+// Copies wave `wave`'s missed bundles host -> slot: misses j with access
+// position n_hit + j in [wave*S, (wave+1)*S). blockIdx.y = copy within the wave
+// (blocks past the wave's copies exit at once); the x blocks of one bundle
 // stride over its 16-byte words, four loads in flight per thread.
 __global__ __launch_bounds__(kCopyThreads) void cache_copy_kernel(const int64_t* __restrict__ ctl,
                                                                  const int2* __restrict__ copies,
                                                                  const uint4* const* __restrict__ src,
                                                                  uint8_t* __restrict__ pool, int64_t stride,
-                                                                 int64_t n16, int n_experts, int n_slots) {
-  const int c = blockIdx.y;
-  if (c >= (int)ctl[kCopies]) return;
+                                                                 int64_t n16, int n_experts, int n_slots, int wave) {
+  const int n_hit = (int)ctl[kStepHits], n_miss = (int)ctl[kCopies];
+  const int j0 = max(0, wave * n_slots - n_hit), j1 = min(n_miss, (wave + 1) * n_slots - n_hit);
+  const int c = j0 + (int)blockIdx.y;
+  if (c >= j1) return;
   const int2 cp = copies[c];
   if (cp.x < 0 || cp.x >= n_experts || cp.y < 0 || cp.y >= n_slots) return;
   const uint4* __restrict__ from = src[cp.x];
@@ -187,7 +193,8 @@ struct expert_slot_cache_dev {
   moe_cache_cfg cfg{};
   int device = -1;
   hipStream_t side = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  int max_waves = 1;
+  std::vector<hipEvent_t> fork, join;  // per wave
   void* block = nullptr;  // device: state, copy list and source pointers
   DevState st{};
   const uint4** src = nullptr;
@@ -199,7 +206,7 @@ namespace {
 size_t state_bytes(int E, int S) {
   return align_up(sizeof(int32_t) * E, 256) + align_up(sizeof(int32_t) * S, 256) +
          align_up(sizeof(int64_t) * E, 256) + align_up(sizeof(int64_t) * kCtlN, 256) +
-         align_up(sizeof(int2) * S, 256) + align_up(sizeof(void*) * E, 256);
+         align_up(sizeof(int2) * E, 256) + align_up(sizeof(void*) * E, 256);
 }
 
 // Empty pool, zero counters (synchronous; not for use under capture).
@@ -217,8 +224,8 @@ moe_status init_state(expert_slot_cache_dev* c) {
 
 void destroy_dev(expert_slot_cache_dev* c) {
   if (c->side) (void)hipStreamSynchronize(c->side);
-  if (c->fork) (void)hipEventDestroy(c->fork);
-  if (c->join) (void)hipEventDestroy(c->join);
+  for (auto& ev : c->fork) if (ev) (void)hipEventDestroy(ev);
+  for (auto& ev : c->join) if (ev) (void)hipEventDestroy(ev);
   if (c->side) (void)hipStreamDestroy(c->side);
   if (c->block) (void)hipFree(c->block);
 }
@@ -275,8 +282,13 @@ extern "C" moe_status expert_slot_cache_dev_create(const moe_cache_cfg* cfg, exp
   const int E = k.n_experts, S = k.n_slots;
   if ((e = hipGetDevice(&c->device)) != hipSuccess) return fail("hipGetDevice", e);
   if ((e = hipStreamCreateWithFlags(&c->side, hipStreamNonBlocking)) != hipSuccess) return fail("hipStreamCreate", e);
-  if ((e = hipEventCreateWithFlags(&c->fork, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
-  if ((e = hipEventCreateWithFlags(&c->join, hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+  c->max_waves = (E + S - 1) / S;
+  c->fork.assign(c->max_waves, nullptr);
+  c->join.assign(c->max_waves, nullptr);
+  for (int w = 0; w < c->max_waves; ++w) {
+    if ((e = hipEventCreateWithFlags(&c->fork[w], hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+    if ((e = hipEventCreateWithFlags(&c->join[w], hipEventDisableTiming)) != hipSuccess) return fail("hipEventCreate", e);
+  }
   if ((e = hipMalloc(&c->block, state_bytes(E, S))) != hipSuccess) return fail("hipMalloc", e);
   char* p = static_cast<char*>(c->block);
   c->st.slot_of = reinterpret_cast<int32_t*>(p);
@@ -288,7 +300,7 @@ extern "C" moe_status expert_slot_cache_dev_create(const moe_cache_cfg* cfg, exp
   c->st.ctl = reinterpret_cast<int64_t*>(p);
   p += align_up(sizeof(int64_t) * kCtlN, 256);
   c->st.copies = reinterpret_cast<int2*>(p);
-  p += align_up(sizeof(int2) * S, 256);
+  p += align_up(sizeof(int2) * E, 256);
   c->src = reinterpret_cast<const uint4**>(p);
   if ((e = hipMemcpy(c->src, src.data(), sizeof(void*) * E, hipMemcpyHostToDevice)) != hipSuccess)
     return fail("hipMemcpy", e);
@@ -316,38 +328,52 @@ extern "C" moe_status expert_slot_cache_dev_reset(expert_slot_cache_dev* c) {
   return init_state(c);
 }
 
+extern "C" int32_t expert_slot_cache_dev_max_waves(const expert_slot_cache_dev* c) {
+  return c ? c->max_waves : 0;
+}
+
 extern "C" moe_status expert_slot_cache_dev_step(expert_slot_cache_dev* c, const int32_t* counts, void* stream,
-                                                 int32_t* hit_table, int32_t* miss_table) {
+                                                 int32_t* hit_table, int32_t* miss_tables) {
   clear_error();
-  MOE_REQUIRE(c && counts && hit_table && miss_table, MOE_EINVAL, "expert_slot_cache_dev_step: NULL argument");
-  MOE_REQUIRE(aligned(counts, 4) && aligned(hit_table, 4) && aligned(miss_table, 4), MOE_EINVAL,
+  MOE_REQUIRE(c && counts && hit_table && miss_tables, MOE_EINVAL, "expert_slot_cache_dev_step: NULL argument");
+  MOE_REQUIRE(aligned(counts, 4) && aligned(hit_table, 4) && aligned(miss_tables, 4), MOE_EINVAL,
               "expert_slot_cache_dev_step: misaligned table");
   if (moe_status s = check_launch("expert_slot_cache_dev_step (earlier work)")) return s;
-  hipStream_t s = as_stream(stream);
-  const int E = c->cfg.n_experts, S = c->cfg.n_slots;
-  hipLaunchKernelGGL(cache_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, counts, c->st, E, S, hit_table, miss_table);
+  hipLaunchKernelGGL(cache_plan_kernel, dim3(1), dim3(kPlanThreads), 0, as_stream(stream), counts, c->st,
+                     c->cfg.n_experts, c->cfg.n_slots, c->max_waves, hit_table, miss_tables);
   if (moe_status r = check_launch("cache_plan_kernel")) return r;
-  MOE_HIP(hipEventRecord(c->fork, s));
-  MOE_HIP(hipStreamWaitEvent(c->side, c->fork, 0));
-  hipLaunchKernelGGL(cache_copy_kernel, dim3(kCopyBlocksPerBundle, S), dim3(kCopyThreads), 0, c->side,
-                     c->st.ctl, c->st.copies, c->src, static_cast<uint8_t*>(c->cfg.pool), (int64_t)c->cfg.slot_stride,
-                     (int64_t)(c->cfg.bundle_bytes / 16), E, S);
-  if (moe_status r = check_launch("cache_copy_kernel")) return r;
-  MOE_HIP(hipEventRecord(c->join, c->side));
   c->stepped = true;
   return MOE_OK;
 }
 
-extern "C" moe_status expert_slot_cache_dev_join(expert_slot_cache_dev* c, void* stream) {
+extern "C" moe_status expert_slot_cache_dev_copy(expert_slot_cache_dev* c, int32_t wave, void* stream) {
   clear_error();
-  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_join: NULL cache");
-  MOE_REQUIRE(c->stepped, MOE_ESTATE, "expert_slot_cache_dev_join: no step was issued");
-  MOE_HIP(hipStreamWaitEvent(as_stream(stream), c->join, 0));
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_copy: NULL cache");
+  MOE_REQUIRE(c->stepped, MOE_ESTATE, "expert_slot_cache_dev_copy: no step was planned");
+  MOE_REQUIRE(wave >= 0 && wave < c->max_waves, MOE_EINVAL, "expert_slot_cache_dev_copy: wave %d outside [0, %d)",
+              wave, c->max_waves);
+  const int E = c->cfg.n_experts, S = c->cfg.n_slots;
+  MOE_HIP(hipEventRecord(c->fork[wave], as_stream(stream)));
+  MOE_HIP(hipStreamWaitEvent(c->side, c->fork[wave], 0));
+  hipLaunchKernelGGL(cache_copy_kernel, dim3(kCopyBlocksPerBundle, S), dim3(kCopyThreads), 0, c->side,
+                     c->st.ctl, c->st.copies, c->src, static_cast<uint8_t*>(c->cfg.pool), (int64_t)c->cfg.slot_stride,
+                     (int64_t)(c->cfg.bundle_bytes / 16), E, S, (int)wave);
+  if (moe_status r = check_launch("cache_copy_kernel")) return r;
+  MOE_HIP(hipEventRecord(c->join[wave], c->side));
   return MOE_OK;
 }
 
-extern "C" moe_status expert_slot_cache_dev_stats(expert_slot_cache_dev* c, moe_cache_stats* out,
-                                                  int64_t* overflow_steps) {
+extern "C" moe_status expert_slot_cache_dev_join(expert_slot_cache_dev* c, int32_t wave, void* stream) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_join: NULL cache");
+  MOE_REQUIRE(c->stepped, MOE_ESTATE, "expert_slot_cache_dev_join: no step was planned");
+  MOE_REQUIRE(wave >= 0 && wave < c->max_waves, MOE_EINVAL, "expert_slot_cache_dev_join: wave %d outside [0, %d)",
+              wave, c->max_waves);
+  MOE_HIP(hipStreamWaitEvent(as_stream(stream), c->join[wave], 0));
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_dev_stats(expert_slot_cache_dev* c, moe_cache_stats* out) {
   clear_error();
   MOE_REQUIRE(c && out, MOE_EINVAL, "expert_slot_cache_dev_stats: NULL argument");
   MOE_HIP(hipDeviceSynchronize());
@@ -358,10 +384,7 @@ extern "C" moe_status expert_slot_cache_dev_stats(expert_slot_cache_dev* c, moe_
   out->hits = ctl[kHits];
   out->misses = ctl[kMisses];
   out->evictions = ctl[kEvictions];
-  out->waves = ctl[kSteps] - ctl[kOverflow];
+  out->waves = ctl[kWaves];
   out->h2d_bytes = ctl[kMisses] * c->cfg.bundle_bytes;
-  if (overflow_steps) *overflow_steps = ctl[kOverflow];
-  MOE_REQUIRE(ctl[kBad] == 0, MOE_ESTATE, "expert_slot_cache_dev_stats: the device plan found no victim slot %lld times",
-              (long long)ctl[kBad]);
   return MOE_OK;
 }

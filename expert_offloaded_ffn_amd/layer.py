@@ -138,11 +138,12 @@ class MoELayer:
             self.slot_pool = torch.empty(pool_slots, stride, dtype=torch.uint8, device=self.device)
             self.slot_table = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
             if device_plan:
-                self.miss_slot_table = torch.full((self.E,), -1, dtype=torch.int32, device=self.device)
                 self.cache_dev = B.DeviceSlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles,
                                                    self.slot_pool)
-                self.miss_table = B.expert_table(self.slot_pool, stride, self.miss_slot_table, self.E, self.d,
-                                                 self.F, self.w_code)
+                nw = self.cache_dev.max_waves
+                self.miss_slot_tables = torch.full((nw, self.E), -1, dtype=torch.int32, device=self.device)
+                self.miss_tables = [B.expert_table(self.slot_pool, stride, self.miss_slot_tables[w], self.E, self.d,
+                                                   self.F, self.w_code) for w in range(nw)]
             else:
                 self.cache = B.SlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles, self.slot_pool,
                                          blocking=blocking)
@@ -259,13 +260,17 @@ class MoELayer:
         elif self.cache_dev is not None:
             # plan on the device; the hits run while the misses' copy kernel reads host memory
             fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
-            self.cache_dev.step(r["counts"], self.slot_table, self.miss_slot_table, stream=main)
-            for part, table in enumerate((self.table, self.miss_table)):
-                if part == 1:
-                    self.cache_dev.join(stream=main)
-                B.grouped_ffn(table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
-                              a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws, stream=main)
-            waves = 1
+            self.cache_dev.step(r["counts"], self.slot_table, self.miss_slot_tables, stream=main)
+            ffn = lambda table: B.grouped_ffn(table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
+                                              a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws,
+                                              stream=main)
+            for w, miss_table in enumerate(self.miss_tables):
+                self.cache_dev.copy(w, stream=main)
+                if w == 0:
+                    ffn(self.table)
+                self.cache_dev.join(w, stream=main)
+                ffn(miss_table)
+            waves = len(self.miss_tables)
         elif self.cache is None:
             fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
             B.grouped_ffn(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,

@@ -466,38 +466,47 @@ moe_status expert_slot_cache_stats(const expert_slot_cache* c, moe_cache_stats* 
  * 8GB GPUs", section "Technical Insight"; "NovaLLM", section 3, removes launch
  * overhead with graph capture). Same readings as expert_slot_cache: per step
  * the touched experts (counts > 0) are accessed resident-first, then the
- * others, each in ascending id; LRU with the lowest free slot first.
+ * others, each in ascending id, in waves of at most n_slots accesses; LRU with
+ * the lowest free slot first. Resident experts are all hits of wave 0.
  *
- * expert_slot_cache_dev_step enqueues on `stream` one plan kernel (reads
- * counts[E], updates the device-resident table, writes hit_table[E] = slot of
- * each touched resident expert and miss_table[E] = slot of each touched expert
- * being loaded, -1 elsewhere), then, on the cache's side stream after that
- * kernel, one copy kernel that reads the missed bundles from pinned host memory
- * (its device mapping) and writes their slots. The caller runs
- * moe_grouped_ffn over hit_table, calls expert_slot_cache_dev_join (`stream`
- * waits for the copies), then runs it over miss_table. All of it may be
- * captured into one graph; the join must be captured too (it rejoins the side
- * stream). Steps on one cache must be issued on one stream, in order.
- * A step touching more than n_slots experts is not planned (both tables all
- * -1, no copies; counted in overflow_steps): size the pool for the largest
- * touched set. Slots, bundles and the pool are caller memory as in
- * moe_cache_cfg (blocking = dry_run = 0; n_experts, n_slots <= 1024;
- * bundle_bytes a multiple of 16; bundles 16-byte aligned).
- * The library allocates the device-side table, one side stream and two events
- * in create. stats and reset synchronise the device.
- * Errors: MOE_EINVAL (sizes, NULL, a bundle not in mapped pinned memory),
- *  MOE_ECAPACITY (slots), MOE_ESTATE (join before any step; an inconsistent
- *  device table, reported by stats), MOE_EHIP. */
+ * Per step, all on `stream` unless said otherwise:
+ *  expert_slot_cache_dev_step: one plan kernel. Reads counts[E], updates the
+ *    device-resident table and writes hit_table[E] (slot of each wave-0 hit,
+ *    else -1) and miss_tables[w*E + e] for w < expert_slot_cache_dev_max_waves
+ *    (slot of expert e if it is loaded in wave w, else -1).
+ *  for each wave w < max_waves (waves the step does not need cost one empty
+ *  copy launch and the caller's launches over an all -1 table):
+ *    expert_slot_cache_dev_copy(w): the cache's side stream waits for the work
+ *      enqueued on `stream` so far (so wave w-1's kernels are done before its
+ *      slots are reused), then one copy kernel reads wave w's missed bundles
+ *      from pinned host memory (their device mapping) into their slots;
+ *    (w = 0) the caller runs moe_grouped_ffn over hit_table, concurrent with
+ *      the copies;
+ *    expert_slot_cache_dev_join(w): `stream` waits for wave w's copies;
+ *    the caller runs moe_grouped_ffn over miss_tables + w*E.
+ * All of it may be captured into one graph (the join of every copied wave
+ * must be captured too: it rejoins the side stream). Steps on one cache are
+ * issued on one stream, in order.
+ * cfg: blocking = dry_run = 0; n_experts, n_slots <= 1024; bundle_bytes a
+ * multiple of 16; bundles in pinned host memory, 16-byte aligned; the pool and
+ * the tables are caller memory. The library allocates the device-side table,
+ * one side stream and two events per wave in create. stats and reset
+ * synchronise the device.
+ * Errors: MOE_EINVAL (sizes, NULL, a bundle without a device mapping, a wave
+ *  out of range), MOE_ECAPACITY (slots), MOE_ESTATE (copy or join before any
+ *  step), MOE_EHIP. */
 typedef struct expert_slot_cache_dev expert_slot_cache_dev;
 moe_status expert_slot_cache_dev_create(const moe_cache_cfg* cfg, expert_slot_cache_dev** out);
 moe_status expert_slot_cache_dev_destroy(expert_slot_cache_dev* c);
 moe_status expert_slot_cache_dev_reset(expert_slot_cache_dev* c);
+int32_t expert_slot_cache_dev_max_waves(const expert_slot_cache_dev* c);   /* ceil(n_experts / n_slots) */
 moe_status expert_slot_cache_dev_step(expert_slot_cache_dev* c, const int32_t* counts, void* stream,
-                                      int32_t* hit_table, int32_t* miss_table);
-moe_status expert_slot_cache_dev_join(expert_slot_cache_dev* c, void* stream);
-/* hits, misses, evictions, steps; waves = planned steps; h2d_bytes = misses x
- * bundle_bytes; copy_ms and the prefetch fields are 0. */
-moe_status expert_slot_cache_dev_stats(expert_slot_cache_dev* c, moe_cache_stats* out, int64_t* overflow_steps);
+                                      int32_t* hit_table, int32_t* miss_tables);
+moe_status expert_slot_cache_dev_copy(expert_slot_cache_dev* c, int32_t wave, void* stream);
+moe_status expert_slot_cache_dev_join(expert_slot_cache_dev* c, int32_t wave, void* stream);
+/* hits, misses, evictions, steps, waves; h2d_bytes = misses x bundle_bytes;
+ * copy_ms and the prefetch fields are 0. */
+moe_status expert_slot_cache_dev_stats(expert_slot_cache_dev* c, moe_cache_stats* out);
 
 /* ---------------------------------------------------------------- profile --
  * Optional per-kernel timing for measurement tools (not part of the layer's

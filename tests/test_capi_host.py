@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def _declared_functions():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?(?:moe_status|size_t|char\s*\*|const\s+char\s*\*)\s*\**\s*(\w+)\s*\(",
+    names = re.findall(r"^\s*(?:const\s+)?(?:moe_status|size_t|int32_t|char\s*\*|const\s+char\s*\*)\s*\**\s*(\w+)\s*\(",
                        src, flags=re.M)
     names += re.findall(r"^\s*const char\*\s+(\w+)\s*\(", src, flags=re.M)
     return sorted(set(names))
