@@ -113,8 +113,11 @@ def cpu_baseline(cfg, w, sample_tokens):
 
 def bench_offload(args, torch, B, synth, MoELayer):
     """Expert-offload decode: T tokens per step through an n_slots HBM slot pool fed from pinned host
-    bundles, Zipf-biased routing re-drawn every zipf_epoch steps. The same steps run three ways: all
-    experts resident (compute time), slot pool with overlapped copies, slot pool in blocking mode."""
+    bundles, Zipf-biased routing re-drawn every zipf_epoch steps. The same steps run these ways: all
+    experts resident (compute time), slot pool with overlapped copies, slot pool in blocking mode,
+    and the pool planned on the device (copy kernels, no host synchronisation), eager and as one
+    graph replay per step. The device-planned graph replays start from an empty pool, as the
+    others do."""
     from expert_offloaded_ffn_amd.layer import W_CODE
     cfg = synth.get_config(args.workload)
     if args.tokens:
@@ -155,13 +158,40 @@ def bench_offload(args, torch, B, synth, MoELayer):
         lay.cache.close()
         del lay
         torch.cuda.empty_cache()
-    o = out["overlapped"]
+    # the device-planned pool: no host synchronisation; eager, then every step one graph replay
+    lay = MoELayer(cfg, router=router, experts=experts, pool_slots=cfg.n_slots, device_plan=True, threads=16)
+    t_wall = run(lay)
+    st = lay.cache_dev.stats()
+    lay.cache_dev.reset()
+    x_static, lb_static = xs[0].clone(), lbs[0].clone()
+    graph, _ = lay.capture(x_static, lb_static)
+    lay.cache_dev.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        x_static.copy_(xs[s])
+        lb_static.copy_(lbs[s])
+        graph.replay()
+    torch.cuda.synchronize()
+    t_graph = time.perf_counter() - t0
+    sg = lay.cache_dev.stats()
+    for mode, t, stt in (("device_plan", t_wall, st), ("device_plan_graph", t_graph, sg)):
+        acc = stt["hits"] + stt["misses"]
+        out[mode] = {"wall_s": round(t, 4), "tokens_per_s": round(cfg.T * steps / t, 1),
+                     "hit_rate": round(stt["hits"] / max(acc, 1), 4), "hits": stt["hits"], "misses": stt["misses"],
+                     "evictions": stt["evictions"], "waves": stt["waves"], "h2d_bytes": stt["h2d_bytes"],
+                     "h2d_GBps_wall": round(stt["h2d_bytes"] / t / 1e9, 2)}
+    lay.cache_dev.close()
+    del lay, graph
+    torch.cuda.empty_cache()
+    best = max((m for m in out if m != "blocking"), key=lambda m: out[m]["tokens_per_s"])
+    o = out[best]
     result = {
         "metric": METRIC, "value": o["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 0,
         "ms_per_step": round(o["wall_s"] / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; Zipf(1.1) log-prior re-drawn every 64 steps)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
-                   "d_ff": cfg.F, "n_slots": cfg.n_slots, "weights": cfg.dtype,
+                   "d_ff": cfg.F, "n_slots": cfg.n_slots, "weights": cfg.dtype, "mode": best,
                    "bundle_bytes": B.bundle_bytes(cfg.d, cfg.F, W_CODE[cfg.dtype])},
         "resident_compute_s": round(t_comp, 4), "offload": out,
     }
