@@ -206,7 +206,8 @@ def bench_stack(args, torch, B, synth, MoELayer):
     layer touched in the previous step, "zipf" the top-N experts of its routing prior for the step
     (the synthetic stand-in for a shadow router). The layers share expert weights (distinct cache
     entries, real copies) and take independent inputs; the same steps also run with every expert
-    resident (compute time) and with no prefetch."""
+    resident (compute time) and with no prefetch, under plain LRU and under the layer order (victims
+    from the layer that runs furthest ahead first)."""
     from expert_offloaded_ffn_amd.layer import W_CODE, SharedSlotPool, pack_bundles
     cfg = synth.get_config(args.workload)
     if args.tokens:
@@ -247,14 +248,16 @@ def bench_stack(args, torch, B, synth, MoELayer):
     torch.cuda.empty_cache()
     bundles = pack_bundles(cfg, experts, cfg.d, cfg.F, pin=True, threads=16)
     out = {}
-    for predictor in ["none"] + [p for p in args.prefetch.split(",") if p != "none"]:
-        pool = SharedSlotPool([bundles] * L, n_slots, cfg.d, cfg.F, W_CODE[cfg.dtype])
+    predictors = ["none"] + [p for p in args.prefetch.split(",") if p and p != "none"]
+    for policy, predictor in [(pol, pr) for pol in args.policies.split(",") for pr in predictors]:
+        key = f"{policy}/{predictor}"
+        pool = SharedSlotPool([bundles] * L, n_slots, cfg.d, cfg.F, W_CODE[cfg.dtype], layer_order=policy == "layer")
         layers = [MoELayer(c, router=r, experts=None, shared_pool=pool, layer_index=l)
                   for l, (c, r) in enumerate(zip(cfgs, routers))]
         t_wall = run(layers, pool, predictor)
         st = pool.cache.stats()
         acc = st["hits"] + st["misses"]
-        out[predictor] = {"wall_s": round(t_wall, 4), "tokens_per_s": round(cfg.T * steps / t_wall, 1),
+        out[key] = {"wall_s": round(t_wall, 4), "tokens_per_s": round(cfg.T * steps / t_wall, 1),
                           "ms_per_step": round(t_wall / steps * 1e3, 3),
                           "hit_rate": round(st["hits"] / max(acc, 1), 4), "hits": st["hits"],
                           "misses": st["misses"], "prefetches": st["prefetches"],
@@ -262,7 +265,7 @@ def bench_stack(args, torch, B, synth, MoELayer):
                           "prefetch_accuracy": round(st["prefetch_used"] / max(st["prefetches"], 1), 4),
                           "h2d_GB": round(st["h2d_bytes"] / 1e9, 3),
                           "h2d_GBps_wall": round(st["h2d_bytes"] / t_wall / 1e9, 2)}
-        log(f"[bench] stack predictor={predictor}: {out[predictor]}")
+        log(f"[bench] stack {key}: {out[key]}")
         pool.cache.close()
         del layers, pool
         torch.cuda.empty_cache()
@@ -401,6 +404,9 @@ def main():
                     help="stack: predictors to run besides none (prev = the layer's previous step, "
                          "zipf = top-N of its routing prior)")
     ap.add_argument("--prefetch-n", type=int, default=16, help="stack: experts the zipf predictor names")
+    ap.add_argument("--policies", default="lru,layer",
+                    help="stack: victim choices to run (lru = plain LRU, layer = the layer that runs furthest "
+                         "ahead first, then LRU)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (HBM ceiling and the "
                          "reference for the FETCH_SIZE/WRITE_SIZE counters), then exit")

@@ -116,6 +116,7 @@ EXPORTS = {
     "expert_slot_cache_wave": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_release": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    "expert_slot_cache_set_layers": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
     "expert_slot_cache_prefetch": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_wave_plan": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(CacheEntry),
@@ -425,6 +426,11 @@ class SlotCache:
 
     def release(self, w, stream=None):
         _check(lib().expert_slot_cache_release(self.h, w, stream_ptr(stream)))
+
+    def set_layers(self, n_layers: int):
+        """Entries are n_layers layer-major groups run in cyclic order: evict from the layer that
+        runs furthest ahead, then LRU (1 = plain LRU)."""
+        _check(lib().expert_slot_cache_set_layers(self.h, int(n_layers)))
 
     def prefetch(self, experts) -> int:
         """Copies the listed (predicted) experts ahead of their step; returns the copies issued."""

@@ -48,6 +48,9 @@ struct expert_slot_cache {
   std::vector<int64_t> last;
   int64_t clock = 0;
   int64_t step_clock = 0;                // clock before the last planned step's first access
+  int32_t n_layers = 1;                  // > 1: entries are layer-major groups run in cyclic order
+  int32_t step_layer = 0;                // layer of the last planned step's entries
+  int64_t wave_clock = 0;                // clock before the current wave's first access
   std::vector<char> prefetched;          // per expert: brought in by prefetch, not yet used by a step
   std::vector<std::vector<moe_cache_entry>> waves;
   bool planned = false;
@@ -78,9 +81,30 @@ void plan_reset(expert_slot_cache* c) {
   c->prefetched.assign(E, 0);
   c->clock = 0;
   c->step_clock = 0;
+  c->step_layer = 0;
+  c->wave_clock = 0;
   c->waves.clear();
   c->planned = false;
   c->st = moe_cache_stats{};
+}
+
+// Victim order: with a layer order, the entry whose layer runs furthest after
+// the current one first (distance (layer - current - 1) mod L, largest first),
+// then the least recently used; plain LRU otherwise. `ok` filters candidates.
+template <class Ok>
+int pick_victim(const expert_slot_cache* c, Ok ok) {
+  const int L = c->n_layers, per = c->cfg.n_experts / L;
+  int victim = -1, vdist = -1;
+  for (int s = 0; s < c->cfg.n_slots; ++s) {
+    const int v = c->owner[s];
+    if (v < 0 || !ok(v)) continue;
+    const int dist = L > 1 ? ((v / per - c->step_layer - 1) % L + L) % L : 0;
+    if (victim < 0 || dist > vdist || (dist == vdist && c->last[v] < c->last[victim])) {
+      victim = v;
+      vdist = dist;
+    }
+  }
+  return victim;
 }
 
 moe_cache_entry access(expert_slot_cache* c, int e) {
@@ -102,11 +126,8 @@ moe_cache_entry access(expert_slot_cache* c, int e) {
   for (int s = 0; s < c->cfg.n_slots; ++s)
     if (c->owner[s] < 0) { slot = s; break; }
   if (slot < 0) {
-    int victim = -1;
-    for (int s = 0; s < c->cfg.n_slots; ++s) {
-      const int v = c->owner[s];
-      if (victim < 0 || c->last[v] < c->last[victim]) victim = v;
-    }
+    // never an entry of the wave being formed (plain LRU cannot pick one: they are the newest)
+    const int victim = pick_victim(c, [&](int v) { return c->last[v] <= c->wave_clock; });
     slot = c->slot_of[victim];
     c->slot_of[victim] = -1;
     c->prefetched[victim] = 0;
@@ -137,12 +158,7 @@ moe_cache_entry prefetch_one(expert_slot_cache* c, int e) {
   for (int s = 0; s < c->cfg.n_slots; ++s)
     if (c->owner[s] < 0) { slot = s; break; }
   if (slot < 0) {
-    int victim = -1;
-    for (int s = 0; s < c->cfg.n_slots; ++s) {
-      const int v = c->owner[s];
-      if (c->last[v] > c->step_clock) continue;
-      if (victim < 0 || c->last[v] < c->last[victim]) victim = v;
-    }
+    const int victim = pick_victim(c, [&](int v) { return c->last[v] <= c->step_clock; });
     if (victim < 0) {
       r.expert = -1;
       return r;
@@ -163,8 +179,19 @@ moe_cache_entry prefetch_one(expert_slot_cache* c, int e) {
   return r;
 }
 
-void plan_step(expert_slot_cache* c, const int32_t* counts) {
+moe_status plan_step(expert_slot_cache* c, const int32_t* counts) {
   const int E = c->cfg.n_experts, S = c->cfg.n_slots;
+  if (c->n_layers > 1) {
+    const int per = E / c->n_layers;
+    int layer = -1;
+    for (int e = 0; e < E; ++e) {
+      if (counts[e] <= 0) continue;
+      MOE_REQUIRE(layer < 0 || e / per == layer, MOE_EINVAL,
+                  "expert_slot_cache: a step touches entries of layers %d and %d", layer, e / per);
+      layer = e / per;
+    }
+    if (layer >= 0) c->step_layer = layer;
+  }
   c->step_clock = c->clock;
   std::vector<int> order;
   for (int e = 0; e < E; ++e)
@@ -173,6 +200,7 @@ void plan_step(expert_slot_cache* c, const int32_t* counts) {
     if (counts[e] > 0 && c->slot_of[e] < 0) order.push_back(e);
   c->waves.clear();
   for (size_t w0 = 0; w0 < order.size(); w0 += S) {
+    c->wave_clock = c->clock;
     std::vector<moe_cache_entry> wave;
     for (size_t i = w0; i < std::min(order.size(), w0 + S); ++i) wave.push_back(access(c, order[i]));
     c->waves.push_back(std::move(wave));
@@ -180,6 +208,7 @@ void plan_step(expert_slot_cache* c, const int32_t* counts) {
   c->st.waves += (int64_t)c->waves.size();
   c->st.steps += 1;
   c->planned = true;
+  return MOE_OK;
 }
 
 // Adds finished copy spans to the stats (events of earlier steps).
@@ -302,7 +331,7 @@ extern "C" moe_status expert_slot_cache_reset(expert_slot_cache* c) {
 extern "C" moe_status expert_slot_cache_plan_host(expert_slot_cache* c, const int32_t* counts_host, int32_t* n_waves_out) {
   clear_error();
   MOE_REQUIRE(c && counts_host, MOE_EINVAL, "expert_slot_cache_plan_host: NULL argument");
-  plan_step(c, counts_host);
+  if (moe_status st = plan_step(c, counts_host)) return st;
   if (n_waves_out) *n_waves_out = (int32_t)c->waves.size();
   return MOE_OK;
 }
@@ -319,7 +348,7 @@ extern "C" moe_status expert_slot_cache_acquire(expert_slot_cache* c, const int3
   c->st.d2h_bytes += (int64_t)sizeof(int32_t) * E;
   collect_timing(c, false);
   std::fill(c->wave_copied.begin(), c->wave_copied.end(), 0);
-  plan_step(c, c->counts_pinned);
+  if (moe_status st = plan_step(c, c->counts_pinned)) return st;
   if (n_waves_out) *n_waves_out = (int32_t)c->waves.size();
   return MOE_OK;
 }
@@ -407,6 +436,15 @@ extern "C" moe_status expert_slot_cache_release(expert_slot_cache* c, int32_t wa
     MOE_HIP(hipEventRecord(c->last_read[en.slot], s));
     c->last_read_valid[en.slot] = 1;
   }
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_set_layers(expert_slot_cache* c, int32_t n_layers) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_set_layers: NULL cache");
+  MOE_REQUIRE(n_layers >= 1 && c->cfg.n_experts % n_layers == 0, MOE_EINVAL,
+              "expert_slot_cache_set_layers: n_layers=%d must divide n_experts=%d", n_layers, c->cfg.n_experts);
+  c->n_layers = n_layers;
   return MOE_OK;
 }
 

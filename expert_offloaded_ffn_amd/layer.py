@@ -63,9 +63,11 @@ class SharedSlotPool:
     """One expert slot pool, and one LRU over it, for the layers of a stack: expert e of layer l
     is entry l*E + e of the cache, so the layers compete for the same HBM slots and one layer's
     step can prefetch the next layer's predicted experts (expert_slot_cache_prefetch).
-    bundles_per_layer: [L] lists of E pinned host bundles (layers may share bundle tensors)."""
+    bundles_per_layer: [L] lists of E pinned host bundles (layers may share bundle tensors).
+    layer_order: victims from the layer that runs furthest ahead, then LRU (expert_slot_cache_set_layers);
+    else plain LRU."""
 
-    def __init__(self, bundles_per_layer, n_slots, d, F, w_dtype, device="cuda"):
+    def __init__(self, bundles_per_layer, n_slots, d, F, w_dtype, device="cuda", layer_order=False):
         self.L = len(bundles_per_layer)
         self.E = len(bundles_per_layer[0])
         self.d, self.F, self.w_code = d, F, w_dtype
@@ -77,6 +79,8 @@ class SharedSlotPool:
         self.slot_table = torch.full((self.L * self.E,), -1, dtype=torch.int32, device=self.device)
         self.counts = torch.zeros(self.L * self.E, dtype=torch.int32, device=self.device)
         self.cache = B.SlotCache(self.L * self.E, n_slots, self.bundle_bytes, self.stride, flat, self.slot_pool)
+        if layer_order:   # evict from the layer that runs furthest ahead, then LRU
+            self.cache.set_layers(self.L)
 
     def table(self, layer: int):
         """The expert table of one layer: its E entries of the shared slot table."""

@@ -424,6 +424,22 @@ moe_status expert_slot_cache_plan_host(expert_slot_cache* c, const int32_t* coun
 moe_status expert_slot_cache_wave(expert_slot_cache* c, int32_t wave, int32_t part, void* stream,
                                   int32_t* slot_of_expert, int32_t* n_experts_in_part);
 moe_status expert_slot_cache_release(expert_slot_cache* c, int32_t wave, void* stream);
+/* Victim order for a pool shared by the layers of a stack. With n_layers > 1
+ * the cache's entries are n_layers layer-major groups of n_experts / n_layers
+ * (entry l * (n_experts / n_layers) + e is expert e of layer l), the layers run
+ * in the cyclic order 0, 1, ..., n_layers - 1, 0, ..., and every step touches
+ * entries of one layer only (else acquire / plan_host fail with MOE_EINVAL).
+ * A miss (or a prefetch) then evicts, among the entries it may evict, one of
+ * the layer whose next step is furthest away, (layer - current - 1) mod
+ * n_layers largest, and within that layer the least recently used one.
+ * n_layers = 1 (the default) is plain LRU. This goes beyond the pages, whose
+ * cache is plain LRU and which name that as its weakness ("Running 35B MoE
+ * Models on 8GB GPUs", section "Gotcha"): a stack that cycles through more
+ * experts than the pool holds makes LRU evict exactly the entries needed next.
+ * Host planner only (not expert_slot_cache_dev).
+ * Errors: MOE_EINVAL (n_layers < 1 or not a divisor of n_experts). */
+moe_status expert_slot_cache_set_layers(expert_slot_cache* c, int32_t n_layers);
+
 /* Prefetch of predicted experts ahead of the step that routes to them.
  * The pages: a background reader fetches the next layer while the current one
  * computes ("NovaLLM: Running Massive MoE Models Fully In-Memory", section 3,

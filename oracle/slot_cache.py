@@ -41,6 +41,14 @@ list). Readings taken:
   rest of the prediction is dropped;
 * a prefetch is neither a hit nor a miss; a later step that touches a
   prefetched expert before it is evicted counts a hit and a "prefetch used".
+
+Layer order (beyond the pages, whose cache is plain LRU and which call that
+naive, "Running 35B MoE Models on 8GB GPUs", section "Gotcha"): the entries may
+be L layer-major groups of a stack whose layers run in the cyclic order
+0..L-1. A step then touches one layer's entries, and every victim choice (a
+miss's or a prefetch's) takes, among the entries it may evict, one of the layer
+whose next step comes last, i.e. the largest (layer - current - 1) mod L, the
+least recently used within it. With L = 1 this is plain LRU.
 """
 from __future__ import annotations
 
@@ -72,10 +80,10 @@ class CacheStats:
 
 
 class LRUSlotCache:
-    def __init__(self, n_experts: int, n_slots: int):
-        if n_slots < 1 or n_experts < 1:
-            raise ValueError("need at least one expert and one slot")
-        self.E, self.S = n_experts, n_slots
+    def __init__(self, n_experts: int, n_slots: int, n_layers: int = 1):
+        if n_slots < 1 or n_experts < 1 or n_experts % n_layers:
+            raise ValueError("need at least one expert and one slot, and layers that divide the entries")
+        self.E, self.S, self.L = n_experts, n_slots, n_layers
         self.reset()
 
     def reset(self):
@@ -83,6 +91,7 @@ class LRUSlotCache:
         self.owner = [-1] * self.S
         self.last = [0] * self.E
         self.clock = 0
+        self.layer = 0                # layer of the most recent step
         self.step_touched = set()     # experts the most recent step accessed, or predicted since
         self.from_prefetch = set()    # prefetched, not yet touched by a step
         self.stats = CacheStats()
@@ -90,7 +99,13 @@ class LRUSlotCache:
     def resident(self):
         return [e for e in range(self.E) if self.slot_of[e] >= 0]
 
-    def _access(self, e: int) -> WaveEntry:
+    def _victim(self, candidates):
+        """The layer whose next step comes last, then the least recently used."""
+        per = self.E // self.L
+        ahead = lambda v: (v // per - self.layer - 1) % self.L
+        return max(candidates, key=lambda v: (ahead(v), -self.last[v]))
+
+    def _access(self, e: int, wave) -> WaveEntry:
         self.clock += 1
         self.step_touched.add(e)
         if self.slot_of[e] >= 0:
@@ -106,7 +121,7 @@ class LRUSlotCache:
         if free:
             slot = free[0]
         else:
-            evicted = min(self.resident(), key=lambda v: self.last[v])
+            evicted = self._victim([v for v in self.resident() if v not in wave])
             slot = self.slot_of[evicted]
             self.slot_of[evicted] = -1
             self.from_prefetch.discard(evicted)
@@ -118,11 +133,17 @@ class LRUSlotCache:
 
     def step(self, touched_experts) -> StepPlan:
         touched = sorted(set(int(e) for e in touched_experts))
+        layers = {e // (self.E // self.L) for e in touched}
+        if len(layers) > 1:
+            raise ValueError("a step touches entries of several layers")
+        if layers:
+            self.layer = layers.pop()
         self.step_touched = set()
         order = [e for e in touched if self.slot_of[e] >= 0] + [e for e in touched if self.slot_of[e] < 0]
         plan = StepPlan()
         for w0 in range(0, len(order), self.S):
-            plan.waves.append([self._access(e) for e in order[w0:w0 + self.S]])
+            wave = order[w0:w0 + self.S]
+            plan.waves.append([self._access(e, wave) for e in wave])
         self.stats.waves += len(plan.waves)
         self.stats.steps += 1
         return plan
@@ -145,7 +166,7 @@ class LRUSlotCache:
                 candidates = [v for v in self.resident() if v not in self.step_touched]
                 if not candidates:
                     break
-                evicted = min(candidates, key=lambda v: self.last[v])
+                evicted = self._victim(candidates)
                 slot = self.slot_of[evicted]
                 self.slot_of[evicted] = -1
                 self.from_prefetch.discard(evicted)

@@ -334,6 +334,39 @@ def test_planner_prefetch_matches_oracle_simulation(E, S, k, T):
     blocking.close()
 
 
+@pytest.mark.parametrize("L,per,S,k,T", [(2, 8, 5, 2, 2), (4, 32, 40, 4, 4), (4, 128, 128, 8, 32)])
+def test_planner_layer_order_matches_oracle_simulation(L, per, S, k, T):
+    """A stack's cyclic layer steps, with and without predictions, under the layer order."""
+    rng = np.random.default_rng(L * per + S)
+    E = L * per
+    c = B.SlotCache(E, S, 1 << 20, 1 << 20, dry_run=True)
+    c.set_layers(L)
+    sim = LRUSlotCache(E, S, n_layers=L)
+    for step in range(30 * L):
+        l = step % L
+        idx = l * per + np.stack([rng.choice(per, size=k, replace=False) for _ in range(T)])
+        counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+        n = c.plan_host(counts)
+        plan = sim.step(idx.ravel())
+        assert n == len(plan.waves)
+        for w, wave in enumerate(plan.waves):
+            assert c.wave_plan(w) == [(en.expert, en.slot, int(en.hit), en.evicted) for en in wave]
+        if step % 3 == 1:
+            nxt = (l + 1) % L
+            pred = (nxt * per + rng.choice(per, size=rng.integers(0, per // 2 + 1), replace=False)).tolist()
+            assert c.prefetch(pred) == len(sim.prefetch(pred))
+    st, s = c.stats(), sim.stats
+    assert (st["hits"], st["misses"], st["evictions"], st["prefetches"]) == (s.hits, s.misses, s.evictions, s.prefetches)
+    bad = np.zeros(E, np.int32)
+    bad[0] = bad[per] = 1   # entries of layers 0 and 1 in one step
+    with pytest.raises(B.MoeError) as ei:
+        c.plan_host(bad)
+    assert ei.value.status == -1
+    with pytest.raises(B.MoeError):
+        c.set_layers(E + 1)
+    c.close()
+
+
 def test_cache_create_validation():
     with pytest.raises(B.MoeError) as ei:
         B.SlotCache(8, 0, 1024, 1024, dry_run=True)

@@ -228,3 +228,75 @@ def test_prefetch_of_resident_or_nothing_changes_no_residency():
     slots = list(c.slot_of)
     assert c.prefetch([]) == [] and c.prefetch([3, 1]) == []
     assert c.slot_of == slots and c.stats.prefetches == 0 and c.stats.evictions == 0
+
+
+# ------------------------------------------------------------- layer order --
+
+def test_layer_order_hand_worked_trace():
+    want_s, want_t = [], None
+    for line in open(os.path.join(GOLDEN, "lru_layer_order_trace.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        tag, *vals = line.split()
+        vals = tuple(int(v) for v in vals)
+        if tag == "S":
+            want_s.append(vals)
+        else:
+            want_t = vals
+    c = LRUSlotCache(6, 3, n_layers=2)
+    got = []
+    for step, touched in enumerate([{3}, {0}, {4}, {1}, {3, 4}], start=1):
+        for w, wave in enumerate(c.step(touched).waves):
+            got += [(step, w, en.expert, en.slot, int(en.hit), en.evicted) for en in wave]
+    assert got == want_s
+    assert (c.stats.hits, c.stats.misses, c.stats.evictions) == want_t
+    plain = LRUSlotCache(6, 3)
+    for touched in [{3}, {0}, {4}, {1}, {3, 4}]:
+        plain.step(touched)
+    assert (plain.stats.hits, plain.stats.misses) == (1, 5)
+
+
+def _furthest_next_use_misses(seq, S):
+    """Offline replacement in the textbook MIN manner, under the pool's constraint that a step's
+    experts stay resident while it runs (each step here is one wave): on a miss with a full pool,
+    evict, among the entries the step does not touch, the one whose next step lies furthest ahead
+    (never used again counts as furthest). Computed from the future of the sequence itself."""
+    cache, misses = set(), 0
+    for i, touched in enumerate(seq):
+        for e in sorted(touched):
+            if e in cache:
+                continue
+            misses += 1
+            if len(cache) == S:
+                def next_use(v):
+                    for j in range(i + 1, len(seq)):
+                        if v in seq[j]:
+                            return j
+                    return len(seq) + 1
+                cache.remove(max((v for v in cache if v not in touched), key=lambda v: (next_use(v), -v)))
+            cache.add(e)
+    return misses
+
+
+@pytest.mark.parametrize("L,per,size,S", [(3, 8, 4, 6), (4, 16, 6, 16), (4, 32, 10, 24), (5, 8, 3, 9)])
+def test_layer_order_is_optimal_on_a_fixed_cycle(L, per, size, S):
+    """Each layer touches the same set every cycle: the layer order then makes exactly as many
+    misses as evicting by furthest next use read off the future sequence, and plain LRU (which
+    evicts what comes next) makes more."""
+    rng = np.random.default_rng(L * per + S)
+    sets = [set((l * per + rng.choice(per, size=size, replace=False)).tolist()) for l in range(L)]
+    seq = [sets[i % L] for i in range(L * 12)]
+    c = LRUSlotCache(L * per, S, n_layers=L)
+    lru = LRUSlotCache(L * per, S)
+    for touched in seq:
+        c.step(touched)
+        lru.step(touched)
+    assert c.stats.misses == _furthest_next_use_misses(seq, S)
+    assert lru.stats.misses > c.stats.misses
+
+
+def test_layer_order_rejects_a_step_across_layers():
+    c = LRUSlotCache(8, 4, n_layers=2)
+    with pytest.raises(ValueError):
+        c.step([1, 5])
