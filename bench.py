@@ -115,6 +115,7 @@ def bench_offload(args, torch, B, synth, MoELayer):
     """Expert-offload decode: T tokens per step through an n_slots HBM slot pool fed from pinned host
     bundles, Zipf-biased routing re-drawn every zipf_epoch steps. The same steps run these ways: all
     experts resident (compute time), slot pool with overlapped copies, slot pool in blocking mode,
+    slot pool with overlapped copies and frequency-aware victims (--freq-decay),
     and the pool planned on the device (copy kernels, no host synchronisation), eager and as one
     graph replay per step. The device-planned graph replays start from an empty pool, as the
     others do."""
@@ -143,8 +144,10 @@ def bench_offload(args, torch, B, synth, MoELayer):
     del res
     torch.cuda.empty_cache()
     out = {}
-    for mode, blocking in (("overlapped", False), ("blocking", True)):
-        lay = MoELayer(cfg, router=router, experts=experts, pool_slots=cfg.n_slots, blocking=blocking, threads=16)
+    for mode, blocking, decay in (("overlapped", False, 0.0), ("blocking", True, 0.0),
+                                  ("overlapped_freq", False, args.freq_decay)):
+        lay = MoELayer(cfg, router=router, experts=experts, pool_slots=cfg.n_slots, blocking=blocking, threads=16,
+                       freq_decay=decay)
         t_wall = run(lay)
         st = lay.cache.stats()
         t_copy = st["copy_ms"] / 1e3
@@ -251,7 +254,9 @@ def bench_stack(args, torch, B, synth, MoELayer):
     predictors = ["none"] + [p for p in args.prefetch.split(",") if p and p != "none"]
     for policy, predictor in [(pol, pr) for pol in args.policies.split(",") for pr in predictors]:
         key = f"{policy}/{predictor}"
-        pool = SharedSlotPool([bundles] * L, n_slots, cfg.d, cfg.F, W_CODE[cfg.dtype], layer_order=policy == "layer")
+        pool = SharedSlotPool([bundles] * L, n_slots, cfg.d, cfg.F, W_CODE[cfg.dtype],
+                              layer_order=policy.startswith("layer"),
+                              freq_decay=args.freq_decay if policy.endswith("freq") else 0.0)
         layers = [MoELayer(c, router=r, experts=None, shared_pool=pool, layer_index=l)
                   for l, (c, r) in enumerate(zip(cfgs, routers))]
         t_wall = run(layers, pool, predictor)
@@ -404,9 +409,11 @@ def main():
                     help="stack: predictors to run besides none (prev = the layer's previous step, "
                          "zipf = top-N of its routing prior)")
     ap.add_argument("--prefetch-n", type=int, default=16, help="stack: experts the zipf predictor names")
-    ap.add_argument("--policies", default="lru,layer",
+    ap.add_argument("--freq-decay", type=float, default=0.8,
+                    help="offload: decay of the routing frequency for the frequency-aware pool modes")
+    ap.add_argument("--policies", default="lru,layer,layerfreq",
                     help="stack: victim choices to run (lru = plain LRU, layer = the layer that runs furthest "
-                         "ahead first, then LRU)")
+                         "ahead first, then LRU, layerfreq = the layer order, then decayed routing frequency)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (HBM ceiling and the "
                          "reference for the FETCH_SIZE/WRITE_SIZE counters), then exit")

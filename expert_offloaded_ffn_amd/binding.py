@@ -117,6 +117,7 @@ EXPORTS = {
                                ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_release": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "expert_slot_cache_set_layers": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
+    "expert_slot_cache_set_frequency": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_double]),
     "expert_slot_cache_prefetch": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                     ctypes.POINTER(ctypes.c_int32)]),
     "expert_slot_cache_wave_plan": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(CacheEntry),
@@ -431,6 +432,11 @@ class SlotCache:
         """Entries are n_layers layer-major groups run in cyclic order: evict from the layer that
         runs furthest ahead, then LRU (1 = plain LRU)."""
         _check(lib().expert_slot_cache_set_layers(self.h, int(n_layers)))
+
+    def set_frequency(self, decay: float):
+        """Victims by decayed routing frequency (freq = decay*freq + counts per step), then recency;
+        0 = plain recency."""
+        _check(lib().expert_slot_cache_set_frequency(self.h, float(decay)))
 
     def prefetch(self, experts) -> int:
         """Copies the listed (predicted) experts ahead of their step; returns the copies issued."""

@@ -51,6 +51,8 @@ struct expert_slot_cache {
   int32_t n_layers = 1;                  // > 1: entries are layer-major groups run in cyclic order
   int32_t step_layer = 0;                // layer of the last planned step's entries
   int64_t wave_clock = 0;                // clock before the current wave's first access
+  double freq_decay = 0.0;               // > 0: victims by decayed routing frequency before recency
+  std::vector<double> freq;              // per entry: sum over planned steps of decay^age * counts
   std::vector<char> prefetched;          // per expert: brought in by prefetch, not yet used by a step
   std::vector<std::vector<moe_cache_entry>> waves;
   bool planned = false;
@@ -79,6 +81,7 @@ void plan_reset(expert_slot_cache* c) {
   c->owner.assign(S, -1);
   c->last.assign(E, 0);
   c->prefetched.assign(E, 0);
+  c->freq.assign(E, 0.0);
   c->clock = 0;
   c->step_clock = 0;
   c->step_layer = 0;
@@ -89,8 +92,10 @@ void plan_reset(expert_slot_cache* c) {
 }
 
 // Victim order: with a layer order, the entry whose layer runs furthest after
-// the current one first (distance (layer - current - 1) mod L, largest first),
-// then the least recently used; plain LRU otherwise. `ok` filters candidates.
+// the current one first (distance (layer - current - 1) mod L, largest first);
+// then, with a frequency decay, the smallest decayed routing frequency; then
+// the least recently used. Plain LRU when neither is set. `ok` filters
+// candidates.
 template <class Ok>
 int pick_victim(const expert_slot_cache* c, Ok ok) {
   const int L = c->n_layers, per = c->cfg.n_experts / L;
@@ -99,7 +104,12 @@ int pick_victim(const expert_slot_cache* c, Ok ok) {
     const int v = c->owner[s];
     if (v < 0 || !ok(v)) continue;
     const int dist = L > 1 ? ((v / per - c->step_layer - 1) % L + L) % L : 0;
-    if (victim < 0 || dist > vdist || (dist == vdist && c->last[v] < c->last[victim])) {
+    bool better = victim < 0 || dist > vdist;
+    if (!better && dist == vdist) {
+      const double fv = c->freq_decay > 0 ? c->freq[v] : 0.0, fw = c->freq_decay > 0 ? c->freq[victim] : 0.0;
+      better = fv < fw || (fv == fw && c->last[v] < c->last[victim]);
+    }
+    if (better) {
       victim = v;
       vdist = dist;
     }
@@ -192,6 +202,8 @@ moe_status plan_step(expert_slot_cache* c, const int32_t* counts) {
     }
     if (layer >= 0) c->step_layer = layer;
   }
+  if (c->freq_decay > 0)
+    for (int e = 0; e < E; ++e) c->freq[e] = c->freq_decay * c->freq[e] + (double)std::max(counts[e], 0);
   c->step_clock = c->clock;
   std::vector<int> order;
   for (int e = 0; e < E; ++e)
@@ -445,6 +457,16 @@ extern "C" moe_status expert_slot_cache_set_layers(expert_slot_cache* c, int32_t
   MOE_REQUIRE(n_layers >= 1 && c->cfg.n_experts % n_layers == 0, MOE_EINVAL,
               "expert_slot_cache_set_layers: n_layers=%d must divide n_experts=%d", n_layers, c->cfg.n_experts);
   c->n_layers = n_layers;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_set_frequency(expert_slot_cache* c, double decay) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_set_frequency: NULL cache");
+  MOE_REQUIRE(decay >= 0.0 && decay <= 1.0, MOE_EINVAL, "expert_slot_cache_set_frequency: decay %g outside [0, 1]",
+              decay);
+  c->freq_decay = decay;
+  std::fill(c->freq.begin(), c->freq.end(), 0.0);
   return MOE_OK;
 }
 

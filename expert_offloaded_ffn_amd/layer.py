@@ -65,9 +65,9 @@ class SharedSlotPool:
     step can prefetch the next layer's predicted experts (expert_slot_cache_prefetch).
     bundles_per_layer: [L] lists of E pinned host bundles (layers may share bundle tensors).
     layer_order: victims from the layer that runs furthest ahead, then LRU (expert_slot_cache_set_layers);
-    else plain LRU."""
+    else plain LRU. freq_decay: victims by decayed routing frequency before recency (0 = off)."""
 
-    def __init__(self, bundles_per_layer, n_slots, d, F, w_dtype, device="cuda", layer_order=False):
+    def __init__(self, bundles_per_layer, n_slots, d, F, w_dtype, device="cuda", layer_order=False, freq_decay=0.0):
         self.L = len(bundles_per_layer)
         self.E = len(bundles_per_layer[0])
         self.d, self.F, self.w_code = d, F, w_dtype
@@ -81,6 +81,8 @@ class SharedSlotPool:
         self.cache = B.SlotCache(self.L * self.E, n_slots, self.bundle_bytes, self.stride, flat, self.slot_pool)
         if layer_order:   # evict from the layer that runs furthest ahead, then LRU
             self.cache.set_layers(self.L)
+        if freq_decay:    # then by decayed routing frequency, then LRU
+            self.cache.set_frequency(freq_decay)
 
     def table(self, layer: int):
         """The expert table of one layer: its E entries of the shared slot table."""
@@ -98,13 +100,15 @@ FUSE_COMBINE_MAX_T = 4
 class MoELayer:
     def __init__(self, cfg, *, router, experts, shared=None, w_shared_gate=None, select_bias=None, device="cuda",
                  pool_slots=None, blocking=False, threads=8, fuse_combine=True, shared_pool=None, layer_index=0,
-                 device_plan=False):
+                 device_plan=False, freq_decay=0.0):
         """router: W_r [d, E] storage; experts: list of synth expert tuples; shared: synth tuple or None.
         pool_slots: None = every expert resident; an int = expert slot pool of that many slots.
         shared_pool: a SharedSlotPool this layer's experts live in (entry layer_index*E + e);
         experts is then unused.
         device_plan: with pool_slots, plan residency and copy missed bundles on the device
         (expert_slot_cache_dev): no host synchronisation, and capture() works.
+        freq_decay: with pool_slots (host-planned), victims by decayed routing frequency before
+        recency (expert_slot_cache_set_frequency); 0 = plain LRU.
         fuse_combine: a decode step of at most FUSE_COMBINE_MAX_T tokens that runs the shared expert
         in the routed experts' launches combines inside the down launch (moe_grouped_ffn_combine)
         instead of a moe_combine call."""
@@ -151,6 +155,8 @@ class MoELayer:
             else:
                 self.cache = B.SlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles, self.slot_pool,
                                          blocking=blocking)
+                if freq_decay:
+                    self.cache.set_frequency(freq_decay)
             self.table = B.expert_table(self.slot_pool, stride, self.slot_table, self.E, self.d, self.F, self.w_code)
         self.shared = None
         if shared is not None:

@@ -440,6 +440,19 @@ moe_status expert_slot_cache_release(expert_slot_cache* c, int32_t wave, void* s
  * Errors: MOE_EINVAL (n_layers < 1 or not a divisor of n_experts). */
 moe_status expert_slot_cache_set_layers(expert_slot_cache* c, int32_t n_layers);
 
+/* Frequency-aware victims (beyond the pages, like the layer order). With
+ * decay in (0, 1] every planned step first updates, for every entry,
+ * freq = decay * freq + counts (the step's routed rows per entry), and a victim
+ * is then chosen (after the layer order, if set) by the smallest freq, ties to
+ * the least recently used. decay = 0 (the default) turns it off: plain
+ * recency. Setting it clears the frequencies. The pages' cache evicts by
+ * recency alone ("Running 35B MoE Models on 8GB GPUs", section "Technical
+ * Insight") and they call that blind to which experts will be needed (section
+ * "Gotcha"); under a skewed, slowly drifting routing prior the experts routed
+ * to most often are the ones needed next. Host planner only.
+ * Errors: MOE_EINVAL (decay outside [0, 1]). */
+moe_status expert_slot_cache_set_frequency(expert_slot_cache* c, double decay);
+
 /* Prefetch of predicted experts ahead of the step that routes to them.
  * The pages: a background reader fetches the next layer while the current one
  * computes ("NovaLLM: Running Massive MoE Models Fully In-Memory", section 3,

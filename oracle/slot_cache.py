@@ -49,6 +49,13 @@ be L layer-major groups of a stack whose layers run in the cyclic order
 miss's or a prefetch's) takes, among the entries it may evict, one of the layer
 whose next step comes last, i.e. the largest (layer - current - 1) mod L, the
 least recently used within it. With L = 1 this is plain LRU.
+
+Routing frequency (beyond the pages, likewise): with a decay in (0, 1], every
+step first sets freq[e] = decay * freq[e] + (rows routed to e in the step) for
+all entries, and a victim (after the layer order, if any) is the entry with
+the smallest freq, the least recently used among equals. The pages' cache is
+recency alone ("Technical Insight"), which they call blind to upcoming needs
+("Gotcha").
 """
 from __future__ import annotations
 
@@ -80,10 +87,10 @@ class CacheStats:
 
 
 class LRUSlotCache:
-    def __init__(self, n_experts: int, n_slots: int, n_layers: int = 1):
-        if n_slots < 1 or n_experts < 1 or n_experts % n_layers:
-            raise ValueError("need at least one expert and one slot, and layers that divide the entries")
-        self.E, self.S, self.L = n_experts, n_slots, n_layers
+    def __init__(self, n_experts: int, n_slots: int, n_layers: int = 1, freq_decay: float = 0.0):
+        if n_slots < 1 or n_experts < 1 or n_experts % n_layers or not 0.0 <= freq_decay <= 1.0:
+            raise ValueError("need an expert, a slot, layers that divide the entries and a decay in [0, 1]")
+        self.E, self.S, self.L, self.decay = n_experts, n_slots, n_layers, freq_decay
         self.reset()
 
     def reset(self):
@@ -92,6 +99,7 @@ class LRUSlotCache:
         self.last = [0] * self.E
         self.clock = 0
         self.layer = 0                # layer of the most recent step
+        self.freq = [0.0] * self.E    # decayed rows routed per entry (used when decay > 0)
         self.step_touched = set()     # experts the most recent step accessed, or predicted since
         self.from_prefetch = set()    # prefetched, not yet touched by a step
         self.stats = CacheStats()
@@ -103,7 +111,8 @@ class LRUSlotCache:
         """The layer whose next step comes last, then the least recently used."""
         per = self.E // self.L
         ahead = lambda v: (v // per - self.layer - 1) % self.L
-        return max(candidates, key=lambda v: (ahead(v), -self.last[v]))
+        f = (lambda v: self.freq[v]) if self.decay > 0 else (lambda v: 0.0)
+        return max(candidates, key=lambda v: (ahead(v), -f(v), -self.last[v]))
 
     def _access(self, e: int, wave) -> WaveEntry:
         self.clock += 1
@@ -132,7 +141,13 @@ class LRUSlotCache:
         return WaveEntry(e, slot, False, evicted)
 
     def step(self, touched_experts) -> StepPlan:
-        touched = sorted(set(int(e) for e in touched_experts))
+        rows = [int(e) for e in touched_experts]
+        touched = sorted(set(rows))
+        if self.decay > 0:
+            routed = [0] * self.E
+            for e in rows:
+                routed[e] += 1
+            self.freq = [self.decay * f + r for f, r in zip(self.freq, routed)]
         layers = {e // (self.E // self.L) for e in touched}
         if len(layers) > 1:
             raise ValueError("a step touches entries of several layers")

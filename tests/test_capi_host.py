@@ -367,6 +367,37 @@ def test_planner_layer_order_matches_oracle_simulation(L, per, S, k, T):
     c.close()
 
 
+@pytest.mark.parametrize("L,decay", [(1, 0.8), (1, 1.0), (4, 0.8)])
+def test_planner_frequency_matches_oracle_simulation(L, decay):
+    """Frequency-aware victims (alone and after the layer order), with predictions."""
+    rng = np.random.default_rng(int(decay * 10) + L)
+    per, S, k, T = 32, 24, 4, 6
+    E = L * per
+    c = B.SlotCache(E, S, 1 << 20, 1 << 20, dry_run=True)
+    if L > 1:
+        c.set_layers(L)
+    c.set_frequency(decay)
+    sim = LRUSlotCache(E, S, n_layers=L, freq_decay=decay)
+    p = rng.dirichlet(np.full(per, 0.5))
+    for step in range(40 * L):
+        l = step % L
+        idx = l * per + np.stack([rng.choice(per, size=k, replace=False, p=p) for _ in range(T)])
+        counts = np.bincount(idx.ravel(), minlength=E).astype(np.int32)
+        n = c.plan_host(counts)
+        plan = sim.step(idx.ravel())
+        assert n == len(plan.waves)
+        for w, wave in enumerate(plan.waves):
+            assert c.wave_plan(w) == [(en.expert, en.slot, int(en.hit), en.evicted) for en in wave]
+        if step % 4 == 3:
+            pred = (((l + 1) % L) * per + rng.choice(per, size=5, replace=False)).tolist()
+            assert c.prefetch(pred) == len(sim.prefetch(pred))
+    st, s = c.stats(), sim.stats
+    assert (st["hits"], st["misses"], st["evictions"]) == (s.hits, s.misses, s.evictions)
+    with pytest.raises(B.MoeError):
+        c.set_frequency(1.5)
+    c.close()
+
+
 def test_cache_create_validation():
     with pytest.raises(B.MoeError) as ei:
         B.SlotCache(8, 0, 1024, 1024, dry_run=True)

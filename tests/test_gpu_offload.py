@@ -22,11 +22,12 @@ def _x(cfg, step):
     return xs, torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-def _run(cfg, steps, *, n_slots, blocking=False, check_outputs=True, tokens=None):
+def _run(cfg, steps, *, n_slots, blocking=False, check_outputs=True, tokens=None, freq_decay=0.0):
     router = synth.gen_router(cfg)
     experts = synth.gen_experts(cfg)
-    layer = MoELayer(cfg, router=router, experts=experts, device=DEV, pool_slots=n_slots, blocking=blocking)
-    sim = LRUSlotCache(cfg.E, n_slots)
+    layer = MoELayer(cfg, router=router, experts=experts, device=DEV, pool_slots=n_slots, blocking=blocking,
+                     freq_decay=freq_decay)
+    sim = LRUSlotCache(cfg.E, n_slots, freq_decay=freq_decay)
     outs = []
     ocache = {}
 
@@ -89,3 +90,10 @@ def test_offload_full_size_few_steps():
     cfg = synth.get_config("offload_decode_bf16")
     outs, sim = _run(cfg, 4, n_slots=cfg.n_slots, tokens=[0, 7, 13, 31])
     assert sim.stats.misses > 0
+
+
+def test_frequency_victims_plans_and_parity():
+    """Frequency-aware victims: every step's plan equals the oracle's, outputs match the oracle."""
+    cfg = synth.get_config("offload_decode_bf16", E=16, d=256, F=256, T=8, k=4, zipf_epoch=6, n_slots=5)
+    outs, sim = _run(cfg, 12, n_slots=5, freq_decay=0.8)
+    assert sim.stats.evictions > 0 and sim.stats.hits > 0

@@ -300,3 +300,78 @@ def test_layer_order_rejects_a_step_across_layers():
     c = LRUSlotCache(8, 4, n_layers=2)
     with pytest.raises(ValueError):
         c.step([1, 5])
+
+
+# --------------------------------------------------------- routing frequency --
+
+def test_frequency_hand_worked_trace():
+    want_s, want_t = [], None
+    for line in open(os.path.join(GOLDEN, "lru_frequency_trace.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        tag, *vals = line.split()
+        vals = tuple(int(v) for v in vals)
+        if tag == "S":
+            want_s.append(vals)
+        else:
+            want_t = vals
+    c = LRUSlotCache(4, 2, freq_decay=0.5)
+    got = []
+    steps = [[0, 0, 0, 1], [2], [0, 3, 3], [1, 2]]       # one id per routed row
+    for step, rows in enumerate(steps, start=1):
+        for w, wave in enumerate(c.step(rows).waves):
+            got += [(step, w, en.expert, en.slot, int(en.hit), en.evicted) for en in wave]
+    assert got == want_s
+    assert (c.stats.hits, c.stats.misses, c.stats.evictions) == want_t
+    assert c.freq == [0.875, 1.125, 1.25, 1.0]
+
+
+def _lfu_run(steps, S):
+    """Textbook LFU over a recency list (index 0 = most recent): a miss with a full cache evicts,
+    among the entries outside the step's wave, the one routed the fewest rows so far, the deepest
+    in the list among equals. Same access order as the pool (resident ascending, then others)."""
+    lst, total = [], {}
+    hits = misses = 0
+    for rows in steps:
+        for e in rows:
+            total[e] = total.get(e, 0) + 1
+        touched = sorted(set(rows))
+        order = [e for e in touched if e in lst] + [e for e in touched if e not in lst]
+        for w0 in range(0, len(order), S):
+            wave = order[w0:w0 + S]
+            for e in wave:
+                if e in lst:
+                    hits += 1
+                    lst.remove(e)
+                else:
+                    misses += 1
+                    if len(lst) == S:
+                        cand = [i for i, v in enumerate(lst) if v not in wave]
+                        fewest = min(total[lst[i]] for i in cand)
+                        lst.pop(max(i for i in cand if total[lst[i]] == fewest))
+                lst.insert(0, e)
+    return hits, misses
+
+
+@pytest.mark.parametrize("E,S,k", [(8, 3, 2), (16, 5, 3), (64, 16, 8)])
+def test_frequency_without_decay_is_textbook_lfu(E, S, k):
+    rng = np.random.default_rng(3 * E + S)
+    p = rng.dirichlet(np.full(E, 0.3))
+    steps = [rng.choice(E, size=(rng.integers(1, 5) * k), p=p).tolist() for _ in range(80)]
+    c = LRUSlotCache(E, S, freq_decay=1.0)
+    for rows in steps:
+        c.step(rows)
+    assert (c.stats.hits, c.stats.misses) == _lfu_run(steps, S)
+
+
+def test_frequency_is_the_decayed_sum_of_routed_rows():
+    rng = np.random.default_rng(5)
+    E, d = 12, 0.8
+    steps = [rng.choice(E, size=10).tolist() for _ in range(40)]
+    c = LRUSlotCache(E, 4, freq_decay=d)
+    for rows in steps:
+        c.step(rows)
+    counts = np.stack([np.bincount(r, minlength=E) for r in steps])
+    closed = (d ** np.arange(len(steps))[::-1, None] * counts).sum(axis=0)
+    assert np.allclose(c.freq, closed, rtol=1e-12, atol=0)
