@@ -162,23 +162,26 @@ def bench_offload(args, torch, B, synth, MoELayer):
         del lay
         torch.cuda.empty_cache()
     # the device-planned pool: no host synchronisation; eager, then every step one graph replay
+    # (LRU, then frequency-aware victims)
     lay = MoELayer(cfg, router=router, experts=experts, pool_slots=cfg.n_slots, device_plan=True, threads=16)
     t_wall = run(lay)
     st = lay.cache_dev.stats()
     lay.cache_dev.reset()
     x_static, lb_static = xs[0].clone(), lbs[0].clone()
     graph, _ = lay.capture(x_static, lb_static)
-    lay.cache_dev.reset()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        x_static.copy_(xs[s])
-        lb_static.copy_(lbs[s])
-        graph.replay()
-    torch.cuda.synchronize()
-    t_graph = time.perf_counter() - t0
-    sg = lay.cache_dev.stats()
-    for mode, t, stt in (("device_plan", t_wall, st), ("device_plan_graph", t_graph, sg)):
+    timed = [("device_plan", t_wall, st)]
+    for mode, decay in (("device_plan_graph", 0.0), ("device_plan_freq_graph", args.freq_decay)):
+        lay.cache_dev.set_frequency(decay)
+        lay.cache_dev.reset()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            x_static.copy_(xs[s])
+            lb_static.copy_(lbs[s])
+            graph.replay()
+        torch.cuda.synchronize()
+        timed.append((mode, time.perf_counter() - t0, lay.cache_dev.stats()))
+    for mode, t, stt in timed:
         acc = stt["hits"] + stt["misses"]
         out[mode] = {"wall_s": round(t, 4), "tokens_per_s": round(cfg.T * steps / t, 1),
                      "hit_rate": round(stt["hits"] / max(acc, 1), 4), "hits": stt["hits"], "misses": stt["misses"],

@@ -38,6 +38,8 @@ struct DevState {
   int64_t* last;      // [E] recency stamps
   int64_t* ctl;       // [kCtlN]
   int2* copies;       // [E] (expert, slot) of the last step's misses, in miss order (up to E of them)
+  double* freq;       // [E] decayed routed rows (used when decay > 0)
+  double* decay;      // [1] frequency decay, read by every plan (graphs see changes); 0 = LRU
 };
 
 // Rank of this thread's flag among the block's set flags (ascending thread
@@ -90,9 +92,15 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t*
   __shared__ int miss_list[kPlanThreads];     // missed experts, ascending
   __shared__ int slot_owner[kPlanThreads];
   __shared__ long long slot_stamp[kPlanThreads];
+  __shared__ double slot_freq[kPlanThreads];
   const int t = threadIdx.x;
+  const double decay = *st.decay;
   bool touched = false, resident = false;
   int my_slot = -1;
+  if (t < E && decay > 0.0) {
+    // separately rounded multiply and add: the same doubles as the host planner's
+    st.freq[t] = __dadd_rn(__dmul_rn(decay, st.freq[t]), (double)max(counts[t], 0));
+  }
   if (t < E) {
     touched = counts[t] > 0;
     my_slot = st.slot_of[t];
@@ -108,17 +116,30 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t*
     if (o >= E) o = -1;
     slot_owner[t] = o;
     slot_stamp[t] = o >= 0 ? (long long)st.last[o] : 0;
+    slot_freq[t] = o >= 0 && decay > 0.0 ? st.freq[o] : 0.0;
   }
   if (touched && !resident) miss_list[miss_rank] = t;
   __syncthreads();
   if (touched && resident) slot_stamp[my_slot] = clock + 1 + hit_rank;  // the hits, in access order
   __syncthreads();
-  // misses one at a time: free slots (key = slot index) before occupied ones (key above all slot indices)
+  // misses one at a time: the lowest free slot; else, outside the current wave, the smallest
+  // routing frequency (when decay > 0; frequencies are >= 0, so their bit patterns order like
+  // the values), then the oldest stamp
   for (int j = 0; j < n_miss; ++j) {
-    long long key = LLONG_MAX;
-    if (t < S) key = slot_owner[t] < 0 ? (long long)t : (1ll << 40) + slot_stamp[t];
-    const long long m = block_min(key, wave_min);
-    if (t < S && key == m) {  // stamps and slot indices are distinct: one thread matches
+    const long long wave_start = clock + 1 + (long long)((n_hit + j) / S) * S;
+    const bool occupied = t < S && slot_owner[t] >= 0;
+    const bool cand = occupied && slot_stamp[t] < wave_start;
+    long long key = t < S && !occupied ? (long long)t : LLONG_MAX;
+    long long m = block_min(key, wave_min);
+    if (m == LLONG_MAX) {  // block-uniform: no free slot
+      const long long fbits = cand ? (long long)__double_as_longlong(slot_freq[t]) : LLONG_MAX;
+      const long long mf = decay > 0.0 ? block_min(fbits, wave_min) : 0;
+      const bool keep = cand && (decay > 0.0 ? fbits == mf : true);
+      key = keep ? slot_stamp[t] : LLONG_MAX;
+      m = block_min(key, wave_min);
+      if (!keep) key = LLONG_MIN;  // never equal to m
+    }
+    if (t < S && key == m) {  // slot indices and stamps are distinct: one thread matches
       const int e = miss_list[j];
       const int wave = (n_hit + j) / S;
       if (wave < max_waves) miss_tables[(size_t)wave * E + e] = t;
@@ -126,6 +147,7 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t*
       if (slot_owner[t] >= 0) atomicAdd(reinterpret_cast<unsigned long long*>(st.ctl + kEvictions), 1ull);
       slot_owner[t] = e;
       slot_stamp[t] = clock + 1 + n_hit + j;
+      slot_freq[t] = decay > 0.0 ? st.freq[e] : 0.0;
     }
     __syncthreads();
   }
@@ -194,6 +216,7 @@ struct expert_slot_cache_dev {
   int device = -1;
   hipStream_t side = nullptr;
   int max_waves = 1;
+  double decay = 0.0;
   std::vector<hipEvent_t> fork, join;  // per wave
   void* block = nullptr;  // device: state, copy list and source pointers
   DevState st{};
@@ -206,7 +229,8 @@ namespace {
 size_t state_bytes(int E, int S) {
   return align_up(sizeof(int32_t) * E, 256) + align_up(sizeof(int32_t) * S, 256) +
          align_up(sizeof(int64_t) * E, 256) + align_up(sizeof(int64_t) * kCtlN, 256) +
-         align_up(sizeof(int2) * E, 256) + align_up(sizeof(void*) * E, 256);
+         align_up(sizeof(int2) * E, 256) + align_up(sizeof(void*) * E, 256) + align_up(sizeof(double) * E, 256) +
+         256;
 }
 
 // Empty pool, zero counters (synchronous; not for use under capture).
@@ -218,6 +242,9 @@ moe_status init_state(expert_slot_cache_dev* c) {
   MOE_HIP(hipMemcpy(c->st.owner, neg.data(), sizeof(int32_t) * S, hipMemcpyHostToDevice));
   MOE_HIP(hipMemcpy(c->st.last, zero.data(), sizeof(int64_t) * E, hipMemcpyHostToDevice));
   MOE_HIP(hipMemcpy(c->st.ctl, zero.data(), sizeof(int64_t) * kCtlN, hipMemcpyHostToDevice));
+  std::vector<double> fzero(E, 0.0);
+  MOE_HIP(hipMemcpy(c->st.freq, fzero.data(), sizeof(double) * E, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(c->st.decay, &c->decay, sizeof(double), hipMemcpyHostToDevice));
   c->stepped = false;
   return MOE_OK;
 }
@@ -302,6 +329,10 @@ extern "C" moe_status expert_slot_cache_dev_create(const moe_cache_cfg* cfg, exp
   c->st.copies = reinterpret_cast<int2*>(p);
   p += align_up(sizeof(int2) * E, 256);
   c->src = reinterpret_cast<const uint4**>(p);
+  p += align_up(sizeof(void*) * E, 256);
+  c->st.freq = reinterpret_cast<double*>(p);
+  p += align_up(sizeof(double) * E, 256);
+  c->st.decay = reinterpret_cast<double*>(p);
   if ((e = hipMemcpy(c->src, src.data(), sizeof(void*) * E, hipMemcpyHostToDevice)) != hipSuccess)
     return fail("hipMemcpy", e);
   if (moe_status s = init_state(c)) {
@@ -326,6 +357,19 @@ extern "C" moe_status expert_slot_cache_dev_reset(expert_slot_cache_dev* c) {
   MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_reset: NULL cache");
   MOE_HIP(hipDeviceSynchronize());
   return init_state(c);
+}
+
+extern "C" moe_status expert_slot_cache_dev_set_frequency(expert_slot_cache_dev* c, double decay) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_set_frequency: NULL cache");
+  MOE_REQUIRE(decay >= 0.0 && decay <= 1.0, MOE_EINVAL,
+              "expert_slot_cache_dev_set_frequency: decay %g outside [0, 1]", decay);
+  MOE_HIP(hipDeviceSynchronize());
+  std::vector<double> fzero(c->cfg.n_experts, 0.0);
+  MOE_HIP(hipMemcpy(c->st.freq, fzero.data(), sizeof(double) * c->cfg.n_experts, hipMemcpyHostToDevice));
+  MOE_HIP(hipMemcpy(c->st.decay, &decay, sizeof(double), hipMemcpyHostToDevice));
+  c->decay = decay;
+  return MOE_OK;
 }
 
 extern "C" int32_t expert_slot_cache_dev_max_waves(const expert_slot_cache_dev* c) {

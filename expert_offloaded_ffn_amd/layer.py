@@ -107,8 +107,8 @@ class MoELayer:
         experts is then unused.
         device_plan: with pool_slots, plan residency and copy missed bundles on the device
         (expert_slot_cache_dev): no host synchronisation, and capture() works.
-        freq_decay: with pool_slots (host-planned), victims by decayed routing frequency before
-        recency (expert_slot_cache_set_frequency); 0 = plain LRU.
+        freq_decay: with pool_slots, victims by decayed routing frequency before recency
+        (expert_slot_cache_set_frequency / expert_slot_cache_dev_set_frequency); 0 = plain LRU.
         fuse_combine: a decode step of at most FUSE_COMBINE_MAX_T tokens that runs the shared expert
         in the routed experts' launches combines inside the down launch (moe_grouped_ffn_combine)
         instead of a moe_combine call."""
@@ -148,6 +148,8 @@ class MoELayer:
             if device_plan:
                 self.cache_dev = B.DeviceSlotCache(self.E, pool_slots, self.bundle_bytes, stride, bundles,
                                                    self.slot_pool)
+                if freq_decay:
+                    self.cache_dev.set_frequency(freq_decay)
                 nw = self.cache_dev.max_waves
                 self.miss_slot_tables = torch.full((nw, self.E), -1, dtype=torch.int32, device=self.device)
                 self.miss_tables = [B.expert_table(self.slot_pool, stride, self.miss_slot_tables[w], self.E, self.d,

@@ -529,6 +529,13 @@ moe_status expert_slot_cache_dev_create(const moe_cache_cfg* cfg, expert_slot_ca
 moe_status expert_slot_cache_dev_destroy(expert_slot_cache_dev* c);
 moe_status expert_slot_cache_dev_reset(expert_slot_cache_dev* c);
 int32_t expert_slot_cache_dev_max_waves(const expert_slot_cache_dev* c);   /* ceil(n_experts / n_slots) */
+/* Frequency-aware victims, as expert_slot_cache_set_frequency (same doubles:
+ * the device rounds the multiply and the add separately). The victim is the
+ * lowest free slot, else, outside the current wave, the smallest frequency,
+ * then the least recently used. decay = 0 (default) is plain LRU. Setting it
+ * synchronises the device and clears the frequencies; the decay lives in device
+ * memory, so graphs captured before see the new value. Errors: MOE_EINVAL. */
+moe_status expert_slot_cache_dev_set_frequency(expert_slot_cache_dev* c, double decay);
 moe_status expert_slot_cache_dev_step(expert_slot_cache_dev* c, const int32_t* counts, void* stream,
                                       int32_t* hit_table, int32_t* miss_tables);
 moe_status expert_slot_cache_dev_copy(expert_slot_cache_dev* c, int32_t wave, void* stream);

@@ -42,11 +42,12 @@ def _check_plan(layer, sim, idx):
     assert np.array_equal(hit_t, want_hit) and np.array_equal(miss_t, want_miss)
 
 
-def _eager(cfg, steps, n_slots, oracle_every=0):
+def _eager(cfg, steps, n_slots, oracle_every=0, freq_decay=0.0):
     router, experts = synth.gen_router(cfg), synth.gen_experts(cfg)
-    layer = MoELayer(cfg, router=router, experts=experts, device=DEV, pool_slots=n_slots, device_plan=True)
+    layer = MoELayer(cfg, router=router, experts=experts, device=DEV, pool_slots=n_slots, device_plan=True,
+                     freq_decay=freq_decay)
     resident = MoELayer(cfg, router=router, experts=experts, device=DEV)
-    sim = LRUSlotCache(cfg.E, n_slots)
+    sim = LRUSlotCache(cfg.E, n_slots, freq_decay=freq_decay)
     oexp = {}
     for step in range(steps):
         xs, x, lb, lb_dev = _inputs(cfg, step)
@@ -83,6 +84,16 @@ def test_device_plan_offload_shape():
     cfg = synth.get_config("offload_decode_bf16")
     sim = _eager(cfg, 4, cfg.n_slots)
     assert sim.stats.misses > 0 and sim.stats.waves > sim.stats.steps
+
+
+def test_device_plan_frequency_victims():
+    """Frequency-aware victims on the device: the same plans as the oracle, single and multi-wave."""
+    small = synth.get_config("offload_decode_bf16", E=16, d=256, F=256, T=8, k=4, zipf_epoch=6)
+    sim = _eager(small, 12, 5, oracle_every=4, freq_decay=0.8)
+    assert sim.stats.evictions > 0 and sim.stats.waves > sim.stats.steps
+    full = synth.get_config("offload_decode_bf16")
+    sim = _eager(full, 6, full.n_slots, freq_decay=0.8)
+    assert sim.stats.hits > 0
 
 
 def test_device_plan_waves_reuse_slots():
