@@ -256,14 +256,17 @@ def bench_stack(args, torch, B, synth, MoELayer):
     out = {}
     predictors = ["none"] + [p for p in args.prefetch.split(",") if p and p != "none"]
     for policy, predictor in [(pol, pr) for pol in args.policies.split(",") for pr in predictors]:
+        dev = policy.startswith("dev")   # planned on the device (no prefetch there)
+        if dev and predictor != "none":
+            continue
         key = f"{policy}/{predictor}"
         pool = SharedSlotPool([bundles] * L, n_slots, cfg.d, cfg.F, W_CODE[cfg.dtype],
-                              layer_order=policy.startswith("layer"),
-                              freq_decay=args.freq_decay if policy.endswith("freq") else 0.0)
+                              layer_order=policy.removeprefix("dev").startswith("layer"),
+                              freq_decay=args.freq_decay if policy.endswith("freq") else 0.0, device_plan=dev)
         layers = [MoELayer(c, router=r, experts=None, shared_pool=pool, layer_index=l)
                   for l, (c, r) in enumerate(zip(cfgs, routers))]
         t_wall = run(layers, pool, predictor)
-        st = pool.cache.stats()
+        st = (pool.cache_dev if dev else pool.cache).stats()
         acc = st["hits"] + st["misses"]
         out[key] = {"wall_s": round(t_wall, 4), "tokens_per_s": round(cfg.T * steps / t_wall, 1),
                           "ms_per_step": round(t_wall / steps * 1e3, 3),
@@ -274,7 +277,7 @@ def bench_stack(args, torch, B, synth, MoELayer):
                           "h2d_GB": round(st["h2d_bytes"] / 1e9, 3),
                           "h2d_GBps_wall": round(st["h2d_bytes"] / t_wall / 1e9, 2)}
         log(f"[bench] stack {key}: {out[key]}")
-        pool.cache.close()
+        (pool.cache_dev if dev else pool.cache).close()
         del layers, pool
         torch.cuda.empty_cache()
     best = max(out, key=lambda k: out[k]["tokens_per_s"])
@@ -414,9 +417,10 @@ def main():
     ap.add_argument("--prefetch-n", type=int, default=16, help="stack: experts the zipf predictor names")
     ap.add_argument("--freq-decay", type=float, default=0.8,
                     help="offload: decay of the routing frequency for the frequency-aware pool modes")
-    ap.add_argument("--policies", default="lru,layer,layerfreq",
+    ap.add_argument("--policies", default="lru,layer,layerfreq,devlayerfreq",
                     help="stack: victim choices to run (lru = plain LRU, layer = the layer that runs furthest "
-                         "ahead first, then LRU, layerfreq = the layer order, then decayed routing frequency)")
+                         "ahead first, then LRU, layerfreq = the layer order, then decayed routing frequency; "
+                         "a dev prefix plans on the device)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only time a plain device-to-device copy of this many MiB (HBM ceiling and the "
                          "reference for the FETCH_SIZE/WRITE_SIZE counters), then exit")

@@ -128,6 +128,7 @@ EXPORTS = {
     "expert_slot_cache_dev_reset": (ctypes.c_int32, [ctypes.c_void_p]),
     "expert_slot_cache_dev_max_waves": (ctypes.c_int32, [ctypes.c_void_p]),
     "expert_slot_cache_dev_set_frequency": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_double]),
+    "expert_slot_cache_dev_set_layers": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32]),
     "expert_slot_cache_dev_step": (ctypes.c_int32, [ctypes.c_void_p] * 5),
     "expert_slot_cache_dev_copy": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "expert_slot_cache_dev_join": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
@@ -491,6 +492,9 @@ class DeviceSlotCache:
 
     def set_frequency(self, decay: float):
         _check(lib().expert_slot_cache_dev_set_frequency(self.h, float(decay)))
+
+    def set_layers(self, n_layers: int):
+        _check(lib().expert_slot_cache_dev_set_layers(self.h, int(n_layers)))
 
     @property
     def max_waves(self) -> int:

@@ -30,7 +30,7 @@ constexpr int kPlanThreads = 1024;   // one thread per expert and per slot
 constexpr int kCopyThreads = 256;
 constexpr int kCopyBlocksPerBundle = 16;
 
-enum Ctl { kClock = 0, kSteps, kHits, kMisses, kEvictions, kWaves, kStepHits, kCopies, kCtlN };
+enum Ctl { kClock = 0, kSteps, kHits, kMisses, kEvictions, kWaves, kStepHits, kCopies, kMixed, kCtlN };
 
 struct DevState {
   int32_t* slot_of;   // [E]
@@ -40,6 +40,7 @@ struct DevState {
   int2* copies;       // [E] (expert, slot) of the last step's misses, in miss order (up to E of them)
   double* freq;       // [E] decayed routed rows (used when decay > 0)
   double* decay;      // [1] frequency decay, read by every plan (graphs see changes); 0 = LRU
+  int64_t* layers;    // [1] layer order: entries are this many layer-major groups (1 = none)
 };
 
 // Rank of this thread's flag among the block's set flags (ascending thread
@@ -95,6 +96,7 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t*
   __shared__ double slot_freq[kPlanThreads];
   const int t = threadIdx.x;
   const double decay = *st.decay;
+  const int L = (int)*st.layers, per = E / L;
   bool touched = false, resident = false;
   int my_slot = -1;
   if (t < E && decay > 0.0) {
@@ -111,6 +113,15 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t*
   const int hit_rank = block_rank(touched && resident, wave_cnt, &n_hit);
   const int miss_rank = block_rank(touched && !resident, wave_cnt, &n_miss);
   const long long clock = st.ctl[kClock];
+  int layer = 0;  // the step's layer (layer order only): that of its lowest touched entry
+  if (L > 1) {
+    const long long lo = block_min(touched ? (long long)t : LLONG_MAX, wave_min);
+    const long long hi = -block_min(touched ? -(long long)t : LLONG_MAX, wave_min);
+    if (lo != LLONG_MAX) {
+      layer = (int)(lo / per);
+      if (hi / per != layer && t == 0) st.ctl[kMixed] += 1;  // reported by stats
+    }
+  }
   if (t < S) {
     int o = st.owner[t];
     if (o >= E) o = -1;
@@ -132,9 +143,16 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(const int32_t*
     long long key = t < S && !occupied ? (long long)t : LLONG_MAX;
     long long m = block_min(key, wave_min);
     if (m == LLONG_MAX) {  // block-uniform: no free slot
-      const long long fbits = cand ? (long long)__double_as_longlong(slot_freq[t]) : LLONG_MAX;
+      bool keep_d = cand;
+      if (L > 1) {  // the layer whose next step is furthest away: (layer - current - 1) mod L largest
+        const int dist = cand ? ((slot_owner[t] / per - layer - 1) % L + L) % L : 0;
+        const long long dkey = cand ? (long long)(L - 1 - dist) : LLONG_MAX;
+        const long long md = block_min(dkey, wave_min);
+        keep_d = cand && dkey == md;
+      }
+      const long long fbits = keep_d ? (long long)__double_as_longlong(slot_freq[t]) : LLONG_MAX;
       const long long mf = decay > 0.0 ? block_min(fbits, wave_min) : 0;
-      const bool keep = cand && (decay > 0.0 ? fbits == mf : true);
+      const bool keep = keep_d && (decay > 0.0 ? fbits == mf : true);
       key = keep ? slot_stamp[t] : LLONG_MAX;
       m = block_min(key, wave_min);
       if (!keep) key = LLONG_MIN;  // never equal to m
@@ -217,6 +235,7 @@ struct expert_slot_cache_dev {
   hipStream_t side = nullptr;
   int max_waves = 1;
   double decay = 0.0;
+  int n_layers = 1;
   std::vector<hipEvent_t> fork, join;  // per wave
   void* block = nullptr;  // device: state, copy list and source pointers
   DevState st{};
@@ -245,6 +264,8 @@ moe_status init_state(expert_slot_cache_dev* c) {
   std::vector<double> fzero(E, 0.0);
   MOE_HIP(hipMemcpy(c->st.freq, fzero.data(), sizeof(double) * E, hipMemcpyHostToDevice));
   MOE_HIP(hipMemcpy(c->st.decay, &c->decay, sizeof(double), hipMemcpyHostToDevice));
+  const int64_t layers = c->n_layers;
+  MOE_HIP(hipMemcpy(c->st.layers, &layers, sizeof(int64_t), hipMemcpyHostToDevice));
   c->stepped = false;
   return MOE_OK;
 }
@@ -333,6 +354,7 @@ extern "C" moe_status expert_slot_cache_dev_create(const moe_cache_cfg* cfg, exp
   c->st.freq = reinterpret_cast<double*>(p);
   p += align_up(sizeof(double) * E, 256);
   c->st.decay = reinterpret_cast<double*>(p);
+  c->st.layers = reinterpret_cast<int64_t*>(p + 8);
   if ((e = hipMemcpy(c->src, src.data(), sizeof(void*) * E, hipMemcpyHostToDevice)) != hipSuccess)
     return fail("hipMemcpy", e);
   if (moe_status s = init_state(c)) {
@@ -369,6 +391,18 @@ extern "C" moe_status expert_slot_cache_dev_set_frequency(expert_slot_cache_dev*
   MOE_HIP(hipMemcpy(c->st.freq, fzero.data(), sizeof(double) * c->cfg.n_experts, hipMemcpyHostToDevice));
   MOE_HIP(hipMemcpy(c->st.decay, &decay, sizeof(double), hipMemcpyHostToDevice));
   c->decay = decay;
+  return MOE_OK;
+}
+
+extern "C" moe_status expert_slot_cache_dev_set_layers(expert_slot_cache_dev* c, int32_t n_layers) {
+  clear_error();
+  MOE_REQUIRE(c, MOE_EINVAL, "expert_slot_cache_dev_set_layers: NULL cache");
+  MOE_REQUIRE(n_layers >= 1 && c->cfg.n_experts % n_layers == 0, MOE_EINVAL,
+              "expert_slot_cache_dev_set_layers: n_layers=%d must divide n_experts=%d", n_layers, c->cfg.n_experts);
+  MOE_HIP(hipDeviceSynchronize());
+  const int64_t layers = n_layers;
+  MOE_HIP(hipMemcpy(c->st.layers, &layers, sizeof(int64_t), hipMemcpyHostToDevice));
+  c->n_layers = n_layers;
   return MOE_OK;
 }
 
@@ -430,5 +464,8 @@ extern "C" moe_status expert_slot_cache_dev_stats(expert_slot_cache_dev* c, moe_
   out->evictions = ctl[kEvictions];
   out->waves = ctl[kWaves];
   out->h2d_bytes = ctl[kMisses] * c->cfg.bundle_bytes;
+  MOE_REQUIRE(ctl[kMixed] == 0, MOE_ESTATE,
+              "expert_slot_cache_dev_stats: %lld steps touched entries of several layers under the layer order",
+              (long long)ctl[kMixed]);
   return MOE_OK;
 }

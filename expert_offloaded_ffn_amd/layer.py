@@ -67,7 +67,8 @@ class SharedSlotPool:
     layer_order: victims from the layer that runs furthest ahead, then LRU (expert_slot_cache_set_layers);
     else plain LRU. freq_decay: victims by decayed routing frequency before recency (0 = off)."""
 
-    def __init__(self, bundles_per_layer, n_slots, d, F, w_dtype, device="cuda", layer_order=False, freq_decay=0.0):
+    def __init__(self, bundles_per_layer, n_slots, d, F, w_dtype, device="cuda", layer_order=False, freq_decay=0.0,
+                 device_plan=False):
         self.L = len(bundles_per_layer)
         self.E = len(bundles_per_layer[0])
         self.d, self.F, self.w_code = d, F, w_dtype
@@ -78,15 +79,26 @@ class SharedSlotPool:
         self.slot_pool = torch.empty(n_slots, self.stride, dtype=torch.uint8, device=self.device)
         self.slot_table = torch.full((self.L * self.E,), -1, dtype=torch.int32, device=self.device)
         self.counts = torch.zeros(self.L * self.E, dtype=torch.int32, device=self.device)
-        self.cache = B.SlotCache(self.L * self.E, n_slots, self.bundle_bytes, self.stride, flat, self.slot_pool)
+        self.cache = self.cache_dev = None
+        if device_plan:   # planned on the device: one hit table and one miss table per wave
+            self.cache_dev = B.DeviceSlotCache(self.L * self.E, n_slots, self.bundle_bytes, self.stride, flat,
+                                               self.slot_pool)
+            self.miss_slot_tables = torch.full((self.cache_dev.max_waves, self.L * self.E), -1, dtype=torch.int32,
+                                               device=self.device)
+            policy = self.cache_dev
+        else:
+            self.cache = B.SlotCache(self.L * self.E, n_slots, self.bundle_bytes, self.stride, flat, self.slot_pool)
+            policy = self.cache
         if layer_order:   # evict from the layer that runs furthest ahead, then LRU
-            self.cache.set_layers(self.L)
+            policy.set_layers(self.L)
         if freq_decay:    # then by decayed routing frequency, then LRU
-            self.cache.set_frequency(freq_decay)
+            policy.set_frequency(freq_decay)
 
-    def table(self, layer: int):
-        """The expert table of one layer: its E entries of the shared slot table."""
-        view = self.slot_table[layer * self.E:(layer + 1) * self.E]
+    def table(self, layer: int, slots=None):
+        """The expert table of one layer: its E entries of the shared slot table (or of `slots`,
+        a per-wave miss table of the device plan)."""
+        slots = self.slot_table if slots is None else slots
+        view = slots[layer * self.E:(layer + 1) * self.E]
         return B.expert_table(self.slot_pool, self.stride, view, self.E, self.d, self.F, self.w_code)
 
 
@@ -124,14 +136,18 @@ class MoELayer:
         self.select_bias = None if select_bias is None else torch.from_numpy(select_bias).to(self.device)
         self.cache = None
         self.cache_dev = None
-        self.cache_base = None
+        self.cache_base = None   # first cache entry of this layer in a shared pool
         if shared_pool is not None:
             self.cache = shared_pool.cache
+            self.cache_dev = shared_pool.cache_dev
             self.cache_base = layer_index * self.E
             self.slot_table = shared_pool.slot_table
             self.counts_all = shared_pool.counts
             self.table = shared_pool.table(layer_index)
             self.bundle_bytes = shared_pool.bundle_bytes
+            if self.cache_dev is not None:
+                self.miss_slot_tables = shared_pool.miss_slot_tables
+                self.miss_tables = [shared_pool.table(layer_index, t) for t in shared_pool.miss_slot_tables]
         else:
             bundles = pack_bundles(cfg, experts, self.d, self.F, pin=pool_slots is not None, threads=threads)
             self.bundle_bytes = bundles[0].numel()
@@ -272,7 +288,12 @@ class MoELayer:
         elif self.cache_dev is not None:
             # plan on the device; the hits run while the misses' copy kernel reads host memory
             fws = self._buf("ffn_ws", B.grouped_ffn_workspace_size(self.table, rows, a_code))
-            self.cache_dev.step(r["counts"], self.slot_table, self.miss_slot_tables, stream=main)
+            counts = r["counts"]
+            if self.cache_base is not None:   # this layer's histogram into the stack-wide one
+                self.counts_all.zero_()
+                self.counts_all[self.cache_base:self.cache_base + E].copy_(counts)
+                counts = self.counts_all
+            self.cache_dev.step(counts, self.slot_table, self.miss_slot_tables, stream=main)
             ffn = lambda table: B.grouped_ffn(table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
                                               a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt, ws=fws,
                                               stream=main)

@@ -536,6 +536,11 @@ int32_t expert_slot_cache_dev_max_waves(const expert_slot_cache_dev* c);   /* ce
  * synchronises the device and clears the frequencies; the decay lives in device
  * memory, so graphs captured before see the new value. Errors: MOE_EINVAL. */
 moe_status expert_slot_cache_dev_set_frequency(expert_slot_cache_dev* c, double decay);
+/* The layer order, as expert_slot_cache_set_layers, applied before the
+ * frequency and recency stages; a step's layer is that of its lowest touched
+ * entry, and steps touching several layers are reported by stats (MOE_ESTATE).
+ * Synchronises the device; kept in device memory like the decay. */
+moe_status expert_slot_cache_dev_set_layers(expert_slot_cache_dev* c, int32_t n_layers);
 moe_status expert_slot_cache_dev_step(expert_slot_cache_dev* c, const int32_t* counts, void* stream,
                                       int32_t* hit_table, int32_t* miss_tables);
 moe_status expert_slot_cache_dev_copy(expert_slot_cache_dev* c, int32_t wave, void* stream);

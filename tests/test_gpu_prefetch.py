@@ -99,3 +99,55 @@ def test_stack_layer_order_plans_and_outputs():
     _, lo = _stack(4, 20, 8, prefetch=True, layer_order=True, check_every=7, **shape)
     _, lru = _stack(4, 20, 8, prefetch=True, **shape)
     assert lo.stats.misses + lo.stats.prefetches < lru.stats.misses + lru.stats.prefetches
+
+
+def _stack_device(L, n_slots, steps, *, layer_order, freq_decay, **shape):
+    base = synth.get_config("offload_decode_bf16", **shape)
+    cfgs = synth.stack_configs(base, L)
+    experts = synth.gen_experts(base)
+    bundles = pack_bundles(base, experts, base.d, base.F, pin=True)
+    pool = SharedSlotPool([bundles] * L, n_slots, base.d, base.F, W_CODE["bf16"], device=DEV,
+                          layer_order=layer_order, freq_decay=freq_decay, device_plan=True)
+    routers = [synth.gen_router(c) for c in cfgs]
+    layers = [MoELayer(c, router=r, experts=None, device=DEV, shared_pool=pool, layer_index=l)
+              for l, (c, r) in enumerate(zip(cfgs, routers))]
+    resident = [MoELayer(c, router=r, experts=experts, device=DEV) for c, r in zip(cfgs, routers)]
+    E = base.E
+    sim = LRUSlotCache(L * E, n_slots, n_layers=L if layer_order else 1, freq_decay=freq_decay)
+    for step in range(steps):
+        for l in range(L):
+            cfg = cfgs[l]
+            xs = synth.gen_x(cfg, step)
+            x = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).to(DEV)
+            lb = torch.from_numpy(synth.zipf_logit_bias(cfg, step)).to(DEV)
+            say(f"  case device-planned stack L={L} slots={n_slots} layer_order={layer_order} decay={freq_decay} "
+                f"step={step} layer={l}: launching")
+            g = layers[l].forward(x, logit_bias=lb)
+            ref = resident[l].forward(x, logit_bias=lb)
+            torch.cuda.synchronize()
+            idx = check_exact_indices(cfg, g["route"], g["perm"], cfg.T)
+            plan = sim.step((l * E + idx).ravel())
+            want_hit = np.full(L * E, -1)
+            want_miss = np.full(tuple(pool.miss_slot_tables.shape), -1)
+            for w, wave in enumerate(plan.waves):
+                for en in wave:
+                    if en.hit:
+                        want_hit[en.expert] = en.slot
+                    else:
+                        want_miss[w, en.expert] = en.slot
+            assert np.array_equal(to_np(pool.slot_table), want_hit)
+            assert np.array_equal(to_np(pool.miss_slot_tables), want_miss)
+            assert np.array_equal(to_np(g["out"]), to_np(ref["out"])), "device-planned stack differs from resident"
+    st, s = pool.cache_dev.stats(), sim.stats
+    assert (st["hits"], st["misses"], st["evictions"], st["waves"]) == (s.hits, s.misses, s.evictions, s.waves)
+    pool.cache_dev.close()
+    return sim
+
+
+@pytest.mark.parametrize("layer_order,decay", [(True, 0.0), (True, 0.8), (False, 0.8)])
+def test_stack_device_planned_policies(layer_order, decay):
+    """The device planner with the layer order and / or frequency-aware victims over a shared
+    pool: every layer step's tables equal the oracle's, outputs equal all-resident."""
+    sim = _stack_device(4, 8, 6, layer_order=layer_order, freq_decay=decay, E=16, d=256, F=256, T=4, k=4,
+                        zipf_epoch=3)
+    assert sim.stats.evictions > 0 and sim.stats.waves > sim.stats.steps
