@@ -418,3 +418,22 @@ def test_profile_label_validation():
     assert L.moe_profile_label(1) == 0
     assert L.moe_profile_label(0) == 0
     assert ctypes.sizeof(B.Profile) == 8 * 8 + 8 * 8   # ms[8] doubles, launches[8] int64
+
+
+def test_device_cache_validation_without_a_device():
+    """Argument checks of the device-planned cache fail before any HIP call."""
+    L = B.lib()
+    h = ctypes.c_void_p()
+    for blocking, dry_run, E, S, nb in [(1, 0, 8, 2, 1024), (0, 1, 8, 2, 1024), (0, 0, 0, 2, 1024),
+                                        (0, 0, 2048, 2, 1024), (0, 0, 8, 0, 1024), (0, 0, 8, 2, 1000)]:
+        cfg = B.CacheCfg(E, S, nb, 1024, None, None, blocking, dry_run)
+        st = L.expert_slot_cache_dev_create(ctypes.byref(cfg), ctypes.byref(h))
+        assert st in (-1, -4), (blocking, dry_run, E, S, nb, st)
+        assert not h.value
+    assert L.expert_slot_cache_dev_set_frequency(None, 0.5) == -1
+    assert L.expert_slot_cache_dev_set_layers(None, 2) == -1
+    assert L.expert_slot_cache_dev_step(None, None, None, None, None) == -1
+    assert L.expert_slot_cache_dev_copy(None, 0, None) == -1
+    assert L.expert_slot_cache_dev_join(None, 0, None) == -1
+    assert L.expert_slot_cache_dev_max_waves(None) == 0
+    assert L.expert_slot_cache_dev_destroy(None) == 0
