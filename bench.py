@@ -352,6 +352,19 @@ def bench_decode(args, torch, B, synth, MoELayer):
     prof = B.profile_read()
     B.profile_enable(False)
     ms = np.array([a.elapsed_time(b) for a, b in evs])
+    if graph is not None:
+        # kernel events cannot be taken inside a replay: the same steps once more as eager
+        # launches, each after the same cache flush, time the kernels for the roofline
+        B.profile_enable(True)
+        for i in range(args.steps):
+            if args.mall_flush == "write":
+                flush.fill_(i & 255)
+            else:
+                flush_words.max()
+            layer.forward(xs[i % nb])
+        torch.cuda.synchronize()
+        prof = B.profile_read()
+        B.profile_enable(False)
     step_bytes = np.array([touched[i % nb] * bundle + shared_bytes + act for i in range(args.steps)], np.float64)
     # the decode gate/up launch streams the touched routed experts' W_gu, and the shared
     # expert's when the layer runs it inside the same launch
@@ -383,7 +396,8 @@ def bench_decode(args, torch, B, synth, MoELayer):
                               "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
-                              "work_per_launch": f"gate/up weight bytes of the touched {who}"}
+                              "work_per_launch": f"gate/up weight bytes of the touched {who}",
+                              "timed": "eager launches of the same steps" if graph is not None else "the timed steps"}
     print(json.dumps(result), flush=True)
     return 0
 
