@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; HBM TB/s (decode) & MFMA TFLOP/s (prefill) vs peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+PEAK_PCIE_GBS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 encoding
 PEAK_HBM_GBS = 8000.0
 WORKLOADS = ["mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16",
              "offload_decode_mxfp4"]
@@ -201,6 +202,13 @@ def bench_offload(args, torch, B, synth, MoELayer):
                    "bundle_bytes": B.bundle_bytes(cfg.d, cfg.F, W_CODE[cfg.dtype])},
         "resident_compute_s": round(t_comp, 4), "offload": out,
     }
+    h2d = o.get("h2d_bytes", 0)
+    if h2d:
+        a = h2d / o["wall_s"] / 1e9
+        result["roofline"] = {"bound": "pcie", "kernel": "host-to-HBM bundle copies of the missed experts",
+                              "achieved": round(a, 2), "peak": PEAK_PCIE_GBS, "unit": "GB/s",
+                              "frac": round(a / PEAK_PCIE_GBS, 4), "traffic": None,
+                              "work_per_launch": "bundle bytes of the step's misses over the whole run's wall time"}
     print(json.dumps(result), flush=True)
     return 0
 
