@@ -300,6 +300,12 @@ def bench_stack(args, torch, B, synth, MoELayer):
                    "bundle_bytes": B.bundle_bytes(cfg.d, cfg.F, W_CODE[cfg.dtype])},
         "resident_compute_s": round(t_comp, 4), "stack": out,
     }
+    b = out[best]
+    if b["h2d_GB"] > 0:
+        result["roofline"] = {"bound": "pcie", "kernel": "host-to-HBM bundle copies of the missed experts",
+                              "achieved": b["h2d_GBps_wall"], "peak": PEAK_PCIE_GBS, "unit": "GB/s",
+                              "frac": round(b["h2d_GBps_wall"] / PEAK_PCIE_GBS, 4), "traffic": None,
+                              "work_per_launch": "bundle bytes copied (misses and prefetches) over the run's wall time"}
     print(json.dumps(result), flush=True)
     return 0
 
