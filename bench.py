@@ -3,8 +3,16 @@
 
 A step is one pass of the whole layer (route -> permute -> grouped SwiGLU FFN ->
 combine, plus the shared expert where the workload has one) over one batch of
-synthetic tokens already resident in HBM. Default workload: the Mixtral-8x7B-shaped
-prefill layer (T=4096, d=4096, E=8, top-2 softmax, F=14336, bf16).
+synthetic tokens already resident in HBM.
+
+With no --workload the suite runs: the headline line is the DeepSeek-V3-shaped fp8
+prefill layer (T=8192, d=7168, E=256, top-8 grouped sigmoid, F=2048 plus a shared
+expert; the largest workload that fits one GPU), timed for exactly --steps steps after
+--warmup; its "configs" object carries the other workloads measured in the same run,
+each with its own roofline, step-time percentiles and CPU baseline: the
+Mixtral-8x7B-shaped bf16 prefill, the Qwen1.5-MoE-shaped bf16 decode at 1, 8 and 64
+tokens (graph replays), and the expert-offload decode through a 32-slot LRU pool (256
+steps; blocking and device-planned modes beside it).
 
 Prints one JSON line: tokens/s for the whole job, the dominant kernel's roofline
 (algorithmic flops or bytes per launch over its average duration, timed with hipEvents
@@ -30,7 +38,7 @@ METRIC = "MoE-layer tokens/s; HBM TB/s (decode) & MFMA TFLOP/s (prefill) vs peak
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 PEAK_PCIE_GBS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 encoding
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = ["mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16",
+WORKLOADS = ["suite", "mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16",
              "offload_decode_mxfp4"]
 
 
@@ -69,8 +77,20 @@ def _x_dev(cfg, x_store, torch):
     return torch.from_numpy(x_store.view(np.int16)).view(torch.bfloat16).to("cuda")
 
 
-def cpu_baseline(cfg, w, sample_tokens):
-    """The float64 oracle, as it stands, on the first `sample_tokens` tokens of batch 0."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, w, sample_tokens, logit_bias=False):
+    """The float64 oracle, as it stands, on the first `sample_tokens` tokens of batches 0, 1, ...
+    (with logit_bias, batch i takes the Zipf prior of decode step i, as the offload stream does)."""
     from oracle import formats, moe  # CPU baseline leg only
 
     def dec(a):
@@ -94,112 +114,153 @@ def cpu_baseline(cfg, w, sample_tokens):
     from expert_offloaded_ffn_amd import synth
     nb = (sample_tokens + cfg.T - 1) // cfg.T
     x_store = np.concatenate([synth.gen_x(cfg, i) for i in range(nb)])[:sample_tokens]
+    lb = None
+    if logit_bias:
+        lb = np.concatenate([np.repeat(synth.zipf_logit_bias(cfg, i)[None], cfg.T, 0) for i in range(nb)])
+        lb = lb[:sample_tokens].astype(np.float64)
     t0 = time.perf_counter()
     x = dec(x_store)
-    r = moe.route(x, dec(w["router"]), k=cfg.k, score_fn=cfg.score_fn, renormalize=bool(cfg.renormalize),
-                  route_scale=cfg.route_scale, n_groups=cfg.n_groups, topk_groups=cfg.topk_groups,
-                  group_topn=cfg.group_topn, select_bias=w.get("sb"),
-                  w_shared_gate=None if w["w_sg"] is None else dec(w["w_sg"]))
+    route_kw = dict(k=cfg.k, score_fn=cfg.score_fn, renormalize=bool(cfg.renormalize), route_scale=cfg.route_scale,
+                    n_groups=cfg.n_groups, topk_groups=cfg.topk_groups, group_topn=cfg.group_topn,
+                    select_bias=w.get("sb"), w_shared_gate=None if w.get("w_sg") is None else dec(w["w_sg"]))
+    if lb is None:
+        r = moe.route(x, dec(w["router"]), **route_kw)
+    else:   # one routing call per batch: the prior differs between steps
+        rs = [moe.route(x[i:i + cfg.T], dec(w["router"]), logit_bias=lb[i], **route_kw)
+              for i in range(0, sample_tokens, cfg.T)]
+        r = moe.Routing(*[None if getattr(rs[0], f) is None else np.concatenate([getattr(q, f) for q in rs])
+                          for f in ("logits", "keys", "idx", "gate", "shared_gate")])
 
     def expert(e):
         return moe.ExpertWeights(*[dec_w(m) for m in w["experts"][e]])
 
-    shared = None if w["shared"] is None else moe.ExpertWeights(*[dec_w(m) for m in w["shared"]])
+    shared = None if w.get("shared") is None else moe.ExpertWeights(*[dec_w(m) for m in w["shared"]])
     moe.moe_layer(x, r, expert, cfg.E, shared=shared, quant_act=cfg.dtype == "fp8")
     dt = time.perf_counter() - t0
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
+            "kind": "oracle",
             "sample": f"first {sample_tokens} tokens of batches 0.. of {cfg.name} (T={cfg.T}), float64, "
                       f"expert weights decoded per expert; {dt:.1f} s"}
 
 
-def bench_offload(args, torch, B, synth, MoELayer):
+def percentiles(ms):
+    return [round(float(np.percentile(ms, q)), 4) for q in (10, 50, 90)]
+
+
+OFFLOAD_MODES = ("overlapped", "blocking", "overlapped_freq", "device_plan", "device_plan_graph",
+                 "device_plan_freq_graph")
+
+
+def bench_offload(args, torch, B, synth, MoELayer, modes=OFFLOAD_MODES, cpu_sample=0):
     """Expert-offload decode: T tokens per step through an n_slots HBM slot pool fed from pinned host
-    bundles, Zipf-biased routing re-drawn every zipf_epoch steps. The same steps run these ways: all
-    experts resident (compute time), slot pool with overlapped copies, slot pool in blocking mode,
-    slot pool with overlapped copies and frequency-aware victims (--freq-decay),
-    and the pool planned on the device (copy kernels, no host synchronisation), eager and as one
-    graph replay per step. The device-planned graph replays start from an empty pool, as the
-    others do."""
+    bundles, Zipf-biased routing re-drawn every zipf_epoch steps. The same steps run with every
+    expert resident (compute time) and then in each of `modes`: the host-planned LRU pool with
+    overlapped copies (the pages' design, and the line's value), the same pool in blocking mode
+    (a wave's copies start after all compute before them: the overlap reference), overlapped with
+    frequency-aware victims (--freq-decay), and the pool planned on the device (copy kernels, no
+    host synchronisation), eager and as one graph replay per step, with LRU and frequency-aware
+    victims. Every mode starts from an empty pool. Returns the result dict."""
     from expert_offloaded_ffn_amd.layer import W_CODE
-    cfg = synth.get_config(args.workload)
+    cfg = synth.get_config(args.workload if args.workload.startswith("offload") else "offload_decode_bf16")
     if args.tokens:
         cfg = cfg.with_T(args.tokens)
-    steps = args.steps
-    log(f"[bench] offload: generating {cfg.E} experts")
+    steps = cfg.steps if args.workload == "suite" else args.steps
+    log(f"[bench] offload {cfg.name}: generating {cfg.E} experts")
     router, experts = synth.gen_router(cfg), synth.gen_experts(cfg, threads=16)
     xs = [_x_dev(cfg, synth.gen_x(cfg, s), torch) for s in range(steps)]
     lbs = [torch.from_numpy(synth.zipf_logit_bias(cfg, s)).to("cuda") for s in range(steps)]
 
     def run(layer):
+        """Wall time of the steps, and each step's span from hipEvents on the compute stream."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for s in range(steps):
+            evs[s][0].record()
             layer.forward(xs[s], logit_bias=lbs[s])
+            evs[s][1].record()
         torch.cuda.synchronize()
-        return time.perf_counter() - t0
+        return time.perf_counter() - t0, np.array([a.elapsed_time(b) for a, b in evs])
 
     res = MoELayer(cfg, router=router, experts=experts, threads=16)
     for s in range(min(3, steps)):
         res.forward(xs[s], logit_bias=lbs[s])
-    t_comp = run(res)
+    t_comp, _ = run(res)
     del res
     torch.cuda.empty_cache()
     out = {}
-    for mode, blocking, decay in (("overlapped", False, 0.0), ("blocking", True, 0.0),
-                                  ("overlapped_freq", False, args.freq_decay)):
+    host_modes = {"overlapped": (False, 0.0), "blocking": (True, 0.0), "overlapped_freq": (False, args.freq_decay)}
+    for mode in [m for m in modes if m in host_modes]:
+        blocking, decay = host_modes[mode]
+        log(f"[bench] offload mode {mode}")
         lay = MoELayer(cfg, router=router, experts=experts, pool_slots=cfg.n_slots, blocking=blocking, threads=16,
                        freq_decay=decay)
-        t_wall = run(lay)
+        t_wall, ms = run(lay)
         st = lay.cache.stats()
         t_copy = st["copy_ms"] / 1e3
         acc = st["hits"] + st["misses"]
         out[mode] = {"wall_s": round(t_wall, 4), "tokens_per_s": round(cfg.T * steps / t_wall, 1),
+                     "step_ms_p10_p50_p90": percentiles(ms),
                      "hit_rate": round(st["hits"] / max(acc, 1), 4), "hits": st["hits"], "misses": st["misses"],
                      "evictions": st["evictions"], "waves": st["waves"], "h2d_bytes": st["h2d_bytes"],
-                     "d2h_bytes": st["d2h_bytes"], "copy_s": round(t_copy, 4),
+                     "d2h_bytes": st["d2h_bytes"], "copy_s": round(t_copy, 4), "wait_s": round(st["wait_ms"] / 1e3, 4),
                      "h2d_GBps": round(st["h2d_bytes"] / max(t_copy, 1e-9) / 1e9, 2),
                      "overlap": round(max(0.0, (t_copy + t_comp - t_wall) / max(min(t_copy, t_comp), 1e-9)), 4)}
         lay.cache.close()
         del lay
         torch.cuda.empty_cache()
-    # the device-planned pool: no host synchronisation; eager, then every step one graph replay
-    # (LRU, then frequency-aware victims)
-    lay = MoELayer(cfg, router=router, experts=experts, pool_slots=cfg.n_slots, device_plan=True, threads=16)
-    t_wall = run(lay)
-    st = lay.cache_dev.stats()
-    lay.cache_dev.reset()
-    x_static, lb_static = xs[0].clone(), lbs[0].clone()
-    graph, _ = lay.capture(x_static, lb_static)
-    timed = [("device_plan", t_wall, st)]
-    for mode, decay in (("device_plan_graph", 0.0), ("device_plan_freq_graph", args.freq_decay)):
-        lay.cache_dev.set_frequency(decay)
+    dev_modes = [m for m in modes if m.startswith("device_plan")]
+    if dev_modes:
+        # the device-planned pool: no host synchronisation; eager, then every step one graph replay
+        log(f"[bench] offload modes {dev_modes}")
+        lay = MoELayer(cfg, router=router, experts=experts, pool_slots=cfg.n_slots, device_plan=True, threads=16)
+        timed = []
+        t_wall, ms = run(lay)
+        if "device_plan" in dev_modes:
+            timed.append(("device_plan", t_wall, ms, lay.cache_dev.stats()))
         lay.cache_dev.reset()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(steps):
-            x_static.copy_(xs[s])
-            lb_static.copy_(lbs[s])
-            graph.replay()
-        torch.cuda.synchronize()
-        timed.append((mode, time.perf_counter() - t0, lay.cache_dev.stats()))
-    for mode, t, stt in timed:
-        acc = stt["hits"] + stt["misses"]
-        out[mode] = {"wall_s": round(t, 4), "tokens_per_s": round(cfg.T * steps / t, 1),
-                     "hit_rate": round(stt["hits"] / max(acc, 1), 4), "hits": stt["hits"], "misses": stt["misses"],
-                     "evictions": stt["evictions"], "waves": stt["waves"], "h2d_bytes": stt["h2d_bytes"],
-                     "h2d_GBps_wall": round(stt["h2d_bytes"] / t / 1e9, 2)}
-    lay.cache_dev.close()
-    del lay, graph
-    torch.cuda.empty_cache()
-    best = max((m for m in out if m != "blocking"), key=lambda m: out[m]["tokens_per_s"])
-    o = out[best]
+        x_static, lb_static = xs[0].clone(), lbs[0].clone()
+        graph, _ = lay.capture(x_static, lb_static)
+        for mode, decay in (("device_plan_graph", 0.0), ("device_plan_freq_graph", args.freq_decay)):
+            if mode not in dev_modes:
+                continue
+            lay.cache_dev.set_frequency(decay)
+            lay.cache_dev.reset()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(steps):
+                x_static.copy_(xs[s])
+                lb_static.copy_(lbs[s])
+                evs[s][0].record()
+                graph.replay()
+                evs[s][1].record()
+            torch.cuda.synchronize()
+            timed.append((mode, time.perf_counter() - t0, np.array([a.elapsed_time(b) for a, b in evs]),
+                          lay.cache_dev.stats()))
+        for mode, t, ms, stt in timed:
+            acc = stt["hits"] + stt["misses"]
+            out[mode] = {"wall_s": round(t, 4), "tokens_per_s": round(cfg.T * steps / t, 1),
+                         "step_ms_p10_p50_p90": percentiles(ms),
+                         "hit_rate": round(stt["hits"] / max(acc, 1), 4), "hits": stt["hits"],
+                         "misses": stt["misses"], "evictions": stt["evictions"], "waves": stt["waves"],
+                         "h2d_bytes": stt["h2d_bytes"], "h2d_GBps_wall": round(stt["h2d_bytes"] / t / 1e9, 2)}
+        lay.cache_dev.close()
+        del lay, graph
+        torch.cuda.empty_cache()
+    # the line's value is the pages' design: LRU over the host-planned pool with overlapped
+    # copies; the other modes are reported beside it
+    main_mode = "overlapped" if "overlapped" in out else next(iter(out))
+    o = out[main_mode]
     result = {
         "metric": METRIC, "value": o["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": 0,
-        "ms_per_step": round(o["wall_s"] / steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded; Zipf(1.1) log-prior re-drawn every 64 steps)",
+        "ms_per_step": round(o["wall_s"] / steps * 1e3, 4), "step_ms_p10_p50_p90": o["step_ms_p10_p50_p90"],
+        "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded; Zipf(1.1) log-prior re-drawn every 64 steps)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
-                   "d_ff": cfg.F, "n_slots": cfg.n_slots, "weights": cfg.dtype, "mode": best,
+                   "d_ff": cfg.F, "n_slots": cfg.n_slots, "weights": cfg.dtype, "policy": "lru", "mode": main_mode,
                    "bundle_bytes": B.bundle_bytes(cfg.d, cfg.F, W_CODE[cfg.dtype])},
+        "hit_rate": o["hit_rate"], "h2d_bytes": o["h2d_bytes"], "overlap": o.get("overlap"),
         "resident_compute_s": round(t_comp, 4), "offload": out,
     }
     h2d = o.get("h2d_bytes", 0)
@@ -209,8 +270,10 @@ def bench_offload(args, torch, B, synth, MoELayer):
                               "achieved": round(a, 2), "peak": PEAK_PCIE_GBS, "unit": "GB/s",
                               "frac": round(a / PEAK_PCIE_GBS, 4), "traffic": None,
                               "work_per_launch": "bundle bytes of the step's misses over the whole run's wall time"}
-    print(json.dumps(result), flush=True)
-    return 0
+    if cpu_sample:
+        log(f"[bench] cpu baseline: oracle on {cpu_sample} tokens")
+        result["cpu_baseline"] = cpu_baseline(cfg, dict(router=router, experts=experts), cpu_sample, logit_bias=True)
+    return result
 
 
 def bench_stack(args, torch, B, synth, MoELayer):
@@ -310,17 +373,22 @@ def bench_stack(args, torch, B, synth, MoELayer):
     return 0
 
 
-def bench_decode(args, torch, B, synth, MoELayer):
+def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=None, warmup=None, graph=None,
+                 cpu_sample=0):
     """Decode layer (few tokens): each step's time is measured alone with hipEvents, after a
     512 MiB pass that evicts the 256 MB last-level cache, so weights stream from HBM (a read by
     default, leaving clean lines as other layers' weight reads would; --mall-flush write leaves
     dirty lines that the step's own reads must first write back). The
     roofline is HBM bytes: the distinct touched experts' bundles + the shared expert + router
-    weights + activations in and out."""
+    weights + activations in and out. Returns the result dict."""
     from expert_offloaded_ffn_amd.layer import FUSE_COMBINE_MAX_T, W_CODE
-    cfg = synth.get_config(args.workload)
-    if args.tokens:
-        cfg = cfg.with_T(args.tokens)
+    workload = workload or args.workload
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    use_graph = args.graph if graph is None else graph
+    cfg = synth.get_config(workload)
+    if T or args.tokens:
+        cfg = cfg.with_T(T or args.tokens)
     log(f"[bench] decode {cfg.name} T={cfg.T}: generating inputs")
     w = dict(router=synth.gen_router(cfg), experts=synth.gen_experts(cfg, threads=16),
              shared=synth.gen_shared(cfg) if cfg.F_shared else None,
@@ -338,18 +406,18 @@ def bench_decode(args, torch, B, synth, MoELayer):
     for x in xs:
         c = B.route(x, layer.w_router_t, **layer.route_args())["counts"].cpu().numpy()
         touched.append(int((c > 0).sum()))
-    for i in range(args.warmup):
+    for i in range(warmup):
         layer.forward(xs[i % nb])
     torch.cuda.synchronize()
     graph = None
-    if args.graph:
+    if use_graph:
         # the whole layer as one HIP graph; inputs are refilled in place before each replay
         x_static = torch.empty_like(xs[0])
         x_static.copy_(xs[0])
         graph, _ = layer.capture(x_static)
-    B.profile_enable(not args.graph)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
+    B.profile_enable(not use_graph)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
         if args.mall_flush == "write":
             flush.fill_(i & 255)      # leaves the last-level cache full of dirty lines
         else:
@@ -370,7 +438,7 @@ def bench_decode(args, torch, B, synth, MoELayer):
         # kernel events cannot be taken inside a replay: the same steps once more as eager
         # launches, each after the same cache flush, time the kernels for the roofline
         B.profile_enable(True)
-        for i in range(args.steps):
+        for i in range(steps):
             if args.mall_flush == "write":
                 flush.fill_(i & 255)
             else:
@@ -379,28 +447,31 @@ def bench_decode(args, torch, B, synth, MoELayer):
         torch.cuda.synchronize()
         prof = B.profile_read()
         B.profile_enable(False)
-    step_bytes = np.array([touched[i % nb] * bundle + shared_bytes + act for i in range(args.steps)], np.float64)
+    del flush, flush_words
+    step_bytes = np.array([touched[i % nb] * bundle + shared_bytes + act for i in range(steps)], np.float64)
     # the decode gate/up launch streams the touched routed experts' W_gu, and the shared
     # expert's when the layer runs it inside the same launch
     merged = layer.shared_in_decode_launch(cfg.T)
     wbytes = 0.5 + 1 / 32 if cfg.dtype == "mxfp4" else 2.0   # bytes per weight (codes and scales)
     shared_gu = 2 * cfg.F_shared * cfg.d * wbytes if merged else 0
-    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * wbytes + shared_gu for i in range(args.steps))
+    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * wbytes + shared_gu for i in range(steps))
     gu_ms, gu_n = prof[B.PROF_DEC_GATEUP]
     hbm = float(step_bytes.sum() / (ms.sum() / 1e3) / 1e9)
+    hbm_med = float(np.median(step_bytes) / (np.median(ms) / 1e3) / 1e9)
     result = {
-        "metric": METRIC, "value": round(cfg.T * args.steps / (ms.sum() / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(float(ms.mean()), 4),
+        "metric": METRIC, "value": round(cfg.T * steps / (ms.sum() / 1e3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(float(ms.mean()), 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
                    "d_ff": cfg.F, "d_ff_shared": cfg.F_shared, "mall_flush_MiB": 512, "mall_flush": args.mall_flush,
-                   "hip_graph": bool(args.graph),
+                   "hip_graph": bool(use_graph),
                    "combine_in_down_launch": bool(layer.fuse_combine and layer.shared_in_decode_launch(cfg.T)
                                                   and cfg.T <= FUSE_COMBINE_MAX_T)},
-        "step_ms_p10_p50_p90": [round(float(np.percentile(ms, q)), 4) for q in (10, 50, 90)],
-        "touched_experts_mean": round(float(np.mean([touched[i % nb] for i in range(args.steps)])), 2),
-        "layer_hbm": {"achieved": round(hbm, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
+        "step_ms_p10_p50_p90": percentiles(ms),
+        "touched_experts_mean": round(float(np.mean([touched[i % nb] for i in range(steps)])), 2),
+        "layer_hbm": {"achieved": round(hbm, 1), "achieved_at_median_step": round(hbm_med, 1), "peak": PEAK_HBM_GBS,
+                      "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
                       "bytes_per_step_mean": int(step_bytes.mean())},
     }
     if gu_n:
@@ -412,8 +483,160 @@ def bench_decode(args, torch, B, synth, MoELayer):
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
                               "work_per_launch": f"gate/up weight bytes of the touched {who}",
                               "timed": "eager launches of the same steps" if graph is not None else "the timed steps"}
-    print(json.dumps(result), flush=True)
-    return 0
+    if graph is not None:
+        del graph
+    del layer, xs
+    torch.cuda.empty_cache()
+    if cpu_sample:
+        log(f"[bench] cpu baseline: oracle on {cpu_sample} tokens")
+        result["cpu_baseline"] = cpu_baseline(cfg, w, cpu_sample)
+    return result
+
+
+def bench_prefill(args, torch, B, synth, MoELayer, workload=None, steps=None, warmup=None, cpu_sample=None):
+    """Prefill layer (thousands of tokens, every expert resident): `warmup` untimed steps, then
+    exactly `steps` timed steps over rotating input batches, bracketed by synchronisations, with
+    an event pair per step for the percentiles. The dominant kernel is the routed experts'
+    gate/up GEMM (real rows only): achieved = its flops per launch / its average launch time,
+    from hipEvents on its own stream. Returns the result dict."""
+    workload = workload or args.workload
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    cfg = synth.get_config(workload)
+    if args.tokens:
+        cfg = cfg.with_T(args.tokens)
+    log(f"[bench] workload {cfg.name} T={cfg.T}: generating inputs")
+    w = dict(router=synth.gen_router(cfg), experts=synth.gen_experts(cfg, threads=16),
+             shared=synth.gen_shared(cfg) if cfg.F_shared else None,
+             w_sg=synth.gen_shared_gate(cfg) if cfg.shared_gate else None,
+             sb=synth.gen_select_bias(cfg) if cfg.select_bias else None)
+    layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
+                     select_bias=w["sb"], threads=16)
+    xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(args.batches)]
+    # skewed prefill: a Zipf(alpha) log-prior over a seeded permutation of the experts added to
+    # every token's logits, so a few experts get several times the average rows
+    lb = None
+    if args.skew_zipf > 0:
+        import dataclasses
+        zcfg = dataclasses.replace(cfg, zipf_alpha=args.skew_zipf, zipf_epoch=1)
+        lb = torch.from_numpy(synth.zipf_logit_bias(zcfg, 0)).to("cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {warmup}")
+    for i in range(warmup):
+        layer.forward(xs[i % len(xs)], logit_bias=lb)
+    torch.cuda.synchronize()
+    # rows per expert of each batch (real rows only; used for the algorithmic work)
+    rows_e = []
+    for x in xs:
+        rows_e.append(B.route(x, layer.w_router_t, logit_bias=lb, select_bias=layer.select_bias,
+                              **layer.route_args())["counts"].cpu().numpy())
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {steps} steps")
+    B.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        evs[i][0].record()
+        layer.forward(xs[i % len(xs)], logit_bias=lb)
+        evs[i][1].record()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = B.profile_read()
+    B.profile_enable(False)
+    ms_total = ev0.elapsed_time(ev1)
+    ms_steps = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_step = ms_total / steps
+    tokens_per_s = cfg.T * steps / (ms_total / 1e3)
+
+    d, F, E, T, k = cfg.d, cfg.F, cfg.E, cfg.T, cfg.k
+    rows = np.array([rows_e[i % len(xs)].sum() for i in range(steps)], dtype=np.float64)
+    gateup_flops = 4.0 * rows * d * F
+    down_flops = 2.0 * rows * F * d
+    shared_flops = 6.0 * T * d * cfg.F_shared
+    router_flops = 2.0 * T * d * E
+    layer_flops = float((gateup_flops + down_flops).mean() + shared_flops + router_flops)
+    gu_ms, gu_n = prof[B.PROF_GATEUP]
+    dn_ms, dn_n = prof[B.PROF_DOWN]
+    dtype = cfg.dtype
+    peak = PEAK_TFLOPS[dtype]
+    result = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 4),
+        "step_ms_p10_p50_p90": percentiles(ms_steps),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
+        "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
+                   "d_ff_shared": cfg.F_shared, "score_fn": cfg.score_fn, "all_experts_resident": True},
+    }
+    if lb is not None:
+        re = np.stack(rows_e)
+        result["config"]["zipf_skew_alpha"] = args.skew_zipf
+        result["data"] += f"; routing skewed by a Zipf({args.skew_zipf}) log-prior"
+        result["rows_per_expert"] = {"max": int(re.max()), "mean": round(float(re.mean()), 1), "min": int(re.min())}
+    # a shared expert that runs as one more group of the routed experts' launches is part of
+    # those launches' work
+    folded = getattr(layer, "shared_in_routed_launch", lambda T: False)(T)
+    gu_work = gateup_flops.mean() + (4.0 * T * d * cfg.F_shared if folded else 0.0)
+    dn_work = down_flops.mean() + (2.0 * T * d * cfg.F_shared if folded else 0.0)
+    if gu_n:
+        gu_avg_s = gu_ms / gu_n / 1e3
+        achieved = float(gu_work) / gu_avg_s / 1e12
+        kname = "ffn_gemm_fp8<gate/up+SwiGLU+requant>" if dtype == "fp8" else "ffn_gemm_bf16<gate/up+SwiGLU>"
+        who = "routed experts and the shared expert" if folded else "routed experts"
+        result["roofline"] = {"bound": "mfma", "kernel": kname,
+                              "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                              "frac": round(achieved / peak, 4), "traffic": recorded_traffic(cfg.name, kname),
+                              "avg_launch_ms": round(gu_ms / gu_n, 4),
+                              "work_per_launch": f"4*rows*d*F flops of the {who}, routed rows = T*k = "
+                                                 f"{int(rows.mean())}" + (f", shared rows = T = {T}" if folded else "")}
+        if dn_n:
+            dn_avg_s = dn_ms / dn_n / 1e3
+            result["down_gemm"] = {"avg_launch_ms": round(dn_ms / dn_n, 4),
+                                   "achieved_tflops": round(float(dn_work) / dn_avg_s / 1e12, 1)}
+        sg_ms, sg_n = prof[B.PROF_LABELED + B.PROF_GATEUP]
+        sd_ms, sd_n = prof[B.PROF_LABELED + B.PROF_DOWN]
+        if sg_n and sd_n:
+            result["shared_expert"] = {"gateup_avg_launch_ms": round(sg_ms / sg_n, 4),
+                                       "down_avg_launch_ms": round(sd_ms / sd_n, 4),
+                                       "note": "side stream, overlapping the routed path"}
+    result["layer_tflops"] = round(layer_flops / (ms_step / 1e3) / 1e12, 1)
+    result["layer_frac_of_peak"] = round(layer_flops / (ms_step / 1e3) / 1e12 / peak, 4)
+    result["host_wall_s"] = round(wall, 3)
+    del layer, xs
+    torch.cuda.empty_cache()
+    if cpu_sample is None and not args.no_cpu_baseline:
+        # sized for roughly 10-30 s of oracle work: the fp8 oracle dequantises every touched
+        # expert to float64, so its sample is a handful of tokens
+        cpu_sample = args.cpu_sample_tokens or (32 if cfg.dtype == "fp8" else 3 * cfg.T)
+    if cpu_sample:
+        log(f"[bench] cpu baseline: oracle on {cpu_sample} tokens")
+        result["cpu_baseline"] = cpu_baseline(cfg, w, cpu_sample)
+    return result
+
+
+def bench_suite(args, torch, B, synth, MoELayer):
+    """The headline (DeepSeek-V3-shaped fp8 prefill, the largest workload on one GPU) and every
+    other workload in one run; returns the headline dict with a "configs" object."""
+    head = bench_prefill(args, torch, B, synth, MoELayer, "dsv3_prefill_fp8",
+                         cpu_sample=0 if args.no_cpu_baseline else 32)
+    configs = {}
+    configs["mixtral_prefill_bf16"] = bench_prefill(args, torch, B, synth, MoELayer, "mixtral_prefill_bf16",
+                                                    steps=max(args.steps, 20), warmup=max(args.warmup, 3),
+                                                    cpu_sample=0 if args.no_cpu_baseline else 8192)
+    for T in (1, 8, 64):
+        configs[f"qwen_decode_bf16_T{T}"] = bench_decode(args, torch, B, synth, MoELayer, "qwen_decode_bf16", T=T,
+                                                         steps=200, warmup=10, graph=True,
+                                                         cpu_sample=0 if args.no_cpu_baseline else 256)
+    configs["offload_decode_bf16"] = bench_offload(args, torch, B, synth, MoELayer,
+                                                   modes=("overlapped", "blocking", "device_plan_graph"),
+                                                   cpu_sample=0 if args.no_cpu_baseline else 64)
+    head["configs"] = configs
+    return head
 
 
 def main():
@@ -421,7 +644,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_prefill_bf16", choices=WORKLOADS)
+    ap.add_argument("--workload", default="suite", choices=WORKLOADS,
+                    help="suite (default): the DeepSeek-V3-shaped fp8 prefill headline plus every other workload")
     ap.add_argument("--tokens", type=int, default=None, help="override T (decode batch size)")
     ap.add_argument("--batches", type=int, default=4, help="rotating input batches")
     ap.add_argument("--cpu-sample-tokens", type=int, default=None)
@@ -481,115 +705,18 @@ def main():
                           "hbm_read_plus_write_GBps": round(2 * n / (ms / 1e3) / 1e9, 1)}), flush=True)
         return 0
 
-    if args.workload.startswith("offload_decode") and args.layers > 1:
+    if args.workload == "suite":
+        result = bench_suite(args, torch, B, synth, MoELayer)
+    elif args.workload.startswith("offload_decode") and args.layers > 1:
         return bench_stack(args, torch, B, synth, MoELayer)
-    if args.workload.startswith("offload_decode") and not args.resident:
-        return bench_offload(args, torch, B, synth, MoELayer)
-    if args.workload == "qwen_decode_bf16" or args.workload.startswith("offload_decode"):
-        return bench_decode(args, torch, B, synth, MoELayer)
-
-    cfg = synth.get_config(args.workload)
-    if args.tokens:
-        cfg = cfg.with_T(args.tokens)
-    log(f"[bench] workload {cfg.name} T={cfg.T}: generating inputs")
-    w = dict(router=synth.gen_router(cfg), experts=synth.gen_experts(cfg, threads=16),
-             shared=synth.gen_shared(cfg) if cfg.F_shared else None,
-             w_sg=synth.gen_shared_gate(cfg) if cfg.shared_gate else None,
-             sb=synth.gen_select_bias(cfg) if cfg.select_bias else None)
-    layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
-                     select_bias=w["sb"], threads=16)
-    xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(args.batches)]
-    # skewed prefill: a Zipf(alpha) log-prior over a seeded permutation of the experts added to
-    # every token's logits, so a few experts get several times the average rows
-    lb = None
-    if args.skew_zipf > 0:
-        import dataclasses
-        zcfg = dataclasses.replace(cfg, zipf_alpha=args.skew_zipf, zipf_epoch=1)
-        lb = torch.from_numpy(synth.zipf_logit_bias(zcfg, 0)).to("cuda")
-    torch.cuda.synchronize()
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        layer.forward(xs[i % len(xs)], logit_bias=lb)
-    torch.cuda.synchronize()
-    # rows per expert of each batch (real rows only; used for the algorithmic work)
-    rows_e = []
-    for x in xs:
-        rows_e.append(B.route(x, layer.w_router_t, logit_bias=lb, **layer.route_args())["counts"].cpu().numpy())
-    torch.cuda.synchronize()
-
-    log(f"[bench] timing {args.steps} steps")
-    B.profile_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for i in range(args.steps):
-        layer.forward(xs[i % len(xs)], logit_bias=lb)
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prof = B.profile_read()
-    B.profile_enable(False)
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
-    tokens_per_s = cfg.T * args.steps / (ms_total / 1e3)
-
-    d, F, E, T, k = cfg.d, cfg.F, cfg.E, cfg.T, cfg.k
-    rows = np.array([rows_e[i % len(xs)].sum() for i in range(args.steps)], dtype=np.float64)
-    # the dominant kernel is the routed experts' gate/up GEMM (real rows only): achieved = its
-    # flops per launch / its average launch time. A shared expert runs concurrently on a side
-    # stream and is profiled under its own (labelled) kinds, reported separately.
-    gateup_flops = 4.0 * rows * d * F
-    down_flops = 2.0 * rows * F * d
-    shared_flops = 6.0 * T * d * cfg.F_shared
-    router_flops = 2.0 * T * d * E
-    layer_flops = float((gateup_flops + down_flops).mean() + shared_flops + router_flops)
-    launches = 1
-    gu_ms, gu_n = prof[B.PROF_GATEUP]
-    dn_ms, dn_n = prof[B.PROF_DOWN]
-    dtype = cfg.dtype
-    peak = PEAK_TFLOPS[dtype]
-    result = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
-        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
-        "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": E, "top_k": k, "d_ff": F,
-                   "d_ff_shared": cfg.F_shared, "score_fn": cfg.score_fn, "all_experts_resident": True},
-    }
-    if lb is not None:
-        re = np.stack(rows_e)
-        result["config"]["zipf_skew_alpha"] = args.skew_zipf
-        result["data"] += f"; routing skewed by a Zipf({args.skew_zipf}) log-prior"
-        result["rows_per_expert"] = {"max": int(re.max()), "mean": round(float(re.mean()), 1), "min": int(re.min())}
-    if gu_n:
-        gu_avg_s = gu_ms / gu_n / 1e3
-        achieved = float(gateup_flops.mean()) / (gu_avg_s * launches) / 1e12
-        kname = "ffn_gemm_fp8<gate/up+SwiGLU+requant>" if dtype == "fp8" else "ffn_gemm_bf16<gate/up+SwiGLU>"
-        result["roofline"] = {"bound": "mfma", "kernel": kname,
-                              "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
-                              "frac": round(achieved / peak, 4), "traffic": recorded_traffic(cfg.name, kname),
-                              "avg_launch_ms": round(gu_ms / gu_n, 4),
-                              "work_per_launch": f"4*rows*d*F flops of the routed experts, rows = T*k = {int(rows.mean())}"}
-        if dn_n:
-            dn_avg_s = dn_ms / dn_n / 1e3
-            result["down_gemm"] = {"avg_launch_ms": round(dn_ms / dn_n, 4),
-                                   "achieved_tflops": round(float(down_flops.mean()) / (dn_avg_s * launches) / 1e12, 1)}
-        sg_ms, sg_n = prof[B.PROF_LABELED + B.PROF_GATEUP]
-        sd_ms, sd_n = prof[B.PROF_LABELED + B.PROF_DOWN]
-        if sg_n and sd_n:
-            result["shared_expert"] = {"gateup_avg_launch_ms": round(sg_ms / sg_n, 4),
-                                       "down_avg_launch_ms": round(sd_ms / sd_n, 4),
-                                       "note": "side stream, overlapping the routed path"}
-    result["layer_tflops"] = round(layer_flops / (ms_step / 1e3) / 1e12, 1)
-    result["layer_frac_of_peak"] = round(layer_flops / (ms_step / 1e3) / 1e12 / peak, 4)
-    result["host_wall_s"] = round(wall, 3)
-    if not args.no_cpu_baseline:
-        # sized for roughly 10-30 s of oracle work: the fp8 oracle dequantises every touched
-        # expert to float64, so its sample is a handful of tokens
-        n = args.cpu_sample_tokens or (32 if cfg.dtype == "fp8" else 3 * cfg.T)
-        log(f"[bench] cpu baseline: oracle on {n} tokens")
-        result["cpu_baseline"] = cpu_baseline(cfg, w, n)
+    elif args.workload.startswith("offload_decode") and not args.resident:
+        result = bench_offload(args, torch, B, synth, MoELayer,
+                               cpu_sample=0 if args.no_cpu_baseline else (args.cpu_sample_tokens or 64))
+    elif args.workload == "qwen_decode_bf16" or args.workload.startswith("offload_decode"):
+        result = bench_decode(args, torch, B, synth, MoELayer,
+                              cpu_sample=0 if args.no_cpu_baseline else (args.cpu_sample_tokens or 256))
+    else:
+        result = bench_prefill(args, torch, B, synth, MoELayer)
     print(json.dumps(result), flush=True)
     return 0
 

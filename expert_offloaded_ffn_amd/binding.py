@@ -67,7 +67,7 @@ class CacheStats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
                 ("evictions", ctypes.c_int64), ("waves", ctypes.c_int64), ("h2d_bytes", ctypes.c_int64),
                 ("d2h_bytes", ctypes.c_int64), ("copy_ms", ctypes.c_double), ("prefetches", ctypes.c_int64),
-                ("prefetch_used", ctypes.c_int64)]
+                ("prefetch_used", ctypes.c_int64), ("wait_ms", ctypes.c_double)]
 
 
 class Profile(ctypes.Structure):

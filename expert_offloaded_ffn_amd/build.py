@@ -50,10 +50,59 @@ def _compile(src: str) -> str:
     return obj
 
 
+# Sources whose kernels load global memory straight into LDS with inline assembly that sets
+# M0 itself (ffn_common.h dma16_asm, gemm_fp8.h dma4_asm). The compiler reserves M0 and does
+# not honour it as a clobber, so the build checks the device code instead: every instruction
+# that names M0 must be one of those sequences.
+M0_CHECKED = ["grouped_ffn.hip"]
+
+
+def _llvm_tool(name: str) -> str:
+    p = os.path.join("/opt/rocm/llvm/bin", name)
+    return p if os.path.exists(p) else name
+
+
+def device_asm(obj: str) -> str:
+    """AMD GPU disassembly of the gfx950 code object embedded in a hipcc object file."""
+    import tempfile
+    with tempfile.TemporaryDirectory() as td:
+        fat, co = os.path.join(td, "fat.bin"), os.path.join(td, "dev.co")
+        subprocess.run([_llvm_tool("llvm-objcopy"), f"--dump-section=.hip_fatbin={fat}", obj, os.path.join(td, "x.o")],
+                       check=True, capture_output=True)
+        subprocess.run([_llvm_tool("clang-offload-bundler"), "--unbundle", "--type=o", f"--input={fat}",
+                        f"--targets=hipv4-amdgcn-amd-amdhsa--{ARCH}", f"--output={co}"], check=True, capture_output=True)
+        return subprocess.run([_llvm_tool("llvm-objdump"), "-d", co], check=True, capture_output=True,
+                              text=True).stdout
+
+
+def check_m0(asm: str) -> int:
+    """Raises unless every instruction naming M0 is `s_mov_b32 m0, sN` directly followed by
+    `s_nop 0` and a global_load_lds instruction. Returns the number of such sequences."""
+    lines = [l.split("//")[0].strip() for l in asm.splitlines()]
+    ins = [l for l in lines if l and not l.endswith(":") and not l.startswith("Disassembly")]
+    n = 0
+    for i, l in enumerate(ins):
+        ops = l.replace(",", " ").split()
+        if "m0" not in ops:
+            continue
+        ok = (len(ops) == 3 and ops[0] == "s_mov_b32" and ops[1] == "m0" and ops[2].startswith("s")
+              and i + 2 < len(ins) and ins[i + 1] == "s_nop 0" and ins[i + 2].startswith("global_load_lds_"))
+        if not ok:
+            ctx = "\n".join(ins[max(0, i - 2):i + 3])
+            raise RuntimeError(f"M0 is used outside the LDS DMA sequences:\n{ctx}")
+        n += 1
+    return n
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
+    for src, obj in zip(SOURCES, objs):
+        if src in M0_CHECKED:
+            n = check_m0(device_asm(obj))
+            if verbose:
+                print(f"{src}: {n} LDS DMA sequences own M0; no other M0 use")
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -141,8 +141,9 @@ __device__ __forceinline__ int take_tile(int32_t* counters, int total, int& rang
 // (global_load_lds_dwordx4, with the LDS base in M0), issued as inline assembly: the
 // compiler then does not track the LDS write, so it adds no "vmcnt(0)" before later LDS
 // reads; callers order them with explicit vmcnt waits and barriers. Each asm block sets M0
-// itself; M0 is reserved by the compiler (so it is not listed as clobbered) and the
-// compiled kernels here make no other use of it. lds_base must be wave-uniform.
+// itself. The compiler reserves M0 and does not honour it as a clobber, so it is not listed;
+// instead the build disassembles the compiled kernels and fails unless every instruction
+// naming M0 is one of these sequences (build.py check_m0). lds_base must be wave-uniform.
 __device__ __forceinline__ void dma16_asm(const void* g, const void* lds_base) {
   const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory");

@@ -5,8 +5,9 @@
 // Optimization #2); only experts the router selected are brought into VRAM,
 // loaded right before they run, with the loads overlapping compute (same page,
 // Optimization #1); the cache intercepts the router's expert list, checks
-// residency, evicts least-recently-used bundles and, when a batch needs more
-// experts than fit, blocks, transfers, then executes in waves ("Running 35B MoE
+// residency and evicts least-recently-used bundles; a step that needs more
+// experts than there are slots runs in waves, each wave's copies finishing
+// before its experts compute ("Running 35B MoE
 // Models on 8GB GPUs", section "Technical Insight"); transfers are asynchronous
 // host-to-HBM copies issued only for non-resident experts ("The Billion-Token
 // Bottleneck", section "Predictive Prefetching").
@@ -32,6 +33,7 @@
 //            stream waits on before a wave's hits run when one of them is still
 //            in flight.
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -63,8 +65,12 @@ struct expert_slot_cache {
   std::vector<hipEvent_t> last_read;     // per slot
   std::vector<char> last_read_valid;
   std::vector<hipEvent_t> copy_begin, copy_done;  // per wave
+  std::vector<hipEvent_t> wait_begin, wait_end;   // per wave: the compute stream around its wait for the copies
   std::vector<char> wave_copied;         // copies issued for the wave this step
   std::vector<char> timing_pending;      // copy span events to be added to copy_ms
+  std::vector<char> wait_pending;        // wait span events to be added to wait_ms
+  int64_t copies_issued = 0;             // bundle copies attempted since create
+  int64_t fail_copy_at = 0;              // > 0: copy number fail_copy_at fails (MOEFFN_FAIL_COPY_AT, tests)
   std::vector<hipEvent_t> fill_done;     // per slot: end of its last prefetch copy
   std::vector<char> fill_pending;        // per slot: the compute stream has not waited for it
   hipEvent_t compute_mark = nullptr;     // blocking mode: all compute enqueued before a wave
@@ -223,17 +229,52 @@ moe_status plan_step(expert_slot_cache* c, const int32_t* counts) {
   return MOE_OK;
 }
 
-// Adds finished copy spans to the stats (events of earlier steps).
+// Adds finished copy spans and compute-stream wait spans to the stats (events of earlier
+// steps; a span whose events have not completed yet stays pending unless `wait`).
 void collect_timing(expert_slot_cache* c, bool wait) {
   for (int w = 0; w < c->max_waves; ++w) {
-    if (!c->timing_pending[w]) continue;
-    if (wait) (void)hipEventSynchronize(c->copy_done[w]);
     float ms = 0.f;
-    if (hipEventElapsedTime(&ms, c->copy_begin[w], c->copy_done[w]) == hipSuccess) {
-      c->st.copy_ms += ms;
-      c->timing_pending[w] = 0;
+    if (c->timing_pending[w]) {
+      if (wait) (void)hipEventSynchronize(c->copy_done[w]);
+      if (hipEventElapsedTime(&ms, c->copy_begin[w], c->copy_done[w]) == hipSuccess) {
+        c->st.copy_ms += ms;
+        c->timing_pending[w] = 0;
+      }
+    }
+    if (c->wait_pending[w]) {
+      if (wait) (void)hipEventSynchronize(c->wait_end[w]);
+      if (hipEventElapsedTime(&ms, c->wait_begin[w], c->wait_end[w]) == hipSuccess) {
+        c->st.wait_ms += ms;
+        c->wait_pending[w] = 0;
+      }
     }
   }
+  (void)hipGetLastError();   // a not-ready query is not an error of a later call
+}
+
+// A bundle copy failed: the slot it was meant for holds no valid bundle, and neither do the
+// slots of the step's misses whose copies were not issued yet (this wave's entries from
+// `from` on, and every miss of the later waves). They all leave the planner's residency, so
+// a later step misses on them again; the step itself ends here (planned = false).
+void drop_unfilled(expert_slot_cache* c, int w, size_t from) {
+  for (int v = w; v < (int)c->waves.size(); ++v) {
+    const auto& wave = c->waves[v];
+    for (size_t i = (v == w ? from : 0); i < wave.size(); ++i) {
+      const moe_cache_entry& en = wave[i];
+      if (en.hit || c->slot_of[en.expert] != en.slot) continue;
+      c->slot_of[en.expert] = -1;
+      c->owner[en.slot] = -1;
+      c->prefetched[en.expert] = 0;
+    }
+  }
+  c->planned = false;
+}
+
+// hipMemcpyAsync of one bundle, or the injected failure of the tests (MOEFFN_FAIL_COPY_AT).
+hipError_t copy_bundle(expert_slot_cache* c, void* dst, const void* src) {
+  c->copies_issued += 1;
+  if (c->fail_copy_at > 0 && c->copies_issued == c->fail_copy_at) return hipErrorInvalidValue;
+  return hipMemcpyAsync(dst, src, (size_t)c->cfg.bundle_bytes, hipMemcpyHostToDevice, c->side);
 }
 
 void destroy_device(expert_slot_cache* c) {
@@ -241,6 +282,8 @@ void destroy_device(expert_slot_cache* c) {
   for (auto& e : c->last_read) if (e) (void)hipEventDestroy(e);
   for (auto& e : c->copy_begin) if (e) (void)hipEventDestroy(e);
   for (auto& e : c->copy_done) if (e) (void)hipEventDestroy(e);
+  for (auto& e : c->wait_begin) if (e) (void)hipEventDestroy(e);
+  for (auto& e : c->wait_end) if (e) (void)hipEventDestroy(e);
   for (auto& e : c->fill_done) if (e) (void)hipEventDestroy(e);
   if (c->compute_mark) (void)hipEventDestroy(c->compute_mark);
   if (c->side) (void)hipStreamDestroy(c->side);
@@ -302,12 +345,18 @@ extern "C" moe_status expert_slot_cache_create(const moe_cache_cfg* cfg, expert_
       return fail("hipEventCreate", e);
     c->copy_begin.assign(c->max_waves, nullptr);
     c->copy_done.assign(c->max_waves, nullptr);
+    c->wait_begin.assign(c->max_waves, nullptr);
+    c->wait_end.assign(c->max_waves, nullptr);
     c->wave_copied.assign(c->max_waves, 0);
     c->timing_pending.assign(c->max_waves, 0);
+    c->wait_pending.assign(c->max_waves, 0);
     for (int w = 0; w < c->max_waves; ++w) {
       if ((e = hipEventCreate(&c->copy_begin[w])) != hipSuccess) return fail("hipEventCreate", e);
       if ((e = hipEventCreate(&c->copy_done[w])) != hipSuccess) return fail("hipEventCreate", e);
+      if ((e = hipEventCreate(&c->wait_begin[w])) != hipSuccess) return fail("hipEventCreate", e);
+      if ((e = hipEventCreate(&c->wait_end[w])) != hipSuccess) return fail("hipEventCreate", e);
     }
+    if (const char* f = std::getenv("MOEFFN_FAIL_COPY_AT")) c->fail_copy_at = std::atoll(f);
     if ((e = hipHostMalloc((void**)&c->counts_pinned, sizeof(int32_t) * k.n_experts, hipHostMallocDefault)) != hipSuccess)
       return fail("hipHostMalloc", e);
     if ((e = hipHostMalloc((void**)&c->tables_pinned, sizeof(int32_t) * k.n_experts * 2 * c->max_waves,
@@ -334,6 +383,7 @@ extern "C" moe_status expert_slot_cache_reset(expert_slot_cache* c) {
     MOE_HIP(hipStreamSynchronize(c->side));
     std::fill(c->last_read_valid.begin(), c->last_read_valid.end(), 0);
     std::fill(c->timing_pending.begin(), c->timing_pending.end(), 0);
+    std::fill(c->wait_pending.begin(), c->wait_pending.end(), 0);
     std::fill(c->fill_pending.begin(), c->fill_pending.end(), 0);
   }
   plan_reset(c);
@@ -376,7 +426,9 @@ moe_status issue_copies(expert_slot_cache* c, int w, hipStream_t compute) {
     MOE_HIP(hipStreamWaitEvent(c->side, c->compute_mark, 0));
   }
   bool any = false;
-  for (const auto& en : c->waves[w]) {
+  const auto& wave = c->waves[w];
+  for (size_t i = 0; i < wave.size(); ++i) {
+    const moe_cache_entry& en = wave[i];
     if (en.hit) continue;
     if (!any) {
       MOE_HIP(hipEventRecord(c->copy_begin[w], c->side));
@@ -385,13 +437,13 @@ moe_status issue_copies(expert_slot_cache* c, int w, hipStream_t compute) {
     if (c->last_read_valid[en.slot]) MOE_HIP(hipStreamWaitEvent(c->side, c->last_read[en.slot], 0));
     c->fill_pending[en.slot] = 0;  // the wave's copy_done covers the slot from now on
     char* dst = static_cast<char*>(c->cfg.pool) + (int64_t)en.slot * c->cfg.slot_stride;
-    const hipError_t err = hipMemcpyAsync(dst, c->bundles[en.expert], (size_t)c->cfg.bundle_bytes,
-                                          hipMemcpyHostToDevice, c->side);
+    const hipError_t err = copy_bundle(c, dst, c->bundles[en.expert]);
     if (err != hipSuccess) {
-      // the slot holds no valid bundle: drop it from the plan's residency
-      c->slot_of[en.expert] = -1;
-      c->owner[en.slot] = -1;
-      set_error("expert_slot_cache: copy of expert %d into slot %d failed: %s", en.expert, en.slot,
+      (void)hipGetLastError();
+      const int expert = en.expert, slot = en.slot;
+      drop_unfilled(c, w, i);
+      c->timing_pending[w] = 0;
+      set_error("expert_slot_cache: copy of expert %d into slot %d failed: %s", expert, slot,
                 hipGetErrorString(err));
       return MOE_EHIP;
     }
@@ -419,7 +471,15 @@ extern "C" moe_status expert_slot_cache_wave(expert_slot_cache* c, int32_t wave,
   std::fill(table, table + E, -1);
   int n = 0;
   const bool blocking = c->cfg.blocking != 0;
-  if (blocking ? part == 0 : part == 1) MOE_HIP(hipStreamWaitEvent(s, c->copy_done[wave], 0));
+  if (blocking ? part == 0 : part == 1) {
+    // the compute stream's wait for the wave's copies, timed by events on that stream (the
+    // previous step's span is complete: acquire synchronised the stream before planning)
+    if (c->wait_pending[wave]) collect_timing(c, true);
+    MOE_HIP(hipEventRecord(c->wait_begin[wave], s));
+    MOE_HIP(hipStreamWaitEvent(s, c->copy_done[wave], 0));
+    MOE_HIP(hipEventRecord(c->wait_end[wave], s));
+    c->wait_pending[wave] = 1;
+  }
   for (const auto& en : c->waves[wave]) {
     const bool take = blocking ? (part == 0) : (part == 0 ? en.hit != 0 : en.hit == 0);
     if (take) {
@@ -489,9 +549,9 @@ extern "C" moe_status expert_slot_cache_prefetch(expert_slot_cache* c, const int
     if (c->cfg.dry_run) continue;
     if (c->last_read_valid[en.slot]) MOE_HIP(hipStreamWaitEvent(c->side, c->last_read[en.slot], 0));
     char* dst = static_cast<char*>(c->cfg.pool) + (int64_t)en.slot * c->cfg.slot_stride;
-    const hipError_t err = hipMemcpyAsync(dst, c->bundles[en.expert], (size_t)c->cfg.bundle_bytes,
-                                          hipMemcpyHostToDevice, c->side);
+    const hipError_t err = copy_bundle(c, dst, c->bundles[en.expert]);
     if (err != hipSuccess) {
+      (void)hipGetLastError();
       c->slot_of[en.expert] = -1;
       c->owner[en.slot] = -1;
       c->prefetched[en.expert] = 0;

@@ -214,10 +214,11 @@ class MoELayer:
 
     def shared_in_decode_launch(self, T: int) -> bool:
         """Whether a T-token forward runs the shared expert inside the routed experts' decode
-        launches (bf16 or MXFP4, resident experts, at most 64 rows per expert) instead of on a side
-        stream."""
-        return (self.shared is not None and self.cache is None and self.w_code in (B.MOE_BF16, B.MOE_MXFP4)
-                and 0 < T <= 64)
+        launches (bf16 or MXFP4, every expert resident, at most 64 rows per expert) instead of on a
+        side stream. A slot pool (host- or device-planned) runs its routed experts in waves through
+        the pool's tables, so its shared expert always takes the side stream."""
+        return (self.shared is not None and self.cache is None and self.cache_dev is None
+                and self.w_code in (B.MOE_BF16, B.MOE_MXFP4) and 0 < T <= 64)
 
     def _shared_ffn(self, T, a, a_scale, a_code, ydt, main):
         """Launches the shared expert's FFN on the side stream once `a` is ready on `main`; the
@@ -244,6 +245,9 @@ class MoELayer:
         is issued, concurrently with the routed experts, and joined before the combine."""
         T = x.shape[0]
         k, E, d = self.k, self.E, self.d
+        if prefetch is not None and self.cache is None:
+            raise ValueError("prefetch= needs the host-planned slot pool (expert_slot_cache_prefetch); this layer "
+                             "is resident or planned on the device")
         main = torch.cuda.current_stream(self.device) if stream is None else stream
         ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
         shared_y = None

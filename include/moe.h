@@ -103,7 +103,7 @@ const char* moe_version(void);
  *  counts       [E] int32 out or NULL: counts[e] = #(t, j) with topk_idx = e
  * Errors: MOE_EINVAL for T < 0, d < 1, E < 1, k outside [1, E], d % 8 != 0,
  *  n_groups not dividing E, topk_groups > n_groups, group_topn outside
- *  [1, E/n_groups], k > topk_groups*E/n_groups, E > 1024, null required pointers,
+ *  [1, min(E/n_groups, 8)], k > topk_groups*E/n_groups, E > 1024, null required pointers,
  *  select_bias with softmax. T = 0 is a no-op (the configuration is still checked;
  *  tensor pointers may then be NULL).
  */
@@ -385,8 +385,16 @@ moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, const moe_ffn_
  * fail with MOE_ESTATE) for expert_slot_cache_plan_host.
  * Errors: MOE_EINVAL (sizes, null pointers, a bundle not in pinned host memory),
  *  MOE_ECAPACITY (n_slots < 1, slot_stride < bundle_bytes), MOE_ESTATE (calls
- *  out of order), MOE_EHIP (a copy or event call failed; the affected slot is
- *  left non-resident).
+ *  out of order), MOE_EHIP (a copy or event call failed). A failed bundle copy
+ *  fails loudly instead of letting a wave run on an incomplete bundle ("Running
+ *  35B MoE Models on 8GB GPUs", section "Technical Insight"): the call returns
+ *  MOE_EHIP, the expert whose copy failed and every miss of the step whose copy
+ *  was not issued yet leave the residency table (their slots become free, so a
+ *  later step misses on them again), and the step ends: expert_slot_cache_wave
+ *  returns MOE_ESTATE until the next acquire. For tests, the environment
+ *  variable MOEFFN_FAIL_COPY_AT=n (read at create) makes the n-th bundle copy of
+ *  the cache (misses and prefetches, counted from 1) fail this way without
+ *  calling hipMemcpyAsync.
  */
 typedef struct expert_slot_cache expert_slot_cache;
 
@@ -407,6 +415,8 @@ typedef struct {
   double copy_ms;   /* sum over steps of side-stream copy spans of the steps' misses (events) */
   int64_t prefetches;     /* bundles copied by expert_slot_cache_prefetch */
   int64_t prefetch_used;  /* of those, bundles a later step hit before they were evicted */
+  double wait_ms;   /* sum over waves of the compute stream's wait for the wave's copies (events on
+                       the compute stream before and after the wait); 0 for the device-planned cache */
 } moe_cache_stats;
 
 /* One entry of a wave's plan (host query for tests and tools). */
@@ -538,7 +548,11 @@ int32_t expert_slot_cache_dev_max_waves(const expert_slot_cache_dev* c);   /* ce
 moe_status expert_slot_cache_dev_set_frequency(expert_slot_cache_dev* c, double decay);
 /* The layer order, as expert_slot_cache_set_layers, applied before the
  * frequency and recency stages; a step's layer is that of its lowest touched
- * entry, and steps touching several layers are reported by stats (MOE_ESTATE).
+ * entry. A step touching entries of several layers is not rejected when it is
+ * planned (the plan kernel cannot return an error without a host sync): it is
+ * planned with the layer of its lowest touched entry, counted on the device,
+ * and the next expert_slot_cache_dev_stats call returns MOE_ESTATE for it (the
+ * host-planned cache and its oracle reject such a step at once).
  * Synchronises the device; kept in device memory like the decay. */
 moe_status expert_slot_cache_dev_set_layers(expert_slot_cache_dev* c, int32_t n_layers);
 moe_status expert_slot_cache_dev_step(expert_slot_cache_dev* c, const int32_t* counts, void* stream,

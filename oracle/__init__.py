@@ -24,8 +24,9 @@ Bottleneck", section "The Geometry of the Problem: Why MoE is Different");
 only the chosen experts' weights are touched ("NovaLLM: Running Massive MoE
 Models Fully In-Memory", sections 2-3); the expert cache intercepts the
 router's expert list, keeps whole expert bundles (weights and quantisation
-scales) resident in VRAM under LRU eviction and, when a batch needs more
-experts than fit, blocks, transfers, then executes ("Running 35B MoE Models on
+scales) resident in VRAM under LRU eviction, and a step that needs more
+experts than there are slots waits for each wave's copies before that wave's
+experts compute ("Running 35B MoE Models on
 8GB GPUs: How vvllm-ms Caches Experts in System RAM", section "Technical
 Insight"). The router math (softmax or sigmoid, renormalisation, group limit,
 tie-break), the SwiGLU form and the fp8 formats are not on the pages; each

@@ -1,10 +1,11 @@
 """Exact simulation of the expert slot pool (oracle side, test infrastructure only).
 
 The pages' expert cache keeps whole expert bundles resident in VRAM, checks
-residency for the experts the router returned, evicts the least recently used
-bundles on a miss, and, when a batch needs more experts than fit, blocks,
-performs the transfers, then executes ("Running 35B MoE Models on 8GB GPUs:
-How vvllm-ms Caches Experts in System RAM", section "Technical Insight"); only
+residency for the experts the router returned and evicts the least recently
+used bundles on a miss; a step that needs more experts than there are slots
+finishes each wave's copies before that wave computes ("Running 35B MoE Models
+on 8GB GPUs: How vvllm-ms Caches Experts in System RAM", section "Technical
+Insight"); only
 experts that actually run are loaded ("NovaLLM: Running Massive MoE Models
 Fully In-Memory", section 3, Optimization #1).
 

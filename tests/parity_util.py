@@ -103,11 +103,20 @@ def route_agreement(cfg, r_ref, g_route, key_tol):
 
 
 def rel_err(got, ref):
+    if np.asarray(ref).size == 0:
+        return 0.0
     return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def elem_err(got, ref):
+    """The secondary error, reported and not gated: max_i |got_i - ref_i| / (|ref_i| + rms(ref))."""
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    return float((np.abs(got - ref) / (np.abs(ref) + max(rms, 1e-30))).max()) if ref.size else 0.0
 
 
 def assert_close(got, ref, dtype, what="output"):
     e = rel_err(got, ref)
-    say(f"    {what}: max-rel err {e:.3e} (tol {TOL[dtype]:.0e})")
+    say(f"    {what}: max-rel err {e:.3e} (tol {TOL[dtype]:.0e}); elementwise vs |ref|+rms {elem_err(got, ref):.3e}")
     assert e <= TOL[dtype], f"{what}: relative error {e} > {TOL[dtype]}"
     return e

@@ -31,7 +31,29 @@ def _x_dev(cfg, x_store):
     return torch.from_numpy(x_store.view(np.int16)).view(torch.bfloat16).to(DEV)
 
 
-def _run_and_check(cfg, layer, w, T, xi=0, tokens=None, logit_bias=None):
+def cover_tokens(g, k, block=64, extra=0, seed=0):
+    """Tokens whose rows cover every expert's rows in blocks of `block` grouped rows: for every
+    expert, the token of its first row, of every block's last row and of its last row (so
+    every m-tile of any height that is a multiple of `block`, including a nearly empty last
+    one, has a checked row), plus `extra` random tokens. Read off the device's grouping."""
+    off = to_np(g["perm"]["offsets"]).astype(np.int64)
+    src = to_np(g["perm"]["perm_src"]).astype(np.int64)
+    rows = []
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi > lo:
+            rows += [lo, hi - 1] + list(range(lo + block - 1, hi, block))
+    toks = set((src[np.array(rows)] // k).tolist())
+    if extra:
+        T = len(src) // k
+        rng = np.random.default_rng(seed)
+        toks |= set(rng.choice(T, min(extra, T), replace=False).tolist())
+    return np.array(sorted(toks))
+
+
+def _run_and_check(cfg, layer, w, T, xi=0, tokens=None, logit_bias=None, tokens_fn=None):
+    """tokens: the tokens checked against the oracle (all when None); tokens_fn(g) picks them
+    from the device's routing instead."""
     x_store = synth.gen_x(cfg, xi, T=T)
     x = _x_dev(cfg, x_store)
     lb = None if logit_bias is None else torch.from_numpy(logit_bias).to(DEV)
@@ -45,8 +67,12 @@ def _run_and_check(cfg, layer, w, T, xi=0, tokens=None, logit_bias=None):
     if cfg.shared_gate:
         err = np.abs(to_np(g["route"]["shared_gate"]) - r_ref.shared_gate).max()
         assert err <= 1e-4, f"shared gate err {err}"
+    if tokens_fn is not None:
+        tokens = tokens_fn(g)
     toks = np.arange(T) if tokens is None else np.asarray(tokens)
     toks = toks[same[toks]]
+    if tokens is not None:
+        say(f"    checking {len(toks)} of {T} tokens")
     cache = {}
 
     def expert(e):
@@ -117,12 +143,11 @@ def test_empty_batch(config_name):
 
 
 def test_mixtral_full_size_sampled():
+    """The full Mixtral-shaped layer: every expert's rows checked in blocks of 64 (each of its
+    m-tiles, the taller last one included), plus random tokens to at least 256."""
     cfg = synth.get_config("mixtral_prefill_bf16")
     layer, w = _build(cfg)
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(cfg.T, 24, replace=False))
-    toks[-1] = cfg.T - 1
-    _run_and_check(cfg, layer, w, cfg.T, 0, tokens=toks)
+    _run_and_check(cfg, layer, w, cfg.T, 0, tokens_fn=lambda g: cover_tokens(g, cfg.k, 64, extra=160))
 
 
 @pytest.mark.parametrize("T", [1, 8, 64])
@@ -207,10 +232,23 @@ def test_fp8_layer_reduced(T, d, E, k, F, Fs, G, TG):
 
 
 def test_dsv3_fp8_full_size_sampled():
+    """The full DeepSeek-V3-shaped layer: for every one of the 256 experts its first and last row
+    and the last row of every block of 64 of its rows are checked (so each m-tile, including a
+    nearly empty last one, has checked rows), with the shared expert on every checked token."""
     cfg = synth.get_config("dsv3_prefill_fp8")
     layer, w = _build(cfg)
-    toks = np.array([0, 1234, 5000, cfg.T - 1])
-    _run_and_check(cfg, layer, w, cfg.T, 0, tokens=toks)
+    _run_and_check(cfg, layer, w, cfg.T, 0, tokens_fn=lambda g: cover_tokens(g, cfg.k, 64))
+
+
+def test_fp8_layer_many_tiles_every_row():
+    """More gate/up tiles (about 512) and down tiles than the persistent grid has blocks, so every
+    block takes several tiles through the same LDS ring and the per-XCD queues hand tiles across
+    XCDs; every row of the layer is checked."""
+    cfg = synth.get_config("dsv3_prefill_fp8", T=2048, d=512, E=64, k=8, F=512, F_shared=512, n_groups=8,
+                           topk_groups=4, name="fp8_many_tiles")
+    layer, w = _build(cfg)
+    g = _run_and_check(cfg, layer, w, cfg.T)
+    assert to_np(g["route"]["counts"]).max() > 256
 
 
 @pytest.mark.parametrize("T", [1, 8])
