@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoeffn.so")
 
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ECAPACITY, MOE_ENOMEM, MOE_ESTATE = 0, -1, -2, -3, -4, -5, -6
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP", -4: "MOE_ECAPACITY",
           -5: "MOE_ENOMEM", -6: "MOE_ESTATE"}
 
@@ -107,6 +108,8 @@ EXPORTS = {
                                                ctypes.POINTER(FfnProblem)]),
     "moe_grouped_ffn_combine": (ctypes.c_int32, [ctypes.POINTER(FfnProblem), ctypes.POINTER(FfnProblem),
                                 ctypes.POINTER(CombineArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "moe_grouped_ffn_combine_noalloc": (ctypes.c_int32, [ctypes.POINTER(FfnProblem), ctypes.POINTER(FfnProblem),
+                                        ctypes.POINTER(CombineArgs), ctypes.c_void_p]),
     "expert_slot_cache_create": (ctypes.c_int32, [ctypes.POINTER(CacheCfg), ctypes.POINTER(ctypes.c_void_p)]),
     "expert_slot_cache_destroy": (ctypes.c_int32, [ctypes.c_void_p]),
     "expert_slot_cache_reset": (ctypes.c_int32, [ctypes.c_void_p]),
@@ -372,6 +375,21 @@ def grouped_ffn_combine(routed: FfnProblem, shared, perm_dst, gate, *, shared_ga
     cb = CombineArgs(T, k, ptr(perm_dst), ptr(gate), ptr(shared_gate), ptr(out), out_dtype)
     _check(lib().moe_grouped_ffn_combine(ctypes.byref(routed), ctypes.byref(shared) if shared is not None else None,
                                          ctypes.byref(cb), ptr(ws), ws.numel(), stream_ptr(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+
+
+def grouped_ffn_combine_noalloc(routed: FfnProblem, shared, perm_dst, gate, out, *, shared_gate=None,
+                                out_dtype=MOE_BF16, stream=None):
+    """moe_grouped_ffn_combine_noalloc: as grouped_ffn_combine, with the workspace in the library's
+    per-device static scratch array; `out` [T, d] is the caller's. Returns out."""
+    T, k = gate.shape
+    cb = CombineArgs(T, k, ptr(perm_dst), ptr(gate), ptr(shared_gate), ptr(out), out_dtype)
+    _check(lib().moe_grouped_ffn_combine_noalloc(ctypes.byref(routed),
+                                                 ctypes.byref(shared) if shared is not None else None,
+                                                 ctypes.byref(cb), stream_ptr(stream)))
     return out
 
 

@@ -16,6 +16,7 @@
 //  this file      ffn_f32_* (fp32 VALU path, one thread per output element) and the host
 //                 side: argument checks, workspace layout, launches
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "decode_bf16.h"
@@ -626,4 +627,56 @@ extern "C" moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, con
   cb.arrived = reinterpret_cast<int32_t*>(w + L.arrived);
   cb.nprob = n;
   return launch_decode(c, n, as_stream(stream), &cb);
+}
+
+// ------------------------------------------------------- no-allocation variant --
+// moe_grouped_ffn_combine for callers that cannot allocate device memory (code under HIP
+// graph capture, tight serving loops, harnesses that forbid hipMalloc): the workspace is a
+// file-scope device array of MOE_NOALLOC_SCRATCH_BYTES, one copy per GPU the library runs on,
+// held until the process ends. In host code `scratch` names a host-side stand-in, not device
+// memory; its device address on each GPU comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is passed to the kernels. The kernels of a
+// call clear the arrival counts they use (the gate/up launch zeroes them for the down launch),
+// so nothing has to start at zero between calls; calls that overlap on one GPU share the array
+// and race.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace moeffn {
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  MOE_HIP(hipGetDevice(&dev));
+  MOE_REQUIRE(dev >= 0 && dev < 64, MOE_EUNSUPPORTED, "moe_grouped_ffn_combine_noalloc: device %d outside [0, 64)",
+              dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    MOE_REQUIRE(p != nullptr && aligned(p, 256), MOE_EHIP,
+                "moe_grouped_ffn_combine_noalloc: no 256-B aligned device address for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace
+}  // namespace moeffn
+
+extern "C" moe_status moe_grouped_ffn_combine_noalloc(const moe_ffn_problem* routed, const moe_ffn_problem* shared,
+                                                      const moe_combine_args* comb, void* stream) {
+  clear_error();
+  MOE_REQUIRE(routed != nullptr && routed->table != nullptr && comb != nullptr, MOE_EINVAL,
+              "moe_grouped_ffn_combine_noalloc: routed problem, its table and comb must not be NULL");
+  const size_t need = moe_grouped_ffn_combine_workspace_size(routed, shared);
+  MOE_REQUIRE(need > 0, MOE_EINVAL, "moe_grouped_ffn_combine_noalloc: invalid problems (no workspace size)");
+  MOE_REQUIRE(need <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_ECAPACITY,
+              "moe_grouped_ffn_combine_noalloc: the step needs %zu bytes of scratch, more than the %zu this entry "
+              "point holds per device (use moe_grouped_ffn_combine with a workspace)",
+              need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (moe_status st = scratch_address(&ws)) return st;
+  return moe_grouped_ffn_combine(routed, shared, comb, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }

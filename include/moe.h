@@ -350,6 +350,23 @@ size_t moe_grouped_ffn_combine_workspace_size(const moe_ffn_problem* routed, con
 moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, const moe_ffn_problem* shared,
                                    const moe_combine_args* comb, void* ws, size_t ws_bytes, void* stream);
 
+/* moe_grouped_ffn_combine without allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc. Same arguments and results as moe_grouped_ffn_combine
+ * (bit for bit), minus the workspace: it lives in a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES, one per GPU the library runs on, held until the
+ * process ends. The caller still passes every input and output. No device
+ * memory is allocated or freed by the call.
+ * Limit: a step whose moe_grouped_ffn_combine_workspace_size exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES is rejected with MOE_ECAPACITY before any launch.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on the same
+ * GPU (other streams or threads) race and must be serialised by the caller.
+ * Errors: as moe_grouped_ffn_combine; MOE_ECAPACITY as above; MOE_EHIP if the
+ * array's device address cannot be obtained. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_grouped_ffn_combine_noalloc(const moe_ffn_problem* routed, const moe_ffn_problem* shared,
+                                           const moe_combine_args* comb, void* stream);
+
 /* ------------------------------------------------------- expert slot cache --
  * Expert-granular residency: a fixed pool of n_slots bundle slots in HBM backed
  * by every expert's bundle in pinned host memory ([NOVA] section 3,
