@@ -85,7 +85,8 @@ def check_m0(asm: str) -> int:
         ops = l.replace(",", " ").split()
         if "m0" not in ops:
             continue
-        ok = (len(ops) == 3 and ops[0] == "s_mov_b32" and ops[1] == "m0" and ops[2].startswith("s")
+        ok = (len(ops) == 3 and ops[0] == "s_mov_b32" and ops[1] == "m0"
+              and (ops[2].startswith("s") or ops[2] in ("vcc_lo", "vcc_hi"))
               and i + 2 < len(ins) and ins[i + 1] == "s_nop 0" and ins[i + 2].startswith("global_load_lds_"))
         if not ok:
             ctx = "\n".join(ins[max(0, i - 2):i + 3])

@@ -1,4 +1,27 @@
 // The fp8 (e4m3 with fp32 block scales) prefill GEMM of the grouped FFN.
+//
+// Operands: activations as e4m3 codes with one fp32 scale per row per 128 columns, weights as
+// e4m3 codes with one fp32 scale per 128 x 128 block (the DeepSeek-V3-shaped workload's
+// format). The scales are arbitrary fp32 values, which the MFMA's power-of-two (E8M0) scale
+// operands cannot carry, so every 16x16x128 MFMA covers exactly one 128-column scale block and
+// its partial product is promoted on the VALU: acc += P * (s_row * s_weight). That is one FMA
+// per output element per 128 columns, so the accumulators live in VGPRs.
+//
+// Tile 256 x 256 on 8 waves (2 wave rows of 128 rows x 4 wave columns of 64 columns, two waves
+// per SIMD): per 128-column stage a block moves 64 KB into LDS for 8.4 M MACs, and a wave
+// reads 24 KB of fragments for 1 M MACs. An expert's m-tiles of one n-tile are adjacent in
+// the tile order and taken by one XCD, so they share the weight tile in its L2.
+//
+// In the gate/up GEMM the weight rows alternate between gate and up every 16 (the bundle
+// layout), so a 256-column tile holds 128 hidden columns of each. Wave columns 0 and 2 take the
+// gate n-blocks of the two halves, 1 and 3 the up n-blocks of the same hidden columns: a wave's
+// 64 columns then share one weight block scale per stage. The epilogue hands the gate values to
+// the up waves through LDS, which form H = silu(G) * U, quantise it per row per 128 hidden
+// columns (one scale per tile row: the tile covers exactly one such block) and store it.
+//
+// One launch runs one or two problems (the routed experts and a shared expert: the shared
+// expert is a group of its own in the same tile list, so it neither competes with the routed
+// GEMM from a second stream nor re-reads its activations once per n-tile from its own launch).
 #pragma once
 
 #include "ffn_common.h"
@@ -6,279 +29,386 @@
 namespace moeffn {
 namespace {
 
-// ----------------------------------------------------------- fp8 path ---
-// e4m3 operands with fp32 block scales (per row per 128 columns for activations, per
-// 128x128 block for weights). The scales are arbitrary fp32 values, which the MFMA's
-// power-of-two (E8M0) scale operands cannot carry, so every 16x16x128 MFMA covers exactly
-// one 128-column scale block and its partial product is promoted on the VALU:
-// acc += P * (s_row * s_weight). The accumulators therefore live in VGPRs, which bounds
-// a wave's tile: block tile 128 x 256 on 8 waves of 64 x 64 (two per SIMD), one
-// 128-column scale block per stage, a 3-deep LDS ring fed by direct-to-LDS loads two
-// stages ahead.
-// LDS stage: A 128 rows x 128 B (8 blocks of 16 rows, row r's 16-byte chunk c at slot
-// 8r + (c ^ f(r)), f(r) = ((r >> 1) + 4 (r & 1)) & 7, so a row is one 128-byte DMA
-// segment and fragment reads are bank-conflict-free), B 16 tiles of 2 KiB (the bundle
-// layout), the 128 row scales of the stage's block.
+constexpr int kQBM = 256, kQBN = 256;
+constexpr int kQMaxKB = 128;     // K up to 16384 (the tile's weight block scales are staged in LDS)
+// LDS ring stage: A 256 rows x 128 B (row r's 16-byte chunk c at 128 r + 16 (c ^ f(r))), B 16
+// n-blocks of 2 KiB in the bundle's fragment order, the 256 row scales of the stage.
+constexpr int kQA = 0, kQB = 32768, kQS = 65536, kQStage = 66560, kQRing = 2 * kQStage;
 
-constexpr int kF8BM = 128, kF8BN = 256, kF8Stages = 3;
-constexpr int kF8MaxKB = 128;   // K up to 16384 (weight scales of a tile are staged in LDS)
-constexpr int kF8A = 0, kF8B = 16384, kF8S = 49152, kF8StageBytes = 50176;
-
-struct Fp8Args {
-  const uint8_t* a;
-  const float* a_scale;        // [*, K/128]
-  const int32_t* a_row_src;
+// One grouped-FFN problem of a launch.
+struct Fp8Prob {
+  const uint8_t* a;            // e4m3 codes, rows of K bytes
+  const float* a_scale_t;      // [K/128][a_scale_ld]: block kb's scale of GEMM row r at kb*ld + r
+  int a_scale_ld;              // >= rows + 256 (a tile may read past the last row)
+  const int32_t* a_row_src;    // NULL: GEMM row r reads row r of a
   int a_row_div;
-  const int32_t* offsets;
+  const int32_t* offsets;      // [E+1]
   const int32_t* slot_of_expert;
-  const int32_t* tile_prefix;
-  int32_t* counters;           // [8] per-XCD tile counters (zeroed by ffn_tile_map)
   const char* pool;
   int64_t slot_stride;
-  int64_t b_off;
-  int64_t s_off0, s_off1;      // GATEUP: gate and up scale grids [F/128][K/128]; DOWN: down grid [d/128][F/128]
-  int N, K;
-  void* out;                   // GATEUP: Hq [rows, N/2] e4m3; DOWN: y [rows, N]
-  float* out_scale;            // GATEUP: Hs [rows, N/256]
+  int64_t b_off;               // byte offset of B (the [N, K] fragment tiles) in a bundle
+  int64_t s_off0, s_off1;      // GATEUP: gate and up scale grids [F/128][K/128]; DOWN: [d/128][F/128]
+  int E, N, K;
+  void* out;                   // GATEUP: Hq [rows, N/2] e4m3; DOWN: y [rows, N] (bf16 or f32)
+  float* out_scale_t;          // GATEUP: Hs [N/256][out_scale_ld] (kb-major for the down GEMM)
+  int out_scale_ld;
   int out_dtype;
-  int E;
 };
 
-// 4 bytes per lane from global into LDS at lds_base + 4 * lane, as inline assembly (see
-// dma16_asm). lds_base must be wave-uniform.
-__device__ __forceinline__ void dma4_asm(const void* g, const void* lds_base) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory");
-}
+struct Fp8Args {
+  Fp8Prob p[2];
+  int E0;                      // experts of problem 0; global expert g >= E0 is problem 1's g - E0
+  int n_exp;                   // E0 (+ E1)
+  const int32_t* tile_prefix;  // [n_exp + 1]: tiles (m-tiles x n-tiles) before global expert g
+  int32_t* counters;           // [8] per-XCD tile counters (zeroed by fp8_tile_map)
+};
 
-// One 128 x 256 tile on 8 waves (2 wave rows of 64 x 4 wave columns of 64, two waves per
-// SIMD, so one wave's block-scale promotion and LDS reads run while the other's MFMAs do).
-// The weight block scales the tile needs (two per 128-column stage) are staged in LDS
-// first (s_wscale), so the main loop issues no global loads of its own besides the ring.
-template <int MODE>
-__device__ __forceinline__ void gemm_fp8_tile(const Fp8Args& p, char (*smem)[kF8StageBytes],
-                                              float (*amax_x)[kF8BM], float (*s_wscale)[kF8MaxKB], int e, int row0,
-                                              int row_end, int n0) {
-  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 2, wn = w & 3;   // wave row (4 m-blocks) x wave column (4 n-blocks)
-  const int KB = p.K / 128;
-  const char* bundle = p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride;
-  const char* B = bundle + p.b_off;
-  // GATEUP: [0] gate and [1] up scales of the tile's 128 hidden rows; DOWN: the scales of
-  // the tile's two 128-column blocks (wave column wn uses [wn / 2])
-  for (int i = threadIdx.x; i < 2 * KB; i += blockDim.x) {
-    const int which = i / KB, s = i - which * KB;
-    const float* grid;
-    int blk;
-    if constexpr (MODE == MODE_GATEUP) {
-      grid = reinterpret_cast<const float*>(bundle + (which ? p.s_off1 : p.s_off0));
-      blk = n0 / 256;
-    } else {
-      grid = reinterpret_cast<const float*>(bundle + p.s_off0);
-      blk = n0 / 128 + which;
-    }
-    s_wscale[which][s] = grid[blk * KB + s];
+// Tile prefixes of the gate/up and the down GEMM for one or two problems (m-tiles of 256 rows
+// times the problem's n-tiles of 256 columns per expert), and zeroed tile counters.
+__global__ __launch_bounds__(1024) void fp8_tile_map(Fp8Args gu, int nt_dn0, int nt_dn1, int32_t* prefix_gu,
+                                                     int32_t* prefix_dn, int32_t* counters, int n_counters) {
+  __shared__ int32_t mt[2 * kMaxE + 2];
+  const int tid = threadIdx.x;
+  if (tid < n_counters) counters[tid] = 0;
+  for (int g = tid; g < gu.n_exp; g += blockDim.x) {
+    const Fp8Prob& p = g < gu.E0 ? gu.p[0] : gu.p[1];
+    const int e = g < gu.E0 ? g : g - gu.E0;
+    const int n = p.offsets[e + 1] - p.offsets[e];
+    mt[g] = (n > 0 && p.slot_of_expert[e] >= 0) ? (n + kQBM - 1) / kQBM : 0;
   }
   __syncthreads();
-  auto f = [](int r) { return ((r >> 1) + 4 * (r & 1)) & 7; };
-  auto src_row = [&](int r) {
-    r = r < row_end ? r : row_end - 1;
-    return p.a_row_src ? p.a_row_src[r] / p.a_row_div : r;
-  };
-
-  // Per stage each wave issues 7 DMA instructions: A rows 16w .. 16w+15 (two of 8 rows;
-  // lane j loads chunk (j%8) ^ f(r) of row r = 16w + 8t + j/8), B n-blocks 2w and 2w+1
-  // (two 1 KiB halves each) and one of the row-scale quarters (rows 64 (w & 1) + lane into
-  // slot w & 3; waves 4-7 repeat 0-3 with the same bytes, so every wave has the same count).
-  const uint8_t* aptr[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int tr = 16 * w + 8 * t + (lane >> 3);   // row within the 128-row tile
-    aptr[t] = p.a + (size_t)src_row(row0 + tr) * p.K + 16 * ((lane & 7) ^ f(tr & 15));
+  if (tid == 0) {
+    int a = 0, b = 0;
+    for (int g = 0; g < gu.n_exp; ++g) {
+      const bool second = g >= gu.E0;
+      prefix_gu[g] = a;
+      prefix_dn[g] = b;
+      a += mt[g] * ((second ? gu.p[1].N : gu.p[0].N) / kQBN);
+      b += mt[g] * (second ? nt_dn1 : nt_dn0);
+    }
+    prefix_gu[gu.n_exp] = a;
+    prefix_dn[gu.n_exp] = b;
   }
-  const float* sptr = p.a_scale + (size_t)src_row(row0 + 64 * (w & 1) + lane) * KB;
-  const char* bptr = B + ((int64_t)(n0 / 16 + w * 2) * KB) * 2048 + 16 * lane;
+}
 
-  auto issue = [&](int s) {
-    char* base = smem[s % kF8Stages];
+// Scales of the activation rows in the order and layout the GEMM reads them:
+// out[kb * ld + r] = a_scale[src(r) * KB + kb] for GEMM rows r < rows (src(r) = a_row_src[r] /
+// div, or r), and 1 for r in [rows, ld), which a last tile may read.
+__global__ __launch_bounds__(256) void fp8_scales_kb_major(const float* __restrict__ a_scale,
+                                                           const int32_t* __restrict__ a_row_src, int div, int rows,
+                                                           int KB, int ld, float* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)KB * ld) return;
+  const int kb = (int)(i / ld), r = (int)(i % ld);
+  float v = 1.0f;
+  if (r < rows) v = a_scale[(size_t)(a_row_src ? a_row_src[r] / div : r) * KB + kb];
+  out[i] = v;
+}
+
+// Direct-to-LDS loads with a scalar base and a 32-bit per-lane offset (global_load_lds with
+// saddr), as inline assembly for the reason given at dma16_asm; each sets M0 itself, which the
+// build checks. lds_base and g_base must be wave-uniform.
+__device__ __forceinline__ void dma16_sb(const void* g_base, uint32_t off, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(g_base), "s"(lds)
+               : "memory");
+}
+__device__ __forceinline__ void dma4_sb(const void* g_base, uint32_t off, const void* lds_base) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)lds_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(g_base), "s"(lds)
+               : "memory");
+}
+
+__device__ __forceinline__ int fp8_swz(int r) { return ((r >> 1) + 4 * (r & 1)) & 7; }
+
+// A pointer the compiler cannot prove wave-uniform (it was loaded through a vector load) made
+// uniform, so it can be a scalar base of the direct-to-LDS loads.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
+
+// One 256 x 256 tile: rows [row0, row_end) of expert e (at most 256 of them), columns n0..n0+255.
+template <int MODE>
+__device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s_wscale)[kQMaxKB],
+                                         float (*amax_x)[kQBM], int e, int row0, int row_end, int n0) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w >> 2, wn = w & 3;
+  const int KB = p.K / 128;
+  const int valid = min(kQBM, row_end - row0);
+  const char* bundle = uniform_ptr(p.pool + (int64_t)p.slot_of_expert[e] * p.slot_stride);
+  // the tile's weight block scales: GATEUP [0] gate, [1] up of hidden block n0/256; DOWN the
+  // scales of column blocks n0/128 and n0/128 + 1 (wave column wn uses [wn >> 1])
+  for (int i = threadIdx.x; i < 2 * KB; i += blockDim.x) {
+    const int which = i / KB, s = i - which * KB;
+    float v;
+    if constexpr (MODE == MODE_GATEUP)
+      v = reinterpret_cast<const float*>(bundle + (which ? p.s_off1 : p.s_off0))[(n0 / 256) * KB + s];
+    else
+      v = reinterpret_cast<const float*>(bundle + p.s_off0)[(n0 / 128 + which) * KB + s];
+    s_wscale[which][s] = v;
+  }
+
+  // DMA: per stage wave w loads tile rows 32w..32w+31 of A (4 instructions of 8 rows; lane j
+  // takes row 32w + 8t + j/8, chunk (j%8) ^ f(row), which lands at position j%8), B n-blocks
+  // 2w and 2w+1 (two 1 KiB halves each) and, for w < 4, the row scales of rows 64w..64w+63.
+  uint32_t a_off[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) dma16_asm(aptr[t] + s * 128, base + kF8A + (2 * w + t) * 1024);
+  for (int t = 0; t < 4; ++t) {
+    const int r = 32 * w + 8 * t + (lane >> 3);
+    const int rr = min(r, valid - 1);
+    const int src = p.a_row_src ? p.a_row_src[row0 + rr] / p.a_row_div : row0 + rr;
+    a_off[t] = (uint32_t)src * (uint32_t)p.K + 16u * (uint32_t)((lane & 7) ^ fp8_swz(r & 15));
+  }
+  const uint32_t b_off = (uint32_t)((n0 / 16 + 2 * w) * KB) * 2048u + 16u * lane;
+  const uint32_t b_step = (uint32_t)KB * 2048u;
+  const char* a_base = uniform_ptr(reinterpret_cast<const char*>(p.a));
+  const char* b_base = uniform_ptr(bundle + p.b_off);
+  const char* s_base = uniform_ptr(reinterpret_cast<const char*>(p.a_scale_t + row0));
+  const int a_rows_w = valid - 32 * w;   // rows of this wave's A share that exist
+  auto issue = [&](int s) {
+    char* buf = ring + (s & 1) * kQStage;
+    const char* ab = a_base + (size_t)s * 128;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (8 * t < a_rows_w) dma16_sb(ab, a_off[t], buf + kQA + (4 * w + t) * 1024);
+    const char* bb = b_base + (size_t)s * 2048;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        dma16_asm(bptr + ((int64_t)i * KB + s) * 2048 + h * 1024, base + kF8B + (w * 2 + i) * 2048 + h * 1024);
-    dma4_asm(sptr + s, base + kF8S + (w & 3) * 256);
-  };
-  auto wait_dma = [&](bool more) {
-    if (more) asm volatile("s_waitcnt vmcnt(7)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        dma16_sb(bb, b_off + i * b_step + h * 1024, buf + kQB + (2 * w + i) * 2048 + h * 1024);
+    if (w < 4) dma4_sb(s_base + (size_t)s * p.a_scale_ld * 4, 4u * (64 * w + lane), buf + kQS + 256 * w);
   };
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[8][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // fragment read offsets: A (row l%16, chunks 2(l/16) and 2(l/16)+1), B (two halves)
-  const int ar = lane & 15, ac = 2 * (lane >> 4);
-  const int a_off0 = 16 * (8 * ar + ((ac + 0) ^ f(ar)));
-  const int a_off1 = 16 * (8 * ar + ((ac + 1) ^ f(ar)));
+  // fragment offsets: A row 16 i + l%16 of the wave row, chunks 2(l/16) and 2(l/16)+1
+  const int fr = fp8_swz(lane & 15), ac = 2 * (lane >> 4);
+  const int a_frag0 = kQA + 128 * (128 * wm + (lane & 15)) + 16 * (ac ^ fr);
+  const int a_frag1 = kQA + 128 * (128 * wm + (lane & 15)) + 16 * ((ac + 1) ^ fr);
+  const int s_frag = kQS + 4 * (128 * wm + 4 * (lane >> 4));
+  // the wave's n-blocks: GATEUP gate (wn even) or up (wn odd) n-blocks of hidden half wn >> 1;
+  // DOWN four consecutive ones
+  auto nblk = [&](int j) { return MODE == MODE_GATEUP ? (wn >> 1) * 8 + 2 * j + (wn & 1) : wn * 4 + j; };
+  const int nmb = min(8, (valid - 128 * wm + 15) >> 4);   // m-blocks of the wave with rows (<= 0: none)
+  const int wsel = MODE == MODE_GATEUP ? (wn & 1) : (wn >> 1);
+  const f32x4_t zero{0.f, 0.f, 0.f, 0.f};
 
-  const int e8m0_one = 127;   // MFMA block scale 2^0: the fp32 block scales are applied in software
-  // A wave row whose 64 rows all lie past the expert's last row (the short last m-tile of an
-  // expert whose rows just pass a multiple of 128) only moves data: it issues its share of
-  // the DMA and joins the barriers, but reads no fragments and issues no MFMAs; its
-  // accumulators stay zero and the epilogue stores no row of it.
-  const bool idle = row0 + wm * 64 >= row_end;
   issue(0);
-  if (KB > 1) issue(1);
   for (int s = 0; s < KB; ++s) {
-    wait_dma(s + 1 < KB);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // stage s has landed for every wave, and every wave is done with stage s - 1's buffer (its
+    // fragment reads have completed; at s = 0 the weight scales above are written)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     barrier_no_fence();
-    if (s + 2 < KB) issue(s + 2);
-    if (idle) continue;
-    const char* base = smem[s % kF8Stages];
-    i32x8_t fa[4];
+    if (s + 1 < KB) issue(s + 1);
+    if (nmb <= 0) continue;
+    const char* buf = ring + (s & 1) * kQStage;
+    const float sw = s_wscale[wsel][s];
+    i32x8_t fb[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const char* blk = base + kF8A + (wm * 4 + i) * 2048;
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk + a_off0);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + a_off1);
-      fa[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    // Software-pipelined block-scale promotion. The 16 MFMAs of the stage (n-block jj,
-    // m-block i: k = 4 jj + i) write a ring of 6 partial tiles; partial k is promoted
-    // (acc += part * row scale * weight scale) after MFMA k + 4 has been issued, so the
-    // VALU work of one tile runs while the matrix core computes the next ones, and every
-    // partial has had four MFMA issue slots to complete (the hazard recognizer does not
-    // see into the inline-asm MFMAs; the drain waits explicitly). GATEUP walks the gate
-    // n-blocks (even j) before the up n-blocks (odd j), so one set of combined scales is
-    // live at a time.
-    const f32x4_t* sa_p = reinterpret_cast<const f32x4_t*>(base + kF8S + 4 * (wm * 64 + 4 * (lane >> 4)));
-    f32x4_t sc[4];
-    auto make_sc = [&](int which) {
-      const float sw = s_wscale[which][s];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[i] = sa_p[4 * i] * sw;
-    };
-    make_sc(MODE == MODE_GATEUP ? 0 : wn >> 1);
-    auto jof = [](int jj) { return MODE == MODE_GATEUP ? ((jj & 1) << 1) | (jj >> 1) : jj; };
-    auto load_b = [&](int jj) {
-      const char* blk = base + kF8B + (wn * 4 + jof(jj)) * 2048 + 16 * lane;
+    for (int j = 0; j < 4; ++j) {
+      const char* blk = buf + kQB + nblk(j) * 2048 + 16 * lane;
       const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
       const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
+      fb[j] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+    auto frag_a = [&](int i) {
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + a_frag0 + 2048 * i);
+      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + a_frag1 + 2048 * i);
       return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
-    i32x8_t fbuf[2];
-    fbuf[0] = load_b(0);
-    f32x4_t part[6];
+    auto row_scales = [&](int i) { return *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * i) * sw; };
+    // operand formats 0 (e4m3), block scales 2^0: the fp32 scales are applied on the VALU
+    auto mfma = [&](const i32x8_t& fa, int j) {
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], zero, 0, 0, 0, 127, 0, 127);
+    };
+    // m-block by m-block, skipping those past the tile's last row (uniform per wave); the
+    // branches also keep the compiler from hoisting every block's fragment reads, which would
+    // not fit the registers. The second wave on the SIMD fills the wait between an MFMA and the
+    // promotion of its result.
 #pragma unroll
-    for (int k = 0; k < 20; ++k) {
-      if (k < 16) {
-        const int jj = k >> 2, i = k & 3;
-        if (i == 0 && jj + 1 < 4) fbuf[(jj + 1) & 1] = load_b(jj + 1);
-        // ("memory" keeps the compiler from sinking the next n-block's LDS reads to their use)
-        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
-                     : "=v"(part[k % 6])
-                     : "v"(fa[i]), "v"(fbuf[jj & 1]), "v"(e8m0_one)
-                     : "memory");
-      }
-      if (k == 16) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-      if (k >= 4) {
-        const int kk = k - 4, i = kk & 3, jj = kk >> 2;
-        if (MODE == MODE_GATEUP && kk == 8) make_sc(1);   // the up n-blocks start here
-        acc[i][jof(jj)] += part[kk % 6] * sc[i];
+    for (int i = 0; i < 8; ++i) {
+      if (i < nmb) {
+        const i32x8_t fa = frag_a(i);
+        const f32x4_t sc = row_scales(i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += mfma(fa, j) * sc;
       }
     }
   }
+  // every wave is done with the ring (its space is reused below)
+  __syncthreads();
 
-  const int rbase = row0 + wm * 64 + 4 * (lane >> 4);
+  // output rows of lane l: 128 wm + 16 i + 4 (l / 16) + q; columns 16 j + l % 16 of the wave's 64
   if constexpr (MODE == MODE_GATEUP) {
-    // H = silu(G) * U over this tile's 128 hidden columns (32 per wave column), then per-row
-    // e4m3 quantisation with one scale per row for the 128 columns (amax over the 4 waves)
-    const int F = p.N / 2;
-    float h[4][2][4];  // [m-block][pair][row q]
-    float am[4][4];    // [m-block][row q]
+    // gate waves hand G to the up waves of the same hidden columns: region (wm, wn >> 1) of
+    // 32 KiB holds [i][j][lane] f32x4
+    f32x4_t* Gr = reinterpret_cast<f32x4_t*>(ring + (wm * 2 + (wn >> 1)) * 32768);
+    if ((wn & 1) == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i)
+        if (i < nmb)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float m = 0.f;
-#pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const float v = silu_f32(acc[i][2 * pp][q]) * acc[i][2 * pp + 1][q];
-          h[i][pp][q] = v;
-          m = fmaxf(m, fabsf(v));
-        }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        am[i][q] = m;
-      }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) amax_x[wn][wm * 64 + i * 16 + 4 * (lane >> 4) + q] = am[i][q];
+          for (int j = 0; j < 4; ++j) Gr[(i * 4 + j) * 64 + lane] = acc[i][j];
     }
     __syncthreads();
-    uint8_t* Hq = static_cast<uint8_t*>(p.out);
-    const int hcol0 = n0 / 2 + wn * 32 + (lane & 15);
+    if (wn & 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i) {
+        if (i < nmb) {
+          float am[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int lr = wm * 64 + i * 16 + 4 * (lane >> 4) + q;
-        const int r = row0 + lr;
-        const float a = fmaxf(fmaxf(amax_x[0][lr], amax_x[1][lr]), fmaxf(amax_x[2][lr], amax_x[3][lr]));
-        const float scale = a > 0.f ? a / 448.0f : 1.0f;
-        if (r < row_end) {
+          for (int j = 0; j < 4; ++j) {
+            const f32x4_t g = Gr[(i * 4 + j) * 64 + lane];
 #pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const float y = fminf(fmaxf(h[i][pp][q] / scale, -448.0f), 448.0f);
-            Hq[(size_t)r * F + hcol0 + pp * 16] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
+            for (int q = 0; q < 4; ++q) {
+              const float h = silu_fast(g[q]) * acc[i][j][q];
+              acc[i][j][q] = h;
+              am[q] = fmaxf(am[q], fabsf(h));
+            }
           }
-          if (wn == 0 && (lane & 15) == 0) p.out_scale[(size_t)r * (F / 128) + n0 / kF8BN] = scale;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) am[q] = fmaxf(am[q], __shfl_xor(am[q], off, 64));
+          }
+          if ((lane & 15) == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) amax_x[wn >> 1][128 * wm + 16 * i + 4 * (lane >> 4) + q] = am[q];
+          }
         }
       }
+    }
+    __syncthreads();
+    if (wn & 1) {
+      // per row: one scale for the tile's 128 hidden columns; codes staged in LDS (the first
+      // 8 KiB of this wave's G region, read above) as [128 rows][64 B] for 16-byte stores
+      uint8_t* codes = reinterpret_cast<uint8_t*>(Gr);
+      const int F = p.N / 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i < nmb) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int lr = 16 * i + 4 * (lane >> 4) + q;          // row within the wave's 128
+            const int tr = 128 * wm + lr;                          // row within the tile
+            const float a = fmaxf(amax_x[0][tr], amax_x[1][tr]);
+            const float scale = a > 0.f ? a / 448.0f : 1.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float y = fminf(fmaxf(acc[i][j][q] / scale, -448.0f), 448.0f);
+              codes[lr * 64 + 16 * j + (lane & 15)] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
+            }
+            if (wn == 1 && (lane & 15) == 0 && tr < valid)
+              p.out_scale_t[(size_t)(n0 / 256) * p.out_scale_ld + row0 + tr] = scale;
+          }
+        }
+      }
+      // this wave's LDS writes are done before its lanes read each other's bytes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      uint8_t* Hq = static_cast<uint8_t*>(p.out);
+      const int hcol0 = n0 / 2 + 64 * (wn >> 1);
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int idx = it * 64 + lane;               // 512 chunks of 16 B: row idx/4, chunk idx%4
+        const int lr = idx >> 2, ch = idx & 3;
+        const int tr = 128 * wm + lr;
+        if (tr < valid) {
+          const i32x4_t v = *reinterpret_cast<const i32x4_t*>(codes + lr * 64 + 16 * ch);
+          *reinterpret_cast<i32x4_t*>(Hq + (size_t)(row0 + tr) * F + hcol0 + 16 * ch) = v;
+        }
+      }
+    }
+  } else if (p.out_dtype == MOE_BF16) {
+    // y staged through LDS per wave ([128 rows][64 cols] bf16, 16 KiB) for 16-byte stores
+    bf16_t* yl = reinterpret_cast<bf16_t*>(ring + w * 16384);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < nmb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            yl[(16 * i + 4 * (lane >> 4) + q) * 64 + 16 * j + (lane & 15)] = f32_to_bf16(acc[i][j][q]);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bf16_t* Y = static_cast<bf16_t*>(p.out);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int idx = it * 64 + lane;               // 1024 chunks of 16 B: row idx/8, chunk idx%8
+      const int lr = idx >> 3, ch = idx & 7;
+      const int tr = 128 * wm + lr;
+      if (tr < valid) {
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(yl + lr * 64 + 8 * ch);
+        *reinterpret_cast<i32x4_t*>(Y + (size_t)(row0 + tr) * p.N + n0 + 64 * wn + 8 * ch) = v;
+      }
+    }
   } else {
+    float* Y = static_cast<float*>(p.out);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i) {
+      if (i < nmb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = rbase + i * 16 + q;
-          if (r < row_end) {
-            if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[(size_t)r * p.N + col] = f32_to_bf16(acc[i][j][q]);
-            else static_cast<float*>(p.out)[(size_t)r * p.N + col] = acc[i][j][q];
+          for (int q = 0; q < 4; ++q) {
+            const int tr = 128 * wm + 16 * i + 4 * (lane >> 4) + q;
+            if (tr < valid) Y[(size_t)(row0 + tr) * p.N + n0 + 64 * wn + 16 * j + (lane & 15)] = acc[i][j][q];
           }
-        }
       }
+    }
   }
 }
 
+// Tile L -> (problem, expert e, m-tile mt, n-tile nt). Tiles run expert by expert; within an
+// expert the m-tiles of one n-tile are adjacent, so the tiles that share a weight tile are
+// taken close together in time by the same XCD.
+__device__ __forceinline__ void fp8_tile_coords(const Fp8Args& a, int NT0, int NT1, int L, int& g, int& mt, int& nt) {
+  const int32_t* pre = a.tile_prefix;
+  int lo = 0, hi = a.n_exp - 1;   // last g with pre[g] <= L
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= L) lo = mid;
+    else hi = mid - 1;
+  }
+  g = lo;
+  const int NT = g < a.E0 ? NT0 : NT1;
+  const int mte = (pre[g + 1] - pre[g]) / NT;
+  const int local = L - pre[g];
+  nt = local / mte;
+  mt = local - nt * mte;
+}
+
 template <int MODE>
-__global__ __launch_bounds__(512, 1) void ffn_gemm_fp8(Fp8Args p) {
-  __shared__ __attribute__((aligned(1024))) char smem[kF8Stages][kF8StageBytes];
-  __shared__ float amax_x[4][kF8BM];
-  __shared__ float s_wscale[2][kF8MaxKB];
+__global__ __launch_bounds__(512, 1) void ffn_gemm_fp8(Fp8Args a) {
+  __shared__ __attribute__((aligned(1024))) char ring[kQRing];
+  __shared__ float s_wscale[2][kQMaxKB];
+  __shared__ float amax_x[2][kQBM];
   __shared__ int s_tile;
-  const int NT = p.N / kF8BN;
-  const int total = p.tile_prefix[p.E] * NT;
+  const int NT0 = a.p[0].N / kQBN, NT1 = a.p[1].N / kQBN;
+  const int total = a.tile_prefix[a.n_exp];
   int range = 0;   // thread 0: XCD ranges this block has used up
   for (;;) {
-    if (threadIdx.x == 0) s_tile = take_tile(p.counters, total, range);
+    if (threadIdx.x == 0) s_tile = take_tile(a.counters, total, range);
     __syncthreads();
-    const int L = s_tile;
+    const int L = __builtin_amdgcn_readfirstlane(s_tile);
     if (L < 0) return;
-    int e, mt, mte, nt;
-    tile_coords(p.tile_prefix, p.E, NT, L, e, mt, mte, nt);
-    const int row0 = p.offsets[e] + mt * kF8BM;
-    gemm_fp8_tile<MODE>(p, smem, amax_x, s_wscale, e, row0, p.offsets[e + 1], nt * kF8BN);
+    int g, mt, nt;
+    fp8_tile_coords(a, NT0, NT1, L, g, mt, nt);
+    const bool second = g >= a.E0;
+    const Fp8Prob& p = second ? a.p[1] : a.p[0];
+    const int e = __builtin_amdgcn_readfirstlane(second ? g - a.E0 : g);
+    const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e] + mt * kQBM);
+    const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+    fp8_tile<MODE>(p, ring, s_wscale, amax_x, e, row0, row_end, __builtin_amdgcn_readfirstlane(nt * kQBN));
     // every wave is done with the ring, the scale and amax arrays, and has read s_tile
     __syncthreads();
   }

@@ -104,18 +104,27 @@ int decode_down_splits(const moe_expert_table* t, int rows) {
   return kt > 64 ? std::min(8, (kt + 47) / 48) : 1;
 }
 
-// Workspace: H [rows, F] (fp32, bf16 or e4m3) [+ e4m3 H scales [rows, F/128]], then the
-// tile prefix and the per-XCD work counters of the persistent GEMMs, then (for a split
-// decode down projection) the fp32 partials [splits][rows][d] and the arrival counts.
+// Workspace: H [rows, F] (fp32, bf16 or e4m3), then the tile prefix and the per-XCD work
+// counters of the persistent GEMMs, then (for a split decode down projection) the fp32
+// partials [splits][rows][d] and the arrival counts. fp8 problems add the e4m3 H scales
+// [F/128][rows + 256] and the activation scales [d/128][rows + 256] (both block-major in GEMM
+// row order, as the fp8 GEMM reads them), and their map holds the gate/up and the down tile
+// prefixes of up to two problems.
+constexpr int kFp8MapInts = 2 * (2 * kMaxE + 2) + 16;
+
 size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off,
-                 size_t* hs_off = nullptr, size_t* part_off = nullptr, size_t* arrived_off = nullptr) {
+                 size_t* hs_off = nullptr, size_t* part_off = nullptr, size_t* arrived_off = nullptr,
+                 size_t* as_off = nullptr) {
   const size_t hsz = act_dtype == MOE_F32 ? 4 : act_dtype == MOE_FP8_E4M3 ? 1 : 2;
   *h_off = 0;
   size_t end = align_up((size_t)rows * t->d_ff * hsz, 256);
   if (hs_off) *hs_off = end;
-  if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)rows * (t->d_ff / 128) * 4, 256);
+  if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)(rows + 256) * (t->d_ff / 128) * 4, 256);
+  if (as_off) *as_off = end;
+  if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)(rows + 256) * (t->d_model / 128) * 4, 256);
   *map_off = end;   // tile prefix [E+1], then the work counters [16]
-  end = *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
+  if (act_dtype == MOE_FP8_E4M3) end = *map_off + align_up((size_t)kFp8MapInts * 4, 256);
+  else end = *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
   const int S = decode_down_splits(t, rows);
   if (part_off) *part_off = end;
   if (S > 1) end += align_up((size_t)S * rows * t->d_model * 4, 256);
@@ -200,11 +209,15 @@ moe_status check_call(const FfnCall& c, const char* who) {
   } else {
     MOE_REQUIRE(act_dtype == MOE_FP8_E4M3 && c.a_scale != nullptr, MOE_EUNSUPPORTED,
                 "%s: fp8 weights need e4m3 activations and their scales", who);
-    MOE_REQUIRE((2 * F) % kF8BN == 0 && d % kF8BN == 0 && d % 128 == 0 && F % 128 == 0, MOE_EUNSUPPORTED,
-                "%s: fp8 tiles need d and 2F multiples of %d and F a multiple of 128", who, kF8BN);
+    MOE_REQUIRE((2 * F) % kQBN == 0 && d % kQBN == 0 && d % 128 == 0 && F % 128 == 0, MOE_EUNSUPPORTED,
+                "%s: fp8 tiles need d and 2F multiples of %d and F a multiple of 128", who, kQBN);
     MOE_REQUIRE(aligned(c.a_scale, 4), MOE_EINVAL, "%s: a_scale must be 4-byte aligned", who);
-    MOE_REQUIRE(d / 128 <= kF8MaxKB && F / 128 <= kF8MaxKB, MOE_EUNSUPPORTED, "%s: fp8 tiles need d and F at most %d",
-                who, 128 * kF8MaxKB);
+    MOE_REQUIRE(d / 128 <= kQMaxKB && F / 128 <= kQMaxKB, MOE_EUNSUPPORTED, "%s: fp8 tiles need d and F at most %d",
+                who, 128 * kQMaxKB);
+    // the fp8 GEMM addresses A rows and weight tiles with 32-bit offsets
+    const long long a_rows = c.a_row_src ? (rows + c.a_row_div - 1) / c.a_row_div : rows;
+    MOE_REQUIRE(std::max(a_rows * d, (long long)rows * F) < (1ll << 32) && 2ll * F * d < (1ll << 32), MOE_EUNSUPPORTED,
+                "%s: fp8 activations or weights larger than 4 GiB per matrix", who);
   }
   return MOE_OK;
 }
@@ -344,6 +357,94 @@ moe_status launch_decode(const FfnCall* calls, int n, hipStream_t s, const Decod
   return check_launch("moe_grouped_ffn bf16 decode");
 }
 
+// One or two checked fp8 problems (the routed experts, then a shared expert) in one gate/up
+// launch and one down launch: the activation scales are laid out block-major in GEMM row
+// order, one tile map covers both problems (in the first problem's workspace), and the
+// persistent GEMMs take the tiles of both from the same queues.
+moe_status run_fp8(const FfnCall* c, int n, hipStream_t s) {
+  Fp8Args gu{}, dn{};
+  int32_t *prefix_gu = nullptr, *prefix_dn = nullptr, *counters = nullptr;
+  long long bound_gu = 0, bound_dn = 0;
+  for (int i = 0; i < n; ++i) {
+    const FfnCall& q = c[i];
+    const moe_expert_table& t = q.t;
+    size_t h_off, map_off, hs_off, as_off;
+    ws_layout(&t, q.rows, q.act_dtype, &h_off, &map_off, &hs_off, nullptr, nullptr, &as_off);
+    const BundleGeom g = bundle_geom(t.d_model, t.d_ff, t.w_dtype);
+    const int d = t.d_model, F = t.d_ff, ld = q.rows + 256;
+    float* As = reinterpret_cast<float*>(q.ws + as_off);
+    float* Hs = reinterpret_cast<float*>(q.ws + hs_off);
+    uint8_t* Hq = reinterpret_cast<uint8_t*>(q.ws + h_off);
+    if (i == 0) {
+      prefix_gu = reinterpret_cast<int32_t*>(q.ws + map_off);
+      prefix_dn = prefix_gu + 2 * kMaxE + 2;
+      counters = prefix_dn + 2 * kMaxE + 2;
+    }
+    const long long n_as = (long long)(d / 128) * ld;
+    hipLaunchKernelGGL(fp8_scales_kb_major, dim3((unsigned)((n_as + 255) / 256)), dim3(256), 0, s, q.a_scale,
+                       q.a_row_src, q.a_row_div, q.rows, d / 128, ld, As);
+    Fp8Prob& a = gu.p[i];
+    a.a = static_cast<const uint8_t*>(q.a);
+    a.a_scale_t = As;
+    a.a_scale_ld = ld;
+    a.a_row_src = q.a_row_src;
+    a.a_row_div = q.a_row_div;
+    a.offsets = q.offsets;
+    a.slot_of_expert = t.slot_of_expert;
+    a.pool = static_cast<const char*>(t.pool);
+    a.slot_stride = t.slot_stride;
+    a.b_off = g.gu_off;
+    a.s_off0 = g.sg_off;
+    a.s_off1 = g.su_off;
+    a.E = t.n_experts;
+    a.N = 2 * F;
+    a.K = d;
+    a.out = Hq;
+    a.out_scale_t = Hs;
+    a.out_scale_ld = ld;
+    a.out_dtype = MOE_FP8_E4M3;
+    Fp8Prob& b = dn.p[i];
+    b = a;
+    b.a = Hq;
+    b.a_scale_t = Hs;
+    b.a_row_src = nullptr;
+    b.a_row_div = 1;
+    b.b_off = g.dn_off;
+    b.s_off0 = g.sd_off;
+    b.s_off1 = 0;
+    b.N = d;
+    b.K = F;
+    b.out = q.y;
+    b.out_scale_t = nullptr;
+    b.out_scale_ld = 0;
+    b.out_dtype = q.y_dtype;
+    // at most rows / 256 + min(E, rows) m-tiles
+    const long long mt = q.rows / kQBM + std::min<long long>(t.n_experts, q.rows);
+    bound_gu += mt * (2 * F / kQBN);
+    bound_dn += mt * (d / kQBN);
+  }
+  gu.E0 = dn.E0 = c[0].t.n_experts;
+  gu.n_exp = dn.n_exp = c[0].t.n_experts + (n > 1 ? c[1].t.n_experts : 0);
+  if (n == 1) gu.p[1] = gu.p[0], dn.p[1] = dn.p[0];
+  hipLaunchKernelGGL(fp8_tile_map, dim3(1), dim3(1024), 0, s, gu, dn.p[0].N / kQBN, dn.p[1].N / kQBN, prefix_gu,
+                     prefix_dn, counters, 16);
+  gu.tile_prefix = prefix_gu;
+  gu.counters = counters;
+  dn.tile_prefix = prefix_dn;
+  dn.counters = counters + 8;
+  const long long n_cu = cu_count();
+  // persistent: at most one block per CU, a multiple of 8 (one per XCD in turn)
+  long long nblk = std::min(bound_gu, n_cu);
+  prof_mark(s, MOE_PROF_GATEUP, false);
+  hipLaunchKernelGGL(ffn_gemm_fp8<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, gu);
+  prof_mark(s, MOE_PROF_GATEUP, true);
+  nblk = std::min(bound_dn, n_cu);
+  prof_mark(s, MOE_PROF_DOWN, false);
+  hipLaunchKernelGGL(ffn_gemm_fp8<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, dn);
+  prof_mark(s, MOE_PROF_DOWN, true);
+  return check_launch("moe_grouped_ffn fp8");
+}
+
 // Runs one checked problem on stream s.
 moe_status run_call(const FfnCall& c, hipStream_t s) {
   if (c.rows == 0) return MOE_OK;
@@ -419,60 +520,10 @@ moe_status run_call(const FfnCall& c, hipStream_t s) {
     prof_mark(s, MOE_PROF_DOWN, true);
     return check_launch("moe_grouped_ffn bf16");
   }
-  {
-    size_t hs_off;
-    ws_layout(&t, rows, act_dtype, &h_off, &map_off, &hs_off);
-    int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
-    uint8_t* Hq = reinterpret_cast<uint8_t*>(wsb + h_off);
-    float* Hs = reinterpret_cast<float*>(wsb + hs_off);
-    int32_t* counters = reinterpret_cast<int32_t*>(wsb + map_off + align_up((size_t)(E + 2) * 4, 256));
-    hipLaunchKernelGGL(ffn_tile_map, dim3(1), dim3(((E + 63) / 64) * 64), 0, s, offsets, t.slot_of_expert,
-                       tile_prefix, E, kF8BM, 0, counters, 16);
-    const int max_mt = (rows + kF8BM - 1) / kF8BM + (E < rows ? E : rows);
-    const long long n_cu = cu_count();
-    Fp8Args p{};
-    p.a = static_cast<const uint8_t*>(a);
-    p.a_scale = a_scale;
-    p.a_row_src = a_row_src;
-    p.a_row_div = a_row_div;
-    p.offsets = offsets;
-    p.slot_of_expert = t.slot_of_expert;
-    p.tile_prefix = tile_prefix;
-    p.counters = counters;
-    p.pool = static_cast<const char*>(t.pool);
-    p.slot_stride = t.slot_stride;
-    p.E = E;
-    p.b_off = g.gu_off;
-    p.s_off0 = g.sg_off;
-    p.s_off1 = g.su_off;
-    p.N = 2 * F;
-    p.K = d;
-    p.out = Hq;
-    p.out_scale = Hs;
-    long long nblk = std::min((long long)max_mt * (p.N / kF8BN), n_cu);
-    prof_mark(s, MOE_PROF_GATEUP, false);
-    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, p);
-    prof_mark(s, MOE_PROF_GATEUP, true);
-    p.a = Hq;
-    p.a_scale = Hs;
-    p.a_row_src = nullptr;
-    p.a_row_div = 1;
-    p.b_off = g.dn_off;
-    p.s_off0 = g.sd_off;
-    p.s_off1 = 0;
-    p.N = d;
-    p.K = F;
-    p.out = y;
-    p.out_scale = nullptr;
-    p.out_dtype = y_dtype;
-    p.counters = counters + 8;
-    nblk = std::min((long long)max_mt * (p.N / kF8BN), n_cu);
-    prof_mark(s, MOE_PROF_DOWN, false);
-    hipLaunchKernelGGL(ffn_gemm_fp8<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, p);
-    prof_mark(s, MOE_PROF_DOWN, true);
-  }
-  return check_launch("moe_grouped_ffn fp8");
+  return run_fp8(&c, 1, s);
 }
+
+
 
 }  // namespace
 }  // namespace moeffn
@@ -529,6 +580,9 @@ extern "C" moe_status moe_grouped_ffn_batch(const moe_ffn_problem* problems, int
   hipStream_t s = as_stream(stream);
   if (n == 2 && decode_path(c[0]) && decode_path(c[1]) && c[0].t.w_dtype == c[1].t.w_dtype)
     return launch_decode(c, 2, s);
+  if (n == 2 && c[0].t.w_dtype == MOE_FP8_E4M3 && c[1].t.w_dtype == MOE_FP8_E4M3 && c[0].rows > 0 && c[1].rows > 0 &&
+      c[0].t.d_model == c[1].t.d_model)
+    return run_fp8(c, 2, s);   // both problems in one launch per GEMM
   for (int i = 0; i < n; ++i)
     if (moe_status st = run_call(c[i], s)) return st;
   return MOE_OK;

@@ -220,6 +220,13 @@ class MoELayer:
         return (self.shared is not None and self.cache is None and self.cache_dev is None
                 and self.w_code in (B.MOE_BF16, B.MOE_MXFP4) and 0 < T <= 64)
 
+    def shared_in_routed_launch(self, T: int) -> bool:
+        """Whether a T-token forward runs the shared expert as one more group of the routed
+        experts' prefill GEMM launches (fp8 weights, every expert resident): one tile list for both,
+        so neither GEMM competes with the other from a second stream."""
+        return (self.shared is not None and self.cache is None and self.cache_dev is None
+                and self.w_code == B.MOE_FP8_E4M3 and T > 0)
+
     def _shared_ffn(self, T, a, a_scale, a_code, ydt, main):
         """Launches the shared expert's FFN on the side stream once `a` is ready on `main`; the
         caller joins the side stream back before the combine."""
@@ -263,7 +270,7 @@ class MoELayer:
             # gather rows through perm_src
             p = B.permute(r["idx"], E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=0, ws=ws, stream=main)
             a, a_scale, a_code = p["x_out"], p["x_out_scale"], B.MOE_FP8_E4M3
-            if self.shared is not None:
+            if self.shared is not None and not self.shared_in_routed_launch(T):
                 shared_y = self._shared_ffn(T, a, a_scale, a_code, ydt, main)
         else:
             # routing and grouping in one call; the routed chain is the critical path, so it
@@ -272,6 +279,19 @@ class MoELayer:
                                     w_shared_gate=self.w_sg, ws=ws, stream=main, **self.route_args())
             if self.shared is not None and not merged:
                 shared_y = self._shared_ffn(T, x, None, self.act_code, ydt, main)
+        if self.shared_in_routed_launch(T):
+            # the routed experts and the shared expert (a group of its own, every token) share
+            # one launch per GEMM
+            shared_y = torch.empty(T, d, device=self.device, dtype=y.dtype)
+            probs = [B.ffn_problem(self.table, rows, p["offsets"], a, a_scale=a_scale, act_dtype=a_code,
+                                   a_row_src=p["perm_src"], a_row_div=k, y=y, y_dtype=ydt),
+                     B.ffn_problem(self.shared.table, T, self._shared_offsets(T), a, a_scale=a_scale,
+                                   act_dtype=a_code, y=shared_y, y_dtype=ydt)]
+            bws = self._buf("batch_ws", B.grouped_ffn_batch_workspace_size(probs))
+            B.grouped_ffn_batch(probs, ws=bws, stream=main)
+            out = B.combine(y, p["perm_dst"], r["gate"], shared_y=shared_y, shared_gate=r["shared_gate"],
+                            stream=main)
+            return {"out": out, "route": r, "perm": p, "y": y, "shared_y": shared_y, "waves": 0}
         if merged:
             # a decode step: the shared expert's blocks (dispatched first, they carry the longer
             # rows of its down projection) and the routed experts' share one launch per GEMM
