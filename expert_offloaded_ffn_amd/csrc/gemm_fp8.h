@@ -229,19 +229,47 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
     auto mfma = [&](const i32x8_t& fa, int j) {
       return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], zero, 0, 0, 0, 127, 0, 127);
     };
-    // m-block by m-block, skipping those past the tile's last row (uniform per wave); the
-    // branches also keep the compiler from hoisting every block's fragment reads, which would
-    // not fit the registers. The second wave on the SIMD fills the wait between an MFMA and the
-    // promotion of its result.
+    // Software pipeline over the wave's 8 m-blocks. Per m-block i: read m-block i + 1's
+    // fragment and row scales from LDS, then issue i's four MFMAs, each followed by four of
+    // the FMAs that promote m-block i - 1's partial products (issued a whole block earlier, so
+    // they are ready), then form i + 1's combined scales. Scheduling-group barriers pin that
+    // order (the compiler would otherwise promote each result right after its MFMA and wait
+    // for it), and a scheduling barrier per m-block keeps it from hoisting every block's
+    // reads, which would not fit the registers. Wave rows with fewer rows still run all 8
+    // m-blocks (their extra rows are clamped copies, never stored); wave rows with none skip.
+    i32x8_t fa = frag_a(0);
+    f32x4_t sc = row_scales(0);
+    f32x4_t part[2][4], psc[2];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i < nmb) {
-        const i32x8_t fa = frag_a(i);
-        const f32x4_t sc = row_scales(i);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += mfma(fa, j) * sc;
+      i32x8_t fa_n;
+      f32x4_t sa_n;
+      if (i < 7) {
+        fa_n = frag_a(i + 1);
+        sa_n = *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * (i + 1));
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) part[i & 1][j] = mfma(fa, j);
+      psc[i & 1] = sc;
+      if (i > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i - 1][j] += part[(i - 1) & 1][j] * psc[(i - 1) & 1];
+      }
+      if (i < 7) {
+        fa = fa_n;
+        sc = sa_n * sw;
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next m-block's LDS reads
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU (promotions)
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // the next combined scales
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[7][j] += part[1][j] * psc[1];
   }
   // every wave is done with the ring (its space is reused below)
   __syncthreads();
