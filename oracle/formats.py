@@ -21,6 +21,13 @@ to travel with the weights as one unit ("Running 35B MoE Models on 8GB GPUs",
 section "Technical Insight"); the exact format is the reading above. They also
 name 4-bit weights (MXFP4 and NVFP4, "guqiong96/Lvllm", section "Highlights"), of
 which MXFP4 is the one taken here.
+
+OCP MXFP8 (same specification): E4M3 elements sharing one E8M0 scale per 32
+consecutive values. It is the activation format taken where MXFP4 experts run on
+the block-scaled matrix instructions, which multiply two MX operands; the
+conversion follows the specification: the shared exponent is floor(log2 of the
+block's largest magnitude) minus 8 (the exponent of E4M3's largest normal), and
+each element is the nearest E4M3 value of v / 2^X, saturated at +-448.
 """
 from __future__ import annotations
 
@@ -169,3 +176,39 @@ def dequantize_mxfp4_weight(codes: np.ndarray, scales: np.ndarray) -> np.ndarray
         raise ValueError("dequantize_mxfp4_weight: the input dimension must be a multiple of 32")
     s = decode_e8m0(scales)
     return (v.reshape(n_in // MX_BLOCK, MX_BLOCK, n_out) * s[:, None, :]).reshape(n_in, n_out)
+
+
+# ------------------------------------------------------------------ MXFP8 --
+E4M3_EMAX = 8   # exponent of E4M3's largest normal: 448 = 1.75 * 2^8
+
+
+def mx_shared_exponent(amax: np.ndarray, emax: int) -> np.ndarray:
+    """Shared exponent X of MX blocks with largest magnitudes `amax`: floor(log2(amax)) - emax,
+    clamped to the E8M0 range [-127, 127]; -127 for an all-zero block. floor(log2) is read off
+    frexp, which is exact (amax = m 2^e with m in [0.5, 1) gives e - 1)."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(np.where(a > 0, a, 1.0))
+    X = np.where(a > 0, e.astype(np.int64) - 1 - emax, -127)
+    return np.clip(X, -127, 127)
+
+
+def quantize_rows_mxfp8(x: np.ndarray, block: int = MX_BLOCK):
+    """Rows -> MXFP8: per `block` consecutive values of a row the shared exponent X
+    (mx_shared_exponent with E4M3's emax 8) and the elements e4m3(v / 2^X), nearest even,
+    saturated at +-448 (v / 2^X is exact). Returns (uint8 codes [R, C], uint8 E8M0 exponents
+    X + 127 [R, C/block])."""
+    v = np.asarray(x, dtype=np.float64)
+    R, C = v.shape
+    if C % block:
+        raise ValueError("quantize_rows_mxfp8: columns must be a multiple of the block")
+    vb = v.reshape(R, C // block, block)
+    X = mx_shared_exponent(np.abs(vb).max(axis=2), E4M3_EMAX)
+    codes = encode_e4m3(np.ldexp(vb, -X[:, :, None]).reshape(R, C))
+    return codes, (X + 127).astype(np.uint8)
+
+
+def dequantize_rows_mxfp8(codes: np.ndarray, exps: np.ndarray, block: int = MX_BLOCK) -> np.ndarray:
+    """Inverse of quantize_rows_mxfp8 in float64: e4m3(code) * 2^(exp - 127)."""
+    v = decode_e4m3(codes)
+    R, C = v.shape
+    return (v.reshape(R, C // block, block) * decode_e8m0(exps)[:, :, None]).reshape(R, C)

@@ -197,17 +197,30 @@ def silu(z: np.ndarray) -> np.ndarray:
     return z * sigmoid(z)
 
 
+def quantize_activations(a: np.ndarray, mode) -> np.ndarray:
+    """The expert inputs as the GEMMs see them (float64): unchanged for mode False/None;
+    True or "e4m3": the per-row per-128 e4m3 quantisation with fp32 scales (the fp8
+    workload); "mxfp8": the OCP MXFP8 conversion (E4M3 with one power-of-two scale per 32), the
+    activations of MXFP4 experts on the block-scaled matrix instructions."""
+    if not mode:
+        return np.asarray(a, np.float64)
+    if mode is True or mode == "e4m3":
+        q, s = formats.quantize_rows_e4m3(a)
+        return formats.dequantize_rows(q, s)
+    if mode == "mxfp8":
+        q, e = formats.quantize_rows_mxfp8(a)
+        return formats.dequantize_rows_mxfp8(q, e)
+    raise ValueError(f"quantize_activations: unknown mode {mode!r}")
+
+
 def swiglu_ffn(a: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray,
-               quant_hidden: bool = False) -> np.ndarray:
+               quant_hidden=False) -> np.ndarray:
     """Y = (silu(A W_gate) * (A W_up)) W_down in float64. A [n, d], W_gate/W_up [d, F],
-    W_down [F, d]. With quant_hidden the hidden activations are passed through the
-    per-row per-128 e4m3 quantisation (fp8 workload) before the down projection."""
+    W_down [F, d]. With quant_hidden (a quantize_activations mode) the hidden activations
+    go through the same quantisation as the inputs before the down projection."""
     a = np.asarray(a, np.float64)
     h = silu(a @ w_gate) * (a @ w_up)
-    if quant_hidden:
-        q, s = formats.quantize_rows_e4m3(h)
-        h = formats.dequantize_rows(q, s)
-    return h @ w_down
+    return quantize_activations(h, quant_hidden) @ w_down
 
 
 # ---------------------------------------------------------------- layer ---
@@ -235,12 +248,13 @@ def combine(gate: np.ndarray, y_rows: np.ndarray, perm_dst: np.ndarray, shared_y
 
 
 def moe_layer(x: np.ndarray, routing: Routing, expert, n_experts: int, *, shared=None,
-              quant_act: bool = False, tokens=None) -> np.ndarray:
+              quant_act=False, tokens=None) -> np.ndarray:
     """Layer output [T', d] float64 for the tokens in `tokens` (all when None).
 
     `expert(e)` returns an ExpertWeights (float64). `shared` is an ExpertWeights or None.
-    With quant_act the expert inputs (x, and the hidden activations) go through the
-    per-row per-128 e4m3 quantisation of the fp8 workload. The routed part follows the
+    With quant_act (a quantize_activations mode: True/"e4m3" for the fp8 workload, "mxfp8"
+    for MXFP4 experts on the block-scaled matrix instructions) the expert inputs (x, and the
+    hidden activations) go through that quantisation. The routed part follows the
     grouped formulation: rows grouped by expert (stable), each expert run once on its
     rows, then the gate-weighted combine back to token order."""
     x = np.asarray(x, np.float64)
@@ -249,9 +263,7 @@ def moe_layer(x: np.ndarray, routing: Routing, expert, n_experts: int, *, shared
     idx = routing.idx[tokens]
     k = idx.shape[1]
     xa = x[tokens]
-    if quant_act:
-        q, s = formats.quantize_rows_e4m3(xa)
-        xa = formats.dequantize_rows(q, s)
+    xa = quantize_activations(xa, quant_act)
     offsets, perm_src, perm_dst = permutation(idx, n_experts)
     y_rows = np.zeros((idx.size, x.shape[1]), dtype=np.float64)
     for e in range(n_experts):

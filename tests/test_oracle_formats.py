@@ -203,3 +203,91 @@ def test_mxfp4_storage_decodes_within_the_rounding_bound():
     # all-zero block: scale 2^-127, codes 0
     c0, s0 = synth.quantize_mxfp4(np.zeros((32, 2), np.float32))
     assert (c0 == 0).all() and (s0 == 0).all()
+
+
+# ------------------------------------------------------------------ MXFP8 --
+
+def _mxfp8_points():
+    pts = []
+    for line in open(os.path.join(GOLDEN, "mxfp8_points.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        vals, exp, codes = [p.split(":", 1)[1].split() for p in line.split("|")]
+        pts.append(([float(v) for v in vals], int(exp[0], 16), [int(c, 16) for c in codes]))
+    return pts
+
+
+def test_mxfp8_worked_points():
+    """The hand-worked blocks of tests/golden/mxfp8_points.txt (OCP MX conversion)."""
+    pts = _mxfp8_points()
+    assert len(pts) >= 7
+    for vals, exp, codes in pts:
+        x = np.zeros((1, 32))
+        x[0, :len(vals)] = vals
+        q, e = formats.quantize_rows_mxfp8(x)
+        assert e.shape == (1, 1) and e[0, 0] == exp, (vals, e)
+        assert q[0, :len(codes)].tolist() == codes, (vals, [hex(c) for c in q[0, :len(codes)]])
+        assert np.all(q[0, len(vals):] == 0)
+
+
+def _all_finite_e4m3():
+    t = formats.e4m3_table()
+    ok = ~np.isnan(t)
+    return np.arange(256)[ok], t[ok]
+
+
+def test_mxfp8_elements_are_the_nearest_code_brute_force():
+    """Every element equals an exhaustive nearest search over the 254 finite codes of the
+    scaled value saturated at 448 (ties to the even code, the sign kept on zero)."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6, 96)) * np.ldexp(1.0, rng.integers(-12, 12, (6, 96)))
+    x[2, 32:64] *= 1e-30
+    q, e = formats.quantize_rows_mxfp8(x)
+    X = e.astype(np.int64) - 127
+    codes, vals = _all_finite_e4m3()
+    for r in range(6):
+        for c in range(96):
+            v = np.clip(x[r, c] * 2.0 ** -X[r, c // 32], -448, 448)
+            d = np.abs(vals - v)
+            best = codes[d == d.min()]
+            if len(best) > 1:   # a halfway case: the even mantissa, then the sign of the input
+                best = best[(best & 1) == 0]
+                if len(best) > 1:
+                    best = best[(best >= 128) == bool(np.signbit(v))]
+            assert q[r, c] == best[0], (r, c, x[r, c], hex(q[r, c]), [hex(b) for b in best])
+
+
+def test_mxfp8_shared_exponent_range_and_round_trip():
+    """X puts the block's largest magnitude in [256, 512) after scaling (so nothing but a value
+    in (448, 512) saturates), and values already of the form e4m3 * 2^X whose block holds a
+    code of the top binade come back with the same codes and exponents."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((4, 128)) * np.ldexp(1.0, rng.integers(-20, 20, (4, 1)))
+    q, e = formats.quantize_rows_mxfp8(x)
+    X = e.astype(np.int64) - 127
+    amax = np.abs(x.reshape(4, 4, 32)).max(axis=2)
+    scaled = amax * 2.0 ** -X
+    assert np.all((scaled >= 256) & (scaled < 512))
+    codes, vals = _all_finite_e4m3()
+    c = rng.choice(codes[np.abs(vals) < 256], size=(3, 64))
+    c[:, 0], c[:, 32] = 0x7A, 0xFC            # 320 and -384: the top binade sets X
+    ex = rng.integers(100, 150, (3, 2)).astype(np.uint8)
+    back_q, back_e = formats.quantize_rows_mxfp8(formats.dequantize_rows_mxfp8(c.astype(np.uint8), ex))
+    assert np.array_equal(back_e, ex)
+    nz = formats.decode_e4m3(c.astype(np.uint8)) != 0
+    assert np.array_equal(back_q[nz], c.astype(np.uint8)[nz])
+
+
+def test_mxfp8_elements_match_torch_e4m3_cast():
+    """Within range (|v / 2^X| <= 448) the elements equal torch's round-to-nearest-even
+    float8_e4m3fn cast of the exactly scaled values (an independent implementation)."""
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((8, 64)).astype(np.float32).astype(np.float64)
+    q, e = formats.quantize_rows_mxfp8(x)
+    X = e.astype(np.int64) - 127
+    scaled = x * 2.0 ** -np.repeat(X, 32, axis=1)
+    ok = np.abs(scaled) <= 448
+    ref = torch.from_numpy(scaled).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert ok.mean() > 0.9
+    assert np.array_equal(q[ok], ref[ok])

@@ -147,3 +147,30 @@ def test_quantised_layer_matches_explicit_dequantisation():
             h = moe.silu(xq[t:t + 1] @ w.w_gate) * (xq[t:t + 1] @ w.w_up)
             ref[t] += r.gate[t, j] * (tq(h) @ w.w_down)[0]
     np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_mxfp8_layer_matches_explicit_dequantisation():
+    """The MXFP4-prefill activations: the layer with quant_act="mxfp8" equals the brute-force
+    token loop on inputs and hidden activations quantised per 32 with a power-of-two scale,
+    written here with torch's e4m3 cast and the shared exponent from the float's exponent
+    field (frexp)."""
+    rng = np.random.default_rng(9)
+    x, w_r, ws = _rand_layer(rng, 6, 64, 4, 96)
+    r = moe.route(x, w_r, k=2)
+    got = moe.moe_layer(x, r, lambda e: ws[e], 4, quant_act="mxfp8")
+
+    def tq(a):
+        b = a.reshape(a.shape[0], -1, 32)
+        _, ex = np.frexp(np.abs(b).max(axis=2, keepdims=True))
+        s = np.ldexp(1.0, ex - 1 - 8)
+        q = torch.from_numpy(np.clip(b / s, -448, 448)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        return (q * s).reshape(a.shape)
+
+    xq = tq(x)
+    ref = np.zeros_like(x)
+    for t in range(6):
+        for j, e in enumerate(r.idx[t]):
+            w = ws[e]
+            h = moe.silu(xq[t:t + 1] @ w.w_gate) * (xq[t:t + 1] @ w.w_up)
+            ref[t] += r.gate[t, j] * (tq(h) @ w.w_down)[0]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
