@@ -35,10 +35,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; HBM TB/s (decode) & MFMA TFLOP/s (prefill) vs peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+# dense MFMA peaks; MXFP4 experts run E4M3 x E2M1 block-scaled MFMAs, priced at the fp8 rate
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "mxfp4": 5000.0, "f32": 157.3}
 PEAK_PCIE_GBS = 63.0   # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 encoding
 PEAK_HBM_GBS = 8000.0
-WORKLOADS = ["suite", "mixtral_prefill_bf16", "dsv3_prefill_fp8", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16",
+WORKLOADS = ["suite", "mixtral_prefill_bf16", "dsv3_prefill_fp8", "mixtral_prefill_mxfp4", "qwen_decode_bf16", "tiny_fp32", "offload_decode_bf16",
              "offload_decode_mxfp4"]
 
 
@@ -135,7 +136,8 @@ def cpu_baseline(cfg, w, sample_tokens, logit_bias=False):
         return moe.ExpertWeights(*[dec_w(m) for m in w["experts"][e]])
 
     shared = None if w.get("shared") is None else moe.ExpertWeights(*[dec_w(m) for m in w["shared"]])
-    moe.moe_layer(x, r, expert, cfg.E, shared=shared, quant_act=cfg.dtype == "fp8")
+    quant = "e4m3" if cfg.dtype == "fp8" else ("mxfp8" if cfg.dtype == "mxfp4" and cfg.T > 64 else None)
+    moe.moe_layer(x, r, expert, cfg.E, shared=shared, quant_act=quant)
     dt = time.perf_counter() - t0
     return {"value": round(sample_tokens / dt, 3), "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
             "kind": "oracle",
@@ -586,7 +588,8 @@ def bench_prefill(args, torch, B, synth, MoELayer, workload=None, steps=None, wa
     if gu_n:
         gu_avg_s = gu_ms / gu_n / 1e3
         achieved = float(gu_work) / gu_avg_s / 1e12
-        kname = "ffn_gemm_fp8<gate/up+SwiGLU+requant>" if dtype == "fp8" else "ffn_gemm_bf16<gate/up+SwiGLU>"
+        kname = {"fp8": "ffn_gemm_fp8<gate/up+SwiGLU+requant>", "mxfp4": "ffn_gemm_mx<gate/up+SwiGLU+MXFP8 requant>"}.get(
+            dtype, "ffn_gemm_bf16<gate/up+SwiGLU>")
         who = "routed experts and the shared expert" if folded else "routed experts"
         result["roofline"] = {"bound": "mfma", "kernel": kname,
                               "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
@@ -612,7 +615,7 @@ def bench_prefill(args, torch, B, synth, MoELayer, workload=None, steps=None, wa
     if cpu_sample is None and not args.no_cpu_baseline:
         # sized for roughly 10-30 s of oracle work: the fp8 oracle dequantises every touched
         # expert to float64, so its sample is a handful of tokens
-        cpu_sample = args.cpu_sample_tokens or (32 if cfg.dtype == "fp8" else 3 * cfg.T)
+        cpu_sample = args.cpu_sample_tokens or {"fp8": 32, "mxfp4": cfg.T}.get(cfg.dtype, 3 * cfg.T)
     if cpu_sample:
         log(f"[bench] cpu baseline: oracle on {cpu_sample} tokens")
         result["cpu_baseline"] = cpu_baseline(cfg, w, cpu_sample)

@@ -16,7 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoeffn.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = 0, 1, 2, 3, 4
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ECAPACITY, MOE_ENOMEM, MOE_ESTATE = 0, -1, -2, -3, -4, -5, -6
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EUNSUPPORTED", -3: "MOE_EHIP", -4: "MOE_ECAPACITY",
@@ -227,11 +227,16 @@ def permute(idx, E, *, x=None, out_dtype=None, gather=1, ws=None, out=None, stre
         rows = T * k if gather else T
         x_out = o.get("x_out")
         if x_out is None:
-            x_out = torch.empty(rows, d, device=dev, dtype=torch.uint8 if odt == MOE_FP8_E4M3 else x.dtype)
+            x_out = torch.empty(rows, d, device=dev,
+                                dtype=torch.uint8 if odt in (MOE_FP8_E4M3, MOE_MXFP8) else x.dtype)
         if odt == MOE_FP8_E4M3:
             xs = o.get("x_out_scale")
             if xs is None:
                 xs = torch.empty(rows, d // 128, device=dev, dtype=torch.float32)
+        elif odt == MOE_MXFP8:   # the E8M0 bytes, one per 32 values
+            xs = o.get("x_out_scale")
+            if xs is None:
+                xs = torch.empty(rows, d // 32, device=dev, dtype=torch.uint8)
     _check(lib().moe_permute(T, k, E, ptr(idx), ptr(offsets), ptr(src), ptr(dst), d, ptr(x), xdt, ptr(x_out), odt,
                              ptr(xs), int(gather), ptr(ws), ws.numel(), stream_ptr(stream)))
     return {"offsets": offsets, "perm_src": src, "perm_dst": dst, "x_out": x_out, "x_out_scale": xs}

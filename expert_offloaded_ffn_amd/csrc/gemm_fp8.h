@@ -63,31 +63,39 @@ struct Fp8Args {
   int32_t* counters;           // [8] per-XCD tile counters (zeroed by fp8_tile_map)
 };
 
-// Tile prefixes of the gate/up and the down GEMM for one or two problems (m-tiles of 256 rows
-// times the problem's n-tiles of 256 columns per expert), and zeroed tile counters.
-__global__ __launch_bounds__(1024) void fp8_tile_map(Fp8Args gu, int nt_dn0, int nt_dn1, int32_t* prefix_gu,
-                                                     int32_t* prefix_dn, int32_t* counters, int n_counters) {
+// Tile prefixes of the gate/up and the down GEMM of a launch of one or two grouped problems
+// (global expert g < E0 is problem 0's expert g, else problem 1's g - E0): per expert its
+// m-tiles of 256 rows times the problem's n-tiles of 256 columns, and zeroed tile counters.
+struct TileMapArgs {
+  const int32_t* offsets[2];
+  const int32_t* slot_of_expert[2];
+  int E0, n_exp;
+  int nt_gu[2], nt_dn[2];
+};
+
+__global__ __launch_bounds__(1024) void grouped_tile_map(TileMapArgs m, int32_t* prefix_gu, int32_t* prefix_dn,
+                                                         int32_t* counters, int n_counters) {
   __shared__ int32_t mt[2 * kMaxE + 2];
   const int tid = threadIdx.x;
   if (tid < n_counters) counters[tid] = 0;
-  for (int g = tid; g < gu.n_exp; g += blockDim.x) {
-    const Fp8Prob& p = g < gu.E0 ? gu.p[0] : gu.p[1];
-    const int e = g < gu.E0 ? g : g - gu.E0;
-    const int n = p.offsets[e + 1] - p.offsets[e];
-    mt[g] = (n > 0 && p.slot_of_expert[e] >= 0) ? (n + kQBM - 1) / kQBM : 0;
+  for (int g = tid; g < m.n_exp; g += blockDim.x) {
+    const int q = g < m.E0 ? 0 : 1;
+    const int e = g - (q ? m.E0 : 0);
+    const int n = m.offsets[q][e + 1] - m.offsets[q][e];
+    mt[g] = (n > 0 && m.slot_of_expert[q][e] >= 0) ? (n + kQBM - 1) / kQBM : 0;
   }
   __syncthreads();
   if (tid == 0) {
     int a = 0, b = 0;
-    for (int g = 0; g < gu.n_exp; ++g) {
-      const bool second = g >= gu.E0;
+    for (int g = 0; g < m.n_exp; ++g) {
+      const int q = g < m.E0 ? 0 : 1;
       prefix_gu[g] = a;
       prefix_dn[g] = b;
-      a += mt[g] * ((second ? gu.p[1].N : gu.p[0].N) / kQBN);
-      b += mt[g] * (second ? nt_dn1 : nt_dn0);
+      a += mt[g] * m.nt_gu[q];
+      b += mt[g] * m.nt_dn[q];
     }
-    prefix_gu[gu.n_exp] = a;
-    prefix_dn[gu.n_exp] = b;
+    prefix_gu[m.n_exp] = a;
+    prefix_dn[m.n_exp] = b;
   }
 }
 
@@ -396,19 +404,20 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
   }
 }
 
-// Tile L -> (problem, expert e, m-tile mt, n-tile nt). Tiles run expert by expert; within an
-// expert the m-tiles of one n-tile are adjacent, so the tiles that share a weight tile are
-// taken close together in time by the same XCD.
-__device__ __forceinline__ void fp8_tile_coords(const Fp8Args& a, int NT0, int NT1, int L, int& g, int& mt, int& nt) {
-  const int32_t* pre = a.tile_prefix;
-  int lo = 0, hi = a.n_exp - 1;   // last g with pre[g] <= L
+// Tile L -> (global expert g, m-tile mt, n-tile nt) from a tile prefix over n_exp experts
+// (problem 0's first, with NT0 n-tiles each, then problem 1's with NT1). Tiles run expert by
+// expert; within an expert the m-tiles of one n-tile are adjacent, so the tiles that share a
+// weight tile are taken close together in time by the same XCD.
+__device__ __forceinline__ void grouped_tile_coords(const int32_t* pre, int n_exp, int E0, int NT0, int NT1, int L,
+                                                    int& g, int& mt, int& nt) {
+  int lo = 0, hi = n_exp - 1;   // last g with pre[g] <= L
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (pre[mid] <= L) lo = mid;
     else hi = mid - 1;
   }
   g = lo;
-  const int NT = g < a.E0 ? NT0 : NT1;
+  const int NT = g < E0 ? NT0 : NT1;
   const int mte = (pre[g + 1] - pre[g]) / NT;
   const int local = L - pre[g];
   nt = local / mte;
@@ -430,7 +439,7 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_fp8(Fp8Args a) {
     const int L = __builtin_amdgcn_readfirstlane(s_tile);
     if (L < 0) return;
     int g, mt, nt;
-    fp8_tile_coords(a, NT0, NT1, L, g, mt, nt);
+    grouped_tile_coords(a.tile_prefix, a.n_exp, a.E0, NT0, NT1, L, g, mt, nt);
     const bool second = g >= a.E0;
     const Fp8Prob& p = second ? a.p[1] : a.p[0];
     const int e = __builtin_amdgcn_readfirstlane(second ? g - a.E0 : g);

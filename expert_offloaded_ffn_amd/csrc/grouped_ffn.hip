@@ -11,6 +11,7 @@
 //                 device, no host sync), the persistent tile queues, DMA helpers
 //  gemm_bf16.h    ffn_gemm_bf16, the bf16 prefill tile engine (gate/up + SwiGLU, down)
 //  gemm_fp8.h     ffn_gemm_fp8, the e4m3 prefill engine with fp32 block scales
+//  gemm_mx.h      ffn_gemm_mx, MXFP4 weights x MXFP8 activations on the block-scaled MFMA
 //  decode_bf16.h  ffn_decode_bf16, weight streaming for at most 64 rows per expert; one
 //                 launch can carry two problems (routed experts and the shared expert)
 //  this file      ffn_f32_* (fp32 VALU path, one thread per output element) and the host
@@ -23,6 +24,7 @@
 #include "ffn_common.h"
 #include "gemm_bf16.h"
 #include "gemm_fp8.h"
+#include "gemm_mx.h"
 #include "moe_internal.h"
 
 namespace moeffn {
@@ -115,15 +117,16 @@ constexpr int kFp8MapInts = 2 * (2 * kMaxE + 2) + 16;
 size_t ws_layout(const moe_expert_table* t, int rows, int act_dtype, size_t* h_off, size_t* map_off,
                  size_t* hs_off = nullptr, size_t* part_off = nullptr, size_t* arrived_off = nullptr,
                  size_t* as_off = nullptr) {
-  const size_t hsz = act_dtype == MOE_F32 ? 4 : act_dtype == MOE_FP8_E4M3 ? 1 : 2;
+  const size_t hsz = act_dtype == MOE_F32 ? 4 : (act_dtype == MOE_FP8_E4M3 || act_dtype == MOE_MXFP8) ? 1 : 2;
   *h_off = 0;
   size_t end = align_up((size_t)rows * t->d_ff * hsz, 256);
   if (hs_off) *hs_off = end;
   if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)(rows + 256) * (t->d_ff / 128) * 4, 256);
+  if (act_dtype == MOE_MXFP8) end += align_up((size_t)rows * (t->d_ff / 32), 256);   // H E8M0 bytes
   if (as_off) *as_off = end;
   if (act_dtype == MOE_FP8_E4M3) end += align_up((size_t)(rows + 256) * (t->d_model / 128) * 4, 256);
   *map_off = end;   // tile prefix [E+1], then the work counters [16]
-  if (act_dtype == MOE_FP8_E4M3) end = *map_off + align_up((size_t)kFp8MapInts * 4, 256);
+  if (act_dtype == MOE_FP8_E4M3 || act_dtype == MOE_MXFP8) end = *map_off + align_up((size_t)kFp8MapInts * 4, 256);
   else end = *map_off + align_up((size_t)(t->n_experts + 2) * 4, 256) + 256;
   const int S = decode_down_splits(t, rows);
   if (part_off) *part_off = end;
@@ -196,12 +199,20 @@ moe_status check_call(const FfnCall& c, const char* who) {
   const int d = t.d_model, F = t.d_ff;
   if (t.w_dtype == MOE_F32) {
     MOE_REQUIRE(act_dtype == MOE_F32, MOE_EUNSUPPORTED, "%s: fp32 weights need fp32 activations", who);
+  } else if (t.w_dtype == MOE_MXFP4 && act_dtype == MOE_MXFP8) {
+    // the block-scaled MFMA path (any rows per expert)
+    MOE_REQUIRE(c.a_scale != nullptr, MOE_EINVAL, "%s: MXFP8 activations need their E8M0 bytes (a_scale)", who);
+    MOE_REQUIRE((2 * F) % kQBN == 0 && d % kQBN == 0, MOE_EUNSUPPORTED,
+                "%s: MXFP4 prefill tiles need d and 2F multiples of %d", who, kQBN);
+    const long long a_rows = c.a_row_src ? (rows + c.a_row_div - 1) / c.a_row_div : rows;
+    MOE_REQUIRE(std::max(a_rows * d, (long long)rows * F) < (1ll << 32) && (long long)F * d < (1ll << 32),
+                MOE_EUNSUPPORTED, "%s: MXFP4 activations or weights larger than 4 GiB per matrix", who);
   } else if (t.w_dtype == MOE_MXFP4) {
-    MOE_REQUIRE(act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "%s: mxfp4 weights need bf16 activations", who);
+    MOE_REQUIRE(act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "%s: mxfp4 weights need bf16 or MXFP8 activations", who);
     const int max_rows_e = c.a_row_src ? (rows + c.a_row_div - 1) / c.a_row_div : rows;
     MOE_REQUIRE(max_rows_e <= 64, MOE_EUNSUPPORTED,
-                "%s: mxfp4 weights run on the decode kernels (at most 64 rows per expert, here up to %d)", who,
-                max_rows_e);
+                "%s: mxfp4 weights with bf16 activations run on the decode kernels (at most 64 rows per expert, "
+                "here up to %d; MXFP8 activations take the prefill path)", who, max_rows_e);
   } else if (t.w_dtype == MOE_BF16) {
     MOE_REQUIRE(act_dtype == MOE_BF16, MOE_EUNSUPPORTED, "%s: bf16 weights need bf16 activations", who);
     MOE_REQUIRE((2 * F) % kBN == 0 && d % kBN == 0, MOE_EUNSUPPORTED,
@@ -226,7 +237,7 @@ moe_status check_call(const FfnCall& c, const char* who) {
 // decode kernels (MXFP4 only those). Rows per expert are bounded by the number of distinct source rows: at most
 // rows / a_row_div tokens (each picks an expert once) or all rows.
 bool decode_path(const FfnCall& c) {
-  if ((c.t.w_dtype != MOE_BF16 && c.t.w_dtype != MOE_MXFP4) || c.rows == 0) return false;
+  if ((c.t.w_dtype != MOE_BF16 && c.t.w_dtype != MOE_MXFP4) || c.act_dtype == MOE_MXFP8 || c.rows == 0) return false;
   const int max_rows_e = c.a_row_src ? (c.rows + c.a_row_div - 1) / c.a_row_div : c.rows;
   return max_rows_e <= 64;
 }
@@ -426,8 +437,16 @@ moe_status run_fp8(const FfnCall* c, int n, hipStream_t s) {
   gu.E0 = dn.E0 = c[0].t.n_experts;
   gu.n_exp = dn.n_exp = c[0].t.n_experts + (n > 1 ? c[1].t.n_experts : 0);
   if (n == 1) gu.p[1] = gu.p[0], dn.p[1] = dn.p[0];
-  hipLaunchKernelGGL(fp8_tile_map, dim3(1), dim3(1024), 0, s, gu, dn.p[0].N / kQBN, dn.p[1].N / kQBN, prefix_gu,
-                     prefix_dn, counters, 16);
+  TileMapArgs m{};
+  for (int i = 0; i < 2; ++i) {
+    m.offsets[i] = gu.p[i].offsets;
+    m.slot_of_expert[i] = gu.p[i].slot_of_expert;
+    m.nt_gu[i] = gu.p[i].N / kQBN;
+    m.nt_dn[i] = dn.p[i].N / kQBN;
+  }
+  m.E0 = gu.E0;
+  m.n_exp = gu.n_exp;
+  hipLaunchKernelGGL(grouped_tile_map, dim3(1), dim3(1024), 0, s, m, prefix_gu, prefix_dn, counters, 16);
   gu.tile_prefix = prefix_gu;
   gu.counters = counters;
   dn.tile_prefix = prefix_dn;
@@ -443,6 +462,89 @@ moe_status run_fp8(const FfnCall* c, int n, hipStream_t s) {
   hipLaunchKernelGGL(ffn_gemm_fp8<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, dn);
   prof_mark(s, MOE_PROF_DOWN, true);
   return check_launch("moe_grouped_ffn fp8");
+}
+
+// One or two checked MXFP4 problems with MXFP8 activations in one gate/up launch and one down
+// launch of the block-scaled MFMA GEMM (tile map in the first problem's workspace).
+moe_status run_mx(const FfnCall* c, int n, hipStream_t s) {
+  MxArgs gu{}, dn{};
+  int32_t *prefix_gu = nullptr, *prefix_dn = nullptr, *counters = nullptr;
+  long long bound_gu = 0, bound_dn = 0;
+  for (int i = 0; i < n; ++i) {
+    const FfnCall& q = c[i];
+    const moe_expert_table& t = q.t;
+    size_t h_off, map_off, hs_off;
+    ws_layout(&t, q.rows, q.act_dtype, &h_off, &map_off, &hs_off);
+    const BundleGeom g = bundle_geom(t.d_model, t.d_ff, t.w_dtype);
+    const int d = t.d_model, F = t.d_ff;
+    uint8_t* Hq = reinterpret_cast<uint8_t*>(q.ws + h_off);
+    uint8_t* He = reinterpret_cast<uint8_t*>(q.ws + hs_off);
+    if (i == 0) {
+      prefix_gu = reinterpret_cast<int32_t*>(q.ws + map_off);
+      prefix_dn = prefix_gu + 2 * kMaxE + 2;
+      counters = prefix_dn + 2 * kMaxE + 2;
+    }
+    MxProb& a = gu.p[i];
+    a.a = static_cast<const uint8_t*>(q.a);
+    a.a_exp = reinterpret_cast<const uint8_t*>(q.a_scale);
+    a.a_row_src = q.a_row_src;
+    a.a_row_div = q.a_row_div;
+    a.offsets = q.offsets;
+    a.slot_of_expert = t.slot_of_expert;
+    a.pool = static_cast<const char*>(t.pool);
+    a.slot_stride = t.slot_stride;
+    a.b_off = g.gu_off;
+    a.bs_off = g.sg_off;
+    a.E = t.n_experts;
+    a.N = 2 * F;
+    a.K = d;
+    a.out = Hq;
+    a.out_exp = He;
+    a.out_dtype = MOE_MXFP8;
+    MxProb& b = dn.p[i];
+    b = a;
+    b.a = Hq;
+    b.a_exp = He;
+    b.a_row_src = nullptr;
+    b.a_row_div = 1;
+    b.b_off = g.dn_off;
+    b.bs_off = g.sd_off;
+    b.N = d;
+    b.K = F;
+    b.out = q.y;
+    b.out_exp = nullptr;
+    b.out_dtype = q.y_dtype;
+    const long long mt = q.rows / kQBM + std::min<long long>(t.n_experts, q.rows);
+    bound_gu += mt * (2 * F / kQBN);
+    bound_dn += mt * (d / kQBN);
+  }
+  gu.E0 = dn.E0 = c[0].t.n_experts;
+  gu.n_exp = dn.n_exp = c[0].t.n_experts + (n > 1 ? c[1].t.n_experts : 0);
+  if (n == 1) gu.p[1] = gu.p[0], dn.p[1] = dn.p[0];
+  TileMapArgs m{};
+  for (int i = 0; i < 2; ++i) {
+    m.offsets[i] = gu.p[i].offsets;
+    m.slot_of_expert[i] = gu.p[i].slot_of_expert;
+    m.nt_gu[i] = gu.p[i].N / kQBN;
+    m.nt_dn[i] = dn.p[i].N / kQBN;
+  }
+  m.E0 = gu.E0;
+  m.n_exp = gu.n_exp;
+  hipLaunchKernelGGL(grouped_tile_map, dim3(1), dim3(1024), 0, s, m, prefix_gu, prefix_dn, counters, 16);
+  gu.tile_prefix = prefix_gu;
+  gu.counters = counters;
+  dn.tile_prefix = prefix_dn;
+  dn.counters = counters + 8;
+  const long long n_cu = cu_count();
+  long long nblk = std::min(bound_gu, n_cu);
+  prof_mark(s, MOE_PROF_GATEUP, false);
+  hipLaunchKernelGGL(ffn_gemm_mx<MODE_GATEUP>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, gu);
+  prof_mark(s, MOE_PROF_GATEUP, true);
+  nblk = std::min(bound_dn, n_cu);
+  prof_mark(s, MOE_PROF_DOWN, false);
+  hipLaunchKernelGGL(ffn_gemm_mx<MODE_DOWN>, dim3((unsigned)((nblk + 7) / 8 * 8)), dim3(512), 0, s, dn);
+  prof_mark(s, MOE_PROF_DOWN, true);
+  return check_launch("moe_grouped_ffn mxfp4");
 }
 
 // Runs one checked problem on stream s.
@@ -472,6 +574,7 @@ moe_status run_call(const FfnCall& c, hipStream_t s) {
                        d, F, E);
     return check_launch("moe_grouped_ffn f32");
   }
+  if (t.w_dtype == MOE_MXFP4 && act_dtype == MOE_MXFP8) return run_mx(&c, 1, s);
   if (t.w_dtype == MOE_MXFP4) return launch_decode(&c, 1, s);   // (check_call admits decode problems only)
   if (t.w_dtype == MOE_BF16) {
     int32_t* tile_prefix = reinterpret_cast<int32_t*>(wsb + map_off);
@@ -583,6 +686,9 @@ extern "C" moe_status moe_grouped_ffn_batch(const moe_ffn_problem* problems, int
   if (n == 2 && c[0].t.w_dtype == MOE_FP8_E4M3 && c[1].t.w_dtype == MOE_FP8_E4M3 && c[0].rows > 0 && c[1].rows > 0 &&
       c[0].t.d_model == c[1].t.d_model)
     return run_fp8(c, 2, s);   // both problems in one launch per GEMM
+  if (n == 2 && c[0].t.w_dtype == MOE_MXFP4 && c[1].t.w_dtype == MOE_MXFP4 && c[0].act_dtype == MOE_MXFP8 &&
+      c[1].act_dtype == MOE_MXFP8 && c[0].rows > 0 && c[1].rows > 0 && c[0].t.d_model == c[1].t.d_model)
+    return run_mx(c, 2, s);
   for (int i = 0; i < n; ++i)
     if (moe_status st = run_call(c[i], s)) return st;
   return MOE_OK;

@@ -195,6 +195,50 @@ __global__ __launch_bounds__(256) void gather_rows_quant_e4m3(const TIn* __restr
   }
 }
 
+// OCP MXFP8 conversion, one wavefront per row; 4 lanes x 8 values cover a 32-value block:
+// shared exponent X = floor(log2 max|v|) - 8 (clamped to [-127, 127], -127 for a zero block),
+// codes e4m3_rne(clamp(v * 2^-X, +-448)) (the scaling is exact), E8M0 byte X + 127.
+template <typename TIn>
+__global__ __launch_bounds__(256) void gather_rows_quant_mxfp8(const TIn* __restrict__ x, uint8_t* __restrict__ out,
+                                                               uint8_t* __restrict__ out_exp,
+                                                               const int32_t* __restrict__ perm_src, int rows, int k,
+                                                               int d) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= rows) return;
+  const int src = perm_src ? perm_src[r] / k : r;
+  const TIn* xs = x + (size_t)src * d;
+  for (int c0 = 0; c0 < d; c0 += 512) {   // 16 blocks of 32 per step
+    const int col = c0 + lane * 8;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (col < d) {
+        if constexpr (sizeof(TIn) == 2) v[i] = bf16_to_f32(xs[col + i]);
+        else v[i] = xs[col + i];
+      } else {
+        v[i] = 0.f;
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int X = min(max(amax > 0.f ? ilogbf(amax) - 8 : -127, -127), 127);
+    if (col < d) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3_rne(fminf(fmaxf(ldexpf(v[i], -X), -448.0f), 448.0f)) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        hi |= f32_to_e4m3_rne(fminf(fmaxf(ldexpf(v[4 + i], -X), -448.0f), 448.0f)) << (8 * i);
+      *reinterpret_cast<uint2*>(out + (size_t)r * d + col) = make_uint2(lo, hi);
+      if ((lane & 3) == 0) out_exp[(size_t)r * (d / 32) + col / 32] = static_cast<uint8_t>(X + 127);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace moeffn
 
@@ -222,7 +266,7 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
   if (x_out != nullptr) {
     MOE_REQUIRE(x != nullptr && d > 0, MOE_EINVAL, "moe_permute: x_out needs x and d > 0");
     MOE_REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_permute: x_dtype %d unsupported", x_dtype);
-    MOE_REQUIRE(out_dtype == x_dtype || out_dtype == MOE_FP8_E4M3, MOE_EUNSUPPORTED,
+    MOE_REQUIRE(out_dtype == x_dtype || out_dtype == MOE_FP8_E4M3 || out_dtype == MOE_MXFP8, MOE_EUNSUPPORTED,
                 "moe_permute: conversion %d -> %d unsupported", x_dtype, out_dtype);
     MOE_REQUIRE(aligned(x, 16) && aligned(x_out, 16), MOE_EINVAL, "moe_permute: x and x_out must be 16-byte aligned");
     const int esz = x_dtype == MOE_F32 ? 4 : 2;
@@ -230,6 +274,10 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
     if (out_dtype == MOE_FP8_E4M3) {
       MOE_REQUIRE(d % 128 == 0 && x_out_scale != nullptr, MOE_EINVAL,
                   "moe_permute: e4m3 output needs d %% 128 == 0 and x_out_scale");
+    }
+    if (out_dtype == MOE_MXFP8) {
+      MOE_REQUIRE(d % 32 == 0 && x_out_scale != nullptr, MOE_EINVAL,
+                  "moe_permute: MXFP8 output needs d %% 32 == 0 and x_out_scale (the E8M0 bytes)");
     }
   }
   hipStream_t s = as_stream(stream);
@@ -267,6 +315,14 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
     const int esz = x_dtype == MOE_F32 ? 4 : 2;
     hipLaunchKernelGGL(gather_rows_copy, grid, dim3(256), 0, s, static_cast<const uint8_t*>(x),
                        static_cast<uint8_t*>(x_out), src, rows, k, d * esz);
+  } else if (out_dtype == MOE_MXFP8) {
+    uint8_t* ex = reinterpret_cast<uint8_t*>(x_out_scale);
+    if (x_dtype == MOE_BF16)
+      hipLaunchKernelGGL(gather_rows_quant_mxfp8<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
+                         static_cast<uint8_t*>(x_out), ex, src, rows, k, d);
+    else
+      hipLaunchKernelGGL(gather_rows_quant_mxfp8<float>, grid, dim3(256), 0, s, static_cast<const float*>(x),
+                         static_cast<uint8_t*>(x_out), ex, src, rows, k, d);
   } else if (x_dtype == MOE_BF16) {
     hipLaunchKernelGGL(gather_rows_quant_e4m3<bf16_t>, grid, dim3(256), 0, s, static_cast<const bf16_t*>(x),
                        static_cast<uint8_t*>(x_out), x_out_scale, src, rows, k, d);

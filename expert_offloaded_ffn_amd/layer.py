@@ -220,12 +220,19 @@ class MoELayer:
         return (self.shared is not None and self.cache is None and self.cache_dev is None
                 and self.w_code in (B.MOE_BF16, B.MOE_MXFP4) and 0 < T <= 64)
 
+    def mx_prefill(self, T: int) -> bool:
+        """Whether a T-token forward runs MXFP4 experts on the block-scaled MFMA (more than 64
+        tokens: activations and hidden activations in MXFP8) rather than on the decode kernels
+        (bf16 activations)."""
+        return self.w_code == B.MOE_MXFP4 and T > 64
+
     def shared_in_routed_launch(self, T: int) -> bool:
         """Whether a T-token forward runs the shared expert as one more group of the routed
-        experts' prefill GEMM launches (fp8 weights, every expert resident): one tile list for both,
-        so neither GEMM competes with the other from a second stream."""
-        return (self.shared is not None and self.cache is None and self.cache_dev is None
-                and self.w_code == B.MOE_FP8_E4M3 and T > 0)
+        experts' prefill GEMM launches (fp8 weights, or MXFP4 weights past the decode sizes; every
+        expert resident): one tile list for both, so neither GEMM competes with the other from a
+        second stream."""
+        return (self.shared is not None and self.cache is None and self.cache_dev is None and T > 0
+                and (self.w_code == B.MOE_FP8_E4M3 or self.mx_prefill(T)))
 
     def _shared_ffn(self, T, a, a_scale, a_code, ydt, main):
         """Launches the shared expert's FFN on the side stream once `a` is ready on `main`; the
@@ -263,13 +270,14 @@ class MoELayer:
         rows = T * k
         y = torch.empty(rows, d, device=self.device, dtype=torch.float32 if ydt == B.MOE_F32 else torch.bfloat16)
         a, a_scale, a_code = x, None, self.act_code
-        if self.w_code == B.MOE_FP8_E4M3:
+        if self.w_code == B.MOE_FP8_E4M3 or self.mx_prefill(T):
+            qcode = B.MOE_FP8_E4M3 if self.w_code == B.MOE_FP8_E4M3 else B.MOE_MXFP8
             r = B.route(x, self.w_router_t, logit_bias=logit_bias, select_bias=self.select_bias,
                         w_shared_gate=self.w_sg, stream=main, **self.route_args())
-            # grouping plus one e4m3 quantisation of every token (token order); the GEMMs
-            # gather rows through perm_src
-            p = B.permute(r["idx"], E, x=x, out_dtype=B.MOE_FP8_E4M3, gather=0, ws=ws, stream=main)
-            a, a_scale, a_code = p["x_out"], p["x_out_scale"], B.MOE_FP8_E4M3
+            # grouping plus one quantisation of every token (token order: e4m3 per 128 for fp8
+            # weights, MXFP8 for MXFP4 weights); the GEMMs gather rows through perm_src
+            p = B.permute(r["idx"], E, x=x, out_dtype=qcode, gather=0, ws=ws, stream=main)
+            a, a_scale, a_code = p["x_out"], p["x_out_scale"], qcode
             if self.shared is not None and not self.shared_in_routed_launch(T):
                 shared_y = self._shared_ffn(T, a, a_scale, a_code, ydt, main)
         else:

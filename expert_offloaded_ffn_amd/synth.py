@@ -24,6 +24,9 @@ Mixtral, Qwen-MoE and DeepSeek-family models without fixing their shapes):
                            T=32 tokens per step for 256 steps; router logits
                            biased by a Zipf(1.1) log-prior over a seed-permuted
                            expert order that is re-drawn every 64 steps.
+* ``mixtral_prefill_mxfp4`` the Mixtral-shaped prefill layer with MXFP4 expert
+                           weights (the experts' fp32 draws converted to MXFP4);
+                           activations reach the experts as MXFP8.
 * ``offload_decode_mxfp4`` the same layer and stream with MXFP4 expert weights
                            (FP4 E2M1 codes, one E8M0 scale per 32 inputs of an
                            output column), bf16 router and activations.
@@ -101,6 +104,8 @@ CONFIGS = {
     "offload_decode_bf16": LayerConfig("offload_decode_bf16", T=32, d=4096, E=128, k=8, F=1536,
                                        dtype="bf16", score_fn="softmax", seed=5, n_slots=32,
                                        steps=256, zipf_alpha=1.1, zipf_epoch=64),
+    "mixtral_prefill_mxfp4": LayerConfig("mixtral_prefill_mxfp4", T=4096, d=4096, E=8, k=2, F=14336,
+                                         dtype="mxfp4", score_fn="softmax", seed=2),
     "offload_decode_mxfp4": LayerConfig("offload_decode_mxfp4", T=32, d=4096, E=128, k=8, F=1536,
                                         dtype="mxfp4", score_fn="softmax", seed=5, n_slots=32,
                                         steps=256, zipf_alpha=1.1, zipf_epoch=64),

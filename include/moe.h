@@ -65,8 +65,11 @@ enum {
  * MOE_MXFP4 (expert weights only) is OCP MXFP4: FP4 E2M1 codes (bias 1, values
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) with one E8M0 scale 2^(e-127)
  * per 32 consecutive inputs of an output column ([LVLLM] "Highlights" names
- * MXFP4 among the expert formats to carry). */
-enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 };
+ * MXFP4 among the expert formats to carry).
+ * MOE_MXFP8 (activations only) is OCP MXFP8: E4M3 codes with one E8M0 scale
+ * 2^(e-127) per 32 consecutive values of a row, stored as uint8 bytes; it is the
+ * A operand of MXFP4 experts on the block-scaled matrix instructions. */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3, MOE_MXFP8 = 4 };
 enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 };
 
 /* Human-readable message for the last failing call on this thread ("" if none). */
@@ -139,7 +142,12 @@ moe_status moe_route(const moe_route_cfg* cfg, const void* x, const void* w_rout
  *  cvt is a copy when out_dtype == x_dtype, or the per-row per-128-column e4m3
  *  quantisation when out_dtype == MOE_FP8_E4M3: a = max|v| over the 128-block,
  *  scale = a / 448 (1 if a == 0) in IEEE fp32, code = e4m3_rne(clamp(v/scale,
- *  +-448)); x_out_scale [rows, d/128] fp32 receives the scales.
+ *  +-448)); x_out_scale [rows, d/128] fp32 receives the scales;
+ *  or the OCP MXFP8 conversion when out_dtype == MOE_MXFP8: per 32 consecutive
+ *  values the shared exponent X = floor(log2 max|v|) - 8 clamped to
+ *  [-127, 127] (-127 for a zero block), code = e4m3_rne(clamp(v * 2^-X, +-448)),
+ *  and x_out_scale (read as uint8 [rows, d/32], so d % 32 == 0) receives the
+ *  E8M0 bytes X + 127.
  * Workspace: moe_permute_workspace_size(T, k, E) bytes at `ws` (256-B aligned).
  * Errors: MOE_EINVAL on bad sizes/null pointers, MOE_ECAPACITY if ws_bytes is
  *  short, MOE_EUNSUPPORTED for an unsupported conversion. Indices outside
@@ -248,10 +256,15 @@ moe_status moe_pack_expert(int32_t d_model, int32_t d_ff, int32_t w_dtype,
  *   y_r = H_r W_down_e                          (fp32 accumulation, y_dtype)
  * Rows of skipped experts are left untouched in y.
  *  a        [*, d] act_dtype: MOE_F32 (f32 weights), MOE_BF16 (bf16 or MXFP4
- *           weights) or MOE_FP8_E4M3 codes (fp8 weights) with a_scale [*, d/128]
- *           fp32. MXFP4 weights are decoded exactly to bf16 (E2M1 times a power of
- *           two) for bf16 MFMAs; they run at most 64 rows per expert (decode
- *           batches; more is MOE_EUNSUPPORTED).
+ *           weights), MOE_FP8_E4M3 codes (fp8 weights) with a_scale [*, d/128]
+ *           fp32, or MOE_MXFP8 codes (MXFP4 weights) with a_scale pointing at
+ *           the uint8 E8M0 bytes [*, d/32].
+ *           MXFP4 weights with bf16 activations are decoded exactly to bf16
+ *           (E2M1 times a power of two) for bf16 MFMAs and run at most 64 rows
+ *           per expert (decode batches; more is MOE_EUNSUPPORTED). With MXFP8
+ *           activations they run on the block-scaled MFMA (E4M3 x E2M1, both
+ *           E8M0 scales applied by the instruction), any number of rows; H is
+ *           then re-quantised to MXFP8 (per row per 32) before the down GEMM.
  *  offsets  device [n_experts + 1] int32 (from moe_permute, or [0, rows] for a
  *           single dense expert such as a shared expert)
  *  y        [rows, d] y_dtype (MOE_F32 or MOE_BF16)
@@ -276,8 +289,10 @@ moe_status moe_grouped_ffn(const moe_expert_table* table, int32_t rows, const in
  * experts sit outside the routed set): when both problems are bf16 with at most
  * 64 rows per expert (a decode step), they share one gate/up launch and one down
  * launch, with the first problem's work dispatched first, instead of running
- * on two streams that a graph must fork and join. Otherwise the problems run one
- * after the other on `stream`. n must be 1 or 2.
+ * on two streams that a graph must fork and join. Two fp8 problems (or two
+ * MXFP4 problems with MXFP8 activations) of the same d_model likewise share one
+ * launch per GEMM: the second is one more group of the first's tile list.
+ * Otherwise the problems run one after the other on `stream`. n must be 1 or 2.
  * Workspace: moe_grouped_ffn_batch_workspace_size(problems, n) bytes at `ws`
  * (256-B aligned): each problem's moe_grouped_ffn workspace, in order, each
  * rounded up to a multiple of 256 B.

@@ -124,3 +124,113 @@ def test_mxfp4_fused_combine_bit_equal():
     torch.cuda.synchronize()
     say("    done")
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+# ------------------------------------------------ prefill: block-scaled MFMA --
+# More than 64 tokens: activations and hidden activations in MXFP8 (E4M3 with a power-of-two
+# scale per 32, the OCP MX conversion), MXFP4 weights on v_mfma_scale_f32_16x16x128_f8f6f4.
+
+def test_permute_mxfp8_quantisation_bit_exact():
+    """moe_permute's MXFP8 output (token order and gathered) equals the oracle's OCP MX
+    conversion code for code and exponent for exponent."""
+    from oracle import formats
+    cfg = synth.get_config("offload_decode_mxfp4", T=200, d=512, E=16, k=4)
+    rng = np.random.default_rng(3)
+    idx = np.stack([rng.choice(cfg.E, cfg.k, replace=False) for _ in range(cfg.T)]).astype(np.int32)
+    xs = synth.gen_x(cfg, 0)
+    xs[7, 32:64] = 0          # an all-zero block
+    x = _x(cfg, xs)
+    say("  case permute mxfp8: launching")
+    tok = B.permute(torch.from_numpy(idx).to(DEV), cfg.E, x=x, out_dtype=B.MOE_MXFP8, gather=0)
+    gat = B.permute(torch.from_numpy(idx).to(DEV), cfg.E, x=x, out_dtype=B.MOE_MXFP8, gather=1)
+    torch.cuda.synchronize()
+    codes, exps = formats.quantize_rows_mxfp8(decode(xs, "bf16"))
+    assert np.array_equal(to_np(tok["x_out"]), codes)
+    assert np.array_equal(to_np(tok["x_out_scale"]), exps)
+    src = to_np(gat["perm_src"]) // cfg.k
+    assert np.array_equal(to_np(gat["x_out"]), codes[src])
+    assert np.array_equal(to_np(gat["x_out_scale"]), exps[src])
+    assert exps[7, 1] == 0
+
+
+def _check_prefill(cfg, layer, router, experts, T, xi, shared=None, w_sg=None, tokens=None):
+    xs = synth.gen_x(cfg, xi, T=T)
+    say(f"  case {cfg.name} T={T} x={xi} (MXFP4 prefill): launching")
+    g = layer.forward(_x(cfg, xs))
+    torch.cuda.synchronize()
+    say("    done")
+    check_exact_indices(cfg, g["route"], g["perm"], T)
+    r_ref = oracle_route(cfg, xs, router, w_sg)
+    same = route_agreement(cfg, r_ref, g["route"], key_tol=1e-4)
+    toks = np.arange(T) if tokens is None else np.asarray(tokens)
+    toks = toks[same[toks]]
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache.clear()
+            cache[e] = oracle_expert(cfg, experts[e])
+        return cache[e]
+
+    ref = moe.moe_layer(decode(xs, "bf16"), r_ref, expert, cfg.E, quant_act="mxfp8", tokens=toks,
+                        shared=None if shared is None else oracle_expert(cfg, shared))
+    assert_close(to_np(g["out"])[toks], ref, "bf16", f"{cfg.name} T={T}")
+    return g
+
+
+@pytest.mark.parametrize("T,d,E,k,F", [(65, 256, 8, 2, 128), (300, 512, 8, 2, 512), (600, 256, 16, 4, 768),
+                                       (100, 512, 32, 8, 256)])
+def test_mxfp4_prefill_layer_reduced(T, d, E, k, F):
+    cfg = synth.get_config("offload_decode_mxfp4", T=T, d=d, E=E, k=k, F=F, name=f"mxfp4p_T{T}_d{d}_E{E}_k{k}_F{F}")
+    router, experts = synth.gen_router(cfg), synth.gen_experts(cfg)
+    layer = MoELayer(cfg, router=router, experts=experts, device=DEV)
+    assert layer.mx_prefill(T)
+    _check_prefill(cfg, layer, router, experts, T, 0)
+
+
+def test_mxfp4_prefill_many_tiles_every_row():
+    """512 gate/up tiles (16 experts x 2 m-tiles x 16 n-tiles), more than the persistent grid,
+    so blocks run several tiles through the 3-stage ring; every row checked."""
+    cfg = synth.get_config("offload_decode_mxfp4", T=2048, d=512, E=16, k=4, F=2048, name="mxfp4p_many_tiles")
+    router, experts = synth.gen_router(cfg), synth.gen_experts(cfg)
+    layer = MoELayer(cfg, router=router, experts=experts, device=DEV)
+    g = _check_prefill(cfg, layer, router, experts, cfg.T, 1)
+    assert to_np(g["route"]["counts"]).max() > 256
+
+
+def test_mxfp4_prefill_offload_shape():
+    """The offload workload's experts (d=4096, E=128 top-8, F=1536) at 512 tokens, resident."""
+    cfg = synth.get_config("offload_decode_mxfp4", T=512)
+    router, experts = synth.gen_router(cfg), synth.gen_experts(cfg, threads=16)
+    layer = MoELayer(cfg, router=router, experts=experts, device=DEV)
+    rng = np.random.default_rng(4)
+    _check_prefill(cfg, layer, router, experts, cfg.T, 2, tokens=np.sort(rng.choice(cfg.T, 96, replace=False)))
+
+
+def test_mxfp4_prefill_with_folded_shared_expert():
+    """A Qwen1.5-MoE-shaped layer with MXFP4 weights at 160 tokens: the shared expert is one more
+    group of the routed experts' block-scaled launches; against the oracle (sigmoid shared gate)."""
+    cfg = synth.get_config("qwen_decode_bf16", dtype="mxfp4", T=160, name="qwen_mxfp4_prefill")
+    router, experts, shared = synth.gen_router(cfg), synth.gen_experts(cfg), synth.gen_shared(cfg)
+    w_sg = synth.gen_shared_gate(cfg)
+    layer = MoELayer(cfg, router=router, experts=experts, shared=shared, w_shared_gate=w_sg, device=DEV)
+    assert layer.shared_in_routed_launch(cfg.T)
+    _check_prefill(cfg, layer, router, experts, cfg.T, 3, shared=shared, w_sg=w_sg)
+
+
+def test_mxfp4_prefill_slot_pool_matches_resident():
+    """The slot pool (8 of 32 experts) running MXFP4 prefill steps in waves gives the resident
+    layer's output bit for bit."""
+    cfg = synth.get_config("offload_decode_mxfp4", d=512, F=256, E=32, k=4, T=96, n_slots=8)
+    router, experts = synth.gen_router(cfg), synth.gen_experts(cfg)
+    res = MoELayer(cfg, router=router, experts=experts, device=DEV)
+    pool = MoELayer(cfg, router=router, experts=experts, device=DEV, pool_slots=8)
+    for step in range(3):
+        x = _x(cfg, synth.gen_x(cfg, step))
+        say(f"  case mxfp4 prefill slot pool step {step}: launching")
+        a = res.forward(x)["out"]
+        g = pool.forward(x)
+        torch.cuda.synchronize()
+        assert g["waves"] >= 2
+        assert torch.equal(a.view(torch.int16), g["out"].view(torch.int16))
+    pool.cache.close()
