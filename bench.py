@@ -396,7 +396,7 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
              shared=synth.gen_shared(cfg) if cfg.F_shared else None,
              w_sg=synth.gen_shared_gate(cfg) if cfg.shared_gate else None)
     layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
-                     threads=16, fuse_combine=not args.no_fuse_combine)
+                     threads=16, fuse_combine=not args.no_fuse_combine, fused_step=not args.separate_calls)
     nb = max(args.batches, 64)
     xs = [_x_dev(cfg, synth.gen_x(cfg, 1 + i), torch) for i in range(nb)]
     flush = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda")
@@ -451,12 +451,25 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
         B.profile_enable(False)
     del flush, flush_words
     step_bytes = np.array([touched[i % nb] * bundle + shared_bytes + act for i in range(steps)], np.float64)
-    # the decode gate/up launch streams the touched routed experts' W_gu, and the shared
-    # expert's when the layer runs it inside the same launch
+    # The launch timed as the roofline kernel streams the touched routed experts' W_gu. In the
+    # fused step (moe_decode_step) it also streams the shared expert's W_dn (the shared gate/up
+    # ran beside the routing); in the separate calls it carries the shared expert's W_gu when
+    # the layer runs the shared expert inside the routed launches.
+    fused = layer.fused_decode_step(cfg.T)
     merged = layer.shared_in_decode_launch(cfg.T)
     wbytes = 0.5 + 1 / 32 if cfg.dtype == "mxfp4" else 2.0   # bytes per weight (codes and scales)
-    shared_gu = 2 * cfg.F_shared * cfg.d * wbytes if merged else 0
-    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * wbytes + shared_gu for i in range(steps))
+    if fused:
+        shared_w = cfg.F_shared * cfg.d * wbytes
+        who = "routed gate/up + shared down" if cfg.F_shared else "routed gate/up"
+        kname = "ffn_decode_down_gateup" if cfg.F_shared else "ffn_decode_bf16<gate/up+SwiGLU>"
+        work = ("gate/up weight bytes of the touched routed experts + the shared expert's down weight bytes"
+                if cfg.F_shared else "gate/up weight bytes of the touched routed experts")
+    else:
+        shared_w = 2 * cfg.F_shared * cfg.d * wbytes if merged else 0
+        who = "routed experts + shared expert" if merged else "routed experts"
+        kname = "ffn_decode_bf16<gate/up+SwiGLU>"
+        work = f"gate/up weight bytes of the touched {who}"
+    gu_bytes = sum(touched[i % nb] * 2 * cfg.F * cfg.d * wbytes + shared_w for i in range(steps))
     gu_ms, gu_n = prof[B.PROF_DEC_GATEUP]
     hbm = float(step_bytes.sum() / (ms.sum() / 1e3) / 1e9)
     hbm_med = float(np.median(step_bytes) / (np.median(ms) / 1e3) / 1e9)
@@ -467,9 +480,9 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(fan_in)) weights)",
         "config": {"workload": cfg.name, "T": cfg.T, "d_model": cfg.d, "n_experts": cfg.E, "top_k": cfg.k,
                    "d_ff": cfg.F, "d_ff_shared": cfg.F_shared, "mall_flush_MiB": 512, "mall_flush": args.mall_flush,
-                   "hip_graph": bool(use_graph),
-                   "combine_in_down_launch": bool(layer.fuse_combine and layer.shared_in_decode_launch(cfg.T)
-                                                  and cfg.T <= FUSE_COMBINE_MAX_T)},
+                   "hip_graph": bool(use_graph), "fused_step": bool(fused),
+                   "combine_in_down_launch": bool(cfg.T <= FUSE_COMBINE_MAX_T and
+                                                  (fused or (layer.fuse_combine and merged)))},
         "step_ms_p10_p50_p90": percentiles(ms),
         "touched_experts_mean": round(float(np.mean([touched[i % nb] for i in range(steps)])), 2),
         "layer_hbm": {"achieved": round(hbm, 1), "achieved_at_median_step": round(hbm_med, 1), "peak": PEAK_HBM_GBS,
@@ -478,12 +491,11 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
     }
     if gu_n:
         a = gu_bytes / (gu_ms / 1e3) / 1e9
-        who = "routed experts + shared expert" if merged else "routed experts"
-        result["roofline"] = {"bound": "hbm", "kernel": f"ffn_decode_bf16<gate/up+SwiGLU> ({who})",
+        result["roofline"] = {"bound": "hbm", "kernel": f"{kname} ({who})",
                               "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
-                              "work_per_launch": f"gate/up weight bytes of the touched {who}",
+                              "work_per_launch": work,
                               "timed": "eager launches of the same steps" if graph is not None else "the timed steps"}
     if graph is not None:
         del graph
@@ -659,6 +671,9 @@ def main():
                          "from HBM each step) instead of the slot pool")
     ap.add_argument("--no-fuse-combine", action="store_true",
                     help="decode: run the combine as its own launch instead of inside the down launch")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="decode: the separate calls (route_permute, the batched FFN, the combine) instead of "
+                         "moe_decode_step")
     ap.add_argument("--skew-zipf", type=float, default=0.0,
                     help="prefill: add a Zipf(alpha) log-prior to the routing logits (0 = unskewed)")
     ap.add_argument("--mall-flush", choices=["read", "write"], default="read",

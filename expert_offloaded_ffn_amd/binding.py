@@ -58,6 +58,13 @@ class CombineArgs(ctypes.Structure):
                 ("out_dtype", ctypes.c_int32)]
 
 
+class DecodeOut(ctypes.Structure):
+    _fields_ = [("shared_gate", ctypes.c_void_p), ("scores", ctypes.c_void_p), ("topk_idx", ctypes.c_void_p),
+                ("topk_gate", ctypes.c_void_p), ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p),
+                ("perm_src", ctypes.c_void_p), ("perm_dst", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("out_dtype", ctypes.c_int32)]
+
+
 class CacheCfg(ctypes.Structure):
     _fields_ = [("n_experts", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("bundle_bytes", ctypes.c_int64),
                 ("slot_stride", ctypes.c_int64), ("bundles_host", ctypes.c_void_p), ("pool", ctypes.c_void_p),
@@ -110,6 +117,11 @@ EXPORTS = {
                                 ctypes.POINTER(CombineArgs), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "moe_grouped_ffn_combine_noalloc": (ctypes.c_int32, [ctypes.POINTER(FfnProblem), ctypes.POINTER(FfnProblem),
                                         ctypes.POINTER(CombineArgs), ctypes.c_void_p]),
+    "moe_decode_step_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(RouteCfg), ctypes.POINTER(ExpertTable),
+                                       ctypes.POINTER(ExpertTable)]),
+    "moe_decode_step": (ctypes.c_int32, [ctypes.POINTER(RouteCfg)] + [ctypes.c_void_p] * 5 +
+                        [ctypes.POINTER(ExpertTable), ctypes.POINTER(ExpertTable), ctypes.POINTER(DecodeOut),
+                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "expert_slot_cache_create": (ctypes.c_int32, [ctypes.POINTER(CacheCfg), ctypes.POINTER(ctypes.c_void_p)]),
     "expert_slot_cache_destroy": (ctypes.c_int32, [ctypes.c_void_p]),
     "expert_slot_cache_reset": (ctypes.c_int32, [ctypes.c_void_p]),
@@ -396,6 +408,49 @@ def grouped_ffn_combine_noalloc(routed: FfnProblem, shared, perm_dst, gate, out,
                                                  ctypes.byref(shared) if shared is not None else None,
                                                  ctypes.byref(cb), stream_ptr(stream)))
     return out
+
+
+def decode_step_workspace_size(T, d, E, k, routed: ExpertTable, shared=None) -> int:
+    cfg = RouteCfg(T, d, E, k, MOE_SOFTMAX, 1, 1.0, 1, 1, 0, MOE_BF16)
+    return int(lib().moe_decode_step_workspace_size(ctypes.byref(cfg), ctypes.byref(routed),
+                                                    ctypes.byref(shared) if shared is not None else None))
+
+
+def decode_step(x, w_router_t, routed: ExpertTable, shared=None, *, k, score_fn=MOE_SOFTMAX, renormalize=1,
+                route_scale=1.0, n_groups=1, topk_groups=1, group_topn=0, logit_bias=None, select_bias=None,
+                w_shared_gate=None, out_dtype=MOE_BF16, ws=None, out=None, stream=None):
+    """moe_decode_step: routing, the routed and shared experts' FFN and the combine of one decode
+    step. `ws` must have been zero-filled before its first use (the call leaves its counters at
+    zero); a new one is allocated zero-filled when None. Returns route_permute()'s dict plus "out"."""
+    T, d = x.shape
+    E = w_router_t.shape[0]
+    dev = x.device
+    o = out or {}
+
+    def get(name, shape, dtype):
+        t = o.get(name)
+        return t if t is not None else torch.empty(*shape, device=dev, dtype=dtype)
+
+    res = {"scores": get("scores", (T, E), torch.float32), "idx": get("idx", (T, k), torch.int32),
+           "gate": get("gate", (T, k), torch.float32), "counts": get("counts", (E,), torch.int32),
+           "shared_gate": get("shared_gate", (T,), torch.float32) if w_shared_gate is not None else None,
+           "offsets": get("offsets", (E + 1,), torch.int32), "perm_src": get("perm_src", (T * k,), torch.int32),
+           "perm_dst": get("perm_dst", (T * k,), torch.int32),
+           "out": get("out", (T, d), torch.bfloat16 if out_dtype == MOE_BF16 else torch.float32)}
+    cfg = RouteCfg(T, d, E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn,
+                   DTYPE_CODE[x.dtype])
+    if ws is None:
+        need = lib().moe_decode_step_workspace_size(ctypes.byref(cfg), ctypes.byref(routed),
+                                                    ctypes.byref(shared) if shared is not None else None)
+        ws = torch.zeros(max(int(need), 256), device=dev, dtype=torch.uint8)
+    do = DecodeOut(ptr(res["shared_gate"]), ptr(res["scores"]), ptr(res["idx"]), ptr(res["gate"]), ptr(res["counts"]),
+                   ptr(res["offsets"]), ptr(res["perm_src"]), ptr(res["perm_dst"]), ptr(res["out"]), out_dtype)
+    _check(lib().moe_decode_step(ctypes.byref(cfg), ptr(x), ptr(w_router_t), ptr(logit_bias), ptr(select_bias),
+                                 ptr(w_shared_gate), ctypes.byref(routed),
+                                 ctypes.byref(shared) if shared is not None else None, ctypes.byref(do), ptr(ws),
+                                 ws.numel(), stream_ptr(stream)))
+    res.update(x_out=None, x_out_scale=None)
+    return res
 
 
 # ---------------------------------------------------------- slot cache ---

@@ -97,10 +97,12 @@ struct DecodeCombine {
   int nprob;                 // problems in the launch (units of both count)
 };
 
-// Number of experts that have rows and a slot (the units of one 32-column group).
+// Number of experts that have rows and a slot (the units of one 32-column group); offsets
+// NULL is one group (see decode_block).
 __device__ __forceinline__ int count_active_experts(const int32_t* __restrict__ offsets,
                                                     const int32_t* __restrict__ slot_of_expert, int E) {
   const int lane = threadIdx.x & 63;
+  if (offsets == nullptr) return slot_of_expert[0] >= 0 ? 1 : 0;
   int n = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
@@ -205,27 +207,33 @@ constexpr int kDecChunk = MOEFFN_DEC_CHUNK;   // k-tiles whose loads are issued 
 constexpr int kDecWaves = MOEFFN_DEC_WAVES;   // waves per workgroup (split-K)
 constexpr int kDecMaxSplits = 8;              // workgroups per (expert, group) of a split down GEMM
 
-// Blocks [0, nb0) work on problem p0, the rest on p1 (two independent grouped FFNs, e.g.
-// the routed experts and the shared expert, in one launch). SPLIT launches carry a down
-// projection split over K (and, for GATEUP, clear its arrival counts); the others compile
-// without that code.
+// One decode workgroup's LDS.
+template <int MB>
+struct DecodeLds {
+  f32x4_t red[kDecWaves - 1][MB][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
+  int s_last;                              // split K: this workgroup arrived last
+  int s_glast;                             // COMB: last unit of its column group
+};
+
+// Workgroup bid of a decode launch of problem p (p0 and p1 are the launch's problems, which
+// the folded combine counts units of). SPLIT launches carry a down projection split over K;
+// the others compile without that code.
 // MB is the number of 16-row m-blocks a pass covers: 1 for decode batches (a quarter of the
 // accumulators and of the reduction LDS of 4, so more workgroups and more loads in flight fit
 // on a CU; an expert with more rows takes several passes, a one-expert problem several
 // workgroups, see rchunks), 4 for larger ones.
-// COMB (DOWN only) folds the combine into the launch (DecodeCombine). WF is the weight
+// YF32 (DOWN only) stores the outputs as the fp32 values of their y-dtype rounding with
+// device-scope stores, for a combine that reads them in the same launch or the next one;
+// COMB (needs YF32) folds that combine into the launch (DecodeCombine). WF is the weight
 // format: 0 bf16 tiles, 1 MXFP4 chunks (codes and scales of 4 k-steps per load, decoded to
 // bf16 in registers; the waves split K in whole chunks).
-template <int MODE, bool SPLIT, int MB, bool COMB = false, int WF = 0>
-__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
-    DecodeArgs p0, DecodeArgs p1, int nb0, DecodeCombine cb) {
+template <int MODE, bool SPLIT, int MB, bool YF32, bool COMB, int WF>
+__device__ __forceinline__ void decode_block(const DecodeArgs& p, int bid, const DecodeArgs& p0,
+                                             const DecodeArgs& p1, const DecodeCombine& cb, DecodeLds<MB>& L) {
   static_assert(!COMB || MODE == MODE_DOWN, "the combine follows the down projection");
-  __shared__ f32x4_t red[kDecWaves - 1][MB][2][64];   // partials of waves 1..: [wave][m-block][n-tile][lane]
-  __shared__ int s_last;                               // split K: this workgroup arrived last
-  __shared__ int s_glast;                              // COMB: last unit of its column group
-  const bool second = (int)blockIdx.x >= nb0;
-  const DecodeArgs p = second ? p1 : p0;
-  const int bid = second ? (int)blockIdx.x - nb0 : (int)blockIdx.x;
+  static_assert(!COMB || YF32, "the folded combine reads fp32 outputs");
+  static_assert(!YF32 || MODE == MODE_DOWN, "only the down projection has outputs to combine");
+  auto& red = L.red;
   if constexpr (MODE == MODE_GATEUP) {
     if (bid == 0 && p.clear != nullptr)
       for (int j = threadIdx.x; j < p.clear_n; j += blockDim.x) p.clear[j] = 0;
@@ -253,10 +261,14 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
   c = __builtin_amdgcn_readfirstlane(c);
   const int i = __builtin_amdgcn_readfirstlane(unit / G);
   const int g = unit - i * G;
-  const int e = __builtin_amdgcn_readfirstlane(nth_active_expert(p.offsets, p.slot_of_expert, p.E, i));
+  // offsets == NULL: one group over rows [0, rows) (a shared expert's problem, whose [0, T]
+  // offsets the caller need not hold)
+  const bool one = p.offsets == nullptr;
+  const int e = __builtin_amdgcn_readfirstlane(one ? ((i == 0 && p.slot_of_expert[0] >= 0) ? 0 : -1)
+                                                    : nth_active_expert(p.offsets, p.slot_of_expert, p.E, i));
   if (e < 0) return;
-  const int row0 = p.offsets[e];
-  const int n_e = p.offsets[e + 1] - row0;
+  const int row0 = one ? 0 : p.offsets[e];
+  const int n_e = one ? p.rows : p.offsets[e + 1] - row0;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int KT = p.K / 32;
   const int ks0 = (KT * s) / S, ks = (KT * (s + 1)) / S - ks0;   // this split's k-steps
@@ -364,7 +376,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
           } else if (S == 1) {
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-              store_y<COMB>(p, (size_t)(row0 + r) * p.N + (2 * g + j) * 16 + (lane & 15), acc[m][j][q]);
+              store_y<YF32>(p, (size_t)(row0 + r) * p.N + (2 * g + j) * 16 + (lane & 15), acc[m][j][q]);
           } else if constexpr (SPLIT) {
             // device-scope stores (written through to the coherent level, not left in this
             // XCD's L2), so no cache-wide write-back is needed to publish them
@@ -386,10 +398,10 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
         wait_vmcnt<0>();
         int last = 0;
         if (lane == 0) last = atomicAdd(&p.arrived[unit], 1) == S - 1;
-        if (lane == 0) s_last = last;
+        if (lane == 0) L.s_last = last;
       }
       __syncthreads();
-      if (s_last) {
+      if (L.s_last) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // no load moves above the count
         // the group's n_e x 32 outputs over the whole workgroup (one pass), the S loads
         // issued before the first add; device-scope loads never
@@ -407,7 +419,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
 #pragma unroll
           for (int t = 1; t < kDecMaxSplits; ++t)
             if (t < S) acc_v += v[t];
-          store_y<COMB>(p, o, acc_v);
+          store_y<YF32>(p, o, acc_v);
         }
       }
     }
@@ -418,7 +430,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
     // was the last of its K splits. Its stores have completed before the unit is counted;
     // the workgroup that counts the group's last unit combines the group's columns.
     bool done = true;
-    if constexpr (SPLIT) done = S == 1 || s_last;
+    if constexpr (SPLIT) done = S == 1 || L.s_last;
     if (done) {
       CombinePre pre;
       decode_combine_preload(cb, pre);   // overlaps the wait for this workgroup's stores
@@ -427,15 +439,41 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
       if (w == 0) {
         const int units = count_active_experts(p0.offsets, p0.slot_of_expert, p0.E) * p0.rchunks +
                           (cb.nprob > 1 ? count_active_experts(p1.offsets, p1.slot_of_expert, p1.E) * p1.rchunks : 0);
-        if (lane == 0) s_glast = atomicAdd(&cb.arrived[g], 1) == units - 1;
+        if (lane == 0) L.s_glast = atomicAdd(&cb.arrived[g], 1) == units - 1;
       }
       __syncthreads();
-      if (s_glast) {
+      if (L.s_glast) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");   // no load moves above the count
         decode_combine_group(cb, g, pre);
       }
     }
   }
+}
+
+// Blocks [0, nb0) work on problem p0, the rest on p1 (two independent grouped FFNs, e.g.
+// the routed experts and the shared expert, in one launch), both in projection MODE.
+template <int MODE, bool SPLIT, int MB, bool COMB = false, int WF = 0>
+__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
+    DecodeArgs p0, DecodeArgs p1, int nb0, DecodeCombine cb) {
+  __shared__ DecodeLds<MB> L;
+  const bool second = (int)blockIdx.x >= nb0;
+  decode_block<MODE, SPLIT, MB, COMB, COMB, WF>(second ? p1 : p0, second ? (int)blockIdx.x - nb0 : (int)blockIdx.x,
+                                                p0, p1, cb, L);
+}
+
+// Two problems in different projections in one launch: blocks [0, nb0) run the down
+// projection of dn (split over K when SPLIT; fp32 outputs for a later folded combine when
+// YF32), the rest the gate/up projection of gu. Both one m-block per pass.
+template <bool SPLIT, bool YF32, int WF>
+__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_down_gateup(DecodeArgs dn,
+                                                                                             DecodeArgs gu,
+                                                                                             int nb0) {
+  __shared__ DecodeLds<1> L;
+  const DecodeCombine no_cb{};
+  if ((int)blockIdx.x < nb0)
+    decode_block<MODE_DOWN, SPLIT, 1, YF32, false, WF>(dn, (int)blockIdx.x, dn, dn, no_cb, L);
+  else
+    decode_block<MODE_GATEUP, false, 1, false, false, WF>(gu, (int)blockIdx.x - nb0, gu, gu, no_cb, L);
 }
 
 }  // namespace

@@ -1,23 +1,24 @@
-// Stable expert-major grouping of at most 64 tokens inside one 1024-thread workgroup.
+// Stable expert-major grouping of at most 64 tokens inside one workgroup of NW wavefronts.
 //
 // The grouping lets each selected expert run once over all of its rows ("NovaLLM:
 // Running Massive MoE Models Fully In-Memory", section 3: only the experts that were
 // hit run); rows of one expert are ordered by ascending token. Every wavefront holds
-// all tokens (lane = token) and takes experts w, w + 16, ...: a ballot per expert gives
+// all tokens (lane = token) and takes experts w, w + NW, ...: a ballot per expert gives
 // its count, a workgroup-wide scan over the experts gives the offsets, and a second
 // ballot per expert ranks each (token, slot) pair among the expert's tokens.
 //
 // Used by moe_permute for one block of tokens and by the fused small-batch routing
-// kernel; both launch 1024 threads and need T <= 64, E <= 1024.
+// kernel (1024 threads, NW = 16), and by the fused decode step (512 threads, NW = 8); all
+// need T <= 64 and E <= 64 * NW.
 #pragma once
 
 #include "moe_internal.h"
 
 namespace moeffn {
 
-// idx [T, k] (device, written before the call and visible to the workgroup); counts may
-// be NULL. off is LDS scratch of E ints, wave_sum LDS scratch of 16 ints.
-template <int KMAX>
+// idx [T, k] (device or LDS, written before the call and visible to the workgroup); counts
+// may be NULL. off is LDS scratch of E ints, wave_sum LDS scratch of NW ints.
+template <int KMAX, int NW = 16>
 __device__ __forceinline__ void group_small(const int32_t* __restrict__ idx, int32_t* __restrict__ counts,
                                             int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                             int32_t* __restrict__ perm_dst, int T, int k, int E, int32_t* off,
@@ -27,7 +28,7 @@ __device__ __forceinline__ void group_small(const int32_t* __restrict__ idx, int
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) mine[j] = (lane < T && j < k) ? idx[(size_t)lane * k + j] : -1;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = wave; e < E; e += 16) {
+  for (int e = wave; e < E; e += NW) {
     bool has = false;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) has |= (mine[j] == e);
@@ -57,7 +58,7 @@ __device__ __forceinline__ void group_small(const int32_t* __restrict__ idx, int
   }
   if (tid == E - 1) offsets[E] = excl + c;
   __syncthreads();
-  for (int e = wave; e < E; e += 16) {
+  for (int e = wave; e < E; e += NW) {
     int slot = -1;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)

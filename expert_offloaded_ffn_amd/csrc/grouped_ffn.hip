@@ -14,6 +14,8 @@
 //  gemm_mx.h      ffn_gemm_mx, MXFP4 weights x MXFP8 activations on the block-scaled MFMA
 //  decode_bf16.h  ffn_decode_bf16, weight streaming for at most 64 rows per expert; one
 //                 launch can carry two problems (routed experts and the shared expert)
+//  decode_step.h  decode_step_front, the routing beside the shared expert's gate/up
+//                 (moe_decode_step)
 //  this file      ffn_f32_* (fp32 VALU path, one thread per output element) and the host
 //                 side: argument checks, workspace layout, launches
 #include <algorithm>
@@ -21,6 +23,7 @@
 #include <type_traits>
 
 #include "decode_bf16.h"
+#include "decode_step.h"
 #include "ffn_common.h"
 #include "gemm_bf16.h"
 #include "gemm_fp8.h"
@@ -787,6 +790,226 @@ extern "C" moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, con
   cb.arrived = reinterpret_cast<int32_t*>(w + L.arrived);
   cb.nprob = n;
   return launch_decode(c, n, as_stream(stream), &cb);
+}
+
+// ---------------------------------------------------------------- decode step --
+// A resident layer's whole decode step in three launches (four past kStepFoldMaxT tokens):
+//  1. decode_step_front: routing (logits split over K, then selection and grouping by the
+//     last workgroups to finish) beside the shared expert's gate/up units;
+//  2. the shared expert's down units beside the routed experts' gate/up units
+//     (ffn_decode_down_gateup), or the routed gate/up alone without a shared expert;
+//  3. the routed experts' down units, with the combine folded in up to kStepFoldMaxT tokens,
+//     else followed by moe_combine.
+// Every piece runs the same arithmetic as moe_route_permute, moe_grouped_ffn_batch and
+// moe_combine (or moe_grouped_ffn_combine), so the results are bit-identical to those calls.
+namespace moeffn {
+namespace {
+
+// Largest step whose combine runs inside the routed down launch. Each workgroup that
+// finishes a unit then waits for its stores and an arrival count before it exits; that pays
+// off only while the down launch is about one round of workgroups (1-4 tokens: MI355X,
+// Qwen1.5-MoE shape, 0.056 vs 0.058 ms per step at one token, 0.1185 vs 0.1175 ms at eight).
+#ifndef MOEFFN_STEP_FOLD_MAX_T
+#define MOEFFN_STEP_FOLD_MAX_T 4
+#endif
+constexpr int kStepFoldMaxT = MOEFFN_STEP_FOLD_MAX_T;
+
+struct StepLayout {
+  size_t part, idx, ws_shared, ws_routed, y_routed, y_shared, comb_arrived, total;
+};
+
+// Workspace: the routing's arrival counters in bytes [0, 256), the partial logits, the
+// published selection, the shared and the routed problem's moe_grouped_ffn workspaces, the
+// expert outputs (fp32 room), the combine's arrival counts.
+StepLayout step_layout(const moe_route_cfg& c, const moe_expert_table* routed, const moe_expert_table* shared) {
+  StepLayout L{};
+  const int T = c.T, k = c.top_k, d = c.d_model;
+  size_t h, m;
+  L.part = 256;
+  L.idx = L.part + align_up((size_t)route_slices(d) * T * (c.n_experts + 1) * 4, 256);
+  L.ws_shared = L.idx + align_up((size_t)T * k * 4, 256);
+  L.ws_routed = L.ws_shared + (shared ? align_up(ws_layout(shared, T, MOE_BF16, &h, &m), 256) : 0);
+  L.y_routed = L.ws_routed + align_up(ws_layout(routed, T * k, MOE_BF16, &h, &m), 256);
+  L.y_shared = L.y_routed + align_up((size_t)T * k * d * 4, 256);
+  L.comb_arrived = L.y_shared + (shared ? align_up((size_t)T * d * 4, 256) : 0);
+  L.total = L.comb_arrived + align_up((size_t)(d / 32) * 4, 256);
+  return L;
+}
+
+}  // namespace
+}  // namespace moeffn
+
+extern "C" size_t moe_decode_step_workspace_size(const moe_route_cfg* cfg, const moe_expert_table* routed,
+                                                 const moe_expert_table* shared) {
+  if (!cfg || !routed || cfg->T < 1 || cfg->T > kStepMaxT || cfg->top_k < 1 || cfg->n_experts < 1 ||
+      cfg->d_model < 32 || cfg->d_model % 32)
+    return 0;
+  if (shared && shared->d_model != routed->d_model) return 0;
+  return step_layout(*cfg, routed, shared).total;
+}
+
+extern "C" moe_status moe_decode_step(const moe_route_cfg* cfg, const void* x, const void* w_router,
+                                      const float* logit_bias, const float* select_bias, const void* w_shared_gate,
+                                      const moe_expert_table* routed, const moe_expert_table* shared,
+                                      const moe_decode_out* o, void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  MOE_REQUIRE(cfg != nullptr && routed != nullptr && o != nullptr, MOE_EINVAL,
+              "moe_decode_step: cfg, the routed table and the outputs must not be NULL");
+  const moe_route_cfg& c = *cfg;
+  if (moe_status st = check_route_config(c, "moe_decode_step")) return st;
+  const int T = c.T, k = c.top_k, E = c.n_experts, d = c.d_model;
+  MOE_REQUIRE(T >= 1 && T <= kStepMaxT, MOE_EUNSUPPORTED, "moe_decode_step: T=%d outside [1, %d] (decode steps only)",
+              T, kStepMaxT);
+  MOE_REQUIRE(c.act_dtype == MOE_BF16 && d % 32 == 0 && E <= kStepMaxE, MOE_EUNSUPPORTED,
+              "moe_decode_step: needs bf16 activations, d_model a multiple of 32 and at most %d experts", kStepMaxE);
+  MOE_REQUIRE(routed->n_experts == E && routed->d_model == d, MOE_EINVAL,
+              "moe_decode_step: the routed table has E=%d d=%d, the routing E=%d d=%d", routed->n_experts,
+              routed->d_model, E, d);
+  MOE_REQUIRE(routed->w_dtype == MOE_BF16 || routed->w_dtype == MOE_MXFP4, MOE_EUNSUPPORTED,
+              "moe_decode_step: weights must be bf16 or MXFP4 (w_dtype %d)", routed->w_dtype);
+  if (shared) {
+    MOE_REQUIRE(shared->n_experts == 1 && shared->d_model == d && shared->w_dtype == routed->w_dtype, MOE_EINVAL,
+                "moe_decode_step: the shared table must hold one expert of the routed experts' d_model and format");
+  }
+  MOE_REQUIRE(!(select_bias && c.score_fn == MOE_SOFTMAX), MOE_EINVAL, "moe_decode_step: select_bias needs sigmoid scoring");
+  MOE_REQUIRE((w_shared_gate == nullptr) == (o->shared_gate == nullptr), MOE_EINVAL,
+              "moe_decode_step: w_shared_gate and shared_gate go together");
+  MOE_REQUIRE(x && w_router && o->scores && o->topk_idx && o->topk_gate && o->offsets && o->perm_src && o->perm_dst &&
+                  o->out && ws,
+              MOE_EINVAL, "moe_decode_step: NULL tensor argument");
+  MOE_REQUIRE(aligned(x, 16) && aligned(w_router, 16) && (!w_shared_gate || aligned(w_shared_gate, 16)) &&
+                  aligned(o->out, 16) && aligned(ws, 256),
+              MOE_EINVAL, "moe_decode_step: x, w_router, w_shared_gate and out need 16-B, ws 256-B alignment");
+  MOE_REQUIRE(o->out_dtype == MOE_F32 || o->out_dtype == MOE_BF16, MOE_EUNSUPPORTED, "moe_decode_step: out_dtype %d",
+              o->out_dtype);
+  const StepLayout L = step_layout(c, routed, shared);
+  MOE_REQUIRE(ws_bytes >= L.total, MOE_ECAPACITY, "moe_decode_step: workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* w = static_cast<char*>(ws);
+  const bool fold = T <= kStepFoldMaxT;
+  size_t h, m;
+  // the two problems, checked as moe_grouped_ffn calls (the shared one is given the routed
+  // offsets only to pass the pointer check: its decode arguments drop them, see below)
+  FfnCall rc{*routed, T * k, o->offsets, x, nullptr, MOE_BF16, o->perm_src, k, w + L.y_routed, MOE_BF16,
+             w + L.ws_routed, ws_layout(routed, T * k, MOE_BF16, &h, &m)};
+  if (moe_status st = check_call(rc, "moe_decode_step (routed)")) return st;
+  MOE_REQUIRE(decode_path(rc), MOE_EUNSUPPORTED, "moe_decode_step: the routed problem is not a decode problem");
+  DecodeArgs gu_r, dn_r, gu_s{}, dn_s{};
+  int ngu_r = 0, ndn_r = 0, ngu_s = 0, ndn_s = 0;
+  decode_args(rc, decode_down_splits(routed, T * k), 1, &gu_r, &dn_r, &ngu_r, &ndn_r);
+  const int S_r = decode_down_splits(routed, T * k);
+  int S_s = 1;
+  if (shared) {
+    FfnCall sc{*shared, T, o->offsets, x, nullptr, MOE_BF16, nullptr, 1, w + L.y_shared, MOE_BF16, w + L.ws_shared,
+               ws_layout(shared, T, MOE_BF16, &h, &m)};
+    if (moe_status st = check_call(sc, "moe_decode_step (shared)")) return st;
+    S_s = decode_down_splits(shared, T);
+    decode_args(sc, S_s, T > 16 ? (T + 15) / 16 : 1, &gu_s, &dn_s, &ngu_s, &ndn_s);
+    gu_s.offsets = dn_s.offsets = nullptr;   // one group over rows [0, T)
+  }
+  DecodeCombine cb{};
+  if (fold) {
+    cb.T = T;
+    cb.k = k;
+    cb.d = d;
+    cb.perm_dst = o->perm_dst;
+    cb.gate = o->topk_gate;
+    cb.shared_gate = shared ? o->shared_gate : nullptr;
+    cb.y_routed = reinterpret_cast<const float*>(w + L.y_routed);
+    cb.y_shared = shared ? reinterpret_cast<const float*>(w + L.y_shared) : nullptr;
+    cb.out = o->out;
+    cb.out_dtype = o->out_dtype;
+    cb.arrived = reinterpret_cast<int32_t*>(w + L.comb_arrived);
+    cb.nprob = 1;
+    gu_r.clear2 = cb.arrived;
+    gu_r.clear2_n = d / 32;
+  }
+  // routing: m-tiles of 16 tokens, each with its (n-tile, slice) items over bpm workgroups
+  StepRoute r{};
+  r.x = static_cast<const bf16_t*>(x);
+  r.w_router = static_cast<const bf16_t*>(w_router);
+  r.w_sg = static_cast<const bf16_t*>(w_shared_gate);
+  r.logit_bias = logit_bias;
+  r.select_bias = select_bias;
+  r.part = reinterpret_cast<float*>(w + L.part);
+  r.idx_stage = reinterpret_cast<int32_t*>(w + L.idx);
+  r.arrive = reinterpret_cast<int32_t*>(w);
+  r.shared_gate = o->shared_gate;
+  r.scores = o->scores;
+  r.topk_idx = o->topk_idx;
+  r.topk_gate = o->topk_gate;
+  r.counts = o->counts;
+  r.offsets = o->offsets;
+  r.perm_src = o->perm_src;
+  r.perm_dst = o->perm_dst;
+  r.T = T;
+  r.d = d;
+  r.E = E;
+  r.ncols = E + (w_shared_gate ? 1 : 0);
+  r.nsl = route_slices(d);
+  r.n_nt = (r.ncols + 15) / 16;
+  r.n_mt = (T + 15) / 16;
+  r.bpm = (r.n_nt * r.nsl + kDecWaves - 1) / kDecWaves;
+  r.k = k;
+  r.score_fn = c.score_fn;
+  r.renormalize = c.renormalize;
+  r.route_scale = c.route_scale;
+  r.n_groups = c.n_groups < 1 ? 1 : c.n_groups;
+  r.topk_groups = c.topk_groups;
+  r.group_topn = c.group_topn;
+  const int nb_route = (r.n_mt * r.bpm + 7) / 8 * 8;
+  hipStream_t s = as_stream(stream);
+  const dim3 block(64 * kDecWaves);
+  const DecodeCombine no_cb{};
+  auto go = [&](auto pl, auto km, auto wf) {
+    constexpr int PL = decltype(pl)::value, KM = decltype(km)::value, WF = decltype(wf)::value;
+    hipLaunchKernelGGL((decode_step_front<PL, KM, WF>), dim3(nb_route + ngu_s), block, 0, s, r, nb_route, gu_s);
+    prof_mark(s, MOE_PROF_DEC_GATEUP, false);
+    if (shared) {
+      auto k2 = [&](auto sp, auto yf) {
+        constexpr bool SP = decltype(sp)::value, YF = decltype(yf)::value;
+        hipLaunchKernelGGL((ffn_decode_down_gateup<SP, YF, WF>), dim3(ndn_s + ngu_r), block, 0, s, dn_s, gu_r, ndn_s);
+      };
+      if (S_s > 1) {
+        if (fold) k2(std::true_type{}, std::true_type{});
+        else k2(std::true_type{}, std::false_type{});
+      } else {
+        if (fold) k2(std::false_type{}, std::true_type{});
+        else k2(std::false_type{}, std::false_type{});
+      }
+    } else {
+      hipLaunchKernelGGL((ffn_decode_bf16<MODE_GATEUP, false, 1, false, WF>), dim3(ngu_r), block, 0, s, gu_r, gu_r,
+                         ngu_r, no_cb);
+    }
+    prof_mark(s, MOE_PROF_DEC_GATEUP, true);
+    prof_mark(s, MOE_PROF_DEC_DOWN, false);
+    auto k3 = [&](auto sp) {
+      constexpr bool SP = decltype(sp)::value;
+      if (fold)
+        hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, 1, true, WF>), dim3(ndn_r), block, 0, s, dn_r, dn_r, ndn_r,
+                           cb);
+      else
+        hipLaunchKernelGGL((ffn_decode_bf16<MODE_DOWN, SP, 1, false, WF>), dim3(ndn_r), block, 0, s, dn_r, dn_r,
+                           ndn_r, no_cb);
+    };
+    if (S_r > 1) k3(std::true_type{});
+    else k3(std::false_type{});
+    prof_mark(s, MOE_PROF_DEC_DOWN, true);
+  };
+  auto by_wf = [&](auto pl, auto km) {
+    if (routed->w_dtype == MOE_MXFP4) go(pl, km, std::integral_constant<int, 1>{});
+    else go(pl, km, std::integral_constant<int, 0>{});
+  };
+  auto by_k = [&](auto pl) {
+    if (k <= 8) by_wf(pl, std::integral_constant<int, 8>{});
+    else by_wf(pl, std::integral_constant<int, 32>{});
+  };
+  if (E <= 64) by_k(std::integral_constant<int, 1>{});
+  else if (E <= 128) by_k(std::integral_constant<int, 2>{});
+  else by_k(std::integral_constant<int, 4>{});
+  if (moe_status st = check_launch("moe_decode_step")) return st;
+  if (fold) return MOE_OK;
+  return moe_combine(T, k, d, w + L.y_routed, MOE_BF16, o->perm_dst, o->topk_gate, shared ? w + L.y_shared : nullptr,
+                     shared ? o->shared_gate : nullptr, o->out, o->out_dtype, stream);
 }
 
 // ------------------------------------------------------- no-allocation variant --

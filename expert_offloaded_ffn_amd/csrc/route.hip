@@ -22,6 +22,7 @@
 
 #include "group_small.h"
 #include "moe_internal.h"
+#include "route_small.h"
 
 namespace moeffn {
 namespace {
@@ -152,168 +153,8 @@ __global__ __launch_bounds__(256) void route_logits_valu(
 }
 
 // -------------------------------------------------------------- select ---
-// Orderable encoding: larger (key, then lower index) -> larger word; 0 = none.
-__device__ __forceinline__ uint64_t pack_key(float key, int idx) {
-  if (key == 0.0f) key = 0.0f;  // -0 and +0 tie
-  uint32_t u = __float_as_uint(key);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return (static_cast<uint64_t>(u) << 32) | static_cast<uint32_t>(0xFFFFFFFFu - static_cast<uint32_t>(idx));
-}
-__device__ __forceinline__ int unpack_idx(uint64_t w) {
-  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(w & 0xFFFFFFFFu));
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 
 constexpr int kSelWaves = 4;     // waves per block
-
-// Selection for token t by one wavefront: keys, the group limit, k rounds of a wave-wide
-// arg-max, the gates, and the sigmoid of the shared gate's logit. Reads the token's raw
-// logits from src (row t at src + t * src_stride: scores itself, or a copy in LDS) and
-// writes its keys to scores; wk is LDS scratch of E floats owned by this wavefront; hist
-// (LDS, may be NULL) counts the selected experts.
-template <int PER_LANE>
-__device__ __forceinline__ void select_token(
-    int t, const float* src, int src_stride, float* __restrict__ scores, const float* __restrict__ logit_bias,
-    const float* __restrict__ select_bias,
-    float* __restrict__ shared_gate, int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate, int* hist,
-    float* wk, int E, int k, int score_fn, int renormalize, float route_scale, int n_groups, int topk_groups,
-    int group_topn, int32_t* idx_copy = nullptr) {
-  const int lane = threadIdx.x & 63;
-  const int gsz = n_groups > 0 ? E / n_groups : E;
-  float logit[PER_LANE], key[PER_LANE];
-  bool live[PER_LANE];
-#pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) {
-    const int e = lane + 64 * i;
-    live[i] = e < E;
-    float l = 0.f;
-    if (live[i]) {
-      l = src[(size_t)t * src_stride + e];
-      if (logit_bias) l += logit_bias[e];
-    }
-    logit[i] = l;
-    float kv = l;
-    if (score_fn == MOE_SIGMOID) {
-      const float s = 1.0f / (1.0f + expf(-l));
-      logit[i] = s;  // for sigmoid routing keep s for the gates
-      kv = s;
-      if (select_bias && live[i]) kv = s + select_bias[e];
-    }
-    key[i] = kv;
-    if (live[i]) scores[(size_t)t * E + e] = kv;
-  }
-
-  // group limit: lanes g < n_groups score their group from the keys in LDS
-  if (n_groups > 1 && topk_groups < n_groups) {
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i)
-      if (live[i]) wk[lane + 64 * i] = key[i];
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    uint64_t gword = 0;
-    if (lane < n_groups) {
-      // the group's group_topn largest keys, summed largest first in fp32
-      float top[8];
-      const int nt = min(group_topn, 8);
-      for (int i = 0; i < nt; ++i) top[i] = -INFINITY;
-      for (int m = 0; m < gsz; ++m) {
-        float v = wk[lane * gsz + m];
-        for (int i = 0; i < nt; ++i) {
-          if (v > top[i]) { float tmp = top[i]; top[i] = v; v = tmp; }
-        }
-      }
-      float sum = top[0];
-      for (int i = 1; i < nt; ++i) sum = sum + top[i];
-      gword = pack_key(sum, lane);
-    }
-    uint64_t keep_mask = 0;
-    for (int r = 0; r < topk_groups; ++r) {
-      const uint64_t best = wave_max_u64(gword);
-      const int g = unpack_idx(best);
-      keep_mask |= 1ull << g;
-      if (lane == g) gword = 0;
-    }
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-      const int e = lane + 64 * i;
-      if (live[i] && !((keep_mask >> (e / gsz)) & 1ull)) live[i] = false;
-    }
-    __builtin_amdgcn_wave_barrier();
-  }
-
-  // top-k: k rounds of a wave-wide arg-max
-  int sel_idx = 0;
-  float sel_val = 0.f;  // logit (softmax) or s (sigmoid) of the lane-th winner
-  for (int r = 0; r < k; ++r) {
-    uint64_t mine = 0;
-    int mine_i = -1;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-      if (live[i]) {
-        const uint64_t w = pack_key(key[i], lane + 64 * i);
-        if (w > mine) { mine = w; mine_i = i; }
-      }
-    }
-    const uint64_t best = wave_max_u64(mine);
-    const int e = unpack_idx(best);
-    float v = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) {
-      if (lane + 64 * i == e) { live[i] = false; v = logit[i]; }
-    }
-    // broadcast the winner's value from its owner lane
-    const int owner = e & 63;
-    v = __shfl(v, owner, 64);
-    if (lane == r) { sel_idx = e; sel_val = v; }
-    (void)mine_i;
-  }
-
-  // gates (lanes r < k hold winner r)
-  float g = 0.f;
-  if (score_fn == MOE_SOFTMAX) {
-    const float m = __shfl(sel_val, 0, 64);  // the best key is the largest selected logit
-    if (renormalize) {
-      const float z = lane < k ? expf(sel_val - m) : 0.f;
-      const float denom = wave_sum_f32(z);
-      g = z / denom;
-    } else {
-      float part = 0.f;
-#pragma unroll
-      for (int i = 0; i < PER_LANE; ++i)
-        if (lane + 64 * i < E) part += expf(logit[i] - m);
-      const float denom = wave_sum_f32(part);
-      g = lane < k ? expf(sel_val - m) / denom : 0.f;
-    }
-  } else {
-    const float s = lane < k ? sel_val : 0.f;
-    if (renormalize) g = s / wave_sum_f32(s);
-    else g = s;
-  }
-  g *= route_scale;
-  if (lane < k) {
-    topk_idx[(size_t)t * k + lane] = sel_idx;
-    if (idx_copy) idx_copy[t * k + lane] = sel_idx;   // (LDS) for a grouping in the same workgroup
-    topk_gate[(size_t)t * k + lane] = g;
-    if (hist) atomicAdd(&hist[sel_idx], 1);
-  }
-  if (shared_gate && lane == 0) {
-    const float l = shared_gate[t];
-    shared_gate[t] = 1.0f / (1.0f + expf(-l));
-  }
-}
 
 template <int PER_LANE>
 __global__ __launch_bounds__(256) void route_select(
@@ -330,7 +171,7 @@ __global__ __launch_bounds__(256) void route_select(
   for (int it = 0; it < tok_per_wave; ++it) {
     const int t = (blockIdx.x * kSelWaves + wave) * tok_per_wave + it;
     if (t >= T) break;
-    select_token<PER_LANE>(t, scores, E, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
+    select_token<PER_LANE>(t, scores + (size_t)t * E, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
                            counts != nullptr ? hist : nullptr, wkeys[wave], E, k, score_fn, renormalize,
                            route_scale, n_groups, topk_groups, group_topn);
   }
@@ -351,22 +192,15 @@ void launch_select(int tpw, hipStream_t s, float* scores, const float* lb, const
 }
 
 // -------------------------------------------------------- small batches ---
-// A decode step routes at most 64 tokens. One workgroup could hold all of their logits, but
-// a single CU pulls the router weights from HBM slowly, so the logits are split over K into
-// slices of kSliceSteps k-steps of 32 that many workgroups compute at once
-// (route_logit_slices: one wave per slice, n-tile of 16 columns and m-tile of 16 tokens,
-// every load of the slice issued at once). Up to 16 tokens, one workgroup then adds each
-// logit's slices in slice order, selects and groups (route_finish_small: select_token,
-// group_small); for more tokens the slices would be as many bytes as the router weights,
-// too many for one workgroup to read back, so a wavefront per token sums and selects
-// (route_select_slices) and the one-workgroup grouping follows.
+// The logits of up to 64 tokens split over K (route_slice_wave in route_small.h). Up to 16
+// tokens, one workgroup then adds each logit's slices in slice order, selects and groups
+// (route_finish_small: select_token, group_small); for more tokens the slices would be as
+// many bytes as the router weights, too many for one workgroup to read back, so a wavefront
+// per token sums and selects (route_select_slices) and the one-workgroup grouping follows.
 // (one workgroup reading back the slices of 17..64 tokens measured slower than the two
 // launches: 0.244 vs 0.231 ms per Qwen-shaped step at 64 tokens)
 constexpr int kFuseMaxT = 16;
 constexpr int kFuseMaxE = 256;
-constexpr int kSliceSteps = 4;
-
-int route_slices(int d) { return (d / 32 + kSliceSteps - 1) / kSliceSteps; }
 
 // grid (slices, column groups of 64, m-tiles of 16), 4 waves: wave w takes n-tile w of the
 // group. Output: part[slice][t][c] fp32 for t < T, c < E (+1 with the shared gate column).
@@ -374,37 +208,13 @@ __global__ __launch_bounds__(256) void route_logit_slices(const bf16_t* __restri
                                                           const bf16_t* __restrict__ w_router,
                                                           const bf16_t* __restrict__ w_sg, float* __restrict__ part,
                                                           int32_t* __restrict__ counts, int T, int d, int E) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   if (counts != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)   // route_select_slices adds to them
     for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
   const int ncols = E + (w_sg != nullptr ? 1 : 0);
-  const int sl = blockIdx.x, c0 = blockIdx.y * 64 + wave * 16, t0 = blockIdx.z * 16;
+  const int c0 = blockIdx.y * 64 + wave * 16;
   if (c0 >= ncols) return;   // the whole wave: its n-tile lies past the last column
-  const int KT = d / 32;
-  const int k0 = sl * kSliceSteps, nk = min(KT - k0, kSliceSteps);
-  const int koff = 8 * (lane >> 4);
-  const int c = min(c0 + (lane & 15), ncols - 1);
-  const bf16_t* brow = (c < E ? w_router + (size_t)c * d : w_sg) + koff + k0 * 32;
-  const bf16_t* arow = x + (size_t)min(t0 + (lane & 15), T - 1) * d + koff + k0 * 32;
-  bf16x8_t b[kSliceSteps], a[kSliceSteps];
-#pragma unroll
-  for (int j = 0; j < kSliceSteps; ++j) {
-    if (j < nk) {
-      b[j] = *reinterpret_cast<const bf16x8_t*>(brow + j * 32);
-      a[j] = *reinterpret_cast<const bf16x8_t*>(arow + j * 32);
-    }
-  }
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < kSliceSteps; ++j)
-    if (j < nk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b[j], acc, 0, 0, 0);
-  // D layout: lane l holds rows 4*(l/16)+i, column l%16
-  const int col = c0 + (lane & 15);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + 4 * (lane >> 4) + i;
-    if (t < T && col < ncols) part[((size_t)sl * T + t) * ncols + col] = acc[i];
-  }
+  route_slice_wave<false>(x, w_router, w_sg, part, T, d, E, ncols, blockIdx.x, c0, blockIdx.z * 16);
 }
 
 template <int PER_LANE, int KMAX>
@@ -421,41 +231,10 @@ __global__ __launch_bounds__(1024) void route_finish_small(
   __shared__ int32_t wave_sum[16];
   __shared__ int32_t idx_lds[kFuseMaxT * 32];   // the selection, read back by the grouping
   const int wave = threadIdx.x >> 6;
-  const int n = T * ncols;
-  // Each logit is the sum of its slices in slice order. A thread takes up to 2 logits at a
-  // time and issues 16 slices of each (32 loads; 16 slices cover d = 2048) before the
-  // first add.
-  constexpr int kE = 2, kS = 16;
-  for (int j0 = threadIdx.x; j0 < n; j0 += kE * blockDim.x) {
-    float v[kE];
-    for (int s0 = 0; s0 < nsl; s0 += kS) {
-      float buf[kE][kS];
-#pragma unroll
-      for (int u = 0; u < kE; ++u) {
-        const int j = j0 + u * blockDim.x;
-#pragma unroll
-        for (int q = 0; q < kS; ++q)
-          if (j < n && s0 + q < nsl) buf[u][q] = part[(size_t)(s0 + q) * n + j];
-      }
-#pragma unroll
-      for (int u = 0; u < kE; ++u)
-#pragma unroll
-        for (int q = 0; q < kS; ++q)
-          if (s0 + q < nsl) v[u] = (s0 + q == 0) ? buf[u][q] : v[u] + buf[u][q];
-    }
-#pragma unroll
-    for (int u = 0; u < kE; ++u) {
-      const int j = j0 + u * blockDim.x;
-      if (j >= n) continue;
-      lg[j] = v[u];
-      const int t = j / ncols, c = j - t * ncols;
-      if (c < E) scores[(size_t)t * E + c] = v[u];
-      else shared_gate[t] = v[u];
-    }
-  }
+  route_sum_slices<false>(part, nsl, T * ncols, 0, T * ncols, lg, scores, shared_gate, E, ncols);
   __syncthreads();
   for (int t = wave; t < T; t += 16)
-    select_token<PER_LANE>(t, lg, ncols, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, nullptr,
+    select_token<PER_LANE>(t, lg + t * ncols, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate, nullptr,
                            wkeys[wave], E, k, score_fn, renormalize, route_scale, n_groups, topk_groups, group_topn,
                            idx_lds);
   __syncthreads();
@@ -498,7 +277,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void route_select_slices(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (shared_gate != nullptr && lane == 0) shared_gate[t] = lg[wave][E];   // the raw logit; sigmoid below
-    select_token<PER_LANE>(t, lg[wave], 0, scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
+    select_token<PER_LANE>(t, lg[wave], scores, logit_bias, select_bias, shared_gate, topk_idx, topk_gate,
                            counts != nullptr ? hist : nullptr, wkeys[wave], E, k, score_fn, renormalize,
                            route_scale, n_groups, topk_groups, group_topn);
   }
@@ -537,6 +316,9 @@ moe_status check_route_cfg(const moe_route_cfg& c, const char* who) {
 }
 
 }  // namespace
+
+moe_status check_route_config(const moe_route_cfg& c, const char* who) { return check_route_cfg(c, who); }
+
 }  // namespace moeffn
 
 using namespace moeffn;

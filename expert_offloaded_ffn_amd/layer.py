@@ -112,7 +112,7 @@ FUSE_COMBINE_MAX_T = 4
 class MoELayer:
     def __init__(self, cfg, *, router, experts, shared=None, w_shared_gate=None, select_bias=None, device="cuda",
                  pool_slots=None, blocking=False, threads=8, fuse_combine=True, shared_pool=None, layer_index=0,
-                 device_plan=False, freq_decay=0.0):
+                 device_plan=False, freq_decay=0.0, fused_step=True):
         """router: W_r [d, E] storage; experts: list of synth expert tuples; shared: synth tuple or None.
         pool_slots: None = every expert resident; an int = expert slot pool of that many slots.
         shared_pool: a SharedSlotPool this layer's experts live in (entry layer_index*E + e);
@@ -123,8 +123,12 @@ class MoELayer:
         (expert_slot_cache_set_frequency / expert_slot_cache_dev_set_frequency); 0 = plain LRU.
         fuse_combine: a decode step of at most FUSE_COMBINE_MAX_T tokens that runs the shared expert
         in the routed experts' launches combines inside the down launch (moe_grouped_ffn_combine)
-        instead of a moe_combine call."""
+        instead of a moe_combine call.
+        fused_step: a resident decode step (fused_decode_step) runs as one moe_decode_step call;
+        False keeps the separate calls (moe_route_permute, the batched FFN, the combine), which
+        give the same bits."""
         self.fuse_combine = fuse_combine
+        self.fused_step = fused_step
         self.cfg = cfg
         self.device = torch.device(device)
         self.act = cfg.act_dtype
@@ -191,6 +195,15 @@ class MoELayer:
             self._ws[name] = t
         return t[:max(numel, 1)] if numel else t[:1]
 
+    def _zbuf(self, name, numel):
+        """A device byte buffer zero-filled when (re)allocated: moe_decode_step's workspace, whose
+        arrival counters must be zero before its first call and are left zero by every call."""
+        t = self._ws.get(name)
+        if t is None or t.numel() < numel:
+            t = torch.zeros(max(numel, 256), dtype=torch.uint8, device=self.device)
+            self._ws[name] = t
+        return t
+
     def _shared_offsets(self, T):
         """Device [0, T] offsets of the single shared-expert group (cached per T)."""
         key = ("shared_offsets", T)
@@ -219,6 +232,12 @@ class MoELayer:
         the pool's tables, so its shared expert always takes the side stream."""
         return (self.shared is not None and self.cache is None and self.cache_dev is None
                 and self.w_code in (B.MOE_BF16, B.MOE_MXFP4) and 0 < T <= 64)
+
+    def fused_decode_step(self, T: int) -> bool:
+        """Whether a T-token forward is one moe_decode_step call: every expert resident, bf16
+        activations, bf16 or MXFP4 weights, 1..64 tokens, at most 256 experts."""
+        return (self.fused_step and self.cache is None and self.cache_dev is None and self.act == "bf16"
+                and self.w_code in (B.MOE_BF16, B.MOE_MXFP4) and 0 < T <= 64 and self.E <= 256 and self.d % 32 == 0)
 
     def mx_prefill(self, T: int) -> bool:
         """Whether a T-token forward runs MXFP4 experts on the block-scaled MFMA (more than 64
@@ -264,6 +283,15 @@ class MoELayer:
                              "is resident or planned on the device")
         main = torch.cuda.current_stream(self.device) if stream is None else stream
         ydt = B.MOE_F32 if self.act == "f32" else B.MOE_BF16
+        if self.fused_decode_step(T):
+            # routing beside the shared expert's gate/up, its down beside the routed gate/up, then
+            # the routed down with the combine: three launches (four past 4 tokens)
+            shared_table = self.shared.table if self.shared is not None else None
+            ws = self._zbuf("step_ws", B.decode_step_workspace_size(T, self.d, E, k, self.table, shared_table))
+            r = B.decode_step(x, self.w_router_t, self.table, shared_table, logit_bias=logit_bias,
+                              select_bias=self.select_bias, w_shared_gate=self.w_sg, out_dtype=ydt, ws=ws,
+                              stream=main, **self.route_args())
+            return {"out": r["out"], "route": r, "perm": r, "y": None, "shared_y": None, "waves": 0}
         shared_y = None
         merged = self.shared_in_decode_launch(T)
         ws = self._buf("perm_ws", B.route_permute_workspace_size(T, k, E, d))

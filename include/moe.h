@@ -382,6 +382,59 @@ moe_status moe_grouped_ffn_combine(const moe_ffn_problem* routed, const moe_ffn_
 moe_status moe_grouped_ffn_combine_noalloc(const moe_ffn_problem* routed, const moe_ffn_problem* shared,
                                            const moe_combine_args* comb, void* stream);
 
+/* ------------------------------------------------------------- decode step --
+ * A whole decode step of a resident layer in one call: moe_route_permute, the
+ * routed experts' and the shared expert's FFN, and the combine ([NOVA]
+ * section 3, Optimization #3: a decode step is many small launches, whose
+ * overhead and idle gaps the step should not pay). Three launches (four past
+ * 4 tokens, where the combine is its own launch):
+ *  1. the router logits split over K beside the shared expert's gate/up
+ *     projection, which needs no routing ([VVLLM] "Gotcha": the shared expert
+ *     sits outside the routed set), so its weights stream while the routing
+ *     runs; the last routing workgroups to finish select and group;
+ *  2. the shared expert's down projection beside the routed experts' gate/up;
+ *  3. the routed experts' down projection, with the combine folded in for
+ *     T <= 4 (as moe_grouped_ffn_combine), else followed by moe_combine.
+ * Results are bit-identical to moe_route_permute(cfg, ...) followed by, for
+ * T <= 4, moe_grouped_ffn_combine and otherwise moe_grouped_ffn_batch plus
+ * moe_combine, with both problems' y_dtype MOE_BF16 (each expert output is
+ * rounded to bf16; the sum runs in fp32, j ascending, shared term last).
+ *  cfg       routing as for moe_route_permute; act_dtype MOE_BF16, 1 <= T <= 64,
+ *            d_model % 32 == 0, n_experts <= 256
+ *  x [T, d] bf16, w_router [E, d] bf16, logit_bias / select_bias / w_shared_gate
+ *            as for moe_route_permute (w_shared_gate given iff o->shared_gate)
+ *  routed    the table of the E routed experts (bf16 or MXFP4 bundles)
+ *  shared    NULL, or a one-expert table of the same d_model and format (its
+ *            rows are the T tokens; no offsets are needed)
+ *  o         the routing outputs of moe_route_permute (counts may be NULL) and
+ *            out [T, d] (16-B aligned) in out_dtype (MOE_F32 or MOE_BF16)
+ * Workspace: moe_decode_step_workspace_size(cfg, routed, shared) bytes, 256-B
+ * aligned. Its first 256 bytes are arrival counters that must be zero when
+ * the first call on that workspace starts (e.g. a zero-filled allocation);
+ * every call leaves them zero. Calls that share a workspace must not overlap.
+ * Errors: as moe_route_permute and moe_grouped_ffn for each problem;
+ * MOE_EUNSUPPORTED outside the sizes above (use the separate calls).
+ */
+typedef struct {
+  float* shared_gate;   /* [T] or NULL (given iff w_shared_gate) */
+  float* scores;        /* [T, E] */
+  int32_t* topk_idx;    /* [T, k] */
+  float* topk_gate;     /* [T, k] */
+  int32_t* counts;      /* [E] or NULL */
+  int32_t* offsets;     /* [E + 1] */
+  int32_t* perm_src;    /* [T * k] */
+  int32_t* perm_dst;    /* [T * k] */
+  void* out;            /* [T, d] out_dtype */
+  int32_t out_dtype;    /* MOE_F32 or MOE_BF16 */
+} moe_decode_out;
+
+size_t moe_decode_step_workspace_size(const moe_route_cfg* cfg, const moe_expert_table* routed,
+                                      const moe_expert_table* shared);
+moe_status moe_decode_step(const moe_route_cfg* cfg, const void* x, const void* w_router,
+                           const float* logit_bias, const float* select_bias, const void* w_shared_gate,
+                           const moe_expert_table* routed, const moe_expert_table* shared,
+                           const moe_decode_out* o, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- expert slot cache --
  * Expert-granular residency: a fixed pool of n_slots bundle slots in HBM backed
  * by every expert's bundle in pinned host memory ([NOVA] section 3,

@@ -80,7 +80,7 @@ def test_grouped_ffn_validation_codes():
 
 _STRUCTS = [("moe_route_cfg", B.RouteCfg), ("moe_expert_table", B.ExpertTable), ("moe_ffn_problem", B.FfnProblem),
             ("moe_cache_cfg", B.CacheCfg), ("moe_cache_stats", B.CacheStats), ("moe_cache_entry", B.CacheEntry),
-            ("moe_profile", B.Profile), ("moe_combine_args", B.CombineArgs)]
+            ("moe_profile", B.Profile), ("moe_combine_args", B.CombineArgs), ("moe_decode_out", B.DecodeOut)]
 
 
 def test_struct_layouts_match_header(tmp_path):
@@ -169,6 +169,54 @@ def test_grouped_ffn_combine_validation_codes():
     empty = B.CombineArgs(0, k, None, None, None, None, B.MOE_BF16)
     r0 = B.FfnProblem(ctypes.pointer(t), 0, None, None, None, B.MOE_BF16, None, k, None, B.MOE_BF16)
     assert L.moe_grouped_ffn_combine(ctypes.byref(r0), None, ctypes.byref(empty), None, 0, None) == 0
+
+
+def test_decode_step_validation_codes():
+    """The fused decode step rejects, before any launch, what the separate calls would reject and
+    the sizes it does not cover (more than 64 tokens, more than 256 experts, fp8 weights), and
+    sizes its workspace as documented."""
+    L = B.lib()
+    fake = ctypes.c_void_p(0x1000)
+    T, d, E, k, F = 4, 256, 8, 2, 512
+    t = B.ExpertTable(ctypes.c_void_p(256), B.bundle_bytes(d, F, B.MOE_BF16), ctypes.c_void_p(256), E, d, F,
+                      B.MOE_BF16)
+    ts = B.ExpertTable(ctypes.c_void_p(256), B.bundle_bytes(d, 1024, B.MOE_BF16), ctypes.c_void_p(256), 1, d, 1024,
+                       B.MOE_BF16)
+    cfg = B.RouteCfg(T, d, E, k, B.MOE_SOFTMAX, 1, 1.0, 1, 1, 0, B.MOE_BF16)
+    out = B.DecodeOut(None, fake, fake, fake, None, fake, fake, fake, fake, B.MOE_BF16)
+    need = L.moe_decode_step_workspace_size(ctypes.byref(cfg), ctypes.byref(t), ctypes.byref(ts))
+    need0 = L.moe_decode_step_workspace_size(ctypes.byref(cfg), ctypes.byref(t), None)
+    one = lambda n: (n + 255) // 256 * 256
+    # counters, logit slices (d/128 slices x T x (E + 1)), the selection, the two FFN workspaces,
+    # fp32 expert outputs, the combine's group counts
+    ffn_s = L.moe_grouped_ffn_workspace_size(ctypes.byref(ts), T, B.MOE_BF16)
+    ffn_r = L.moe_grouped_ffn_workspace_size(ctypes.byref(t), T * k, B.MOE_BF16)
+    assert need == (256 + one(d // 128 * T * (E + 1) * 4) + one(T * k * 4) + one(ffn_s) + one(ffn_r) +
+                    one(T * k * d * 4) + one(T * d * 4) + one(d // 32 * 4))
+    assert need0 == need - one(ffn_s) - one(T * d * 4)
+    go = lambda c, o, ws, n, shared=ctypes.byref(ts): L.moe_decode_step(
+        ctypes.byref(c), fake, fake, None, None, None, ctypes.byref(t), shared, o, ws, n, None)
+    assert L.moe_decode_step(None, fake, fake, None, None, None, ctypes.byref(t), None, ctypes.byref(out), fake, need,
+                             None) == -1
+    assert go(cfg, ctypes.byref(out), fake, need - 1) == -4                          # short workspace
+    assert go(cfg, ctypes.byref(out), ctypes.c_void_p(0x1010), need) == -1           # misaligned workspace
+    big = B.RouteCfg(65, d, E, k, B.MOE_SOFTMAX, 1, 1.0, 1, 1, 0, B.MOE_BF16)
+    assert go(big, ctypes.byref(out), fake, 1 << 30) == -2                           # not a decode step
+    assert b"decode steps only" in L.moe_last_error()
+    f32 = B.RouteCfg(T, d, E, k, B.MOE_SOFTMAX, 1, 1.0, 1, 1, 0, B.MOE_F32)
+    assert go(f32, ctypes.byref(out), fake, need) == -2
+    with_gate = B.DecodeOut(fake, fake, fake, fake, None, fake, fake, fake, fake, B.MOE_BF16)
+    assert go(cfg, ctypes.byref(with_gate), fake, need) == -1                         # gate output, no weights
+    assert b"go together" in L.moe_last_error()
+    t8 = B.ExpertTable(ctypes.c_void_p(256), B.bundle_bytes(d, F, B.MOE_FP8_E4M3), ctypes.c_void_p(256), E, d, F,
+                       B.MOE_FP8_E4M3)
+    assert L.moe_decode_step(ctypes.byref(cfg), fake, fake, None, None, None, ctypes.byref(t8), None,
+                             ctypes.byref(out), fake, 1 << 30, None) == -2
+    wrong_e = B.ExpertTable(ctypes.c_void_p(256), B.bundle_bytes(d, F, B.MOE_BF16), ctypes.c_void_p(256), E + 1, d,
+                            F, B.MOE_BF16)
+    assert L.moe_decode_step(ctypes.byref(cfg), fake, fake, None, None, None, ctypes.byref(wrong_e), None,
+                             ctypes.byref(out), fake, 1 << 30, None) == -1
+    assert L.moe_decode_step_workspace_size(ctypes.byref(big), ctypes.byref(t), None) == 0
 
 
 def test_route_permute_workspace_only_holds_slices_when_used():

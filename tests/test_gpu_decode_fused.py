@@ -25,8 +25,9 @@ def qwen():
     cfg = synth.get_config("qwen_decode_bf16")
     w = dict(router=synth.gen_router(cfg), experts=synth.gen_experts(cfg), shared=synth.gen_shared(cfg),
              w_sg=synth.gen_shared_gate(cfg))
+    # the separate calls (fused_step=False): this module tests moe_grouped_ffn_combine
     layer = MoELayer(cfg, router=w["router"], experts=w["experts"], shared=w["shared"], w_shared_gate=w["w_sg"],
-                     device=DEV)
+                     device=DEV, fused_step=False)
     return cfg, layer, w
 
 
