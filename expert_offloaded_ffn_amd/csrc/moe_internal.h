@@ -47,9 +47,6 @@ int device_cu_count();
 // Timing marks around heavy kernels (no-op unless moe_profile_enable(1)).
 void prof_mark(hipStream_t s, int kind, bool end);
 
-// The routing configuration checks of moe_route (MOE_OK or the error, recorded for who).
-moe_status check_route_config(const moe_route_cfg& c, const char* who);
-
 // ----------------------------------------------------------- conversions --
 typedef unsigned short bf16_t;  // bf16 bit pattern
 

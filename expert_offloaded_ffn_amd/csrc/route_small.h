@@ -11,6 +11,11 @@
 #include "moe_internal.h"
 
 namespace moeffn {
+
+// The routing configuration checks of moe_route (MOE_OK or the error, recorded for who);
+// defined in route.hip.
+moe_status check_route_config(const moe_route_cfg& c, const char* who);
+
 namespace {
 
 // -------------------------------------------------------------- select ---
