@@ -24,6 +24,8 @@
 // GEMM from a second stream nor re-reads its activations once per n-tile from its own launch).
 #pragma once
 
+#include <type_traits>
+
 #include "ffn_common.h"
 
 namespace moeffn {
@@ -209,76 +211,90 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
   const int wsel = MODE == MODE_GATEUP ? (wn & 1) : (wn >> 1);
   const f32x4_t zero{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  for (int s = 0; s < KB; ++s) {
-    // stage s has landed for every wave, and every wave is done with stage s - 1's buffer (its
-    // fragment reads have completed; at s = 0 the weight scales above are written)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    barrier_no_fence();
-    if (s + 1 < KB) issue(s + 1);
-    if (nmb <= 0) continue;
-    const char* buf = ring + (s & 1) * kQStage;
-    const float sw = s_wscale[wsel][s];
-    i32x8_t fb[4];
+  // The k loop for NMB computed m-blocks per wave (0, 2, 4, 6 or 8: the wave's m-blocks with
+  // rows, rounded up to an even count). The extra m-block of an odd count computes on rows past
+  // the tile's last (clamped copies of it, or stale LDS where no load was issued); those rows
+  // are never stored.
+  auto kloop = [&](auto nmb_c) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    issue(0);
+    for (int s = 0; s < KB; ++s) {
+      // stage s has landed for every wave, and every wave is done with stage s - 1's buffer
+      // (its fragment reads have completed; at s = 0 the weight scales above are written)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      barrier_no_fence();
+      if (s + 1 < KB) issue(s + 1);
+      if constexpr (NMB > 0) {
+        const char* buf = ring + (s & 1) * kQStage;
+        const float sw = s_wscale[wsel][s];
+        i32x8_t fb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const char* blk = buf + kQB + nblk(j) * 2048 + 16 * lane;
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
-      fb[j] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int j = 0; j < 4; ++j) {
+          const char* blk = buf + kQB + nblk(j) * 2048 + 16 * lane;
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
+          fb[j] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+        auto frag_a = [&](int i) {
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + a_frag0 + 2048 * i);
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + a_frag1 + 2048 * i);
+          return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        auto row_scales = [&](int i) { return *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * i) * sw; };
+        // operand formats 0 (e4m3), block scales 2^0: the fp32 scales are applied on the VALU
+        auto mfma = [&](const i32x8_t& fa, int j) {
+          return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], zero, 0, 0, 0, 127, 0, 127);
+        };
+        // Software pipeline over the wave's NMB m-blocks. Per m-block i: read m-block i + 1's
+        // fragment and row scales from LDS, then issue i's four MFMAs, each followed by four of
+        // the FMAs that promote m-block i - 1's partial products (issued a whole block earlier,
+        // so they are ready), then form i + 1's combined scales. Scheduling-group barriers pin
+        // that order (the compiler would otherwise promote each result right after its MFMA
+        // and wait for it), and a scheduling barrier per m-block keeps it from hoisting every
+        // block's reads, which would not fit the registers.
+        i32x8_t fa = frag_a(0);
+        f32x4_t sc = row_scales(0);
+        f32x4_t part[2][4], psc[2];
+#pragma unroll
+        for (int i = 0; i < NMB; ++i) {
+          i32x8_t fa_n;
+          f32x4_t sa_n;
+          if (i < NMB - 1) {
+            fa_n = frag_a(i + 1);
+            sa_n = *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * (i + 1));
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) part[i & 1][j] = mfma(fa, j);
+          psc[i & 1] = sc;
+          if (i > 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i - 1][j] += part[(i - 1) & 1][j] * psc[(i - 1) & 1];
+          }
+          if (i < NMB - 1) {
+            fa = fa_n;
+            sc = sa_n * sw;
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next m-block's LDS reads
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU (promotions)
+          }
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // the next combined scales
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[NMB - 1][j] += part[(NMB - 1) & 1][j] * psc[(NMB - 1) & 1];
+      }
     }
-    auto frag_a = [&](int i) {
-      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + a_frag0 + 2048 * i);
-      const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + a_frag1 + 2048 * i);
-      return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    };
-    auto row_scales = [&](int i) { return *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * i) * sw; };
-    // operand formats 0 (e4m3), block scales 2^0: the fp32 scales are applied on the VALU
-    auto mfma = [&](const i32x8_t& fa, int j) {
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], zero, 0, 0, 0, 127, 0, 127);
-    };
-    // Software pipeline over the wave's 8 m-blocks. Per m-block i: read m-block i + 1's
-    // fragment and row scales from LDS, then issue i's four MFMAs, each followed by four of
-    // the FMAs that promote m-block i - 1's partial products (issued a whole block earlier, so
-    // they are ready), then form i + 1's combined scales. Scheduling-group barriers pin that
-    // order (the compiler would otherwise promote each result right after its MFMA and wait
-    // for it), and a scheduling barrier per m-block keeps it from hoisting every block's
-    // reads, which would not fit the registers. Wave rows with fewer rows still run all 8
-    // m-blocks (their extra rows are clamped copies, never stored); wave rows with none skip.
-    i32x8_t fa = frag_a(0);
-    f32x4_t sc = row_scales(0);
-    f32x4_t part[2][4], psc[2];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      i32x8_t fa_n;
-      f32x4_t sa_n;
-      if (i < 7) {
-        fa_n = frag_a(i + 1);
-        sa_n = *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * (i + 1));
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) part[i & 1][j] = mfma(fa, j);
-      psc[i & 1] = sc;
-      if (i > 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i - 1][j] += part[(i - 1) & 1][j] * psc[(i - 1) & 1];
-      }
-      if (i < 7) {
-        fa = fa_n;
-        sc = sa_n * sw;
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next m-block's LDS reads
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU (promotions)
-      }
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // the next combined scales
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[7][j] += part[1][j] * psc[1];
-  }
+  };
+  // nmb is uniform (from the tile's row range and the wave row), so this is a scalar branch
+  const int nmb_even = nmb <= 0 ? 0 : (nmb + 1) & ~1;
+  if (nmb_even == 0) kloop(std::integral_constant<int, 0>{});
+  else if (nmb_even == 2) kloop(std::integral_constant<int, 2>{});
+  else if (nmb_even == 4) kloop(std::integral_constant<int, 4>{});
+  else if (nmb_even == 6) kloop(std::integral_constant<int, 6>{});
+  else kloop(std::integral_constant<int, 8>{});
   // every wave is done with the ring (its space is reused below)
   __syncthreads();
 
