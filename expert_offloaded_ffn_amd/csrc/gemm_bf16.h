@@ -36,9 +36,9 @@ constexpr int kStageBytes = kStageA + kBN * 64;   // + B: 256 rows x 32 bf16 (36
 
 // One 256-column tile of B against a (256 or, on an expert's last m-tile, up to 320)-row
 // tile of A. TALL selects 10 instead of 8 m-blocks of 16 rows per wave.
-template <int MODE, bool TALL>
+template <int MODE, bool TALL, typename Claim>
 __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[kStageBytes], int e, int row0,
-                                               int row_end, int n0) {
+                                               int row_end, int n0, Claim&& claim) {
   constexpr int MB = TALL ? 10 : 8;   // m-blocks per wave
   // the wave index is uniform across the wave: keep it (and what derives from it) scalar
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -153,6 +153,8 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
     }
     if (s + 1 < KS) barrier_no_fence();
   }
+  // the next tile is claimed now, so the atomic's round trip overlaps the epilogue
+  claim();
   // the last MFMAs must retire before their accumulators are read (the hazard
   // recognizer does not see inside the inline assembly)
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -199,24 +201,38 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
 template <int MODE>
 __global__ __launch_bounds__(64 * kGemmWaves, 1) void ffn_gemm_bf16(GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[kStages][kStageBytes];
+  __shared__ int32_t s_prefix[kMaxE + 1];   // the m-tile prefix, searched once per tile
   __shared__ int s_tile;
   const int NT = p.N / kBN;
+  for (int i = threadIdx.x; i <= p.E; i += blockDim.x) s_prefix[i] = p.tile_prefix[i];
   const int total = p.tile_prefix[p.E] * NT;
   int range = 0;   // thread 0: how many XCD ranges this block has used up
-  for (;;) {
+  // thread 0 claims a block's next tile: the first here, each later one right after the k loop
+  // of the tile before it (its atomic then overlaps that tile's epilogue)
+  auto claim = [&]() {
     if (threadIdx.x == 0) s_tile = take_tile(p.counters, total, range);
-    __syncthreads();
-    const int L = s_tile;
+  };
+  claim();
+  __syncthreads();
+  for (;;) {
+    const int L = __builtin_amdgcn_readfirstlane(s_tile);
     if (L < 0) return;
     int e, mt, mte, nt;
-    tile_coords(p.tile_prefix, p.E, NT, L, e, mt, mte, nt);
+    tile_coords(s_prefix, p.E, NT, L, e, mt, mte, nt);
+    // (read from LDS, so the compiler cannot see they are uniform: keep them scalar)
+    e = __builtin_amdgcn_readfirstlane(e);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    mte = __builtin_amdgcn_readfirstlane(mte);
+    nt = __builtin_amdgcn_readfirstlane(nt);
     const int row0 = p.offsets[e] + mt * kBM;
     const int row_end = mt + 1 < mte ? row0 + kBM : p.offsets[e + 1];
+    // every wave reads s_tile before the tile's first barrier, and thread 0 overwrites it only
+    // after the k loop
     if (kTallRows > 0 && row_end - row0 > kBM)
-      gemm_bf16_tile<MODE, (kTallRows > 0)>(p, smem, e, row0, row_end, nt * kBN);
+      gemm_bf16_tile<MODE, (kTallRows > 0)>(p, smem, e, row0, row_end, nt * kBN, claim);
     else
-      gemm_bf16_tile<MODE, false>(p, smem, e, row0, row_end, nt * kBN);
-    // every wave is done with the LDS ring and has read s_tile before they are reused
+      gemm_bf16_tile<MODE, false>(p, smem, e, row0, row_end, nt * kBN, claim);
+    // every wave is done with the LDS ring, and s_tile holds the next tile
     __syncthreads();
   }
 }

@@ -141,9 +141,10 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
 }
 
 // One 256 x 256 tile: rows [row0, row_end) of expert e (at most 256 of them), columns n0..n0+255.
-template <int MODE>
+template <int MODE, typename Claim>
 __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s_wscale)[kQMaxKB],
-                                         float (*amax_x)[kQBM], int e, int row0, int row_end, int n0) {
+                                         float (*amax_x)[kQBM], int e, int row0, int row_end, int n0,
+                                         Claim&& claim) {
   const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w >> 2, wn = w & 3;
   const int KB = p.K / 128;
@@ -295,6 +296,8 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
   else if (nmb_even == 4) kloop(std::integral_constant<int, 4>{});
   else if (nmb_even == 6) kloop(std::integral_constant<int, 6>{});
   else kloop(std::integral_constant<int, 8>{});
+  // the next tile is claimed now, so the atomic's round trip overlaps the epilogue
+  claim();
   // every wave is done with the ring (its space is reused below)
   __syncthreads();
 
@@ -445,24 +448,37 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_fp8(Fp8Args a) {
   __shared__ __attribute__((aligned(1024))) char ring[kQRing];
   __shared__ float s_wscale[2][kQMaxKB];
   __shared__ float amax_x[2][kQBM];
+  __shared__ int32_t s_prefix[2 * kMaxE + 2];   // the tile prefix, searched once per tile
   __shared__ int s_tile;
   const int NT0 = a.p[0].N / kQBN, NT1 = a.p[1].N / kQBN;
+  for (int i = threadIdx.x; i <= a.n_exp; i += blockDim.x) s_prefix[i] = a.tile_prefix[i];
   const int total = a.tile_prefix[a.n_exp];
   int range = 0;   // thread 0: XCD ranges this block has used up
-  for (;;) {
+  // thread 0 claims a block's next tile: the first here, each later one right after the k loop
+  // of the tile before it (its atomic then overlaps that tile's epilogue)
+  auto claim = [&]() {
     if (threadIdx.x == 0) s_tile = take_tile(a.counters, total, range);
-    __syncthreads();
+  };
+  claim();
+  __syncthreads();
+  for (;;) {
     const int L = __builtin_amdgcn_readfirstlane(s_tile);
     if (L < 0) return;
     int g, mt, nt;
-    grouped_tile_coords(a.tile_prefix, a.n_exp, a.E0, NT0, NT1, L, g, mt, nt);
+    grouped_tile_coords(s_prefix, a.n_exp, a.E0, NT0, NT1, L, g, mt, nt);
+    // (read from LDS, so the compiler cannot see they are uniform: keep them scalar)
+    g = __builtin_amdgcn_readfirstlane(g);
+    mt = __builtin_amdgcn_readfirstlane(mt);
+    nt = __builtin_amdgcn_readfirstlane(nt);
     const bool second = g >= a.E0;
     const Fp8Prob& p = second ? a.p[1] : a.p[0];
     const int e = __builtin_amdgcn_readfirstlane(second ? g - a.E0 : g);
     const int row0 = __builtin_amdgcn_readfirstlane(p.offsets[e] + mt * kQBM);
     const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
-    fp8_tile<MODE>(p, ring, s_wscale, amax_x, e, row0, row_end, __builtin_amdgcn_readfirstlane(nt * kQBN));
-    // every wave is done with the ring, the scale and amax arrays, and has read s_tile
+    // every wave reads s_tile before the k loop's first barrier, and thread 0 overwrites it
+    // only after the k loop
+    fp8_tile<MODE>(p, ring, s_wscale, amax_x, e, row0, row_end, __builtin_amdgcn_readfirstlane(nt * kQBN), claim);
+    // every wave is done with the ring, the scale and amax arrays, and s_tile holds the next tile
     __syncthreads();
   }
 }
