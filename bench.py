@@ -491,9 +491,11 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
     }
     if gu_n:
         a = gu_bytes / (gu_ms / 1e3) / 1e9
+        # HBM bytes per launch from the committed counter record of this workload and batch size
+        traffic = recorded_traffic(f"{cfg.name}@T{cfg.T}", f"{kname} ({who})")
         result["roofline"] = {"bound": "hbm", "kernel": f"{kname} ({who})",
                               "achieved": round(a, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                              "frac": round(a / PEAK_HBM_GBS, 4), "traffic": None,
+                              "frac": round(a / PEAK_HBM_GBS, 4), "traffic": traffic,
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
                               "work_per_launch": work,
                               "timed": "eager launches of the same steps" if graph is not None else "the timed steps"}
