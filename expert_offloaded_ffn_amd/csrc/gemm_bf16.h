@@ -155,8 +155,10 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
   }
   // the next tile is claimed now, so the atomic's round trip overlaps the epilogue
   claim();
-  // the last MFMAs must retire before their accumulators are read (the hazard
-  // recognizer does not see inside the inline assembly)
+  // the last MFMAs must retire before their accumulators are read: the hazard recognizer
+  // does not see inside the inline assembly, so the wait states are placed by hand. The
+  // CDNA3/CDNA4 ISA asks for at most 19 between an XDL MFMA (16 passes at most) writing a
+  // VGPR and a VALU or memory instruction reading it; these four s_nop 7 give 32.
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 
   // epilogue: lane holds rows 4*(lane/16)+q, column lane%16 of each 16x16 tile

@@ -77,25 +77,59 @@ struct TileMapArgs {
 
 __global__ __launch_bounds__(1024) void grouped_tile_map(TileMapArgs m, int32_t* prefix_gu, int32_t* prefix_dn,
                                                          int32_t* counters, int n_counters) {
-  __shared__ int32_t mt[2 * kMaxE + 2];
-  const int tid = threadIdx.x;
+  __shared__ int32_t wsum[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid < n_counters) counters[tid] = 0;
-  for (int g = tid; g < m.n_exp; g += blockDim.x) {
-    const int q = g < m.E0 ? 0 : 1;
-    const int e = g - (q ? m.E0 : 0);
-    const int n = m.offsets[q][e + 1] - m.offsets[q][e];
-    mt[g] = (n > 0 && m.slot_of_expert[q][e] >= 0) ? (n + kQBM - 1) / kQBM : 0;
+  // thread tid owns the experts [c0, c1): their tiles, summed, then an exclusive scan of the
+  // per-thread sums over the workgroup (shuffles within a wavefront, then the wavefront sums)
+  const int per = (m.n_exp + 1023) / 1024;   // at most 3 (n_exp <= 2 * kMaxE + 2)
+  const int c0 = min(m.n_exp, tid * per), c1 = min(m.n_exp, c0 + per);
+  int ta[3], tb[3];
+  int sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    ta[i] = tb[i] = 0;
+    const int g = c0 + i;
+    if (g < c1) {
+      const int q = g < m.E0 ? 0 : 1;
+      const int e = g - (q ? m.E0 : 0);
+      const int n = m.offsets[q][e + 1] - m.offsets[q][e];
+      const int mt = (n > 0 && m.slot_of_expert[q][e] >= 0) ? (n + kQBM - 1) / kQBM : 0;
+      ta[i] = mt * m.nt_gu[q];
+      tb[i] = mt * m.nt_dn[q];
+    }
+    sa += ta[i];
+    sb += tb[i];
+  }
+  int ia = sa, ib = sb;   // inclusive scans within the wavefront
+  for (int o = 1; o < 64; o <<= 1) {
+    const int va = __shfl_up(ia, o, 64), vb = __shfl_up(ib, o, 64);
+    if (lane >= o) {
+      ia += va;
+      ib += vb;
+    }
+  }
+  if (lane == 63) {
+    wsum[0][wave] = ia;
+    wsum[1][wave] = ib;
   }
   __syncthreads();
-  if (tid == 0) {
-    int a = 0, b = 0;
-    for (int g = 0; g < m.n_exp; ++g) {
-      const int q = g < m.E0 ? 0 : 1;
+  int a = ia - sa, b = ib - sb;   // exclusive
+  for (int w = 0; w < wave; ++w) {
+    a += wsum[0][w];
+    b += wsum[1][w];
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int g = c0 + i;
+    if (g < c1) {
       prefix_gu[g] = a;
       prefix_dn[g] = b;
-      a += mt[g] * m.nt_gu[q];
-      b += mt[g] * m.nt_dn[q];
+      a += ta[i];
+      b += tb[i];
     }
+  }
+  if (tid == 1023) {   // the last thread's running sums are the totals
     prefix_gu[m.n_exp] = a;
     prefix_dn[m.n_exp] = b;
   }

@@ -6,7 +6,8 @@
 // were hit run). The order inside an expert is by ascending token, which makes
 // the permutation unique and the whole path deterministic.
 //
-// Three passes of a counting sort, each a single wavefront per 64-token block:
+// Three passes of a counting sort over blocks of 64 tokens (a block's experts are split over
+// the kPermWaves wavefronts of its workgroup, each walking its share: e = w, w + kPermWaves, ...):
 //  block_counts  for every expert e, a 64-lane ballot of "this token picked e";
 //                popcount = the block's count for e.
 //  scan          one 1024-thread block: chunked sums over the blocks of each
@@ -24,17 +25,22 @@ namespace moeffn {
 namespace {
 
 constexpr int kMaxE = 1024;
+// Wavefronts per 64-token block in the count and scatter passes: the walk over the experts is
+// a chain of dependent ballots, so splitting it shortens each chain (DeepSeek-V3 shape: 8192
+// tokens, 256 experts).
+constexpr int kPermWaves = 4;
 
 // KMAX is a compile-time bound on k, so each lane's expert list stays in registers.
 template <int KMAX>
-__global__ __launch_bounds__(64) void permute_block_counts(const int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
-                                                           int T, int k, int E) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kPermWaves) void permute_block_counts(const int32_t* __restrict__ idx,
+                                                                        int32_t* __restrict__ cnt, int T, int k,
+                                                                        int E) {
+  const int b = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = b * 64 + lane;
   int mine[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) mine[j] = (t < T && j < k) ? idx[(size_t)t * k + j] : -1;
-  for (int e = 0; e < E; ++e) {
+  for (int e = w; e < E; e += kPermWaves) {
     bool has = false;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) has |= (mine[j] == e);
@@ -59,9 +65,17 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
   const bool on = e < E;
   const int per = (nb + C - 1) / C;
   const int b0 = min(nb, c * per), b1 = min(nb, b0 + per);
+  // (the counts are loaded 8 at a time, so a thread's chunk costs a few memory round trips,
+  // not one per block)
   int sum = 0;
   if (on)
-    for (int b = b0; b < b1; ++b) sum += cnt[(size_t)b * E + e];
+    for (int b = b0; b < b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? cnt[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
   int inc = sum;   // inclusive scan over the chunks of expert e
   for (int o = 1; o < C; o <<= 1) {
     const int v = __shfl_up(inc, o, 64);
@@ -90,9 +104,16 @@ __global__ __launch_bounds__(1024) void permute_scan(const int32_t* __restrict__
   __syncthreads();
   if (on) {
     int running = off[e] + inc - sum;
-    for (int b = b0; b < b1; ++b) {
-      base[(size_t)b * E + e] = running;
-      running += cnt[(size_t)b * E + e];
+    for (int b = b0; b < b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = b + u < b1 ? cnt[(size_t)(b + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b + u < b1) {
+          base[(size_t)(b + u) * E + e] = running;
+          running += v[u];
+        }
     }
   }
 }
@@ -109,16 +130,18 @@ __global__ __launch_bounds__(1024) void permute_small(const int32_t* __restrict_
 }
 
 template <int KMAX>
-__global__ __launch_bounds__(64) void permute_scatter(const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-                                                      const int32_t* __restrict__ base, int32_t* __restrict__ perm_src,
-                                                      int32_t* __restrict__ perm_dst, int T, int k, int E) {
-  const int b = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kPermWaves) void permute_scatter(const int32_t* __restrict__ idx,
+                                                                   const int32_t* __restrict__ cnt,
+                                                                   const int32_t* __restrict__ base,
+                                                                   int32_t* __restrict__ perm_src,
+                                                                   int32_t* __restrict__ perm_dst, int T, int k, int E) {
+  const int b = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = b * 64 + lane;
   int mine[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) mine[j] = (t < T && j < k) ? idx[(size_t)t * k + j] : -1;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int e = 0; e < E; ++e) {
+  for (int e = w; e < E; e += kPermWaves) {
     if (cnt[(size_t)b * E + e] == 0) continue;  // uniform across the wave
     int jj = -1;
 #pragma unroll
@@ -297,10 +320,10 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
       hipLaunchKernelGGL(permute_small<KM>, dim3(1), dim3(1024), 0, s, topk_idx, offsets, perm_src, perm_dst, T, k, E);
       return;
     }
-    hipLaunchKernelGGL(permute_block_counts<KM>, dim3(nb), dim3(64), 0, s, topk_idx, cnt, T, k, E);
+    hipLaunchKernelGGL(permute_block_counts<KM>, dim3(nb), dim3(64 * kPermWaves), 0, s, topk_idx, cnt, T, k, E);
     hipLaunchKernelGGL(permute_scan, dim3(1), dim3(1024), 0, s, cnt, base, offsets, nb, E);
-    hipLaunchKernelGGL(permute_scatter<KM>, dim3(nb), dim3(64), 0, s, topk_idx, cnt, base, perm_src, perm_dst, T, k,
-                       E);
+    hipLaunchKernelGGL(permute_scatter<KM>, dim3(nb), dim3(64 * kPermWaves), 0, s, topk_idx, cnt, base, perm_src,
+                       perm_dst, T, k, E);
   };
   if (k <= 2) sort(std::integral_constant<int, 2>{});
   else if (k <= 4) sort(std::integral_constant<int, 4>{});
