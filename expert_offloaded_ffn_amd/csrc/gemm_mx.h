@@ -124,50 +124,82 @@ __device__ __forceinline__ void mx_tile(const MxProb& p, char* ring, int e, int 
   // loads this wave issues per stage: its A instructions (rows past the tile's last row are
   // not loaded), two B code loads and one exponent load
   const int n_ld = min(4, max(0, (a_rows_w + 7) >> 3)) + 3;
-  issue(0);
-  if (KC > 1) issue(1);
-  for (int s = 0; s < KC; ++s) {
-    // stage s has landed for every wave (each wave waits until only its loads of stage s + 1
-    // are outstanding), and every wave is done with stage s - 1's buffer, which the loads of
-    // stage s + 2 issued below overwrite
-    if (s + 1 < KC) {
-      switch (n_ld) {
-        case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
-        case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-        case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
-        case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
-        default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+  // The k loop for NMB computed m-blocks per wave (the wave's m-blocks with rows, rounded up to
+  // an even count; the extra one of an odd count computes on rows past the tile's last and is
+  // never stored).
+  auto kloop = [&](auto nmb_c) {
+    constexpr int NMB = decltype(nmb_c)::value;
+    issue(0);
+    if (KC > 1) issue(1);
+    for (int s = 0; s < KC; ++s) {
+      // stage s has landed for every wave (each wave waits until only its loads of stage
+      // s + 1 are outstanding), and every wave is done with stage s - 1's buffer, which the
+      // loads of stage s + 2 issued below overwrite
+      if (s + 1 < KC) {
+        switch (n_ld) {
+          case 3: asm volatile("s_waitcnt vmcnt(3)" ::: "memory"); break;
+          case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+          case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+          case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+          default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+        }
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    barrier_no_fence();
-    if (s + 2 < KC) issue(s + 2);
-    if (nmb <= 0) continue;
-    const char* buf = ring + (s % kXStages) * kXStage;
-    i32x8_t fb[4];
-    int sb[4];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      barrier_no_fence();
+      if (s + 2 < KC) issue(s + 2);
+      if constexpr (NMB > 0) {
+        const char* buf = ring + (s % kXStages) * kXStage;
+        i32x8_t fb[4];
+        int sb[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const char* blk = buf + kXB + nblk(j) * 1024 + 4 * g4;
-      const int* q = reinterpret_cast<const int*>(blk + 16 * (lane & 15));
-      fb[j] = i32x8_t{q[0], q[64], q[128], q[192], 0, 0, 0, 0};   // pieces of lanes (l%16) + 16 p
-      sb[j] = *reinterpret_cast<const uint8_t*>(buf + kXBS + nblk(j) * 64 + 4 * (lane & 15) + g4);
-    }
+        for (int j = 0; j < 4; ++j) {
+          const char* blk = buf + kXB + nblk(j) * 1024 + 4 * g4;
+          const int* q = reinterpret_cast<const int*>(blk + 16 * (lane & 15));
+          fb[j] = i32x8_t{q[0], q[64], q[128], q[192], 0, 0, 0, 0};   // pieces of lanes (l%16) + 16 p
+          sb[j] = *reinterpret_cast<const uint8_t*>(buf + kXBS + nblk(j) * 64 + 4 * (lane & 15) + g4);
+        }
+        auto frag_a = [&](int i) {
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + a_frag0 + 2048 * i);
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + a_frag1 + 2048 * i);
+          return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        auto scale_a = [&](int i) { return (int)*reinterpret_cast<const uint8_t*>(buf + a_xfrag + 64 * i); };
+        // Software pipeline over the m-blocks: m-block i + 1's fragment and scale are read
+        // from LDS before m-block i's four MFMAs issue, so the reads overlap the matrix core;
+        // scheduling-group barriers pin that order.
+        i32x8_t fa = frag_a(0);
+        int sa = scale_a(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i < nmb) {
-        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + a_frag0 + 2048 * i);
-        const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + a_frag1 + 2048 * i);
-        const i32x8_t fa = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const int sa = *reinterpret_cast<const uint8_t*>(buf + a_xfrag + 64 * i);
+        for (int i = 0; i < NMB; ++i) {
+          i32x8_t fa_n;
+          int sa_n = 0;
+          if (i < NMB - 1) {
+            fa_n = frag_a(i + 1);
+            sa_n = scale_a(i + 1);
+          }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)   // formats: A E4M3 (0), B E2M1 (4)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+          for (int j = 0; j < 4; ++j)   // formats: A E4M3 (0), B E2M1 (4)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], 0, 4, 0, sa, 0, sb[j]);
+          if (i < NMB - 1) {
+            fa = fa_n;
+            sa = sa_n;
+          }
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // the next m-block's LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // this m-block's MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
-  }
+  };
+  // nmb is uniform (from the tile's row range and the wave row), so this is a scalar branch
+  const int nmb_even = nmb <= 0 ? 0 : (nmb + 1) & ~1;
+  if (nmb_even == 0) kloop(std::integral_constant<int, 0>{});
+  else if (nmb_even == 2) kloop(std::integral_constant<int, 2>{});
+  else if (nmb_even == 4) kloop(std::integral_constant<int, 4>{});
+  else if (nmb_even == 6) kloop(std::integral_constant<int, 6>{});
+  else kloop(std::integral_constant<int, 8>{});
   __syncthreads();   // every wave is done with the ring (its space is reused below)
 
   if constexpr (MODE == MODE_GATEUP) {
