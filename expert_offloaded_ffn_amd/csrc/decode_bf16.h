@@ -206,6 +206,16 @@ __device__ __forceinline__ void store_y(const DecodeArgs& p, size_t o, float v) 
 constexpr int kDecChunk = MOEFFN_DEC_CHUNK;   // k-tiles whose loads are issued together
 constexpr int kDecWaves = MOEFFN_DEC_WAVES;   // waves per workgroup (split-K)
 constexpr int kDecMaxSplits = 8;              // workgroups per (expert, group) of a split down GEMM
+#ifndef MOEFFN_DEC_MX_CHUNKS
+#define MOEFFN_DEC_MX_CHUNKS 2
+#endif
+constexpr int kDecMxChunks = MOEFFN_DEC_MX_CHUNKS;   // MXFP4 chunks of 4 k-steps loaded at once
+// Waves per SIMD the one-m-block MXFP4 kernels are built for (the second launch bound):
+// 6 keeps three workgroups per CU with the chunks above in flight.
+#ifndef MOEFFN_DEC_MX_WAVES_PER_SIMD
+#define MOEFFN_DEC_MX_WAVES_PER_SIMD 6
+#endif
+constexpr int kDecMxWavesPerSimd = MOEFFN_DEC_MX_WAVES_PER_SIMD;
 
 // One decode workgroup's LDS.
 template <int MB>
@@ -305,24 +315,53 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& p, int bid, const
     f32x4_t acc[MB][2];
 #pragma unroll
     for (int m = 0; m < MB; ++m) acc[m][0] = acc[m][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = kt0; k0 < kt1; k0 += kDecChunk) {
+    if constexpr (WF == 1) {
+      // MXFP4: a chunk of 4 k-steps is 16 bytes of codes and 4 of scales per lane and n-tile,
+      // a third of a bf16 chunk's bytes, so up to kDecMxChunks chunks are loaded at once (one
+      // round trip for the wave's K range at these sizes) and each k-step is decoded to bf16
+      // fragments just before its MFMAs
+      constexpr int NC = MB == 1 ? kDecMxChunks : 1;   // (a four-m-block pass has no registers to spare)
+      for (int k0 = kt0; k0 < kt1; k0 += 4 * NC) {
+        uint4 w0[NC], w1[NC];
+        uint32_t e0[NC], e1[NC];
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+          if (k0 + 4 * u < kt1) {
+            const int64_t ch = k0 / 4 + u;
+            w0[u] = *reinterpret_cast<const uint4*>(b0 + ch * 1024);
+            w1[u] = *reinterpret_cast<const uint4*>(b1 + ch * 1024);
+            e0[u] = *reinterpret_cast<const uint32_t*>(sc0 + ch * 64);
+            e1[u] = *reinterpret_cast<const uint32_t*>(sc1 + ch * 64);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+          if (k0 + 4 * u < kt1) {
+            const uint32_t c0w[4] = {w0[u].x, w0[u].y, w0[u].z, w0[u].w};
+            const uint32_t c1w[4] = {w1[u].x, w1[u].y, w1[u].z, w1[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const bf16x8_t f0 = fp4x8_to_bf16(c0w[c], (e0[u] >> (8 * c)) & 255u);
+              const bf16x8_t f1 = fp4x8_to_bf16(c1w[c], (e1[u] >> (8 * c)) & 255u);
+#pragma unroll
+              for (int m = 0; m < MB; ++m) {
+                if (m < mbn) {
+                  const bf16x8_t fa = *reinterpret_cast<const bf16x8_t*>(arow[m] + (int64_t)(k0 + 4 * u + c) * 32);
+                  acc[m][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f0, acc[m][0], 0, 0, 0);
+                  acc[m][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, f1, acc[m][1], 0, 0, 0);
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    for (int k0 = kt0; WF == 0 && k0 < kt1; k0 += kDecChunk) {
       const int nk = min(kDecChunk, kt1 - k0);
       // the chunk's tiles as constant offsets from one pointer per n-tile, so the loads issue
       // back to back with immediate offsets
       bf16x8_t fb[kDecChunk][2];
-      if constexpr (WF == 1) {
-        static_assert(kDecChunk == 4, "an MXFP4 chunk is 4 k-steps");
-        const uint4 w0 = *reinterpret_cast<const uint4*>(b0 + (int64_t)(k0 / 4) * 1024);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(b1 + (int64_t)(k0 / 4) * 1024);
-        const uint32_t e0 = *reinterpret_cast<const uint32_t*>(sc0 + (int64_t)(k0 / 4) * 64);
-        const uint32_t e1 = *reinterpret_cast<const uint32_t*>(sc1 + (int64_t)(k0 / 4) * 64);
-        const uint32_t c0w[4] = {w0.x, w0.y, w0.z, w0.w}, c1w[4] = {w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          fb[c][0] = fp4x8_to_bf16(c0w[c], (e0 >> (8 * c)) & 255u);
-          fb[c][1] = fp4x8_to_bf16(c1w[c], (e1 >> (8 * c)) & 255u);
-        }
-      } else {
+      {
         const char* q0 = b0 + (int64_t)k0 * 1024;
         const char* q1 = b1 + (int64_t)k0 * 1024;
 #pragma unroll
@@ -453,7 +492,7 @@ __device__ __forceinline__ void decode_block(const DecodeArgs& p, int bid, const
 // Blocks [0, nb0) work on problem p0, the rest on p1 (two independent grouped FFNs, e.g.
 // the routed experts and the shared expert, in one launch), both in projection MODE.
 template <int MODE, bool SPLIT, int MB, bool COMB = false, int WF = 0>
-__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
+__global__ __launch_bounds__(64 * kDecWaves, WF == 1 && MB == 1 ? kDecMxWavesPerSimd : MOEFFN_DEC_MINBLOCKS) void ffn_decode_bf16(
     DecodeArgs p0, DecodeArgs p1, int nb0, DecodeCombine cb) {
   __shared__ DecodeLds<MB> L;
   const bool second = (int)blockIdx.x >= nb0;
@@ -465,7 +504,7 @@ __global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_deco
 // projection of dn (split over K when SPLIT; fp32 outputs for a later folded combine when
 // YF32), the rest the gate/up projection of gu. Both one m-block per pass.
 template <bool SPLIT, bool YF32, int WF>
-__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void ffn_decode_down_gateup(DecodeArgs dn,
+__global__ __launch_bounds__(64 * kDecWaves, WF == 1 ? kDecMxWavesPerSimd : MOEFFN_DEC_MINBLOCKS) void ffn_decode_down_gateup(DecodeArgs dn,
                                                                                              DecodeArgs gu,
                                                                                              int nb0) {
   __shared__ DecodeLds<1> L;

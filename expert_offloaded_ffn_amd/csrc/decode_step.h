@@ -110,7 +110,7 @@ __device__ __forceinline__ void step_route_block(const StepRoute& r, int b, Step
 // rounded up to a multiple of 8 so the shared expert's units keep their XCD placement), the
 // rest run the shared expert's gate/up units (gu), when there is a shared expert.
 template <int PL, int KM, int WF>
-__global__ __launch_bounds__(64 * kDecWaves, MOEFFN_DEC_MINBLOCKS) void decode_step_front(StepRoute r, int nb_route,
+__global__ __launch_bounds__(64 * kDecWaves, WF == 1 ? kDecMxWavesPerSimd : MOEFFN_DEC_MINBLOCKS) void decode_step_front(StepRoute r, int nb_route,
                                                                                         DecodeArgs gu) {
   __shared__ union {
     StepRouteLds route;
