@@ -2,67 +2,97 @@
 // order, plus the always-resident shared expert ("Running 35B MoE Models on 8GB
 // GPUs", section "Gotcha": shared experts sit outside the routed, cached set).
 //
-// One wavefront per token (large batches) or per (token, 512-column chunk) (small
-// ones); each lane owns 8 consecutive columns per step, reads the k expert rows through perm_dst with 16-byte (bf16) or
-// 32-byte (fp32) loads, accumulates in fp32 in slot order j = 0..k-1, adds the
-// shared term last and rounds once.
+// One wavefront per (token, 512-column chunk); each lane owns 8 consecutive columns, reads
+// the k expert rows through perm_dst with 16-byte (bf16) or 32-byte (fp32) loads, eight rows'
+// loads in flight at once, accumulates in fp32 in slot order j = 0..k-1, adds the shared
+// term last and rounds once.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moeffn {
 namespace {
 
+// Eight consecutive values of a row: the raw 16 (bf16) or 32 (fp32) bytes, loaded first and
+// converted later, so several rows' loads can be in flight at once.
 template <typename TY>
-__device__ __forceinline__ void load8(const TY* p, float v[8]);
+struct Raw8;
 template <>
-__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float v[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+struct Raw8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float v[8]) const {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
   }
-}
+};
 template <>
-__device__ __forceinline__ void load8<float>(const float* p, float v[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
+struct Raw8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const float4*>(p);
+    b = *reinterpret_cast<const float4*>(p + 4);
+  }
+  __device__ __forceinline__ void get(float v[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
 
-template <typename TY, typename TO>
+// KMAX bounds k (8 or 32), so the token's rows and gates stay in registers; the rows of a
+// column chunk are loaded 8 at a time before the first add (the adds keep slot order).
+template <typename TY, typename TO, int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, const int32_t* __restrict__ perm_dst,
                                                       const float* __restrict__ gate, const TY* __restrict__ shared_y,
                                                       const float* __restrict__ shared_gate, TO* __restrict__ out,
                                                       int T, int k, int d, int span) {
-  // one wavefront per (token, span of 512-column chunks): a small batch spreads each token
-  // over d / 512 wavefronts (span 1), a large one gives a wavefront the whole row
+  // one wavefront per (token, span of 512-column chunks)
   const int nchunk = (d + 511) / 512;
   const int groups = (nchunk + span - 1) / span;
   const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int t = item / groups, gi = item - t * groups;
   const int lane = threadIdx.x & 63;
   if (t >= T) return;
-  int rows[32];
-  float g[32];
-  for (int j = 0; j < k; ++j) {
-    rows[j] = perm_dst[(size_t)t * k + j];
-    g[j] = gate[(size_t)t * k + j];
+  int rows[KMAX];
+  float g[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      rows[j] = perm_dst[(size_t)t * k + j];
+      g[j] = gate[(size_t)t * k + j];
+    }
   }
   const float sg = shared_y ? (shared_gate ? shared_gate[t] : 1.0f) : 0.0f;
   const int c_end = min(d, (gi + 1) * span * 512);
   for (int c = gi * span * 512 + lane * 8; c < c_end; c += 512) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      float v[8];
-      load8<TY>(y + (size_t)rows[j] * d + c, v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j], v[i], acc[i]);
+    for (int j0 = 0; j0 < KMAX; j0 += 8) {
+      if (j0 < k) {
+        Raw8<TY> raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < k) raw[u].load(y + (size_t)rows[j0 + u] * d + c);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (j0 + u < k) {
+            float v[8];
+            raw[u].get(v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[j0 + u], v[i], acc[i]);
+          }
+        }
+      }
     }
     if (shared_y) {
+      Raw8<TY> raw;
+      raw.load(shared_y + (size_t)t * d + c);
       float v[8];
-      load8<TY>(shared_y + (size_t)t * d + c, v);
+      raw.get(v);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(sg, v[i], acc[i]);
     }
@@ -78,6 +108,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, 
     }
   }
 }
+
+// 512-column chunks per wavefront for large batches. One: many short wavefronts leave no
+// partly filled last round (DeepSeek-V3 shape, 8,192 tokens x 7,168 columns, k = 8: 223 us,
+// against 230 / 234 / 243 us for 2 / 4 / 14 chunks, and 263 us with the rows loaded one at a time).
+#ifndef MOEFFN_COMBINE_SPAN
+#define MOEFFN_COMBINE_SPAN 1
+#endif
+constexpr int kCombineSpan = MOEFFN_COMBINE_SPAN;
 
 }  // namespace
 }  // namespace moeffn
@@ -98,20 +136,25 @@ extern "C" moe_status moe_combine(int32_t T, int32_t k, int32_t d, const void* y
               "moe_combine: y, shared_y and out must be 16-byte aligned");
   hipStream_t s = as_stream(stream);
   const int nchunk = (d + 511) / 512;
-  const int span = T >= 512 ? nchunk : 1;   // enough tokens fill the chip with a row each
+  const int span = T >= 512 ? min(nchunk, kCombineSpan) : 1;
   const long long items = (long long)T * ((nchunk + span - 1) / span);
   dim3 grid((unsigned)((items + 3) / 4)), block(256);
-  if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16)
-    hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t>), grid, block, 0, s, (const bf16_t*)y, perm_dst, topk_gate,
-                       (const bf16_t*)shared_y, shared_gate, (bf16_t*)out, T, k, d, span);
-  else if (y_dtype == MOE_BF16)
-    hipLaunchKernelGGL((combine_kernel<bf16_t, float>), grid, block, 0, s, (const bf16_t*)y, perm_dst, topk_gate,
-                       (const bf16_t*)shared_y, shared_gate, (float*)out, T, k, d, span);
-  else if (out_dtype == MOE_BF16)
-    hipLaunchKernelGGL((combine_kernel<float, bf16_t>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
-                       (const float*)shared_y, shared_gate, (bf16_t*)out, T, k, d, span);
-  else
-    hipLaunchKernelGGL((combine_kernel<float, float>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
-                       (const float*)shared_y, shared_gate, (float*)out, T, k, d, span);
+  auto go = [&](auto km) {
+    constexpr int KM = decltype(km)::value;
+    if (y_dtype == MOE_BF16 && out_dtype == MOE_BF16)
+      hipLaunchKernelGGL((combine_kernel<bf16_t, bf16_t, KM>), grid, block, 0, s, (const bf16_t*)y, perm_dst,
+                         topk_gate, (const bf16_t*)shared_y, shared_gate, (bf16_t*)out, T, k, d, span);
+    else if (y_dtype == MOE_BF16)
+      hipLaunchKernelGGL((combine_kernel<bf16_t, float, KM>), grid, block, 0, s, (const bf16_t*)y, perm_dst,
+                         topk_gate, (const bf16_t*)shared_y, shared_gate, (float*)out, T, k, d, span);
+    else if (out_dtype == MOE_BF16)
+      hipLaunchKernelGGL((combine_kernel<float, bf16_t, KM>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
+                         (const float*)shared_y, shared_gate, (bf16_t*)out, T, k, d, span);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, float, KM>), grid, block, 0, s, (const float*)y, perm_dst, topk_gate,
+                         (const float*)shared_y, shared_gate, (float*)out, T, k, d, span);
+  };
+  if (k <= 8) go(std::integral_constant<int, 8>{});
+  else go(std::integral_constant<int, 32>{});
   return check_launch("moe_combine");
 }
