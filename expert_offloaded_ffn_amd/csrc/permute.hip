@@ -201,17 +201,11 @@ __global__ __launch_bounds__(256) void gather_rows_quant_e4m3(const TIn* __restr
     for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
     const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
     if (col < d) {
-      uint32_t lo = 0, hi = 0;
+      float q[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float q = fminf(fmaxf(v[i] / scale, -448.0f), 448.0f);
-        lo |= f32_to_e4m3_rne(q) << (8 * i);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float q = fminf(fmaxf(v[4 + i] / scale, -448.0f), 448.0f);
-        hi |= f32_to_e4m3_rne(q) << (8 * i);
-      }
+      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(v[i] / scale, -448.0f), 448.0f);
+      const uint32_t lo = f32x4_to_e4m3x4(q[0], q[1], q[2], q[3]);
+      const uint32_t hi = f32x4_to_e4m3x4(q[4], q[5], q[6], q[7]);
       *reinterpret_cast<uint2*>(out + (size_t)r * d + col) = make_uint2(lo, hi);
       if ((lane & 15) == 0) out_scale[(size_t)r * (d / 128) + col / 128] = scale;
     }
@@ -250,12 +244,11 @@ __global__ __launch_bounds__(256) void gather_rows_quant_mxfp8(const TIn* __rest
     amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
     const int X = min(max(amax > 0.f ? ilogbf(amax) - 8 : -127, -127), 127);
     if (col < d) {
-      uint32_t lo = 0, hi = 0;
+      float q[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3_rne(fminf(fmaxf(ldexpf(v[i], -X), -448.0f), 448.0f)) << (8 * i);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        hi |= f32_to_e4m3_rne(fminf(fmaxf(ldexpf(v[4 + i], -X), -448.0f), 448.0f)) << (8 * i);
+      for (int i = 0; i < 8; ++i) q[i] = fminf(fmaxf(ldexpf(v[i], -X), -448.0f), 448.0f);
+      const uint32_t lo = f32x4_to_e4m3x4(q[0], q[1], q[2], q[3]);
+      const uint32_t hi = f32x4_to_e4m3x4(q[4], q[5], q[6], q[7]);
       *reinterpret_cast<uint2*>(out + (size_t)r * d + col) = make_uint2(lo, hi);
       if ((lane & 3) == 0) out_exp[(size_t)r * (d / 32) + col / 32] = static_cast<uint8_t>(X + 127);
     }
