@@ -99,8 +99,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const TY* __restrict__ y, 
     if constexpr (sizeof(TO) == 2) {
       uint32_t w[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)f32_to_bf16(acc[2 * i]) | ((uint32_t)f32_to_bf16(acc[2 * i + 1]) << 16);
+      for (int i = 0; i < 4; ++i) w[i] = f32x2_to_bf16x2(acc[2 * i], acc[2 * i + 1]);
       *reinterpret_cast<uint4*>(out + (size_t)t * d + c) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
       *reinterpret_cast<float4*>(out + (size_t)t * d + c) = make_float4(acc[0], acc[1], acc[2], acc[3]);

@@ -171,8 +171,8 @@ __device__ __forceinline__ void decode_combine_group(const DecodeCombine& cb, in
                                               __HIP_MEMORY_SCOPE_AGENT), acc[q]);
   }
   if (cb.out_dtype == MOE_BF16) {
-    const uint32_t w0 = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-    const uint32_t w1 = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    const uint32_t w0 = f32x2_to_bf16x2(acc[0], acc[1]);
+    const uint32_t w1 = f32x2_to_bf16x2(acc[2], acc[3]);
     *reinterpret_cast<uint2*>(static_cast<bf16_t*>(cb.out) + (size_t)t * d + c) = make_uint2(w0, w1);
   } else {
     *reinterpret_cast<float4*>(static_cast<float*>(cb.out) + (size_t)t * d + c) =

@@ -176,7 +176,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
           const int r = rbase + i * 16 + q;
           if (r < row_end) {
             const float g = acc[i][2 * pp][q], u = acc[i][2 * pp + 1][q];
-            H[(size_t)r * F + hcol] = f32_to_bf16(silu_fast(g) * u);
+            H[(size_t)r * F + hcol] = f32_to_bf16_int(silu_fast(g) * u);
           }
         }
       }
@@ -191,7 +191,7 @@ __device__ __forceinline__ void gemm_bf16_tile(const GemmArgs& p, char (*smem)[k
         for (int q = 0; q < 4; ++q) {
           const int r = rbase + i * 16 + q;
           if (r < row_end) {
-            if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[(size_t)r * p.N + col] = f32_to_bf16(acc[i][j][q]);
+            if (p.out_dtype == MOE_BF16) static_cast<bf16_t*>(p.out)[(size_t)r * p.N + col] = f32_to_bf16_int(acc[i][j][q]);
             else static_cast<float*>(p.out)[(size_t)r * p.N + col] = acc[i][j][q];
           }
         }
