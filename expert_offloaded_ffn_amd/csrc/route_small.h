@@ -30,13 +30,38 @@ __device__ __forceinline__ int unpack_idx(uint64_t w) {
   return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(w & 0xFFFFFFFFu));
 }
 
+// The 64-bit value of the lane that the DPP control CTRL names (a permutation inside each row
+// of 16 lanes; every lane of the wavefront active).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Largest value over the wavefront, in every lane (called with every lane active). Inside each
+// row of 16 lanes four DPP steps (swap neighbours, swap pairs, mirror halves of 8, mirror the
+// row) leave the row's largest value in all its lanes; the four rows' values are then read
+// into scalar registers. (Register moves between lanes, where a butterfly of shuffles would
+// take an LDS permute per 32-bit half and step.)
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  uint64_t o;
+  o = dpp_u64<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v = o > v ? o : v;
+  o = dpp_u64<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v = o > v ? o : v;
+  o = dpp_u64<0x141>(v);   // row_half_mirror
+  v = o > v ? o : v;
+  o = dpp_u64<0x140>(v);   // row_mirror
+  v = o > v ? o : v;
+  uint64_t m = 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    const uint64_t x = ((uint64_t)hi << 32) | lo;
+    m = x > m ? x : m;
   }
-  return v;
+  return m;
 }
 __device__ __forceinline__ float wave_sum_f32(float v) {
 #pragma unroll
