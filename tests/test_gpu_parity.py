@@ -202,6 +202,66 @@ def test_permute_gather_and_e4m3_quantisation_bit_exact():
     assert np.array_equal(to_np(c["x_out"]), xf[src // cfg.k])
 
 
+def _rounding_case_values():
+    """Every e4m3 code value, every midpoint between consecutive codes and the two bf16 neighbours
+    of each midpoint, both signs: the exact ties and near-ties that random inputs almost never
+    reach. All of them are bf16 values."""
+    from oracle import formats
+    pos = formats.e4m3_table()[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    mb = synth.to_bf16_bits(mids.astype(np.float32)).astype(np.int64)
+    below = formats.decode_bf16((mb - 1).astype(np.uint16))
+    above = formats.decode_bf16((mb + 1).astype(np.uint16))
+    v = np.concatenate([pos, mids, below, above])
+    v = np.concatenate([v, -v])
+    assert np.array_equal(formats.decode_bf16(synth.to_bf16_bits(v.astype(np.float32))), v)
+    return v
+
+
+def _rounding_case_rows(v, block, ks):
+    """One row per power of two 2^k in ks: blocks of `block` columns, each led by 448 * 2^k (so the
+    block's e4m3 scale, or MX exponent, is exactly 2^k) and followed by values of v times 2^k."""
+    per = block - 1
+    nb = -(-len(v) // per)
+    rows = []
+    for k in ks:
+        r = np.zeros((nb, block))
+        r[:, 0] = 448.0 * 2.0 ** k
+        vv = np.zeros(nb * per)
+        vv[:len(v)] = v * 2.0 ** k
+        r[:, 1:] = vv.reshape(nb, per)
+        rows.append(r.reshape(-1))
+    return np.stack(rows)
+
+
+def test_e4m3_and_mxfp8_rounding_at_ties_bit_exact():
+    """The device's e4m3 rounding (a gfx950 conversion instruction) at every code, every midpoint
+    between codes and the bf16 neighbours of each midpoint, through moe_permute's e4m3 (per 128
+    columns) and MXFP8 (per 32) token quantisation: codes and scales bit for bit against the oracle,
+    with block scales 2^k exact so each test value reaches the rounding unchanged."""
+    from oracle import formats
+    v = _rounding_case_values()
+    for block, out in ((128, B.MOE_FP8_E4M3), (32, B.MOE_MXFP8)):
+        xf = _rounding_case_rows(v, block, (0, -5, 3))
+        bits = synth.to_bf16_bits(xf.astype(np.float32))
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+        T = x.shape[0]
+        idx = torch.zeros(T, 1, dtype=torch.int32, device=DEV)
+        say(f"  case rounding ties, {block}-column blocks: launching")
+        q = B.permute(idx, 1, x=x, out_dtype=out, gather=0)
+        torch.cuda.synchronize()
+        if out == B.MOE_FP8_E4M3:
+            codes, scales = formats.quantize_rows_e4m3(xf)
+            assert np.array_equal(to_np(q["x_out_scale"]), scales)
+        else:
+            codes, scales = formats.quantize_rows_mxfp8(xf)
+            assert np.array_equal(to_np(q["x_out_scale"]), scales)
+        got = to_np(q["x_out"])
+        bad = np.argwhere(got != codes)
+        assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[0]}: value {xf[tuple(bad[0])]}, got " \
+                              f"{got[tuple(bad[0])]:#04x}, oracle {codes[tuple(bad[0])]:#04x}"
+
+
 def test_dsv3_routing_full_size():
     """Group-limited sigmoid routing with selection bias at the full DeepSeek-V3 shape (bf16 router)."""
     cfg = synth.get_config("dsv3_prefill_fp8")
