@@ -33,9 +33,15 @@ namespace {
 
 constexpr int kQBM = 256, kQBN = 256;
 constexpr int kQMaxKB = 128;     // K up to 16384 (the tile's weight block scales are staged in LDS)
-// LDS ring stage: A 256 rows x 128 B (row r's 16-byte chunk c at 128 r + 16 (c ^ f(r))), B 16
-// n-blocks of 2 KiB in the bundle's fragment order, the 256 row scales of the stage.
-constexpr int kQA = 0, kQB = 32768, kQS = 65536, kQStage = 66560, kQRing = 2 * kQStage;
+// LDS ring stage of a tile of more than 128 rows (two stages): A 256 rows x 128 B (row r's
+// 16-byte chunk c at 128 r + 16 (c ^ f(r))), B 16 n-blocks of 2 KiB in the bundle's fragment
+// order, the 256 row scales of the stage.
+constexpr int kQA = 0, kQB = 32768, kQS = 65536, kQStage = 66560;
+// A tile of at most 128 rows computes on its first wave row only, so a stage's MFMAs are short
+// against the round trip of its loads: three stages of A 128 rows, B and 128 row scales keep
+// the loads of two stages in flight while one is computed.
+constexpr int kQsA = 0, kQsB = 16384, kQsS = 49152, kQsStage = 49664, kQsStages = 3;
+constexpr int kQRing = 2 * kQStage > kQsStages * kQsStage ? 2 * kQStage : kQsStages * kQsStage;
 
 // One grouped-FFN problem of a launch.
 struct Fp8Prob {
@@ -196,37 +202,32 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
     s_wscale[which][s] = v;
   }
 
-  // DMA: per stage wave w loads tile rows 32w..32w+31 of A (4 instructions of 8 rows; lane j
-  // takes row 32w + 8t + j/8, chunk (j%8) ^ f(row), which lands at position j%8), B n-blocks
-  // 2w and 2w+1 (two 1 KiB halves each) and, for w < 4, the row scales of rows 64w..64w+63.
+  // DMA: per stage wave w loads tile rows RW w .. RW w + RW - 1 of A (RW = 32, or 16 in a tile
+  // of at most 128 rows: instructions of 8 rows; lane j takes row RW w + 8t + j/8, chunk
+  // (j%8) ^ f(row), which lands at position j%8), B n-blocks 2w and 2w+1 (two 1 KiB halves
+  // each) and, for w < 4 (w < 2), the row scales of rows 64w..64w+63.
+  const bool small = valid <= 128;
+  const int rpw = small ? 16 : 32, n_ta = small ? 2 : 4;
   uint32_t a_off[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int r = 32 * w + 8 * t + (lane >> 3);
-    const int rr = min(r, valid - 1);
-    const int src = p.a_row_src ? p.a_row_src[row0 + rr] / p.a_row_div : row0 + rr;
-    a_off[t] = (uint32_t)src * (uint32_t)p.K + 16u * (uint32_t)((lane & 7) ^ fp8_swz(r & 15));
+    a_off[t] = 0;
+    if (t < n_ta) {
+      const int r = rpw * w + 8 * t + (lane >> 3);
+      const int rr = min(r, valid - 1);
+      const int src = p.a_row_src ? p.a_row_src[row0 + rr] / p.a_row_div : row0 + rr;
+      a_off[t] = (uint32_t)src * (uint32_t)p.K + 16u * (uint32_t)((lane & 7) ^ fp8_swz(r & 15));
+    }
   }
   const uint32_t b_off = (uint32_t)((n0 / 16 + 2 * w) * KB) * 2048u + 16u * lane;
   const uint32_t b_step = (uint32_t)KB * 2048u;
   const char* a_base = uniform_ptr(reinterpret_cast<const char*>(p.a));
   const char* b_base = uniform_ptr(bundle + p.b_off);
   const char* s_base = uniform_ptr(reinterpret_cast<const char*>(p.a_scale_t + row0));
-  const int a_rows_w = valid - 32 * w;   // rows of this wave's A share that exist
-  auto issue = [&](int s) {
-    char* buf = ring + (s & 1) * kQStage;
-    const char* ab = a_base + (size_t)s * 128;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      if (8 * t < a_rows_w) dma16_sb(ab, a_off[t], buf + kQA + (4 * w + t) * 1024);
-    const char* bb = b_base + (size_t)s * 2048;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        dma16_sb(bb, b_off + i * b_step + h * 1024, buf + kQB + (2 * w + i) * 2048 + h * 1024);
-    if (w < 4) dma4_sb(s_base + (size_t)s * p.a_scale_ld * 4, 4u * (64 * w + lane), buf + kQS + 256 * w);
-  };
+  const int a_rows_w = valid - rpw * w;   // rows of this wave's A share that exist
+  // loads this wave issues per stage of a small tile: its A instructions (rows past the tile's
+  // last row are not loaded), four B loads and, for w < 2, one row-scale load
+  const int n_ld_small = min(2, max(0, (a_rows_w + 7) >> 3)) + 4 + (w < 2 ? 1 : 0);
 
   f32x4_t acc[8][4];
 #pragma unroll
@@ -236,9 +237,9 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
 
   // fragment offsets: A row 16 i + l%16 of the wave row, chunks 2(l/16) and 2(l/16)+1
   const int fr = fp8_swz(lane & 15), ac = 2 * (lane >> 4);
-  const int a_frag0 = kQA + 128 * (128 * wm + (lane & 15)) + 16 * (ac ^ fr);
-  const int a_frag1 = kQA + 128 * (128 * wm + (lane & 15)) + 16 * ((ac + 1) ^ fr);
-  const int s_frag = kQS + 4 * (128 * wm + 4 * (lane >> 4));
+  const int a_frag0 = 128 * (128 * wm + (lane & 15)) + 16 * (ac ^ fr);
+  const int a_frag1 = 128 * (128 * wm + (lane & 15)) + 16 * ((ac + 1) ^ fr);
+  const int s_frag = 4 * (128 * wm + 4 * (lane >> 4));
   // the wave's n-blocks: GATEUP gate (wn even) or up (wn odd) n-blocks of hidden half wn >> 1;
   // DOWN four consecutive ones
   auto nblk = [&](int j) { return MODE == MODE_GATEUP ? (wn >> 1) * 8 + 2 * j + (wn & 1) : wn * 4 + j; };
@@ -247,35 +248,70 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
   const f32x4_t zero{0.f, 0.f, 0.f, 0.f};
 
   // The k loop for NMB computed m-blocks per wave (0, 2, 4, 6 or 8: the wave's m-blocks with
-  // rows, rounded up to an even count). The extra m-block of an odd count computes on rows past
+  // rows, rounded up to an even count) on the two-stage ring (SMALL false) or the three-stage
+  // ring of a tile of at most 128 rows. The extra m-block of an odd count computes on rows past
   // the tile's last (clamped copies of it, or stale LDS where no load was issued); those rows
   // are never stored.
-  auto kloop = [&](auto nmb_c) {
+  auto kloop = [&](auto small_c, auto nmb_c) {
+    constexpr bool SMALL = decltype(small_c)::value;
     constexpr int NMB = decltype(nmb_c)::value;
+    constexpr int A0 = SMALL ? kQsA : kQA, B0 = SMALL ? kQsB : kQB, S0 = SMALL ? kQsS : kQS;
+    constexpr int STAGE = SMALL ? kQsStage : kQStage, NS = SMALL ? kQsStages : 2, TA = SMALL ? 2 : 4;
+    auto issue = [&](int s) {
+      char* buf = ring + (s % NS) * STAGE;
+      const char* ab = a_base + (size_t)s * 128;
+#pragma unroll
+      for (int t = 0; t < TA; ++t)
+        if (8 * t < a_rows_w) dma16_sb(ab, a_off[t], buf + A0 + (TA * w + t) * 1024);
+      const char* bb = b_base + (size_t)s * 2048;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          dma16_sb(bb, b_off + i * b_step + h * 1024, buf + B0 + (2 * w + i) * 2048 + h * 1024);
+      if (w < (SMALL ? 2 : 4)) dma4_sb(s_base + (size_t)s * p.a_scale_ld * 4, 4u * (64 * w + lane), buf + S0 + 256 * w);
+    };
     issue(0);
+    if (NS > 2 && KB > 1) issue(1);
     for (int s = 0; s < KB; ++s) {
-      // stage s has landed for every wave, and every wave is done with stage s - 1's buffer
-      // (its fragment reads have completed; at s = 0 the weight scales above are written)
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      // stage s has landed for every wave (on the three-stage ring each wave waits until only
+      // its loads of stage s + 1 are outstanding), and every wave is done with stage s - 1's
+      // buffer, which the loads issued below overwrite (at s = 0 the weight scales above are
+      // written)
+      if constexpr (NS == 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
+        if (s + 1 < KB) {
+          switch (n_ld_small) {
+            case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+            case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
+            case 6: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+            default: asm volatile("s_waitcnt vmcnt(7)" ::: "memory"); break;
+          }
+        } else {
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       barrier_no_fence();
-      if (s + 1 < KB) issue(s + 1);
+      if (s + NS - 1 < KB) issue(s + NS - 1);
       if constexpr (NMB > 0) {
-        const char* buf = ring + (s & 1) * kQStage;
+        const char* buf = ring + (s % NS) * STAGE;
         const float sw = s_wscale[wsel][s];
         i32x8_t fb[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const char* blk = buf + kQB + nblk(j) * 2048 + 16 * lane;
+          const char* blk = buf + B0 + nblk(j) * 2048 + 16 * lane;
           const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(blk);
           const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(blk + 1024);
           fb[j] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
         auto frag_a = [&](int i) {
-          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + a_frag0 + 2048 * i);
-          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + a_frag1 + 2048 * i);
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(buf + A0 + a_frag0 + 2048 * i);
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(buf + A0 + a_frag1 + 2048 * i);
           return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         };
-        auto row_scales = [&](int i) { return *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * i) * sw; };
+        auto row_scales = [&](int i) { return *reinterpret_cast<const f32x4_t*>(buf + S0 + s_frag + 64 * i) * sw; };
         // operand formats 0 (e4m3), block scales 2^0: the fp32 scales are applied on the VALU
         auto mfma = [&](const i32x8_t& fa, int j) {
           return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], zero, 0, 0, 0, 127, 0, 127);
@@ -296,7 +332,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
           f32x4_t sa_n;
           if (i < NMB - 1) {
             fa_n = frag_a(i + 1);
-            sa_n = *reinterpret_cast<const f32x4_t*>(buf + s_frag + 64 * (i + 1));
+            sa_n = *reinterpret_cast<const f32x4_t*>(buf + S0 + s_frag + 64 * (i + 1));
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) part[i & 1][j] = mfma(fa, j);
@@ -323,13 +359,24 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
       }
     }
   };
-  // nmb is uniform (from the tile's row range and the wave row), so this is a scalar branch
+  // nmb is uniform (from the tile's row range and the wave row), so these are scalar branches.
+  // A tile of more than 128 rows gives its first wave row 8 m-blocks, its second 1 to 8; one of
+  // at most 128 rows gives its first wave row 1 to 8 and its second none.
+  using Big = std::false_type;
+  using Small = std::true_type;
   const int nmb_even = nmb <= 0 ? 0 : (nmb + 1) & ~1;
-  if (nmb_even == 0) kloop(std::integral_constant<int, 0>{});
-  else if (nmb_even == 2) kloop(std::integral_constant<int, 2>{});
-  else if (nmb_even == 4) kloop(std::integral_constant<int, 4>{});
-  else if (nmb_even == 6) kloop(std::integral_constant<int, 6>{});
-  else kloop(std::integral_constant<int, 8>{});
+  if (small) {
+    if (nmb_even == 0) kloop(Small{}, std::integral_constant<int, 0>{});
+    else if (nmb_even == 2) kloop(Small{}, std::integral_constant<int, 2>{});
+    else if (nmb_even == 4) kloop(Small{}, std::integral_constant<int, 4>{});
+    else if (nmb_even == 6) kloop(Small{}, std::integral_constant<int, 6>{});
+    else kloop(Small{}, std::integral_constant<int, 8>{});
+  } else {
+    if (nmb_even == 2) kloop(Big{}, std::integral_constant<int, 2>{});
+    else if (nmb_even == 4) kloop(Big{}, std::integral_constant<int, 4>{});
+    else if (nmb_even == 6) kloop(Big{}, std::integral_constant<int, 6>{});
+    else kloop(Big{}, std::integral_constant<int, 8>{});
+  }
   // the next tile is claimed now, so the atomic's round trip overlaps the epilogue
   claim();
   // every wave is done with the ring (its space is reused below)
