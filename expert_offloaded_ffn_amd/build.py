@@ -51,10 +51,10 @@ def _compile(src: str) -> str:
 
 
 # Sources whose kernels load global memory straight into LDS with inline assembly that sets
-# M0 itself (ffn_common.h dma16_asm, gemm_fp8.h dma4_asm). The compiler reserves M0 and does
+# M0 itself (lds_dma.h dma16_asm, gemm_fp8.h dma4_asm). The compiler reserves M0 and does
 # not honour it as a clobber, so the build checks the device code instead: every instruction
 # that names M0 must be one of those sequences.
-M0_CHECKED = ["grouped_ffn.hip"]
+M0_CHECKED = ["grouped_ffn.hip", "route.hip"]
 
 
 def _llvm_tool(name: str) -> str:

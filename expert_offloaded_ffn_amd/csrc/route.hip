@@ -9,6 +9,8 @@
 //  route_logits_mfma  bf16 logits on MFMA 16x16x32, split over K across the waves
 //                     of a block (operands read straight from global in the MFMA
 //                     fragment layout; the router weights stay L2-resident).
+//  route_logits_wide  bf16 logits of large batches over many experts: 64 x 128 tiles
+//                     over all of K, both operands through a direct-to-LDS ring.
 //  route_logits_f32   fp32 logits, one thread per (token, expert) dot product.
 //  route_select       one wavefront per token: keys, group limit, k rounds of a
 //                     64-lane arg-max over packed (key, ~index) words, gates, and
@@ -21,6 +23,7 @@
 #include <type_traits>
 
 #include "group_small.h"
+#include "lds_dma.h"
 #include "moe_internal.h"
 #include "route_small.h"
 
@@ -121,6 +124,113 @@ __global__ __launch_bounds__(64 * WK) void route_logits_mfma(
         if (t < T && c < ncols) {
           if (c < E) scores[(size_t)t * E + c] = v[i];
           else shared_logit[t] = v[i];
+        }
+      }
+    }
+}
+
+// More than 256 tokens over more than 64 columns: a block owns 64 tokens x 128 columns over all
+// of K, so x is read once per 128 columns and the router weights once per 64 tokens. Both
+// operands stream through an LDS ring of kRlStages stages of 64 K-values (direct-to-LDS loads:
+// 64 token rows, 8 KiB, and 128 weight rows, 16 KiB, a stage; row r's 16-byte chunk c sits at
+// 128 r + 16 (c ^ f(r)), so the 16 rows of a fragment read cover every bank once), issued
+// kRlStages - 1 stages ahead of the MFMAs. Wave w owns columns 32w..32w+31 of the block's 64
+// tokens: 4 x 2 tiles of 16x16x32 bf16 MFMAs accumulated in k order. Output as
+// route_logits_mfma.
+constexpr int kRlStages = 6, kRlA = 0, kRlB = 8192, kRlStage = 24576;
+
+__device__ __forceinline__ int rl_swz(int r) { return ((r >> 1) + 4 * (r & 1)) & 7; }
+
+__global__ __launch_bounds__(256) void route_logits_wide(const bf16_t* __restrict__ x,
+                                                         const bf16_t* __restrict__ w_router,
+                                                         const bf16_t* __restrict__ w_sg, float* __restrict__ scores,
+                                                         float* __restrict__ shared_logit, int32_t* __restrict__ counts,
+                                                         int T, int d, int E) {
+  __shared__ __attribute__((aligned(1024))) char ring[kRlStages * kRlStage];
+  if (counts != nullptr && blockIdx.x == 0 && blockIdx.y == 0) {
+    for (int e = threadIdx.x; e < E; e += blockDim.x) counts[e] = 0;
+  }
+  const int ncols = E + (w_sg != nullptr ? 1 : 0);
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t0 = blockIdx.x * 64, c0 = blockIdx.y * 128;
+  const int KS = d / 64;
+  // this lane's sources: token rows 16w + 8i + l/8 (i < 2) and weight rows 32w + 8i + l/8
+  // (i < 4) of the tile, chunk (l % 8) ^ f(row), which lands at position l % 8 of its row;
+  // rows past the last token or column read a clamped copy, never stored
+  const bf16_t* asrc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * w + 8 * i + (lane >> 3);
+    asrc[i] = x + (size_t)min(t0 + r, T - 1) * d + 8 * ((lane & 7) ^ rl_swz(r));
+  }
+  const bf16_t* bsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * w + 8 * i + (lane >> 3);
+    const int c = min(c0 + r, ncols - 1);
+    bsrc[i] = (c < E ? w_router + (size_t)c * d : w_sg) + 8 * ((lane & 7) ^ rl_swz(r));
+  }
+  auto issue = [&](int s) {
+    char* buf = ring + (s % kRlStages) * kRlStage;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16_asm(asrc[i] + s * 64, buf + kRlA + (2 * w + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16_asm(bsrc[i] + s * 64, buf + kRlB + (4 * w + i) * 1024);
+  };
+  // fragment offsets within a stage for k-step ks of 2: A row 16 m + l % 16, B row
+  // 32 w + 16 n + l % 16, chunk 4 ks + l / 16
+  const int fr = rl_swz(lane & 15), g4 = lane >> 4;
+  f32x4_t acc[4][2];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = 0; s < min(kRlStages - 1, KS); ++s) issue(s);
+  for (int s = 0; s < KS; ++s) {
+    // stage s has landed for this wave when at most the 6 loads of each later stage already
+    // issued are outstanding; the barrier then makes it so for every wave, and every wave is
+    // done with stage s - 1's buffer, which the loads issued below overwrite
+    switch (min(kRlStages - 2, KS - 1 - s)) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<6>(); break;
+      case 2: wait_vmcnt<12>(); break;
+      case 3: wait_vmcnt<18>(); break;
+      default: wait_vmcnt<24>(); break;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier_no_fence();
+    if (s + kRlStages - 1 < KS) issue(s + kRlStages - 1);
+    const char* buf = ring + (s % kRlStages) * kRlStage;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = 16 * ((4 * ks + g4) ^ fr);
+      bf16x8_t a[4], b[2];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        a[m] = *reinterpret_cast<const bf16x8_t*>(buf + kRlA + 128 * (16 * m + (lane & 15)) + ch);
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+        b[n] = *reinterpret_cast<const bf16x8_t*>(buf + kRlB + 128 * (32 * w + 16 * n + (lane & 15)) + ch);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b[n], acc[m][n], 0, 0, 0);
+    }
+  }
+  // D layout: lane l holds rows 4 (l / 16) + i, column l % 16
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int c = c0 + 32 * w + 16 * n + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * m + 4 * g4 + i;
+        if (t < T && c < ncols) {
+          if (c < E) scores[(size_t)t * E + c] = acc[m][n][i];
+          else shared_logit[t] = acc[m][n][i];
         }
       }
     }
@@ -354,6 +464,10 @@ extern "C" moe_status moe_route(const moe_route_cfg* cfg, const void* x, const v
       dim3 grid((c.T + 15) / 16, (ncols + 63) / 64);
       hipLaunchKernelGGL((route_logits_mfma<1, 16>), grid, dim3(1024), 0, s, xb, wb, sgb, scores, shared_gate, counts,
                          c.T, c.d_model, c.n_experts);
+    } else if (c.d_model % 64 == 0) {
+      dim3 grid((c.T + 63) / 64, (ncols + 127) / 128);
+      hipLaunchKernelGGL(route_logits_wide, grid, dim3(256), 0, s, xb, wb, sgb, scores, shared_gate, counts, c.T,
+                         c.d_model, c.n_experts);
     } else {
       dim3 grid((c.T + 63) / 64, (ncols + 63) / 64);
       hipLaunchKernelGGL((route_logits_mfma<4, 4>), grid, dim3(256), 0, s, xb, wb, sgb, scores, shared_gate, counts,

@@ -283,6 +283,44 @@ def test_dsv3_routing_full_size():
     np.testing.assert_allclose(g.sum(axis=1), 2.5, rtol=1e-5)
 
 
+_WIDE_CASES = [
+    # moe_route's large-batch logits (more than 256 tokens over more than 64 columns, d a multiple
+    # of 64: 64-token x 128-column tiles over all of K through a 6-stage LDS ring): ragged token
+    # and column tiles, K of 3, 5, 1 and 12 stages, the shared-gate column inside a partly filled
+    # column tile
+    ("dsv3_prefill_fp8", dict(T=300, d=192)),
+    ("qwen_decode_bf16", dict(T=600, E=100, d=320)),
+    ("mixtral_prefill_bf16", dict(T=257, E=72, d=64)),
+    ("qwen_decode_bf16", dict(T=1000, E=130, d=768)),
+]
+
+
+@pytest.mark.parametrize("name,over", _WIDE_CASES)
+def test_route_logits_wide_tiles(name, over):
+    cfg = synth.get_config(name, **over)
+    router = synth.gen_router(cfg)
+    w_sg = synth.gen_shared_gate(cfg) if cfg.shared_gate else None
+    sb = synth.gen_select_bias(cfg) if cfg.select_bias else None
+    x_store = synth.gen_x(cfg, 0)
+    x = _x_dev(cfg, x_store)
+    wr = torch.from_numpy(np.ascontiguousarray(router.T).view(np.int16)).view(torch.bfloat16).to(DEV)
+    sg_dev = None if w_sg is None else torch.from_numpy(w_sg.view(np.int16)).view(torch.bfloat16).to(DEV)
+    say(f"  case route wide {name} {over}: launching")
+    r = B.route(x, wr, k=cfg.k, score_fn=B.MOE_SIGMOID if cfg.score_fn == "sigmoid" else B.MOE_SOFTMAX,
+                renormalize=cfg.renormalize, route_scale=cfg.route_scale, n_groups=cfg.n_groups,
+                topk_groups=cfg.topk_groups, group_topn=cfg.group_topn,
+                select_bias=None if sb is None else torch.from_numpy(sb).to(DEV), w_shared_gate=sg_dev)
+    p = B.permute(r["idx"], cfg.E)
+    torch.cuda.synchronize()
+    say("    done")
+    check_exact_indices(cfg, r, p, cfg.T)
+    r_ref = oracle_route(cfg, x_store, router, w_sg, sb)
+    route_agreement(cfg, r_ref, r, key_tol=1e-5)
+    if cfg.shared_gate:
+        err = np.abs(to_np(r["shared_gate"]) - r_ref.shared_gate).max()
+        assert err <= 1e-5, f"shared gate err {err}"
+
+
 @pytest.mark.parametrize("T,d,E,k,F,Fs,G,TG", [(300, 512, 16, 4, 256, 256, 4, 2), (70, 256, 32, 8, 128, 128, 8, 4)])
 def test_fp8_layer_reduced(T, d, E, k, F, Fs, G, TG):
     cfg = synth.get_config("dsv3_prefill_fp8", T=T, d=d, E=E, k=k, F=F, F_shared=Fs, n_groups=G, topk_groups=TG,
