@@ -224,6 +224,10 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
   const char* a_base = uniform_ptr(reinterpret_cast<const char*>(p.a));
   const char* b_base = uniform_ptr(bundle + p.b_off);
   const char* s_base = uniform_ptr(reinterpret_cast<const char*>(p.a_scale_t + row0));
+  // bytes between the row scales of consecutive stages, in a register: the loads' asm blocks
+  // clobber memory, so a field of p read inside the loop is reloaded from the kernel
+  // arguments every stage
+  const size_t s_step = (size_t)p.a_scale_ld * 4;
   const int a_rows_w = valid - rpw * w;   // rows of this wave's A share that exist
   // loads this wave issues per stage of a small tile: its A instructions (rows past the tile's
   // last row are not loaded), four B loads and, for w < 2, one row-scale load
@@ -269,7 +273,7 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           dma16_sb(bb, b_off + i * b_step + h * 1024, buf + B0 + (2 * w + i) * 2048 + h * 1024);
-      if (w < (SMALL ? 2 : 4)) dma4_sb(s_base + (size_t)s * p.a_scale_ld * 4, 4u * (64 * w + lane), buf + S0 + 256 * w);
+      if (w < (SMALL ? 2 : 4)) dma4_sb(s_base + (size_t)s * s_step, 4u * (64 * w + lane), buf + S0 + 256 * w);
     };
     issue(0);
     if (NS > 2 && KB > 1) issue(1);
