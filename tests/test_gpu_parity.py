@@ -292,6 +292,9 @@ _WIDE_CASES = [
     ("qwen_decode_bf16", dict(T=600, E=100, d=320)),
     ("mixtral_prefill_bf16", dict(T=257, E=72, d=64)),
     ("qwen_decode_bf16", dict(T=1000, E=130, d=768)),
+    # d a multiple of 32 but not of 64: the same batches fall back to route_logits_mfma's 64-token
+    # x 64-column blocks with K split over four waves
+    ("qwen_decode_bf16", dict(T=300, E=100, d=224)),
 ]
 
 
