@@ -11,8 +11,9 @@ expert; the largest workload that fits one GPU), timed for exactly --steps steps
 --warmup; its "configs" object carries the other workloads measured in the same run,
 each with its own roofline, step-time percentiles and CPU baseline: the
 Mixtral-8x7B-shaped bf16 prefill, the Qwen1.5-MoE-shaped bf16 decode at 1, 8 and 64
-tokens (graph replays), and the expert-offload decode through a 32-slot LRU pool (256
-steps; blocking and device-planned modes beside it).
+tokens (eager launches queued ahead of the GPU, graph replays beside them), and the
+expert-offload decode through a 32-slot LRU pool (256 steps; blocking and device-planned
+modes beside it).
 
 Prints one JSON line: tokens/s for the whole job, the dominant kernel's roofline
 (algorithmic flops or bytes per launch over its average duration, timed with hipEvents
@@ -375,14 +376,49 @@ def bench_stack(args, torch, B, synth, MoELayer):
     return 0
 
 
+def _sleep_cycles_per_ms(torch):
+    """Cycles of torch.cuda._sleep (a bounded spin on the shader clock) per millisecond."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c = 20_000_000
+    torch.cuda._sleep(c)
+    e0.record()
+    torch.cuda._sleep(c)
+    e1.record()
+    torch.cuda.synchronize()
+    return c / max(e0.elapsed_time(e1), 1e-3)
+
+
+def queued_ahead(torch, n, body, group=25):
+    """Runs body(i) for i < n, each group of steps queued by the host behind a bounded GPU sleep
+    long enough for the host to issue the whole group, so no step waits on the host's launches:
+    event spans inside body then time the GPU's work. body(-1) is an untimed step that sizes the
+    sleep. Returns the host's time per body() call in ms."""
+    cpm = _sleep_cycles_per_ms(torch)
+    t0 = time.perf_counter()
+    for i in range(min(3, n)):     # the host's cost of one step, untimed
+        body(-1)
+    torch.cuda.synchronize()
+    host_ms = (time.perf_counter() - t0) / min(3, n) * 1e3
+    for g0 in range(0, n, group):
+        g = min(group, n - g0)
+        torch.cuda._sleep(int(min(500.0, 2.0 + 1.5 * g * host_ms) * cpm))
+        for i in range(g0, g0 + g):
+            body(i)
+        torch.cuda.synchronize()
+    return host_ms
+
+
 def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=None, warmup=None, graph=None,
                  cpu_sample=0):
     """Decode layer (few tokens): each step's time is measured alone with hipEvents, after a
     512 MiB pass that evicts the 256 MB last-level cache, so weights stream from HBM (a read by
     default, leaving clean lines as other layers' weight reads would; --mall-flush write leaves
-    dirty lines that the step's own reads must first write back). The
-    roofline is HBM bytes: the distinct touched experts' bundles + the shared expert + router
-    weights + activations in and out. Returns the result dict."""
+    dirty lines that the step's own reads must first write back). The host issues the flush and
+    the step faster than a serving loop would need but slower than the GPU runs them (the flush
+    alone costs it more host time than the step costs the GPU), so the steps are queued ahead of
+    the GPU in groups (queued_ahead) and the events time the GPU's work; the host's own time per
+    step is reported beside it. The roofline is HBM bytes: the distinct touched experts' bundles
+    + the shared expert + router weights + activations in and out. Returns the result dict."""
     from expert_offloaded_ffn_amd.layer import FUSE_COMBINE_MAX_T, W_CODE
     workload = workload or args.workload
     steps = args.steps if steps is None else steps
@@ -417,38 +453,46 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
         x_static = torch.empty_like(xs[0])
         x_static.copy_(xs[0])
         graph, _ = layer.capture(x_static)
-    B.profile_enable(not use_graph)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i in range(steps):
+
+    def flush_cache(i):
         if args.mall_flush == "write":
             flush.fill_(i & 255)      # leaves the last-level cache full of dirty lines
         else:
             flush_words.max()         # reads 512 MiB: clean lines, as other layers' weight reads leave it
+
+    host_s = [0.0]   # the host's time in the layer's launches (replay or forward) over the timed steps
+
+    def step(i):
+        flush_cache(max(i, 0))
+        x = xs[max(i, 0) % nb]
         if graph is not None:
-            x_static.copy_(xs[i % nb])
+            x_static.copy_(x)
+        if i >= 0:
             evs[i][0].record()
+        t = time.perf_counter()
+        if graph is not None:
             graph.replay()
         else:
-            evs[i][0].record()
-            layer.forward(xs[i % nb])
-        evs[i][1].record()
-    torch.cuda.synchronize()
+            layer.forward(x)
+        if i >= 0:
+            host_s[0] += time.perf_counter() - t
+            evs[i][1].record()
+
+    def eager_step(i):
+        flush_cache(max(i, 0))
+        layer.forward(xs[max(i, 0) % nb])
+
+    # the timed steps run without the library's per-launch events (they cost GPU time between
+    # the launches); the same steps once more as eager launches with the events, each after the
+    # same cache flush, time the kernels for the roofline (events cannot be taken inside a replay)
+    B.profile_enable(False)
+    queued_ahead(torch, steps, step)
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    B.profile_enable(True)
+    queued_ahead(torch, steps, eager_step)
     prof = B.profile_read()
     B.profile_enable(False)
-    ms = np.array([a.elapsed_time(b) for a, b in evs])
-    if graph is not None:
-        # kernel events cannot be taken inside a replay: the same steps once more as eager
-        # launches, each after the same cache flush, time the kernels for the roofline
-        B.profile_enable(True)
-        for i in range(steps):
-            if args.mall_flush == "write":
-                flush.fill_(i & 255)
-            else:
-                flush_words.max()
-            layer.forward(xs[i % nb])
-        torch.cuda.synchronize()
-        prof = B.profile_read()
-        B.profile_enable(False)
     del flush, flush_words
     step_bytes = np.array([touched[i % nb] * bundle + shared_bytes + act for i in range(steps)], np.float64)
     # The launch timed as the roofline kernel streams the touched routed experts' W_gu. In the
@@ -484,6 +528,8 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
                    "combine_in_down_launch": bool(cfg.T <= FUSE_COMBINE_MAX_T and
                                                   (fused or (layer.fuse_combine and merged)))},
         "step_ms_p10_p50_p90": percentiles(ms),
+        "timing": "GPU time per step: each group of steps queued by the host behind a bounded GPU sleep",
+        "host_ms_per_step": round(host_s[0] / steps * 1e3, 4),
         "touched_experts_mean": round(float(np.mean([touched[i % nb] for i in range(steps)])), 2),
         "layer_hbm": {"achieved": round(hbm, 1), "achieved_at_median_step": round(hbm_med, 1), "peak": PEAK_HBM_GBS,
                       "unit": "GB/s", "frac": round(hbm / PEAK_HBM_GBS, 4),
@@ -498,7 +544,7 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
                               "frac": round(a / PEAK_HBM_GBS, 4), "traffic": traffic,
                               "avg_launch_ms": round(gu_ms / gu_n, 4),
                               "work_per_launch": work,
-                              "timed": "eager launches of the same steps" if graph is not None else "the timed steps"}
+                              "timed": "eager launches of the same steps, with per-launch events"}
     if graph is not None:
         del graph
     del layer, xs
@@ -646,9 +692,14 @@ def bench_suite(args, torch, B, synth, MoELayer):
                                                     steps=max(args.steps, 20), warmup=max(args.warmup, 3),
                                                     cpu_sample=0 if args.no_cpu_baseline else 8192)
     for T in (1, 8, 64):
-        configs[f"qwen_decode_bf16_T{T}"] = bench_decode(args, torch, B, synth, MoELayer, "qwen_decode_bf16", T=T,
-                                                         steps=200, warmup=10, graph=True,
-                                                         cpu_sample=0 if args.no_cpu_baseline else 256)
+        # eager launches: with the steps queued ahead of the GPU, a graph replay of the same three
+        # launches takes about 8 us longer per step on this ROCm stack (measured beside it)
+        r = bench_decode(args, torch, B, synth, MoELayer, "qwen_decode_bf16", T=T, steps=200, warmup=10,
+                         graph=False, cpu_sample=0 if args.no_cpu_baseline else 256)
+        g = bench_decode(args, torch, B, synth, MoELayer, "qwen_decode_bf16", T=T, steps=200, warmup=10, graph=True)
+        r["graph_replay"] = {"ms_per_step": g["ms_per_step"], "step_ms_p10_p50_p90": g["step_ms_p10_p50_p90"],
+                             "host_ms_per_step": g["host_ms_per_step"]}
+        configs[f"qwen_decode_bf16_T{T}"] = r
     configs["offload_decode_bf16"] = bench_offload(args, torch, B, synth, MoELayer,
                                                    modes=("overlapped", "blocking", "device_plan_graph"),
                                                    cpu_sample=0 if args.no_cpu_baseline else 64)
