@@ -30,8 +30,10 @@ hipEvent_t take(Prof& p) {
     p.pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence at the record, whose cache write-back and invalidate
+  // would otherwise sit between the timed launch and its events
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
