@@ -376,6 +376,57 @@ def bench_stack(args, torch, B, synth, MoELayer):
     return 0
 
 
+class TimingEvent:
+    """A timing-only hipEvent created with hipEventDisableSystemFence: its record runs no
+    system-scope cache write-back and invalidate between the timed work and the event (torch's
+    events carry one). Created through the HIP runtime the process already has loaded."""
+    _hip = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._hip is None:
+            import ctypes
+            path = "libamdhip64.so"
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64" in line:
+                        path = line.split()[-1]
+                        break
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self, torch):
+        import ctypes
+        self._torch, self._c = torch, ctypes
+        self.e = ctypes.c_void_p()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(self.e), 0x20000000)  # hipEventDisableSystemFence
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self):
+        rc = self._hip.hipEventRecord(self.e, self._c.c_void_p(self._torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, end):
+        if self._hip.hipEventSynchronize(end.e) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = self._c.c_float()
+        if self._hip.hipEventElapsedTime(self._c.byref(ms), self.e, end.e) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        if self._hip is not None and self.e:
+            self._hip.hipEventDestroy(self.e)
+
+
 def _sleep_cycles_per_ms(torch):
     """Cycles of torch.cuda._sleep (a bounded spin on the shader clock) per millisecond."""
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -453,7 +504,7 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
         x_static = torch.empty_like(xs[0])
         x_static.copy_(xs[0])
         graph, _ = layer.capture(x_static)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    evs = [(TimingEvent(torch), TimingEvent(torch)) for _ in range(steps)]
 
     def flush_cache(i):
         if args.mall_flush == "write":
