@@ -609,9 +609,9 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
 def bench_prefill(args, torch, B, synth, MoELayer, workload=None, steps=None, warmup=None, cpu_sample=None):
     """Prefill layer (thousands of tokens, every expert resident): `warmup` untimed steps, then
     exactly `steps` timed steps over rotating input batches, bracketed by synchronisations, with
-    an event pair per step for the percentiles. The dominant kernel is the routed experts'
-    gate/up GEMM (real rows only): achieved = its flops per launch / its average launch time,
-    from hipEvents on its own stream. Returns the result dict."""
+    an event pair per step for the percentiles (timing-only events, TimingEvent). The dominant
+    kernel is the routed experts' gate/up GEMM (real rows only): achieved = its flops per launch
+    / its average launch time, from hipEvents on its own stream. Returns the result dict."""
     workload = workload or args.workload
     steps = args.steps if steps is None else steps
     warmup = args.warmup if warmup is None else warmup
@@ -647,8 +647,8 @@ def bench_prefill(args, torch, B, synth, MoELayer, workload=None, steps=None, wa
 
     log(f"[bench] timing {steps} steps")
     B.profile_enable(True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev0, ev1 = TimingEvent(torch), TimingEvent(torch)
+    evs = [(TimingEvent(torch), TimingEvent(torch)) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record()
