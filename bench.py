@@ -422,9 +422,18 @@ class TimingEvent:
             raise RuntimeError("hipEventElapsedTime failed")
         return float(ms.value)
 
-    def __del__(self):
-        if self._hip is not None and self.e:
+    def destroy(self):
+        """Frees the event (explicitly, while the runtime is up: not from a finaliser, which can
+        run after the runtime has shut down at interpreter exit)."""
+        if self.e:
             self._hip.hipEventDestroy(self.e)
+            self.e = self._c.c_void_p()
+
+
+def destroy_events(evs):
+    for pair in evs:
+        for e in pair:
+            e.destroy()
 
 
 def _sleep_cycles_per_ms(torch):
@@ -540,6 +549,7 @@ def bench_decode(args, torch, B, synth, MoELayer, workload=None, T=None, steps=N
     B.profile_enable(False)
     queued_ahead(torch, steps, step)
     ms = np.array([a.elapsed_time(b) for a, b in evs])
+    destroy_events(evs)
     B.profile_enable(True)
     queued_ahead(torch, steps, eager_step)
     prof = B.profile_read()
@@ -663,6 +673,7 @@ def bench_prefill(args, torch, B, synth, MoELayer, workload=None, steps=None, wa
     B.profile_enable(False)
     ms_total = ev0.elapsed_time(ev1)
     ms_steps = np.array([a.elapsed_time(b) for a, b in evs])
+    destroy_events(evs + [(ev0, ev1)])
     ms_step = ms_total / steps
     tokens_per_s = cfg.T * steps / (ms_total / 1e3)
 
