@@ -450,9 +450,12 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
             const int tr = 128 * wm + lr;                          // row within the tile
             const float a = fmaxf(amax_x[0][tr], amax_x[1][tr]);
             const float scale = a > 0.f ? a / 448.0f : 1.0f;
+            // one reciprocal per row instead of a full-precision divide per value: the
+            // quotient may move by an ulp, which changes a code only next to a rounding tie
+            const float inv = 1.0f / scale;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float y = fminf(fmaxf(acc[i][j][q] / scale, -448.0f), 448.0f);
+              const float y = fminf(fmaxf(acc[i][j][q] * inv, -448.0f), 448.0f);
               codes[lr * 64 + 16 * j + (lane & 15)] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
             }
             if (wn == 1 && (lane & 15) == 0 && tr < valid)
