@@ -235,8 +235,7 @@ __device__ __forceinline__ void mx_tile(const MxProb& p, char* ring, int e, int 
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
               float m = fmaxf(fabsf(h[2 * b][q]), fabsf(h[2 * b + 1][q]));
-#pragma unroll
-              for (int off = 1; off < 16; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+              m = max_row16(m);
               const int ex = mx_exp_e4m3(m);
               const float inv = ldexpf(1.0f, 127 - ex);   // 2^-X, exact
 #pragma unroll

@@ -109,4 +109,22 @@ typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 __device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
+// Largest v over each row of 16 lanes, in every lane of the row; called with every lane active.
+// Four DPP moves inside the row (swap neighbours, swap pairs, mirror each half of 8, mirror the
+// row) take the place of a butterfly of LDS permutes. The maximum is exact, so the result is the
+// same whatever the order.
+__device__ __forceinline__ float max_row16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+// The same over each group of 4 lanes (two quad swaps).
+__device__ __forceinline__ float max_quad(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  return v;
+}
+
 }  // namespace moeffn

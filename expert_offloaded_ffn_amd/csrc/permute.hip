@@ -197,8 +197,7 @@ __global__ __launch_bounds__(256) void gather_rows_quant_e4m3(const TIn* __restr
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    amax = max_row16(amax);
     const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
     if (col < d) {
       float q[8];
@@ -240,8 +239,7 @@ __global__ __launch_bounds__(256) void gather_rows_quant_mxfp8(const TIn* __rest
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = max_quad(amax);
     const int X = min(max(amax > 0.f ? ilogbf(amax) - 8 : -127, -127), 127);
     if (col < d) {
       float q[8];
