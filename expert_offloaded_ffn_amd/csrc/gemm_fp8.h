@@ -397,85 +397,97 @@ __device__ __forceinline__ void fp8_tile(const Fp8Prob& p, char* ring, float (*s
 
   // output rows of lane l: 128 wm + 16 i + 4 (l / 16) + q; columns 16 j + l % 16 of the wave's 64
   if constexpr (MODE == MODE_GATEUP) {
-    // gate waves hand G to the up waves of the same hidden columns: region (wm, wn >> 1) of
-    // 32 KiB holds [i][j][lane] f32x4
-    f32x4_t* Gr = reinterpret_cast<f32x4_t*>(ring + (wm * 2 + (wn >> 1)) * 32768);
-    if ((wn & 1) == 0) {
+    // The gate wave (wn even) and the up wave (wn odd) of a hidden half hold G and U of the
+    // same 128 x 64 block. The up wave finishes m-blocks [0, h), the gate wave [h, nmb): each
+    // hands the other its values of the other's m-blocks through the pair's 32 KiB of LDS
+    // ([i][j][lane] f32x4: G of m-blocks < h, U of the rest), so all eight waves (all four
+    // SIMDs) share the epilogue instead of the four up waves alone.
+    const int h = (nmb + 1) >> 1;
+    const bool up = (wn & 1) != 0;
+    f32x4_t* X = reinterpret_cast<f32x4_t*>(ring + (wm * 2 + (wn >> 1)) * 32768);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < nmb)
+    for (int i = 0; i < 8; ++i) {
+      if (up ? (i >= h && i < nmb) : (i < h)) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) Gr[(i * 4 + j) * 64 + lane] = acc[i][j];
+        for (int j = 0; j < 4; ++j) X[(i * 4 + j) * 64 + lane] = acc[i][j];
+      }
     }
     __syncthreads();
-    if (wn & 1) {
+    // H = silu(G) U for this wave's m-blocks, and its rows' maxima over its 64 hidden columns
+    const int i0 = up ? 0 : h, i1 = up ? h : nmb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < nmb) {
-          float am[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i) {
+      if (i >= i0 && i < i1) {
+        float am[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t o = X[(i * 4 + j) * 64 + lane];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g = up ? o[q] : acc[i][j][q];
+            const float u = up ? acc[i][j][q] : o[q];
+            const float hv = silu_fast(g) * u;
+            acc[i][j][q] = hv;
+            am[q] = fmaxf(am[q], fabsf(hv));
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) am[q] = fmaxf(am[q], __shfl_xor(am[q], off, 64));
+        }
+        if ((lane & 15) == 0) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) amax_x[wn >> 1][128 * wm + 16 * i + 4 * (lane >> 4) + q] = am[q];
+        }
+      }
+    }
+    __syncthreads();
+    // per row: one scale for the tile's 128 hidden columns; this wave's codes staged in LDS
+    // (4 KiB per wave, [64 rows][64 B], rows from m-block i0) for 16-byte stores
+    uint8_t* codes = reinterpret_cast<uint8_t*>(ring + w * 4096);
+    const int F = p.N / 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i >= i0 && i < i1) {
+        // lane l computes the scale of row 4 (l / 16) + l % 4 of the m-block (one divide and
+        // one reciprocal where every lane took four of each); DPP quad broadcasts hand row q's
+        // to the lanes that hold it. One reciprocal per row instead of a full-precision divide
+        // per value: the quotient may move by an ulp, which changes a code only next to a
+        // rounding tie.
+        const int trq = 128 * wm + 16 * i + 4 * (lane >> 4) + (lane & 3);
+        const float aq = fmaxf(amax_x[0][trq], amax_x[1][trq]);
+        const float scq = aq > 0.f ? aq / 448.0f : 1.0f;
+        const float invq = 1.0f / scq;
+        // the hidden half 0 pair writes the rows' scales (each row by the one wave that
+        // finishes it)
+        if ((wn >> 1) == 0 && (lane & 15) < 4 && trq < valid)
+          p.out_scale_t[(size_t)(n0 / 256) * p.out_scale_ld + row0 + trq] = scq;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lr = 16 * (i - i0) + 4 * (lane >> 4) + q;   // row among this wave's
+          const float inv = quad_bcast(invq, q);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const f32x4_t g = Gr[(i * 4 + j) * 64 + lane];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float h = silu_fast(g[q]) * acc[i][j][q];
-              acc[i][j][q] = h;
-              am[q] = fmaxf(am[q], fabsf(h));
-            }
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) am[q] = fmaxf(am[q], __shfl_xor(am[q], off, 64));
-          }
-          if ((lane & 15) == 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) amax_x[wn >> 1][128 * wm + 16 * i + 4 * (lane >> 4) + q] = am[q];
+            const float y = fminf(fmaxf(acc[i][j][q] * inv, -448.0f), 448.0f);
+            codes[lr * 64 + 16 * j + (lane & 15)] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
           }
         }
       }
     }
-    __syncthreads();
-    if (wn & 1) {
-      // per row: one scale for the tile's 128 hidden columns; codes staged in LDS (the first
-      // 8 KiB of this wave's G region, read above) as [128 rows][64 B] for 16-byte stores
-      uint8_t* codes = reinterpret_cast<uint8_t*>(Gr);
-      const int F = p.N / 2;
+    // this wave's LDS writes are done before its lanes read each other's bytes
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    uint8_t* Hq = static_cast<uint8_t*>(p.out);
+    const int hcol0 = n0 / 2 + 64 * (wn >> 1);
+    const int nrows = 16 * (i1 - i0);   // at most 64
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < nmb) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int lr = 16 * i + 4 * (lane >> 4) + q;          // row within the wave's 128
-            const int tr = 128 * wm + lr;                          // row within the tile
-            const float a = fmaxf(amax_x[0][tr], amax_x[1][tr]);
-            const float scale = a > 0.f ? a / 448.0f : 1.0f;
-            // one reciprocal per row instead of a full-precision divide per value: the
-            // quotient may move by an ulp, which changes a code only next to a rounding tie
-            const float inv = 1.0f / scale;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float y = fminf(fmaxf(acc[i][j][q] * inv, -448.0f), 448.0f);
-              codes[lr * 64 + 16 * j + (lane & 15)] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
-            }
-            if (wn == 1 && (lane & 15) == 0 && tr < valid)
-              p.out_scale_t[(size_t)(n0 / 256) * p.out_scale_ld + row0 + tr] = scale;
-          }
-        }
-      }
-      // this wave's LDS writes are done before its lanes read each other's bytes
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      uint8_t* Hq = static_cast<uint8_t*>(p.out);
-      const int hcol0 = n0 / 2 + 64 * (wn >> 1);
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int idx = it * 64 + lane;               // 512 chunks of 16 B: row idx/4, chunk idx%4
-        const int lr = idx >> 2, ch = idx & 3;
-        const int tr = 128 * wm + lr;
-        if (tr < valid) {
-          const i32x4_t v = *reinterpret_cast<const i32x4_t*>(codes + lr * 64 + 16 * ch);
-          *reinterpret_cast<i32x4_t*>(Hq + (size_t)(row0 + tr) * F + hcol0 + 16 * ch) = v;
-        }
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 64 + lane;               // 256 chunks of 16 B: row idx/4, chunk idx%4
+      const int lr = idx >> 2, ch = idx & 3;
+      const int tr = 128 * wm + 16 * i0 + lr;
+      if (lr < nrows && tr < valid) {
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(codes + lr * 64 + 16 * ch);
+        *reinterpret_cast<i32x4_t*>(Hq + (size_t)(row0 + tr) * F + hcol0 + 16 * ch) = v;
       }
     }
   } else if (p.out_dtype == MOE_BF16) {

@@ -127,4 +127,15 @@ __device__ __forceinline__ float max_quad(float v) {
   return v;
 }
 
+// Lane q's v of each group of 4 lanes, in all four (q a compile-time constant after unrolling;
+// every lane active).
+__device__ __forceinline__ float quad_bcast(float v, int q) {
+  switch (q) {
+    case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x00, 0xF, 0xF, false));
+    case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x55, 0xF, 0xF, false));
+    case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xAA, 0xF, 0xF, false));
+    default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xFF, 0xF, 0xF, false));
+  }
+}
+
 }  // namespace moeffn
