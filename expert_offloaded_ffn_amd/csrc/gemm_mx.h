@@ -203,64 +203,77 @@ __device__ __forceinline__ void mx_tile(const MxProb& p, char* ring, int e, int 
   __syncthreads();   // every wave is done with the ring (its space is reused below)
 
   if constexpr (MODE == MODE_GATEUP) {
-    // gate waves hand G to the up waves of the same hidden columns ([i][j][lane] f32x4)
-    f32x4_t* Gr = reinterpret_cast<f32x4_t*>(ring + (wm * 2 + (wn >> 1)) * 32768);
-    if ((wn & 1) == 0) {
+    // The gate wave (wn even) and the up wave (wn odd) of a hidden half hold G and U of the
+    // same 128 x 64 block. The up wave finishes m-blocks [0, h), the gate wave [h, nmb): each
+    // hands the other its values of the other's m-blocks through the pair's 32 KiB of LDS
+    // ([i][j][lane] f32x4: G of m-blocks < h, U of the rest), so all eight waves share the
+    // epilogue.
+    const int h = (nmb + 1) >> 1;
+    const bool up = (wn & 1) != 0;
+    f32x4_t* X = reinterpret_cast<f32x4_t*>(ring + (wm * 2 + (wn >> 1)) * 32768);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        if (i < nmb)
+    for (int i = 0; i < 8; ++i) {
+      if (up ? (i >= h && i < nmb) : (i < h)) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) Gr[(i * 4 + j) * 64 + lane] = acc[i][j];
+        for (int j = 0; j < 4; ++j) X[(i * 4 + j) * 64 + lane] = acc[i][j];
+      }
     }
     __syncthreads();
-    if (wn & 1) {
-      // H = silu(G) * U; its MX blocks of 32 hidden columns are the n-block pairs (0, 1) and
-      // (2, 3) of this wave, so a row's block maximum is a 16-lane reduction
-      uint8_t* codes = reinterpret_cast<uint8_t*>(Gr);
-      const int F = p.N / 2;
-      const int hcol0 = n0 / 2 + 64 * (wn >> 1);
+    // H = silu(G) * U; its MX blocks of 32 hidden columns are the n-block pairs (0, 1) and
+    // (2, 3) of this wave, so a row's block maximum is a 16-lane reduction. The codes are
+    // staged ([rows from m-block i0][64 B]) over the part of the pair region this wave reads
+    // (from m-block i0 on, 4 KiB each), which the other wave does not touch: m-block i's codes
+    // end below m-block i + 1's values, and a wave's LDS accesses complete in order.
+    const int i0 = up ? 0 : h, i1 = up ? h : nmb;
+    uint8_t* codes = reinterpret_cast<uint8_t*>(ring + (wm * 2 + (wn >> 1)) * 32768 + i0 * 4096);
+    const int F = p.N / 2;
+    const int hcol0 = n0 / 2 + 64 * (wn >> 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (i < nmb) {
-          float h[4][4];
+    for (int i = 0; i < 8; ++i) {
+      if (i >= i0 && i < i1) {
+        float hv[4][4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4_t gv = Gr[(i * 4 + j) * 64 + lane];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) h[j][q] = silu_fast(gv[q]) * acc[i][j][q];
-          }
+        for (int j = 0; j < 4; ++j) {
+          const f32x4_t o = X[(i * 4 + j) * 64 + lane];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int lr = 16 * i + 4 * (lane >> 4) + q;   // row within the wave's 128
+            const float g = up ? o[q] : acc[i][j][q];
+            const float u = up ? acc[i][j][q] : o[q];
+            hv[j][q] = silu_fast(g) * u;
+          }
+        }
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              float m = fmaxf(fabsf(h[2 * b][q]), fabsf(h[2 * b + 1][q]));
-              m = max_row16(m);
-              const int ex = mx_exp_e4m3(m);
-              const float inv = ldexpf(1.0f, 127 - ex);   // 2^-X, exact
+        for (int q = 0; q < 4; ++q) {
+          const int lr = 16 * (i - i0) + 4 * (lane >> 4) + q;   // row among this wave's
+          const int tr = 128 * wm + 16 * i + 4 * (lane >> 4) + q;   // row within the tile
 #pragma unroll
-              for (int jj = 0; jj < 2; ++jj) {
-                const float y = fminf(fmaxf(h[2 * b + jj][q] * inv, -448.0f), 448.0f);
-                codes[lr * 64 + 16 * (2 * b + jj) + (lane & 15)] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
-              }
-              const int tr = 128 * wm + lr;
-              if ((lane & 15) == 0 && tr < valid)
-                p.out_exp[(size_t)(row0 + tr) * (F / 32) + hcol0 / 32 + b] = static_cast<uint8_t>(ex);
+          for (int b = 0; b < 2; ++b) {
+            float m = fmaxf(fabsf(hv[2 * b][q]), fabsf(hv[2 * b + 1][q]));
+            m = max_row16(m);
+            const int ex = mx_exp_e4m3(m);
+            const float inv = ldexpf(1.0f, 127 - ex);   // 2^-X, exact
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const float y = fminf(fmaxf(hv[2 * b + jj][q] * inv, -448.0f), 448.0f);
+              codes[lr * 64 + 16 * (2 * b + jj) + (lane & 15)] = static_cast<uint8_t>(f32_to_e4m3_rne(y));
             }
+            if ((lane & 15) == 0 && tr < valid)
+              p.out_exp[(size_t)(row0 + tr) * (F / 32) + hcol0 / 32 + b] = static_cast<uint8_t>(ex);
           }
         }
       }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own writes, read back below
-      uint8_t* Hq = static_cast<uint8_t*>(p.out);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the wave's own writes, read back below
+    uint8_t* Hq = static_cast<uint8_t*>(p.out);
+    const int nrows = 16 * (i1 - i0);   // at most 64
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const int idx = it * 64 + lane;   // 512 chunks of 16 B: row idx/4, chunk idx%4
-        const int lr = idx >> 2, ch = idx & 3;
-        const int tr = 128 * wm + lr;
-        if (tr < valid) {
-          const i32x4_t v = *reinterpret_cast<const i32x4_t*>(codes + lr * 64 + 16 * ch);
-          *reinterpret_cast<i32x4_t*>(Hq + (size_t)(row0 + tr) * F + hcol0 + 16 * ch) = v;
-        }
+    for (int it = 0; it < 4; ++it) {
+      const int idx = it * 64 + lane;   // 256 chunks of 16 B: row idx/4, chunk idx%4
+      const int lr = idx >> 2, ch = idx & 3;
+      const int tr = 128 * wm + 16 * i0 + lr;
+      if (lr < nrows && tr < valid) {
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(codes + lr * 64 + 16 * ch);
+        *reinterpret_cast<i32x4_t*>(Hq + (size_t)(row0 + tr) * F + hcol0 + 16 * ch) = v;
       }
     }
   } else if (p.out_dtype == MOE_BF16) {
